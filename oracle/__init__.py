@@ -1,0 +1,273 @@
+"""CPU oracle of the multi-row speculative-decode step.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import this package.  The product library
+(``bit_weight_streaming_q4_amd``) never imports, links or calls it, and shares
+no code with it; the two meet only through the seeded inputs of :mod:`synth`.
+
+The arithmetic lives in ``oracle.c`` (plain C, double accumulation, no FMA
+contraction); this module marshals numpy arrays and composes the C steps in
+the order the pages give them.  Each function names the step it follows:
+
+  C1 dequant        Q4_K-style superblock -> fp32 weights
+  C2 quantize_rows  per-32 int8 activation quantization
+  C3 qgemv          T-row GEMV (dequantize, accumulate in double)
+  C4 ffn            SiLU(gate) * up, then down
+  C5 layer          pre-RMSNorm, projections, FFN, fp32 residual (synthetic glue)
+  C6 lmhead/verify  logits, argmax, accepted-prefix length, emitted tokens
+  C7 gdn_step       gated delta rule with commit through the accepted row
+  C8 decode_step    composition of one whole step
+
+Pages: richland.au "Fusing the whole speculative-decoding cycle into one CUDA
+kernel" (section "What shipped"), richland.au "OpenJet's CUDA megakernel runs
+4 coding agents" (section "Why it matters"), pulse-3k2 "UPDATE: ... KL
+divergence" (section "Decode accuracy").
+
+Parity status: C1-C4, C6 and C7 are pinned by tests against brute force,
+closed forms and library routines.  C5's glue (pre-RMSNorm, identity mixer)
+and C8's composition are readings of the pages: parity unpinned beyond the
+pinned parts they compose.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liborc.so")
+_lib = None
+RMS_EPS = 1e-6
+
+
+def build(force: bool = True) -> str:
+    """Compile ``liborc.so`` with gcc: -O2, OpenMP, no FMA contraction, no fast-math."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-D_GNU_SOURCE",
+               "-shared", "-fPIC", os.path.join(_HERE, "oracle.c"), "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=False)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    lib.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.orc_f16_to_f32.restype = ctypes.c_float
+    lib.orc_dequant.argtypes = [P, P, P, P, P, i32, i32, P]
+    lib.orc_quantize_rows.argtypes = [P, i32, i32, P, P, P]
+    lib.orc_qgemv_q8.argtypes = [P, P, P, P, P, i32, i32, P, P, i32, P]
+    lib.orc_qgemv.argtypes = [P, P, P, P, P, i32, i32, P, i32, P]
+    lib.orc_q4k_partials.argtypes = [P, i32, i32, P, i32, P]
+    lib.orc_silu_mul.argtypes = [P, P, i64, P]
+    lib.orc_ffn.argtypes = [P] * 15 + [i32, i32, P, i32, P, P]
+    lib.orc_rmsnorm.argtypes = [P, i32, i32, dbl, P]
+    lib.orc_residual_add.argtypes = [P, P, i64]
+    lib.orc_lmhead.argtypes = [P, i32, i32, P, i32, P, P, P, P, P, P, P]
+    lib.orc_verify.argtypes = [P, P, i32, P, P, P]
+    lib.orc_gdn_rows.argtypes = [P, i32, i32, P, P, P, P, P, i32, i64, i64, i64, P, i64, ctypes.c_int]
+    lib.orc_gdn_step.argtypes = [P, i32, i32, i32, P, P, P, P, P, i32, i32, P]
+    _lib = lib
+    return lib
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def _p(a):
+    return a.ctypes.data if a is not None else None
+
+
+def _fields(W):
+    d = _c(W["d"], np.uint16)
+    dmin = _c(W["dmin"], np.uint16)
+    sc = _c(W["sc"], np.uint8)
+    m = _c(W["m"], np.uint8)
+    q = _c(W["q"], np.uint8)
+    return d, dmin, sc, m, q
+
+
+def f16_to_f32(bits: int) -> float:
+    return float(_load().orc_f16_to_f32(int(bits)))
+
+
+def dequant(W) -> np.ndarray:
+    """C1: fp32 weights [N][K] of a field-array matrix."""
+    d, dmin, sc, m, q = _fields(W)
+    N, K = q.shape
+    w = np.empty((N, K), np.float32)
+    _load().orc_dequant(_p(d), _p(dmin), _p(sc), _p(m), _p(q), N, K, _p(w))
+    return w
+
+
+def quantize_rows(x):
+    """C2: (a8 int8 [T][K], s fp32 [T][K/32], gsum int32 [T][K/32])."""
+    x = _c(np.atleast_2d(x), np.float32)
+    T, K = x.shape
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    a8 = np.empty((T, K), np.int8)
+    s = np.empty((T, K // 32), np.float32)
+    gs = np.empty((T, K // 32), np.int32)
+    _load().orc_quantize_rows(_p(x), T, K, _p(a8), _p(s), _p(gs))
+    return a8, s, gs
+
+
+def qgemv_q8(W, a8, s) -> np.ndarray:
+    """C3 on quantized rows: y fp32 [T][N]."""
+    d, dmin, sc, m, q = _fields(W)
+    N, K = q.shape
+    a8 = _c(a8, np.int8)
+    s = _c(s, np.float32)
+    T = a8.shape[0]
+    y = np.empty((T, N), np.float32)
+    _load().orc_qgemv_q8(_p(d), _p(dmin), _p(sc), _p(m), _p(q), N, K, _p(a8), _p(s), T, _p(y))
+    return y
+
+
+def qgemv(W, x) -> np.ndarray:
+    """C3: y fp32 [T][N] = W . q8(x)."""
+    d, dmin, sc, m, q = _fields(W)
+    N, K = q.shape
+    x = _c(np.atleast_2d(x), np.float32)
+    T = x.shape[0]
+    assert x.shape[1] == K
+    y = np.empty((T, N), np.float32)
+    _load().orc_qgemv(_p(d), _p(dmin), _p(sc), _p(m), _p(q), N, K, _p(x), T, _p(y))
+    return y
+
+
+def q4k_partials(W, a8) -> np.ndarray:
+    """Exact integer partial sums P[t][o][g] = sum_{i<32} q*a8 over group g."""
+    q = _c(W["q"], np.uint8)
+    N, K = q.shape
+    a8 = _c(a8, np.int8)
+    T = a8.shape[0]
+    P = np.empty((T, N, K // 32), np.int32)
+    _load().orc_q4k_partials(_p(q), N, K, _p(a8), T, _p(P))
+    return P
+
+
+def silu_mul(g, u) -> np.ndarray:
+    g = _c(g, np.float32)
+    u = _c(u, np.float32)
+    h = np.empty_like(g)
+    _load().orc_silu_mul(_p(g), _p(u), g.size, _p(h))
+    return h
+
+
+def ffn(Wg, Wu, Wd, x, return_h=False):
+    """C4: y = W_d . q8(SiLU(W_g . q8(x)) * (W_u . q8(x)))."""
+    x = _c(np.atleast_2d(x), np.float32)
+    T, H = x.shape
+    F = Wg["q"].shape[0]
+    arrs = list(_fields(Wg)) + list(_fields(Wu)) + list(_fields(Wd))
+    y = np.empty((T, H), np.float32)
+    h = np.empty((T, F), np.float32)
+    _load().orc_ffn(*[_p(a) for a in arrs], H, F, _p(x), T, _p(y), _p(h))
+    return (y, h) if return_h else y
+
+
+def rmsnorm(x, eps=RMS_EPS) -> np.ndarray:
+    x = _c(np.atleast_2d(x), np.float32)
+    T, K = x.shape
+    a = np.empty_like(x)
+    _load().orc_rmsnorm(_p(x), T, K, eps, _p(a))
+    return a
+
+
+def residual_add(x, y) -> np.ndarray:
+    out = _c(x, np.float32).copy()
+    y = _c(y, np.float32)
+    _load().orc_residual_add(_p(out), _p(y), out.size)
+    return out
+
+
+def layer(x, Wl) -> np.ndarray:
+    """C5 (one synthetic layer; reading of the pages, parity unpinned beyond
+    its parts): x += P_out.q8(P_in.q8(RMSNorm x)); x += FFN(RMSNorm x)."""
+    u = qgemv(Wl["p_in"], rmsnorm(x))
+    x = residual_add(x, qgemv(Wl["p_out"], u))
+    return residual_add(x, ffn(Wl["gate"], Wl["up"], Wl["down"], rmsnorm(x)))
+
+
+def lmhead(W16, hid, return_logits=False) -> dict:
+    """C6 logits: argmax (lowest index on ties, NaN never wins), runner-up and
+    the sums of |W*hid| of both (for the near-tie bound)."""
+    W16 = _c(W16, np.uint16)
+    V, H = W16.shape
+    hid = _c(np.atleast_2d(hid), np.float32)
+    T = hid.shape[0]
+    out = {k: np.empty(T, np.int32) for k in ("top1", "top2")}
+    for k in ("top1_val", "top2_val", "abs1", "abs2"):
+        out[k] = np.empty(T, np.float64)
+    lg = np.empty((T, V), np.float64) if return_logits else None
+    _load().orc_lmhead(_p(W16), V, H, _p(hid), T, _p(lg), _p(out["top1"]), _p(out["top1_val"]),
+                       _p(out["top2"]), _p(out["top2_val"]), _p(out["abs1"]), _p(out["abs2"]))
+    if return_logits:
+        out["logits"] = lg
+    return out
+
+
+def near_tie_tau(H, abs1, abs2):
+    """Near-tie bound per row: 8 * 2^-24 * sqrt(H) * max(sum|W h|) of the top two."""
+    return 8.0 * 2.0 ** -24 * np.sqrt(H) * np.maximum(abs1, abs2)
+
+
+def verify(argmax, group_start, drafts):
+    """C6 verify: (n_acc [G], tokens [T]); unused token slots are -1."""
+    argmax = _c(argmax, np.int32)
+    gs = _c(group_start, np.int32)
+    G = len(gs) - 1
+    drafts = _c(drafts, np.int32)
+    n_acc = np.empty(G, np.int32)
+    tokens = np.full(len(argmax), -1, np.int32)
+    _load().orc_verify(_p(argmax), _p(gs), G, _p(drafts), _p(n_acc), _p(tokens))
+    return n_acc, tokens
+
+
+def gdn_rows(S, q, k, v, g, beta, literal=False):
+    """C7 rows on one head: S (float64 [dk][dv]) is updated in place; returns o [n][dv]."""
+    assert S.dtype == np.float64 and S.flags["C_CONTIGUOUS"]
+    dk, dv = S.shape
+    k = _c(np.atleast_2d(k), np.float32)
+    v = _c(np.atleast_2d(v), np.float32)
+    n = k.shape[0]
+    q = _c(np.atleast_2d(q), np.float32) if q is not None else None
+    g = _c(np.atleast_1d(g), np.float32)
+    beta = _c(np.atleast_1d(beta), np.float32)
+    o = np.empty((n, dv), np.float32) if q is not None else None
+    _load().orc_gdn_rows(_p(S), dk, dv, _p(q), _p(k), _p(v), _p(g), _p(beta), n, dk, dv, 1, _p(o), dv,
+                         int(bool(literal)))
+    return o
+
+
+def gdn_step(S, q, k, v, g, beta, a):
+    """C7 + C8 on nh heads: S fp32 [nh][dk][dv] (or [L][H][dk][dv]) is replaced
+    by the state committed through row a; returns o [T][nh][dv]."""
+    S32 = _c(S, np.float32).copy()
+    shp = S32.shape
+    dk, dv = shp[-2], shp[-1]
+    nh = S32.size // (dk * dv)
+    q = _c(q, np.float32).reshape(-1, nh, dk)
+    T = q.shape[0]
+    k = _c(k, np.float32).reshape(T, nh, dk)
+    v = _c(v, np.float32).reshape(T, nh, dv)
+    g = _c(g, np.float32).reshape(T, nh)
+    beta = _c(beta, np.float32).reshape(T, nh)
+    if not 0 <= a < T:
+        raise ValueError("accept length out of range")
+    o = np.empty((T, nh, dv), np.float32)
+    _load().orc_gdn_step(_p(S32), nh, dk, dv, _p(q), _p(k), _p(v), _p(g), _p(beta), T, int(a), _p(o))
+    return S32.reshape(shp), o

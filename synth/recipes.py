@@ -1,0 +1,124 @@
+"""Workload recipes: which seeded streams and distributions each synthetic
+workload draws.  Shapes mirror a 27B dense hybrid decoder (hidden 5120,
+FFN 17408, 64 layers of which 48 are Gated DeltaNet layers, 32 heads of
+128, vocabulary 151,936).  Every tensor is regenerable on its own from
+(seed, tensor id); nothing here computes any part of the decode method.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import gdn_step_inputs, normal_f16, normal_f32, q4k_fields, uniform_f64, uniform_i32
+
+HIDDEN = 5120
+FFN = 17408
+PROJ = 10240
+VOCAB = 151936
+DRAFT_VOCAB = 32768
+N_LAYERS = 64
+GDN_HEADS = 32
+GDN_DK = 128
+GDN_DV = 128
+
+
+def gdn_layers(n_layers: int = N_LAYERS) -> list[int]:
+    """Layers that carry a Gated DeltaNet mixer: three of every four (the
+    fourth is a full-attention layer), giving 48 of 64."""
+    return [l for l in range(n_layers) if l % 4 != 3]
+
+
+# ---------------------------------------------------------------- single GEMV
+def gemv_weight(n_out=HIDDEN, n_in=HIDDEN, seed=0, tensor=1, r0=0, r1=None):
+    return q4k_fields(seed, tensor, n_out, n_in, r0, r1)
+
+
+def rows_f32(T, K, seed=0, tensor=2):
+    """T activation rows ~ N(0, 1), fp32, [T][K]."""
+    return normal_f32(seed, tensor, 0, T * K).reshape(T, K)
+
+
+# ---------------------------------------------------------------- FFN block
+def ffn_weights(hidden=HIDDEN, ffn=FFN, seed=1, base=11):
+    return {
+        "gate": q4k_fields(seed, base + 0, ffn, hidden),
+        "up": q4k_fields(seed, base + 1, ffn, hidden),
+        "down": q4k_fields(seed, base + 2, hidden, ffn),
+    }
+
+
+# ---------------------------------------------------------------- layer stack
+STACK_SEED = 2
+STACK_MATS = ("p_in", "p_out", "gate", "up", "down")
+
+
+def stack_tensor_id(layer: int, mat: str) -> int:
+    return 100 + 8 * layer + STACK_MATS.index(mat)
+
+
+def stack_shapes(hidden=HIDDEN, proj=PROJ, ffn=FFN) -> dict:
+    return {"p_in": (proj, hidden), "p_out": (hidden, proj), "gate": (ffn, hidden),
+            "up": (ffn, hidden), "down": (hidden, ffn)}
+
+
+def stack_weight(layer, mat, hidden=HIDDEN, proj=PROJ, ffn=FFN, r0=0, r1=None, seed=STACK_SEED):
+    n_out, n_in = stack_shapes(hidden, proj, ffn)[mat]
+    return q4k_fields(seed, stack_tensor_id(layer, mat), n_out, n_in, r0, r1)
+
+
+def stack_step_input(step, T, hidden=HIDDEN, seed=STACK_SEED):
+    return normal_f32(seed, 10000 + step, 0, T * hidden).reshape(T, hidden)
+
+
+def stack_gdn_inputs(step, T, n_gdn_layers, heads=GDN_HEADS, dk=GDN_DK, dv=GDN_DV, seed=STACK_SEED):
+    return gdn_step_inputs(seed, 20000 + step, T, n_gdn_layers * heads, dk, dv)
+
+
+def stack_gdn_state(agent, n_gdn_layers, heads=GDN_HEADS, dk=GDN_DK, dv=GDN_DV, seed=STACK_SEED):
+    n = n_gdn_layers * heads * dk * dv
+    return normal_f32(seed, 40000 + agent, 0, n, 0.0, 0.01).reshape(n_gdn_layers, heads, dk, dv)
+
+
+def stack_lm_head(vocab=VOCAB, hidden=HIDDEN, seed=STACK_SEED, r0=0, r1=None):
+    r1 = vocab if r1 is None else r1
+    return normal_f16(seed, 30000, 0, (r1 - r0) * hidden, 0.0, 0.02, start=r0 * hidden).reshape(r1 - r0, hidden)
+
+
+# ---------------------------------------------------------------- lm_head + verify
+LM_SEED = 3
+
+
+def lm_head_weight(vocab=VOCAB, hidden=HIDDEN, seed=LM_SEED, r0=0, r1=None):
+    """fp16 bit patterns ~ N(0, 0.02), [vocab][hidden]; rows [r0, r1)."""
+    r1 = vocab if r1 is None else r1
+    return normal_f16(seed, 1, 0, (r1 - r0) * hidden, 0.0, 0.02, start=r0 * hidden).reshape(r1 - r0, hidden)
+
+
+def lm_hidden(T, hidden=HIDDEN, seed=LM_SEED, trial=0):
+    return normal_f32(seed, 2, trial, T * hidden).reshape(T, hidden)
+
+
+def drafts_from_argmax(true_argmax, vocab, p_match=0.7, seed=LM_SEED, trial=0):
+    """Draft i equals the true argmax of row i with probability p_match,
+    otherwise a uniform id in [0, vocab).  ``true_argmax`` has T-1 entries."""
+    n = len(true_argmax)
+    u = uniform_f64(seed, 3, trial, n)
+    rnd = uniform_i32(seed, 4, trial, n, 0, vocab - 1)
+    return np.where(u < p_match, np.asarray(true_argmax, np.int32), rnd).astype(np.int32)
+
+
+# ---------------------------------------------------------------- Gated DeltaNet
+GDN_SEED = 4
+
+
+def gdn_initial_state(n_layers=48, heads=GDN_HEADS, dk=GDN_DK, dv=GDN_DV, seed=GDN_SEED):
+    n = n_layers * heads * dk * dv
+    return normal_f32(seed, 1, 0, n, 0.0, 0.01).reshape(n_layers, heads, dk, dv)
+
+
+def gdn_step(step, T, n_layers=48, heads=GDN_HEADS, dk=GDN_DK, dv=GDN_DV, seed=GDN_SEED):
+    return gdn_step_inputs(seed, 100 + step, T, n_layers * heads, dk, dv)
+
+
+def gdn_accept_lengths(n_steps, T=5, seed=GDN_SEED):
+    """Seeded accept lengths, uniform on 0..T-1."""
+    return uniform_i32(seed, 2, 0, n_steps, 0, T - 1)

@@ -1,0 +1,386 @@
+"""Pins of the CPU oracle against things other than itself: brute force in
+exact rational arithmetic, closed forms, invariants and library routines.
+Each test names the step it pins (C1..C8, see oracle/__init__.py)."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synth
+from synth import recipes
+
+
+def _f16(bits):
+    return np.array(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+# ----------------------------------------------------------------- generator
+def test_generator_is_counter_based_and_deterministic():
+    a = synth.normal_f32(7, 3, 1, 1000)
+    b = synth.normal_f32(7, 3, 1, 1000)
+    assert np.array_equal(a, b)
+    # any slice regenerates on its own
+    c = synth.normal_f32(7, 3, 1, 100, start=450)
+    assert np.array_equal(a[450:550], c)
+    # row slices of a weight matrix regenerate the same fields
+    full = synth.q4k_fields(5, 9, 40, 512)
+    part = synth.q4k_fields(5, 9, 40, 512, 17, 29)
+    for k in ("d", "dmin", "sc", "m", "q"):
+        assert np.array_equal(full[k][17:29], part[k])
+    # different streams differ
+    assert not np.array_equal(a, synth.normal_f32(7, 3, 2, 1000))
+
+
+def test_generator_fp16_rounding_matches_numpy():
+    rng = np.random.default_rng(1)
+    v = rng.standard_normal(20000) * np.logspace(-9, 5, 20000)
+    # exact half-way cases between adjacent fp16 values, incl. subnormals
+    hw = (np.arange(1, 2000, dtype=np.float64) + 0.5) * 2.0 ** -24
+    hw2 = (1024 + np.arange(0, 1000) + 0.5) * 2.0 ** -10
+    allv = np.concatenate([v, -v, hw, hw2, [0.0, 65504.0, 65519.99, 65520.0, 1e9, 2.0 ** -25, 2.0 ** -24]])
+    got = np.array([synth.f64_to_f16_bits(x) for x in allv], np.uint16)
+    with np.errstate(over="ignore"):
+        ref = allv.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_generator_field_ranges_and_distribution():
+    W = synth.q4k_fields(0, 1, 256, 2048)
+    assert W["q"].max() == 15 and W["q"].min() == 0
+    assert W["sc"].max() == 63 and W["m"].max() == 63 and W["sc"].min() == 0
+    d = _f16(W["d"])
+    assert (d >= 0).all()
+    # E|N(0, 0.01)| = 0.01*sqrt(2/pi)
+    assert abs(d.mean() - 0.01 * np.sqrt(2 / np.pi)) < 3e-4
+    # some d are fp16 subnormal (< 2^-14): about 0.49% of |N(0, 0.01)|
+    frac_sub = np.mean(d < 2.0 ** -14)
+    assert 0.002 < frac_sub < 0.009
+    # codes uniform on 0..15
+    counts = np.bincount(W["q"].ravel(), minlength=16) / W["q"].size
+    assert np.abs(counts - 1 / 16).max() < 0.003
+    x = synth.normal_f32(0, 2, 0, 200000)
+    assert abs(x.mean()) < 0.01 and abs(x.std() - 1) < 0.01
+
+
+# ----------------------------------------------------------------- C1 fp16
+def test_f16_to_f32_all_bit_patterns(orc):
+    bits = np.arange(65536, dtype=np.uint32)
+    got = np.array([orc.f16_to_f32(b) for b in bits[::7]], np.float32)
+    ref = bits[::7].astype(np.uint16).view(np.float16).astype(np.float32)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+
+
+# ----------------------------------------------------------------- C2 quantizer
+def test_quantizer_closed_form_properties(orc):
+    x = synth.normal_f32(11, 1, 0, 7 * 4096).reshape(7, 4096)
+    x[3, 64:96] = 0.0  # one all-zero group
+    a8, s, gs = orc.quantize_rows(x)
+    assert np.abs(a8.astype(int)).max() <= 127
+    g = a8.reshape(7, -1, 32).astype(np.int64)
+    assert np.array_equal(g.sum(-1), gs)
+    nz = s > 0
+    assert np.all(np.abs(g).max(-1)[nz] == 127)  # every non-zero group attains +-127
+    assert np.all(g[~nz] == 0) and (~nz).sum() == 1
+    err = np.abs(x.reshape(7, -1, 32).astype(np.float64) - s[..., None].astype(np.float64) * g)
+    assert np.all(err <= s[..., None] / 2 * (1 + 2.0 ** -22))
+    # power-of-two scaling is exact
+    a8b, sb, _ = orc.quantize_rows(x * 4)
+    assert np.array_equal(a8, a8b) and np.array_equal(sb, s * 4)
+
+
+def test_quantizer_identity_and_round_half_even(orc):
+    rng = np.random.default_rng(3)
+    xi = rng.integers(-127, 128, size=(3, 256)).astype(np.float32)
+    xi.reshape(3, -1, 32)[:, :, 0] = 127.0  # every group contains 127 -> s = 1 exactly
+    a8, s, gs = orc.quantize_rows(xi)
+    assert np.all(s == 1.0) and np.array_equal(a8.astype(np.float32), xi)
+    # half-way values with s = 1 round to even
+    h = np.zeros((1, 32), np.float32)
+    h[0, 0] = 127
+    h[0, 1:9] = [0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5, 126.5]
+    a8, s, _ = orc.quantize_rows(h)
+    assert s[0, 0] == 1.0
+    assert list(a8[0, 1:9]) == [0, 2, 2, 0, -2, -2, 4, 126]
+
+
+# ----------------------------------------------------------------- C1 + C3 GEMV
+def _brute_gemv(W, a8, s):
+    """Exact rational y[t][o] = sum_k (d*sc*q - dmin*m) * s * a8 from the definition."""
+    N, K = W["q"].shape
+    T = a8.shape[0]
+    d = [[Fraction(float(v)) for v in row] for row in _f16(W["d"])]
+    dm = [[Fraction(float(v)) for v in row] for row in _f16(W["dmin"])]
+    out = np.zeros((T, N))
+    for t in range(T):
+        for o in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                b, j = k // 256, (k % 256) // 32
+                w = d[o][b] * int(W["sc"][o, b, j]) * int(W["q"][o, k]) - dm[o][b] * int(W["m"][o, b, j])
+                acc += w * Fraction(float(s[t, k // 32])) * int(a8[t, k])
+            out[t, o] = float(acc)
+    return out
+
+
+@pytest.mark.parametrize("N,K,T", [(3, 256, 1), (2, 512, 5), (4, 256, 12)])
+def test_gemv_vs_exact_rational_brute_force(orc, N, K, T):
+    W = synth.q4k_fields(21, N * 100 + T, N, K)
+    x = synth.normal_f32(21, 7, T, T * K).reshape(T, K)
+    a8, s, _ = orc.quantize_rows(x)
+    y = orc.qgemv(W, x)
+    ref = _brute_gemv(W, a8, s)
+    scale = np.abs(ref).max()
+    assert np.abs(y - ref).max() <= 1e-6 * scale
+    # integer partial sums are exact
+    P = orc.q4k_partials(W, a8)
+    for t in range(T):
+        for o in range(N):
+            for g in range(K // 32):
+                exp = sum(int(W["q"][o, g * 32 + i]) * int(a8[t, g * 32 + i]) for i in range(32))
+                assert P[t, o, g] == exp
+
+
+def _family(N, K, d_bits, dmin_bits, sc, m, seed):
+    rng = np.random.default_rng(seed)
+    nsb = K // 256
+    return {"d": np.full((N, nsb), d_bits, np.uint16), "dmin": np.full((N, nsb), dmin_bits, np.uint16),
+            "sc": np.broadcast_to(np.asarray(sc, np.uint8), (N, nsb, 8)).copy() if np.ndim(sc) < 3 else sc,
+            "m": np.broadcast_to(np.asarray(m, np.uint8), (N, nsb, 8)).copy() if np.ndim(m) < 3 else m,
+            "q": rng.integers(0, 16, size=(N, K)).astype(np.uint8)}
+
+
+def _int_rows(T, K, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-127, 128, size=(T, K)).astype(np.float32)
+    x.reshape(T, -1, 32)[:, :, 5] = -127.0  # |x| max 127 in every group -> s = 1
+    return x
+
+
+def test_gemv_exact_integer_families(orc):
+    N, K, T = 24, 1024, 3
+    x = _int_rows(T, K, 5)
+    one, zero = 0x3C00, 0x0000
+    # E1: d = 1, dmin = 0, sc = 1 -> y = sum q*x
+    W = _family(N, K, one, zero, 1, 0, 1)
+    assert np.array_equal(orc.qgemv(W, x), (x.astype(np.int64) @ W["q"].T.astype(np.int64)).astype(np.float32))
+    # E2: d = 0, dmin = 1, m = 1 -> y = -sum x
+    W = _family(N, K, zero, one, 0, 1, 2)
+    assert np.array_equal(orc.qgemv(W, x), np.repeat(-x.sum(1, keepdims=True), N, 1).astype(np.float32))
+    # E3: random sc, m per sub-block, d = dmin = 1 -> exact int64 combination
+    rng = np.random.default_rng(9)
+    sc = rng.integers(0, 64, size=(N, K // 256, 8)).astype(np.uint8)
+    m = rng.integers(0, 64, size=(N, K // 256, 8)).astype(np.uint8)
+    W = _family(N, K, one, one, sc, m, 3)
+    xi = x.astype(np.int64).reshape(T, K // 32, 32)
+    qi = W["q"].astype(np.int64).reshape(N, K // 32, 32)
+    P = np.einsum("tgi,ogi->tog", xi, qi)
+    scg, mg = sc.reshape(N, -1).astype(np.int64), m.reshape(N, -1).astype(np.int64)
+    exp = (P * scg[None]).sum(-1) - (xi.sum(-1)[:, None, :] * mg[None]).sum(-1)
+    assert np.abs(exp).max() < 2 ** 24
+    assert np.array_equal(orc.qgemv(W, x), exp.astype(np.float32))
+    # power-of-two scaling of d and dmin scales y exactly (0x4400 = 4.0)
+    W4 = dict(W, d=np.full_like(W["d"], 0x4400), dmin=np.full_like(W["dmin"], 0x4400))
+    assert np.array_equal(orc.qgemv(W4, x), 4 * exp.astype(np.float32))
+
+
+def test_gemv_rows_are_independent(orc):
+    W = synth.q4k_fields(4, 4, 64, 768)
+    x = synth.normal_f32(4, 5, 0, 6 * 768).reshape(6, 768)
+    y = orc.qgemv(W, x)
+    for t in range(6):
+        assert np.array_equal(y[t], orc.qgemv(W, x[t:t + 1])[0])
+
+
+# ----------------------------------------------------------------- C4 FFN
+def test_silu_closed_forms(orc):
+    z = np.linspace(-30, 30, 2001).astype(np.float32)
+    one = np.ones_like(z)
+    h = orc.silu_mul(z, one).astype(np.float64)
+    hn = orc.silu_mul(-z, one).astype(np.float64)
+    assert orc.silu_mul(np.zeros(3, np.float32), np.ones(3, np.float32)).tolist() == [0, 0, 0]
+    assert np.all(np.abs(h - hn - z) <= 4 * np.spacing(np.abs(z).astype(np.float32)) + 1e-30)
+    assert np.all(np.abs(h[z > 20] - z[z > 20]) <= 1e-6 * z[z > 20])
+    assert np.all(np.abs(h[z < -20]) < 1e-6)
+
+
+def test_ffn_is_its_composition(orc):
+    H, F, T = 512, 768, 3
+    Wg, Wu, Wd = (synth.q4k_fields(8, 1, F, H), synth.q4k_fields(8, 2, F, H), synth.q4k_fields(8, 3, H, F))
+    x = synth.normal_f32(8, 4, 0, T * H).reshape(T, H)
+    y, h = orc.ffn(Wg, Wu, Wd, x, return_h=True)
+    h2 = orc.silu_mul(orc.qgemv(Wg, x), orc.qgemv(Wu, x))
+    assert np.array_equal(h, h2)
+    assert np.array_equal(y, orc.qgemv(Wd, h2))
+
+
+def test_rmsnorm_closed_form(orc):
+    x = synth.normal_f32(9, 1, 0, 4 * 5120, 0.0, 3.0).reshape(4, 5120)
+    a = orc.rmsnorm(x).astype(np.float64)
+    ms = np.mean(x.astype(np.float64) ** 2, 1)
+    assert np.allclose(np.mean(a ** 2, 1), ms / (ms + 1e-6), rtol=1e-6)
+    # direction preserved
+    assert np.allclose(a / np.linalg.norm(a, axis=1, keepdims=True),
+                       x / np.linalg.norm(x.astype(np.float64), axis=1, keepdims=True), atol=1e-6)
+
+
+# ----------------------------------------------------------------- C6 lm_head + verify
+def test_lmhead_vs_numpy_and_planted_cases(orc):
+    V, H, T = 1500, 384, 5
+    W = synth.normal_f16(3, 50, 0, V * H, 0.0, 0.02).reshape(V, H)
+    hid = synth.normal_f32(3, 51, 0, T * H).reshape(T, H)
+    r = orc.lmhead(W, hid, return_logits=True)
+    ref = hid.astype(np.float64) @ _f16(W).T  # library matmul in float64
+    assert np.allclose(r["logits"], ref, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(r["top1"], np.argmax(ref, 1))
+    # planted maximum: row 977 points along hid[2]
+    W2 = W.copy()
+    W2[977] = np.sign(hid[2]).astype(np.float16).view(np.uint16)
+    assert orc.lmhead(W2, hid)["top1"][2] == 977
+    # planted exact tie: rows 311 and 1200 identical and maximal for row 0 -> lowest index
+    W3 = W.copy()
+    W3[311] = np.sign(hid[0]).astype(np.float16).view(np.uint16)
+    W3[1200] = W3[311]
+    r3 = orc.lmhead(W3, hid)
+    assert r3["top1"][0] == 311 and r3["top2"][0] == 1200 and r3["top1_val"][0] == r3["top2_val"][0]
+    # NaN never wins
+    W4 = W3.copy()
+    W4[5] = 0x7E00
+    assert orc.lmhead(W4, hid)["top1"][0] == 311
+
+
+def test_verify_exhaustive_match_patterns(orc):
+    for n in range(1, 7):
+        for pat in range(1 << (n - 1)):
+            argmax = np.arange(100, 100 + n, dtype=np.int32)
+            drafts = np.array([argmax[i] if (pat >> i) & 1 else 7 for i in range(n - 1)], np.int32)
+            n_acc, tok = orc.verify(argmax, [0, n], drafts)
+            lead = 0
+            while lead < n - 1 and (pat >> lead) & 1:
+                lead += 1
+            assert n_acc[0] == lead
+            assert list(tok[:lead + 1]) == list(drafts[:lead]) + [argmax[lead]]
+
+
+def test_verify_groups_and_drafter_statistics(orc):
+    # 4 groups of 3 rows (4 agents x [token + 2 drafts])
+    argmax = np.arange(12, dtype=np.int32) * 3
+    gs = [0, 3, 6, 9, 12]
+    drafts = np.array([0, 3, 9, 99, 18, 21, 27, 30], np.int32)  # g0: 2 ok; g1: 1; g2: 2; g3: 2
+    n_acc, tok = orc.verify(argmax, gs, drafts)
+    assert list(n_acc) == [2, 1, 2, 2]
+    assert list(tok[:3]) == [0, 3, 6] and list(tok[3:5]) == [9, 12]
+    # drafter of the lm_head workload: P(n_acc = k) = .7^k .3 (k < 4), .7^4 (k = 4); mean 1.7731
+    trials = 3000
+    counts = np.zeros(5)
+    for tr in range(trials):
+        am = synth.uniform_i32(3, 77, tr, 5, 0, 151935)
+        dr = recipes.drafts_from_argmax(am[:4], 151936, trial=tr)
+        counts[orc.verify(am, [0, 5], dr)[0][0]] += 1
+    p = np.array([0.3, 0.21, 0.147, 0.1029, 0.2401])
+    chi2 = ((counts - trials * p) ** 2 / (trials * p)).sum()
+    assert chi2 < 18.5  # 4 dof, p = 0.001
+    assert abs((counts * np.arange(5)).sum() / trials - 1.7731) < 0.08
+
+
+# ----------------------------------------------------------------- C7 Gated DeltaNet
+def _full_matrix_update(S, k, v, g, b):
+    k = k.astype(np.float64)
+    v = v.astype(np.float64)
+    A = np.eye(len(k)) - b * np.outer(k, k)
+    return g * (A @ S) + b * np.outer(k, v)
+
+
+@pytest.mark.parametrize("d", [2, 4, 8, 128])
+def test_gdn_rank1_vs_full_matrix(orc, d):
+    inp = synth.gdn_step_inputs(4, 900 + d, 6, 1, d, d)
+    S0 = synth.normal_f32(4, 901, d, d * d, 0.0, 0.01).reshape(d, d).astype(np.float64)
+    S = S0.copy()
+    o = orc.gdn_rows(S, inp["q"][:, 0], inp["k"][:, 0], inp["v"][:, 0], inp["g"][:, 0], inp["beta"][:, 0])
+    R = S0.copy()
+    for t in range(6):
+        R = _full_matrix_update(R, inp["k"][t, 0], inp["v"][t, 0], float(inp["g"][t, 0]), float(inp["beta"][t, 0]))
+        assert np.allclose(o[t], (R.T @ inp["q"][t, 0].astype(np.float64)).astype(np.float32), rtol=1e-5,
+                           atol=1e-7)
+    assert np.allclose(S, R, rtol=1e-12, atol=1e-14)
+
+
+def test_gdn_closed_forms(orc):
+    d = 16
+    rng = np.random.default_rng(2)
+    S0 = rng.standard_normal((d, d))
+    ks = rng.standard_normal((5, d)).astype(np.float32)
+    vs = rng.standard_normal((5, d)).astype(np.float32)
+    gs = np.array([0.9, 0.5, 0.75, 0.8, 0.95], np.float32)
+    # beta = 0: pure decay
+    S = S0.copy()
+    orc.gdn_rows(S, None, ks, vs, gs, np.zeros(5, np.float32))
+    assert np.allclose(S, np.prod(gs.astype(np.float64)) * S0, rtol=1e-12)
+    # g = beta = 1 with a unit key: retrieval S^T k = v after the update
+    k = ks[0] / np.linalg.norm(ks[0])
+    S = S0.copy()
+    orc.gdn_rows(S, None, k[None].astype(np.float32), vs[:1], np.ones(1, np.float32), np.ones(1, np.float32))
+    kk = k.astype(np.float32).astype(np.float64)
+    # k is fp32-rounded, so |k| = 1 only to ~1e-7
+    assert np.allclose(S.T @ kk, vs[0], atol=1e-6)
+    # the printed right-multiplied form does not retrieve v
+    S = S0.copy()
+    orc.gdn_rows(S, None, k[None].astype(np.float32), vs[:1], np.ones(1, np.float32), np.ones(1, np.float32),
+                 literal=True)
+    assert not np.allclose(S.T @ kk, vs[0], atol=1e-3)
+    # orthonormal keys, g = beta = 1: S = (I - sum k k^T) S0 + sum k v^T
+    Q, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    K4 = Q[:, :4].T.astype(np.float32)
+    S = S0.copy()
+    orc.gdn_rows(S, None, K4, vs[:4], np.ones(4, np.float32), np.ones(4, np.float32))
+    Kd = K4.astype(np.float64)
+    exp = (np.eye(d) - Kd.T @ Kd) @ S0 + Kd.T @ vs[:4].astype(np.float64)
+    assert np.allclose(S, exp, atol=1e-5)
+
+
+def test_gdn_step_commits_through_accepted_row(orc):
+    nh, d, T = 3, 32, 5
+    S0 = synth.normal_f32(4, 950, 0, nh * d * d, 0.0, 0.01).reshape(nh, d, d)
+    inp = synth.gdn_step_inputs(4, 951, T, nh, d, d)
+    for a in range(T):
+        S1, o = orc.gdn_step(S0, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], a)
+        for h in range(nh):
+            R = S0[h].astype(np.float64)
+            for t in range(a + 1):
+                R = _full_matrix_update(R, inp["k"][t, h], inp["v"][t, h], float(inp["g"][t, h]),
+                                        float(inp["beta"][t, h]))
+            assert np.allclose(S1[h], R.astype(np.float32), rtol=1e-6, atol=1e-9)
+        # outputs do not depend on the accept length
+        _, o0 = orc.gdn_step(S0, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], 0)
+        assert np.array_equal(o, o0)
+
+
+def test_gdn_chain_equivalence_and_contraction(orc):
+    nh, d, T = 2, 16, 4
+    S = synth.normal_f32(4, 960, 0, nh * d * d, 0.0, 0.01).reshape(nh, d, d)
+    S_one = S.copy()
+    for step in range(20):
+        inp = synth.gdn_step_inputs(4, 961 + step, T, nh, d, d)
+        S, o = orc.gdn_step(S, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], T - 1)
+        for t in range(T):
+            S_one, o1 = orc.gdn_step(S_one, inp["q"][t:t + 1], inp["k"][t:t + 1], inp["v"][t:t + 1],
+                                     inp["g"][t:t + 1], inp["beta"][t:t + 1], 0)
+            assert np.allclose(o1[0], o[t], rtol=1e-5, atol=1e-6)
+        assert np.allclose(S, S_one, rtol=1e-5, atol=1e-7)
+    # g < 1, beta in (0, 1), unit keys: the state stays bounded
+    assert np.abs(S).max() < 10.0
+
+
+# ----------------------------------------------------------------- byte accounting
+def test_stack_bytes_match_the_pages_arithmetic():
+    import json
+    import os
+    fig = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+    shapes = recipes.stack_shapes()
+    per_layer = sum(n * k // 256 * 144 for n, k in shapes.values())
+    assert per_layer == 209_387_520
+    assert per_layer * fig["layers_total"]["value"] == 13_400_801_280
+    # the page's own arithmetic: ~17 GB at 936 GB/s is about 18 ms
+    ms = fig["weights_per_step_gb"]["value"] / fig["rtx3090_bandwidth_gb_s"]["value"] * 1e3
+    assert abs(ms - fig["weight_read_ms"]["value"]) < 0.5
+    assert len(recipes.gdn_layers()) == fig["layers_gdn"]["value"]
