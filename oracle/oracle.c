@@ -261,14 +261,15 @@ void orc_lmhead(const uint16_t* W, int32_t V, int32_t H, const float* hid, int32
  * drafts[gs[g]-g .. gs[g+1]-g-2]; draft i of the group proposes the token of
  * row i+1, so it is accepted when it equals the argmax of row i.  n_acc[g] is
  * the number of leading accepted drafts; the group emits its n_acc accepted
- * drafts followed by the argmax of row n_acc (written at tokens[gs[g] + i]). */
+ * drafts followed by the argmax of row n_acc (written at tokens[gs[g] + i]).
+ * A row whose logits are all NaN has argmax -1, which no draft matches. */
 void orc_verify(const int32_t* argmax, const int32_t* gs, int32_t G, const int32_t* drafts, int32_t* n_acc,
                 int32_t* tokens) {
   for (int g = 0; g < G; ++g) {
     const int r = gs[g], n = gs[g + 1] - gs[g];
     const int32_t* dr = drafts + (r - g);
     int a = 0;
-    while (a < n - 1 && dr[a] == argmax[r + a]) ++a;
+    while (a < n - 1 && argmax[r + a] >= 0 && dr[a] == argmax[r + a]) ++a;
     n_acc[g] = a;
     for (int i = 0; i < a; ++i) tokens[r + i] = dr[i];
     tokens[r + a] = argmax[r + a];
