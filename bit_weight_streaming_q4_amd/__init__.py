@@ -1,0 +1,239 @@
+"""Python binding of libmk, the MI355X (gfx950) library of the multi-row
+speculative-verification decode step (C ABI in ``include/mk.h``).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libmk.so``.  Device buffers are torch tensors on the ROCm device; the
+current torch stream is passed to every call.  There is no CPU fallback: if
+``libmk.so`` is missing, importing the compute functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmk.so")
+
+MK_OK, MK_ERR_ARG, MK_ERR_SHAPE, MK_ERR_ALIGN, MK_ERR_RANGE = 0, -1, -2, -3, -4
+MK_ERR_WORKSPACE, MK_ERR_LAUNCH, MK_ERR_COOP, MK_ERR_DEVICE = -5, -6, -7, -8
+MK_PATH_AUTO, MK_PATH_DOT4, MK_PATH_MFMA = 0, 1, 2
+MK_T_MAX = 16
+
+
+class MkError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+class mk_q4k(ctypes.Structure):
+    _fields_ = [("blocks", ctypes.c_void_p), ("n_out", ctypes.c_int32), ("n_in", ctypes.c_int32)]
+
+
+class mk_deltanet(ctypes.Structure):
+    _fields_ = [("S", ctypes.c_void_p), ("ring", ctypes.c_void_p), ("n_acc", ctypes.c_void_p),
+                ("nh", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("T_max", ctypes.c_int32)]
+
+
+class mk_stack_desc(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("proj", ctypes.c_int32),
+                ("ffn", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("p_in", ctypes.POINTER(mk_q4k)), ("p_out", ctypes.POINTER(mk_q4k)),
+                ("gate", ctypes.POINTER(mk_q4k)), ("up", ctypes.POINTER(mk_q4k)),
+                ("down", ctypes.POINTER(mk_q4k)), ("lm_head", ctypes.c_void_p),
+                ("h_gdn_layer", ctypes.c_void_p), ("n_agents", ctypes.c_int32),
+                ("dn", ctypes.POINTER(mk_deltanet))]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmk.so (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with bit_weight_streaming_q4_amd/build.py")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.mk_status_string.argtypes = [ctypes.c_int]
+    L.mk_status_string.restype = ctypes.c_char_p
+    L.mk_last_error.restype = ctypes.c_char_p
+    L.mk_init.argtypes = [ctypes.c_int]
+    L.mk_q4k_bytes.argtypes = [i32, i32]
+    L.mk_q4k_bytes.restype = sz
+    L.mk_q4k_pack.argtypes = [P, P, P, P, P, i32, i32, i32, i32, P]
+    L.mk_q4k_unpack.argtypes = [P, i32, i32, P, P, P, P, P]
+    L.mk_quantize_rows.argtypes = [P, i32, i32, P, P, P, P]
+    L.mk_qgemv_rows_workspace.argtypes = [i32, i32, i32]
+    L.mk_qgemv_rows_workspace.restype = sz
+    L.mk_qgemv_rows.argtypes = [ctypes.POINTER(mk_q4k), P, i32, P, P, sz, P]
+    L.mk_qgemv_rows_ex.argtypes = [ctypes.POINTER(mk_q4k), P, i32, P, i32, P, sz, P]
+    L.mk_ffn_rows_workspace.argtypes = [i32, i32, i32]
+    L.mk_ffn_rows_workspace.restype = sz
+    L.mk_ffn_rows.argtypes = [ctypes.POINTER(mk_q4k)] * 3 + [P, i32, P, P, P, sz, P]
+    L.mk_lmhead_verify_workspace.argtypes = [i32, i32, i32]
+    L.mk_lmhead_verify_workspace.restype = sz
+    L.mk_lmhead_verify.argtypes = [P, i32, i32, P, i32, P, i32, P, P, P, P, P, sz, P]
+    L.mk_deltanet_step.argtypes = [ctypes.POINTER(mk_deltanet), i32, P, P, P, P, P, i32, P, P]
+    L.mk_deltanet_commit.argtypes = [ctypes.POINTER(mk_deltanet), P]
+    L.mk_stack_create.argtypes = [ctypes.POINTER(mk_stack_desc), ctypes.POINTER(ctypes.c_void_p)]
+    L.mk_stack_destroy.argtypes = [P]
+    L.mk_decode_step_workspace.argtypes = [P, i32]
+    L.mk_decode_step_workspace.restype = sz
+    L.mk_decode_step.argtypes = [P, P, i32, P, i32, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str):
+    if status != MK_OK:
+        msg = lib().mk_last_error().decode(errors="replace")
+        raise MkError(status, f"{what}: {msg or lib().mk_status_string(status).decode()}")
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _np_ptr(a):
+    return a.ctypes.data
+
+
+def mk_init(device: int = 0):
+    _check(lib().mk_init(device), "mk_init")
+
+
+# --------------------------------------------------------------------- weights
+def mk_q4k_bytes(n_out: int, n_in: int) -> int:
+    return int(lib().mk_q4k_bytes(n_out, n_in))
+
+
+def mk_q4k_pack(fields: dict, r0: int = 0, r1: int | None = None) -> np.ndarray:
+    """Host packing of field arrays (rows [r0, r1) of an n_out x n_in matrix;
+    the arrays hold exactly those rows) into the device layout."""
+    n_in = int(fields["n_in"])
+    n_out = int(fields.get("n_out_total", fields["n_out"]))
+    r1 = n_out if r1 is None else r1
+    rows_t = (r1 - r0 + 63) // 64
+    out = np.empty(rows_t * (n_in // 256) * 9216, np.uint8)
+    arrs = [np.ascontiguousarray(fields[k]) for k in ("d", "dmin", "sc", "m", "q")]
+    _check(lib().mk_q4k_pack(*[_np_ptr(a) for a in arrs], n_out, n_in, r0, r1, _np_ptr(out)), "mk_q4k_pack")
+    return out
+
+
+def mk_q4k_unpack(blocks: np.ndarray, n_out: int, n_in: int) -> dict:
+    nsb = n_in // 256
+    f = {"d": np.empty((n_out, nsb), np.uint16), "dmin": np.empty((n_out, nsb), np.uint16),
+         "sc": np.empty((n_out, nsb, 8), np.uint8), "m": np.empty((n_out, nsb, 8), np.uint8),
+         "q": np.empty((n_out, n_in), np.uint8)}
+    blocks = np.ascontiguousarray(blocks)
+    _check(lib().mk_q4k_unpack(_np_ptr(blocks), n_out, n_in, *[_np_ptr(f[k]) for k in ("d", "dmin", "sc", "m", "q")]),
+           "mk_q4k_unpack")
+    return f
+
+
+class Q4K:
+    """A packed Q4_K-style matrix resident in device memory."""
+
+    def __init__(self, blocks, n_out: int, n_in: int):
+        self.blocks = blocks  # torch uint8 tensor on the device
+        self.n_out, self.n_in = n_out, n_in
+        self.c = mk_q4k(blocks.data_ptr(), n_out, n_in)
+
+    @classmethod
+    def from_fields(cls, fields: dict, device="cuda"):
+        import torch
+        host = mk_q4k_pack(fields)
+        return cls(torch.from_numpy(host).to(device), int(fields["n_out"]), int(fields["n_in"]))
+
+    @classmethod
+    def empty(cls, n_out: int, n_in: int, device="cuda"):
+        import torch
+        return cls(torch.empty(mk_q4k_bytes(n_out, n_in), dtype=torch.uint8, device=device), n_out, n_in)
+
+
+def workspace(nbytes: int, device="cuda"):
+    import torch
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------------- compute
+def mk_quantize_rows(x, a8, s, gsum, stream=None):
+    T, K = x.shape
+    _check(lib().mk_quantize_rows(_ptr(x), T, K, _ptr(a8), _ptr(s), _ptr(gsum), _stream(stream)),
+           "mk_quantize_rows")
+
+
+def mk_qgemv_rows_workspace(T: int, n_out: int, n_in: int) -> int:
+    return int(lib().mk_qgemv_rows_workspace(T, n_out, n_in))
+
+
+def mk_qgemv_rows(W: Q4K, x, y, ws=None, path: int = MK_PATH_AUTO, stream=None):
+    T = x.shape[0]
+    if ws is None:
+        ws = workspace(mk_qgemv_rows_workspace(T, W.n_out, W.n_in), x.device)
+    _check(lib().mk_qgemv_rows_ex(ctypes.byref(W.c), _ptr(x), T, _ptr(y), path, _ptr(ws), ws.numel(),
+                                  _stream(stream)), "mk_qgemv_rows")
+
+
+def mk_ffn_rows_workspace(T: int, H: int, F: int) -> int:
+    return int(lib().mk_ffn_rows_workspace(T, H, F))
+
+
+def mk_ffn_rows(gate: Q4K, up: Q4K, down: Q4K, x, y, h_out=None, ws=None, stream=None):
+    T, H = x.shape
+    if ws is None:
+        ws = workspace(mk_ffn_rows_workspace(T, H, gate.n_out), x.device)
+    _check(lib().mk_ffn_rows(ctypes.byref(gate.c), ctypes.byref(up.c), ctypes.byref(down.c), _ptr(x), T, _ptr(y),
+                             _ptr(h_out), _ptr(ws), ws.numel(), _stream(stream)), "mk_ffn_rows")
+
+
+def mk_lmhead_verify_workspace(V: int, H: int, T: int) -> int:
+    return int(lib().mk_lmhead_verify_workspace(V, H, T))
+
+
+def mk_lmhead_verify(W16, hid, group_start, drafts, argmax, n_acc, tokens, ws=None, V=None, stream=None):
+    """W16: int16/uint16-bit fp16 tensor [V][H] (V may be a prefix of its rows)."""
+    H = W16.shape[1]
+    V = W16.shape[0] if V is None else V
+    T = hid.shape[0]
+    if group_start is None:
+        gs, G = None, 1
+    else:
+        gs_np = np.ascontiguousarray(group_start, np.int32)
+        gs, G = gs_np.ctypes.data, len(gs_np) - 1
+    if ws is None:
+        ws = workspace(mk_lmhead_verify_workspace(V, H, T), hid.device)
+    _check(lib().mk_lmhead_verify(_ptr(W16), V, H, _ptr(hid), T, gs, G, _ptr(drafts), _ptr(argmax), _ptr(n_acc),
+                                  _ptr(tokens), _ptr(ws), ws.numel(), _stream(stream)), "mk_lmhead_verify")
+
+
+class DeltaNetState:
+    """Device buffers of one Gated DeltaNet state: S [nh][128][128], ring, n_acc."""
+
+    def __init__(self, nh: int, T_max: int, device="cuda", S=None):
+        import torch
+        self.S = torch.zeros(nh, 128, 128, dtype=torch.float32, device=device) if S is None else S
+        self.ring = torch.zeros(nh, T_max - 1, 258, dtype=torch.float32, device=device)
+        self.n_acc = torch.zeros(1, dtype=torch.int32, device=device)
+        self.c = mk_deltanet(self.S.data_ptr(), self.ring.data_ptr(), self.n_acc.data_ptr(), nh, 128, 128, T_max)
+
+
+def mk_deltanet_step(st: DeltaNetState, q, k, v, g, beta, o, use_prev_acc: bool = True, stream=None):
+    T = q.shape[0]
+    _check(lib().mk_deltanet_step(ctypes.byref(st.c), int(use_prev_acc), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                  _ptr(beta), T, _ptr(o), _stream(stream)), "mk_deltanet_step")
+
+
+def mk_deltanet_commit(st: DeltaNetState, stream=None):
+    _check(lib().mk_deltanet_commit(ctypes.byref(st.c), _stream(stream)), "mk_deltanet_commit")

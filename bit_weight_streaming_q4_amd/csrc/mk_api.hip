@@ -1,0 +1,399 @@
+// mk_api.hip — the C ABI of libmk (declared in include/mk.h): host-side
+// argument validation, workspace carving, block packing, and the launches.
+// Every entry point validates before touching the GPU; on error it enqueues
+// nothing, returns a negative status and records a thread-local message.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "mk.h"
+#include "mk_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MK_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+std::mutex g_dev_mu;
+std::vector<int> g_cu;  // CU count per device (0 = not queried)
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if ((int)g_cu.size() <= dev) g_cu.resize(dev + 1, 0);
+  if (g_cu[dev] == 0) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return 256;
+    g_cu[dev] = p.multiProcessorCount;
+  }
+  return g_cu[dev];
+}
+
+hipStream_t S(void* s) { return (hipStream_t)s; }
+
+int launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MK_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int check_q4k(const mk_q4k* W, const char* name) {
+  if (!W || !W->blocks) return fail(MK_ERR_ARG, "%s: null weight", name);
+  if (W->n_out <= 0 || W->n_in <= 0) return fail(MK_ERR_SHAPE, "%s: empty matrix %d x %d", name, W->n_out, W->n_in);
+  if (W->n_in % 256) return fail(MK_ERR_SHAPE, "%s: n_in = %d is not a multiple of 256", name, W->n_in);
+  if (!aligned(W->blocks, 256)) return fail(MK_ERR_ALIGN, "%s: blocks not 256-B aligned", name);
+  return MK_OK;
+}
+
+int check_T(int T) {
+  if (T < 1 || T > MK_T_MAX) return fail(MK_ERR_RANGE, "T = %d outside 1..%d", T, MK_T_MAX);
+  return MK_OK;
+}
+
+int check_ptr(const void* p, const char* name, size_t align = 16) {
+  if (!p) return fail(MK_ERR_ARG, "%s is null", name);
+  if (!aligned(p, align)) return fail(MK_ERR_ALIGN, "%s not %zu-B aligned", name, align);
+  return MK_OK;
+}
+
+// Workspace of one quantized activation record (a8 + interleaved scales).
+size_t qact_bytes(int T, int K) { return align256((size_t)T * K) + align256((size_t)(K / 32) * mk::kTPadHost * 8); }
+
+mk::QActBuf carve_qact(uint8_t*& p, int T, int K) {
+  mk::QActBuf q;
+  q.a8 = (int8_t*)p;
+  p += align256((size_t)T * K);
+  q.ssg = (float2*)p;
+  p += align256((size_t)(K / 32) * mk::kTPadHost * 8);
+  q.K = K;
+  q.T = T;
+  return q;
+}
+
+int pick_path(int path, int T) {
+  if (path == MK_PATH_DOT4 || path == MK_PATH_MFMA) return path;
+  return T <= mk::kDot4MaxTAuto ? MK_PATH_DOT4 : MK_PATH_MFMA;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mk_status_string(int status) {
+  switch (status) {
+    case MK_OK: return "ok";
+    case MK_ERR_ARG: return "invalid argument";
+    case MK_ERR_SHAPE: return "unsupported shape";
+    case MK_ERR_ALIGN: return "misaligned pointer";
+    case MK_ERR_RANGE: return "value out of range";
+    case MK_ERR_WORKSPACE: return "workspace too small";
+    case MK_ERR_LAUNCH: return "HIP launch failed";
+    case MK_ERR_COOP: return "cooperative launch unavailable";
+    case MK_ERR_DEVICE: return "device error";
+    default: return "unknown status";
+  }
+}
+
+const char* mk_last_error(void) { return g_err; }
+
+int mk_version(void) { return 1; }
+
+int mk_init(int device) {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return fail(MK_ERR_DEVICE, "no HIP device");
+  if (device < 0 || device >= n) return fail(MK_ERR_RANGE, "device %d outside 0..%d", device, n - 1);
+  if (hipSetDevice(device) != hipSuccess) return fail(MK_ERR_DEVICE, "hipSetDevice(%d) failed", device);
+  device_cu_count();
+  return ok();
+}
+
+// ------------------------------------------------------------------ packing
+size_t mk_q4k_bytes(int32_t n_out, int32_t n_in) {
+  if (n_out <= 0 || n_in <= 0 || n_in % 256) return 0;
+  return (size_t)((n_out + 63) / 64) * (size_t)(n_in / 256) * mk::kUnitBytesHost;
+}
+
+int mk_q4k_pack(const uint16_t* h_d, const uint16_t* h_dmin, const uint8_t* h_sc, const uint8_t* h_m,
+                const uint8_t* h_q, int32_t n_out, int32_t n_in, int32_t r0, int32_t r1, void* h_blocks) {
+  if (!h_d || !h_dmin || !h_sc || !h_m || !h_q || !h_blocks) return fail(MK_ERR_ARG, "pack: null pointer");
+  if (n_out <= 0 || n_in <= 0 || n_in % 256) return fail(MK_ERR_SHAPE, "pack: bad shape %d x %d", n_out, n_in);
+  if (r0 < 0 || r1 > n_out || r0 >= r1 || r0 % 64 || (r1 % 64 && r1 != n_out))
+    return fail(MK_ERR_RANGE, "pack: row slice [%d, %d) must be tile aligned within %d", r0, r1, n_out);
+  const int nsb = n_in / 256;
+  const int rows = r1 - r0;
+  for (size_t i = 0; i < (size_t)rows * nsb * 8; ++i)
+    if (h_sc[i] > 63 || h_m[i] > 63) return fail(MK_ERR_RANGE, "pack: sc/m value above 63");
+  for (size_t i = 0; i < (size_t)rows * n_in; ++i)
+    if (h_q[i] > 15) return fail(MK_ERR_RANGE, "pack: code above 15");
+  uint8_t* out = (uint8_t*)h_blocks;
+  const int t0 = r0 / 64, t1 = (r1 + 63) / 64;
+  memset(out, 0, (size_t)(t1 - t0) * nsb * mk::kUnitBytesHost);
+  for (int r = r0; r < r1; ++r) {
+    const int tile = r / 64 - t0, rr = r % 64;
+    const size_t lr = (size_t)(r - r0);
+    for (int b = 0; b < nsb; ++b) {
+      uint8_t* u = out + ((size_t)tile * nsb + b) * mk::kUnitBytesHost;
+      uint8_t* h = u + rr * 16;
+      const uint16_t d = h_d[lr * nsb + b], dm = h_dmin[lr * nsb + b];
+      h[0] = d & 0xff;
+      h[1] = d >> 8;
+      h[2] = dm & 0xff;
+      h[3] = dm >> 8;
+      const uint8_t* sc = h_sc + (lr * nsb + b) * 8;
+      const uint8_t* m = h_m + (lr * nsb + b) * 8;
+      for (int j = 0; j < 8; ++j) h[4 + j] = (uint8_t)(sc[j] | ((m[j] >> 4) << 6));
+      for (int i = 0; i < 4; ++i) h[12 + i] = (uint8_t)((m[i] & 15) | ((m[i + 4] & 15) << 4));
+      const uint8_t* q = h_q + lr * n_in + (size_t)b * 256;
+      for (int j = 0; j < 8; ++j) {
+        uint8_t* c = u + 1024 + j * 1024 + rr * 16;
+        for (int w = 0; w < 4; ++w)
+          for (int i = 0; i < 4; ++i)
+            c[4 * w + i] = (uint8_t)(q[32 * j + 8 * w + i] | (q[32 * j + 8 * w + 4 + i] << 4));
+      }
+    }
+  }
+  return ok();
+}
+
+int mk_q4k_unpack(const void* h_blocks, int32_t n_out, int32_t n_in, uint16_t* h_d, uint16_t* h_dmin,
+                  uint8_t* h_sc, uint8_t* h_m, uint8_t* h_q) {
+  if (!h_blocks || !h_d || !h_dmin || !h_sc || !h_m || !h_q) return fail(MK_ERR_ARG, "unpack: null pointer");
+  if (n_out <= 0 || n_in <= 0 || n_in % 256) return fail(MK_ERR_SHAPE, "unpack: bad shape");
+  const int nsb = n_in / 256;
+  const uint8_t* in = (const uint8_t*)h_blocks;
+  for (int r = 0; r < n_out; ++r) {
+    const int tile = r / 64, rr = r % 64;
+    for (int b = 0; b < nsb; ++b) {
+      const uint8_t* u = in + ((size_t)tile * nsb + b) * mk::kUnitBytesHost;
+      const uint8_t* h = u + rr * 16;
+      h_d[(size_t)r * nsb + b] = (uint16_t)(h[0] | (h[1] << 8));
+      h_dmin[(size_t)r * nsb + b] = (uint16_t)(h[2] | (h[3] << 8));
+      uint8_t* sc = h_sc + ((size_t)r * nsb + b) * 8;
+      uint8_t* m = h_m + ((size_t)r * nsb + b) * 8;
+      for (int j = 0; j < 8; ++j) {
+        sc[j] = h[4 + j] & 63;
+        const int lo = j < 4 ? (h[12 + j] & 15) : (h[12 + j - 4] >> 4);
+        m[j] = (uint8_t)(lo | ((h[4 + j] >> 6) << 4));
+      }
+      uint8_t* q = h_q + (size_t)r * n_in + (size_t)b * 256;
+      for (int j = 0; j < 8; ++j) {
+        const uint8_t* c = u + 1024 + j * 1024 + rr * 16;
+        for (int w = 0; w < 4; ++w)
+          for (int i = 0; i < 4; ++i) {
+            q[32 * j + 8 * w + i] = c[4 * w + i] & 15;
+            q[32 * j + 8 * w + 4 + i] = c[4 * w + i] >> 4;
+          }
+      }
+    }
+  }
+  return ok();
+}
+
+// ------------------------------------------------------------------ quantizer
+int mk_quantize_rows(const float* x, int32_t T, int32_t K, int8_t* a8, float* s, int32_t* gsum, void* stream) {
+  int r;
+  if ((r = check_T(T))) return r;
+  if (K <= 0 || K % 32) return fail(MK_ERR_SHAPE, "quantize: K = %d not a positive multiple of 32", K);
+  if ((r = check_ptr(x, "x")) || (r = check_ptr(a8, "a8")) || (r = check_ptr(s, "s")) ||
+      (r = check_ptr(gsum, "gsum")))
+    return r;
+  return launch_status(mk::launch_quantize(x, T, K, a8, s, gsum, nullptr, S(stream)), "quantize");
+}
+
+// ------------------------------------------------------------------ GEMV
+size_t mk_qgemv_rows_workspace(int32_t T, int32_t n_out, int32_t n_in) {
+  if (T < 1 || T > MK_T_MAX || n_out <= 0 || n_in <= 0 || n_in % 256) return 0;
+  const mk::GemvPlan p = mk::plan_gemv(T, n_out, n_in, 1, device_cu_count());
+  return qact_bytes(T, n_in) + align256(p.partial_elems * 4);
+}
+
+int mk_qgemv_rows_ex(const mk_q4k* W, const float* x, int32_t T, float* y, int32_t path, void* ws,
+                     size_t ws_bytes, void* stream) {
+  int r;
+  if ((r = check_q4k(W, "W")) || (r = check_T(T)) || (r = check_ptr(x, "x")) || (r = check_ptr(y, "y")))
+    return r;
+  if (path < MK_PATH_AUTO || path > MK_PATH_MFMA) return fail(MK_ERR_ARG, "unknown path %d", path);
+  const int eng = pick_path(path, T);
+  if (eng == MK_PATH_DOT4 && T > mk::kDot4MaxT)
+    return fail(MK_ERR_RANGE, "dot4 path supports T <= %d (T = %d)", mk::kDot4MaxT, T);
+  const size_t need = mk_qgemv_rows_workspace(T, W->n_out, W->n_in);
+  if (!ws || ws_bytes < need) return fail(MK_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if ((r = check_ptr(ws, "workspace", 256))) return r;
+  const mk::GemvPlan p = mk::plan_gemv(T, W->n_out, W->n_in, 1, device_cu_count());
+  uint8_t* wp = (uint8_t*)ws;
+  const mk::QActBuf act = carve_qact(wp, T, W->n_in);
+  float* partial = (float*)wp;
+  hipError_t e = mk::launch_quantize(x, T, W->n_in, act.a8, nullptr, nullptr, act.ssg, S(stream));
+  if (e != hipSuccess) return launch_status(e, "quantize");
+  const uint8_t* wb[2] = {(const uint8_t*)W->blocks, nullptr};
+  e = mk::launch_gemv(wb, p, act, eng, partial, S(stream));
+  if (e != hipSuccess) return launch_status(e, "gemv");
+  return launch_status(mk::launch_reduce(partial, p, T, W->n_out, y, S(stream)), "reduce");
+}
+
+int mk_qgemv_rows(const mk_q4k* W, const float* x, int32_t T, float* y, void* ws, size_t ws_bytes, void* stream) {
+  return mk_qgemv_rows_ex(W, x, T, y, MK_PATH_AUTO, ws, ws_bytes, stream);
+}
+
+// ------------------------------------------------------------------ FFN
+size_t mk_ffn_rows_workspace(int32_t T, int32_t H, int32_t F) {
+  if (T < 1 || T > MK_T_MAX || H <= 0 || F <= 0 || H % 256 || F % 256) return 0;
+  const int cu = device_cu_count();
+  const mk::GemvPlan pg = mk::plan_gemv(T, F, H, 2, cu);
+  const mk::GemvPlan pd = mk::plan_gemv(T, H, F, 1, cu);
+  return qact_bytes(T, H) + align256(pg.partial_elems * 4) + align256((size_t)T * F * 4) + qact_bytes(T, F) +
+         align256(pd.partial_elems * 4);
+}
+
+int mk_ffn_rows(const mk_q4k* gate, const mk_q4k* up, const mk_q4k* down, const float* x, int32_t T, float* y,
+                float* h_out, void* ws, size_t ws_bytes, void* stream) {
+  int r;
+  if ((r = check_q4k(gate, "gate")) || (r = check_q4k(up, "up")) || (r = check_q4k(down, "down"))) return r;
+  if ((r = check_T(T)) || (r = check_ptr(x, "x")) || (r = check_ptr(y, "y"))) return r;
+  if (h_out && (r = check_ptr(h_out, "h_out"))) return r;
+  const int H = gate->n_in, F = gate->n_out;
+  if (up->n_in != H || up->n_out != F || down->n_in != F || down->n_out != H)
+    return fail(MK_ERR_SHAPE, "ffn: shapes gate %dx%d up %dx%d down %dx%d do not chain", gate->n_out, gate->n_in,
+                up->n_out, up->n_in, down->n_out, down->n_in);
+  if (F % 256) return fail(MK_ERR_SHAPE, "ffn: F = %d not a multiple of 256", F);
+  const size_t need = mk_ffn_rows_workspace(T, H, F);
+  if (!ws || ws_bytes < need) return fail(MK_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if ((r = check_ptr(ws, "workspace", 256))) return r;
+  const int cu = device_cu_count();
+  const mk::GemvPlan pg = mk::plan_gemv(T, F, H, 2, cu);
+  const mk::GemvPlan pd = mk::plan_gemv(T, H, F, 1, cu);
+  uint8_t* wp = (uint8_t*)ws;
+  const mk::QActBuf ax = carve_qact(wp, T, H);
+  float* part_gu = (float*)wp;
+  wp += align256(pg.partial_elems * 4);
+  float* h = (float*)wp;
+  wp += align256((size_t)T * F * 4);
+  if (h_out) h = h_out;
+  const mk::QActBuf ah = carve_qact(wp, T, F);
+  float* part_d = (float*)wp;
+  const int eng = pick_path(MK_PATH_AUTO, T);
+  hipStream_t st = S(stream);
+  hipError_t e = mk::launch_quantize(x, T, H, ax.a8, nullptr, nullptr, ax.ssg, st);
+  if (e != hipSuccess) return launch_status(e, "quantize x");
+  const uint8_t* wgu[2] = {(const uint8_t*)gate->blocks, (const uint8_t*)up->blocks};
+  if ((e = mk::launch_gemv(wgu, pg, ax, eng, part_gu, st)) != hipSuccess) return launch_status(e, "gate/up");
+  if ((e = mk::launch_reduce_silu(part_gu, pg, T, F, h, st)) != hipSuccess) return launch_status(e, "silu");
+  if ((e = mk::launch_quantize(h, T, F, ah.a8, nullptr, nullptr, ah.ssg, st)) != hipSuccess)
+    return launch_status(e, "quantize h");
+  const uint8_t* wd[2] = {(const uint8_t*)down->blocks, nullptr};
+  if ((e = mk::launch_gemv(wd, pd, ah, eng, part_d, st)) != hipSuccess) return launch_status(e, "down");
+  return launch_status(mk::launch_reduce(part_d, pd, T, H, y, st), "reduce down");
+}
+
+// ------------------------------------------------------------------ lm_head
+size_t mk_lmhead_verify_workspace(int32_t V, int32_t H, int32_t T) {
+  if (V <= 0 || H <= 0 || H % 64 || T < 1 || T > MK_T_MAX) return 0;
+  return mk::lm_workspace_bytes(V, H);
+}
+
+static int check_groups(const int32_t* gs, int G, int T, std::vector<int32_t>& out) {
+  if (!gs) {
+    if (G != 1) return fail(MK_ERR_ARG, "h_group_start is null but G = %d", G);
+    out = {0, T};
+    return MK_OK;
+  }
+  if (G < 1 || G > MK_LM_MAX_G || G > T) return fail(MK_ERR_RANGE, "G = %d outside 1..min(T, %d)", G, MK_LM_MAX_G);
+  if (gs[0] != 0 || gs[G] != T) return fail(MK_ERR_RANGE, "group starts must run from 0 to T");
+  for (int g = 0; g < G; ++g)
+    if (gs[g + 1] <= gs[g]) return fail(MK_ERR_RANGE, "group %d is empty", g);
+  out.assign(gs, gs + G + 1);
+  return MK_OK;
+}
+
+int mk_lmhead_verify(const uint16_t* W_f16, int32_t V, int32_t H, const float* hid, int32_t T,
+                     const int32_t* h_group_start, int32_t G, const int32_t* drafts, int32_t* argmax,
+                     int32_t* n_acc, int32_t* tokens, void* ws, size_t ws_bytes, void* stream) {
+  int r;
+  if ((r = check_T(T))) return r;
+  if (V <= 0 || H <= 0 || H % 64) return fail(MK_ERR_SHAPE, "lm_head: V = %d, H = %d (H % 64 == 0)", V, H);
+  if ((r = check_ptr(W_f16, "W")) || (r = check_ptr(hid, "hid")) || (r = check_ptr(argmax, "argmax", 4)) ||
+      (r = check_ptr(n_acc, "n_acc", 4)) || (r = check_ptr(tokens, "tokens", 4)))
+    return r;
+  std::vector<int32_t> gs;
+  if ((r = check_groups(h_group_start, G, T, gs))) return r;
+  if (T > G && (r = check_ptr(drafts, "drafts", 4))) return r;
+  const size_t need = mk_lmhead_verify_workspace(V, H, T);
+  if (!ws || ws_bytes < need) return fail(MK_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if ((r = check_ptr(ws, "workspace", 256))) return r;
+  return launch_status(mk::launch_lmhead(W_f16, V, H, hid, T, gs.data(), G, drafts, argmax, n_acc, tokens, ws,
+                                         S(stream)),
+                       "lm_head");
+}
+
+// ------------------------------------------------------------------ Gated DeltaNet
+static int check_dn(const mk_deltanet* st) {
+  int r;
+  if (!st) return fail(MK_ERR_ARG, "deltanet: null state");
+  if (st->dk != 128 || st->dv != 128) return fail(MK_ERR_SHAPE, "deltanet: dk = dv = 128 required");
+  if (st->nh <= 0) return fail(MK_ERR_SHAPE, "deltanet: nh = %d", st->nh);
+  if (st->T_max < 2 || st->T_max > MK_T_MAX) return fail(MK_ERR_RANGE, "deltanet: T_max = %d", st->T_max);
+  if ((r = check_ptr(st->S, "S")) || (r = check_ptr(st->ring, "ring")) || (r = check_ptr(st->n_acc, "n_acc", 4)))
+    return r;
+  return MK_OK;
+}
+
+int mk_deltanet_step(const mk_deltanet* st, int32_t use_prev_acc, const float* q, const float* k, const float* v,
+                     const float* g, const float* beta, int32_t T, float* o, void* stream) {
+  int r;
+  if ((r = check_dn(st))) return r;
+  if (T < 1 || T > st->T_max) return fail(MK_ERR_RANGE, "deltanet: T = %d outside 1..%d", T, st->T_max);
+  if ((r = check_ptr(q, "q")) || (r = check_ptr(k, "k")) || (r = check_ptr(v, "v")) || (r = check_ptr(g, "g", 4)) ||
+      (r = check_ptr(beta, "beta", 4)) || (r = check_ptr(o, "o")))
+    return r;
+  mk::GdnArgs a;
+  a.S = st->S;
+  a.ring = st->ring;
+  a.n_acc = use_prev_acc ? st->n_acc : nullptr;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.o = o;
+  a.nh = st->nh;
+  a.T = T;
+  a.T_max = st->T_max;
+  return launch_status(mk::launch_gdn_step(a, S(stream)), "deltanet step");
+}
+
+int mk_deltanet_commit(const mk_deltanet* st, void* stream) {
+  int r;
+  if ((r = check_dn(st))) return r;
+  mk::GdnArgs a = {};
+  a.S = st->S;
+  a.ring = st->ring;
+  a.n_acc = st->n_acc;
+  a.nh = st->nh;
+  a.T = 0;
+  a.T_max = st->T_max;
+  hipError_t e = mk::launch_gdn_commit(a, S(stream));
+  if (e != hipSuccess) return launch_status(e, "deltanet commit");
+  return launch_status(hipMemsetAsync(st->n_acc, 0, sizeof(int32_t), S(stream)), "deltanet commit reset");
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// mk_internal.h — host-side launchers shared between the C-ABI layer and the
+// kernel translation units of libmk.  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mk {
+
+constexpr int kTPadHost = 16;         // activation-scale rows padded to 16
+constexpr int kUnitBytesHost = 9216;  // 64 rows x 144 B per superblock
+constexpr int kDot4MaxT = 8;          // dot4 engine instances exist for T = 1..8
+constexpr int kDot4MaxTAuto = 7;      // automatic choice: dot4 below 8 rows, matrix cores from 8
+
+struct QActBuf {
+  int8_t* a8;    // [T][K]
+  float2* ssg;   // [K/32][16]
+  int32_t K, T;
+};
+
+// x [T][K] -> a8/s/gsum (API arrays, each may be null) and/or the internal
+// record (ssg may be null).  Zero-fills ssg rows T..15.
+hipError_t launch_quantize(const float* x, int T, int K, int8_t* a8, float* s, int32_t* gsum, float2* ssg,
+                           hipStream_t st);
+
+struct GemvPlan {
+  int ntiles, nsb, per_wg, ksplit, nmat;
+  size_t partial_elems;  // nmat * ksplit * T * ntiles*64
+};
+GemvPlan plan_gemv(int T, int n_out, int n_in, int nmat, int cu_count);
+
+// Writes partial[mat][ks][t][tile*64 + r] for both matrices of W (nmat 1 or 2).
+hipError_t launch_gemv(const uint8_t* const* W, const GemvPlan& p, const QActBuf& act, int path, float* partial,
+                       hipStream_t st);
+
+// y[t][o] = sum_ks partial[0][ks][t][o], o < n_out.
+hipError_t launch_reduce(const float* partial, const GemvPlan& p, int T, int n_out, float* y, hipStream_t st);
+// h[t][o] = SiLU(sum_ks partial[0]) * sum_ks partial[1].
+hipError_t launch_reduce_silu(const float* partial, const GemvPlan& p, int T, int n_out, float* h,
+                              hipStream_t st);
+
+}  // namespace mk
+
+#define MK_LM_MAX_G 16
+namespace mk {
+size_t lm_workspace_bytes(int V, int H);
+hipError_t launch_lmhead(const uint16_t* W, int V, int H, const float* hid, int T, const int32_t* gs, int G,
+                         const int32_t* drafts, int32_t* argmax, int32_t* n_acc, int32_t* tokens, void* ws,
+                         hipStream_t st);
+
+// Gated DeltaNet: one block per head (dk = dv = 128).
+struct GdnArgs {
+  float* S;          // [nh][128][128]
+  float* ring;       // [nh][T_max-1][258]
+  const int32_t* n_acc;  // device accept length of the previous step (may be null: 0)
+  const float *q, *k, *v, *g, *beta;  // [T][nh][..]
+  float* o;          // [T][nh][128]
+  int nh, T, T_max;
+};
+hipError_t launch_gdn_step(const GdnArgs& a, hipStream_t st);
+hipError_t launch_gdn_commit(const GdnArgs& a, hipStream_t st);
+}  // namespace mk

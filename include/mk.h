@@ -1,0 +1,216 @@
+/*
+ * mk.h — C ABI of the multi-row speculative-verification decode step for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (from the pages):
+ *   - richland.au, "Fusing the whole speculative-decoding cycle into one CUDA
+ *     kernel", section "What shipped": one pass runs the main model over
+ *     T = 1 + n_draft rows, then lm_head and verification on the device, and
+ *     the host reads back only the accepted tokens; the Gated DeltaNet state is
+ *     committed only through the surely-accepted token and drafts are replayed
+ *     from a small (k, v, g, beta) ring; the GEMV shares activations so that
+ *     T rows cost about the memory time of one.
+ *   - richland.au, "OpenJet's CUDA megakernel runs 4 coding agents on one RTX
+ *     3090", section "Why it matters": every step streams all weights once and
+ *     multiplies each loaded weight against all stacked rows (4 agents x
+ *     [token + 2 drafts] = 12 rows) while it is on chip.
+ *   - pulse-3k2, "UPDATE: ... KL divergence 0.0009 vs llama.cpp", section
+ *     "Decode accuracy": greedy output is exactly the main model's greedy choice.
+ * The block format (Q4_K-style: 256-weight superblocks with fp16 d and dmin,
+ * eight 32-weight sub-blocks with 6-bit scale sc and min m, 4-bit codes q,
+ * w = d*sc*q - dmin*m) and the per-32 int8 activation quantization follow the
+ * workload definition that accompanies those pages.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless the name starts with h_ (host).
+ *     Arrays are row-major and contiguous.  The caller owns every buffer; the
+ *     library never allocates or frees device memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     asynchronous on that stream unless stated otherwise.
+ *   - Arguments are validated on the host first.  On error the call returns a
+ *     negative MK_ERR_* code, enqueues nothing and records a message that
+ *     mk_last_error() returns (thread-local).  No call prints or aborts.
+ *   - Alignment: Q4K blobs 256 B, every other buffer 16 B (MK_ERR_ALIGN).
+ *   - Row counts T are 1..16 (MK_ERR_RANGE).  Reduction orders are fixed, so
+ *     a call is bit-reproducible for the same inputs and the same T.
+ *   - Concurrent calls on different streams need distinct workspaces.
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MK_OK = 0,
+  MK_ERR_ARG = -1,       /* NULL pointer or invalid enum value            */
+  MK_ERR_SHAPE = -2,     /* dimension not allowed (e.g. n_in % 256 != 0)  */
+  MK_ERR_ALIGN = -3,     /* misaligned pointer                            */
+  MK_ERR_RANGE = -4,     /* value outside its documented range            */
+  MK_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required       */
+  MK_ERR_LAUNCH = -6,    /* a HIP launch or copy failed                   */
+  MK_ERR_COOP = -7,      /* cooperative launch not possible on the device */
+  MK_ERR_DEVICE = -8     /* no usable device, or a device-side error word */
+};
+
+#define MK_T_MAX 16
+
+const char* mk_status_string(int status);
+const char* mk_last_error(void);
+int mk_version(void);
+
+/* Binds the calling thread's current device and queries its CU count and
+ * co-residency limits.  Idempotent.  Returns MK_ERR_DEVICE without a GPU. */
+int mk_init(int device);
+
+/* ------------------------------------------------------------------ weights */
+/* A Q4_K-style matrix of n_out x n_in weights in the library's device layout
+ * (see mk_q4k_pack).  n_in % 256 == 0.  `blocks` is 256-B aligned. */
+typedef struct {
+  const void* blocks;
+  int32_t n_out, n_in;
+} mk_q4k;
+
+/* Bytes of the packed layout: 144 B per 256 weights, rows padded to a
+ * multiple of 64 (padding rows are zero and never written to outputs). */
+size_t mk_q4k_bytes(int32_t n_out, int32_t n_in);
+
+/* Host-side conversion between field arrays and the packed layout.
+ * Fields (as produced by a generator or a model loader):
+ *   h_d, h_dmin [n_out][n_in/256]   fp16 bit patterns
+ *   h_sc, h_m   [n_out][n_in/256][8] values 0..63
+ *   h_q         [n_out][n_in]        values 0..15
+ * Packed layout: 64-row tiles; each (tile, superblock) unit is 9216 B = a
+ * 1024-B header block (row r: d, dmin, 12 B of scales) and eight 1024-B code
+ * blocks (sub-block j, row r: 16 B holding 32 codes).  Pack rows [r0, r1)
+ * only (r0 % 64 == 0) so large matrices can be packed in slices; h_blocks then
+ * points at the unit of tile r0/64.  Returns MK_ERR_RANGE for a field value
+ * outside its range. */
+int mk_q4k_pack(const uint16_t* h_d, const uint16_t* h_dmin, const uint8_t* h_sc, const uint8_t* h_m,
+                const uint8_t* h_q, int32_t n_out, int32_t n_in, int32_t r0, int32_t r1, void* h_blocks);
+int mk_q4k_unpack(const void* h_blocks, int32_t n_out, int32_t n_in, uint16_t* h_d, uint16_t* h_dmin,
+                  uint8_t* h_sc, uint8_t* h_m, uint8_t* h_q);
+
+/* ------------------------------------------------------ activation quantizer */
+/* Per row t and group of 32 consecutive elements: s = amax/127 (IEEE fp32
+ * division; 0 when the group is all zero), a8 = clamp(rne(x/s), -127, 127),
+ * gsum = sum of a8.  x [T][K], a8 [T][K], s and gsum [T][K/32]; K % 32 == 0.
+ * Bit-identical to the CPU definition. */
+int mk_quantize_rows(const float* x, int32_t T, int32_t K, int8_t* a8, float* s, int32_t* gsum, void* stream);
+
+/* ----------------------------------------------------------------- T-row GEMV */
+/* y[t][o] = sum_k w[o][k] * s[t][k/32] * a8[t][k] for the quantized rows of x:
+ * every weight block is read from HBM once and multiplied against all T rows.
+ * Integer sub-block sums (32 codes x 32 int8 values) are exact; they are
+ * combined with d, dmin, sc, m and the activation scales in fp32.
+ * x [T][n_in] fp32, y [T][n_out] fp32.  Workspace from mk_qgemv_rows_workspace. */
+size_t mk_qgemv_rows_workspace(int32_t T, int32_t n_out, int32_t n_in);
+int mk_qgemv_rows(const mk_q4k* W, const float* x, int32_t T, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Same, with the inner-product engine chosen explicitly:
+ * MK_PATH_AUTO (by T), MK_PATH_DOT4 (packed int8 dot products, T <= 8) or
+ * MK_PATH_MFMA (int8 matrix cores, rows padded to 16). */
+enum { MK_PATH_AUTO = 0, MK_PATH_DOT4 = 1, MK_PATH_MFMA = 2 };
+int mk_qgemv_rows_ex(const mk_q4k* W, const float* x, int32_t T, float* y, int32_t path, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ FFN block */
+/* y = W_down . q8(SiLU(W_gate . q8(x)) * (W_up . q8(x))); gate, up are
+ * F x H, down is H x F.  x, y [T][H] fp32; h_out (optional, NULL to skip)
+ * receives the fp32 intermediate [T][F]. */
+size_t mk_ffn_rows_workspace(int32_t T, int32_t H, int32_t F);
+int mk_ffn_rows(const mk_q4k* gate, const mk_q4k* up, const mk_q4k* down, const float* x, int32_t T, float* y,
+                float* h_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------- lm_head + verify */
+/* logits[t][v] = sum_h f32(W[v][h]) * hid[t][h] (fp16 weights widened exactly,
+ * fp32 hidden, fp32 accumulation); argmax[t] = lowest index of the maximum
+ * (NaN never wins; -1 if all logits of the row are NaN).  Rows are split into
+ * G groups by h_group_start[0..G] (host array, h_group_start[0] = 0,
+ * h_group_start[G] = T, every group non-empty; NULL = one group of T rows).
+ * Group g has n = rows and n-1 drafts at drafts[h_group_start[g] - g ...];
+ * draft i is accepted when it equals argmax of the group's row i.  n_acc[g] =
+ * number of leading accepted drafts; tokens[h_group_start[g] + i] for
+ * i = 0..n_acc[g] receives the accepted drafts then the argmax of row n_acc[g]
+ * (other slots are set to -1).  A draft id outside [0, V) is a mismatch.
+ * W [V][H] fp16 bits, hid [T][H], drafts [T-G] int32 (may be NULL if T == G),
+ * argmax [T], n_acc [G], tokens [T] (all device).  H % 64 == 0. */
+size_t mk_lmhead_verify_workspace(int32_t V, int32_t H, int32_t T);
+int mk_lmhead_verify(const uint16_t* W_f16, int32_t V, int32_t H, const float* hid, int32_t T,
+                     const int32_t* h_group_start, int32_t G, const int32_t* drafts, int32_t* argmax,
+                     int32_t* n_acc, int32_t* tokens, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------- Gated DeltaNet */
+/* State of nh independent heads (e.g. layers x heads) with rollback ring.
+ *   S    [nh][dk][dv] fp32, S[h][i][j] (i key index, j value index)
+ *   ring [nh][T_max-1][dk+dv+2] fp32: rows 1..T-1 of the last step as (k, v, g, beta)
+ *   n_acc  one int32 (device): accept length of the last step, read by the next
+ *          step to replay ring rows 1..n_acc; the decode step writes it.
+ * dk = dv = 128 (this build).  2 <= T_max <= 16. */
+typedef struct {
+  float* S;
+  float* ring;
+  int32_t* n_acc;
+  int32_t nh, dk, dv, T_max;
+} mk_deltanet;
+
+/* One step, per head: replay ring rows 1..a (a = *st->n_acc if use_prev_acc,
+ * else 0; a is clamped to 0..T_max-1), then for t = 0..T-1:
+ *   S <- g_t (I - beta_t k_t k_t^T) S + beta_t k_t v_t^T,   o_t = S^T q_t,
+ * committing S after row 0 and storing rows 1..T-1 in the ring.
+ * q, k [T][nh][dk]; v [T][nh][dv]; g, beta [T][nh]; o [T][nh][dv].  1 <= T <= T_max. */
+int mk_deltanet_step(const mk_deltanet* st, int32_t use_prev_acc, const float* q, const float* k, const float* v,
+                     const float* g, const float* beta, int32_t T, float* o, void* stream);
+
+/* Replays ring rows 1..a (a = *st->n_acc, clamped) into S without new rows, so
+ * that S holds the state through the accepted row; then sets *n_acc = 0. */
+int mk_deltanet_commit(const mk_deltanet* st, void* stream);
+
+/* --------------------------------------------------- persistent decode step */
+/* A synthetic layer stack: per layer a = RMSNorm(x); x += P_out.q8(P_in.q8(a));
+ * a = RMSNorm(x); x += W_down.q8(SiLU(W_gate.q8(a)) * W_up.q8(a)).  RMSNorm has
+ * unit gain and eps 1e-6; the norm scale is applied to the activation scales
+ * (equal in exact arithmetic to quantizing the normalised row).  Layers with
+ * gdn_layer[l] != 0 also run one Gated DeltaNet step per agent in their mixer
+ * slot on the caller's seeded inputs (its output is not fed back).  After the
+ * last layer: final RMSNorm, lm_head, argmax and verification per group. */
+typedef struct {
+  int32_t n_layers, hidden, proj, ffn, vocab;
+  const mk_q4k* p_in;  /* [n_layers], proj x hidden   */
+  const mk_q4k* p_out; /* [n_layers], hidden x proj   */
+  const mk_q4k* gate;  /* [n_layers], ffn x hidden    */
+  const mk_q4k* up;    /* [n_layers], ffn x hidden    */
+  const mk_q4k* down;  /* [n_layers], hidden x ffn    */
+  const uint16_t* lm_head; /* [vocab][hidden] fp16 bits */
+  const uint8_t* h_gdn_layer; /* host [n_layers] flags, NULL = none */
+  int32_t n_agents;           /* Gated DeltaNet states (one per verify group) */
+  const mk_deltanet* dn;      /* host array [n_agents]; nh = gdn layers * heads */
+} mk_stack_desc;
+
+typedef struct mk_stack mk_stack; /* opaque host-side descriptor */
+int mk_stack_create(const mk_stack_desc* desc, mk_stack** out);
+void mk_stack_destroy(mk_stack* st);
+size_t mk_decode_step_workspace(const mk_stack* st, int32_t T);
+
+/* One decode step in ONE persistent launch, then one D->H copy of the
+ * emitted tokens and accept lengths and one stream synchronisation.
+ *   x [T][hidden] (in: step input rows; out: final residual),
+ *   h_group_start as in mk_lmhead_verify (G groups == agents when GDN is on),
+ *   drafts [T-G] (device), gdn_* [T][nh][d] (device seeded inputs, NULL when
+ *   the stack has no GDN layers), gdn_o [T][nh][dv] (device, may be NULL),
+ *   h_tokens [T], h_n_acc [G] (host outputs), d_argmax [T] (device, optional),
+ *   trace (device, optional): [n_layers][T][hidden] residual after each layer.
+ * Returns MK_ERR_DEVICE if the device error word is set (grid-barrier watchdog). */
+int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_start, int32_t G,
+                   const int32_t* drafts, const float* gdn_q, const float* gdn_k, const float* gdn_v,
+                   const float* gdn_g, const float* gdn_beta, float* gdn_o, int32_t* h_tokens, int32_t* h_n_acc,
+                   int32_t* d_argmax, float* trace, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

@@ -1,0 +1,123 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every entry point
+that include/mk.h declares, packs/unpacks the block layout losslessly, and
+rejects bad arguments on the host before any GPU work (no compute calls)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_weight_streaming_q4_amd as mk
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "mk.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mk_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_entry_point():
+    L = mk.lib()
+    names = _declared()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_pack_unpack_round_trip_and_layout():
+    W = synth.q4k_fields(0, 77, 150, 768)  # ragged: 150 rows = 2 tiles + 22
+    blocks = mk.mk_q4k_pack(W)
+    assert blocks.nbytes == mk.mk_q4k_bytes(150, 768) == 3 * 3 * 9216
+    back = mk.mk_q4k_unpack(blocks, 150, 768)
+    for k in ("d", "dmin", "sc", "m", "q"):
+        assert np.array_equal(back[k], W[k]), k
+    # layout spot check: code k of row r sits in unit (r//64, k//256), sub-block
+    # j = (k%256)//32 at byte 16*(r%64) + 4*w + i (low nibble for the first four
+    # of each 8, high nibble for the next four)
+    r, k = 101, 3 * 256 - 256 + 77
+    b, j, e = k // 256, (k % 256) // 32, k % 32
+    w, i, hi = e // 8, e % 4, (e % 8) >= 4
+    unit = (r // 64) * 3 + b
+    byte = blocks[unit * 9216 + 1024 + j * 1024 + (r % 64) * 16 + 4 * w + i]
+    assert (byte >> 4 if hi else byte & 15) == W["q"][r, k]
+    # padding rows of the last tile are zero
+    last = blocks[2 * 3 * 9216:].reshape(3, 9216)
+    assert not last[:, 22 * 16:1024].any()
+
+
+def test_pack_in_row_slices_matches_whole():
+    W = synth.q4k_fields(0, 78, 192, 512)
+    whole = mk.mk_q4k_pack(W)
+    parts = []
+    for r0 in (0, 64, 128):
+        Wi = synth.q4k_fields(0, 78, 192, 512, r0, r0 + 64)
+        Wi["n_out_total"] = 192
+        parts.append(mk.mk_q4k_pack(Wi, r0, r0 + 64))
+    assert np.array_equal(np.concatenate(parts), whole)
+
+
+def test_pack_rejects_out_of_range_fields():
+    W = synth.q4k_fields(0, 79, 64, 256)
+    W["q"][3, 5] = 16
+    with pytest.raises(mk.MkError) as e:
+        mk.mk_q4k_pack(W)
+    assert e.value.status == mk.MK_ERR_RANGE
+
+
+def _q4k(ptr, n_out, n_in):
+    return mk.mk_q4k(ptr, n_out, n_in)
+
+
+def test_host_validation_before_any_gpu_work():
+    L = mk.lib()
+    fake = 1 << 20  # never dereferenced: validation fails first
+    x = ctypes.c_void_p(fake)
+    W = _q4k(fake, 64, 512)
+    # T outside 1..16
+    assert L.mk_qgemv_rows(ctypes.byref(W), x, 0, x, x, 1 << 30, None) == mk.MK_ERR_RANGE
+    assert L.mk_qgemv_rows(ctypes.byref(W), x, 17, x, x, 1 << 30, None) == mk.MK_ERR_RANGE
+    # n_in not a multiple of 256
+    Wb = _q4k(fake, 64, 500)
+    assert L.mk_qgemv_rows(ctypes.byref(Wb), x, 1, x, x, 1 << 30, None) == mk.MK_ERR_SHAPE
+    # misaligned blocks
+    Wm = _q4k(fake + 16, 64, 512)
+    assert L.mk_qgemv_rows(ctypes.byref(Wm), x, 1, x, x, 1 << 30, None) == mk.MK_ERR_ALIGN
+    # null input
+    assert L.mk_qgemv_rows(ctypes.byref(W), None, 1, x, x, 1 << 30, None) == mk.MK_ERR_ARG
+    # workspace too small
+    assert L.mk_qgemv_rows(ctypes.byref(W), x, 1, x, x, 16, None) == mk.MK_ERR_WORKSPACE
+    assert b"workspace" in L.mk_last_error()
+    # dot4 engine is limited to T <= 8
+    assert L.mk_qgemv_rows_ex(ctypes.byref(W), x, 9, x, mk.MK_PATH_DOT4, x, 1 << 30, None) == mk.MK_ERR_RANGE
+    assert L.mk_qgemv_rows_ex(ctypes.byref(W), x, 4, x, 7, x, 1 << 30, None) == mk.MK_ERR_ARG
+    # quantizer K % 32
+    assert L.mk_quantize_rows(x, 2, 48, x, x, x, None) == mk.MK_ERR_SHAPE
+    # FFN shapes must chain
+    G = _q4k(fake, 512, 256)
+    D = _q4k(fake, 256, 768)
+    assert L.mk_ffn_rows(ctypes.byref(G), ctypes.byref(G), ctypes.byref(D), x, 1, x, None, x, 1 << 30,
+                         None) == mk.MK_ERR_SHAPE
+    # lm_head: bad groups, bad H
+    gs = (ctypes.c_int32 * 3)(0, 3, 4)
+    assert L.mk_lmhead_verify(x, 100, 512, x, 5, gs, 2, x, x, x, x, x, 1 << 30, None) == mk.MK_ERR_RANGE
+    gs2 = (ctypes.c_int32 * 3)(0, 0, 5)
+    assert L.mk_lmhead_verify(x, 100, 512, x, 5, gs2, 2, x, x, x, x, x, 1 << 30, None) == mk.MK_ERR_RANGE
+    assert L.mk_lmhead_verify(x, 100, 500, x, 5, None, 1, x, x, x, x, x, 1 << 30, None) == mk.MK_ERR_SHAPE
+    # deltanet: head size and T range
+    dn = mk.mk_deltanet(fake, fake, fake, 4, 64, 128, 5)
+    assert L.mk_deltanet_step(ctypes.byref(dn), 0, x, x, x, x, x, 1, x, None) == mk.MK_ERR_SHAPE
+    dn = mk.mk_deltanet(fake, fake, fake, 4, 128, 128, 5)
+    assert L.mk_deltanet_step(ctypes.byref(dn), 0, x, x, x, x, x, 6, x, None) == mk.MK_ERR_RANGE
+    assert L.mk_status_string(mk.MK_ERR_WORKSPACE) == b"workspace too small"
+
+
+def test_workspace_queries_are_host_only():
+    assert mk.mk_qgemv_rows_workspace(5, 5120, 5120) > 5 * 5120
+    assert mk.mk_qgemv_rows_workspace(0, 5120, 5120) == 0
+    assert mk.mk_ffn_rows_workspace(5, 5120, 17408) > 0
+    assert mk.mk_lmhead_verify_workspace(151936, 5120, 5) > 151936 // 64 * 16 * 8
+    assert mk.mk_q4k_bytes(5120, 5120) == 14_745_600

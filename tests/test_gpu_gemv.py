@@ -1,0 +1,172 @@
+"""GPU parity of the activation quantizer, the T-row Q4_K-style GEMV (both
+engines) and the FFN block, against the CPU oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth import recipes
+from tests._util import FP32_TOL, need_gpu, norm_err, rel_err, say, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _mk():
+    import bit_weight_streaming_q4_amd as mk
+    return mk
+
+
+def test_quantize_bit_exact():
+    torch = need_gpu()
+    mk = _mk()
+    T, K = 16, 65536
+    x = synth.normal_f32(5, 1, 0, T * K).reshape(T, K)
+    x[0, :32] = 0.0  # all-zero group
+    # exact half-way cases: group max 127 gives s = 1, then n + 0.5 values
+    x[1, :32] = np.arange(32) - 15.5
+    x[1, 0] = 127.0
+    x[2, :32] = (np.arange(32) - 16) * 3.0 + 1.5
+    x[2, 31] = -127.0 * 3.0
+    x[3, :32] *= 1e-30  # tiny magnitudes (s subnormal-adjacent)
+    say("quantize", T, K)
+    xd = to_dev(x)
+    a8 = torch.empty(T, K, dtype=torch.int8, device="cuda")
+    s = torch.empty(T, K // 32, dtype=torch.float32, device="cuda")
+    gs = torch.empty(T, K // 32, dtype=torch.int32, device="cuda")
+    mk.mk_quantize_rows(xd, a8, s, gs)
+    ra8, rs, rgs = oracle.quantize_rows(x)
+    assert np.array_equal(to_np(a8), ra8)
+    assert np.array_equal(to_np(s).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(to_np(gs), rgs)
+
+
+def _gemv_gpu(mk, W, x, path, torch):
+    Wd = mk.Q4K.from_fields(W)
+    xd = to_dev(x)
+    y = torch.empty(x.shape[0], W["n_out"], dtype=torch.float32, device="cuda")
+    mk.mk_qgemv_rows(Wd, xd, y, path=path)
+    return to_np(y)
+
+
+@pytest.mark.parametrize("N,K", [(200, 768), (64, 256), (130, 2304)])
+def test_gemv_vs_oracle_shapes_and_paths(N, K):
+    torch = need_gpu()
+    mk = _mk()
+    W = synth.q4k_fields(7, N + K, N, K)
+    for T in (1, 2, 3, 5, 7, 8, 12, 16):
+        x = synth.normal_f32(7, 900 + T, 0, T * K).reshape(T, K)
+        ref = oracle.qgemv(W, x)
+        paths = [mk.MK_PATH_MFMA] + ([mk.MK_PATH_DOT4] if T <= 8 else [])
+        for path in paths:
+            say("gemv", N, K, T, path)
+            y = _gemv_gpu(mk, W, x, path, torch)
+            assert rel_err(y, ref) <= FP32_TOL, (T, path, rel_err(y, ref))
+            assert norm_err(y, ref) <= 1e-5
+
+
+def _int_rows(T, K, seed):
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-127, 128, size=(T, K)).astype(np.float32)
+    x.reshape(T, -1, 32)[:, :, 7] = 127.0  # max |x| = 127 in every group -> s = 1
+    return x
+
+
+def _family(N, K, d_bits, dmin_bits, sc, m, seed):
+    rng = np.random.default_rng(seed)
+    nsb = K // 256
+    return {"d": np.full((N, nsb), d_bits, np.uint16), "dmin": np.full((N, nsb), dmin_bits, np.uint16),
+            "sc": sc if np.ndim(sc) == 3 else np.full((N, nsb, 8), sc, np.uint8),
+            "m": m if np.ndim(m) == 3 else np.full((N, nsb, 8), m, np.uint8),
+            "q": rng.integers(0, 16, size=(N, K)).astype(np.uint8), "n_out": N, "n_in": K}
+
+
+def test_gemv_integer_families_are_exact():
+    """The integer sub-block sums are exact: with d, dmin, sc, m and the
+    activation scale chosen so every partial result is an integer below 2^24,
+    the fp32 outputs equal the exact integer results bit for bit."""
+    torch = need_gpu()
+    mk = _mk()
+    N, K = 192, 1024
+    one = 0x3C00
+    rng = np.random.default_rng(11)
+    sc = rng.integers(0, 64, size=(N, K // 256, 8)).astype(np.uint8)
+    m = rng.integers(0, 64, size=(N, K // 256, 8)).astype(np.uint8)
+    fams = {"E1": _family(N, K, one, 0, 1, 0, 1), "E2": _family(N, K, 0, one, 0, 1, 2),
+            "E3": _family(N, K, one, one, sc, m, 3)}
+    for T in (1, 5, 12):
+        x = _int_rows(T, K, 40 + T)
+        xi = x.astype(np.int64).reshape(T, K // 32, 32)
+        for name, W in fams.items():
+            qi = W["q"].astype(np.int64).reshape(N, K // 32, 32)
+            P = np.einsum("tgi,ogi->tog", xi, qi)
+            scg = W["sc"].reshape(N, -1).astype(np.int64)
+            mg = W["m"].reshape(N, -1).astype(np.int64)
+            dd = 1 if name != "E2" else 0
+            dm = 1 if name != "E1" else 0
+            exp = dd * (P * scg[None]).sum(-1) - dm * (xi.sum(-1)[:, None, :] * mg[None]).sum(-1)
+            # every partial sum the kernel can form is an integer below 2^24
+            bound = dd * (np.abs(P) * scg[None]).sum(-1) + dm * (np.abs(xi.sum(-1))[:, None, :] * mg[None]).sum(-1)
+            assert bound.max() < 2 ** 24
+            for path in [mk.MK_PATH_MFMA] + ([mk.MK_PATH_DOT4] if T <= 8 else []):
+                say("family", name, T, path)
+                y = _gemv_gpu(mk, W, x, path, torch)
+                assert np.array_equal(y, exp.astype(np.float32)), (name, T, path)
+
+
+def test_gemv_rows_paths_and_reruns_bit_identical():
+    torch = need_gpu()
+    mk = _mk()
+    N, K = 320, 1536
+    W = synth.q4k_fields(8, 1, N, K)
+    Wd = mk.Q4K.from_fields(W)
+    x = synth.normal_f32(8, 2, 0, 8 * K).reshape(8, K)
+    xd = to_dev(x)
+    outs = {}
+    for path in (mk.MK_PATH_DOT4, mk.MK_PATH_MFMA):
+        y = torch.empty(8, N, dtype=torch.float32, device="cuda")
+        mk.mk_qgemv_rows(Wd, xd, y, path=path)
+        outs[path] = to_np(y)
+        y2 = torch.empty_like(y)
+        mk.mk_qgemv_rows(Wd, xd, y2, path=path)
+        assert np.array_equal(to_np(y2), outs[path]), "rerun differs"
+        for t in range(8):
+            y1 = torch.empty(1, N, dtype=torch.float32, device="cuda")
+            mk.mk_qgemv_rows(Wd, xd[t:t + 1].contiguous(), y1, path=path)
+            assert np.array_equal(to_np(y1)[0], outs[path][t]), ("row", t, path)
+    say("paths agree bitwise")
+    assert np.array_equal(outs[mk.MK_PATH_DOT4], outs[mk.MK_PATH_MFMA])
+
+
+def test_gemv_full_size_single_row():
+    """5120 x 5120 weight, one fp32 row ~ N(0, 1), seed 0: every output."""
+    torch = need_gpu()
+    mk = _mk()
+    W = recipes.gemv_weight()
+    x = recipes.rows_f32(1, 5120)
+    ref = oracle.qgemv(W, x)
+    for path in (mk.MK_PATH_AUTO, mk.MK_PATH_MFMA):
+        say("gemv 5120x5120 T=1", path)
+        y = _gemv_gpu(mk, W, x, path, torch)
+        assert rel_err(y, ref) <= FP32_TOL
+        assert norm_err(y, ref) <= 1e-6
+
+
+def test_ffn_full_size_five_rows():
+    """gate/up 5120 -> 17408 and down 17408 -> 5120, T = 5 (token + 4 drafts).
+    The intermediate h is compared at tolerance; the down projection is checked
+    teacher-forced (oracle applied to the GPU's h) and end to end."""
+    torch = need_gpu()
+    mk = _mk()
+    Ws = recipes.ffn_weights()
+    x = recipes.rows_f32(5, 5120, seed=1, tensor=14)
+    say("ffn cfg1 T=5")
+    g, u, d = (mk.Q4K.from_fields(Ws[k]) for k in ("gate", "up", "down"))
+    xd = to_dev(x)
+    y = torch.empty(5, 5120, dtype=torch.float32, device="cuda")
+    h = torch.empty(5, 17408, dtype=torch.float32, device="cuda")
+    mk.mk_ffn_rows(g, u, d, xd, y, h_out=h)
+    yg, hg = to_np(y), to_np(h)
+    ref_y, ref_h = oracle.ffn(Ws["gate"], Ws["up"], Ws["down"], x, return_h=True)
+    assert rel_err(hg, ref_h) <= FP32_TOL
+    assert rel_err(yg, oracle.qgemv(Ws["down"], hg)) <= FP32_TOL
+    assert rel_err(yg, ref_y) <= FP32_TOL, rel_err(yg, ref_y)
