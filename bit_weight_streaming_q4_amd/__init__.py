@@ -124,6 +124,8 @@ def mk_q4k_pack(fields: dict, r0: int = 0, r1: int | None = None) -> np.ndarray:
     n_in = int(fields["n_in"])
     n_out = int(fields.get("n_out_total", fields["n_out"]))
     r1 = n_out if r1 is None else r1
+    if r0 % 64 or (r1 % 64 and r1 != n_out):
+        raise ValueError("row slices must be 64-row aligned")
     rows_t = (r1 - r0 + 63) // 64
     out = np.empty(rows_t * (n_in // 256) * 9216, np.uint8)
     arrs = [np.ascontiguousarray(fields[k]) for k in ("d", "dmin", "sc", "m", "q")]
@@ -219,13 +221,15 @@ def mk_lmhead_verify(W16, hid, group_start, drafts, argmax, n_acc, tokens, ws=No
 
 
 class DeltaNetState:
-    """Device buffers of one Gated DeltaNet state: S [nh][128][128], ring, n_acc."""
+    """Device buffers of one Gated DeltaNet state: S [nh][128][128], the
+    two-half ring [2][nh][T_max-1][258] and n_acc = [accept length, ring half]."""
 
     def __init__(self, nh: int, T_max: int, device="cuda", S=None):
         import torch
         self.S = torch.zeros(nh, 128, 128, dtype=torch.float32, device=device) if S is None else S
-        self.ring = torch.zeros(nh, T_max - 1, 258, dtype=torch.float32, device=device)
-        self.n_acc = torch.zeros(1, dtype=torch.int32, device=device)
+        self.ring = torch.zeros(2, nh, T_max - 1, 258, dtype=torch.float32, device=device)
+        self.n_acc = torch.zeros(2, dtype=torch.int32, device=device)
+        self.nh, self.T_max = nh, T_max
         self.c = mk_deltanet(self.S.data_ptr(), self.ring.data_ptr(), self.n_acc.data_ptr(), nh, 128, 128, T_max)
 
 
@@ -237,3 +241,97 @@ def mk_deltanet_step(st: DeltaNetState, q, k, v, g, beta, o, use_prev_acc: bool 
 
 def mk_deltanet_commit(st: DeltaNetState, stream=None):
     _check(lib().mk_deltanet_commit(ctypes.byref(st.c), _stream(stream)), "mk_deltanet_commit")
+
+
+# --------------------------------------------------------------------- decode step
+class Stack:
+    """A synthetic layer stack for mk_decode_step: per layer p_in, p_out, gate,
+    up, down (Q4K), an fp16 lm_head [vocab][hidden], the layers that carry a
+    Gated DeltaNet mixer, and one DeltaNetState per agent (verify group)."""
+
+    def __init__(self, layers, lm_head, gdn_layers=None, agents=None):
+        import torch
+        self.layers = layers
+        L = len(layers)
+        self.hidden, self.proj = layers[0]["p_in"].n_in, layers[0]["p_in"].n_out
+        self.ffn = layers[0]["gate"].n_out
+        self.lm_head = lm_head
+        self.vocab = lm_head.shape[0]
+        self.agents = agents or []
+        arr = {k: (mk_q4k * L)(*[layers[l][k].c for l in range(L)]) for k in ("p_in", "p_out", "gate", "up", "down")}
+        self._arr = arr
+        flags = np.zeros(L, np.uint8)
+        if gdn_layers is not None:
+            for l in gdn_layers:
+                flags[l] = 1
+        self._flags = flags
+        self._dn = (mk_deltanet * max(1, len(self.agents)))(*[a.c for a in self.agents])
+        desc = mk_stack_desc(L, self.hidden, self.proj, self.ffn, self.vocab, arr["p_in"], arr["p_out"],
+                             arr["gate"], arr["up"], arr["down"], lm_head.data_ptr(),
+                             flags.ctypes.data if gdn_layers is not None else None, len(self.agents), self._dn)
+        self._desc = desc
+        h = ctypes.c_void_p()
+        _check(lib().mk_stack_create(ctypes.byref(desc), ctypes.byref(h)), "mk_stack_create")
+        self.h = h
+        self._ws = {}
+
+    def __del__(self):
+        try:
+            if getattr(self, "h", None):
+                lib().mk_stack_destroy(self.h)
+                self.h = None
+        except Exception:
+            pass
+
+    def workspace_bytes(self, T: int) -> int:
+        return int(lib().mk_decode_step_workspace(self.h, T))
+
+    def workspace(self, T: int, device="cuda"):
+        if T not in self._ws:
+            self._ws[T] = workspace(self.workspace_bytes(T), device)
+        return self._ws[T]
+
+
+def mk_decode_step(st: Stack, x, group_start=None, drafts=None, gdn=None, gdn_o=None, argmax=None, trace=None,
+                   ws=None, stream=None):
+    """One decode step in one persistent launch.  x [T][hidden] (in/out).
+    gdn: dict of q, k, v, g, beta device tensors [T][nh][..] (None without GDN
+    layers).  Returns (tokens [T] int32 host, n_acc [G] int32 host)."""
+    T = x.shape[0]
+    if group_start is None:
+        gs, G = None, 1
+        gsa = None
+    else:
+        gsa = np.ascontiguousarray(group_start, np.int32)
+        gs, G = gsa.ctypes.data, len(gsa) - 1
+    tokens = np.full(T, -1, np.int32)
+    n_acc = np.zeros(G, np.int32)
+    if ws is None:
+        ws = st.workspace(T, x.device)
+    g = gdn or {}
+    _check(lib().mk_decode_step(st.h, _ptr(x), T, gs, G, _ptr(drafts), _ptr(g.get("q")), _ptr(g.get("k")),
+                                _ptr(g.get("v")), _ptr(g.get("g")), _ptr(g.get("beta")), _ptr(gdn_o),
+                                tokens.ctypes.data, n_acc.ctypes.data, _ptr(argmax), _ptr(trace), _ptr(ws),
+                                ws.numel(), _stream(stream)), "mk_decode_step")
+    return tokens, n_acc
+
+
+def pack_to_device(fields: dict, device="cuda", slice_rows: int = 4096) -> Q4K:
+    """Packs a field-array matrix on the host in row slices (in parallel) and
+    uploads it."""
+    import concurrent.futures as cf
+    import torch
+    n_out, n_in = int(fields["n_out"]), int(fields["n_in"])
+    blocks = np.empty(mk_q4k_bytes(n_out, n_in), np.uint8)
+    unit_rows = (n_in // 256) * 9216 // 64  # bytes per row-of-a-tile slice
+
+    def one(r0):
+        r1 = min(n_out, r0 + slice_rows)
+        sl = {k: fields[k][r0:r1] for k in ("d", "dmin", "sc", "m", "q")}
+        sl.update(n_out=r1 - r0, n_in=n_in, n_out_total=n_out)
+        out = mk_q4k_pack(sl, r0, r1)
+        blocks[r0 * unit_rows: r0 * unit_rows + out.size] = out
+
+    with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4)) as ex:
+        list(ex.map(one, range(0, n_out, slice_rows)))
+    return Q4K(torch.from_numpy(blocks).to(device), n_out, n_in)

@@ -25,6 +25,18 @@ int fail(int status, const char* fmt, ...) {
   return status;
 }
 
+}  // namespace
+
+int mk::set_error(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+namespace {
+
 int ok() {
   g_err[0] = '\0';
   return MK_OK;
@@ -368,7 +380,8 @@ int mk_deltanet_step(const mk_deltanet* st, int32_t use_prev_acc, const float* q
   mk::GdnArgs a;
   a.S = st->S;
   a.ring = st->ring;
-  a.n_acc = use_prev_acc ? st->n_acc : nullptr;
+  a.n_acc = st->n_acc;
+  a.use_prev = use_prev_acc ? 1 : 0;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -391,9 +404,7 @@ int mk_deltanet_commit(const mk_deltanet* st, void* stream) {
   a.nh = st->nh;
   a.T = 0;
   a.T_max = st->T_max;
-  hipError_t e = mk::launch_gdn_commit(a, S(stream));
-  if (e != hipSuccess) return launch_status(e, "deltanet commit");
-  return launch_status(hipMemsetAsync(st->n_acc, 0, sizeof(int32_t), S(stream)), "deltanet commit reset");
+  return launch_status(mk::launch_gdn_commit(a, S(stream)), "deltanet commit");
 }
 
 }  // extern "C"

@@ -43,6 +43,17 @@ __device__ __forceinline__ const T __attribute__((address_space(4)))* as_const(c
   return (const T __attribute__((address_space(4)))*)(uintptr_t)p;
 }
 
+// Wave-uniform copies (the value is the same in every lane; this tells the
+// compiler so, which keeps it in scalar registers).
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <typename T>
+__device__ __forceinline__ T* uniform(T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }

@@ -6,6 +6,9 @@
 
 namespace mk {
 
+// Records a thread-local error message for mk_last_error() and returns status.
+int set_error(int status, const char* fmt, ...);
+
 constexpr int kTPadHost = 16;         // activation-scale rows padded to 16
 constexpr int kUnitBytesHost = 9216;  // 64 rows x 144 B per superblock
 constexpr int kDot4MaxT = 8;          // dot4 engine instances exist for T = 1..8
@@ -47,13 +50,14 @@ hipError_t launch_lmhead(const uint16_t* W, int V, int H, const float* hid, int 
                          const int32_t* drafts, int32_t* argmax, int32_t* n_acc, int32_t* tokens, void* ws,
                          hipStream_t st);
 
-// Gated DeltaNet: one block per head (dk = dv = 128).
+// Gated DeltaNet: one wave per half head (dk = dv = 128).
 struct GdnArgs {
-  float* S;          // [nh][128][128]
-  float* ring;       // [nh][T_max-1][258]
-  const int32_t* n_acc;  // device accept length of the previous step (may be null: 0)
+  float* S;              // [nh][128][128]
+  float* ring;           // [2][nh][T_max-1][258]
+  int32_t* n_acc;        // device [2]: accept length of the previous step, ring half
+  int use_prev;          // replay n_acc[0] rows (else none)
   const float *q, *k, *v, *g, *beta;  // [T][nh][..]
-  float* o;          // [T][nh][128]
+  float* o;              // [T][nh][128]
   int nh, T, T_max;
 };
 hipError_t launch_gdn_step(const GdnArgs& a, hipStream_t st);

@@ -146,10 +146,14 @@ int mk_lmhead_verify(const uint16_t* W_f16, int32_t V, int32_t H, const float* h
 
 /* ------------------------------------------------------- Gated DeltaNet */
 /* State of nh independent heads (e.g. layers x heads) with rollback ring.
- *   S    [nh][dk][dv] fp32, S[h][i][j] (i key index, j value index)
- *   ring [nh][T_max-1][dk+dv+2] fp32: rows 1..T-1 of the last step as (k, v, g, beta)
- *   n_acc  one int32 (device): accept length of the last step, read by the next
- *          step to replay ring rows 1..n_acc; the decode step writes it.
+ *   S     [nh][dk][dv] fp32, S[h][i][j] (i key index, j value index)
+ *   ring  [2][nh][T_max-1][dk+dv+2] fp32: two halves used on alternate steps;
+ *         a step stores its rows 1..T-1 as (k, v, g, beta) in one half while
+ *         it replays the previous step's rows from the other half
+ *   n_acc 2 int32 (device): [0] accept length of the last step, read by the
+ *         next step to replay ring rows 1..n_acc[0] (the decode step writes
+ *         it from its verification); [1] the half holding the last step's rows.
+ *         Zero-initialise both before the first step.
  * dk = dv = 128 (this build).  2 <= T_max <= 16. */
 typedef struct {
   float* S;
@@ -158,7 +162,7 @@ typedef struct {
   int32_t nh, dk, dv, T_max;
 } mk_deltanet;
 
-/* One step, per head: replay ring rows 1..a (a = *st->n_acc if use_prev_acc,
+/* One step, per head: replay ring rows 1..a (a = n_acc[0] if use_prev_acc,
  * else 0; a is clamped to 0..T_max-1), then for t = 0..T-1:
  *   S <- g_t (I - beta_t k_t k_t^T) S + beta_t k_t v_t^T,   o_t = S^T q_t,
  * committing S after row 0 and storing rows 1..T-1 in the ring.
@@ -166,8 +170,8 @@ typedef struct {
 int mk_deltanet_step(const mk_deltanet* st, int32_t use_prev_acc, const float* q, const float* k, const float* v,
                      const float* g, const float* beta, int32_t T, float* o, void* stream);
 
-/* Replays ring rows 1..a (a = *st->n_acc, clamped) into S without new rows, so
- * that S holds the state through the accepted row; then sets *n_acc = 0. */
+/* Replays ring rows 1..a (a = n_acc[0], clamped) into S without new rows, so
+ * that S holds the state through the accepted row; then sets n_acc[0] = 0. */
 int mk_deltanet_commit(const mk_deltanet* st, void* stream);
 
 /* --------------------------------------------------- persistent decode step */

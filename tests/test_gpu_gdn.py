@@ -29,7 +29,7 @@ def _run_steps(mk, torch, S0, steps, T, accepts, nh):
         q, k, v, g, b = _inputs_dev(inp)
         o = torch.empty(T, nh, 128, dtype=torch.float32, device="cuda")
         mk.mk_deltanet_step(st, q, k, v, g, b, o, use_prev_acc=s > 0)
-        st.n_acc.fill_(int(accepts[s]))
+        st.n_acc[0] = int(accepts[s])
         outs.append(to_np(o))
     mk.mk_deltanet_commit(st)
     return to_np(st.S), outs
@@ -91,7 +91,7 @@ def test_gdn_full_size_steps():
         o = torch.empty(T, nh, 128, dtype=torch.float32, device="cuda")
         say("gdn full step", s)
         mk.mk_deltanet_step(st, q, k, v, g, b, o, use_prev_acc=s > 0)
-        st.n_acc.fill_(int(accepts[s]))
+        st.n_acc[0] = int(accepts[s])
         S, oref = oracle.gdn_step(S, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], int(accepts[s]))
         assert rel_err(to_np(o), oref) <= FP32_TOL
     mk.mk_deltanet_commit(st)

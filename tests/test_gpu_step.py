@@ -1,0 +1,111 @@
+"""GPU parity of the persistent decode step (mk_decode_step): every layer is
+checked teacher-forced against the oracle (the oracle's layer applied to the
+GPU's residual entering it), then the final RMSNorm + lm_head argmax, the
+verification, and the Gated DeltaNet outputs and committed state across steps
+(with the accept lengths the step itself produced)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests._util import FP32_TOL, need_gpu, rel_err, say, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _mk():
+    import bit_weight_streaming_q4_amd as mk
+    return mk
+
+
+MATS = ("p_in", "p_out", "gate", "up", "down")
+
+
+def small_stack(mk, seed, L, H, P, F, V, n_agents, T_max=5, gdn=True):
+    shapes = {"p_in": (P, H), "p_out": (H, P), "gate": (F, H), "up": (F, H), "down": (H, F)}
+    fields = [{m: synth.q4k_fields(seed, 100 + 8 * l + i, *shapes[m]) for i, m in enumerate(MATS)}
+              for l in range(L)]
+    layers = [{m: mk.Q4K.from_fields(fields[l][m]) for m in MATS} for l in range(L)]
+    W16 = synth.normal_f16(seed, 30000, 0, V * H, 0.0, 0.02).reshape(V, H)
+    lm = to_dev(W16)
+    gl = [l for l in range(L) if l % 4 != 3] if gdn else []
+    nh = len(gl) * 32
+    S0 = [synth.normal_f32(seed, 40000 + a, 0, nh * 128 * 128, 0.0, 0.01).reshape(nh, 128, 128)
+          for a in range(n_agents)] if gdn else []
+    agents = [mk.DeltaNetState(nh, T_max, S=to_dev(S0[a].copy())) for a in range(n_agents)] if gdn else []
+    st = mk.Stack(layers, lm, gdn_layers=gl if gdn else None, agents=agents)
+    dry = mk.Stack(layers, lm)  # same weights, no mixer: used to preview the argmax for drafts
+    return st, dry, fields, W16, S0, nh
+
+
+def _check_layers(fields, x_in, trace):
+    L = len(fields)
+    prev = x_in
+    worst = 0.0
+    for l in range(L):
+        ref = oracle.layer(prev, fields[l])
+        e = rel_err(trace[l], ref)
+        worst = max(worst, e)
+        assert e <= FP32_TOL, (l, e)
+        prev = trace[l]
+    return worst
+
+
+def _check_head(W16, x_final, am, na, tok, gs, drafts):
+    hid = oracle.rmsnorm(x_final)
+    r = oracle.lmhead(W16, hid)
+    tau = oracle.near_tie_tau(W16.shape[1], r["abs1"], r["abs2"])
+    near = (r["top1_val"] - r["top2_val"]) <= tau
+    for t in range(len(am)):
+        assert am[t] == r["top1"][t] or (near[t] and am[t] == r["top2"][t]), (t, am[t], r["top1"][t])
+    n_ref, t_ref = oracle.verify(am, gs, drafts)
+    assert np.array_equal(na, n_ref) and np.array_equal(tok, t_ref)
+    return r["top1"]
+
+
+@pytest.mark.parametrize("T,gs", [(1, [0, 1]), (5, [0, 5]), (12, [0, 3, 6, 9, 12])])
+def test_decode_step_small_stack(T, gs):
+    torch = need_gpu()
+    mk = _mk()
+    L, H, P, F, V = 4, 512, 1024, 768, 1000
+    G = len(gs) - 1
+    st, dry, fields, W16, S0, nh = small_stack(mk, 21, L, H, P, F, V, G)
+    S_ref = [s.copy() for s in S0]
+    for step in range(3):
+        x = synth.normal_f32(21, 10000 + step, 0, T * H).reshape(T, H)
+        # preview the argmax (the layer path does not depend on the mixer), then
+        # draft so that some groups accept some drafts
+        xd = to_dev(x)
+        am_prev = torch.empty(T, dtype=torch.int32, device="cuda")
+        drafts0 = np.zeros(max(T - G, 1), np.int32)
+        mk.mk_decode_step(dry, xd, gs, to_dev(drafts0), argmax=am_prev)
+        amp = to_np(am_prev)
+        drafts = []
+        for g in range(G):
+            n = gs[g + 1] - gs[g]
+            for i in range(n - 1):
+                drafts.append(int(amp[gs[g] + i]) if (i + g + step) % 3 != 2 else 3)
+        drafts = np.asarray(drafts if drafts else [0], np.int32)
+        inp = synth.gdn_step_inputs(21, 20000 + step, T, nh, 128, 128)
+        gin = {k: to_dev(inp[k]) for k in ("q", "k", "v", "g", "beta")}
+        go = torch.empty(T, nh, 128, dtype=torch.float32, device="cuda")
+        xd = to_dev(x)
+        trace = torch.empty(L, T, H, dtype=torch.float32, device="cuda")
+        am = torch.empty(T, dtype=torch.int32, device="cuda")
+        say("decode small", T, step)
+        tok, na = mk.mk_decode_step(st, xd, gs, to_dev(drafts), gdn=gin, gdn_o=go, argmax=am, trace=trace)
+        tr = to_np(trace)
+        assert np.array_equal(to_np(xd), tr[L - 1])
+        assert np.array_equal(to_np(am), amp)
+        _check_layers(fields, x, tr)
+        _check_head(W16, tr[L - 1], to_np(am), na, tok, gs, drafts[:T - G])
+        # Gated DeltaNet per agent: outputs of this step and (below) the committed state
+        og = to_np(go)
+        for a in range(G):
+            r0, r1 = gs[a], gs[a + 1]
+            sl = {k: inp[k][r0:r1] for k in inp}
+            S_ref[a], o_ref = oracle.gdn_step(S_ref[a], sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], int(na[a]))
+            assert rel_err(og[r0:r1], o_ref) <= FP32_TOL, (a, rel_err(og[r0:r1], o_ref))
+    for a in range(G):
+        mk.mk_deltanet_commit(st.agents[a])
+        assert rel_err(to_np(st.agents[a].S), S_ref[a]) <= FP32_TOL
