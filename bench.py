@@ -1,0 +1,263 @@
+"""Benchmark of the persistent decode step on one MI355X.
+
+Workload (synthetic, seeded): a 64-layer stack with hidden 5120, projections
+5120 -> 10240 -> 5120 and a 5120 -> 17408 -> 5120 SiLU FFN per layer in
+Q4_K-style blocks (13.40 GB), an fp16 lm_head of 151,936 x 5120, and a Gated
+DeltaNet mixer (32 heads of 128 x 128 fp32 state) in 48 of the 64 layers, one
+state per agent.  A step is one mk_decode_step call: one persistent launch
+over all layers, lm_head, argmax and verification, plus the readback of the
+accepted tokens.  The primary line is T = 12 rows (4 agents x [token + 2
+drafts]); T = 1 and T = 5 (one sequence, 4 drafts) are measured too.
+
+Each agent replays the largest possible number of ring rows every step
+(T_agent - 1), which makes the Gated DeltaNet part of the step its most
+expensive; drafts are uniform random ids.
+
+Prints ONE JSON line.  --gpus N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+HIDDEN, PROJ, FFN, VOCAB, LAYERS = 5120, 10240, 17408, 151936, 64
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_step_T12.json")
+KERNEL_SOURCES = ["bit_weight_streaming_q4_amd/csrc/mk_step.hip", "bit_weight_streaming_q4_amd/csrc/mk_device.h",
+                  "bit_weight_streaming_q4_amd/csrc/mk_gdn.h"]
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stack_bytes(layers=LAYERS, hidden=HIDDEN, proj=PROJ, ffn=FFN) -> int:
+    per = (proj * hidden + hidden * proj + 2 * ffn * hidden + hidden * ffn) // 256 * 144
+    return per * layers
+
+
+def step_bytes(T, n_agents, layers=LAYERS, vocab=VOCAB, hidden=HIDDEN, replay=True):
+    """Algorithmic HBM bytes of one step: every weight block once, the lm_head
+    once, each agent's GDN state read and written once, and the GDN step's
+    inputs, outputs and ring traffic."""
+    from synth.recipes import gdn_layers
+    w = stack_bytes(layers)
+    lm = vocab * hidden * 2
+    nh = len(gdn_layers(layers)) * 32
+    state = 2 * n_agents * nh * 128 * 128 * 4
+    t_a = T // n_agents
+    io = T * nh * (3 * 128 * 4 + 2 * 4) + T * nh * 128 * 4  # q, k, v, g, beta in; o out
+    ring = n_agents * nh * 258 * 4 * (t_a - 1) * (2 if replay else 1)
+    return {"weights": w, "lm_head": lm, "gdn": state + io + ring, "total": w + lm + state + io + ring}
+
+
+# ------------------------------------------------------------------ setup
+def build_stack(device="cuda", layers=LAYERS, progress=True):
+    """Generates and uploads the 64-layer synthetic stack and the lm_head."""
+    import torch
+
+    import bit_weight_streaming_q4_amd as mk
+    from synth import recipes
+
+    t0 = time.time()
+    Ls = []
+    bufs = {}  # field arrays reused across layers (fresh arrays cost page faults)
+    host = np.empty(mk.mk_q4k_bytes(FFN, HIDDEN), np.uint8)
+    for l in range(layers):
+        Ls.append({})
+        for m in recipes.STACK_MATS:
+            bufs[m] = recipes.stack_weight(l, m, out=bufs.get(m))
+            Ls[-1][m] = mk.pack_to_device(bufs[m], device, host_buf=host)
+        if progress and (l % 8 == 7 or l == layers - 1):
+            log(f"layers generated {l + 1}/{layers} ({time.time() - t0:.1f}s)")
+    lm = torch.from_numpy(recipes.stack_lm_head()).to(device)
+    torch.cuda.synchronize()
+    log(f"lm_head uploaded ({time.time() - t0:.1f}s)")
+    return Ls, lm
+
+
+def make_agents(n_agents, n_gdn_layers, T_max, device="cuda"):
+    import torch
+
+    import bit_weight_streaming_q4_amd as mk
+    from synth import recipes
+
+    out = []
+    for a in range(n_agents):
+        S0 = torch.from_numpy(recipes.stack_gdn_state(a, n_gdn_layers)).to(device)
+        out.append(mk.DeltaNetState(n_gdn_layers * 32, T_max, device=device, S=S0.view(-1, 128, 128)))
+    return out
+
+
+def step_inputs(T, steps, n_gdn_layers, device="cuda"):
+    import torch
+
+    from synth import recipes
+    xs = [torch.from_numpy(recipes.stack_step_input(s, T)).to(device) for s in range(steps)]
+    g = recipes.stack_gdn_inputs(0, T, n_gdn_layers)
+    gin = {k: torch.from_numpy(v).to(device) for k, v in g.items()}
+    return xs, gin
+
+
+# ------------------------------------------------------------------ timing
+def time_steps(stack, T, gs, n_agents, xs, gin, steps, warmup):
+    import torch
+
+    import bit_weight_streaming_q4_amd as mk
+    from synth import recipes
+    dev = xs[0].device
+    G = len(gs) - 1
+    drafts = torch.from_numpy(np.ascontiguousarray(
+        recipes.uniform_i32(2, 50000 + T, 0, max(T - G, 1), 0, VOCAB - 1))).to(dev)
+    nh = gin["q"].shape[1]
+    go = torch.empty(T, nh, 128, dtype=torch.float32, device=dev)
+    ws = stack.workspace(T, dev)
+    xbuf = torch.empty_like(xs[0])
+    t_agent = T // n_agents
+
+    def one(i):
+        xbuf.copy_(xs[i % len(xs)])
+        for a in stack.agents:
+            a.n_acc[0:1].fill_(t_agent - 1)  # replay the most ring rows possible
+        return mk.mk_decode_step(stack, xbuf, gs, drafts, gdn=gin, gdn_o=go, ws=ws)
+
+    for i in range(warmup):
+        one(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(steps):
+        one(warmup + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_event = ev0.elapsed_time(ev1) / steps
+    return {"ms_per_step": wall * 1e3 / steps, "ms_event": ms_event}
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(T=12):
+    """The oracle (as it stands) on a bounded sample of the same step: one
+    full layer (P_in, P_out, gate, up, down) and 1/32 of the lm_head rows at
+    T = 12, timed on this host's cores and reported as weight GB/s."""
+    import oracle
+    from synth import recipes
+    cores = len(os.sched_getaffinity(0))
+    Wl = {m: recipes.stack_weight(0, m) for m in recipes.STACK_MATS}
+    x = recipes.stack_step_input(0, T)
+    lmrows = VOCAB // 32
+    W16 = recipes.stack_lm_head(r1=lmrows)
+    t0 = time.perf_counter()
+    y = oracle.layer(x, Wl)
+    oracle.lmhead(W16, oracle.rmsnorm(y))
+    dt = time.perf_counter() - t0
+    nbytes = stack_bytes(1) + lmrows * HIDDEN * 2
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"1 of 64 layers + {lmrows} of {VOCAB} lm_head rows at T={T}, {dt:.1f} s"}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only-primary", action="store_true", help="measure T = 12 only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=LAYERS)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import __graft_entry__
+    import bit_weight_streaming_q4_amd as mk
+    from synth import recipes
+    if not os.path.exists(mk.LIB_PATH):
+        __graft_entry__.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mk.mk_init(0)
+    L = args.layers
+    gl = recipes.gdn_layers(L)
+    layers, lm = build_stack(layers=L)
+    results = {}
+    for T, gs, n_agents in ((12, [0, 3, 6, 9, 12], 4), (5, [0, 5], 1), (1, [0, 1], 1)):
+        if args.only_primary and T != 12:
+            continue
+        agents = make_agents(n_agents, len(gl), 5)
+        stack = mk.Stack(layers, lm, gdn_layers=gl, agents=agents)
+        xs, gin = step_inputs(T, min(args.steps + args.warmup, 8), len(gl))
+        log(f"timing T={T}")
+        r = time_steps(stack, T, gs, n_agents, xs, gin, args.steps, args.warmup)
+        b = step_bytes(T, n_agents, L)
+        r["bytes"] = b
+        r["weight_gb_s"] = (b["weights"] + b["lm_head"]) / (r["ms_event"] * 1e-3) / 1e9
+        r["total_gb_s"] = b["total"] / (r["ms_event"] * 1e-3) / 1e9
+        r["steps_per_s"] = 1e3 / r["ms_per_step"]
+        results[T] = r
+        log(f"T={T}: {r['ms_per_step']:.3f} ms/step (events {r['ms_event']:.3f}), "
+            f"weights {r['weight_gb_s']:.0f} GB/s, total {r['total_gb_s']:.0f} GB/s")
+        del stack, agents
+        torch.cuda.empty_cache()
+    p = results[12]
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tj = json.load(open(TRAFFIC_FILE))
+        if tj.get("kernel_source_hash") == kernel_source_hash():
+            traffic = tj.get("bytes_per_launch")
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+    out = {
+        "metric": "weight-stream GB/s (% of 8 TB/s) and decode steps/s at T=1,5,12 rows",
+        "value": round(p["weight_gb_s"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(p["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q4k-int8",
+        "data": "synthetic (seeded Q4_K-style weights, fp16 lm_head, fp32 Gated DeltaNet states)",
+        "config": {"workload": "64-layer Q4_K-style stack (hidden 5120, proj 10240, ffn 17408) + fp16 lm_head "
+                               "151936x5120 + 48 GDN layers x 4 agents, T=12 (4 agents x 3 rows), one "
+                               "persistent launch per step",
+                   "rows": 12, "layers": L, "weight_bytes_per_step": p["bytes"]["weights"] + p["bytes"]["lm_head"],
+                   "pct_of_8TBs": round(100 * p["weight_gb_s"] / PEAK_HBM_GBS, 2),
+                   "per_T": {str(T): {"ms_per_step": round(r["ms_per_step"], 4),
+                                      "steps_per_s": round(r["steps_per_s"], 2),
+                                      "rows_steps_per_s": round(r["steps_per_s"] * T, 1),
+                                      "weight_gb_s": round(r["weight_gb_s"], 1),
+                                      "total_gb_s": round(r["total_gb_s"], 1)} for T, r in results.items()}},
+        "roofline": {"bound": "hbm", "achieved": round(p["total_gb_s"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(p["total_gb_s"] / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "kernel": "k_decode_step<12>", "algorithmic_bytes_per_launch": p["bytes"]["total"]},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

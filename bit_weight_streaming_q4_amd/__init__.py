@@ -316,22 +316,13 @@ def mk_decode_step(st: Stack, x, group_start=None, drafts=None, gdn=None, gdn_o=
     return tokens, n_acc
 
 
-def pack_to_device(fields: dict, device="cuda", slice_rows: int = 4096) -> Q4K:
-    """Packs a field-array matrix on the host in row slices (in parallel) and
-    uploads it."""
-    import concurrent.futures as cf
+def pack_to_device(fields: dict, device="cuda", host_buf=None) -> Q4K:
+    """Packs a field-array matrix on the host and uploads it (host_buf: an
+    optional reusable uint8 numpy buffer of at least mk_q4k_bytes bytes)."""
     import torch
     n_out, n_in = int(fields["n_out"]), int(fields["n_in"])
-    blocks = np.empty(mk_q4k_bytes(n_out, n_in), np.uint8)
-    unit_rows = (n_in // 256) * 9216 // 64  # bytes per row-of-a-tile slice
-
-    def one(r0):
-        r1 = min(n_out, r0 + slice_rows)
-        sl = {k: fields[k][r0:r1] for k in ("d", "dmin", "sc", "m", "q")}
-        sl.update(n_out=r1 - r0, n_in=n_in, n_out_total=n_out)
-        out = mk_q4k_pack(sl, r0, r1)
-        blocks[r0 * unit_rows: r0 * unit_rows + out.size] = out
-
-    with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 4)) as ex:
-        list(ex.map(one, range(0, n_out, slice_rows)))
+    nb = mk_q4k_bytes(n_out, n_in)
+    blocks = host_buf[:nb] if host_buf is not None and host_buf.size >= nb else np.empty(nb, np.uint8)
+    arrs = [np.ascontiguousarray(fields[k]) for k in ("d", "dmin", "sc", "m", "q")]
+    _check(lib().mk_q4k_pack(*[_np_ptr(a) for a in arrs], n_out, n_in, 0, n_out, _np_ptr(blocks)), "mk_q4k_pack")
     return Q4K(torch.from_numpy(blocks).to(device), n_out, n_in)

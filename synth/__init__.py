@@ -91,23 +91,27 @@ def f64_to_f16_bits(x: float) -> int:
     return int(_load().synth_f64_to_f16(float(x)))
 
 
-def q4k_fields(seed, tensor, n_out, n_in, r0=0, r1=None, d_std=0.01) -> dict:
+def q4k_fields(seed, tensor, n_out, n_in, r0=0, r1=None, d_std=0.01, out=None) -> dict:
     """Field arrays of a Q4_K-style matrix (rows [r0, r1)).
 
     Returns d, dmin (uint16 fp16 bits, [rows][n_in/256]), sc, m (uint8 0..63,
-    [rows][n_in/256][8]) and q (uint8 0..15, [rows][n_in]).
+    [rows][n_in/256][8]) and q (uint8 0..15, [rows][n_in]).  `out` may hold
+    arrays of those shapes from an earlier call, which are then refilled.
     """
     if n_in % 256:
         raise ValueError("n_in must be a multiple of 256")
     r1 = n_out if r1 is None else r1
     rows, nsb = r1 - r0, n_in // 256
-    d = np.empty((rows, nsb), np.uint16)
-    dmin = np.empty((rows, nsb), np.uint16)
-    sc = np.empty((rows, nsb, 8), np.uint8)
-    m = np.empty((rows, nsb, 8), np.uint8)
-    q = np.empty((rows, n_in), np.uint8)
-    _load().synth_q4k_fields(seed, tensor, n_out, n_in, r0, r1, d_std, _p(d), _p(dmin), _p(sc), _p(m), _p(q))
-    return {"d": d, "dmin": dmin, "sc": sc, "m": m, "q": q, "n_out": rows, "n_in": n_in}
+    shapes = {"d": ((rows, nsb), np.uint16), "dmin": ((rows, nsb), np.uint16), "sc": ((rows, nsb, 8), np.uint8),
+              "m": ((rows, nsb, 8), np.uint8), "q": ((rows, n_in), np.uint8)}
+    f = {}
+    for k, (shp, dt) in shapes.items():
+        a = None if out is None else out.get(k)
+        f[k] = a if a is not None and a.shape == shp and a.dtype == dt and a.flags["C_CONTIGUOUS"] else np.empty(shp, dt)
+    _load().synth_q4k_fields(seed, tensor, n_out, n_in, r0, r1, d_std, _p(f["d"]), _p(f["dmin"]), _p(f["sc"]),
+                             _p(f["m"]), _p(f["q"]))
+    f.update(n_out=rows, n_in=n_in)
+    return f
 
 
 def gdn_step_inputs(seed, tensor, T, nh, dk, dv) -> dict:

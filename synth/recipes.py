@@ -60,9 +60,9 @@ def stack_shapes(hidden=HIDDEN, proj=PROJ, ffn=FFN) -> dict:
             "up": (ffn, hidden), "down": (hidden, ffn)}
 
 
-def stack_weight(layer, mat, hidden=HIDDEN, proj=PROJ, ffn=FFN, r0=0, r1=None, seed=STACK_SEED):
+def stack_weight(layer, mat, hidden=HIDDEN, proj=PROJ, ffn=FFN, r0=0, r1=None, seed=STACK_SEED, out=None):
     n_out, n_in = stack_shapes(hidden, proj, ffn)[mat]
-    return q4k_fields(seed, stack_tensor_id(layer, mat), n_out, n_in, r0, r1)
+    return q4k_fields(seed, stack_tensor_id(layer, mat), n_out, n_in, r0, r1, out=out)
 
 
 def stack_step_input(step, T, hidden=HIDDEN, seed=STACK_SEED):

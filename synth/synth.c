@@ -13,9 +13,10 @@
  * stream is identified by (seed, tensor id, sub-stream); its starting state is
  * a mix of the three, so streams do not overlap in practice.
  *
- * Normals: Box-Muller (cosine branch) in double from two uniforms drawn at
- * counters 2i and 2i+1 of the element's stream, rounded once to the storage
- * type with round-to-nearest-even.
+ * Normals: Box-Muller in double.  Pair p of a stream uses the uniforms at
+ * counters 2p and 2p+1; element 2p is the cosine branch and element 2p+1 the
+ * sine branch.  Each value is rounded once to its storage type with
+ * round-to-nearest-even.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC synth.c -lm
  */
@@ -47,44 +48,52 @@ static inline double unif_open0(uint64_t u) { return ((double)(u >> 11) + 1.0) *
 /* Uniform double in [0, 1). */
 static inline double unif(uint64_t u) { return (double)(u >> 11) * (1.0 / 9007199254740992.0); }
 
+/* Normals come in Box-Muller pairs: pair p uses uniforms at counters 2p and
+ * 2p+1; element 2p takes the cosine branch and element 2p+1 the sine branch. */
+static inline void normal_pair(uint64_t key, uint64_t p, double* z0, double* z1) {
+  const double u1 = unif_open0(draw(key, 2 * p));
+  const double u2 = unif(draw(key, 2 * p + 1));
+  const double r = sqrt(-2.0 * log(u1)), th = 6.283185307179586476925286766559 * u2;
+  double sn, cs;
+  sincos(th, &sn, &cs);
+  *z0 = r * cs;
+  *z1 = r * sn;
+}
+
 static inline double std_normal(uint64_t key, uint64_t i) {
-  const double u1 = unif_open0(draw(key, 2 * i));
-  const double u2 = unif(draw(key, 2 * i + 1));
-  return sqrt(-2.0 * log(u1)) * cos(6.283185307179586476925286766559 * u2);
+  double z0, z1;
+  normal_pair(key, i >> 1, &z0, &z1);
+  return (i & 1) ? z1 : z0;
 }
 
 /* double -> IEEE binary16 bit pattern, round to nearest even, subnormals kept,
- * overflow to +-inf.  Written from the binary16 format definition. */
+ * overflow to +-inf.  Written from the two formats' definitions: the double's
+ * significand (53 bits with the implicit one) is shifted right to the 11 bits
+ * a normal half keeps (or fewer for a subnormal half) and rounded to nearest,
+ * ties to even, on the discarded bits. */
 uint16_t synth_f64_to_f16(double x) {
-  uint16_t sign = 0;
-  if (signbit(x)) { sign = 0x8000; x = -x; }
-  if (isnan(x)) return (uint16_t)(sign | 0x7E00);
-  if (x >= 65520.0) return (uint16_t)(sign | 0x7C00); /* rounds to inf */
-  if (x < 0x1p-25) {
-    /* below half the smallest subnormal: 0 (exactly half rounds to even = 0) */
-    return sign;
-  }
-  int e;
-  double f = frexp(x, &e); /* x = f * 2^e, f in [0.5, 1) */
-  /* normal fp16: exponent field E = e - 1 + 15 in 1..30, value = 1.m * 2^(e-1) */
-  int E = e - 1 + 15;
-  double scaled;
+  uint64_t b;
+  memcpy(&b, &x, 8);
+  const uint16_t sign = (uint16_t)((b >> 48) & 0x8000);
+  const int e = (int)((b >> 52) & 0x7FF);
+  uint64_t m = b & 0xFFFFFFFFFFFFFULL;
+  if (e == 0x7FF) return (uint16_t)(sign | (m ? 0x7E00 : 0x7C00));
+  if (e == 0) return sign; /* double zero or subnormal: far below half of 2^-24 */
+  m |= 1ULL << 52;         /* value = m * 2^(e - 1075) */
+  const int E = e - 1023 + 15; /* biased half exponent if normal */
+  int shift;                   /* bits of m to discard */
+  if (E >= 1) shift = 42;      /* keep 11 significant bits */
+  else shift = 42 + (1 - E);   /* subnormal half: value = k * 2^-24 */
+  if (shift > 63) return sign;
+  const uint64_t keep = m >> shift, rem = m & ((1ULL << shift) - 1), half = 1ULL << (shift - 1);
+  uint64_t q = keep + ((rem > half || (rem == half && (keep & 1))) ? 1 : 0);
   if (E >= 1) {
-    scaled = ldexp(f, 11); /* in [1024, 2048): 11 significant bits incl. implicit */
-  } else {
-    /* subnormal: value = m * 2^-24 */
-    scaled = ldexp(x, 24);
-    E = 0;
+    int EE = E;
+    if (q == 2048) { q = 1024; ++EE; }
+    if (EE >= 31) return (uint16_t)(sign | 0x7C00);
+    return (uint16_t)(sign | (EE << 10) | (q - 1024));
   }
-  double r = nearbyint(scaled); /* current rounding mode is round-to-nearest-even */
-  uint32_t mant = (uint32_t)r;
-  if (E >= 1) {
-    if (mant == 2048) { mant = 1024; E += 1; }
-    if (E >= 31) return (uint16_t)(sign | 0x7C00);
-    return (uint16_t)(sign | (E << 10) | (mant - 1024));
-  }
-  /* subnormal (mant may round up to 1024 = smallest normal, which encodes correctly) */
-  return (uint16_t)(sign | mant);
+  return (uint16_t)(sign | q); /* q == 1024 encodes the smallest normal */
 }
 
 /* ---------------------------------------------------------------- raw draws */
@@ -95,28 +104,33 @@ void synth_u64(uint64_t seed, uint64_t tensor, uint64_t sub, uint64_t start, int
   for (int64_t i = 0; i < n; ++i) out[i] = draw(key, start + (uint64_t)i);
 }
 
+/* Fills out[0..n) with elements start..start+n of a normal stream, pairwise. */
+#define NORMAL_FILL(STORE)                                                          \
+  const uint64_t key = stream_key(seed, tensor, sub);                               \
+  const uint64_t p0 = start >> 1, p1 = (start + (uint64_t)n + 1) >> 1;              \
+  _Pragma("omp parallel for schedule(static)")                                      \
+  for (int64_t pp = (int64_t)p0; pp < (int64_t)p1; ++pp) {                          \
+    double z[2];                                                                    \
+    normal_pair(key, (uint64_t)pp, &z[0], &z[1]);                                   \
+    for (int b = 0; b < 2; ++b) {                                                   \
+      const uint64_t e = 2 * (uint64_t)pp + b;                                      \
+      if (e < start || e >= start + (uint64_t)n) continue;                          \
+      double v = mean + std * z[b];                                                 \
+      if (absval) v = fabs(v);                                                      \
+      STORE;                                                                        \
+    }                                                                               \
+  }
+
 /* Normal(mean, std) rounded to fp32; if absval, |N(mean, std)|. */
 void synth_normal_f32(uint64_t seed, uint64_t tensor, uint64_t sub, uint64_t start, int64_t n, double mean,
                       double std, int absval, float* out) {
-  const uint64_t key = stream_key(seed, tensor, sub);
-#pragma omp parallel for schedule(static)
-  for (int64_t i = 0; i < n; ++i) {
-    double v = mean + std * std_normal(key, start + (uint64_t)i);
-    if (absval) v = fabs(v);
-    out[i] = (float)v;
-  }
+  NORMAL_FILL(out[e - start] = (float)v)
 }
 
 /* Normal(mean, std) rounded to fp16 (bit patterns); if absval, |N(mean, std)|. */
 void synth_normal_f16(uint64_t seed, uint64_t tensor, uint64_t sub, uint64_t start, int64_t n, double mean,
                       double std, int absval, uint16_t* out) {
-  const uint64_t key = stream_key(seed, tensor, sub);
-#pragma omp parallel for schedule(static)
-  for (int64_t i = 0; i < n; ++i) {
-    double v = mean + std * std_normal(key, start + (uint64_t)i);
-    if (absval) v = fabs(v);
-    out[i] = synth_f64_to_f16(v);
-  }
+  NORMAL_FILL(out[e - start] = synth_f64_to_f16(v))
 }
 
 /* Integers uniform on [lo, hi] by the 64x64->128 multiply-shift map. */
@@ -143,7 +157,8 @@ void synth_uniform_f64(uint64_t seed, uint64_t tensor, uint64_t sub, uint64_t st
  * Field arrays of an n_out x n_in block-quantized matrix, rows [r0, r1).
  * Superblock s = row*(n_in/256) + b (global index, so any slice regenerates
  * the same values):
- *   d[s], dmin[s] : fp16(|N(0, 0.01)|)              sub-streams 0 and 1
+ *   d[s], dmin[s] : fp16(|N(0, 0.01)|): the two branches of Box-Muller pair s
+ *                   of sub-stream 0
  *   sc[s][j]      : 6 raw bits (j = 0..7) of draw s  sub-stream 2
  *   m[s][j]       : 6 raw bits (j = 0..7) of draw s  sub-stream 3
  *   q[row][k]     : 4 raw bits; draw (row*n_in + k)/16 of sub-stream 4 holds
@@ -154,7 +169,7 @@ void synth_q4k_fields(uint64_t seed, uint64_t tensor, int32_t n_out, int32_t n_i
                       double d_std, uint16_t* d, uint16_t* dmin, uint8_t* sc, uint8_t* m, uint8_t* q) {
   (void)n_out;
   const int64_t nsb = n_in / 256;
-  const uint64_t kd = stream_key(seed, tensor, 0), kdm = stream_key(seed, tensor, 1);
+  const uint64_t kd = stream_key(seed, tensor, 0);
   const uint64_t ksc = stream_key(seed, tensor, 2), km = stream_key(seed, tensor, 3);
   const uint64_t kq = stream_key(seed, tensor, 4);
 #pragma omp parallel for schedule(static)
@@ -163,8 +178,10 @@ void synth_q4k_fields(uint64_t seed, uint64_t tensor, int32_t n_out, int32_t n_i
     for (int64_t b = 0; b < nsb; ++b) {
       const uint64_t s = (uint64_t)(r * nsb + b);
       const int64_t ls = lr * nsb + b;
-      d[ls] = synth_f64_to_f16(fabs(d_std * std_normal(kd, s)));
-      dmin[ls] = synth_f64_to_f16(fabs(d_std * std_normal(kdm, s)));
+      double z0, z1;
+      normal_pair(kd, s, &z0, &z1);
+      d[ls] = synth_f64_to_f16(fabs(d_std * z0));
+      dmin[ls] = synth_f64_to_f16(fabs(d_std * z1));
       const uint64_t us = draw(ksc, s), um = draw(km, s);
       for (int j = 0; j < 8; ++j) {
         sc[ls * 8 + j] = (uint8_t)((us >> (6 * j)) & 63);
