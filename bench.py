@@ -151,7 +151,20 @@ def time_steps(stack, T, gs, n_agents, xs, gin, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_event = ev0.elapsed_time(ev1) / steps
-    return {"ms_per_step": wall * 1e3 / steps, "ms_event": ms_event}
+    r = {"ms_per_step": wall * 1e3 / steps, "ms_event": ms_event}
+    if os.environ.get("MK_BENCH_PHASES"):
+        st = mk.mk_decode_step_stamps(stack, T, ws)
+        L = (len(st) - 8) // 4  # stamps: start, prep, 4 per layer, lm_prep, ..., end
+        n_layers = stack.d_layers
+        d = np.diff(st[: 2 + 4 * n_layers + 1])
+        per = d[1:1 + 4 * n_layers].reshape(n_layers, 4) * 1e6
+        log(f"T={T} phases (us): prep {d[0] * 1e6:.1f}, per-layer mean P_in {per[:, 0].mean():.1f} "
+            f"P_out {per[:, 1].mean():.1f} gate/up {per[:, 2].mean():.1f} down {per[:, 3].mean():.1f}, "
+            f"lm_prep {d[-1] * 1e6:.1f}, lm+verify {(st[-1] - st[2 + 4 * n_layers]) * 1e6:.1f}, "
+            f"total {st[-1] * 1e6:.1f}")
+        log(f"T={T} P_out with GDN {per[[l for l in range(n_layers) if l % 4 != 3], 1].mean():.1f} us, "
+            f"without {per[[l for l in range(n_layers) if l % 4 == 3], 1].mean():.1f} us")
+    return r
 
 
 # ------------------------------------------------------------------ CPU baseline

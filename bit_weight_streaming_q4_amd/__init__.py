@@ -85,6 +85,7 @@ def lib():
     L.mk_decode_step_workspace.argtypes = [P, i32]
     L.mk_decode_step_workspace.restype = sz
     L.mk_decode_step.argtypes = [P, P, i32, P, i32, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+    L.mk_decode_step_stamps.argtypes = [P, i32, P, P, i32, P]
     _lib = L
     return L
 
@@ -253,6 +254,7 @@ class Stack:
         import torch
         self.layers = layers
         L = len(layers)
+        self.d_layers = L
         self.hidden, self.proj = layers[0]["p_in"].n_in, layers[0]["p_in"].n_out
         self.ffn = layers[0]["gate"].n_out
         self.lm_head = lm_head
@@ -314,6 +316,18 @@ def mk_decode_step(st: Stack, x, group_start=None, drafts=None, gdn=None, gdn_o=
                                 tokens.ctypes.data, n_acc.ctypes.data, _ptr(argmax), _ptr(trace), _ptr(ws),
                                 ws.numel(), _stream(stream)), "mk_decode_step")
     return tokens, n_acc
+
+
+def mk_decode_step_stamps(st: Stack, T: int, ws=None, n_max: int = 520):
+    """Device clock stamps of the last step on this workspace (seconds from
+    the launch start): [0] start, [i] after barrier i, [-1] end."""
+    ws = st.workspace(T) if ws is None else ws
+    h = np.zeros(n_max, np.uint64)
+    hz = ctypes.c_int64()
+    n = lib().mk_decode_step_stamps(st.h, T, _ptr(ws), h.ctypes.data, n_max, ctypes.byref(hz))
+    if n < 0:
+        _check(n, "mk_decode_step_stamps")
+    return (h[:n].astype(np.float64) - float(h[0])) / float(hz.value)
 
 
 def pack_to_device(fields: dict, device="cuda", host_buf=None) -> Q4K:

@@ -146,13 +146,11 @@ __device__ __forceinline__ void dot4_unit(const Unit& x, int b, const QAct& act,
 }
 
 // Accumulates units [b0, b1) of one tile with the next unit's loads issued
-// before the current unit's arithmetic.
+// before the current unit's arithmetic.  u0 already holds unit b0.
 template <int T>
-__device__ __forceinline__ void dot4_range(const uint8_t* __restrict__ tile, int b0, int b1, const QAct& act,
-                                           int lane, float (&acc)[T]) {
-  if (b0 >= b1) return;
-  Unit u0, u1;  // ping-pong buffers: no register copies between iterations
-  load_unit(tile + (size_t)b0 * kUnitBytes, lane, u0);
+__device__ __forceinline__ void dot4_range_from(const uint8_t* __restrict__ tile, int b0, int b1, const QAct& act,
+                                                int lane, float (&acc)[T], Unit& u0) {
+  Unit u1;  // ping-pong buffers: no register copies between iterations
   for (int b = b0; b < b1; b += 2) {
     if (b + 1 < b1) load_unit(tile + (size_t)(b + 1) * kUnitBytes, lane, u1);
     dot4_unit<T>(u0, b, act, acc);
@@ -160,6 +158,15 @@ __device__ __forceinline__ void dot4_range(const uint8_t* __restrict__ tile, int
     if (b + 2 < b1) load_unit(tile + (size_t)(b + 2) * kUnitBytes, lane, u0);
     dot4_unit<T>(u1, b + 1, act, acc);
   }
+}
+
+template <int T>
+__device__ __forceinline__ void dot4_range(const uint8_t* __restrict__ tile, int b0, int b1, const QAct& act,
+                                           int lane, float (&acc)[T]) {
+  if (b0 >= b1) return;
+  Unit u0;
+  load_unit(tile + (size_t)b0 * kUnitBytes, lane, u0);
+  dot4_range_from<T>(tile, b0, b1, act, lane, acc, u0);
 }
 
 // Matrix-core engine (any T <= 16): v_mfma_i32_16x16x32_i8 with the

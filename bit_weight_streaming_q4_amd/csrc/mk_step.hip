@@ -44,12 +44,14 @@ namespace mk {
 constexpr int kMaxAgents = 16;
 constexpr int kMaxLayers = 128;
 constexpr int kTicketTiles = 512;  // tickets per phase instance (max n_out / 64)
+constexpr int kTicketStride = 16;  // counters 64 B apart
 constexpr int kGdnHeadsPerLayer = 32;
 constexpr int kGdnJobWeight = 7;  // a half-head job ~ 64 KB of state traffic ~ 7 units
-constexpr int kBlock = 256;
+constexpr int kBlock = 512;
 constexpr int kWavesPerBlock = kBlock / 64;
 constexpr float kRmsEps = 1e-6f;
 constexpr unsigned kSpinLimit = 1u << 26;  // grid-barrier watchdog (~seconds)
+constexpr int kMaxStamps = 4 * kMaxLayers + 8;
 
 enum { K_X = 0, K_U = 1, K_X2 = 2, K_H = 3 };
 
@@ -90,6 +92,7 @@ struct StepArgs {
   float* lm_val;
   int* lm_idx;
   int32_t* out;  // [0] error word, [16..31] n_acc, [32..47] tokens, [48..63] argmax
+  uint64_t* stamps;  // [kMaxStamps]: block 0's clock after each barrier
 };
 
 __device__ __forceinline__ bool layer_is_gdn(const StepArgs& a, int l) {
@@ -104,26 +107,52 @@ __device__ __forceinline__ P* fresh(P* p) {
   return p;
 }
 
+// Cross-workgroup data of a step (partials, residual, sums of squares,
+// activations) is stored and loaded with device-scope (sc1) accesses, which
+// are coherent across the XCDs' L2 caches without whole-cache write-back or
+// invalidation; ordering comes from waiting for the stores (workgroup-scope
+// release) before the ticket/barrier atomic.  Activations are read through
+// the scalar cache: every activation buffer is written once per launch and
+// only read after its producer phase, so no stale line can be cached.
+__device__ __forceinline__ void st_coh(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh_i8(int8_t* p, int8_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coh(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_coh_i(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned ticket_add(unsigned* p) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // this wave's stores have completed
+  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------------------ grid barrier
-// Arrive: release fence, one atomic per block.  Wait: spin on the counter
-// with an agent-scope load, then an acquire fence.  The counter only grows
-// within a launch (zeroed before it), so barrier n waits for n * gridDim.x.
-// A bounded spin sets the error word instead of hanging.
+// Arrive: one device-scope atomic per block once all its waves' stores have
+// completed.  Wait: spin on the counter with device-scope loads.  The counter
+// only grows within a launch (zeroed before it), so barrier n waits for
+// n * gridDim.x.  A bounded spin sets the error word instead of hanging, and
+// every later barrier then falls through.
 __device__ void grid_barrier(const StepArgs& a, unsigned& gen) {
+  const int idx = gen / gridDim.x;
   gen += gridDim.x;
-  __syncthreads();
+  __syncthreads();  // every wave of the block has completed its stores
   if (threadIdx.x == 0) {
-    __threadfence();
-    atomicAdd(a.bar, 1u);
+    __hip_atomic_fetch_add(a.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     unsigned spins = 0;
     while (__hip_atomic_load(a.bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gen) {
       __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
+      if (++spins > kSpinLimit || __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
         atomicOr(a.err, 1);
         break;
       }
     }
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (blockIdx.x == 0 && idx + 1 < kMaxStamps) a.stamps[idx + 1] = wall_clock64();
   }
   __syncthreads();
 }
@@ -164,33 +193,37 @@ __device__ __forceinline__ void store_q8(const ActRef& o, int tau, int lane, con
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const Q8 q = quant_group32(val[t]);
-    o.a8[(size_t)t * o.K + (size_t)tau * 64 + lane] = (int8_t)q.a8;
+    st_coh_i8(o.a8 + (size_t)t * o.K + (size_t)tau * 64 + lane, (int8_t)q.a8);
     if ((lane & 31) == 0) {
       float* p = o.ssg + ((size_t)g * kTPad + t) * 2;
-      p[0] = q.s;
-      p[1] = q.s * (float)q.gsum;
+      st_coh(p, q.s);
+      st_coh(p + 1, q.s * (float)q.gsum);
     }
   }
   if ((lane & 31) == 0)
     for (int t = T; t < kTPad; ++t) {
       float* p = o.ssg + ((size_t)g * kTPad + t) * 2;
-      p[0] = 0.0f;
-      p[1] = 0.0f;
+      st_coh(p, 0.0f);
+      st_coh(p + 1, 0.0f);
     }
 }
 
 // 1/sqrt(mean(x_t^2) + eps) from the per-tile sums of squares, for row t = lane
 // (lanes >= T return 0); the sum runs over tiles in order.
 __device__ __forceinline__ float rnorm_lane(const StepArgs& a, int ss_idx, int lane) {
-  const int ntH = a.H / 64;
-  float r = 0.0f;
-  if (lane < a.T) {
-    const float* ss = a.ss + (size_t)ss_idx * ntH * 16;
-    float sum = 0.0f;
-    for (int i = 0; i < ntH; ++i) sum += __builtin_nontemporal_load(ss + i * 16 + lane);
-    r = 1.0f / __builtin_sqrtf(sum / (float)a.H + kRmsEps);
+  const int ntH = uniform(a.H / 64);
+  const int tl = lane < a.T ? lane : 0;  // every lane loads (in range); lanes >= T are discarded
+  const float* ss = a.ss + (size_t)ss_idx * ntH * 16 + tl;
+  float sum = 0.0f;
+  for (int i0 = 0; i0 < ntH; i0 += 16) {
+    float tmp[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tmp[i] = ld_coh(ss + (size_t)(i0 + i < ntH ? i0 + i : ntH - 1) * 16);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (i0 + i < ntH) sum += tmp[i];
   }
-  return r;
+  return lane < a.T ? 1.0f / __builtin_sqrtf(sum / (float)a.H + kRmsEps) : 0.0f;
 }
 
 // Sum of squares of the 64 lanes' values (fixed butterfly order).
@@ -243,18 +276,32 @@ __device__ __forceinline__ PhaseDesc phase_desc(const StepArgs& a, int ph, int l
   return d;
 }
 
-// Sum of the partials of (tile, matrix) tm, in contributing-wave order.
+// Sum of the partials of (tile, matrix) tm, in contributing-wave order.  The
+// device-scope loads are issued in batches of 4 partials so their latencies
+// overlap (a loop of single loads waits for each one).
 template <int T>
 __device__ __forceinline__ void sum_partials(const StepArgs& a, const PhaseDesc& d, const Split& sp, int nsb,
                                              int tm, int lane, float (&v)[T]) {
   const long u0 = (long)tm * nsb;
   const int lo = wave_of_weight(sp, sp.Gw + u0), hi = wave_of_weight(sp, sp.Gw + u0 + nsb - 1);
-  const float* base = a.part + ((size_t)tm * a.cmax[d.plan]) * T * 64;
+  const int n = uniform(hi - lo + 1);
+  const float* base = a.part + ((size_t)tm * a.cmax[d.plan]) * T * 64 + lane;
 #pragma unroll
   for (int t = 0; t < T; ++t) v[t] = 0.0f;
-  for (int c = 0; c <= hi - lo; ++c)
+  for (int c0 = 0; c0 < n; c0 += 4) {
+    float tmp[4][T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) v[t] += __builtin_nontemporal_load(base + ((size_t)c * T + t) * 64 + lane);
+    for (int i = 0; i < 4; ++i) {
+      const int c = c0 + i < n ? c0 + i : n - 1;  // in-range address; extra values are not added
+#pragma unroll
+      for (int t = 0; t < T; ++t) tmp[i][t] = ld_coh(base + ((size_t)c * T + t) * 64);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (c0 + i < n)
+#pragma unroll
+        for (int t = 0; t < T; ++t) v[t] += tmp[i][t];
+  }
 }
 
 template <int T>
@@ -283,15 +330,15 @@ __device__ void epilogue(const StepArgs& a, const PhaseDesc& d, const Split& sp,
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       float* xp = a.x + (size_t)t * a.H + col;
-      xn[t] = *xp + v0[t];
-      *xp = xn[t];
+      xn[t] = ld_coh(xp) + v0[t];
+      st_coh(xp, xn[t]);
     }
     const int ss_idx = d.ph == 1 ? 2 * l + 1 : 2 * l + 2;
     float* ss = a.ss + ((size_t)ss_idx * (a.H / 64) + tau) * 16;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const float s2 = wave_sum(xn[t] * xn[t]);
-      if (lane == 0) ss[t] = s2;
+      if (lane == 0) st_coh(ss + t, s2);
     }
     if (d.ph == 3 && a.trace) {
 #pragma unroll
@@ -336,57 +383,96 @@ __device__ void gdn_job(const StepArgs& a, int layer, long j, int lane) {
   gdn_half_step(x, lane);
 }
 
-template <int T>
-__device__ void gemv_phase(const StepArgs& a, const PhaseDesc& d, int w, int lane) {
+// Issues the loads of the first weight unit of wave w's stretch of phase d
+// (weights do not depend on activations, so this can precede the barrier
+// that makes the activations ready).  Returns false if the stretch is empty.
+__device__ __forceinline__ bool prefetch_first(const StepArgs& a, const PhaseDesc& d, int w, int lane, Unit& out) {
   const int nsb = d.K / 256;
-  const int ntiles = d.N / 64;
   Split sp;
   sp.Gw = d.gdn_jobs * kGdnJobWeight;
-  sp.S = sp.Gw + (long)ntiles * d.nm * nsb;
+  sp.S = sp.Gw + (long)(d.N / 64) * d.nm * nsb;
   sp.W = a.wp[d.plan];
-  if (w >= sp.W) return;
+  if (w >= sp.W) return false;
   const long s0 = split_start(sp, w), s1 = split_start(sp, w + 1);
-  // Gated DeltaNet jobs whose start falls in this stretch
-  for (long j = (s0 + kGdnJobWeight - 1) / kGdnJobWeight; j * kGdnJobWeight < s1 && j < d.gdn_jobs; ++j)
-    gdn_job(a, d.layer, j, lane);
+  if (s0 < sp.Gw) return false;  // this wave starts with Gated DeltaNet jobs
+  const long u = s0 - sp.Gw, u1 = (s1 > sp.Gw ? s1 : sp.Gw) - sp.Gw;
+  if (u >= u1) return false;
+  const int tm = (int)(u / nsb), b0 = (int)(u % nsb);
+  load_unit(d.W[tm % d.nm] + ((size_t)(tm / d.nm) * nsb + b0) * kUnitBytes, lane, out);
+  return true;
+}
+
+// One segment of a wave's stretch: the units of one (tile, matrix) from u on;
+// flushes the partial, takes the tile's ticket and, if last, runs the
+// epilogue.  Returns the number of units done.  With USE_PRE, `pre` holds the
+// segment's first unit.
+template <int T, bool USE_PRE>
+__device__ __forceinline__ int gemv_segment(const StepArgs& a, const PhaseDesc& d, const Split& sp, const QAct& act,
+                                            long u, long u1, int w, int lane, unsigned* tickets, Unit& pre) {
+  const int nsb = d.K / 256;
+  const int tm = (int)(u / nsb);
+  const int b0 = (int)(u % nsb);
+  const int len = (int)((u1 - u) < (long)(nsb - b0) ? (u1 - u) : (long)(nsb - b0));
+  const int tau = tm / d.nm, m = tm % d.nm;
+  float acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = 0.0f;
+  if (USE_PRE)
+    dot4_range_from<T>(d.W[m] + (size_t)tau * nsb * kUnitBytes, b0, b0 + len, act, lane, acc, pre);
+  else
+    dot4_range<T>(d.W[m] + (size_t)tau * nsb * kUnitBytes, b0, b0 + len, act, lane, acc);
+  const int lo = wave_of_weight(sp, sp.Gw + (long)tm * nsb);
+  float* dst = a.part + ((size_t)tm * a.cmax[d.plan] + (w - lo)) * T * 64;
+#pragma unroll
+  for (int t = 0; t < T; ++t) st_coh(dst + t * 64 + lane, acc[t]);
+  // ticket: the last contribution to this tile runs its epilogue
+  int expect = 0;
+  for (int mm = 0; mm < d.nm; ++mm) {
+    const long uu = ((long)tau * d.nm + mm) * nsb;
+    expect += wave_of_weight(sp, sp.Gw + uu + nsb - 1) - wave_of_weight(sp, sp.Gw + uu) + 1;
+  }
+  unsigned prev = 0;
+  if (lane == 0) prev = ticket_add(tickets + (size_t)tau * kTicketStride);
+  prev = uniform((int)__shfl(prev, 0, 64));
+  if ((int)prev == expect - 1) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    epilogue<T>(a, d, sp, nsb, tau, lane);
+  }
+  return len;
+}
+
+template <int T, bool USE_PRE>
+__device__ void gemv_units(const StepArgs& a, const PhaseDesc& d, const Split& sp, long s0, long s1, int w,
+                           int lane, Unit& pre, bool have_pre) {
   QAct act;
-  act.a8 = fresh(d.in.a8);
-  act.ssg = fresh(d.in.ssg);
+  act.a8 = fresh(uniform(d.in.a8));
+  act.ssg = fresh(uniform(d.in.ssg));
   act.K = d.K;
   act.T = T;
   long u = (s0 > sp.Gw ? s0 : sp.Gw) - sp.Gw;
   const long u1 = (s1 > sp.Gw ? s1 : sp.Gw) - sp.Gw;
-  unsigned* tickets = a.tickets + ((size_t)d.layer * 4 + d.ph) * kTicketTiles;
-  while (u < u1) {
-    const int tm = (int)(u / nsb);
-    const int b0 = (int)(u % nsb);
-    const int len = (int)((u1 - u) < (long)(nsb - b0) ? (u1 - u) : (long)(nsb - b0));
-    const int tau = tm / d.nm, m = tm % d.nm;
-    float acc[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) acc[t] = 0.0f;
-    dot4_range<T>(d.W[m] + (size_t)tau * nsb * kUnitBytes, b0, b0 + len, act, lane, acc);
-    const int lo = wave_of_weight(sp, sp.Gw + (long)tm * nsb);
-    float* dst = a.part + ((size_t)tm * a.cmax[d.plan] + (w - lo)) * T * 64;
-#pragma unroll
-    for (int t = 0; t < T; ++t) dst[t * 64 + lane] = acc[t];
-    // ticket: the last contribution to this tile runs its epilogue
-    int expect = 0;
-    for (int mm = 0; mm < d.nm; ++mm) {
-      const long uu = ((long)tau * d.nm + mm) * nsb;
-      expect += wave_of_weight(sp, sp.Gw + uu + nsb - 1) - wave_of_weight(sp, sp.Gw + uu) + 1;
-    }
-    unsigned prev = 0;
-    if (lane == 0) {
-      __threadfence();
-      prev = atomicAdd(tickets + tau, 1u);
-    }
-    prev = __shfl(prev, 0, 64);
-    if ((int)prev == expect - 1) {
-      __threadfence();
-      epilogue<T>(a, d, sp, nsb, tau, lane);
-    }
-    u += len;
+  unsigned* tickets = a.tickets + ((size_t)d.layer * 4 + d.ph) * kTicketTiles * kTicketStride;
+  if (USE_PRE && have_pre && u < u1) u += gemv_segment<T, true>(a, d, sp, act, u, u1, w, lane, tickets, pre);
+  while (u < u1) u += gemv_segment<T, false>(a, d, sp, act, u, u1, w, lane, tickets, pre);
+}
+
+template <int T>
+__device__ void gemv_phase(const StepArgs& a, const PhaseDesc& d, int w, int lane, Unit& pre, bool have_pre) {
+  const int nsb = d.K / 256;
+  Split sp;
+  sp.Gw = d.gdn_jobs * kGdnJobWeight;
+  sp.S = sp.Gw + (long)(d.N / 64) * d.nm * nsb;
+  sp.W = a.wp[d.plan];
+  if (w >= sp.W) return;
+  const long s0 = split_start(sp, w), s1 = split_start(sp, w + 1);
+  if (s0 < sp.Gw) {
+    // Gated DeltaNet jobs whose start falls in this stretch; no unit was
+    // prefetched for such a wave (see prefetch_first)
+    for (long j = (s0 + kGdnJobWeight - 1) / kGdnJobWeight; j * kGdnJobWeight < s1 && j < d.gdn_jobs; ++j)
+      gdn_job(a, d.layer, j, lane);
+    gemv_units<T, false>(a, d, sp, s0, s1, w, lane, pre, false);
+  } else {
+    gemv_units<T, true>(a, d, sp, s0, s1, w, lane, pre, have_pre);
   }
 }
 
@@ -397,12 +483,12 @@ __device__ void prep_phase(const StepArgs& a, int w, int lane, int nw) {
   for (int tau = w; tau < ntH; tau += nw) {
     float xv[T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) xv[t] = a.x[(size_t)t * a.H + tau * 64 + lane];
+    for (int t = 0; t < T; ++t) xv[t] = ld_coh(a.x + (size_t)t * a.H + tau * 64 + lane);
     float* ss = a.ss + (size_t)tau * 16;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const float s2 = wave_sum(xv[t] * xv[t]);
-      if (lane == 0) ss[t] = s2;
+      if (lane == 0) st_coh(ss + t, s2);
     }
     store_q8<T>(act_ref(a, 0, K_X, a.H), tau, lane, xv);
   }
@@ -413,15 +499,58 @@ __device__ void lm_prep_phase(const StepArgs& a, int w, int lane, int nw) {
   const int t = lane & 15, kq = lane >> 4;
   const float rl = rnorm_lane(a, 2 * a.L, lane);
   const float r = __shfl(rl, t, 64);
+  const int tt = t < a.T ? t : 0;  // every lane loads an in-range value
   for (int c = w; c < nc; c += nw) {
-    _Float16* o = a.frag + ((size_t)c * 64 + lane) * 32;
+    float* o = (float*)(a.frag + ((size_t)c * 64 + lane) * 32);
+    float xr[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float xv = t < a.T ? r * a.x[(size_t)t * a.H + 64 * c + 16 * kq + e] : 0.0f;
-      const _Float16 hi = (_Float16)xv;
-      o[e] = hi;
-      o[16 + e] = (_Float16)(xv - (float)hi);
+    for (int e = 0; e < 16; ++e) xr[e] = ld_coh(a.x + (size_t)tt * a.H + 64 * c + 16 * kq + e);
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const float x0 = t < a.T ? r * xr[e] : 0.0f, x1 = t < a.T ? r * xr[e + 1] : 0.0f;
+      const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+      const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+      st_coh(o + e / 2, __builtin_bit_cast(float, (h2){h0, h1}));
+      st_coh(o + 8 + e / 2, __builtin_bit_cast(float, (h2){l0, l1}));
     }
+  }
+}
+
+// One 64-wide hidden chunk of 64 vocabulary rows: the weight fragments of
+// the 4 row groups and the hi/lo fragments of the hidden rows.
+struct LmChunk {
+  u32x4 wa[4][2];
+  u32x4 bh0, bh1, bl0, bl1;
+};
+
+__device__ __forceinline__ void lm_load(const StepArgs& a, int v0, int c, int l, int vl, int kq, LmChunk& x) {
+  const u32x4* fp = (const u32x4*)(a.frag + ((size_t)c * 64 + l) * 32);
+  x.bh0 = fp[0];
+  x.bh1 = fp[1];
+  x.bl0 = fp[2];
+  x.bl1 = fp[3];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int v = v0 + 16 * g + vl;
+    const int vv = v < a.V ? v : a.V - 1;  // in-range row; results of rows >= V are never used
+    const u32x4* wpp = (const u32x4*)(a.lm + (size_t)vv * a.H + 64 * c + 16 * kq);
+    x.wa[g][0] = __builtin_nontemporal_load(wpp);
+    x.wa[g][1] = __builtin_nontemporal_load(wpp + 1);
+  }
+}
+
+__device__ __forceinline__ void lm_mfma(const LmChunk& x, f32x4 (&acc)[4]) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x.wa[g][0]),
+                                                    __builtin_bit_cast(f16x8, x.bh0), acc[g], 0, 0, 0);
+    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x.wa[g][0]),
+                                                    __builtin_bit_cast(f16x8, x.bl0), acc[g], 0, 0, 0);
+    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x.wa[g][1]),
+                                                    __builtin_bit_cast(f16x8, x.bh1), acc[g], 0, 0, 0);
+    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x.wa[g][1]),
+                                                    __builtin_bit_cast(f16x8, x.bl1), acc[g], 0, 0, 0);
   }
 }
 
@@ -434,15 +563,16 @@ __device__ __forceinline__ bool lm_better(float va, int ia, float vb, int ib) {
 }
 
 __device__ void lm_phase(const StepArgs& a) {
-  __shared__ float red[4][64][16];
+  constexpr int NW = kWavesPerBlock, TPT = kBlock / 16, RPP = 64 / TPT;  // threads per row t, rows per thread
+  __shared__ float red[NW][64][16];
   __shared__ int last;
   __shared__ int fin[16];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
   const int vl = l & 15, kq = l >> 4;
   const int nc = a.H / 64;
-  const int c0 = (nc * w) / 4, c1 = (nc * (w + 1)) / 4;
+  const int c0 = (nc * w) / NW, c1 = (nc * (w + 1)) / NW;
   const int nblk = (a.V + 63) / 64;
-  const int t_own = threadIdx.x >> 4, part = threadIdx.x & 15;
+  const int t_own = threadIdx.x / TPT, part = threadIdx.x % TPT;
   float best = 0.0f;
   int bidx = -1;
   for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
@@ -450,43 +580,26 @@ __device__ void lm_phase(const StepArgs& a) {
     f32x4 acc[4];
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[g] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    for (int c = c0; c < c1; ++c) {
-      const u32x4* fp = (const u32x4*)(a.frag + ((size_t)c * 64 + l) * 32);
-      const u32x4 bh0 = fp[0], bh1 = fp[1], bl0 = fp[2], bl1 = fp[3];
-      u32x4 wa[4][2];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int v = v0 + 16 * g + vl;
-        if (v < a.V) {
-          const u32x4* wpp = (const u32x4*)(a.lm + (size_t)v * a.H + 64 * c + 16 * kq);
-          wa[g][0] = __builtin_nontemporal_load(wpp);
-          wa[g][1] = __builtin_nontemporal_load(wpp + 1);
-        } else {
-          wa[g][0] = (u32x4){0u, 0u, 0u, 0u};
-          wa[g][1] = (u32x4){0u, 0u, 0u, 0u};
-        }
-      }
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, wa[g][0]),
-                                                        __builtin_bit_cast(f16x8, bh0), acc[g], 0, 0, 0);
-        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, wa[g][0]),
-                                                        __builtin_bit_cast(f16x8, bl0), acc[g], 0, 0, 0);
-        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, wa[g][1]),
-                                                        __builtin_bit_cast(f16x8, bh1), acc[g], 0, 0, 0);
-        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, wa[g][1]),
-                                                        __builtin_bit_cast(f16x8, bl1), acc[g], 0, 0, 0);
-      }
+    LmChunk b0c, b1c;  // ping-pong: the next chunk's loads are issued before this chunk's MFMAs
+    if (c0 < c1) lm_load(a, v0, c0, l, vl, kq, b0c);
+    for (int c = c0; c < c1; c += 2) {
+      if (c + 1 < c1) lm_load(a, v0, c + 1, l, vl, kq, b1c);
+      lm_mfma(b0c, acc);
+      if (c + 1 >= c1) break;
+      if (c + 2 < c1) lm_load(a, v0, c + 2, l, vl, kq, b0c);
+      lm_mfma(b1c, acc);
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[w][16 * g + 4 * kq + i][vl] = acc[g][i];
     __syncthreads();
-    for (int r = 4 * part; r < 4 * part + 4; ++r) {
+    for (int r = RPP * part; r < RPP * part + RPP; ++r) {
       const int v = v0 + r;
       if (v >= a.V) break;
-      const float xv = ((red[0][r][t_own] + red[1][r][t_own]) + red[2][r][t_own]) + red[3][r][t_own];
+      float xv = red[0][r][t_own];
+#pragma unroll
+      for (int q = 1; q < NW; ++q) xv += red[q][r][t_own];
       if (lm_better(xv, v, best, bidx)) {
         best = xv;
         bidx = v;
@@ -495,40 +608,37 @@ __device__ void lm_phase(const StepArgs& a) {
     __syncthreads();
   }
 #pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) {
-    const float ov = __shfl_xor(best, m, 16);
-    const int oi = __shfl_xor(bidx, m, 16);
+  for (int m = TPT / 2; m >= 1; m >>= 1) {
+    const float ov = __shfl_xor(best, m, TPT);
+    const int oi = __shfl_xor(bidx, m, TPT);
     if (lm_better(ov, oi, best, bidx)) {
       best = ov;
       bidx = oi;
     }
   }
   if (part == 0) {
-    a.lm_val[(size_t)blockIdx.x * 16 + t_own] = best;
-    a.lm_idx[(size_t)blockIdx.x * 16 + t_own] = bidx;
+    st_coh(a.lm_val + (size_t)blockIdx.x * 16 + t_own, best);
+    st_coh((float*)a.lm_idx + (size_t)blockIdx.x * 16 + t_own, __builtin_bit_cast(float, bidx));
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    last = (atomicAdd(a.lm_ticket, 1u) == gridDim.x - 1);
-  }
+  if (threadIdx.x == 0) last = (ticket_add(a.lm_ticket) == gridDim.x - 1);
   __syncthreads();
   if (!last) return;
-  __threadfence();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   best = 0.0f;
   bidx = -1;
-  for (int b = part; b < (int)gridDim.x; b += 16) {
-    const float xv = __builtin_nontemporal_load(a.lm_val + (size_t)b * 16 + t_own);
-    const int iv = __builtin_nontemporal_load(a.lm_idx + (size_t)b * 16 + t_own);
+  for (int b = part; b < (int)gridDim.x; b += TPT) {
+    const float xv = ld_coh(a.lm_val + (size_t)b * 16 + t_own);
+    const int iv = ld_coh_i(a.lm_idx + (size_t)b * 16 + t_own);
     if (lm_better(xv, iv, best, bidx)) {
       best = xv;
       bidx = iv;
     }
   }
 #pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) {
-    const float ov = __shfl_xor(best, m, 16);
-    const int oi = __shfl_xor(bidx, m, 16);
+  for (int m = TPT / 2; m >= 1; m >>= 1) {
+    const float ov = __shfl_xor(best, m, TPT);
+    const int oi = __shfl_xor(bidx, m, TPT);
     if (lm_better(ov, oi, best, bidx)) {
       best = ov;
       bidx = oi;
@@ -561,18 +671,26 @@ __global__ __launch_bounds__(kBlock) void k_decode_step(StepArgs a) {
   const int w = blockIdx.x * kWavesPerBlock + wib;
   const int nw = gridDim.x * kWavesPerBlock;
   unsigned gen = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.stamps[0] = wall_clock64();
+  // the first weight unit of each phase is requested before the barrier that
+  // precedes the phase
+  Unit pre;
+  bool have = prefetch_first(a, phase_desc(a, 0, 0), w, lane, pre);
   prep_phase<T>(a, w, lane, nw);
   grid_barrier(a, gen);
   for (int l = 0; l < a.L; ++l) {
     for (int ph = 0; ph < 4; ++ph) {
       const PhaseDesc d = phase_desc(a, ph, l);
-      gemv_phase<T>(a, d, w, lane);
+      gemv_phase<T>(a, d, w, lane, pre, have);
+      const int nph = ph == 3 ? 0 : ph + 1, nl = ph == 3 ? l + 1 : l;
+      have = nl < a.L ? prefetch_first(a, phase_desc(a, nph, nl), w, lane, pre) : false;
       grid_barrier(a, gen);
     }
   }
   lm_prep_phase(a, w, lane, nw);
   grid_barrier(a, gen);
   lm_phase(a);
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.stamps[kMaxStamps - 1] = wall_clock64();
 }
 
 // ------------------------------------------------------------ host side
@@ -627,7 +745,7 @@ struct StepLayout {
   int grid, waves;
   int wp[5], cmax[5];
   size_t off_ctrl, n_ctrl;  // zeroed before each launch: barrier, tickets
-  size_t off_out, off_tickets, off_lmticket, off_table, off_a8, off_ssg, off_ss, off_part, off_frag, off_lmv,
+  size_t off_out, off_stamps, off_tickets, off_lmticket, off_table, off_a8, off_ssg, off_ss, off_part, off_frag, off_lmv,
       off_lmi, total;
   size_t a8_layer, ssg_layer, a8_off[4], ssg_off[4];
 };
@@ -688,10 +806,12 @@ StepLayout layout(const mk_stack* st, int T) {
   y.off_lmticket = o;
   o += 256;
   y.off_tickets = o;
-  o += a256((size_t)d.n_layers * 4 * kTicketTiles * 4);
+  o += a256((size_t)d.n_layers * 4 * kTicketTiles * kTicketStride * 4);
   y.n_ctrl = o - y.off_ctrl;
   y.off_out = o;
   o += 256;
+  y.off_stamps = o;
+  o += a256(sizeof(uint64_t) * kMaxStamps);
   y.off_table = o;
   o += a256(sizeof(LayerW) * d.n_layers);
   y.off_a8 = o;
@@ -872,6 +992,7 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
   a.tickets = (unsigned*)(w8 + y.off_tickets);
   a.out = (int32_t*)(w8 + y.off_out);
   a.err = a.out;
+  a.stamps = (uint64_t*)(w8 + y.off_stamps);
   a.a8 = (int8_t*)(w8 + y.off_a8);
   a.ssg = (float*)(w8 + y.off_ssg);
   a.a8_layer = y.a8_layer;
@@ -902,6 +1023,23 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
   for (int t = 0; t < T; ++t) h_tokens[t] = hout[32 + t];
   set_error(MK_OK, "");
   return MK_OK;
+}
+
+int mk_decode_step_stamps(const mk_stack* st, int32_t T, const void* ws, uint64_t* h_stamps, int32_t n,
+                          int64_t* h_clock_hz) {
+  if (!st || !ws || !h_stamps || n < 1) return sfail(MK_ERR_ARG, "stamps: null argument");
+  const StepLayout y = layout(st, T);
+  const int m = n < kMaxStamps ? n : kMaxStamps;
+  if (hipMemcpy(h_stamps, (const uint8_t*)ws + y.off_stamps, sizeof(uint64_t) * m, hipMemcpyDeviceToHost) !=
+      hipSuccess)
+    return sfail(MK_ERR_LAUNCH, "stamps: copy failed");
+  if (h_clock_hz) {
+    int dev = 0, khz = 0;
+    hipGetDevice(&dev);
+    hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+    *h_clock_hz = (int64_t)khz * 1000;
+  }
+  return m;
 }
 
 }  // extern "C"

@@ -214,6 +214,14 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
                    const float* gdn_g, const float* gdn_beta, float* gdn_o, int32_t* h_tokens, int32_t* h_n_acc,
                    int32_t* d_argmax, float* trace, void* ws, size_t ws_bytes, void* stream);
 
+/* Profiling aid: copies (synchronously) the device clock stamps the last
+ * mk_decode_step on workspace `ws` recorded: stamp 0 at the launch start,
+ * stamp i after the i-th grid barrier (1 + 4 per layer + 1 of them), and the
+ * last of the n_max at the launch end.  h_clock_hz receives the clock rate.
+ * Returns the number of stamps copied or a negative status. */
+int mk_decode_step_stamps(const mk_stack* st, int32_t T, const void* ws, uint64_t* h_stamps, int32_t n_max,
+                          int64_t* h_clock_hz);
+
 #ifdef __cplusplus
 }
 #endif
