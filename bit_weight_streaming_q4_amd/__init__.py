@@ -86,6 +86,8 @@ def lib():
     L.mk_decode_step_workspace.restype = sz
     L.mk_decode_step.argtypes = [P, P, i32, P, i32, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
     L.mk_decode_step_stamps.argtypes = [P, i32, P, P, i32, P]
+    L.mk_decode_step_last_ms.argtypes = [P]
+    L.mk_decode_step_last_ms.restype = ctypes.c_float
     _lib = L
     return L
 
@@ -316,6 +318,11 @@ def mk_decode_step(st: Stack, x, group_start=None, drafts=None, gdn=None, gdn_o=
                                 tokens.ctypes.data, n_acc.ctypes.data, _ptr(argmax), _ptr(trace), _ptr(ws),
                                 ws.numel(), _stream(stream)), "mk_decode_step")
     return tokens, n_acc
+
+
+def mk_decode_step_last_ms(st: Stack) -> float:
+    """Event-timed duration (ms) of the last persistent launch on this stack."""
+    return float(lib().mk_decode_step_last_ms(st.h))
 
 
 def mk_decode_step_stamps(st: Stack, T: int, ws=None, n_max: int = 520):

@@ -735,6 +735,8 @@ struct mk_stack {
   int n_gdn_layers = 0;
   int8_t gdn_idx[kMaxLayers];
   void* uploaded_ws = nullptr;  // workspace that holds the current weight table
+  hipEvent_t ev[2] = {nullptr, nullptr};  // around the last launch (no device memory)
+  float last_ms = -1.0f;
 };
 
 namespace {
@@ -894,11 +896,21 @@ int mk_stack_create(const mk_stack_desc* desc, mk_stack** out) {
       st->dn.push_back(s);
     }
   }
+  if (hipEventCreate(&st->ev[0]) != hipSuccess || hipEventCreate(&st->ev[1]) != hipSuccess) {
+    st->ev[0] = st->ev[1] = nullptr;
+  }
   *out = st;
   return MK_OK;
 }
 
-void mk_stack_destroy(mk_stack* st) { delete st; }
+void mk_stack_destroy(mk_stack* st) {
+  if (!st) return;
+  for (int i = 0; i < 2; ++i)
+    if (st->ev[i]) hipEventDestroy(st->ev[i]);
+  delete st;
+}
+
+float mk_decode_step_last_ms(const mk_stack* st) { return st ? st->last_ms : -1.0f; }
 
 size_t mk_decode_step_workspace(const mk_stack* st, int32_t T) {
   if (!st || T < 1 || T > MK_T_MAX) return 0;
@@ -1007,7 +1019,9 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
   a.lm_val = (float*)(w8 + y.off_lmv);
   a.lm_idx = (int*)(w8 + y.off_lmi);
   void* args[] = {&a};
+  if (st->ev[0]) hipEventRecord(st->ev[0], s);
   hipError_t e = hipLaunchCooperativeKernel((const void*)step_kernel(T), dim3(y.grid), dim3(kBlock), args, 0, s);
+  if (st->ev[1]) hipEventRecord(st->ev[1], s);
   if (e != hipSuccess)
     return set_error(e == hipErrorCooperativeLaunchTooLarge ? MK_ERR_COOP : MK_ERR_LAUNCH,
                      "decode: cooperative launch failed: %s", hipGetErrorString(e));
@@ -1018,6 +1032,8 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
   if (hipMemcpyAsync(hout, w8 + y.off_out, sizeof(hout), hipMemcpyDeviceToHost, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess)
     return sfail(MK_ERR_LAUNCH, "decode: readback failed");
+  st->last_ms = -1.0f;
+  if (st->ev[0] && st->ev[1]) hipEventElapsedTime(&st->last_ms, st->ev[0], st->ev[1]);
   if (hout[0]) return sfail(MK_ERR_DEVICE, "decode: grid-barrier watchdog fired");
   for (int g = 0; g < G; ++g) h_n_acc[g] = hout[16 + g];
   for (int t = 0; t < T; ++t) h_tokens[t] = hout[32 + t];

@@ -214,6 +214,11 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
                    const float* gdn_g, const float* gdn_beta, float* gdn_o, int32_t* h_tokens, int32_t* h_n_acc,
                    int32_t* d_argmax, float* trace, void* ws, size_t ws_bytes, void* stream);
 
+/* Duration in ms of the last mk_decode_step's persistent launch on this
+ * stack, from HIP events recorded around the launch on its stream (-1 if
+ * unavailable). */
+float mk_decode_step_last_ms(const mk_stack* st);
+
 /* Profiling aid: copies (synchronously) the device clock stamps the last
  * mk_decode_step on workspace `ws` recorded: stamp 0 at the launch start,
  * stamp i after the i-th grid barrier (1 + 4 per layer + 1 of them), and the
