@@ -11,8 +11,8 @@
 //   prep       q8(x) and the per-tile sums of squares of x (RMSNorm input)
 //   per layer  P_in    u  = r(x) * (P_in . q8(x))         -> q8(u)
 //              P_out   x += P_out . q8(u)                  -> q8(x), sums of squares
-//                      (+ Gated DeltaNet step per agent in GDN layers)
 //              gate/up h  = SiLU(r g) * (r u)              -> q8(h)
+//                      (+ Gated DeltaNet step per agent in GDN layers)
 //              down    x += W_down . q8(h)                 -> q8(x), sums of squares
 //   lm_prep    hid = r(x) * x, split into fp16 hi + lo fragments
 //   lm         logits, per-block argmax, last block: argmax, verify, accept
@@ -21,13 +21,27 @@
 // t, so the GEMV runs on q8 of the un-normalised row and the factor is applied
 // once in the epilogue.
 //
-// Work split: each GEMV phase is a line of "units" (64 output rows x one
-// superblock = 9216 B of weights), tile-major; the participating waves take
-// equal contiguous stretches of it (stream-K), computed arithmetically.  A
-// wave flushes one fp32 partial per (tile, matrix) it touches; the last wave
-// to flush a tile (atomic ticket) adds the partials in wave order and runs the
-// epilogue, so results do not depend on timing.  GDN half-head jobs sit at the
-// front of the P_out line with a weight of several units.
+// Roles inside a block of 8 waves (one block per CU):
+//   compute waves (7)  Each walks a fixed stream of weight units (64 rows x
+//                      one superblock = 9216 B) through all phases of the
+//                      step, with the loads of the next 3 units always in
+//                      flight in registers.  The stream does not stop at a
+//                      phase end: the first units of the next phase load
+//                      while the wave waits for the grid barrier that makes
+//                      that phase's activations ready.  A wave's partial
+//                      sums of a (tile, matrix) go to an LDS mailbox; it
+//                      never writes global memory, so its vector-memory
+//                      counter only ever holds its own weight loads.
+//   service wave (1)   Sums the mailboxes of its block per (tile, matrix) in
+//                      wave order, stores one partial per block, takes the
+//                      tiles' tickets (the last block to contribute runs the
+//                      tile's epilogue: sum of partials in block order,
+//                      RMSNorm factor, SiLU, residual, q8 of the outputs),
+//                      runs the block's Gated DeltaNet jobs, the prep and
+//                      lm_prep phases and the grid barrier.
+// Each GEMV phase is a line of units, tile-major; compute wave w of W takes
+// the contiguous stretch [S*w/W, S*(w+1)/W), so a block's stretch is the
+// union of its waves' and results do not depend on timing.
 #include <hip/hip_runtime.h>
 #include <string.h>
 
@@ -46,11 +60,12 @@ constexpr int kMaxLayers = 128;
 constexpr int kTicketTiles = 512;  // tickets per phase instance (max n_out / 64)
 constexpr int kTicketStride = 16;  // counters 64 B apart
 constexpr int kGdnHeadsPerLayer = 32;
-constexpr int kGdnJobWeight = 7;  // a half-head job ~ 64 KB of state traffic ~ 7 units
 constexpr int kBlock = 512;
 constexpr int kWavesPerBlock = kBlock / 64;
+constexpr int kCompute = kWavesPerBlock - 1;  // compute waves per block; the last wave serves
+constexpr int kPartBatch = 8;                 // partials loaded per batch in an epilogue
 constexpr float kRmsEps = 1e-6f;
-constexpr unsigned kSpinLimit = 1u << 26;  // grid-barrier watchdog (~seconds)
+constexpr unsigned kSpinLimit = 1u << 26;  // bound of every wait (~seconds)
 constexpr int kMaxStamps = 4 * kMaxLayers + 8;
 
 enum { K_X = 0, K_U = 1, K_X2 = 2, K_H = 3 };
@@ -62,8 +77,8 @@ struct LayerW {
 struct StepArgs {
   int L, H, P, F, V, T, G;
   int gs[MK_LM_MAX_G + 1];
-  int wp[5];    // participating waves per plan: P_in, P_out, gate/up, down, P_out+GDN
-  int cmax[5];  // partial slots per (tile, matrix) per plan
+  int Wc;       // compute waves in the grid
+  int cmax4;    // byte k: largest number of blocks contributing to one (tile, matrix) of phase kind k
   const LayerW* layers;
   const uint16_t* lm;
   uint64_t gdn_mask[2];
@@ -100,7 +115,7 @@ __device__ __forceinline__ bool layer_is_gdn(const StepArgs& a, int l) {
 }
 
 // Keeps loads through p from being issued before this point (the scalar-cache
-// reads of a phase's activations must follow the grid barrier).
+// reads of a phase's activations must follow the barrier release).
 template <typename P>
 __device__ __forceinline__ P* fresh(P* p) {
   asm volatile("" : "+s"(p)::"memory");
@@ -126,51 +141,131 @@ __device__ __forceinline__ float ld_coh(const float* p) {
 __device__ __forceinline__ int ld_coh_i(const int* p) {
   return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ unsigned ticket_add(unsigned* p) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // this wave's stores have completed
-  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// The atomic may only be performed once this wave's stores are in memory.  A
+// workgroup-scope release fence does not wait for them on this target (the
+// waves of a workgroup share one L1), so the wait is explicit; with every
+// shared store device-scope (sc1), completion means visibility to all CUs.
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ unsigned ticket_add(unsigned* p, unsigned n = 1u) {
+  stores_done();
+  return __hip_atomic_fetch_add(p, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ------------------------------------------------------------ grid barrier
-// Arrive: one device-scope atomic per block once all its waves' stores have
-// completed.  Wait: spin on the counter with device-scope loads.  The counter
-// only grows within a launch (zeroed before it), so barrier n waits for
-// n * gridDim.x.  A bounded spin sets the error word instead of hanging, and
-// every later barrier then falls through.
-__device__ void grid_barrier(const StepArgs& a, unsigned& gen) {
-  const int idx = gen / gridDim.x;
-  gen += gridDim.x;
-  __syncthreads();  // every wave of the block has completed its stores
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(a.bar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned spins = 0;
-    while (__hip_atomic_load(a.bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gen) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit || __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-        atomicOr(a.err, 1);
-        break;
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    if (blockIdx.x == 0 && idx + 1 < kMaxStamps) a.stamps[idx + 1] = wall_clock64();
-  }
-  __syncthreads();
+// LDS words shared by the waves of a block.  The LDS executes each wave's
+// accesses in order, so only the compiler must keep program order (the empty
+// asm statements); no wait on the vector-memory counter is involved, which
+// keeps a compute wave's weight loads in flight while it polls.
+typedef __attribute__((address_space(3))) int lds_int;
+__device__ __forceinline__ int lds_ld(const int* p) {
+  const int v = __hip_atomic_load((lds_int*)const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  asm volatile("" ::: "memory");
+  return v;
+}
+__device__ __forceinline__ void lds_st(int* p, int v) {
+  asm volatile("" ::: "memory");
+  __hip_atomic_store((lds_int*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// ------------------------------------------------------------ work split
-struct Split {
-  long S;   // total weight of the phase line
-  long Gw;  // weight of the GDN jobs at its front
-  int W;    // participating waves
+// ------------------------------------------------------------ block state
+// ring[c][k]: weight slot k of compute wave c (one 9216-B unit), filled by
+// the wave's own LDS-DMA loads.  mb[c][k]: mailbox k of compute wave c, the
+// partial sums [t][64] of one (tile, matrix) with its tag ((phase + 1) << 16 |
+// tile-matrix), 0 when free.  done[c] = phases finished by compute wave c;
+// rel = grid barriers completed.  wt: the per-layer weight pointers (read by
+// the compute waves at every phase change).  After the last GEMV phase the ring area
+// holds the lm phase's cross-wave reduction.
+constexpr int kSlots = 2;
+template <int T>
+struct MbCount {
+  static constexpr int value = T <= 7 ? 2 : 1;  // keeps the block within 160 KB of LDS
+};
+template <int T>
+struct BlockState {
+  static constexpr int NMB = MbCount<T>::value;
+  uint8_t ring[kCompute][kSlots][kUnitBytes] __attribute__((aligned(16)));
+  const uint8_t* wt[kMaxLayers][5];  // the weight table, copied at the start
+  float mb[kCompute][NMB][T][64];
+  int tag[kCompute][NMB];
+  int done[kCompute];
+  int rel;
+  int abort;
 };
 
-__device__ __forceinline__ long split_start(const Split& s, int w) { return (long)w * s.S / s.W; }
-// wave whose stretch contains weight position p
-__device__ __forceinline__ int wave_of_weight(const Split& s, long p) {
-  return (int)(((p + 1) * (long)s.W - 1) / s.S);
+// Waits until *p >= v.  A wait that exceeds the bound (or sees another wave
+// give up) records the failure and returns false; every later wait then
+// falls through and the launch ends without the lm phase.
+template <int T>
+__device__ __forceinline__ bool wait_ge(const StepArgs& a, BlockState<T>& s, const int* p, int v) {
+  unsigned spins = 0;
+  while (lds_ld(p) < v) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > kSpinLimit || lds_ld(&s.abort)) {
+      lds_st(&s.abort, 1);
+      if ((threadIdx.x & 63) == 0) atomicOr(a.err, 1);
+      return false;
+    }
+  }
+  return true;
 }
 
-// ------------------------------------------------------------ activations
+// ------------------------------------------------------------ phase lines
+struct Line {
+  int S;    // units in the phase
+  int nsb;  // superblocks per row (units per (tile, matrix))
+  int nm;   // matrices sharing the input (gate/up: 2)
+  int K, N;
+  int W;    // compute waves that share the line: min(all compute waves, S), so none is idle inside it
+};
+
+// Opaque copy of a wave-uniform value: a choice among such copies stays a
+// choice among values.  (A choice among fields of the argument block would
+// become a variable offset into it, which makes the compiler keep a private
+// copy of the whole block and read every field through vector memory.)
+__device__ __forceinline__ size_t opaque(size_t v) {
+  uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  asm volatile("" : "+s"(lo), "+s"(hi));
+  return ((size_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ int opaque_i(int v) {
+  v = __builtin_amdgcn_readfirstlane(v);
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
+__device__ __forceinline__ Line line_of(const StepArgs& a, int ph) {
+  // opaque copies: the choice below is among values (see opaque())
+  const int H = opaque_i(a.H), P = opaque_i(a.P), F = opaque_i(a.F);
+  Line ln;
+  ln.K = ph == 1 ? P : ph == 3 ? F : H;
+  ln.N = ph == 0 ? P : ph == 2 ? F : H;
+  ln.nm = ph == 2 ? 2 : 1;
+  ln.nsb = ln.K / 256;
+  ln.S = (ln.N / 64) * ln.nm * ln.nsb;
+  const int Wc = opaque_i(a.Wc);
+  ln.W = Wc < ln.S ? Wc : ln.S;
+  return ln;
+}
+
+// first unit of compute wave w's stretch of a line of S units shared by W <= S
+// waves (waves w >= W have none)
+__device__ __forceinline__ int stretch_lo(int S, int W, int w) {
+  return w >= W ? S : (int)(((unsigned long long)S * (unsigned)w) / (unsigned)W);
+}
+// compute wave whose stretch holds unit p
+__device__ __forceinline__ int wave_of(int S, int W, int p) {
+  return (int)((((unsigned long long)p + 1) * (unsigned)W - 1) / (unsigned)S);
+}
+// blocks contributing to (tile, matrix) tm, and the first of them (every
+// wave between two contributing waves has units, so the blocks are a range)
+__device__ __forceinline__ int first_block(const Line& ln, int tm) {
+  return wave_of(ln.S, ln.W, tm * ln.nsb) / kCompute;
+}
+__device__ __forceinline__ int n_blocks(const Line& ln, int tm) {
+  return wave_of(ln.S, ln.W, tm * ln.nsb + ln.nsb - 1) / kCompute - first_block(ln, tm) + 1;
+}
+
+// activation record of (layer, kind)
 struct ActRef {
   int8_t* a8;
   float* ssg;
@@ -178,11 +273,23 @@ struct ActRef {
 };
 
 __device__ __forceinline__ ActRef act_ref(const StepArgs& a, int layer, int kind, int K) {
+  const size_t o0 = opaque(a.a8_off[0]), o1 = opaque(a.a8_off[1]), o2 = opaque(a.a8_off[2]), o3 = opaque(a.a8_off[3]);
+  const size_t s0 = opaque(a.ssg_off[0]), s1 = opaque(a.ssg_off[1]), s2 = opaque(a.ssg_off[2]),
+               s3 = opaque(a.ssg_off[3]);
   ActRef r;
-  r.a8 = a.a8 + (size_t)layer * a.a8_layer + a.a8_off[kind];
-  r.ssg = a.ssg + (size_t)layer * a.ssg_layer + a.ssg_off[kind];
+  r.a8 = a.a8 + (size_t)layer * a.a8_layer + (kind == 0 ? o0 : kind == 1 ? o1 : kind == 2 ? o2 : o3);
+  r.ssg = a.ssg + (size_t)layer * a.ssg_layer + (kind == 0 ? s0 : kind == 1 ? s1 : kind == 2 ? s2 : s3);
   r.K = K;
   return r;
+}
+
+__device__ __forceinline__ ActRef phase_input(const StepArgs& a, int l, int ph) {
+  switch (ph) {
+    case 0: return act_ref(a, l, K_X, a.H);
+    case 1: return act_ref(a, l, K_U, a.P);
+    case 2: return act_ref(a, l, K_X2, a.H);
+    default: return act_ref(a, l, K_H, a.F);
+  }
 }
 
 // Quantizes, per row t < T, the 64 values val[t] (lane = column of tile tau)
@@ -208,150 +315,291 @@ __device__ __forceinline__ void store_q8(const ActRef& o, int tau, int lane, con
     }
 }
 
-// 1/sqrt(mean(x_t^2) + eps) from the per-tile sums of squares, for row t = lane
-// (lanes >= T return 0); the sum runs over tiles in order.
-__device__ __forceinline__ float rnorm_lane(const StepArgs& a, int ss_idx, int lane) {
-  const int ntH = uniform(a.H / 64);
-  const int tl = lane < a.T ? lane : 0;  // every lane loads (in range); lanes >= T are discarded
-  const float* ss = a.ss + (size_t)ss_idx * ntH * 16 + tl;
-  float sum = 0.0f;
-  for (int i0 = 0; i0 < ntH; i0 += 16) {
-    float tmp[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) tmp[i] = ld_coh(ss + (size_t)(i0 + i < ntH ? i0 + i : ntH - 1) * 16);
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (i0 + i < ntH) sum += tmp[i];
-  }
-  return lane < a.T ? 1.0f / __builtin_sqrtf(sum / (float)a.H + kRmsEps) : 0.0f;
-}
-
-// Sum of squares of the 64 lanes' values (fixed butterfly order).
+// Sum over the 64 lanes (fixed butterfly order).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
   return v;
 }
 
-// ------------------------------------------------------------ GEMV phases
-struct PhaseDesc {
-  int ph, plan, layer, nm, K, N;
-  const uint8_t* W[2];
-  ActRef in;
-  long gdn_jobs;
+// r[t] = 1/sqrt(mean(x_t^2) + eps) from the per-tile sums of squares of
+// record ss_idx: lane i adds tiles i, i+64, ... in order (the loads of two
+// such chunks are issued together), then the lanes are summed by the
+// butterfly; the same order for every caller.
+template <int T>
+__device__ __forceinline__ void rnorm_rows(const StepArgs& a, int ss_idx, int lane, float (&r)[T]) {
+  const int ntH = a.H / 64;
+  const float* ss = a.ss + (size_t)ss_idx * ntH * 16;
+  float acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = 0.0f;
+  for (int k0 = 0; k0 * 64 < ntH; k0 += 2) {
+    float v[2][T];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int tile = (k0 + k) * 64 + lane;
+      const int tl = tile < ntH ? tile : 0;  // in-range address; the value is not added
+#pragma unroll
+      for (int t = 0; t < T; ++t) v[k][t] = ld_coh(ss + (size_t)tl * 16 + t);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if ((k0 + k) * 64 + lane < ntH)
+#pragma unroll
+        for (int t = 0; t < T; ++t) acc[t] += v[k][t];
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t) r[t] = 1.0f / __builtin_sqrtf(wave_sum(acc[t]) / (float)a.H + kRmsEps);
+}
+
+// ------------------------------------------------------------ compute waves
+// Position in the wave's unit stream: phase q (layer q / 4, kind q % 4), the
+// units [u, u1) of its stretch still to load, the (tile, matrix) tm and
+// superblock b of unit u, and the phase's weight matrices.  q == 4L: ended.
+struct Cursor {
+  int q, u, u1, tm, b, nsb, nm;
+  const uint8_t* W0;
+  const uint8_t* W1;
 };
 
-__device__ __forceinline__ PhaseDesc phase_desc(const StepArgs& a, int ph, int l) {
-  PhaseDesc d;
-  d.ph = ph;
-  d.plan = ph;
-  d.layer = l;
-  // the weight table is written before the launch: scalar loads are safe
-  const uint8_t* lw[5];
-#pragma unroll
-  for (int i = 0; i < 5; ++i) lw[i] = *as_const<const uint8_t*>(&a.layers[l].w[i]);
-  d.gdn_jobs = 0;
-  switch (ph) {
-    case 0:
-      d.nm = 1, d.K = a.H, d.N = a.P, d.W[0] = lw[0], d.W[1] = lw[0];
-      d.in = act_ref(a, l, K_X, a.H);
-      break;
-    case 1:
-      d.nm = 1, d.K = a.P, d.N = a.H, d.W[0] = lw[1], d.W[1] = lw[1];
-      d.in = act_ref(a, l, K_U, a.P);
-      if (a.n_agents > 0 && layer_is_gdn(a, l)) {
-        d.gdn_jobs = (long)a.n_agents * kGdnHeadsPerLayer * 2;
-        d.plan = 4;
-      }
-      break;
-    case 2:
-      d.nm = 2, d.K = a.H, d.N = a.F, d.W[0] = lw[2], d.W[1] = lw[3];
-      d.in = act_ref(a, l, K_X2, a.H);
-      break;
-    default:
-      d.nm = 1, d.K = a.F, d.N = a.H, d.W[0] = lw[4], d.W[1] = lw[4];
-      d.in = act_ref(a, l, K_H, a.F);
-      break;
-  }
-  return d;
-}
-
-// Sum of the partials of (tile, matrix) tm, in contributing-wave order.  The
-// device-scope loads are issued in batches of 4 partials so their latencies
-// overlap (a loop of single loads waits for each one).
-template <int T>
-__device__ __forceinline__ void sum_partials(const StepArgs& a, const PhaseDesc& d, const Split& sp, int nsb,
-                                             int tm, int lane, float (&v)[T]) {
-  const long u0 = (long)tm * nsb;
-  const int lo = wave_of_weight(sp, sp.Gw + u0), hi = wave_of_weight(sp, sp.Gw + u0 + nsb - 1);
-  const int n = uniform(hi - lo + 1);
-  const float* base = a.part + ((size_t)tm * a.cmax[d.plan]) * T * 64 + lane;
-#pragma unroll
-  for (int t = 0; t < T; ++t) v[t] = 0.0f;
-  for (int c0 = 0; c0 < n; c0 += 4) {
-    float tmp[4][T];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = c0 + i < n ? c0 + i : n - 1;  // in-range address; extra values are not added
-#pragma unroll
-      for (int t = 0; t < T; ++t) tmp[i][t] = ld_coh(base + ((size_t)c * T + t) * 64);
+__device__ __forceinline__ void cursor_settle(const StepArgs& a, const uint8_t* const (*wt)[5], Cursor& c, int w) {
+  while (c.q < 4 * a.L) {
+    const int ph = c.q & 3, l = c.q >> 2;
+    const Line ln = line_of(a, ph);
+    c.u = stretch_lo(ln.S, ln.W, w);
+    c.u1 = stretch_lo(ln.S, ln.W, w + 1);
+    if (c.u < c.u1) {
+      c.nsb = ln.nsb;
+      c.nm = ln.nm;
+      c.tm = c.u / ln.nsb;
+      c.b = c.u - c.tm * ln.nsb;
+      const int m0 = ph == 0 ? 0 : ph == 1 ? 1 : ph == 2 ? 2 : 4;
+      c.W0 = uniform(wt[l][m0]);
+      c.W1 = uniform(wt[l][ph == 2 ? 3 : m0]);
+      return;
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (c0 + i < n)
-#pragma unroll
-        for (int t = 0; t < T; ++t) v[t] += tmp[i][t];
+    ++c.q;
   }
 }
 
+// LDS address (for M0) of slot k of compute wave c.
 template <int T>
-__device__ void epilogue(const StepArgs& a, const PhaseDesc& d, const Split& sp, int nsb, int tau, int lane) {
-  float v0[T], v1[T];
-  sum_partials<T>(a, d, sp, nsb, tau * d.nm, lane, v0);
-  if (d.nm == 2) sum_partials<T>(a, d, sp, nsb, tau * 2 + 1, lane, v1);
-  const int l = d.layer;
-  const int col = tau * 64 + lane;
-  if (d.ph == 0 || d.ph == 2) {
-    const float rl = rnorm_lane(a, d.ph == 0 ? 2 * l : 2 * l + 1, lane);
-    float y[T];
+__device__ __forceinline__ uint32_t slot_lds(BlockState<T>& s, int c, int k) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&s.ring[c][k][0];
+}
+
+// Starts the 9 LDS-DMA loads (1 KB each: 16 B per lane) of the cursor's unit
+// into the LDS slot at byte address lds, records (q, tm, b) of the unit and
+// moves on.  The loads are written in assembly so that the compiler neither
+// moves them nor waits for them: the wave waits with wait_units() (in-order
+// completion of its vector-memory operations), and it issues no other
+// vector-memory operation while units are in flight.  Returns whether loads
+// were issued.
+__device__ __forceinline__ bool issue(const StepArgs& a, const uint8_t* const (*wt)[5], Cursor& c, int w, int lane,
+                                      uint32_t lds, int& mq, int& mtm, int& mb) {
+  mq = c.q;
+  mtm = c.tm;
+  mb = c.b;
+  if (c.q >= 4 * a.L) return false;
+  const int tau = c.nm == 2 ? c.tm >> 1 : c.tm;
+  const uint8_t* W = (c.nm == 2 && (c.tm & 1)) ? c.W1 : c.W0;
+  const uint8_t* g = W + ((size_t)tau * c.nsb + c.b) * kUnitBytes + lane * 16;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds);
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const float r = __shfl(rl, t, 64);
-      if (d.ph == 0) {
-        y[t] = r * v0[t];
-      } else {
-        const float g = r * v0[t], u = r * v1[t];
-        y[t] = g * u / (1.0f + expf(-g));
-      }
+  for (int i = 0; i < 9; ++i)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds0 + i * 1024), "v"(g + i * 1024)
+                 : "memory", "m0");
+  if (++c.b == c.nsb) {
+    c.b = 0;
+    ++c.tm;
+  }
+  if (++c.u >= c.u1) {
+    ++c.q;
+    cursor_settle(a, wt, c, w);
+  }
+  return true;
+}
+
+// Waits until only the loads of `newer` units issued after the awaited one
+// are still in flight.
+__device__ __forceinline__ void wait_units(int newer) {
+  if (newer > 0)
+    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// dot4 on one unit.  With one row, all of the unit's activation loads
+// (8 x 32 B of codes' partners and 8 scale pairs) are issued before the
+// first use, so the unit costs one scalar-cache round trip, not eight.
+template <int T>
+__device__ __forceinline__ void step_dot4(const Unit& x, int b, const QAct& act, float (&acc)[T]) {
+  if constexpr (T == 1) {
+    u32x8 av[8];
+    f32x2 sv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      av[j] = *as_const<u32x8>(act.a8 + (size_t)(b * 8 + j) * 32);
+      sv[j] = *as_const<f32x2>(act.ssg + (size_t)(b * 8 + j) * kTPad * 2);
     }
-    store_q8<T>(act_ref(a, l, d.ph == 0 ? K_U : K_H, d.ph == 0 ? a.P : a.F), tau, lane, y);
+    Hdr hd;
+    decode_hdr(x.h, hd);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int p = dot_sub(x.c[j], av[j]);
+      acc[0] = __builtin_fmaf((float)p * hd.dsc[j], sv[j].x, acc[0]);
+      acc[0] = __builtin_fmaf(-hd.dm[j], sv[j].y, acc[0]);
+    }
   } else {
-    float xn[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      float* xp = a.x + (size_t)t * a.H + col;
-      xn[t] = ld_coh(xp) + v0[t];
-      st_coh(xp, xn[t]);
-    }
-    const int ss_idx = d.ph == 1 ? 2 * l + 1 : 2 * l + 2;
-    float* ss = a.ss + ((size_t)ss_idx * (a.H / 64) + tau) * 16;
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const float s2 = wave_sum(xn[t] * xn[t]);
-      if (lane == 0) st_coh(ss + t, s2);
-    }
-    if (d.ph == 3 && a.trace) {
-#pragma unroll
-      for (int t = 0; t < T; ++t) a.trace[((size_t)l * T + t) * a.H + col] = xn[t];
-    }
-    if (d.ph == 1)
-      store_q8<T>(act_ref(a, l, K_X2, a.H), tau, lane, xn);
-    else if (l + 1 < a.L)
-      store_q8<T>(act_ref(a, l + 1, K_X, a.H), tau, lane, xn);
+    dot4_unit<T>(x, b, act, acc);
   }
 }
 
-__device__ void gdn_job(const StepArgs& a, int layer, long j, int lane) {
+// The unit in an LDS slot as the dot4 engine consumes it (lane = row).
+__device__ __forceinline__ void unit_from_lds(const uint8_t* slot, int lane, Unit& x) {
+  typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+  const lds_u32x4* p = (const lds_u32x4*)(__attribute__((address_space(3))) const uint8_t*)(slot + lane * 16);
+  x.h = p[0];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x.c[j] = p[64 * (j + 1)];
+}
+
+// What a compute wave accumulates: the open (tile, matrix) of phase q.
+template <int T>
+struct Consumer {
+  int q;      // current phase (-1 before the first)
+  int tm;     // open (tile, matrix), -1 if none
+  int nflush;
+  int done;   // phases reported finished
+  QAct act;
+  float acc[T];
+};
+
+template <int T>
+__device__ __forceinline__ void flush(BlockState<T>& s, int c, int lane, Consumer<T>& k, bool& ok) {
+  const int slot = BlockState<T>::NMB == 2 ? (k.nflush & 1) : 0;
+  // a mailbox is free when its tag is 0
+  unsigned spins = 0;
+  while (ok && lds_ld(&s.tag[c][slot]) != 0) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > kSpinLimit || lds_ld(&s.abort)) {
+      lds_st(&s.abort, 1);  // the service wave reports the failure
+      ok = false;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t) s.mb[c][slot][t][lane] = k.acc[t];
+  if (lane == 0) lds_st(&s.tag[c][slot], ((k.q + 1) << 16) | k.tm);
+  ++k.nflush;
+  k.tm = -1;
+}
+
+// LDS-only wait (a compute wave issues no global atomics: the service wave
+// reports failures).
+template <int T>
+__device__ __forceinline__ bool cw_wait_ge(BlockState<T>& s, const int* p, int v) {
+  unsigned spins = 0;
+  while (lds_ld(p) < v) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > kSpinLimit || lds_ld(&s.abort)) {
+      lds_st(&s.abort, 1);
+      return false;
+    }
+  }
+  return true;
+}
+
+// Ends phases until phase q is current: flushes the open partial, reports
+// each finished phase and waits for the barrier that opens the next one.
+template <int T>
+__device__ __forceinline__ void advance_to(const StepArgs& a, BlockState<T>& s, int c, int lane, Consumer<T>& k,
+                                           int q, bool& ok) {
+  while (k.q < q) {
+    if (k.q >= 0) {
+      if (k.tm >= 0) flush<T>(s, c, lane, k, ok);
+      if (k.done < k.q + 1) {
+        k.done = k.q + 1;
+        if (lane == 0) lds_st(&s.done[c], k.done);
+      }
+    }
+    ++k.q;
+    if (k.q < 4 * a.L) {
+      ok = ok && cw_wait_ge(s, &s.rel, k.q + 1);
+      const Line ln = line_of(a, k.q & 3);
+      const ActRef in = phase_input(a, k.q >> 2, k.q & 3);
+      k.act.a8 = fresh(uniform(in.a8));
+      k.act.ssg = fresh(uniform(in.ssg));
+      k.act.K = ln.K;
+      k.act.T = T;
+    }
+  }
+}
+
+template <int T>
+__device__ __forceinline__ void consume(const StepArgs& a, BlockState<T>& s, int c, int lane, Consumer<T>& k, int mq,
+                                        int mtm, int mb, int slot, bool& ok) {
+  if (mq != k.q) advance_to<T>(a, s, c, lane, k, mq, ok);
+  if (mtm != k.tm) {
+    if (k.tm >= 0) flush<T>(s, c, lane, k, ok);
+    k.tm = mtm;
+#pragma unroll
+    for (int t = 0; t < T; ++t) k.acc[t] = 0.0f;
+  }
+  Unit r;
+  unit_from_lds(&s.ring[c][slot][0], lane, r);
+  step_dot4<T>(r, mb, k.act, k.acc);
+}
+
+// After a unit: if the next unit (nq, ntm) of the stream leaves the open
+// (tile, matrix) or the phase, hand over the partial now and report the
+// finished phase, so the service wave does not wait for the next unit's
+// bookkeeping.
+template <int T>
+__device__ __forceinline__ void finish_early(BlockState<T>& s, int c, int lane, Consumer<T>& k, int nq, int ntm,
+                                             bool& ok) {
+  if (k.tm >= 0 && (nq != k.q || ntm != k.tm)) flush<T>(s, c, lane, k, ok);
+  if (nq != k.q && k.done < k.q + 1) {
+    k.done = k.q + 1;
+    if (lane == 0) lds_st(&s.done[c], k.done);
+  }
+}
+
+template <int T>
+__device__ __forceinline__ void compute_wave(const StepArgs& a, BlockState<T>& s, int c, int lane) {
+  const int w = blockIdx.x * kCompute + c;
+  const int qend = 4 * a.L;
+  const uint32_t l0 = slot_lds(s, c, 0), l1 = slot_lds(s, c, 1);
+  const uint8_t* const(*wt)[5] = s.wt;
+  Cursor cur;
+  cur.q = 0;
+  cursor_settle(a, wt, cur, w);
+  int mq0, mtm0, mb0, mq1, mtm1, mb1;
+  issue(a, wt, cur, w, lane, l0, mq0, mtm0, mb0);
+  bool in1 = issue(a, wt, cur, w, lane, l1, mq1, mtm1, mb1);
+  Consumer<T> k;
+  k.q = -1;
+  k.tm = -1;
+  k.nflush = 0;
+  k.done = 0;
+  bool ok = true;
+  while (ok) {
+    if (mq0 >= qend) break;
+    wait_units(in1 ? 1 : 0);  // slot 0 has landed; slot 1 may still be in flight
+    consume<T>(a, s, c, lane, k, mq0, mtm0, mb0, 0, ok);
+    finish_early<T>(s, c, lane, k, mq1, mtm1, ok);
+    // the slot's LDS reads have completed (their values were used) before it is refilled
+    const bool in0 = issue(a, wt, cur, w, lane, l0, mq0, mtm0, mb0);
+    if (mq1 >= qend) break;
+    wait_units(in0 ? 1 : 0);
+    consume<T>(a, s, c, lane, k, mq1, mtm1, mb1, 1, ok);
+    finish_early<T>(s, c, lane, k, mq0, mtm0, ok);
+    in1 = issue(a, wt, cur, w, lane, l1, mq1, mtm1, mb1);
+  }
+  advance_to<T>(a, s, c, lane, k, qend, ok);  // finishes the phases after the last unit
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load outlives the stream (also after an abort)
+}
+
+__device__ __forceinline__ void gdn_job(const StepArgs& a, int layer, long j, int lane) {
   const int agent = (int)(j / (kGdnHeadsPerLayer * 2));
   const int head = (int)((j / 2) % kGdnHeadsPerLayer);
   const int half = (int)(j & 1);
@@ -383,104 +631,45 @@ __device__ void gdn_job(const StepArgs& a, int layer, long j, int lane) {
   gdn_half_step(x, lane);
 }
 
-// Issues the loads of the first weight unit of wave w's stretch of phase d
-// (weights do not depend on activations, so this can precede the barrier
-// that makes the activations ready).  Returns false if the stretch is empty.
-__device__ __forceinline__ bool prefetch_first(const StepArgs& a, const PhaseDesc& d, int w, int lane, Unit& out) {
-  const int nsb = d.K / 256;
-  Split sp;
-  sp.Gw = d.gdn_jobs * kGdnJobWeight;
-  sp.S = sp.Gw + (long)(d.N / 64) * d.nm * nsb;
-  sp.W = a.wp[d.plan];
-  if (w >= sp.W) return false;
-  const long s0 = split_start(sp, w), s1 = split_start(sp, w + 1);
-  if (s0 < sp.Gw) return false;  // this wave starts with Gated DeltaNet jobs
-  const long u = s0 - sp.Gw, u1 = (s1 > sp.Gw ? s1 : sp.Gw) - sp.Gw;
-  if (u >= u1) return false;
-  const int tm = (int)(u / nsb), b0 = (int)(u % nsb);
-  load_unit(d.W[tm % d.nm] + ((size_t)(tm / d.nm) * nsb + b0) * kUnitBytes, lane, out);
+// ------------------------------------------------------------ service wave
+// Grid barrier k (0-based): the block arrives once its compute waves have
+// finished `done` phases and this wave's stores have completed; the wave spins
+// on the counter with device-scope loads and then opens the next phase for
+// its block (rel = k + 1).  The counter only grows within a launch (zeroed
+// before it), so barrier k waits for (k + 1) * gridDim.x arrivals.
+template <int T>
+__device__ __forceinline__ bool svc_barrier(const StepArgs& a, BlockState<T>& s, int k, int done, int lane, bool ok) {
+  for (int c = 0; c < kCompute && ok; ++c) ok = wait_ge(a, s, &s.done[c], done);
+  if (!ok) return false;
+  const unsigned target = (unsigned)(k + 1) * gridDim.x;
+  int fail = 0;
+  if (lane == 0) {
+    ticket_add(a.bar);
+    unsigned spins = 0;
+    while (__hip_atomic_load(a.bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit || __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+        atomicOr(a.err, 1);
+        fail = 1;
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (blockIdx.x == 0 && k + 1 < kMaxStamps) a.stamps[k + 1] = wall_clock64();
+  }
+  fail = __shfl(fail, 0, 64);
+  if (fail) {
+    lds_st(&s.abort, 1);
+    return false;
+  }
+  if (lane == 0) lds_st(&s.rel, k + 1);
   return true;
 }
 
-// One segment of a wave's stretch: the units of one (tile, matrix) from u on;
-// flushes the partial, takes the tile's ticket and, if last, runs the
-// epilogue.  Returns the number of units done.  With USE_PRE, `pre` holds the
-// segment's first unit.
-template <int T, bool USE_PRE>
-__device__ __forceinline__ int gemv_segment(const StepArgs& a, const PhaseDesc& d, const Split& sp, const QAct& act,
-                                            long u, long u1, int w, int lane, unsigned* tickets, Unit& pre) {
-  const int nsb = d.K / 256;
-  const int tm = (int)(u / nsb);
-  const int b0 = (int)(u % nsb);
-  const int len = (int)((u1 - u) < (long)(nsb - b0) ? (u1 - u) : (long)(nsb - b0));
-  const int tau = tm / d.nm, m = tm % d.nm;
-  float acc[T];
-#pragma unroll
-  for (int t = 0; t < T; ++t) acc[t] = 0.0f;
-  if (USE_PRE)
-    dot4_range_from<T>(d.W[m] + (size_t)tau * nsb * kUnitBytes, b0, b0 + len, act, lane, acc, pre);
-  else
-    dot4_range<T>(d.W[m] + (size_t)tau * nsb * kUnitBytes, b0, b0 + len, act, lane, acc);
-  const int lo = wave_of_weight(sp, sp.Gw + (long)tm * nsb);
-  float* dst = a.part + ((size_t)tm * a.cmax[d.plan] + (w - lo)) * T * 64;
-#pragma unroll
-  for (int t = 0; t < T; ++t) st_coh(dst + t * 64 + lane, acc[t]);
-  // ticket: the last contribution to this tile runs its epilogue
-  int expect = 0;
-  for (int mm = 0; mm < d.nm; ++mm) {
-    const long uu = ((long)tau * d.nm + mm) * nsb;
-    expect += wave_of_weight(sp, sp.Gw + uu + nsb - 1) - wave_of_weight(sp, sp.Gw + uu) + 1;
-  }
-  unsigned prev = 0;
-  if (lane == 0) prev = ticket_add(tickets + (size_t)tau * kTicketStride);
-  prev = uniform((int)__shfl(prev, 0, 64));
-  if ((int)prev == expect - 1) {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    epilogue<T>(a, d, sp, nsb, tau, lane);
-  }
-  return len;
-}
-
-template <int T, bool USE_PRE>
-__device__ void gemv_units(const StepArgs& a, const PhaseDesc& d, const Split& sp, long s0, long s1, int w,
-                           int lane, Unit& pre, bool have_pre) {
-  QAct act;
-  act.a8 = fresh(uniform(d.in.a8));
-  act.ssg = fresh(uniform(d.in.ssg));
-  act.K = d.K;
-  act.T = T;
-  long u = (s0 > sp.Gw ? s0 : sp.Gw) - sp.Gw;
-  const long u1 = (s1 > sp.Gw ? s1 : sp.Gw) - sp.Gw;
-  unsigned* tickets = a.tickets + ((size_t)d.layer * 4 + d.ph) * kTicketTiles * kTicketStride;
-  if (USE_PRE && have_pre && u < u1) u += gemv_segment<T, true>(a, d, sp, act, u, u1, w, lane, tickets, pre);
-  while (u < u1) u += gemv_segment<T, false>(a, d, sp, act, u, u1, w, lane, tickets, pre);
-}
-
 template <int T>
-__device__ void gemv_phase(const StepArgs& a, const PhaseDesc& d, int w, int lane, Unit& pre, bool have_pre) {
-  const int nsb = d.K / 256;
-  Split sp;
-  sp.Gw = d.gdn_jobs * kGdnJobWeight;
-  sp.S = sp.Gw + (long)(d.N / 64) * d.nm * nsb;
-  sp.W = a.wp[d.plan];
-  if (w >= sp.W) return;
-  const long s0 = split_start(sp, w), s1 = split_start(sp, w + 1);
-  if (s0 < sp.Gw) {
-    // Gated DeltaNet jobs whose start falls in this stretch; no unit was
-    // prefetched for such a wave (see prefetch_first)
-    for (long j = (s0 + kGdnJobWeight - 1) / kGdnJobWeight; j * kGdnJobWeight < s1 && j < d.gdn_jobs; ++j)
-      gdn_job(a, d.layer, j, lane);
-    gemv_units<T, false>(a, d, sp, s0, s1, w, lane, pre, false);
-  } else {
-    gemv_units<T, true>(a, d, sp, s0, s1, w, lane, pre, have_pre);
-  }
-}
-
-// ------------------------------------------------------------ small phases
-template <int T>
-__device__ void prep_phase(const StepArgs& a, int w, int lane, int nw) {
+__device__ __forceinline__ void svc_prep(const StepArgs& a, int lane) {
   const int ntH = a.H / 64;
-  for (int tau = w; tau < ntH; tau += nw) {
+  for (int tau = blockIdx.x; tau < ntH; tau += gridDim.x) {
     float xv[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) xv[t] = ld_coh(a.x + (size_t)t * a.H + tau * 64 + lane);
@@ -494,13 +683,187 @@ __device__ void prep_phase(const StepArgs& a, int w, int lane, int nw) {
   }
 }
 
-__device__ void lm_prep_phase(const StepArgs& a, int w, int lane, int nw) {
+// Sum of the block partials of (tile, matrix) pairs tau*nm + m, m < nm, in
+// block order; all loads of up to kPartBatch partials are issued together.
+template <int T>
+__device__ __forceinline__ void sum_partials(const StepArgs& a, const Line& ln, int ph, int tau, int lane,
+                                             float (&v0)[T], float (&v1)[T]) {
+  const int tm0 = tau * ln.nm;
+  const int n0 = uniform(n_blocks(ln, tm0));
+  const int n1 = ln.nm == 2 ? uniform(n_blocks(ln, tm0 + 1)) : 0;
+  const int n = n0 + n1, cm = (a.cmax4 >> (8 * ph)) & 255;
+#pragma unroll
+  for (int t = 0; t < T; ++t) v0[t] = v1[t] = 0.0f;
+  for (int e0 = 0; e0 < n; e0 += kPartBatch) {
+    float tmp[kPartBatch][T];
+#pragma unroll
+    for (int i = 0; i < kPartBatch; ++i) {
+      const int e = e0 + i < n ? e0 + i : n - 1;  // in-range address; extra values are not added
+      const int m = e < n0 ? 0 : 1, r = e < n0 ? e : e - n0;
+      const float* p = a.part + ((size_t)((tm0 + m) * cm + r) * T) * 64 + lane;
+#pragma unroll
+      for (int t = 0; t < T; ++t) tmp[i][t] = ld_coh(p + t * 64);
+    }
+#pragma unroll
+    for (int i = 0; i < kPartBatch; ++i) {
+      if (e0 + i >= n) break;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        if (e0 + i < n0)
+          v0[t] += tmp[i][t];
+        else
+          v1[t] += tmp[i][t];
+      }
+    }
+  }
+}
+
+template <int T>
+__device__ __forceinline__ void svc_epilogue(const StepArgs& a, int q, int tau, int lane) {
+  const int l = q >> 2, ph = q & 3;
+  const Line ln = line_of(a, ph);
+  float v0[T], v1[T];
+  sum_partials<T>(a, ln, ph, tau, lane, v0, v1);
+  const int col = tau * 64 + lane;
+  if (ph == 0 || ph == 2) {
+    float r[T];
+    rnorm_rows<T>(a, ph == 0 ? 2 * l : 2 * l + 1, lane, r);
+    float y[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      if (ph == 0) {
+        y[t] = r[t] * v0[t];
+      } else {
+        const float g = r[t] * v0[t], u = r[t] * v1[t];
+        y[t] = g * u / (1.0f + expf(-g));
+      }
+    }
+    store_q8<T>(act_ref(a, l, ph == 0 ? K_U : K_H, ph == 0 ? a.P : a.F), tau, lane, y);
+  } else {
+    float xn[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) xn[t] = ld_coh(a.x + (size_t)t * a.H + col);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      xn[t] += v0[t];
+      st_coh(a.x + (size_t)t * a.H + col, xn[t]);
+    }
+    const int ss_idx = ph == 1 ? 2 * l + 1 : 2 * l + 2;
+    float* ss = a.ss + ((size_t)ss_idx * (a.H / 64) + tau) * 16;
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const float s2 = wave_sum(xn[t] * xn[t]);
+      if (lane == 0) st_coh(ss + t, s2);
+    }
+    if (ph == 3 && a.trace) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) a.trace[((size_t)l * T + t) * a.H + col] = xn[t];
+    }
+    if (ph == 1)
+      store_q8<T>(act_ref(a, l, K_X2, a.H), tau, lane, xn);
+    else if (l + 1 < a.L)
+      store_q8<T>(act_ref(a, l + 1, K_X, a.H), tau, lane, xn);
+  }
+}
+
+// One GEMV phase seen from the service wave of block b: wait for the compute
+// waves' mailboxes of each (tile, matrix) the block touches, sum them in wave
+// order, store the block partial, then take the tiles' tickets (one atomic
+// per tile, all in flight together) and run the epilogues this block won.
+template <int T>
+__device__ __forceinline__ bool svc_phase(const StepArgs& a, BlockState<T>& s, int q, int lane, bool ok) {
+  const int l = q >> 2, ph = q & 3;
+  if (ph == 2 && a.n_agents > 0 && layer_is_gdn(a, l)) {
+    // the block's share of this layer's Gated DeltaNet half-head jobs runs
+    // while the gate/up weights stream
+    const long nj = (long)a.n_agents * kGdnHeadsPerLayer * 2;
+    for (long j = nj * blockIdx.x / gridDim.x; j < nj * (blockIdx.x + 1) / gridDim.x; ++j) gdn_job(a, l, j, lane);
+  }
+  const Line ln = line_of(a, ph);
+  const int bw0 = blockIdx.x * kCompute;
+  const int ub0 = stretch_lo(ln.S, ln.W, bw0), ub1 = stretch_lo(ln.S, ln.W, bw0 + kCompute);
+  if (ub0 >= ub1 || !ok) return ok;
+  const int tm0 = ub0 / ln.nsb, tm1 = (ub1 - 1) / ln.nsb;
+  const int cm = (a.cmax4 >> (8 * ph)) & 255;
+  const int bfirst_base = blockIdx.x;
+  for (int tm = tm0; tm <= tm1; ++tm) {
+    const int p0 = tm * ln.nsb > ub0 ? tm * ln.nsb : ub0;
+    const int p1 = (tm + 1) * ln.nsb < ub1 ? (tm + 1) * ln.nsb : ub1;
+    const int c_lo = wave_of(ln.S, ln.W, p0) - bw0, c_hi = wave_of(ln.S, ln.W, p1 - 1) - bw0;
+    const int want = ((q + 1) << 16) | tm;
+    // lane NMB*c + k watches mailbox k of compute wave c
+    constexpr int NMB = BlockState<T>::NMB;
+    constexpr uint64_t kAll = (1ull << NMB) - 1;
+    uint64_t have = 0;
+    unsigned spins = 0;
+    while (true) {
+      const int tg = lane < NMB * kCompute ? lds_ld(&s.tag[lane / NMB][lane % NMB]) : 0;
+      have = __ballot(tg == want);
+      bool all = true;
+      for (int c = c_lo; c <= c_hi; ++c) all = all && ((have >> (NMB * c)) & kAll) != 0;
+      if (all) break;
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit || lds_ld(&s.abort)) {
+        lds_st(&s.abort, 1);
+        if (lane == 0) atomicOr(a.err, 1);
+        return false;
+      }
+    }
+    float v[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) v[t] = 0.0f;
+    for (int c = c_lo; c <= c_hi; ++c) {
+      const int k = ((have >> (NMB * c)) & 1ull) ? 0 : 1;
+#pragma unroll
+      for (int t = 0; t < T; ++t) v[t] += s.mb[c][k][t][lane];
+    }
+    for (int c = c_lo; c <= c_hi; ++c) {
+      const int k = ((have >> (NMB * c)) & 1ull) ? 0 : 1;
+      if (lane == 0) lds_st(&s.tag[c][k], 0);
+    }
+    const int rank = bfirst_base - first_block(ln, tm);
+    float* dst = a.part + ((size_t)(tm * cm + rank) * T) * 64 + lane;
+#pragma unroll
+    for (int t = 0; t < T; ++t) st_coh(dst + t * 64, v[t]);
+  }
+  // tickets: lane i takes tile tau0 + i for all of this block's (tile, matrix)
+  // pairs of it; the contribution that completes a tile's count wins it
+  const int tau0 = tm0 / ln.nm, tau1 = tm1 / ln.nm;
+  unsigned* tk = a.tickets + ((size_t)l * 4 + ph) * kTicketTiles * kTicketStride;
+  for (int base = tau0; base <= tau1; base += 64) {
+    const int tau = base + lane;
+    bool won = false;
+    if (tau <= tau1) {
+      int cnt = 0, expect = 0;
+      for (int m = 0; m < ln.nm; ++m) {
+        const int tm = tau * ln.nm + m;
+        if (tm >= tm0 && tm <= tm1) ++cnt;
+        expect += n_blocks(ln, tm);
+      }
+      const unsigned prev = ticket_add(tk + (size_t)tau * kTicketStride, (unsigned)cnt);
+      won = (int)prev + cnt == expect;
+    }
+    uint64_t wm = __ballot(won);
+    while (wm) {
+      const int i = __builtin_ctzll(wm);
+      wm &= wm - 1;
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      svc_epilogue<T>(a, q, uniform(base + i), lane);
+    }
+  }
+  return true;
+}
+
+template <int T>
+__device__ __forceinline__ void svc_lm_prep(const StepArgs& a, int lane, const float (&rt)[T]) {
   const int nc = a.H / 64;
   const int t = lane & 15, kq = lane >> 4;
-  const float rl = rnorm_lane(a, 2 * a.L, lane);
-  const float r = __shfl(rl, t, 64);
+  float r = 0.0f;
+#pragma unroll
+  for (int i = 0; i < T; ++i)
+    if (t == i) r = rt[i];
   const int tt = t < a.T ? t : 0;  // every lane loads an in-range value
-  for (int c = w; c < nc; c += nw) {
+  for (int c = blockIdx.x; c < nc; c += gridDim.x) {
     float* o = (float*)(a.frag + ((size_t)c * 64 + lane) * 32);
     float xr[16];
 #pragma unroll
@@ -515,6 +878,21 @@ __device__ void lm_prep_phase(const StepArgs& a, int w, int lane, int nw) {
       st_coh(o + 8 + e / 2, __builtin_bit_cast(float, (h2){l0, l1}));
     }
   }
+}
+
+template <int T>
+__device__ __forceinline__ void service_wave(const StepArgs& a, BlockState<T>& s, int lane) {
+  svc_prep<T>(a, lane);
+  bool ok = svc_barrier<T>(a, s, 0, 0, lane, true);
+  for (int q = 0; q < 4 * a.L && ok; ++q) {
+    ok = svc_phase<T>(a, s, q, lane, ok);
+    ok = ok && svc_barrier<T>(a, s, q + 1, q + 1, lane, ok);
+  }
+  if (!ok) return;
+  float r[T];
+  rnorm_rows<T>(a, 2 * a.L, lane, r);
+  svc_lm_prep<T>(a, lane, r);
+  svc_barrier<T>(a, s, 4 * a.L + 1, 4 * a.L, lane, ok);
 }
 
 // One 64-wide hidden chunk of 64 vocabulary rows: the weight fragments of
@@ -562,9 +940,8 @@ __device__ __forceinline__ bool lm_better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-__device__ void lm_phase(const StepArgs& a) {
+__device__ __forceinline__ void lm_phase(const StepArgs& a, float (*red)[64][16]) {
   constexpr int NW = kWavesPerBlock, TPT = kBlock / 16, RPP = 64 / TPT;  // threads per row t, rows per thread
-  __shared__ float red[NW][64][16];
   __shared__ int last;
   __shared__ int fin[16];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
@@ -620,6 +997,7 @@ __device__ void lm_phase(const StepArgs& a) {
     st_coh(a.lm_val + (size_t)blockIdx.x * 16 + t_own, best);
     st_coh((float*)a.lm_idx + (size_t)blockIdx.x * 16 + t_own, __builtin_bit_cast(float, bidx));
   }
+  stores_done();  // every wave's stores are in memory before thread 0 takes the ticket
   __syncthreads();
   if (threadIdx.x == 0) last = (ticket_add(a.lm_ticket) == gridDim.x - 1);
   __syncthreads();
@@ -666,30 +1044,27 @@ __device__ void lm_phase(const StepArgs& a) {
 // ------------------------------------------------------------ the kernel
 template <int T>
 __global__ __launch_bounds__(kBlock) void k_decode_step(StepArgs a) {
+  __shared__ BlockState<T> s;
   const int lane = threadIdx.x & 63;
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int w = blockIdx.x * kWavesPerBlock + wib;
-  const int nw = gridDim.x * kWavesPerBlock;
-  unsigned gen = 0;
-  if (blockIdx.x == 0 && threadIdx.x == 0) a.stamps[0] = wall_clock64();
-  // the first weight unit of each phase is requested before the barrier that
-  // precedes the phase
-  Unit pre;
-  bool have = prefetch_first(a, phase_desc(a, 0, 0), w, lane, pre);
-  prep_phase<T>(a, w, lane, nw);
-  grid_barrier(a, gen);
-  for (int l = 0; l < a.L; ++l) {
-    for (int ph = 0; ph < 4; ++ph) {
-      const PhaseDesc d = phase_desc(a, ph, l);
-      gemv_phase<T>(a, d, w, lane, pre, have);
-      const int nph = ph == 3 ? 0 : ph + 1, nl = ph == 3 ? l + 1 : l;
-      have = nl < a.L ? prefetch_first(a, phase_desc(a, nph, nl), w, lane, pre) : false;
-      grid_barrier(a, gen);
-    }
+  if (threadIdx.x < BlockState<T>::NMB * kCompute) (&s.tag[0][0])[threadIdx.x] = 0;
+  if (threadIdx.x < kCompute) s.done[threadIdx.x] = 0;
+  // the weight table is written before the launch: plain loads are safe
+  for (int i = threadIdx.x; i < a.L * 5; i += kBlock) s.wt[i / 5][i % 5] = a.layers[i / 5].w[i % 5];
+  if (threadIdx.x == 0) {
+    s.rel = 0;
+    s.abort = 0;
+    if (blockIdx.x == 0) a.stamps[0] = wall_clock64();
   }
-  lm_prep_phase(a, w, lane, nw);
-  grid_barrier(a, gen);
-  lm_phase(a);
+  __syncthreads();
+  if (wib < kCompute)
+    compute_wave<T>(a, s, wib, lane);
+  else
+    service_wave<T>(a, s, lane);
+  // every wave of the block takes part in the lm phase once lm_prep is done
+  if (!wait_ge(a, s, &s.rel, 4 * a.L + 2)) return;
+  static_assert(sizeof(s.ring) >= sizeof(float) * kWavesPerBlock * 64 * 16, "lm reduction does not fit the ring");
+  lm_phase(a, (float (*)[64][16]) & s.ring[0][0][0]);
   if (blockIdx.x == 0 && threadIdx.x == 0) a.stamps[kMaxStamps - 1] = wall_clock64();
 }
 
@@ -744,8 +1119,8 @@ namespace {
 size_t a256(size_t n) { return (n + 255) / 256 * 256; }
 
 struct StepLayout {
-  int grid, waves;
-  int wp[5], cmax[5];
+  int grid, Wc;
+  int cmax[4];
   size_t off_ctrl, n_ctrl;  // zeroed before each launch: barrier, tickets
   size_t off_out, off_stamps, off_tickets, off_lmticket, off_table, off_a8, off_ssg, off_ss, off_part, off_frag, off_lmv,
       off_lmi, total;
@@ -754,20 +1129,17 @@ struct StepLayout {
 
 int host_wave_of(long S, int W, long p) { return (int)(((p + 1) * (long)W - 1) / S); }
 
-// Participating waves and the largest number of partials a (tile, matrix)
-// receives, for one GEMV phase.
-void plan_phase(long units_tiles, int nm, int nsb, long gdn_w, int waves, int& wp, int& cmax) {
-  const long S = gdn_w + units_tiles * nm * nsb;
-  // at least one unit per participating wave, and at least ~1.5 on average
-  long want = S * 2 / 3;
-  if (want < 1) want = 1;
-  wp = (int)std::min<long>(waves, std::min<long>(want, S));
-  cmax = 1;
-  for (long tm = 0; tm < units_tiles * nm; ++tm) {
-    const long u0 = gdn_w + tm * nsb;
-    const int c = host_wave_of(S, wp, u0 + nsb - 1) - host_wave_of(S, wp, u0) + 1;
+// Largest number of blocks that contribute to one (tile, matrix) of a line of
+// n_tm (tile, matrix) pairs of nsb units each, split over Wc compute waves.
+int plan_cmax(long n_tm, int nsb, int Wc) {
+  const long S = n_tm * nsb;
+  if (Wc > S) Wc = (int)S;  // the line is shared by at most S waves, each with a unit or more
+  int cmax = 1;
+  for (long tm = 0; tm < n_tm; ++tm) {
+    const int c = host_wave_of(S, Wc, tm * nsb + nsb - 1) / kCompute - host_wave_of(S, Wc, tm * nsb) / kCompute + 1;
     cmax = std::max(cmax, c);
   }
+  return cmax;
 }
 
 StepLayout layout(const mk_stack* st, int T) {
@@ -779,18 +1151,14 @@ StepLayout layout(const mk_stack* st, int T) {
   if (hipGetDeviceProperties(&p, dev) == hipSuccess) cu = p.multiProcessorCount;
   int per_cu = 0;
   StepKernel k = step_kernel(T);
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k, kBlock, 0) != hipSuccess || per_cu < 1)
-    per_cu = 1;
-  per_cu = std::min(per_cu, 4);
-  y.grid = cu * per_cu;
-  y.waves = y.grid * kWavesPerBlock;
-  const int n_agents = st->dn.empty() ? 0 : d.n_agents;
-  const long gdn_w = (long)n_agents * kGdnHeadsPerLayer * 2 * kGdnJobWeight;
-  plan_phase(d.proj / 64, 1, d.hidden / 256, 0, y.waves, y.wp[0], y.cmax[0]);
-  plan_phase(d.hidden / 64, 1, d.proj / 256, 0, y.waves, y.wp[1], y.cmax[1]);
-  plan_phase(d.ffn / 64, 2, d.hidden / 256, 0, y.waves, y.wp[2], y.cmax[2]);
-  plan_phase(d.hidden / 64, 1, d.ffn / 256, 0, y.waves, y.wp[3], y.cmax[3]);
-  plan_phase(d.hidden / 64, 1, d.proj / 256, gdn_w, y.waves, y.wp[4], y.cmax[4]);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)k, kBlock, 0) != hipSuccess) per_cu = 0;
+  y.grid = per_cu >= 1 ? cu : 0;  // one block (7 compute waves + 1 service wave) per CU
+  y.Wc = y.grid * kCompute;
+  const int ntiles[4] = {d.proj / 64, d.hidden / 64, d.ffn / 64, d.hidden / 64};
+  const int nms[4] = {1, 1, 2, 1};
+  const int nsbs[4] = {d.hidden / 256, d.proj / 256, d.hidden / 256, d.ffn / 256};
+  for (int i = 0; i < 4; ++i) y.cmax[i] = y.Wc ? plan_cmax((long)ntiles[i] * nms[i], nsbs[i], y.Wc) : 1;
+  // (each count must fit a byte of the packed kernel argument)
   y.a8_off[K_X] = 0;
   y.a8_off[K_U] = a256((size_t)T * d.hidden);
   y.a8_off[K_X2] = y.a8_off[K_U] + a256((size_t)T * d.proj);
@@ -824,9 +1192,7 @@ StepLayout layout(const mk_stack* st, int T) {
   o += a256((size_t)(2 * d.n_layers + 1) * (d.hidden / 64) * 16 * 4);
   y.off_part = o;
   size_t part = 0;
-  const int tiles[5] = {d.proj / 64, d.hidden / 64, d.ffn / 64, d.hidden / 64, d.hidden / 64};
-  const int nms[5] = {1, 1, 2, 1, 1};
-  for (int i = 0; i < 5; ++i) part = std::max(part, (size_t)tiles[i] * nms[i] * y.cmax[i] * T * 64 * 4);
+  for (int i = 0; i < 4; ++i) part = std::max(part, (size_t)ntiles[i] * nms[i] * y.cmax[i] * T * 64 * 4);
   o += a256(part);
   y.off_frag = o;
   o += a256((size_t)(d.hidden / 64) * 64 * 32 * 2);
@@ -946,6 +1312,7 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
       if (gs[g + 1] - gs[g] > st->dn[g].T_max) return sfail(MK_ERR_RANGE, "decode: group longer than its T_max");
   }
   const StepLayout y = layout(st, T);
+  if (y.grid < 1) return sfail(MK_ERR_COOP, "decode: the step kernel does not fit on a compute unit");
   if (!ws || ws_bytes < y.total) return set_error(MK_ERR_WORKSPACE, "decode: workspace %zu < %zu bytes", ws_bytes, y.total);
   if ((uintptr_t)ws % 256) return sfail(MK_ERR_ALIGN, "decode: workspace not 256-B aligned");
   hipStream_t s = (hipStream_t)stream;
@@ -970,10 +1337,9 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
   a.T = T;
   a.G = G;
   for (int i = 0; i <= MK_LM_MAX_G; ++i) a.gs[i] = i <= G ? gs[i] : T;
-  for (int i = 0; i < 5; ++i) {
-    a.wp[i] = y.wp[i];
-    a.cmax[i] = y.cmax[i];
-  }
+  a.Wc = y.Wc;
+  a.cmax4 = 0;
+  for (int i = 0; i < 4; ++i) a.cmax4 |= y.cmax[i] << (8 * i);
   a.layers = (const LayerW*)(w8 + y.off_table);
   a.lm = d.lm_head;
   for (int l = 0; l < d.n_layers; ++l)
