@@ -60,9 +60,17 @@ constexpr int kMaxLayers = 128;
 constexpr int kTicketTiles = 512;  // tickets per phase instance (max n_out / 64)
 constexpr int kTicketStride = 16;  // counters 64 B apart
 constexpr int kGdnHeadsPerLayer = 32;
-constexpr int kBlock = 512;
+constexpr int kBlock = 320;
 constexpr int kWavesPerBlock = kBlock / 64;
-constexpr int kCompute = kWavesPerBlock - 1;  // compute waves per block; the last wave serves
+constexpr int kCompute = kWavesPerBlock - 1;  // compute waves per block (one per SIMD); the last wave serves
+// Activation record of one GEMV input, per superblock b (256 values of K),
+// kActBytes bytes: the int8 rows in the order the matrix-core A operand reads
+// them ([sub-block j][octet q][row t][8 B], rows 0..15, rows >= T zero), then
+// s[j][t] and s*gsum[j][t] as floats ([8][16] each).
+constexpr int kActA = 8 * 4 * 16 * 8;        // 4096
+constexpr int kActBytes = kActA + 2 * 8 * 16 * 4;  // 5120
+// An LDS slot holds one weight unit and the activations of its superblock.
+constexpr int kSlotBytes = kUnitBytes + kActBytes;
 constexpr int kPartBatch = 8;                 // partials loaded per batch in an epilogue
 constexpr float kRmsEps = 1e-6f;
 constexpr unsigned kSpinLimit = 1u << 26;  // bound of every wait (~seconds)
@@ -97,10 +105,9 @@ struct StepArgs {
   int* err;
   unsigned* tickets;
   unsigned* lm_ticket;
-  int8_t* a8;
-  float* ssg;
-  size_t a8_layer, ssg_layer;
-  size_t a8_off[4], ssg_off[4];
+  uint8_t* act;         // activation records, [layer][kind] (see kActBytes)
+  size_t act_layer;     // bytes per layer
+  size_t act_off[4];    // bytes from the layer's first record, per kind
   float* ss;  // [(2L+1)][H/64][16]
   float* part;
   _Float16* frag;
@@ -167,8 +174,8 @@ __device__ __forceinline__ void lds_st(int* p, int v) {
 }
 
 // ------------------------------------------------------------ block state
-// ring[c][k]: weight slot k of compute wave c (one 9216-B unit), filled by
-// the wave's own LDS-DMA loads.  mb[c][k]: mailbox k of compute wave c, the
+// ring[c][k]: slot k of compute wave c (a 9216-B weight unit and the 5120-B
+// activation block of its superblock), filled by the wave's own LDS-DMA loads.  mb[c][k]: mailbox k of compute wave c, the
 // partial sums [t][64] of one (tile, matrix) with its tag ((phase + 1) << 16 |
 // tile-matrix), 0 when free.  done[c] = phases finished by compute wave c;
 // rel = grid barriers completed.  wt: the per-layer weight pointers (read by
@@ -177,12 +184,12 @@ __device__ __forceinline__ void lds_st(int* p, int v) {
 constexpr int kSlots = 2;
 template <int T>
 struct MbCount {
-  static constexpr int value = T <= 7 ? 2 : 1;  // keeps the block within 160 KB of LDS
+  static constexpr int value = 2;
 };
 template <int T>
 struct BlockState {
   static constexpr int NMB = MbCount<T>::value;
-  uint8_t ring[kCompute][kSlots][kUnitBytes] __attribute__((aligned(16)));
+  uint8_t ring[kCompute][kSlots][kSlotBytes] __attribute__((aligned(16)));
   const uint8_t* wt[kMaxLayers][5];  // the weight table, copied at the start
   float mb[kCompute][NMB][T][64];
   int tag[kCompute][NMB];
@@ -266,53 +273,41 @@ __device__ __forceinline__ int n_blocks(const Line& ln, int tm) {
 }
 
 // activation record of (layer, kind)
-struct ActRef {
-  int8_t* a8;
-  float* ssg;
-  int K;
-};
-
-__device__ __forceinline__ ActRef act_ref(const StepArgs& a, int layer, int kind, int K) {
-  const size_t o0 = opaque(a.a8_off[0]), o1 = opaque(a.a8_off[1]), o2 = opaque(a.a8_off[2]), o3 = opaque(a.a8_off[3]);
-  const size_t s0 = opaque(a.ssg_off[0]), s1 = opaque(a.ssg_off[1]), s2 = opaque(a.ssg_off[2]),
-               s3 = opaque(a.ssg_off[3]);
-  ActRef r;
-  r.a8 = a.a8 + (size_t)layer * a.a8_layer + (kind == 0 ? o0 : kind == 1 ? o1 : kind == 2 ? o2 : o3);
-  r.ssg = a.ssg + (size_t)layer * a.ssg_layer + (kind == 0 ? s0 : kind == 1 ? s1 : kind == 2 ? s2 : s3);
-  r.K = K;
-  return r;
+__device__ __forceinline__ uint8_t* act_rec(const StepArgs& a, int layer, int kind) {
+  const size_t o0 = opaque(a.act_off[0]), o1 = opaque(a.act_off[1]), o2 = opaque(a.act_off[2]),
+               o3 = opaque(a.act_off[3]);
+  return a.act + (size_t)layer * a.act_layer + (kind == 0 ? o0 : kind == 1 ? o1 : kind == 2 ? o2 : o3);
 }
 
-__device__ __forceinline__ ActRef phase_input(const StepArgs& a, int l, int ph) {
-  switch (ph) {
-    case 0: return act_ref(a, l, K_X, a.H);
-    case 1: return act_ref(a, l, K_U, a.P);
-    case 2: return act_ref(a, l, K_X2, a.H);
-    default: return act_ref(a, l, K_H, a.F);
-  }
+__device__ __forceinline__ uint8_t* phase_input(const StepArgs& a, int l, int ph) {
+  return act_rec(a, l, ph == 0 ? K_X : ph == 1 ? K_U : ph == 2 ? K_X2 : K_H);
 }
 
-// Quantizes, per row t < T, the 64 values val[t] (lane = column of tile tau)
-// into the activation record; rows T..15 of the scale table get zeros.
+// Quantizes, per row t < T, the 64 values val[t] (lane = column of tile tau
+// of the record's K) into the record; rows T..15 get zero codes and scales.
+// Column c of superblock b = tau / 4: sub-block j = (c % 256) / 32, octet
+// q = (c % 32) / 8, byte c % 8.
 template <int T>
-__device__ __forceinline__ void store_q8(const ActRef& o, int tau, int lane, const float (&val)[T]) {
-  const int g = 2 * tau + (lane >> 5);
+__device__ __forceinline__ void store_q8(uint8_t* rec, int tau, int lane, const float (&val)[T]) {
+  uint8_t* blk = rec + (size_t)(tau >> 2) * kActBytes;
+  const int j = (tau & 3) * 2 + (lane >> 5), e = lane & 31;
+  int8_t* a8 = (int8_t*)blk + ((j * 4 + (e >> 3)) * 16) * 8 + (e & 7);
+  float* sc = (float*)(blk + kActA);
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const Q8 q = quant_group32(val[t]);
-    st_coh_i8(o.a8 + (size_t)t * o.K + (size_t)tau * 64 + lane, (int8_t)q.a8);
-    if ((lane & 31) == 0) {
-      float* p = o.ssg + ((size_t)g * kTPad + t) * 2;
-      st_coh(p, q.s);
-      st_coh(p + 1, q.s * (float)q.gsum);
+    st_coh_i8(a8 + t * 8, (int8_t)q.a8);
+    if (e == 0) {
+      st_coh(sc + j * 16 + t, q.s);
+      st_coh(sc + 128 + j * 16 + t, q.s * (float)q.gsum);
     }
   }
-  if ((lane & 31) == 0)
-    for (int t = T; t < kTPad; ++t) {
-      float* p = o.ssg + ((size_t)g * kTPad + t) * 2;
-      st_coh(p, 0.0f);
-      st_coh(p + 1, 0.0f);
-    }
+#pragma unroll
+  for (int t = T; t < kTPad; ++t) st_coh_i8(a8 + t * 8, (int8_t)0);
+  if (e < kTPad - T) {
+    st_coh(sc + j * 16 + T + e, 0.0f);
+    st_coh(sc + 128 + j * 16 + T + e, 0.0f);
+  }
 }
 
 // Sum over the 64 lanes (fixed butterfly order).
@@ -388,27 +383,65 @@ __device__ __forceinline__ uint32_t slot_lds(BlockState<T>& s, int c, int k) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&s.ring[c][k][0];
 }
 
-// Starts the 9 LDS-DMA loads (1 KB each: 16 B per lane) of the cursor's unit
-// into the LDS slot at byte address lds, records (q, tm, b) of the unit and
-// moves on.  The loads are written in assembly so that the compiler neither
-// moves them nor waits for them: the wave waits with wait_units() (in-order
-// completion of its vector-memory operations), and it issues no other
-// vector-memory operation while units are in flight.  Returns whether loads
-// were issued.
-__device__ __forceinline__ bool issue(const StepArgs& a, const uint8_t* const (*wt)[5], Cursor& c, int w, int lane,
-                                      uint32_t lds, int& mq, int& mtm, int& mb) {
-  mq = c.q;
-  mtm = c.tm;
-  mb = c.b;
-  if (c.q >= 4 * a.L) return false;
+// n LDS-DMA loads of 1 KB (16 B per lane) from global g (this lane's first
+// byte) into LDS at byte address lds.  Written in assembly so that the
+// compiler neither moves them nor waits for them: the wave waits with
+// wait_ops() (its vector-memory operations complete in issue order), and a
+// compute wave issues no other vector-memory operation while loads are in
+// flight.
+// COH: device-scope (sc1) loads, for data other CUs wrote during the launch.
+template <int N, bool COH>
+__device__ __forceinline__ void dma(uint32_t lds, const uint8_t* g) {
+  const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (COH)
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off sc1" ::"s"(l0 + i * 1024), "v"(g + i * 1024)
+                   : "memory", "m0");
+    else
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l0 + i * 1024), "v"(g + i * 1024)
+                   : "memory", "m0");
+  }
+}
+
+// Waits until at most n of this wave's vector-memory operations are in flight.
+__device__ __forceinline__ void wait_ops(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(14)" ::: "memory"); break;
+  }
+}
+
+// One slot of a compute wave: which unit it holds and the vector-memory
+// operations its loads still count (weights 9, activations 5).
+struct Slot {
+  int q, tm, b;
+  int ops;     // DMA operations issued for this slot
+  bool act;    // activations loaded (or in flight)
+};
+
+// Starts the weight loads of the cursor's unit into slot lds (and its
+// activations if phase `open` is the unit's, i.e. they are ready), records
+// the unit and moves on.  Returns the number of operations issued.
+__device__ __forceinline__ void issue(const StepArgs& a, const uint8_t* const (*wt)[5], Cursor& c, int w, int lane,
+                                      uint32_t lds, int open, Slot& sl) {
+  sl.q = c.q;
+  sl.tm = c.tm;
+  sl.b = c.b;
+  sl.ops = 0;
+  sl.act = false;
+  if (c.q >= 4 * a.L) return;
   const int tau = c.nm == 2 ? c.tm >> 1 : c.tm;
   const uint8_t* W = (c.nm == 2 && (c.tm & 1)) ? c.W1 : c.W0;
-  const uint8_t* g = W + ((size_t)tau * c.nsb + c.b) * kUnitBytes + lane * 16;
-  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds);
-#pragma unroll
-  for (int i = 0; i < 9; ++i)
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds0 + i * 1024), "v"(g + i * 1024)
-                 : "memory", "m0");
+  dma<9, false>(lds, W + ((size_t)tau * c.nsb + c.b) * kUnitBytes + lane * 16);
+  sl.ops = 9;
+  if (c.q == open) {
+    dma<5, true>(lds + kUnitBytes, phase_input(a, c.q >> 2, c.q & 3) + (size_t)c.b * kActBytes + lane * 16);
+    sl.ops = 14;
+    sl.act = true;
+  }
   if (++c.b == c.nsb) {
     c.b = 0;
     ++c.tm;
@@ -417,64 +450,130 @@ __device__ __forceinline__ bool issue(const StepArgs& a, const uint8_t* const (*
     ++c.q;
     cursor_settle(a, wt, c, w);
   }
-  return true;
 }
 
-// Waits until only the loads of `newer` units issued after the awaited one
-// are still in flight.
-__device__ __forceinline__ void wait_units(int newer) {
-  if (newer > 0)
-    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
+typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+typedef __attribute__((address_space(3))) const uint64_t lds_u64;
+typedef __attribute__((address_space(3))) const float lds_f32;
+typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
 
-// dot4 on one unit.  With one row, all of the unit's activation loads
-// (8 x 32 B of codes' partners and 8 scale pairs) are issued before the
-// first use, so the unit costs one scalar-cache round trip, not eight.
+__device__ __forceinline__ lds_u8* as_lds(const uint8_t* p) { return (lds_u8*)p; }
+
+// dot4 engine on a slot (lane = output row): the unit's codes and header from
+// LDS, the activations as wave-uniform LDS reads (every lane the same address).
 template <int T>
-__device__ __forceinline__ void step_dot4(const Unit& x, int b, const QAct& act, float (&acc)[T]) {
-  if constexpr (T == 1) {
-    u32x8 av[8];
-    f32x2 sv[8];
+__device__ __forceinline__ void slot_dot4(lds_u8* sl, int b_unused, int lane, float (&acc)[T]) {
+  (void)b_unused;
+  const lds_u32x4* w = (const lds_u32x4*)(sl + lane * 16);
+  Unit x;
+  x.h = w[0];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      av[j] = *as_const<u32x8>(act.a8 + (size_t)(b * 8 + j) * 32);
-      sv[j] = *as_const<f32x2>(act.ssg + (size_t)(b * 8 + j) * kTPad * 2);
-    }
-    Hdr hd;
-    decode_hdr(x.h, hd);
+  for (int j = 0; j < 8; ++j) x.c[j] = w[64 * (j + 1)];
+  Hdr hd;
+  decode_hdr(x.h, hd);
+  lds_u8* act = sl + kUnitBytes;
+  lds_f32* sc = (lds_f32*)(act + kActA);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int p = dot_sub(x.c[j], av[j]);
-      acc[0] = __builtin_fmaf((float)p * hd.dsc[j], sv[j].x, acc[0]);
-      acc[0] = __builtin_fmaf(-hd.dm[j], sv[j].y, acc[0]);
+  for (int j = 0; j < 8; ++j) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      u32x8 av;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint64_t v = *(lds_u64*)(act + ((j * 4 + q) * 16 + t) * 8);
+        av[2 * q] = (uint32_t)v;
+        av[2 * q + 1] = (uint32_t)(v >> 32);
+      }
+      const int p = dot_sub(x.c[j], av);
+      acc[t] = __builtin_fmaf((float)p * hd.dsc[j], sc[j * 16 + t], acc[t]);
+      acc[t] = __builtin_fmaf(-hd.dm[j], sc[128 + j * 16 + t], acc[t]);
     }
-  } else {
-    dot4_unit<T>(x, b, act, acc);
   }
 }
 
-// The unit in an LDS slot as the dot4 engine consumes it (lane = row).
-__device__ __forceinline__ void unit_from_lds(const uint8_t* slot, int lane, Unit& x) {
-  typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
-  const lds_u32x4* p = (const lds_u32x4*)(__attribute__((address_space(3))) const uint8_t*)(slot + lane * 16);
-  x.h = p[0];
+// Matrix-core engine on a slot.  Lane l = 16 q + n.  For row group nb (rows
+// 16 nb .. 16 nb + 15) and sub-block j, v_mfma_i32_16x16x32_i8 takes the
+// activations as A (row t = n, octet q: 8 bytes) and the codes as B (row
+// 16 nb + n, octet q: one dword, nibbles widened to bytes) and gives the
+// exact sub-block sums P[t = 4q + i][row 16 nb + n].  The combine adds
+// s[t][j] * d * sc_j * P, and the min term - dmin * m_j * (s*gsum)[t][j] is a
+// v_mfma_f32_16x16x4_f32 over j into the same accumulator.
+__device__ __forceinline__ void slot_mfma(lds_u8* sl, int lane, f32x4 (&acc)[4]) {
+  const int q = lane >> 4, n = lane & 15;
+  lds_u8* act = sl + kUnitBytes;
+  lds_f32* sc = (lds_f32*)(act + kActA);
+  // headers of rows 16 nb + n
+  u32x4 h[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) x.c[j] = p[64 * (j + 1)];
+  for (int nb = 0; nb < 4; ++nb) h[nb] = *(const lds_u32x4*)(sl + (16 * nb + n) * 16);
+  float d[4], dmin[4];
+  uint32_t sc03[4], sc47[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    d[nb] = f16_bits_to_f32(h[nb].x & 0xffffu);
+    dmin[nb] = f16_bits_to_f32(h[nb].x >> 16);
+    sc03[nb] = h[nb].y & 0x3F3F3F3Fu;
+    sc47[nb] = h[nb].z & 0x3F3F3F3Fu;
+  }
+  // min term: B[k][n] = -dmin * m_k for k = q (first MFMA) and q + 4 (second)
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const uint32_t m03 = (h[nb].w & 0x0F0F0F0Fu) | ((h[nb].y >> 2) & 0x30303030u);
+    const uint32_t m47 = ((h[nb].w >> 4) & 0x0F0F0F0Fu) | ((h[nb].z >> 2) & 0x30303030u);
+    const float bm0 = -dmin[nb] * (float)((m03 >> (8 * q)) & 0xffu);
+    const float bm1 = -dmin[nb] * (float)((m47 >> (8 * q)) & 0xffu);
+    const float am0 = sc[128 + q * 16 + n], am1 = sc[128 + (q + 4) * 16 + n];
+    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(am0, bm0, acc[nb], 0, 0, 0);
+    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(am1, bm1, acc[nb], 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint64_t aop = *(lds_u64*)(act + ((j * 4 + q) * 16 + n) * 8);
+    const f32x4 st = *(const lds_f32x4*)(sc + j * 16 + 4 * q);  // s of rows t = 4q .. 4q + 3
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const uint32_t cw = *(const lds_u32*)(sl + kHdrBytes + j * kSubBytes + (16 * nb + n) * 16 + q * 4);
+      const uint64_t bop = (uint64_t)(cw & 0x0F0F0F0Fu) | ((uint64_t)((cw >> 4) & 0x0F0F0F0Fu) << 32);
+      const i32x4 z = {0, 0, 0, 0};
+      const i32x4 p = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)aop, (long)bop, z, 0, 0, 0);
+      const uint32_t scw = j < 4 ? sc03[nb] : sc47[nb];
+      const float f = d[nb] * (float)((scw >> (8 * (j & 3))) & 0xffu);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[nb][i] = __builtin_fmaf((float)p[i], f * st[i], acc[nb][i]);
+    }
+  }
 }
 
-// What a compute wave accumulates: the open (tile, matrix) of phase q.
+// Which engine a T-row instance uses.
+template <int T>
+struct UseMfma {
+  static constexpr bool value = T > 2;
+};
+
+// What a compute wave accumulates: the open (tile, matrix) of phase q.  The
+// dot4 engine keeps row = lane, T rows (acc); the matrix-core engine keeps
+// the 4 row groups x 4 rows t of the C layout (macc).
 template <int T>
 struct Consumer {
   int q;      // current phase (-1 before the first)
   int tm;     // open (tile, matrix), -1 if none
   int nflush;
   int done;   // phases reported finished
-  QAct act;
   float acc[T];
+  f32x4 macc[4];
 };
 
+template <int T>
+__device__ __forceinline__ void acc_zero(Consumer<T>& k) {
+#pragma unroll
+  for (int t = 0; t < T; ++t) k.acc[t] = 0.0f;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) k.macc[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+}
+
+// Writes the open partial to the wave's mailbox as [t][64 rows of the tile].
 template <int T>
 __device__ __forceinline__ void flush(BlockState<T>& s, int c, int lane, Consumer<T>& k, bool& ok) {
   const int slot = BlockState<T>::NMB == 2 ? (k.nflush & 1) : 0;
@@ -487,8 +586,17 @@ __device__ __forceinline__ void flush(BlockState<T>& s, int c, int lane, Consume
       ok = false;
     }
   }
+  if constexpr (UseMfma<T>::value) {
+    const int q = lane >> 4, n = lane & 15;
 #pragma unroll
-  for (int t = 0; t < T; ++t) s.mb[c][slot][t][lane] = k.acc[t];
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * q + i < T) s.mb[c][slot][4 * q + i][16 * nb + n] = k.macc[nb][i];
+  } else {
+#pragma unroll
+    for (int t = 0; t < T; ++t) s.mb[c][slot][t][lane] = k.acc[t];
+  }
   if (lane == 0) lds_st(&s.tag[c][slot], ((k.q + 1) << 16) | k.tm);
   ++k.nflush;
   k.tm = -1;
@@ -523,31 +631,8 @@ __device__ __forceinline__ void advance_to(const StepArgs& a, BlockState<T>& s, 
       }
     }
     ++k.q;
-    if (k.q < 4 * a.L) {
-      ok = ok && cw_wait_ge(s, &s.rel, k.q + 1);
-      const Line ln = line_of(a, k.q & 3);
-      const ActRef in = phase_input(a, k.q >> 2, k.q & 3);
-      k.act.a8 = fresh(uniform(in.a8));
-      k.act.ssg = fresh(uniform(in.ssg));
-      k.act.K = ln.K;
-      k.act.T = T;
-    }
+    if (k.q < 4 * a.L) ok = ok && cw_wait_ge(s, &s.rel, k.q + 1);
   }
-}
-
-template <int T>
-__device__ __forceinline__ void consume(const StepArgs& a, BlockState<T>& s, int c, int lane, Consumer<T>& k, int mq,
-                                        int mtm, int mb, int slot, bool& ok) {
-  if (mq != k.q) advance_to<T>(a, s, c, lane, k, mq, ok);
-  if (mtm != k.tm) {
-    if (k.tm >= 0) flush<T>(s, c, lane, k, ok);
-    k.tm = mtm;
-#pragma unroll
-    for (int t = 0; t < T; ++t) k.acc[t] = 0.0f;
-  }
-  Unit r;
-  unit_from_lds(&s.ring[c][slot][0], lane, r);
-  step_dot4<T>(r, mb, k.act, k.acc);
 }
 
 // After a unit: if the next unit (nq, ntm) of the stream leaves the open
@@ -564,6 +649,38 @@ __device__ __forceinline__ void finish_early(BlockState<T>& s, int c, int lane, 
   }
 }
 
+// Consumes the unit of slot `cur` (the other slot `oth` holds the next one).
+// Entering a new phase: wait for its barrier, then start the activation
+// loads of both slots' units of that phase, and wait for all loads.
+template <int T>
+__device__ __forceinline__ void consume(const StepArgs& a, BlockState<T>& s, int c, int lane, Consumer<T>& k,
+                                        Slot& cur, Slot& oth, int kcur, uint32_t lcur, uint32_t loth, bool& ok) {
+  if (cur.q != k.q) {
+    advance_to<T>(a, s, c, lane, k, cur.q, ok);
+    if (!cur.act) {
+      dma<5, true>(lcur + kUnitBytes, phase_input(a, cur.q >> 2, cur.q & 3) + (size_t)cur.b * kActBytes + lane * 16);
+      cur.act = true;
+    }
+    if (oth.q == cur.q && oth.ops && !oth.act) {
+      dma<5, true>(loth + kUnitBytes, phase_input(a, oth.q >> 2, oth.q & 3) + (size_t)oth.b * kActBytes + lane * 16);
+      oth.act = true;
+    }
+    wait_ops(0);
+  } else {
+    wait_ops(oth.ops);  // this slot's loads are older than the other slot's
+  }
+  if (cur.tm != k.tm) {
+    if (k.tm >= 0) flush<T>(s, c, lane, k, ok);
+    k.tm = cur.tm;
+    acc_zero<T>(k);
+  }
+  lds_u8* sl = as_lds(&s.ring[c][kcur][0]);
+  if constexpr (UseMfma<T>::value)
+    slot_mfma(sl, lane, k.macc);
+  else
+    slot_dot4<T>(sl, cur.b, lane, k.acc);
+}
+
 template <int T>
 __device__ __forceinline__ void compute_wave(const StepArgs& a, BlockState<T>& s, int c, int lane) {
   const int w = blockIdx.x * kCompute + c;
@@ -573,27 +690,26 @@ __device__ __forceinline__ void compute_wave(const StepArgs& a, BlockState<T>& s
   Cursor cur;
   cur.q = 0;
   cursor_settle(a, wt, cur, w);
-  int mq0, mtm0, mb0, mq1, mtm1, mb1;
-  issue(a, wt, cur, w, lane, l0, mq0, mtm0, mb0);
-  bool in1 = issue(a, wt, cur, w, lane, l1, mq1, mtm1, mb1);
+  Slot s0, s1;
+  issue(a, wt, cur, w, lane, l0, -1, s0);
+  issue(a, wt, cur, w, lane, l1, -1, s1);
   Consumer<T> k;
   k.q = -1;
   k.tm = -1;
   k.nflush = 0;
   k.done = 0;
+  acc_zero<T>(k);
   bool ok = true;
   while (ok) {
-    if (mq0 >= qend) break;
-    wait_units(in1 ? 1 : 0);  // slot 0 has landed; slot 1 may still be in flight
-    consume<T>(a, s, c, lane, k, mq0, mtm0, mb0, 0, ok);
-    finish_early<T>(s, c, lane, k, mq1, mtm1, ok);
+    if (s0.q >= qend) break;
+    consume<T>(a, s, c, lane, k, s0, s1, 0, l0, l1, ok);
+    finish_early<T>(s, c, lane, k, s1.q, s1.tm, ok);
     // the slot's LDS reads have completed (their values were used) before it is refilled
-    const bool in0 = issue(a, wt, cur, w, lane, l0, mq0, mtm0, mb0);
-    if (mq1 >= qend) break;
-    wait_units(in0 ? 1 : 0);
-    consume<T>(a, s, c, lane, k, mq1, mtm1, mb1, 1, ok);
-    finish_early<T>(s, c, lane, k, mq0, mtm0, ok);
-    in1 = issue(a, wt, cur, w, lane, l1, mq1, mtm1, mb1);
+    issue(a, wt, cur, w, lane, l0, k.q, s0);
+    if (s1.q >= qend) break;
+    consume<T>(a, s, c, lane, k, s1, s0, 1, l1, l0, ok);
+    finish_early<T>(s, c, lane, k, s0.q, s0.tm, ok);
+    issue(a, wt, cur, w, lane, l1, k.q, s1);
   }
   advance_to<T>(a, s, c, lane, k, qend, ok);  // finishes the phases after the last unit
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load outlives the stream (also after an abort)
@@ -679,7 +795,7 @@ __device__ __forceinline__ void svc_prep(const StepArgs& a, int lane) {
       const float s2 = wave_sum(xv[t] * xv[t]);
       if (lane == 0) st_coh(ss + t, s2);
     }
-    store_q8<T>(act_ref(a, 0, K_X, a.H), tau, lane, xv);
+    store_q8<T>(act_rec(a, 0, K_X), tau, lane, xv);
   }
 }
 
@@ -738,7 +854,7 @@ __device__ __forceinline__ void svc_epilogue(const StepArgs& a, int q, int tau, 
         y[t] = g * u / (1.0f + expf(-g));
       }
     }
-    store_q8<T>(act_ref(a, l, ph == 0 ? K_U : K_H, ph == 0 ? a.P : a.F), tau, lane, y);
+    store_q8<T>(act_rec(a, l, ph == 0 ? K_U : K_H), tau, lane, y);
   } else {
     float xn[T];
 #pragma unroll
@@ -760,9 +876,9 @@ __device__ __forceinline__ void svc_epilogue(const StepArgs& a, int q, int tau, 
       for (int t = 0; t < T; ++t) a.trace[((size_t)l * T + t) * a.H + col] = xn[t];
     }
     if (ph == 1)
-      store_q8<T>(act_ref(a, l, K_X2, a.H), tau, lane, xn);
+      store_q8<T>(act_rec(a, l, K_X2), tau, lane, xn);
     else if (l + 1 < a.L)
-      store_q8<T>(act_ref(a, l + 1, K_X, a.H), tau, lane, xn);
+      store_q8<T>(act_rec(a, l + 1, K_X), tau, lane, xn);
   }
 }
 
@@ -941,7 +1057,7 @@ __device__ __forceinline__ bool lm_better(float va, int ia, float vb, int ib) {
 }
 
 __device__ __forceinline__ void lm_phase(const StepArgs& a, float (*red)[64][16]) {
-  constexpr int NW = kWavesPerBlock, TPT = kBlock / 16, RPP = 64 / TPT;  // threads per row t, rows per thread
+  constexpr int NW = kWavesPerBlock, TPT = 16;  // waves; threads per row t in the scans (256 of the block)
   __shared__ int last;
   __shared__ int fin[16];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
@@ -949,7 +1065,8 @@ __device__ __forceinline__ void lm_phase(const StepArgs& a, float (*red)[64][16]
   const int nc = a.H / 64;
   const int c0 = (nc * w) / NW, c1 = (nc * (w + 1)) / NW;
   const int nblk = (a.V + 63) / 64;
-  const int t_own = threadIdx.x / TPT, part = threadIdx.x % TPT;
+  const bool scan = threadIdx.x < 16 * TPT;  // threads that scan: row t_own, every TPT-th vocabulary row
+  const int t_own = scan ? threadIdx.x / TPT : 0, part = threadIdx.x % TPT;
   float best = 0.0f;
   int bidx = -1;
   for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
@@ -971,7 +1088,7 @@ __device__ __forceinline__ void lm_phase(const StepArgs& a, float (*red)[64][16]
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[w][16 * g + 4 * kq + i][vl] = acc[g][i];
     __syncthreads();
-    for (int r = RPP * part; r < RPP * part + RPP; ++r) {
+    for (int r = part; r < 64 && scan; r += TPT) {
       const int v = v0 + r;
       if (v >= a.V) break;
       float xv = red[0][r][t_own];
@@ -993,7 +1110,7 @@ __device__ __forceinline__ void lm_phase(const StepArgs& a, float (*red)[64][16]
       bidx = oi;
     }
   }
-  if (part == 0) {
+  if (scan && part == 0) {
     st_coh(a.lm_val + (size_t)blockIdx.x * 16 + t_own, best);
     st_coh((float*)a.lm_idx + (size_t)blockIdx.x * 16 + t_own, __builtin_bit_cast(float, bidx));
   }
@@ -1005,7 +1122,7 @@ __device__ __forceinline__ void lm_phase(const StepArgs& a, float (*red)[64][16]
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   best = 0.0f;
   bidx = -1;
-  for (int b = part; b < (int)gridDim.x; b += TPT) {
+  for (int b = part; b < (int)gridDim.x && scan; b += TPT) {
     const float xv = ld_coh(a.lm_val + (size_t)b * 16 + t_own);
     const int iv = ld_coh_i(a.lm_idx + (size_t)b * 16 + t_own);
     if (lm_better(xv, iv, best, bidx)) {
@@ -1022,7 +1139,7 @@ __device__ __forceinline__ void lm_phase(const StepArgs& a, float (*red)[64][16]
       bidx = oi;
     }
   }
-  if (part == 0) fin[t_own] = bidx;
+  if (scan && part == 0) fin[t_own] = bidx;
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int t = 0; t < a.T; ++t) a.out[48 + t] = fin[t];
@@ -1122,9 +1239,9 @@ struct StepLayout {
   int grid, Wc;
   int cmax[4];
   size_t off_ctrl, n_ctrl;  // zeroed before each launch: barrier, tickets
-  size_t off_out, off_stamps, off_tickets, off_lmticket, off_table, off_a8, off_ssg, off_ss, off_part, off_frag, off_lmv,
+  size_t off_out, off_stamps, off_tickets, off_lmticket, off_table, off_act, off_ss, off_part, off_frag, off_lmv,
       off_lmi, total;
-  size_t a8_layer, ssg_layer, a8_off[4], ssg_off[4];
+  size_t act_layer, act_off[4];
 };
 
 int host_wave_of(long S, int W, long p) { return (int)(((p + 1) * (long)W - 1) / S); }
@@ -1159,17 +1276,13 @@ StepLayout layout(const mk_stack* st, int T) {
   const int nsbs[4] = {d.hidden / 256, d.proj / 256, d.hidden / 256, d.ffn / 256};
   for (int i = 0; i < 4; ++i) y.cmax[i] = y.Wc ? plan_cmax((long)ntiles[i] * nms[i], nsbs[i], y.Wc) : 1;
   // (each count must fit a byte of the packed kernel argument)
-  y.a8_off[K_X] = 0;
-  y.a8_off[K_U] = a256((size_t)T * d.hidden);
-  y.a8_off[K_X2] = y.a8_off[K_U] + a256((size_t)T * d.proj);
-  y.a8_off[K_H] = y.a8_off[K_X2] + a256((size_t)T * d.hidden);
-  y.a8_layer = y.a8_off[K_H] + a256((size_t)T * d.ffn);
-  auto sgb = [](int K) { return a256((size_t)(K / 32) * kTPad * 8); };
-  y.ssg_off[K_X] = 0;
-  y.ssg_off[K_U] = sgb(d.hidden);
-  y.ssg_off[K_X2] = y.ssg_off[K_U] + sgb(d.proj);
-  y.ssg_off[K_H] = y.ssg_off[K_X2] + sgb(d.hidden);
-  y.ssg_layer = y.ssg_off[K_H] + sgb(d.ffn);
+  // activation records: kActBytes per superblock of each input (x, u, x2, h)
+  auto rec = [](int K) { return (size_t)(K / 256) * kActBytes; };
+  y.act_off[K_X] = 0;
+  y.act_off[K_U] = rec(d.hidden);
+  y.act_off[K_X2] = y.act_off[K_U] + rec(d.proj);
+  y.act_off[K_H] = y.act_off[K_X2] + rec(d.hidden);
+  y.act_layer = y.act_off[K_H] + rec(d.ffn);
   size_t o = 0;
   y.off_ctrl = o;
   o += 256;  // barrier counter
@@ -1184,10 +1297,8 @@ StepLayout layout(const mk_stack* st, int T) {
   o += a256(sizeof(uint64_t) * kMaxStamps);
   y.off_table = o;
   o += a256(sizeof(LayerW) * d.n_layers);
-  y.off_a8 = o;
-  o += y.a8_layer * d.n_layers;
-  y.off_ssg = o;
-  o += y.ssg_layer * d.n_layers;
+  y.off_act = o;
+  o += y.act_layer * d.n_layers;
   y.off_ss = o;
   o += a256((size_t)(2 * d.n_layers + 1) * (d.hidden / 64) * 16 * 4);
   y.off_part = o;
@@ -1371,13 +1482,10 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
   a.out = (int32_t*)(w8 + y.off_out);
   a.err = a.out;
   a.stamps = (uint64_t*)(w8 + y.off_stamps);
-  a.a8 = (int8_t*)(w8 + y.off_a8);
-  a.ssg = (float*)(w8 + y.off_ssg);
-  a.a8_layer = y.a8_layer;
-  a.ssg_layer = y.ssg_layer / 4;
+  a.act = w8 + y.off_act;
+  a.act_layer = y.act_layer;
   for (int i = 0; i < 4; ++i) {
-    a.a8_off[i] = y.a8_off[i];
-    a.ssg_off[i] = y.ssg_off[i] / 4;
+    a.act_off[i] = y.act_off[i];
   }
   a.ss = (float*)(w8 + y.off_ss);
   a.part = (float*)(w8 + y.off_part);
