@@ -60,9 +60,11 @@ constexpr int kMaxLayers = 128;
 constexpr int kTicketTiles = 512;  // tickets per phase instance (max n_out / 64)
 constexpr int kTicketStride = 16;  // counters 64 B apart
 constexpr int kGdnHeadsPerLayer = 32;
-constexpr int kBlock = 320;
+constexpr int kBlock = 384;
 constexpr int kWavesPerBlock = kBlock / 64;
-constexpr int kCompute = kWavesPerBlock - 1;  // compute waves per block (one per SIMD); the last wave serves
+constexpr int kCompute = 4;        // compute waves per block (one per SIMD): waves 0..3
+constexpr int kServiceWave = 4;    // partials, tickets, epilogues, barrier
+constexpr int kGdnWave = 5;        // the block's Gated DeltaNet jobs
 // Activation record of one GEMV input, per superblock b (256 values of K),
 // kActBytes bytes: the int8 rows in the order the matrix-core A operand reads
 // them ([sub-block j][octet q][row t][8 B], rows 0..15, rows >= T zero), then
@@ -196,6 +198,7 @@ struct BlockState {
   int done[kCompute];
   int rel;
   int abort;
+  int gdn_done;  // the block's Gated DeltaNet jobs have finished
 };
 
 // Waits until *p >= v.  A wait that exceeds the bound (or sees another wave
@@ -834,16 +837,19 @@ __device__ __forceinline__ void sum_partials(const StepArgs& a, const Line& ln, 
   }
 }
 
+// The epilogue of tile tau of phase q, run by the tile's owner once every
+// contribution is in: r[t] (RMSNorm factors of the phase input, phases 0
+// and 2) and xo[t] (the residual rows of the tile, phases 1 and 3) were
+// loaded at the start of the phase.
 template <int T>
-__device__ __forceinline__ void svc_epilogue(const StepArgs& a, int q, int tau, int lane) {
+__device__ __forceinline__ void svc_epilogue(const StepArgs& a, int q, int tau, int lane, const float (&r)[T],
+                                             const float (&xo)[T]) {
   const int l = q >> 2, ph = q & 3;
   const Line ln = line_of(a, ph);
   float v0[T], v1[T];
   sum_partials<T>(a, ln, ph, tau, lane, v0, v1);
   const int col = tau * 64 + lane;
   if (ph == 0 || ph == 2) {
-    float r[T];
-    rnorm_rows<T>(a, ph == 0 ? 2 * l : 2 * l + 1, lane, r);
     float y[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -858,10 +864,8 @@ __device__ __forceinline__ void svc_epilogue(const StepArgs& a, int q, int tau, 
   } else {
     float xn[T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) xn[t] = ld_coh(a.x + (size_t)t * a.H + col);
-#pragma unroll
     for (int t = 0; t < T; ++t) {
-      xn[t] += v0[t];
+      xn[t] = xo[t] + v0[t];
       st_coh(a.x + (size_t)t * a.H + col, xn[t]);
     }
     const int ss_idx = ph == 1 ? 2 * l + 1 : 2 * l + 2;
@@ -882,23 +886,39 @@ __device__ __forceinline__ void svc_epilogue(const StepArgs& a, int q, int tau, 
   }
 }
 
-// One GEMV phase seen from the service wave of block b: wait for the compute
-// waves' mailboxes of each (tile, matrix) the block touches, sum them in wave
-// order, store the block partial, then take the tiles' tickets (one atomic
-// per tile, all in flight together) and run the epilogues this block won.
+// One GEMV phase seen from the service wave of block b.  Tiles are owned by
+// blocks in equal shares (tile tau by block tau * G / n_tiles), whatever
+// blocks contribute to them.  At the start of the phase the owner loads what
+// its epilogues need besides the partials (row factors or residual rows).
+// Then: wait for the compute waves' mailboxes of each (tile, matrix) the
+// block touches, sum them in wave order, store the block partial, count the
+// contributions on the tiles' tickets (one atomic per tile), and, as owner,
+// wait for each owned tile's count to complete and run its epilogue.
 template <int T>
 __device__ __forceinline__ bool svc_phase(const StepArgs& a, BlockState<T>& s, int q, int lane, bool ok) {
   const int l = q >> 2, ph = q & 3;
-  if (ph == 2 && a.n_agents > 0 && layer_is_gdn(a, l)) {
-    // the block's share of this layer's Gated DeltaNet half-head jobs runs
-    // while the gate/up weights stream
-    const long nj = (long)a.n_agents * kGdnHeadsPerLayer * 2;
-    for (long j = nj * blockIdx.x / gridDim.x; j < nj * (blockIdx.x + 1) / gridDim.x; ++j) gdn_job(a, l, j, lane);
-  }
   const Line ln = line_of(a, ph);
+  const int ntile = ln.N / 64;
+  const int own0 = (int)((long)ntile * blockIdx.x / gridDim.x), own1 = (int)((long)ntile * (blockIdx.x + 1) / gridDim.x);
+  float r[T], xo[2][T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) r[t] = xo[0][t] = xo[1][t] = 0.0f;
+  if (own0 < own1) {
+    if (ph == 0 || ph == 2) {
+      rnorm_rows<T>(a, ph == 0 ? 2 * l : 2 * l + 1, lane, r);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (own0 + i < own1)
+#pragma unroll
+          for (int t = 0; t < T; ++t) xo[i][t] = ld_coh(a.x + (size_t)t * a.H + (own0 + i) * 64 + lane);
+    }
+  }
   const int bw0 = blockIdx.x * kCompute;
   const int ub0 = stretch_lo(ln.S, ln.W, bw0), ub1 = stretch_lo(ln.S, ln.W, bw0 + kCompute);
-  if (ub0 >= ub1 || !ok) return ok;
+  if (!ok) return ok;
+  unsigned* tk = a.tickets + ((size_t)l * 4 + ph) * kTicketTiles * kTicketStride;
+  if (ub0 < ub1) {
   const int tm0 = ub0 / ln.nsb, tm1 = (ub1 - 1) / ln.nsb;
   const int cm = (a.cmax4 >> (8 * ph)) & 255;
   const int bfirst_base = blockIdx.x;
@@ -942,30 +962,44 @@ __device__ __forceinline__ bool svc_phase(const StepArgs& a, BlockState<T>& s, i
 #pragma unroll
     for (int t = 0; t < T; ++t) st_coh(dst + t * 64, v[t]);
   }
-  // tickets: lane i takes tile tau0 + i for all of this block's (tile, matrix)
-  // pairs of it; the contribution that completes a tile's count wins it
+  // contributions: lane i counts this block's (tile, matrix) pairs of tile tau0 + i
   const int tau0 = tm0 / ln.nm, tau1 = tm1 / ln.nm;
-  unsigned* tk = a.tickets + ((size_t)l * 4 + ph) * kTicketTiles * kTicketStride;
-  for (int base = tau0; base <= tau1; base += 64) {
-    const int tau = base + lane;
-    bool won = false;
-    if (tau <= tau1) {
-      int cnt = 0, expect = 0;
-      for (int m = 0; m < ln.nm; ++m) {
-        const int tm = tau * ln.nm + m;
-        if (tm >= tm0 && tm <= tm1) ++cnt;
-        expect += n_blocks(ln, tm);
+  stores_done();
+  for (int tau = tau0 + lane; tau <= tau1; tau += 64) {
+    int cnt = 0;
+    for (int m = 0; m < ln.nm; ++m) {
+      const int tm = tau * ln.nm + m;
+      if (tm >= tm0 && tm <= tm1) ++cnt;
+    }
+    __hip_atomic_fetch_add(tk + (size_t)tau * kTicketStride, (unsigned)cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  }
+  // owned tiles: wait for all contributions, then the epilogue
+  for (int tau = own0; tau < own1; ++tau) {
+    int expect = 0;
+    for (int m = 0; m < ln.nm; ++m) expect += n_blocks(ln, tau * ln.nm + m);
+    unsigned spins = 0;
+    while ((int)__hip_atomic_load(tk + (size_t)tau * kTicketStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < expect) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit || lds_ld(&s.abort)) {
+        lds_st(&s.abort, 1);
+        if (lane == 0) atomicOr(a.err, 1);
+        return false;
       }
-      const unsigned prev = ticket_add(tk + (size_t)tau * kTicketStride, (unsigned)cnt);
-      won = (int)prev + cnt == expect;
     }
-    uint64_t wm = __ballot(won);
-    while (wm) {
-      const int i = __builtin_ctzll(wm);
-      wm &= wm - 1;
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      svc_epilogue<T>(a, q, uniform(base + i), lane);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    float xt[T];
+    if (tau < own0 + 2) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) xt[t] = tau == own0 ? xo[0][t] : xo[1][t];
+    } else if (ph == 1 || ph == 3) {  // more owned tiles than prefetched (small grids)
+#pragma unroll
+      for (int t = 0; t < T; ++t) xt[t] = ld_coh(a.x + (size_t)t * a.H + tau * 64 + lane);
+    } else {
+#pragma unroll
+      for (int t = 0; t < T; ++t) xt[t] = 0.0f;
     }
+    svc_epilogue<T>(a, q, uniform(tau), lane, r, xt);
   }
   return true;
 }
@@ -1008,7 +1042,22 @@ __device__ __forceinline__ void service_wave(const StepArgs& a, BlockState<T>& s
   float r[T];
   rnorm_rows<T>(a, 2 * a.L, lane, r);
   svc_lm_prep<T>(a, lane, r);
+  // the lm phase rewrites the accept lengths that the Gated DeltaNet jobs read
+  if (!wait_ge(a, s, &s.gdn_done, 1)) return;
   svc_barrier<T>(a, s, 4 * a.L + 1, 4 * a.L, lane, ok);
+}
+
+// The block's share of every GDN layer's half-head jobs, in layer order.
+// Nothing in the step consumes their outputs, so they run beside the layer
+// pipeline instead of inside one of its phases; the block's last barrier
+// waits for them (see service_wave).
+__device__ __forceinline__ void gdn_wave(const StepArgs& a, int lane) {
+  if (a.n_agents <= 0) return;
+  const long nj = (long)a.n_agents * kGdnHeadsPerLayer * 2;
+  const long j0 = nj * blockIdx.x / gridDim.x, j1 = nj * (blockIdx.x + 1) / gridDim.x;
+  for (int l = 0; l < a.L; ++l)
+    if (layer_is_gdn(a, l))
+      for (long j = j0; j < j1; ++j) gdn_job(a, l, j, lane);
 }
 
 // One 64-wide hidden chunk of 64 vocabulary rows: the weight fragments of
@@ -1171,13 +1220,19 @@ __global__ __launch_bounds__(kBlock) void k_decode_step(StepArgs a) {
   if (threadIdx.x == 0) {
     s.rel = 0;
     s.abort = 0;
+    s.gdn_done = 0;
     if (blockIdx.x == 0) a.stamps[0] = wall_clock64();
   }
   __syncthreads();
-  if (wib < kCompute)
+  if (wib < kCompute) {
     compute_wave<T>(a, s, wib, lane);
-  else
+  } else if (wib == kServiceWave) {
     service_wave<T>(a, s, lane);
+  } else {
+    gdn_wave(a, lane);
+    stores_done();
+    if (lane == 0) lds_st(&s.gdn_done, 1);
+  }
   // every wave of the block takes part in the lm phase once lm_prep is done
   if (!wait_ge(a, s, &s.rel, 4 * a.L + 2)) return;
   static_assert(sizeof(s.ring) >= sizeof(float) * kWavesPerBlock * 64 * 16, "lm reduction does not fit the ring");
