@@ -60,11 +60,14 @@ constexpr int kMaxLayers = 128;
 constexpr int kTicketTiles = 512;  // tickets per phase instance (max n_out / 64)
 constexpr int kTicketStride = 16;  // counters 64 B apart
 constexpr int kGdnHeadsPerLayer = 32;
-constexpr int kBlock = 384;
+constexpr int kBlock = 448;
 constexpr int kWavesPerBlock = kBlock / 64;
 constexpr int kCompute = 4;        // compute waves per block (one per SIMD): waves 0..3
-constexpr int kServiceWave = 4;    // partials, tickets, epilogues, barrier
+constexpr int kServiceWave = 4;    // partials, tickets, epilogues
 constexpr int kGdnWave = 5;        // the block's Gated DeltaNet jobs
+constexpr int kWatchWave = 6;      // opens phases when their inputs are complete
+constexpr int kRdySlots = 8;       // finished-tile counters per producer phase (block b adds to b % 8)
+constexpr int kRdyStride = 32;     // u32 between counters (one 128-B line each)
 // Activation record of one GEMV input, per superblock b (256 values of K),
 // kActBytes bytes: the int8 rows in the order the matrix-core A operand reads
 // them ([sub-block j][octet q][row t][8 B], rows 0..15, rows >= T zero), then
@@ -107,6 +110,8 @@ struct StepArgs {
   int* err;
   unsigned* tickets;
   unsigned* lm_ticket;
+  unsigned* rdy;        // [4L + 1][kRdySlots][kRdyStride]: tiles finished per producer phase (prep, then phase q + 1)
+  size_t part_half;     // floats per partial buffer (phases alternate between two)
   uint8_t* act;         // activation records, [layer][kind] (see kActBytes)
   size_t act_layer;     // bytes per layer
   size_t act_off[4];    // bytes from the layer's first record, per kind
@@ -160,6 +165,26 @@ __device__ __forceinline__ unsigned ticket_add(unsigned* p, unsigned n = 1u) {
   return __hip_atomic_fetch_add(p, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Device-coherent reads through the scalar unit (glc): they bypass the
+// scalar cache and, unlike vector loads, do not queue behind the weight
+// loads the compute waves keep in flight on the same CU.  The address is
+// wave-uniform.
+__device__ __forceinline__ uint64_t sgpr_addr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ unsigned sld1(const unsigned* p) {
+  unsigned v;
+  asm volatile("s_load_dword %0, %1, 0x0 glc\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(sgpr_addr(p)) : "memory");
+  return v;
+}
+__device__ __forceinline__ u32x8 sld8(const unsigned* p) {
+  u32x8 v;
+  asm volatile("s_load_dwordx8 %0, %1, 0x0 glc\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(sgpr_addr(p)) : "memory");
+  return v;
+}
+
 // LDS words shared by the waves of a block.  The LDS executes each wave's
 // accesses in order, so only the compiler must keep program order (the empty
 // asm statements); no wait on the vector-memory counter is involved, which
@@ -181,7 +206,8 @@ __device__ __forceinline__ void lds_st(int* p, int v) {
 // partial sums [t][64] of one (tile, matrix) with its tag ((phase + 1) << 16 |
 // tile-matrix), 0 when free.  done[c] = phases finished by compute wave c;
 // rel = grid barriers completed.  wt: the per-layer weight pointers (read by
-// the compute waves at every phase change).  After the last GEMV phase the ring area
+// the compute waves at every phase change).  rel = phases opened by the watcher wave
+// (phase q is open once every tile of its input is finished).  After the last GEMV phase the ring area
 // holds the lm phase's cross-wave reduction.
 constexpr int kSlots = 2;
 template <int T>
@@ -311,6 +337,12 @@ __device__ __forceinline__ void store_q8(uint8_t* rec, int tau, int lane, const 
     st_coh(sc + j * 16 + T + e, 0.0f);
     st_coh(sc + 128 + j * 16 + T + e, 0.0f);
   }
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
 }
 
 // Sum over the 64 lanes (fixed butterfly order).
@@ -757,7 +789,8 @@ __device__ __forceinline__ void gdn_job(const StepArgs& a, int layer, long j, in
 // its block (rel = k + 1).  The counter only grows within a launch (zeroed
 // before it), so barrier k waits for (k + 1) * gridDim.x arrivals.
 template <int T>
-__device__ __forceinline__ bool svc_barrier(const StepArgs& a, BlockState<T>& s, int k, int done, int lane, bool ok) {
+__device__ __forceinline__ bool svc_barrier(const StepArgs& a, BlockState<T>& s, int k, int done, int lane, bool ok,
+                                            int rel_val) {
   for (int c = 0; c < kCompute && ok; ++c) ok = wait_ge(a, s, &s.done[c], done);
   if (!ok) return false;
   const unsigned target = (unsigned)(k + 1) * gridDim.x;
@@ -774,14 +807,14 @@ __device__ __forceinline__ bool svc_barrier(const StepArgs& a, BlockState<T>& s,
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    if (blockIdx.x == 0 && k + 1 < kMaxStamps) a.stamps[k + 1] = wall_clock64();
+    if (blockIdx.x == 0 && rel_val < kMaxStamps) a.stamps[rel_val] = wall_clock64();
   }
   fail = __shfl(fail, 0, 64);
   if (fail) {
     lds_st(&s.abort, 1);
     return false;
   }
-  if (lane == 0) lds_st(&s.rel, k + 1);
+  if (lane == 0) lds_st(&s.rel, rel_val);
   return true;
 }
 
@@ -800,13 +833,20 @@ __device__ __forceinline__ void svc_prep(const StepArgs& a, int lane) {
     }
     store_q8<T>(act_rec(a, 0, K_X), tau, lane, xv);
   }
+  const int n = ntH > (int)blockIdx.x ? (ntH - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  if (n) {
+    stores_done();
+    if (lane == 0) __hip_atomic_fetch_add(a.rdy + (blockIdx.x % kRdySlots) * kRdyStride, (unsigned)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // Sum of the block partials of (tile, matrix) pairs tau*nm + m, m < nm, in
 // block order; all loads of up to kPartBatch partials are issued together.
 template <int T>
-__device__ __forceinline__ void sum_partials(const StepArgs& a, const Line& ln, int ph, int tau, int lane,
+__device__ __forceinline__ void sum_partials(const StepArgs& a, const Line& ln, int q, int tau, int lane,
                                              float (&v0)[T], float (&v1)[T]) {
+  const int ph = q & 3;
+  const float* part = a.part + (size_t)(q & 1) * a.part_half;
   const int tm0 = tau * ln.nm;
   const int n0 = uniform(n_blocks(ln, tm0));
   const int n1 = ln.nm == 2 ? uniform(n_blocks(ln, tm0 + 1)) : 0;
@@ -819,7 +859,7 @@ __device__ __forceinline__ void sum_partials(const StepArgs& a, const Line& ln, 
     for (int i = 0; i < kPartBatch; ++i) {
       const int e = e0 + i < n ? e0 + i : n - 1;  // in-range address; extra values are not added
       const int m = e < n0 ? 0 : 1, r = e < n0 ? e : e - n0;
-      const float* p = a.part + ((size_t)((tm0 + m) * cm + r) * T) * 64 + lane;
+      const float* p = part + ((size_t)((tm0 + m) * cm + r) * T) * 64 + lane;
 #pragma unroll
       for (int t = 0; t < T; ++t) tmp[i][t] = ld_coh(p + t * 64);
     }
@@ -847,7 +887,7 @@ __device__ __forceinline__ void svc_epilogue(const StepArgs& a, int q, int tau, 
   const int l = q >> 2, ph = q & 3;
   const Line ln = line_of(a, ph);
   float v0[T], v1[T];
-  sum_partials<T>(a, ln, ph, tau, lane, v0, v1);
+  sum_partials<T>(a, ln, q, tau, lane, v0, v1);
   const int col = tau * 64 + lane;
   if (ph == 0 || ph == 2) {
     float y[T];
@@ -903,6 +943,8 @@ __device__ __forceinline__ bool svc_phase(const StepArgs& a, BlockState<T>& s, i
   float r[T], xo[2][T];
 #pragma unroll
   for (int t = 0; t < T; ++t) r[t] = xo[0][t] = xo[1][t] = 0.0f;
+  // the row factors need every tile of the phase input (its sums of squares)
+  if (!wait_ge(a, s, &s.rel, q + 1)) return false;
   if (own0 < own1) {
     if (ph == 0 || ph == 2) {
       rnorm_rows<T>(a, ph == 0 ? 2 * l : 2 * l + 1, lane, r);
@@ -958,7 +1000,7 @@ __device__ __forceinline__ bool svc_phase(const StepArgs& a, BlockState<T>& s, i
       if (lane == 0) lds_st(&s.tag[c][k], 0);
     }
     const int rank = bfirst_base - first_block(ln, tm);
-    float* dst = a.part + ((size_t)(tm * cm + rank) * T) * 64 + lane;
+    float* dst = a.part + (size_t)(q & 1) * a.part_half + ((size_t)(tm * cm + rank) * T) * 64 + lane;
 #pragma unroll
     for (int t = 0; t < T; ++t) st_coh(dst + t * 64, v[t]);
   }
@@ -979,7 +1021,7 @@ __device__ __forceinline__ bool svc_phase(const StepArgs& a, BlockState<T>& s, i
     int expect = 0;
     for (int m = 0; m < ln.nm; ++m) expect += n_blocks(ln, tau * ln.nm + m);
     unsigned spins = 0;
-    while ((int)__hip_atomic_load(tk + (size_t)tau * kTicketStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < expect) {
+    while ((int)sld1(tk + (size_t)tau * kTicketStride) < expect) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins > kSpinLimit || lds_ld(&s.abort)) {
         lds_st(&s.abort, 1);
@@ -1000,6 +1042,13 @@ __device__ __forceinline__ bool svc_phase(const StepArgs& a, BlockState<T>& s, i
       for (int t = 0; t < T; ++t) xt[t] = 0.0f;
     }
     svc_epilogue<T>(a, q, uniform(tau), lane, r, xt);
+  }
+  // the owned tiles' outputs are complete: count them for the watchers
+  if (own0 < own1) {
+    stores_done();
+    if (lane == 0)
+      __hip_atomic_fetch_add(a.rdy + ((size_t)(q + 1) * kRdySlots + blockIdx.x % kRdySlots) * kRdyStride, (unsigned)(own1 - own0),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   return true;
 }
@@ -1033,18 +1082,44 @@ __device__ __forceinline__ void svc_lm_prep(const StepArgs& a, int lane, const f
 template <int T>
 __device__ __forceinline__ void service_wave(const StepArgs& a, BlockState<T>& s, int lane) {
   svc_prep<T>(a, lane);
-  bool ok = svc_barrier<T>(a, s, 0, 0, lane, true);
-  for (int q = 0; q < 4 * a.L && ok; ++q) {
-    ok = svc_phase<T>(a, s, q, lane, ok);
-    ok = ok && svc_barrier<T>(a, s, q + 1, q + 1, lane, ok);
-  }
-  if (!ok) return;
+  bool ok = true;
+  for (int q = 0; q < 4 * a.L && ok; ++q) ok = svc_phase<T>(a, s, q, lane, ok);
+  // lm_prep needs the final residual: every tile of the last phase
+  if (!ok || !wait_ge(a, s, &s.rel, 4 * a.L + 1)) return;
   float r[T];
   rnorm_rows<T>(a, 2 * a.L, lane, r);
   svc_lm_prep<T>(a, lane, r);
   // the lm phase rewrites the accept lengths that the Gated DeltaNet jobs read
   if (!wait_ge(a, s, &s.gdn_done, 1)) return;
-  svc_barrier<T>(a, s, 4 * a.L + 1, 4 * a.L, lane, ok);
+  // the one grid barrier of the step: every block's hidden fragments are in
+  svc_barrier<T>(a, s, 0, 4 * a.L, lane, ok, 4 * a.L + 2);
+}
+
+// Opens the phases of the block in order: phase q (and, as q = 4L, lm_prep)
+// opens once the producer of its input has finished every tile, counted on
+// the kRdySlots counters of that producer phase.
+template <int T>
+__device__ __forceinline__ void watch_wave(const StepArgs& a, BlockState<T>& s, int lane) {
+  const int qn = 4 * a.L;
+  for (int q = 0; q <= qn; ++q) {
+    const int need = q == 0 || q == qn ? a.H / 64 : line_of(a, q & 3).K / 64;
+    const unsigned* c = a.rdy + (size_t)q * kRdySlots * kRdyStride;
+    unsigned spins = 0;
+    while (true) {
+      // lanes 0..7 read the counters (one line each)
+      const unsigned v = lane < kRdySlots ? (unsigned)ld_coh_i((const int*)c + lane * kRdyStride) : 0u;
+      const unsigned n = (unsigned)wave_sum_i((int)v);
+      if ((int)n >= need) break;
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit / 8 || lds_ld(&s.abort)) {
+        lds_st(&s.abort, 1);
+        if (lane == 0) atomicOr(a.err, 1);
+        return;
+      }
+    }
+    if (blockIdx.x == 0 && lane == 0 && q + 1 < kMaxStamps) a.stamps[q + 1] = wall_clock64();
+    if (lane == 0) lds_st(&s.rel, q + 1);
+  }
 }
 
 // The block's share of every GDN layer's half-head jobs, in layer order.
@@ -1228,6 +1303,8 @@ __global__ __launch_bounds__(kBlock) void k_decode_step(StepArgs a) {
     compute_wave<T>(a, s, wib, lane);
   } else if (wib == kServiceWave) {
     service_wave<T>(a, s, lane);
+  } else if (wib == kWatchWave) {
+    watch_wave<T>(a, s, lane);
   } else {
     gdn_wave(a, lane);
     stores_done();
@@ -1294,6 +1371,7 @@ struct StepLayout {
   int grid, Wc;
   int cmax[4];
   size_t off_ctrl, n_ctrl;  // zeroed before each launch: barrier, tickets
+  size_t off_rdy, part_half;
   size_t off_out, off_stamps, off_tickets, off_lmticket, off_table, off_act, off_ss, off_part, off_frag, off_lmv,
       off_lmi, total;
   size_t act_layer, act_off[4];
@@ -1343,6 +1421,8 @@ StepLayout layout(const mk_stack* st, int T) {
   o += 256;  // barrier counter
   y.off_lmticket = o;
   o += 256;
+  y.off_rdy = o;
+  o += a256((size_t)(4 * d.n_layers + 1) * kRdySlots * kRdyStride * 4);
   y.off_tickets = o;
   o += a256((size_t)d.n_layers * 4 * kTicketTiles * kTicketStride * 4);
   y.n_ctrl = o - y.off_ctrl;
@@ -1359,7 +1439,8 @@ StepLayout layout(const mk_stack* st, int T) {
   y.off_part = o;
   size_t part = 0;
   for (int i = 0; i < 4; ++i) part = std::max(part, (size_t)ntiles[i] * nms[i] * y.cmax[i] * T * 64 * 4);
-  o += a256(part);
+  y.part_half = a256(part) / 4;  // floats; two buffers, by phase parity
+  o += 2 * a256(part);
   y.off_frag = o;
   o += a256((size_t)(d.hidden / 64) * 64 * 32 * 2);
   y.off_lmv = o;
@@ -1534,6 +1615,8 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
   a.bar = (unsigned*)(w8 + y.off_ctrl);
   a.lm_ticket = (unsigned*)(w8 + y.off_lmticket);
   a.tickets = (unsigned*)(w8 + y.off_tickets);
+  a.rdy = (unsigned*)(w8 + y.off_rdy);
+  a.part_half = y.part_half;
   a.out = (int32_t*)(w8 + y.off_out);
   a.err = a.out;
   a.stamps = (uint64_t*)(w8 + y.off_stamps);
