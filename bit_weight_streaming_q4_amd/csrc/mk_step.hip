@@ -111,6 +111,7 @@ struct StepArgs {
   unsigned* tickets;
   unsigned* lm_ticket;
   unsigned* rdy;        // [4L + 1][kRdySlots][kRdyStride]: tiles finished per producer phase (prep, then phase q + 1)
+  unsigned* open;       // [grid][kRdyStride]: phases opened for block b (written by block 0's watcher)
   size_t part_half;     // floats per partial buffer (phases alternate between two)
   uint8_t* act;         // activation records, [layer][kind] (see kActBytes)
   size_t act_layer;     // bytes per layer
@@ -178,6 +179,25 @@ __device__ __forceinline__ unsigned sld1(const unsigned* p) {
   unsigned v;
   asm volatile("s_load_dword %0, %1, 0x0 glc\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(sgpr_addr(p)) : "memory");
   return v;
+}
+// Sum of the 8 words p[0], p[S], ..., p[7 S] (S = kRdyStride words), all
+// loads in flight together.
+__device__ __forceinline__ unsigned sld_sum8(const unsigned* p) {
+  unsigned v0, v1, v2, v3, v4, v5, v6, v7;
+  asm volatile(
+      "s_load_dword %0, %8, 0x0 glc\n\t"
+      "s_load_dword %1, %8, 0x80 glc\n\t"
+      "s_load_dword %2, %8, 0x100 glc\n\t"
+      "s_load_dword %3, %8, 0x180 glc\n\t"
+      "s_load_dword %4, %8, 0x200 glc\n\t"
+      "s_load_dword %5, %8, 0x280 glc\n\t"
+      "s_load_dword %6, %8, 0x300 glc\n\t"
+      "s_load_dword %7, %8, 0x380 glc\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(v0), "=&s"(v1), "=&s"(v2), "=&s"(v3), "=&s"(v4), "=&s"(v5), "=&s"(v6), "=&s"(v7)
+      : "s"(sgpr_addr(p))
+      : "memory");
+  return v0 + v1 + v2 + v3 + v4 + v5 + v6 + v7;
 }
 __device__ __forceinline__ u32x8 sld8(const unsigned* p) {
   u32x8 v;
@@ -1096,20 +1116,45 @@ __device__ __forceinline__ void service_wave(const StepArgs& a, BlockState<T>& s
 }
 
 // Opens the phases of the block in order: phase q (and, as q = 4L, lm_prep)
-// opens once the producer of its input has finished every tile, counted on
-// the kRdySlots counters of that producer phase.
+// opens once the producer of its input has finished every tile.  Block 0's
+// watcher is the only reader of the finished-tile counters: when a producer
+// phase is complete it writes the number of open phases into every block's
+// own line, which that block's watcher alone polls.  (Many readers polling one
+// line slow down its readers and its writers alike.)
 template <int T>
 __device__ __forceinline__ void watch_wave(const StepArgs& a, BlockState<T>& s, int lane) {
   const int qn = 4 * a.L;
-  for (int q = 0; q <= qn; ++q) {
-    const int need = q == 0 || q == qn ? a.H / 64 : line_of(a, q & 3).K / 64;
-    const unsigned* c = a.rdy + (size_t)q * kRdySlots * kRdyStride;
-    unsigned spins = 0;
-    while (true) {
-      // lanes 0..7 read the counters (one line each)
-      const unsigned v = lane < kRdySlots ? (unsigned)ld_coh_i((const int*)c + lane * kRdyStride) : 0u;
-      const unsigned n = (unsigned)wave_sum_i((int)v);
-      if ((int)n >= need) break;
+  unsigned spins = 0;
+  if (blockIdx.x == 0) {
+    for (int q = 0; q <= qn; ++q) {
+      const int need = q == 0 || q == qn ? a.H / 64 : line_of(a, q & 3).K / 64;
+      const unsigned* c = a.rdy + (size_t)q * kRdySlots * kRdyStride;
+      while (true) {
+        static_assert(kRdySlots == 8 && kRdyStride == 32, "sld_sum8 reads 8 words 128 B apart");
+        const unsigned n = sld_sum8(c);
+        if ((int)n >= need) break;
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit / 8 || lds_ld(&s.abort)) {
+          lds_st(&s.abort, 1);
+          if (lane == 0) atomicOr(a.err, 1);
+          return;
+        }
+      }
+      if (lane == 0 && q + 1 < kMaxStamps) a.stamps[q + 1] = wall_clock64();
+      for (int b = lane; b < (int)gridDim.x; b += 64)
+        __hip_atomic_store(a.open + (size_t)b * kRdyStride, (unsigned)(q + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) lds_st(&s.rel, q + 1);
+    }
+  } else {
+    const unsigned* mine = a.open + (size_t)blockIdx.x * kRdyStride;
+    int rel = 0;
+    while (rel <= qn) {
+      const int v = (int)sld1(mine);
+      if (v > rel) {
+        rel = v;
+        if (lane == 0) lds_st(&s.rel, rel);
+        continue;
+      }
       __builtin_amdgcn_s_sleep(1);
       if (++spins > kSpinLimit / 8 || lds_ld(&s.abort)) {
         lds_st(&s.abort, 1);
@@ -1117,8 +1162,6 @@ __device__ __forceinline__ void watch_wave(const StepArgs& a, BlockState<T>& s, 
         return;
       }
     }
-    if (blockIdx.x == 0 && lane == 0 && q + 1 < kMaxStamps) a.stamps[q + 1] = wall_clock64();
-    if (lane == 0) lds_st(&s.rel, q + 1);
   }
 }
 
@@ -1371,7 +1414,7 @@ struct StepLayout {
   int grid, Wc;
   int cmax[4];
   size_t off_ctrl, n_ctrl;  // zeroed before each launch: barrier, tickets
-  size_t off_rdy, part_half;
+  size_t off_rdy, off_open, part_half;
   size_t off_out, off_stamps, off_tickets, off_lmticket, off_table, off_act, off_ss, off_part, off_frag, off_lmv,
       off_lmi, total;
   size_t act_layer, act_off[4];
@@ -1423,6 +1466,8 @@ StepLayout layout(const mk_stack* st, int T) {
   o += 256;
   y.off_rdy = o;
   o += a256((size_t)(4 * d.n_layers + 1) * kRdySlots * kRdyStride * 4);
+  y.off_open = o;
+  o += a256((size_t)std::max(y.grid, 1) * kRdyStride * 4);
   y.off_tickets = o;
   o += a256((size_t)d.n_layers * 4 * kTicketTiles * kTicketStride * 4);
   y.n_ctrl = o - y.off_ctrl;
@@ -1616,6 +1661,7 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
   a.lm_ticket = (unsigned*)(w8 + y.off_lmticket);
   a.tickets = (unsigned*)(w8 + y.off_tickets);
   a.rdy = (unsigned*)(w8 + y.off_rdy);
+  a.open = (unsigned*)(w8 + y.off_open);
   a.part_half = y.part_half;
   a.out = (int32_t*)(w8 + y.off_out);
   a.err = a.out;
