@@ -248,10 +248,72 @@ struct Q8 {
   int gsum;
 };
 
+// Cross-lane reduction steps on the VALU (DPP and the gfx950 row swaps)
+// rather than LDS permutes.  The two quad permutes make each group of 4
+// lanes uniform; the half-row and row mirrors then pair every lane with the
+// other half of its 8- and 16-lane group; the row swaps pair 16-lane rows
+// and 32-lane halves.  Every lane of a reduced group ends with the same
+// value, combined in the same order.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+// (row 2r, row 2r + 1) values of a 16-lane row pair, in every lane of both rows
+__device__ __forceinline__ void rows16(float v, float& lo, float& hi) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  lo = __builtin_bit_cast(float, (unsigned)p[0]);
+  hi = __builtin_bit_cast(float, (unsigned)p[1]);
+}
+// (lanes 0..31, lanes 32..63) values, in every lane
+__device__ __forceinline__ void halves32(float v, float& lo, float& hi) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  lo = __builtin_bit_cast(float, (unsigned)p[0]);
+  hi = __builtin_bit_cast(float, (unsigned)p[1]);
+}
+__device__ __forceinline__ float max32(float v) {
+  v = __builtin_fmaxf(v, dpp_f<0xB1>(v));   // lane ^ 1
+  v = __builtin_fmaxf(v, dpp_f<0x4E>(v));   // lane ^ 2
+  v = __builtin_fmaxf(v, dpp_f<0x141>(v));  // half-row mirror
+  v = __builtin_fmaxf(v, dpp_f<0x140>(v));  // row mirror
+  float lo, hi;
+  rows16(v, lo, hi);
+  return __builtin_fmaxf(lo, hi);
+}
+__device__ __forceinline__ int sum32_i(int v) {
+  v += dpp_i<0xB1>(v);
+  v += dpp_i<0x4E>(v);
+  v += dpp_i<0x141>(v);
+  v += dpp_i<0x140>(v);
+  float lo, hi;
+  rows16(__builtin_bit_cast(float, v), lo, hi);
+  return __builtin_bit_cast(int, lo) + __builtin_bit_cast(int, hi);
+}
+__device__ __forceinline__ float sum64(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
+  float lo, hi;
+  rows16(v, lo, hi);
+  v = lo + hi;
+  halves32(v, lo, hi);
+  return lo + hi;
+}
+__device__ __forceinline__ int sum64_i(int v) {
+  const int s32 = sum32_i(v);
+  float lo, hi;
+  halves32(__builtin_bit_cast(float, s32), lo, hi);
+  return __builtin_bit_cast(int, lo) + __builtin_bit_cast(int, hi);
+}
+
 __device__ __forceinline__ Q8 quant_group32(float x) {
-  float amax = __builtin_fabsf(x);
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, m, 32));
+  const float amax = max32(__builtin_fabsf(x));
   Q8 r;
   if (amax == 0.0f) {
     r.s = 0.0f;
@@ -262,10 +324,7 @@ __device__ __forceinline__ Q8 quant_group32(float x) {
     q = __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
     r.a8 = (int)q;
   }
-  int sum = r.a8;
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 32);
-  r.gsum = sum;
+  r.gsum = sum32_i(r.a8);
   return r;
 }
 

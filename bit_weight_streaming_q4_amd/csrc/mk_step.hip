@@ -359,18 +359,10 @@ __device__ __forceinline__ void store_q8(uint8_t* rec, int tau, int lane, const 
   }
 }
 
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
+__device__ __forceinline__ int wave_sum_i(int v) { return sum64_i(v); }
 
-// Sum over the 64 lanes (fixed butterfly order).
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
-}
+// Sum over the 64 lanes (a fixed order; every lane gets the same value).
+__device__ __forceinline__ float wave_sum(float v) { return sum64(v); }
 
 // r[t] = 1/sqrt(mean(x_t^2) + eps) from the per-tile sums of squares of
 // record ss_idx: lane i adds tiles i, i+64, ... in order (the loads of two
