@@ -83,6 +83,26 @@ constexpr int kMaxStamps = 4 * kMaxLayers + 8;
 
 enum { K_X = 0, K_U = 1, K_X2 = 2, K_H = 3 };
 
+constexpr int kMaxTm = 8;   // (tile, matrix) pairs one block contributes to in one phase
+constexpr int kMaxOwn = 4;  // tiles one block owns in one phase
+// The work of one block in each of the four phase kinds, computed on the
+// host (the unit split has no cheap device-side form: it needs 64-bit
+// divisions).
+struct BlockPlan {
+  int wu[4][kCompute][4];     // per compute wave: first unit, end unit, (tile, matrix) and superblock of the first
+  int kp[4][4];               // first contributed (tile, matrix), count, first owned tile, count
+  uint8_t tmc[4][kMaxTm][4];  // per contributed pair: first and last compute wave of the block, rank among contributors
+  uint8_t oc[4][kMaxOwn][2];  // per owned tile: contributing blocks of matrix 0 and matrix 1
+};
+constexpr int kPlanWords = (int)(sizeof(BlockPlan) / 4);
+static_assert(sizeof(BlockPlan) % 16 == 0, "plans are copied in 16-B words");
+
+// Rows of a partial or mailbox, padded to whole 16-B words.
+template <int T>
+struct TPad {
+  static constexpr int value = (T + 3) & ~3;
+};
+
 struct LayerW {
   const uint8_t* w[5];  // p_in, p_out, gate, up, down
 };
@@ -123,6 +143,7 @@ struct StepArgs {
   int* lm_idx;
   int32_t* out;  // [0] error word, [16..31] n_acc, [32..47] tokens, [48..63] argmax
   uint64_t* stamps;  // [kMaxStamps]: block 0's clock after each barrier
+  const BlockPlan* plans;  // [grid]
 };
 
 __device__ __forceinline__ bool layer_is_gdn(const StepArgs& a, int l) {
@@ -156,6 +177,19 @@ __device__ __forceinline__ float ld_coh(const float* p) {
 __device__ __forceinline__ int ld_coh_i(const int* p) {
   return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16-B device-scope (sc1) accesses through a buffer resource on a
+// wave-uniform base; off is the lane's byte offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+constexpr int kSc1 = 16;  // cache-policy bits of a device-scope access
+__device__ __forceinline__ f32x4 ld16(const void* base, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rsrc(base), off, 0, kSc1);
+}
+__device__ __forceinline__ void st16(void* base, int off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, rsrc(base), off, 0, kSc1);
+}
+
 // The atomic may only be performed once this wave's stores are in memory.  A
 // workgroup-scope release fence does not wait for them on this target (the
 // waves of a workgroup share one L1), so the wait is explicit; with every
@@ -223,7 +257,7 @@ __device__ __forceinline__ void lds_st(int* p, int v) {
 // ------------------------------------------------------------ block state
 // ring[c][k]: slot k of compute wave c (a 9216-B weight unit and the 5120-B
 // activation block of its superblock), filled by the wave's own LDS-DMA loads.  mb[c][k]: mailbox k of compute wave c, the
-// partial sums [t][64] of one (tile, matrix) with its tag ((phase + 1) << 16 |
+// partial sums [64][t] of one (tile, matrix) with its tag ((phase + 1) << 16 |
 // tile-matrix), 0 when free.  done[c] = phases finished by compute wave c;
 // rel = grid barriers completed.  wt: the per-layer weight pointers (read by
 // the compute waves at every phase change).  rel = phases opened by the watcher wave
@@ -239,7 +273,9 @@ struct BlockState {
   static constexpr int NMB = MbCount<T>::value;
   uint8_t ring[kCompute][kSlots][kSlotBytes] __attribute__((aligned(16)));
   const uint8_t* wt[kMaxLayers][5];  // the weight table, copied at the start
-  float mb[kCompute][NMB][T][64];
+  float mb[kCompute][NMB][64][TPad<T>::value] __attribute__((aligned(16)));  // [row of the tile][t]
+  uint8_t stage[1024 + 256] __attribute__((aligned(16)));  // one tile's record part, staged by the service wave
+  BlockPlan plan __attribute__((aligned(16)));
   int tag[kCompute][NMB];
   int done[kCompute];
   int rel;
@@ -303,23 +339,6 @@ __device__ __forceinline__ Line line_of(const StepArgs& a, int ph) {
   return ln;
 }
 
-// first unit of compute wave w's stretch of a line of S units shared by W <= S
-// waves (waves w >= W have none)
-__device__ __forceinline__ int stretch_lo(int S, int W, int w) {
-  return w >= W ? S : (int)(((unsigned long long)S * (unsigned)w) / (unsigned)W);
-}
-// compute wave whose stretch holds unit p
-__device__ __forceinline__ int wave_of(int S, int W, int p) {
-  return (int)((((unsigned long long)p + 1) * (unsigned)W - 1) / (unsigned)S);
-}
-// blocks contributing to (tile, matrix) tm, and the first of them (every
-// wave between two contributing waves has units, so the blocks are a range)
-__device__ __forceinline__ int first_block(const Line& ln, int tm) {
-  return wave_of(ln.S, ln.W, tm * ln.nsb) / kCompute;
-}
-__device__ __forceinline__ int n_blocks(const Line& ln, int tm) {
-  return wave_of(ln.S, ln.W, tm * ln.nsb + ln.nsb - 1) / kCompute - first_block(ln, tm) + 1;
-}
 
 // activation record of (layer, kind)
 __device__ __forceinline__ uint8_t* act_rec(const StepArgs& a, int layer, int kind) {
@@ -333,29 +352,37 @@ __device__ __forceinline__ uint8_t* phase_input(const StepArgs& a, int l, int ph
 }
 
 // Quantizes, per row t < T, the 64 values val[t] (lane = column of tile tau
-// of the record's K) into the record; rows T..15 get zero codes and scales.
-// Column c of superblock b = tau / 4: sub-block j = (c % 256) / 32, octet
-// q = (c % 32) / 8, byte c % 8.
+// of the record's K) and writes the tile's part of the record: its two
+// sub-blocks' 1024 code bytes ([j][q][t][8 B]; rows T..15 zero) and their
+// 2 x 16 scales and scaled code sums.  Both are staged in LDS so that each
+// goes out as one 16-B store per lane.  Column c of superblock b = tau / 4:
+// sub-block j = (c % 256) / 32, octet q = (c % 32) / 8, byte c % 8.
 template <int T>
-__device__ __forceinline__ void store_q8(uint8_t* rec, int tau, int lane, const float (&val)[T]) {
-  uint8_t* blk = rec + (size_t)(tau >> 2) * kActBytes;
-  const int j = (tau & 3) * 2 + (lane >> 5), e = lane & 31;
-  int8_t* a8 = (int8_t*)blk + ((j * 4 + (e >> 3)) * 16) * 8 + (e & 7);
-  float* sc = (float*)(blk + kActA);
+__device__ __forceinline__ void store_q8(uint8_t* rec, int tau, int lane, const float (&val)[T], uint8_t* stage) {
+  const int jj = lane >> 5, e = lane & 31;
+  uint8_t* cb = stage + ((jj * 4 + (e >> 3)) * 16) * 8 + (e & 7);
+  float* sst = (float*)(stage + 1024);  // [s: 2 x 16][s * gsum: 2 x 16]
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     const Q8 q = quant_group32(val[t]);
-    st_coh_i8(a8 + t * 8, (int8_t)q.a8);
+    cb[t * 8] = (uint8_t)q.a8;
     if (e == 0) {
-      st_coh(sc + j * 16 + t, q.s);
-      st_coh(sc + 128 + j * 16 + t, q.s * (float)q.gsum);
+      sst[jj * 16 + t] = q.s;
+      sst[32 + jj * 16 + t] = q.s * (float)q.gsum;
     }
   }
 #pragma unroll
-  for (int t = T; t < kTPad; ++t) st_coh_i8(a8 + t * 8, (int8_t)0);
+  for (int t = T; t < kTPad; ++t) cb[t * 8] = 0;
   if (e < kTPad - T) {
-    st_coh(sc + j * 16 + T + e, 0.0f);
-    st_coh(sc + 128 + j * 16 + T + e, 0.0f);
+    sst[jj * 16 + T + e] = 0.0f;
+    sst[32 + jj * 16 + T + e] = 0.0f;
+  }
+  uint8_t* blk = rec + (size_t)(tau >> 2) * kActBytes;
+  st16(blk, (tau & 3) * 1024 + lane * 16, *(const f32x4*)(stage + lane * 16));
+  if (lane < 16) {
+    const int j0 = (tau & 3) * 2;
+    const int fo = lane < 8 ? j0 * 16 + lane * 4 : 128 + j0 * 16 + (lane - 8) * 4;
+    st16(blk + kActA, fo * 4, *(const f32x4*)(stage + 1024 + lane * 16));
   }
 }
 
@@ -365,33 +392,47 @@ __device__ __forceinline__ int wave_sum_i(int v) { return sum64_i(v); }
 __device__ __forceinline__ float wave_sum(float v) { return sum64(v); }
 
 // r[t] = 1/sqrt(mean(x_t^2) + eps) from the per-tile sums of squares of
-// record ss_idx: lane i adds tiles i, i+64, ... in order (the loads of two
-// such chunks are issued together), then the lanes are summed by the
-// butterfly; the same order for every caller.
+// record ss_idx ([tile][16]): lane i adds tiles i, i+64, ... in order (the
+// loads of two such chunks are issued together), then the lanes are summed;
+// the same order for every caller.
 template <int T>
 __device__ __forceinline__ void rnorm_rows(const StepArgs& a, int ss_idx, int lane, float (&r)[T]) {
+  constexpr int TP = TPad<T>::value;
   const int ntH = a.H / 64;
   const float* ss = a.ss + (size_t)ss_idx * ntH * 16;
-  float acc[T];
+  f32x4 acc[TP / 4];
 #pragma unroll
-  for (int t = 0; t < T; ++t) acc[t] = 0.0f;
+  for (int i = 0; i < TP / 4; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 * 64 < ntH; k0 += 2) {
-    float v[2][T];
+    f32x4 v[2][TP / 4];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int tile = (k0 + k) * 64 + lane;
       const int tl = tile < ntH ? tile : 0;  // in-range address; the value is not added
 #pragma unroll
-      for (int t = 0; t < T; ++t) v[k][t] = ld_coh(ss + (size_t)tl * 16 + t);
+      for (int i = 0; i < TP / 4; ++i) v[k][i] = ld16(ss, tl * 64 + i * 16);
     }
 #pragma unroll
     for (int k = 0; k < 2; ++k)
       if ((k0 + k) * 64 + lane < ntH)
 #pragma unroll
-        for (int t = 0; t < T; ++t) acc[t] += v[k][t];
+        for (int i = 0; i < TP / 4; ++i) acc[i] += v[k][i];
   }
 #pragma unroll
-  for (int t = 0; t < T; ++t) r[t] = 1.0f / __builtin_sqrtf(wave_sum(acc[t]) / (float)a.H + kRmsEps);
+  for (int t = 0; t < T; ++t) r[t] = 1.0f / __builtin_sqrtf(wave_sum(acc[t / 4][t % 4]) / (float)a.H + kRmsEps);
+}
+
+// Sums of squares of the T rows of a 64-column tile into its 16 slots (lane t
+// writes slot t; slots T..15 are zero).
+template <int T>
+__device__ __forceinline__ void store_ss(float* ss16, int lane, const float (&x)[T]) {
+  float mine = 0.0f;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const float s2 = wave_sum(x[t] * x[t]);
+    if (lane == t) mine = s2;
+  }
+  if (lane < kTPad) st_coh(ss16 + lane, mine);
 }
 
 // ------------------------------------------------------------ compute waves
@@ -404,17 +445,21 @@ struct Cursor {
   const uint8_t* W1;
 };
 
-__device__ __forceinline__ void cursor_settle(const StepArgs& a, const uint8_t* const (*wt)[5], Cursor& c, int w) {
+// wu: the block plan's unit ranges, [kind][compute wave][4]
+typedef const int (*WaveUnits)[kCompute][4];
+__device__ __forceinline__ void cursor_settle(const StepArgs& a, const uint8_t* const (*wt)[5], WaveUnits wu, Cursor& c,
+                                              int cw) {
   while (c.q < 4 * a.L) {
     const int ph = c.q & 3, l = c.q >> 2;
-    const Line ln = line_of(a, ph);
-    c.u = stretch_lo(ln.S, ln.W, w);
-    c.u1 = stretch_lo(ln.S, ln.W, w + 1);
+    const int* p = wu[ph][cw];
+    c.u = uniform(p[0]);
+    c.u1 = uniform(p[1]);
     if (c.u < c.u1) {
+      const Line ln = line_of(a, ph);
       c.nsb = ln.nsb;
       c.nm = ln.nm;
-      c.tm = c.u / ln.nsb;
-      c.b = c.u - c.tm * ln.nsb;
+      c.tm = uniform(p[2]);
+      c.b = uniform(p[3]);
       const int m0 = ph == 0 ? 0 : ph == 1 ? 1 : ph == 2 ? 2 : 4;
       c.W0 = uniform(wt[l][m0]);
       c.W1 = uniform(wt[l][ph == 2 ? 3 : m0]);
@@ -472,8 +517,8 @@ struct Slot {
 // Starts the weight loads of the cursor's unit into slot lds (and its
 // activations if phase `open` is the unit's, i.e. they are ready), records
 // the unit and moves on.  Returns the number of operations issued.
-__device__ __forceinline__ void issue(const StepArgs& a, const uint8_t* const (*wt)[5], Cursor& c, int w, int lane,
-                                      uint32_t lds, int open, Slot& sl) {
+__device__ __forceinline__ void issue(const StepArgs& a, const uint8_t* const (*wt)[5], WaveUnits wu, Cursor& c, int w,
+                                      int lane, uint32_t lds, int open, Slot& sl) {
   sl.q = c.q;
   sl.tm = c.tm;
   sl.b = c.b;
@@ -495,7 +540,7 @@ __device__ __forceinline__ void issue(const StepArgs& a, const uint8_t* const (*
   }
   if (++c.u >= c.u1) {
     ++c.q;
-    cursor_settle(a, wt, c, w);
+    cursor_settle(a, wt, wu, c, w);
   }
 }
 
@@ -634,15 +679,14 @@ __device__ __forceinline__ void flush(BlockState<T>& s, int c, int lane, Consume
     }
   }
   if constexpr (UseMfma<T>::value) {
+    // C layout: lane 16 q + n holds rows t = 4q .. 4q + 3 of tile row 16 nb + n
     const int q = lane >> 4, n = lane & 15;
+    if (4 * q < TPad<T>::value)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * q + i < T) s.mb[c][slot][4 * q + i][16 * nb + n] = k.macc[nb][i];
+      for (int nb = 0; nb < 4; ++nb) *(f32x4*)&s.mb[c][slot][16 * nb + n][4 * q] = k.macc[nb];
   } else {
 #pragma unroll
-    for (int t = 0; t < T; ++t) s.mb[c][slot][t][lane] = k.acc[t];
+    for (int t = 0; t < T; ++t) s.mb[c][slot][lane][t] = k.acc[t];
   }
   if (lane == 0) lds_st(&s.tag[c][slot], ((k.q + 1) << 16) | k.tm);
   ++k.nflush;
@@ -730,16 +774,17 @@ __device__ __forceinline__ void consume(const StepArgs& a, BlockState<T>& s, int
 
 template <int T>
 __device__ __forceinline__ void compute_wave(const StepArgs& a, BlockState<T>& s, int c, int lane) {
-  const int w = blockIdx.x * kCompute + c;
+  const int w = c;  // the plan indexes compute waves within the block
   const int qend = 4 * a.L;
   const uint32_t l0 = slot_lds(s, c, 0), l1 = slot_lds(s, c, 1);
   const uint8_t* const(*wt)[5] = s.wt;
+  WaveUnits wu = s.plan.wu;
   Cursor cur;
   cur.q = 0;
-  cursor_settle(a, wt, cur, w);
+  cursor_settle(a, wt, wu, cur, w);
   Slot s0, s1;
-  issue(a, wt, cur, w, lane, l0, -1, s0);
-  issue(a, wt, cur, w, lane, l1, -1, s1);
+  issue(a, wt, wu, cur, w, lane, l0, -1, s0);
+  issue(a, wt, wu, cur, w, lane, l1, -1, s1);
   Consumer<T> k;
   k.q = -1;
   k.tm = -1;
@@ -752,11 +797,11 @@ __device__ __forceinline__ void compute_wave(const StepArgs& a, BlockState<T>& s
     consume<T>(a, s, c, lane, k, s0, s1, 0, l0, l1, ok);
     finish_early<T>(s, c, lane, k, s1.q, s1.tm, ok);
     // the slot's LDS reads have completed (their values were used) before it is refilled
-    issue(a, wt, cur, w, lane, l0, k.q, s0);
+    issue(a, wt, wu, cur, w, lane, l0, k.q, s0);
     if (s1.q >= qend) break;
     consume<T>(a, s, c, lane, k, s1, s0, 1, l1, l0, ok);
     finish_early<T>(s, c, lane, k, s0.q, s0.tm, ok);
-    issue(a, wt, cur, w, lane, l1, k.q, s1);
+    issue(a, wt, wu, cur, w, lane, l1, k.q, s1);
   }
   advance_to<T>(a, s, c, lane, k, qend, ok);  // finishes the phases after the last unit
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load outlives the stream (also after an abort)
@@ -831,19 +876,14 @@ __device__ __forceinline__ bool svc_barrier(const StepArgs& a, BlockState<T>& s,
 }
 
 template <int T>
-__device__ __forceinline__ void svc_prep(const StepArgs& a, int lane) {
+__device__ __forceinline__ void svc_prep(const StepArgs& a, int lane, uint8_t* stage) {
   const int ntH = a.H / 64;
   for (int tau = blockIdx.x; tau < ntH; tau += gridDim.x) {
     float xv[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) xv[t] = ld_coh(a.x + (size_t)t * a.H + tau * 64 + lane);
-    float* ss = a.ss + (size_t)tau * 16;
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const float s2 = wave_sum(xv[t] * xv[t]);
-      if (lane == 0) st_coh(ss + t, s2);
-    }
-    store_q8<T>(act_rec(a, 0, K_X), tau, lane, xv);
+    store_ss<T>(a.ss + (size_t)tau * 16, lane, xv);
+    store_q8<T>(act_rec(a, 0, K_X), tau, lane, xv, stage);
   }
   const int n = ntH > (int)blockIdx.x ? (ntH - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
   if (n) {
@@ -852,40 +892,46 @@ __device__ __forceinline__ void svc_prep(const StepArgs& a, int lane) {
   }
 }
 
-// Sum of the block partials of (tile, matrix) pairs tau*nm + m, m < nm, in
-// block order; all loads of up to kPartBatch partials are issued together.
+// Sum of the block partials of (tile, matrix) pairs tau*nm + m, m < nm (n0
+// and n1 contributing blocks), in block order; all loads of up to
+// kPartBatch partials are issued together.  A partial is [64 rows][TP].
 template <int T>
-__device__ __forceinline__ void sum_partials(const StepArgs& a, const Line& ln, int q, int tau, int lane,
+__device__ __forceinline__ void sum_partials(const StepArgs& a, int q, int nm, int tau, int n0, int n1, int lane,
                                              float (&v0)[T], float (&v1)[T]) {
+  constexpr int TP = TPad<T>::value;
   const int ph = q & 3;
   const float* part = a.part + (size_t)(q & 1) * a.part_half;
-  const int tm0 = tau * ln.nm;
-  const int n0 = uniform(n_blocks(ln, tm0));
-  const int n1 = ln.nm == 2 ? uniform(n_blocks(ln, tm0 + 1)) : 0;
+  const int tm0 = tau * nm;
   const int n = n0 + n1, cm = (a.cmax4 >> (8 * ph)) & 255;
+  f32x4 s0[TP / 4], s1[TP / 4];
 #pragma unroll
-  for (int t = 0; t < T; ++t) v0[t] = v1[t] = 0.0f;
+  for (int i = 0; i < TP / 4; ++i) s0[i] = s1[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
   for (int e0 = 0; e0 < n; e0 += kPartBatch) {
-    float tmp[kPartBatch][T];
+    f32x4 tmp[kPartBatch][TP / 4];
 #pragma unroll
     for (int i = 0; i < kPartBatch; ++i) {
       const int e = e0 + i < n ? e0 + i : n - 1;  // in-range address; extra values are not added
       const int m = e < n0 ? 0 : 1, r = e < n0 ? e : e - n0;
-      const float* p = part + ((size_t)((tm0 + m) * cm + r) * T) * 64 + lane;
+      const int off = (((tm0 + m) * cm + r) * 64 + lane) * TP * 4;
 #pragma unroll
-      for (int t = 0; t < T; ++t) tmp[i][t] = ld_coh(p + t * 64);
+      for (int k = 0; k < TP / 4; ++k) tmp[i][k] = ld16(part, off + k * 16);
     }
 #pragma unroll
     for (int i = 0; i < kPartBatch; ++i) {
       if (e0 + i >= n) break;
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
+      for (int k = 0; k < TP / 4; ++k) {
         if (e0 + i < n0)
-          v0[t] += tmp[i][t];
+          s0[k] += tmp[i][k];
         else
-          v1[t] += tmp[i][t];
+          s1[k] += tmp[i][k];
       }
     }
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    v0[t] = s0[t / 4][t % 4];
+    v1[t] = s1[t / 4][t % 4];
   }
 }
 
@@ -894,12 +940,11 @@ __device__ __forceinline__ void sum_partials(const StepArgs& a, const Line& ln, 
 // and 2) and xo[t] (the residual rows of the tile, phases 1 and 3) were
 // loaded at the start of the phase.
 template <int T>
-__device__ __forceinline__ void svc_epilogue(const StepArgs& a, int q, int tau, int lane, const float (&r)[T],
-                                             const float (&xo)[T]) {
+__device__ __forceinline__ void svc_epilogue(const StepArgs& a, int q, int tau, int n0, int n1, int lane,
+                                             const float (&r)[T], const float (&xo)[T], uint8_t* stage) {
   const int l = q >> 2, ph = q & 3;
-  const Line ln = line_of(a, ph);
   float v0[T], v1[T];
-  sum_partials<T>(a, ln, q, tau, lane, v0, v1);
+  sum_partials<T>(a, q, ph == 2 ? 2 : 1, tau, n0, n1, lane, v0, v1);
   const int col = tau * 64 + lane;
   if (ph == 0 || ph == 2) {
     float y[T];
@@ -912,7 +957,7 @@ __device__ __forceinline__ void svc_epilogue(const StepArgs& a, int q, int tau, 
         y[t] = g * u / (1.0f + expf(-g));
       }
     }
-    store_q8<T>(act_rec(a, l, ph == 0 ? K_U : K_H), tau, lane, y);
+    store_q8<T>(act_rec(a, l, ph == 0 ? K_U : K_H), tau, lane, y, stage);
   } else {
     float xn[T];
 #pragma unroll
@@ -921,20 +966,15 @@ __device__ __forceinline__ void svc_epilogue(const StepArgs& a, int q, int tau, 
       st_coh(a.x + (size_t)t * a.H + col, xn[t]);
     }
     const int ss_idx = ph == 1 ? 2 * l + 1 : 2 * l + 2;
-    float* ss = a.ss + ((size_t)ss_idx * (a.H / 64) + tau) * 16;
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const float s2 = wave_sum(xn[t] * xn[t]);
-      if (lane == 0) st_coh(ss + t, s2);
-    }
+    store_ss<T>(a.ss + ((size_t)ss_idx * (a.H / 64) + tau) * 16, lane, xn);
     if (ph == 3 && a.trace) {
 #pragma unroll
       for (int t = 0; t < T; ++t) a.trace[((size_t)l * T + t) * a.H + col] = xn[t];
     }
     if (ph == 1)
-      store_q8<T>(act_rec(a, l, K_X2), tau, lane, xn);
+      store_q8<T>(act_rec(a, l, K_X2), tau, lane, xn, stage);
     else if (l + 1 < a.L)
-      store_q8<T>(act_rec(a, l + 1, K_X), tau, lane, xn);
+      store_q8<T>(act_rec(a, l + 1, K_X), tau, lane, xn, stage);
   }
 }
 
@@ -948,90 +988,90 @@ __device__ __forceinline__ void svc_epilogue(const StepArgs& a, int q, int tau, 
 // wait for each owned tile's count to complete and run its epilogue.
 template <int T>
 __device__ __forceinline__ bool svc_phase(const StepArgs& a, BlockState<T>& s, int q, int lane, bool ok) {
+  constexpr int TP = TPad<T>::value;
   const int l = q >> 2, ph = q & 3;
-  const Line ln = line_of(a, ph);
-  const int ntile = ln.N / 64;
-  const int own0 = (int)((long)ntile * blockIdx.x / gridDim.x), own1 = (int)((long)ntile * (blockIdx.x + 1) / gridDim.x);
+  const int nm = ph == 2 ? 2 : 1;
+  const int tm0 = uniform(s.plan.kp[ph][0]), ntm = uniform(s.plan.kp[ph][1]);
+  const int own0 = uniform(s.plan.kp[ph][2]), nown = uniform(s.plan.kp[ph][3]);
   float r[T], xo[2][T];
 #pragma unroll
   for (int t = 0; t < T; ++t) r[t] = xo[0][t] = xo[1][t] = 0.0f;
   // the row factors need every tile of the phase input (its sums of squares)
   if (!wait_ge(a, s, &s.rel, q + 1)) return false;
-  if (own0 < own1) {
+  if (nown > 0) {
     if (ph == 0 || ph == 2) {
       rnorm_rows<T>(a, ph == 0 ? 2 * l : 2 * l + 1, lane, r);
     } else {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        if (own0 + i < own1)
+        if (i < nown)
 #pragma unroll
           for (int t = 0; t < T; ++t) xo[i][t] = ld_coh(a.x + (size_t)t * a.H + (own0 + i) * 64 + lane);
     }
   }
-  const int bw0 = blockIdx.x * kCompute;
-  const int ub0 = stretch_lo(ln.S, ln.W, bw0), ub1 = stretch_lo(ln.S, ln.W, bw0 + kCompute);
   if (!ok) return ok;
   unsigned* tk = a.tickets + ((size_t)l * 4 + ph) * kTicketTiles * kTicketStride;
-  if (ub0 < ub1) {
-  const int tm0 = ub0 / ln.nsb, tm1 = (ub1 - 1) / ln.nsb;
-  const int cm = (a.cmax4 >> (8 * ph)) & 255;
-  const int bfirst_base = blockIdx.x;
-  for (int tm = tm0; tm <= tm1; ++tm) {
-    const int p0 = tm * ln.nsb > ub0 ? tm * ln.nsb : ub0;
-    const int p1 = (tm + 1) * ln.nsb < ub1 ? (tm + 1) * ln.nsb : ub1;
-    const int c_lo = wave_of(ln.S, ln.W, p0) - bw0, c_hi = wave_of(ln.S, ln.W, p1 - 1) - bw0;
-    const int want = ((q + 1) << 16) | tm;
-    // lane NMB*c + k watches mailbox k of compute wave c
-    constexpr int NMB = BlockState<T>::NMB;
-    constexpr uint64_t kAll = (1ull << NMB) - 1;
-    uint64_t have = 0;
-    unsigned spins = 0;
-    while (true) {
-      const int tg = lane < NMB * kCompute ? lds_ld(&s.tag[lane / NMB][lane % NMB]) : 0;
-      have = __ballot(tg == want);
-      bool all = true;
-      for (int c = c_lo; c <= c_hi; ++c) all = all && ((have >> (NMB * c)) & kAll) != 0;
-      if (all) break;
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit || lds_ld(&s.abort)) {
-        lds_st(&s.abort, 1);
-        if (lane == 0) atomicOr(a.err, 1);
-        return false;
+  if (ntm > 0) {
+    const int cm = (a.cmax4 >> (8 * ph)) & 255;
+    float* part = a.part + (size_t)(q & 1) * a.part_half;
+    for (int i = 0; i < ntm; ++i) {
+      const int tm = tm0 + i;
+      const uint32_t pc = uniform(*(const uint32_t*)&s.plan.tmc[ph][i][0]);
+      const int c_lo = pc & 255, c_hi = (pc >> 8) & 255, rank = (pc >> 16) & 255;
+      const int want = ((q + 1) << 16) | tm;
+      // lane NMB*c + k watches mailbox k of compute wave c
+      constexpr int NMB = BlockState<T>::NMB;
+      constexpr uint64_t kAll = (1ull << NMB) - 1;
+      uint64_t have = 0;
+      unsigned spins = 0;
+      while (true) {
+        const int tg = lane < NMB * kCompute ? lds_ld(&s.tag[lane / NMB][lane % NMB]) : 0;
+        have = __ballot(tg == want);
+        bool all = true;
+        for (int c = c_lo; c <= c_hi; ++c) all = all && ((have >> (NMB * c)) & kAll) != 0;
+        if (all) break;
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit || lds_ld(&s.abort)) {
+          lds_st(&s.abort, 1);
+          if (lane == 0) atomicOr(a.err, 1);
+          return false;
+        }
       }
-    }
-    float v[T];
+      f32x4 v[TP / 4];
 #pragma unroll
-    for (int t = 0; t < T; ++t) v[t] = 0.0f;
-    for (int c = c_lo; c <= c_hi; ++c) {
-      const int k = ((have >> (NMB * c)) & 1ull) ? 0 : 1;
+      for (int k = 0; k < TP / 4; ++k) v[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int c = c_lo; c <= c_hi; ++c) {
+        const int k = ((have >> (NMB * c)) & 1ull) ? 0 : 1;
 #pragma unroll
-      for (int t = 0; t < T; ++t) v[t] += s.mb[c][k][t][lane];
-    }
-    for (int c = c_lo; c <= c_hi; ++c) {
-      const int k = ((have >> (NMB * c)) & 1ull) ? 0 : 1;
-      if (lane == 0) lds_st(&s.tag[c][k], 0);
-    }
-    const int rank = bfirst_base - first_block(ln, tm);
-    float* dst = a.part + (size_t)(q & 1) * a.part_half + ((size_t)(tm * cm + rank) * T) * 64 + lane;
+        for (int j = 0; j < TP / 4; ++j) v[j] += *(const f32x4*)&s.mb[c][k][lane][4 * j];
+      }
+      for (int c = c_lo; c <= c_hi; ++c) {
+        const int k = ((have >> (NMB * c)) & 1ull) ? 0 : 1;
+        if (lane == 0) lds_st(&s.tag[c][k], 0);
+      }
+      const int off = ((tm * cm + rank) * 64 + lane) * TP * 4;
 #pragma unroll
-    for (int t = 0; t < T; ++t) st_coh(dst + t * 64, v[t]);
-  }
-  // contributions: lane i counts this block's (tile, matrix) pairs of tile tau0 + i
-  const int tau0 = tm0 / ln.nm, tau1 = tm1 / ln.nm;
-  stores_done();
-  for (int tau = tau0 + lane; tau <= tau1; tau += 64) {
-    int cnt = 0;
-    for (int m = 0; m < ln.nm; ++m) {
-      const int tm = tau * ln.nm + m;
-      if (tm >= tm0 && tm <= tm1) ++cnt;
+      for (int j = 0; j < TP / 4; ++j) st16(part, off + j * 16, v[j]);
     }
-    __hip_atomic_fetch_add(tk + (size_t)tau * kTicketStride, (unsigned)cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+    // contributions: lane i counts this block's (tile, matrix) pairs of tile tau0 + i
+    const int tm1 = tm0 + ntm - 1;
+    const int tau0 = tm0 / nm, tau1 = tm1 / nm;
+    stores_done();
+    for (int tau = tau0 + lane; tau <= tau1; tau += 64) {
+      int cnt = 0;
+      for (int m = 0; m < nm; ++m) {
+        const int tm = tau * nm + m;
+        if (tm >= tm0 && tm <= tm1) ++cnt;
+      }
+      __hip_atomic_fetch_add(tk + (size_t)tau * kTicketStride, (unsigned)cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   // owned tiles: wait for all contributions, then the epilogue
-  for (int tau = own0; tau < own1; ++tau) {
-    int expect = 0;
-    for (int m = 0; m < ln.nm; ++m) expect += n_blocks(ln, tau * ln.nm + m);
+  for (int o = 0; o < nown; ++o) {
+    const int tau = own0 + o;
+    const uint32_t oc = uniform((uint32_t)s.plan.oc[ph][o][0] | ((uint32_t)s.plan.oc[ph][o][1] << 8));
+    const int n0 = oc & 255, n1 = oc >> 8;
+    const int expect = n0 + n1;
     unsigned spins = 0;
     while ((int)sld1(tk + (size_t)tau * kTicketStride) < expect) {
       __builtin_amdgcn_s_sleep(1);
@@ -1043,9 +1083,9 @@ __device__ __forceinline__ bool svc_phase(const StepArgs& a, BlockState<T>& s, i
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     float xt[T];
-    if (tau < own0 + 2) {
+    if (o < 2) {
 #pragma unroll
-      for (int t = 0; t < T; ++t) xt[t] = tau == own0 ? xo[0][t] : xo[1][t];
+      for (int t = 0; t < T; ++t) xt[t] = o == 0 ? xo[0][t] : xo[1][t];
     } else if (ph == 1 || ph == 3) {  // more owned tiles than prefetched (small grids)
 #pragma unroll
       for (int t = 0; t < T; ++t) xt[t] = ld_coh(a.x + (size_t)t * a.H + tau * 64 + lane);
@@ -1053,13 +1093,13 @@ __device__ __forceinline__ bool svc_phase(const StepArgs& a, BlockState<T>& s, i
 #pragma unroll
       for (int t = 0; t < T; ++t) xt[t] = 0.0f;
     }
-    svc_epilogue<T>(a, q, uniform(tau), lane, r, xt);
+    svc_epilogue<T>(a, q, uniform(tau), n0, n1, lane, r, xt, s.stage);
   }
   // the owned tiles' outputs are complete: count them for the watchers
-  if (own0 < own1) {
+  if (nown > 0) {
     stores_done();
     if (lane == 0)
-      __hip_atomic_fetch_add(a.rdy + ((size_t)(q + 1) * kRdySlots + blockIdx.x % kRdySlots) * kRdyStride, (unsigned)(own1 - own0),
+      __hip_atomic_fetch_add(a.rdy + ((size_t)(q + 1) * kRdySlots + blockIdx.x % kRdySlots) * kRdyStride, (unsigned)nown,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   return true;
@@ -1093,7 +1133,7 @@ __device__ __forceinline__ void svc_lm_prep(const StepArgs& a, int lane, const f
 
 template <int T>
 __device__ __forceinline__ void service_wave(const StepArgs& a, BlockState<T>& s, int lane) {
-  svc_prep<T>(a, lane);
+  svc_prep<T>(a, lane, s.stage);
   bool ok = true;
   for (int q = 0; q < 4 * a.L && ok; ++q) ok = svc_phase<T>(a, s, q, lane, ok);
   // lm_prep needs the final residual: every tile of the last phase
@@ -1327,6 +1367,8 @@ __global__ __launch_bounds__(kBlock) void k_decode_step(StepArgs a) {
   if (threadIdx.x < kCompute) s.done[threadIdx.x] = 0;
   // the weight table is written before the launch: plain loads are safe
   for (int i = threadIdx.x; i < a.L * 5; i += kBlock) s.wt[i / 5][i % 5] = a.layers[i / 5].w[i % 5];
+  for (int i = threadIdx.x; i < kPlanWords / 4; i += kBlock)
+    ((u32x4*)&s.plan)[i] = ((const u32x4*)(a.plans + blockIdx.x))[i];
   if (threadIdx.x == 0) {
     s.rel = 0;
     s.abort = 0;
@@ -1393,7 +1435,9 @@ struct mk_stack {
   std::vector<uint8_t> gdn_flag;
   int n_gdn_layers = 0;
   int8_t gdn_idx[kMaxLayers];
-  void* uploaded_ws = nullptr;  // workspace that holds the current weight table
+  void* uploaded_ws = nullptr;  // workspace that holds the current weight table and block plans
+  std::vector<BlockPlan> plans;  // for plans_grid blocks
+  int plans_grid = -1;
   hipEvent_t ev[2] = {nullptr, nullptr};  // around the last launch (no device memory)
   float last_ms = -1.0f;
 };
@@ -1407,6 +1451,7 @@ struct StepLayout {
   int cmax[4];
   size_t off_ctrl, n_ctrl;  // zeroed before each launch: barrier, tickets
   size_t off_rdy, off_open, part_half;
+  size_t off_plans;
   size_t off_out, off_stamps, off_tickets, off_lmticket, off_table, off_act, off_ss, off_part, off_frag, off_lmv,
       off_lmi, total;
   size_t act_layer, act_off[4];
@@ -1469,13 +1514,16 @@ StepLayout layout(const mk_stack* st, int T) {
   o += a256(sizeof(uint64_t) * kMaxStamps);
   y.off_table = o;
   o += a256(sizeof(LayerW) * d.n_layers);
+  y.off_plans = o;
+  o += a256(sizeof(BlockPlan) * std::max(y.grid, 1));
   y.off_act = o;
   o += y.act_layer * d.n_layers;
   y.off_ss = o;
   o += a256((size_t)(2 * d.n_layers + 1) * (d.hidden / 64) * 16 * 4);
   y.off_part = o;
   size_t part = 0;
-  for (int i = 0; i < 4; ++i) part = std::max(part, (size_t)ntiles[i] * nms[i] * y.cmax[i] * T * 64 * 4);
+  const int tp = (T + 3) & ~3;
+  for (int i = 0; i < 4; ++i) part = std::max(part, (size_t)ntiles[i] * nms[i] * y.cmax[i] * tp * 64 * 4);
   y.part_half = a256(part) / 4;  // floats; two buffers, by phase parity
   o += 2 * a256(part);
   y.off_frag = o;
@@ -1489,6 +1537,70 @@ StepLayout layout(const mk_stack* st, int T) {
 }
 
 int sfail(int status, const char* msg) { return set_error(status, "%s", msg); }
+
+// The split of every phase kind's line of units over the grid's compute
+// waves (wave w of W takes units [S w / W, S (w + 1) / W)), written per block:
+// each compute wave's range, the (tile, matrix) pairs the block contributes
+// to with the waves and the rank of its contribution, and the tiles it owns
+// (tile tau by block tau * grid / n_tiles) with their contributor counts.
+// Returns false when a block would exceed the plan's fixed capacities.
+bool make_plans(const mk_stack_desc& d, int grid, std::vector<BlockPlan>& out) {
+  const long Wc = (long)grid * kCompute;
+  const int ntiles[4] = {d.proj / 64, d.hidden / 64, d.ffn / 64, d.hidden / 64};
+  const int nms[4] = {1, 1, 2, 1};
+  const int nsbs[4] = {d.hidden / 256, d.proj / 256, d.hidden / 256, d.ffn / 256};
+  out.assign(grid, BlockPlan());
+  memset(out.data(), 0, sizeof(BlockPlan) * out.size());
+  for (int k = 0; k < 4; ++k) {
+    const long nsb = nsbs[k], S = (long)ntiles[k] * nms[k] * nsb;
+    const long W = std::min(Wc, S);
+    auto lo = [&](long w) { return w >= W ? S : S * w / W; };
+    auto wave_of = [&](long p) { return (long)(((p + 1) * W - 1) / S); };
+    auto first_block = [&](long tm) { return wave_of(tm * nsb) / kCompute; };
+    auto n_blocks = [&](long tm) { return wave_of(tm * nsb + nsb - 1) / kCompute - first_block(tm) + 1; };
+    for (int b = 0; b < grid; ++b) {
+      BlockPlan& p = out[b];
+      for (int c = 0; c < kCompute; ++c) {
+        const long w = (long)b * kCompute + c, u = lo(w), u1 = lo(w + 1);
+        p.wu[k][c][0] = (int)u;
+        p.wu[k][c][1] = (int)u1;
+        p.wu[k][c][2] = u < u1 ? (int)(u / nsb) : 0;
+        p.wu[k][c][3] = u < u1 ? (int)(u % nsb) : 0;
+      }
+      const long ub0 = lo((long)b * kCompute), ub1 = lo((long)(b + 1) * kCompute);
+      int tm0 = 0, ntm = 0;
+      if (ub0 < ub1) {
+        tm0 = (int)(ub0 / nsb);
+        ntm = (int)((ub1 - 1) / nsb) - tm0 + 1;
+        if (ntm > kMaxTm) return false;
+        for (int i = 0; i < ntm; ++i) {
+          const long tm = tm0 + i;
+          const long p0 = std::max(tm * nsb, ub0), p1 = std::min((tm + 1) * nsb, ub1);
+          const long clo = wave_of(p0) - (long)b * kCompute, chi = wave_of(p1 - 1) - (long)b * kCompute;
+          const long rank = b - first_block(tm);
+          if (clo < 0 || chi >= kCompute || rank < 0 || rank > 255) return false;
+          p.tmc[k][i][0] = (uint8_t)clo;
+          p.tmc[k][i][1] = (uint8_t)chi;
+          p.tmc[k][i][2] = (uint8_t)rank;
+        }
+      }
+      const int own0 = (int)((long)ntiles[k] * b / grid), own1 = (int)((long)ntiles[k] * (b + 1) / grid);
+      if (own1 - own0 > kMaxOwn) return false;
+      for (int o = 0; o < own1 - own0; ++o) {
+        const long tau = own0 + o;
+        const long n0 = n_blocks(tau * nms[k]), n1 = nms[k] == 2 ? n_blocks(tau * nms[k] + 1) : 0;
+        if (n0 > 255 || n1 > 255) return false;
+        p.oc[k][o][0] = (uint8_t)n0;
+        p.oc[k][o][1] = (uint8_t)n1;
+      }
+      p.kp[k][0] = tm0;
+      p.kp[k][1] = ntm;
+      p.kp[k][2] = own0;
+      p.kp[k][3] = own1 - own0;
+    }
+  }
+  return true;
+}
 
 int valid_q(const mk_q4k& w, int n_out, int n_in) {
   return w.blocks && w.n_out == n_out && w.n_in == n_in && ((uintptr_t)w.blocks % 256) == 0;
@@ -1601,9 +1713,16 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
   if ((uintptr_t)ws % 256) return sfail(MK_ERR_ALIGN, "decode: workspace not 256-B aligned");
   hipStream_t s = (hipStream_t)stream;
   uint8_t* w8 = (uint8_t*)ws;
+  if (st->plans_grid != y.grid) {
+    if (!make_plans(st->d, y.grid, st->plans)) return sfail(MK_ERR_SHAPE, "decode: shapes too small for the grid's work plan");
+    st->plans_grid = y.grid;
+    st->uploaded_ws = nullptr;
+  }
   if (st->uploaded_ws != ws) {
     if (hipMemcpyAsync(w8 + y.off_table, st->layers.data(), sizeof(LayerW) * st->layers.size(),
-                       hipMemcpyHostToDevice, s) != hipSuccess)
+                       hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipMemcpyAsync(w8 + y.off_plans, st->plans.data(), sizeof(BlockPlan) * st->plans.size(), hipMemcpyHostToDevice,
+                       s) != hipSuccess)
       return sfail(MK_ERR_LAUNCH, "decode: weight table upload failed");
     st->uploaded_ws = ws;
   }
@@ -1625,6 +1744,7 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
   a.cmax4 = 0;
   for (int i = 0; i < 4; ++i) a.cmax4 |= y.cmax[i] << (8 * i);
   a.layers = (const LayerW*)(w8 + y.off_table);
+  a.plans = (const BlockPlan*)(w8 + y.off_plans);
   a.lm = d.lm_head;
   for (int l = 0; l < d.n_layers; ++l)
     if (st->gdn_flag[l]) a.gdn_mask[l >> 6] |= 1ull << (l & 63);
