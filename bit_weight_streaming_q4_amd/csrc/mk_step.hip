@@ -60,12 +60,13 @@ constexpr int kMaxLayers = 128;
 constexpr int kTicketTiles = 512;  // tickets per phase instance (max n_out / 64)
 constexpr int kTicketStride = 16;  // counters 64 B apart
 constexpr int kGdnHeadsPerLayer = 32;
-constexpr int kBlock = 448;
+constexpr int kBlock = 512;
 constexpr int kWavesPerBlock = kBlock / 64;
 constexpr int kCompute = 4;        // compute waves per block (one per SIMD): waves 0..3
-constexpr int kServiceWave = 4;    // partials, tickets, epilogues
+constexpr int kServiceWave = 4;    // the block's contributions: mailboxes -> partials, tickets
 constexpr int kGdnWave = 5;        // the block's Gated DeltaNet jobs
 constexpr int kWatchWave = 6;      // opens phases when their inputs are complete
+constexpr int kOwnerWave = 7;      // epilogues of the tiles the block owns, prep, lm_prep
 constexpr int kRdySlots = 8;       // finished-tile counters per producer phase (block b adds to b % 8)
 constexpr int kRdyStride = 32;     // u32 between counters (one 128-B line each)
 // Activation record of one GEMV input, per superblock b (256 values of K),
@@ -987,28 +988,13 @@ __device__ __forceinline__ void svc_epilogue(const StepArgs& a, int q, int tau, 
 // contributions on the tiles' tickets (one atomic per tile), and, as owner,
 // wait for each owned tile's count to complete and run its epilogue.
 template <int T>
-__device__ __forceinline__ bool svc_phase(const StepArgs& a, BlockState<T>& s, int q, int lane, bool ok) {
+__device__ __forceinline__ bool svc_contrib(const StepArgs& a, BlockState<T>& s, int q, int lane, bool ok) {
   constexpr int TP = TPad<T>::value;
   const int l = q >> 2, ph = q & 3;
   const int nm = ph == 2 ? 2 : 1;
   const int tm0 = uniform(s.plan.kp[ph][0]), ntm = uniform(s.plan.kp[ph][1]);
   const int own0 = uniform(s.plan.kp[ph][2]), nown = uniform(s.plan.kp[ph][3]);
-  float r[T], xo[2][T];
-#pragma unroll
-  for (int t = 0; t < T; ++t) r[t] = xo[0][t] = xo[1][t] = 0.0f;
-  // the row factors need every tile of the phase input (its sums of squares)
   if (!wait_ge(a, s, &s.rel, q + 1)) return false;
-  if (nown > 0) {
-    if (ph == 0 || ph == 2) {
-      rnorm_rows<T>(a, ph == 0 ? 2 * l : 2 * l + 1, lane, r);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        if (i < nown)
-#pragma unroll
-          for (int t = 0; t < T; ++t) xo[i][t] = ld_coh(a.x + (size_t)t * a.H + (own0 + i) * 64 + lane);
-    }
-  }
   if (!ok) return ok;
   unsigned* tk = a.tickets + ((size_t)l * 4 + ph) * kTicketTiles * kTicketStride;
   if (ntm > 0) {
@@ -1066,6 +1052,34 @@ __device__ __forceinline__ bool svc_phase(const StepArgs& a, BlockState<T>& s, i
       __hip_atomic_fetch_add(tk + (size_t)tau * kTicketStride, (unsigned)cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+  return true;
+}
+
+template <int T>
+__device__ __forceinline__ bool svc_own(const StepArgs& a, BlockState<T>& s, int q, int lane, bool ok) {
+  constexpr int TP = TPad<T>::value;
+  const int l = q >> 2, ph = q & 3;
+  const int nm = ph == 2 ? 2 : 1;
+  const int tm0 = uniform(s.plan.kp[ph][0]), ntm = uniform(s.plan.kp[ph][1]);
+  const int own0 = uniform(s.plan.kp[ph][2]), nown = uniform(s.plan.kp[ph][3]);
+  float r[T], xo[2][T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) r[t] = xo[0][t] = xo[1][t] = 0.0f;
+  // the row factors need every tile of the phase input (its sums of squares)
+  if (!wait_ge(a, s, &s.rel, q + 1)) return false;
+  if (nown > 0) {
+    if (ph == 0 || ph == 2) {
+      rnorm_rows<T>(a, ph == 0 ? 2 * l : 2 * l + 1, lane, r);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (i < nown)
+#pragma unroll
+          for (int t = 0; t < T; ++t) xo[i][t] = ld_coh(a.x + (size_t)t * a.H + (own0 + i) * 64 + lane);
+    }
+  }
+  if (!ok) return ok;
+  unsigned* tk = a.tickets + ((size_t)l * 4 + ph) * kTicketTiles * kTicketStride;
   // owned tiles: wait for all contributions, then the epilogue
   for (int o = 0; o < nown; ++o) {
     const int tau = own0 + o;
@@ -1131,11 +1145,20 @@ __device__ __forceinline__ void svc_lm_prep(const StepArgs& a, int lane, const f
   }
 }
 
+// The contributions of the block, phase after phase.
 template <int T>
-__device__ __forceinline__ void service_wave(const StepArgs& a, BlockState<T>& s, int lane) {
+__device__ __forceinline__ void contrib_wave(const StepArgs& a, BlockState<T>& s, int lane) {
+  bool ok = true;
+  for (int q = 0; q < 4 * a.L && ok; ++q) ok = svc_contrib<T>(a, s, q, lane, ok);
+}
+
+// The epilogues of the block's tiles, phase after phase; then lm_prep and the
+// step's one grid barrier.
+template <int T>
+__device__ __forceinline__ void owner_wave(const StepArgs& a, BlockState<T>& s, int lane) {
   svc_prep<T>(a, lane, s.stage);
   bool ok = true;
-  for (int q = 0; q < 4 * a.L && ok; ++q) ok = svc_phase<T>(a, s, q, lane, ok);
+  for (int q = 0; q < 4 * a.L && ok; ++q) ok = svc_own<T>(a, s, q, lane, ok);
   // lm_prep needs the final residual: every tile of the last phase
   if (!ok || !wait_ge(a, s, &s.rel, 4 * a.L + 1)) return;
   float r[T];
@@ -1379,7 +1402,9 @@ __global__ __launch_bounds__(kBlock) void k_decode_step(StepArgs a) {
   if (wib < kCompute) {
     compute_wave<T>(a, s, wib, lane);
   } else if (wib == kServiceWave) {
-    service_wave<T>(a, s, lane);
+    contrib_wave<T>(a, s, lane);
+  } else if (wib == kOwnerWave) {
+    owner_wave<T>(a, s, lane);
   } else if (wib == kWatchWave) {
     watch_wave<T>(a, s, lane);
   } else {
