@@ -1251,8 +1251,8 @@ __device__ __forceinline__ void lm_load(const StepArgs& a, int v0, int c, int l,
     const int v = v0 + 16 * g + vl;
     const int vv = v < a.V ? v : a.V - 1;  // in-range row; results of rows >= V are never used
     const u32x4* wpp = (const u32x4*)(a.lm + (size_t)vv * a.H + 64 * c + 16 * kq);
-    x.wa[g][0] = __builtin_nontemporal_load(wpp);
-    x.wa[g][1] = __builtin_nontemporal_load(wpp + 1);
+    x.wa[g][0] = wpp[0];
+    x.wa[g][1] = wpp[1];
   }
 }
 
@@ -1297,13 +1297,21 @@ __device__ __forceinline__ void lm_phase(const StepArgs& a, float (*red)[64][16]
 #pragma unroll
     for (int g = 0; g < 4; ++g) acc[g] = (f32x4){0.f, 0.f, 0.f, 0.f};
     LmChunk b0c, b1c;  // ping-pong: the next chunk's loads are issued before this chunk's MFMAs
-    if (c0 < c1) lm_load(a, v0, c0, l, vl, kq, b0c);
-    for (int c = c0; c < c1; c += 2) {
-      if (c + 1 < c1) lm_load(a, v0, c + 1, l, vl, kq, b1c);
-      lm_mfma(b0c, acc);
-      if (c + 1 >= c1) break;
-      if (c + 2 < c1) lm_load(a, v0, c + 2, l, vl, kq, b0c);
-      lm_mfma(b1c, acc);
+    // The loads are unconditional (a chunk past the wave's range re-reads its
+    // last one, unused) and the scheduling barriers pin their position, so
+    // that both buffers keep their registers and a load is always in flight.
+    if (c0 < c1) {
+      lm_load(a, v0, c0, l, vl, kq, b0c);
+      for (int c = c0; c < c1; c += 2) {
+        lm_load(a, v0, c + 1 < c1 ? c + 1 : c1 - 1, l, vl, kq, b1c);
+        __builtin_amdgcn_sched_barrier(0);
+        lm_mfma(b0c, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        lm_load(a, v0, c + 2 < c1 ? c + 2 : c1 - 1, l, vl, kq, b0c);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + 1 < c1) lm_mfma(b1c, acc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g)
