@@ -170,6 +170,95 @@ def time_steps(stack, T, gs, n_agents, xs, gin, steps, warmup):
     return r
 
 
+# ------------------------------------------------------------------ standalone entry points
+def _time_calls(fn, n, warm=3):
+    """Mean ms per call of fn(i) over n calls, from events on the current stream."""
+    import torch
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        fn(warm + i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def kernel_bench(lm, device="cuda"):
+    """The standalone entry points at the pages' single-kernel workloads, each
+    on rotating device copies of its weights (more bytes than the 256 MB
+    Infinity Cache, so every call streams from HBM): the T-row GEMV (5120 x
+    5120), the FFN block (5120 -> 17408 -> 5120, T = 5), lm_head + verify
+    (151936 x 5120 and the 32768-row draft prefix, T = 5) and the Gated
+    DeltaNet step + commit (48 x 32 heads of 128 x 128, T = 5)."""
+    import torch
+
+    import bit_weight_streaming_q4_amd as mk
+    from synth import recipes
+    out = {}
+
+    def rec(name, ms, nbytes):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"us": round(ms * 1e3, 2), "gb_s": round(gbs, 1), "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4),
+                     "bytes": int(nbytes)}
+        log(f"kernel {name}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s")
+
+    # T-row GEMV, 64 copies (944 MB)
+    W = mk.pack_to_device(recipes.gemv_weight(), device)
+    copies = [W] + [mk.Q4K(W.blocks.clone(), W.n_out, W.n_in) for _ in range(63)]
+    for T in (1, 5, 12):
+        x = torch.from_numpy(recipes.rows_f32(T, HIDDEN)).to(device)
+        y = torch.empty(T, HIDDEN, dtype=torch.float32, device=device)
+        ws = mk.workspace(mk.mk_qgemv_rows_workspace(T, HIDDEN, HIDDEN), device)
+        ms = _time_calls(lambda i: mk.mk_qgemv_rows(copies[i % 64], x, y, ws=ws), 128)
+        rec(f"qgemv_5120x5120_T{T}", ms, HIDDEN * HIDDEN // 256 * 144 + T * 2 * HIDDEN * 4)
+    del copies, W
+    # FFN block, 4 copies (602 MB)
+    fw = recipes.ffn_weights()
+    g0, u0, d0 = (mk.pack_to_device(fw[m], device) for m in ("gate", "up", "down"))
+    del fw
+    sets = [(g0, u0, d0)] + [tuple(mk.Q4K(w.blocks.clone(), w.n_out, w.n_in) for w in (g0, u0, d0)) for _ in range(3)]
+    for T in (5,):
+        x = torch.from_numpy(recipes.rows_f32(T, HIDDEN)).to(device)
+        y = torch.empty(T, HIDDEN, dtype=torch.float32, device=device)
+        ws = mk.workspace(mk.mk_ffn_rows_workspace(T, HIDDEN, FFN), device)
+        ms = _time_calls(lambda i: mk.mk_ffn_rows(*sets[i % 4], x, y, ws=ws), 32)
+        rec(f"ffn_5120_17408_T{T}", ms, 3 * HIDDEN * FFN // 256 * 144 + T * (2 * HIDDEN + 2 * FFN) * 4)
+    del sets, g0, u0, d0
+    torch.cuda.empty_cache()
+    # lm_head + verify, T = 5 (one group, 4 drafts); full vocabulary and draft prefix
+    T = 5
+    hid = torch.from_numpy(recipes.lm_hidden(T)).to(device)
+    drafts = torch.from_numpy(recipes.uniform_i32(3, 50, 0, T - 1, 0, VOCAB - 1)).to(device)
+    am = torch.empty(T, dtype=torch.int32, device=device)
+    na = torch.empty(1, dtype=torch.int32, device=device)
+    tok = torch.empty(T, dtype=torch.int32, device=device)
+    for V in (VOCAB, recipes.DRAFT_VOCAB):
+        ws = mk.workspace(mk.mk_lmhead_verify_workspace(V, HIDDEN, T), device)
+        ms = _time_calls(lambda i: mk.mk_lmhead_verify(lm, hid, None, drafts, am, na, tok, ws=ws, V=V), 20)
+        rec(f"lmhead_verify_V{V}_T{T}", ms, V * HIDDEN * 2 + T * HIDDEN * 4)
+    # Gated DeltaNet step + commit, 48 x 32 heads, T = 5, seeded accept lengths
+    nh = 48 * 32
+    st = mk.DeltaNetState(nh, T, device=device,
+                          S=torch.from_numpy(recipes.gdn_initial_state().reshape(nh, 128, 128)).to(device))
+    g = recipes.gdn_step(0, T)
+    gin = [torch.from_numpy(g[k]).to(device) for k in ("q", "k", "v", "g", "beta")]
+    o = torch.empty(T, nh, 128, dtype=torch.float32, device=device)
+    acc = recipes.gdn_accept_lengths(64, T)
+
+    def gdn(i):
+        st.n_acc[0:1].fill_(int(acc[i % 64]))
+        mk.mk_deltanet_step(st, *gin, o)
+    ms = _time_calls(gdn, 32)
+    io = T * nh * (3 * 128 + 2) * 4 + T * nh * 128 * 4
+    rec(f"deltanet_step_48x32_T{T}", ms, 2 * nh * 128 * 128 * 4 + io + nh * 258 * 4 * (T - 1) * 2)
+    del st
+    torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------------ CPU baseline
 def cpu_baseline(T=12):
     """The oracle (as it stands) on a bounded sample of the same step: one
@@ -199,6 +288,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only-primary", action="store_true", help="measure T = 12 only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernels", action="store_true", help="skip the standalone entry-point timings")
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the HBM byte counters)")
@@ -255,6 +345,7 @@ def main():
         tj = json.load(open(TRAFFIC_FILE))
         if tj.get("kernel_source_hash") == kernel_source_hash():
             traffic = tj.get("bytes_per_launch")
+    kernels = None if args.no_kernels else kernel_bench(lm)
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     out = {
         "metric": "weight-stream GB/s (% of 8 TB/s) and decode steps/s at T=1,5,12 rows",
@@ -278,7 +369,8 @@ def main():
                                       "steps_per_s": round(r["steps_per_s"], 2),
                                       "rows_steps_per_s": round(r["steps_per_s"] * T, 1),
                                       "weight_gb_s": round(r["weight_gb_s"], 1),
-                                      "total_gb_s": round(r["total_gb_s"], 1)} for T, r in results.items()}},
+                                      "total_gb_s": round(r["total_gb_s"], 1)} for T, r in results.items()},
+                   "standalone_kernels": kernels},
         "roofline": {"bound": "hbm", "achieved": round(p["kernel_gb_s"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(p["kernel_gb_s"] / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "k_decode_step<12>", "kernel_ms": round(p["kernel_ms"], 4),

@@ -83,8 +83,8 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
       const int v = v0 + 16 * g + vl;
       if (v < a.V) {
         const u32x4* wp = (const u32x4*)(a.W + (size_t)v * a.H + 64 * c + 16 * kq);
-        wa[g][0] = __builtin_nontemporal_load(wp);
-        wa[g][1] = __builtin_nontemporal_load(wp + 1);
+        wa[g][0] = wp[0];  // cached: the two half-line loads of a row merge in L2
+        wa[g][1] = wp[1];
       } else {
         wa[g][0] = (u32x4){0u, 0u, 0u, 0u};
         wa[g][1] = (u32x4){0u, 0u, 0u, 0u};
