@@ -352,31 +352,70 @@ __device__ __forceinline__ uint8_t* phase_input(const StepArgs& a, int l, int ph
   return act_rec(a, l, ph == 0 ? K_X : ph == 1 ? K_U : ph == 2 ? K_X2 : K_H);
 }
 
-// Quantizes, per row t < T, the 64 values val[t] (lane = column of tile tau
-// of the record's K) and writes the tile's part of the record: its two
-// sub-blocks' 1024 code bytes ([j][q][t][8 B]; rows T..15 zero) and their
-// 2 x 16 scales and scaled code sums.  Both are staged in LDS so that each
-// goes out as one 16-B store per lane.  Column c of superblock b = tau / 4:
-// sub-block j = (c % 256) / 32, octet q = (c % 32) / 8, byte c % 8.
+// Row-group form of a 64-column tile's rows, used by the epilogues: lane
+// 16 tr + cq holds rows tr, tr + 4, ... (TP / 4 of them) at columns 4 cq ..
+// 4 cq + 3.  A 32-column quantization group is then 8 lanes of one row.
 template <int T>
-__device__ __forceinline__ void store_q8(uint8_t* rec, int tau, int lane, const float (&val)[T], uint8_t* stage) {
-  const int jj = lane >> 5, e = lane & 31;
-  uint8_t* cb = stage + ((jj * 4 + (e >> 3)) * 16) * 8 + (e & 7);
+struct RG {
+  static constexpr int TP = TPad<T>::value;
+  static constexpr int G = TP / 4;  // rows per lane
+};
+
+// max / sum over an aligned group of 8 lanes (lane ^ 1, lane ^ 2, half-row
+// mirror), and sums over a 16-lane row (plus the row mirror)
+__device__ __forceinline__ float max8(float v) {
+  v = __builtin_fmaxf(v, dpp_f<0xB1>(v));
+  v = __builtin_fmaxf(v, dpp_f<0x4E>(v));
+  return __builtin_fmaxf(v, dpp_f<0x141>(v));
+}
+__device__ __forceinline__ int sum8_i(int v) {
+  v += dpp_i<0xB1>(v);
+  v += dpp_i<0x4E>(v);
+  return v + dpp_i<0x141>(v);
+}
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  return v + dpp_f<0x140>(v);
+}
+
+// Quantizes the tile's rows (row-group form; rows >= T hold zeros) and
+// writes the tile's part of the record: its two sub-blocks' 1024 code bytes
+// ([j][q][t][8 B]) and their 2 x 16 scales and scaled code sums.  Both are
+// staged in LDS (rows >= TP stay zero there from the start of the launch) so
+// that each goes out as one 16-B store per lane.  Group g of row t: lanes
+// 16 tr + 8 g .. + 7; each lane's 4 codes are one dword of the record:
+// sub-block j = g, octet q = (cq % 8) / 2, bytes 4 (cq % 2) .. + 3.
+template <int T>
+__device__ __forceinline__ void store_q8(uint8_t* rec, int tau, int lane, const f32x4 (&val)[RG<T>::G],
+                                         uint8_t* stage) {
+  const int tr = lane >> 4, cq = lane & 15;
+  const int jj = cq >> 3, q = (cq & 7) >> 1;
+  uint8_t* cb = stage + (jj * 4 + q) * 128 + (cq & 1) * 4;
   float* sst = (float*)(stage + 1024);  // [s: 2 x 16][s * gsum: 2 x 16]
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const Q8 q = quant_group32(val[t]);
-    cb[t * 8] = (uint8_t)q.a8;
-    if (e == 0) {
-      sst[jj * 16 + t] = q.s;
-      sst[32 + jj * 16 + t] = q.s * (float)q.gsum;
-    }
-  }
+  for (int k = 0; k < RG<T>::G; ++k) {
+    const int t = tr + 4 * k;
+    const f32x4 x = val[k];
+    float amax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(x[0]), __builtin_fabsf(x[1])),
+                                 __builtin_fmaxf(__builtin_fabsf(x[2]), __builtin_fabsf(x[3])));
+    amax = max8(amax);
+    float sc = 0.0f;
+    int c[4] = {0, 0, 0, 0};
+    if (amax != 0.0f) {
+      sc = amax / 127.0f;
 #pragma unroll
-  for (int t = T; t < kTPad; ++t) cb[t * 8] = 0;
-  if (e < kTPad - T) {
-    sst[jj * 16 + T + e] = 0.0f;
-    sst[32 + jj * 16 + T + e] = 0.0f;
+      for (int i = 0; i < 4; ++i)
+        c[i] = (int)__builtin_fminf(__builtin_fmaxf(__builtin_rintf(x[i] / sc), -127.0f), 127.0f);
+    }
+    const int gsum = sum8_i(c[0] + c[1] + c[2] + c[3]);
+    *(uint32_t*)(cb + t * 8) =
+        (uint32_t)(c[0] & 255) | ((uint32_t)(c[1] & 255) << 8) | ((uint32_t)(c[2] & 255) << 16) | ((uint32_t)c[3] << 24);
+    if ((cq & 7) == 0) {
+      sst[jj * 16 + t] = sc;
+      sst[32 + jj * 16 + t] = sc * (float)gsum;
+    }
   }
   uint8_t* blk = rec + (size_t)(tau >> 2) * kActBytes;
   st16(blk, (tau & 3) * 1024 + lane * 16, *(const f32x4*)(stage + lane * 16));
@@ -384,6 +423,33 @@ __device__ __forceinline__ void store_q8(uint8_t* rec, int tau, int lane, const 
     const int j0 = (tau & 3) * 2;
     const int fo = lane < 8 ? j0 * 16 + lane * 4 : 128 + j0 * 16 + (lane - 8) * 4;
     st16(blk + kActA, fo * 4, *(const f32x4*)(stage + 1024 + lane * 16));
+  }
+}
+
+// Sums of squares of the tile's rows (row-group form) into its 16 slots
+// (slot t < TP; rows >= T are zero).
+template <int T>
+__device__ __forceinline__ void store_ss(float* ss16, int lane, const f32x4 (&x)[RG<T>::G]) {
+  const int tr = lane >> 4, cq = lane & 15;
+#pragma unroll
+  for (int k = 0; k < RG<T>::G; ++k) {
+    float p = x[k][0] * x[k][0];
+    p = __builtin_fmaf(x[k][1], x[k][1], p);
+    p = __builtin_fmaf(x[k][2], x[k][2], p);
+    p = __builtin_fmaf(x[k][3], x[k][3], p);
+    p = sum16(p);
+    if (cq == 0) st_coh(ss16 + tr + 4 * k, p);
+  }
+}
+
+// The tile's rows of x (row-group form), rows >= T zero.
+template <int T>
+__device__ __forceinline__ void load_rows(const float* x, int H, int tau, int lane, f32x4 (&v)[RG<T>::G]) {
+  const int tr = lane >> 4, cq = lane & 15;
+#pragma unroll
+  for (int k = 0; k < RG<T>::G; ++k) {
+    const int t = tr + 4 * k;
+    v[k] = t < T ? ld16(x, ((t * H) + tau * 64 + cq * 4) * 4) : (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 }
 
@@ -421,19 +487,6 @@ __device__ __forceinline__ void rnorm_rows(const StepArgs& a, int ss_idx, int la
   }
 #pragma unroll
   for (int t = 0; t < T; ++t) r[t] = 1.0f / __builtin_sqrtf(wave_sum(acc[t / 4][t % 4]) / (float)a.H + kRmsEps);
-}
-
-// Sums of squares of the T rows of a 64-column tile into its 16 slots (lane t
-// writes slot t; slots T..15 are zero).
-template <int T>
-__device__ __forceinline__ void store_ss(float* ss16, int lane, const float (&x)[T]) {
-  float mine = 0.0f;
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const float s2 = wave_sum(x[t] * x[t]);
-    if (lane == t) mine = s2;
-  }
-  if (lane < kTPad) st_coh(ss16 + lane, mine);
 }
 
 // ------------------------------------------------------------ compute waves
@@ -880,9 +933,8 @@ template <int T>
 __device__ __forceinline__ void svc_prep(const StepArgs& a, int lane, uint8_t* stage) {
   const int ntH = a.H / 64;
   for (int tau = blockIdx.x; tau < ntH; tau += gridDim.x) {
-    float xv[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) xv[t] = ld_coh(a.x + (size_t)t * a.H + tau * 64 + lane);
+    f32x4 xv[RG<T>::G];
+    load_rows<T>(a.x, a.H, tau, lane, xv);
     store_ss<T>(a.ss + (size_t)tau * 16, lane, xv);
     store_q8<T>(act_rec(a, 0, K_X), tau, lane, xv, stage);
   }
@@ -894,45 +946,41 @@ __device__ __forceinline__ void svc_prep(const StepArgs& a, int lane, uint8_t* s
 }
 
 // Sum of the block partials of (tile, matrix) pairs tau*nm + m, m < nm (n0
-// and n1 contributing blocks), in block order; all loads of up to
-// kPartBatch partials are issued together.  A partial is [64 rows][TP].
+// and n1 contributing blocks), in block order, in row-group form; all loads
+// of up to kPartBatch partials are issued together.  A partial is
+// [TP rows][64 columns].
 template <int T>
 __device__ __forceinline__ void sum_partials(const StepArgs& a, int q, int nm, int tau, int n0, int n1, int lane,
-                                             float (&v0)[T], float (&v1)[T]) {
-  constexpr int TP = TPad<T>::value;
+                                             f32x4 (&v0)[RG<T>::G], f32x4 (&v1)[RG<T>::G]) {
+  constexpr int TP = RG<T>::TP, G = RG<T>::G;
   const int ph = q & 3;
   const float* part = a.part + (size_t)(q & 1) * a.part_half;
   const int tm0 = tau * nm;
   const int n = n0 + n1, cm = (a.cmax4 >> (8 * ph)) & 255;
-  f32x4 s0[TP / 4], s1[TP / 4];
+  const int lo = ((lane >> 4) * 64 + (lane & 15) * 4) * 4;  // bytes: row tr, column 4 cq
 #pragma unroll
-  for (int i = 0; i < TP / 4; ++i) s0[i] = s1[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < G; ++k) v0[k] = v1[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
   for (int e0 = 0; e0 < n; e0 += kPartBatch) {
-    f32x4 tmp[kPartBatch][TP / 4];
+    f32x4 tmp[kPartBatch][G];
 #pragma unroll
     for (int i = 0; i < kPartBatch; ++i) {
       const int e = e0 + i < n ? e0 + i : n - 1;  // in-range address; extra values are not added
       const int m = e < n0 ? 0 : 1, r = e < n0 ? e : e - n0;
-      const int off = (((tm0 + m) * cm + r) * 64 + lane) * TP * 4;
+      const int off = ((tm0 + m) * cm + r) * TP * 64 * 4 + lo;
 #pragma unroll
-      for (int k = 0; k < TP / 4; ++k) tmp[i][k] = ld16(part, off + k * 16);
+      for (int k = 0; k < G; ++k) tmp[i][k] = ld16(part, off + k * 4 * 64 * 4);
     }
 #pragma unroll
     for (int i = 0; i < kPartBatch; ++i) {
       if (e0 + i >= n) break;
 #pragma unroll
-      for (int k = 0; k < TP / 4; ++k) {
+      for (int k = 0; k < G; ++k) {
         if (e0 + i < n0)
-          s0[k] += tmp[i][k];
+          v0[k] += tmp[i][k];
         else
-          s1[k] += tmp[i][k];
+          v1[k] += tmp[i][k];
       }
     }
-  }
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    v0[t] = s0[t / 4][t % 4];
-    v1[t] = s1[t / 4][t % 4];
   }
 }
 
@@ -942,36 +990,45 @@ __device__ __forceinline__ void sum_partials(const StepArgs& a, int q, int nm, i
 // loaded at the start of the phase.
 template <int T>
 __device__ __forceinline__ void svc_epilogue(const StepArgs& a, int q, int tau, int n0, int n1, int lane,
-                                             const float (&r)[T], const float (&xo)[T], uint8_t* stage) {
+                                             const f32x4 (&r)[RG<T>::G], const f32x4 (&xo)[RG<T>::G],
+                                             uint8_t* stage) {
+  constexpr int G = RG<T>::G;
   const int l = q >> 2, ph = q & 3;
-  float v0[T], v1[T];
+  const int tr = lane >> 4, cq = lane & 15;
+  f32x4 v0[G], v1[G];
   sum_partials<T>(a, q, ph == 2 ? 2 : 1, tau, n0, n1, lane, v0, v1);
-  const int col = tau * 64 + lane;
-  if (ph == 0 || ph == 2) {
-    float y[T];
+  // rows >= T of a partial are not results (the dot-product engine leaves them unset)
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      if (ph == 0) {
-        y[t] = r[t] * v0[t];
-      } else {
-        const float g = r[t] * v0[t], u = r[t] * v1[t];
-        y[t] = g * u / (1.0f + expf(-g));
+  for (int k = 0; k < G; ++k)
+    if (tr + 4 * k >= T) v0[k] = v1[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  if (ph == 0 || ph == 2) {
+    f32x4 y[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (ph == 0) {
+          y[k][i] = r[k][i] * v0[k][i];
+        } else {
+          const float g = r[k][i] * v0[k][i], u = r[k][i] * v1[k][i];
+          y[k][i] = g * u / (1.0f + expf(-g));
+        }
       }
     }
     store_q8<T>(act_rec(a, l, ph == 0 ? K_U : K_H), tau, lane, y, stage);
   } else {
-    float xn[T];
+    f32x4 xn[G];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      xn[t] = xo[t] + v0[t];
-      st_coh(a.x + (size_t)t * a.H + col, xn[t]);
+    for (int k = 0; k < G; ++k) {
+      xn[k] = xo[k] + v0[k];
+      const int t = tr + 4 * k;
+      if (t < T) {
+        st16(a.x, (t * a.H + tau * 64 + cq * 4) * 4, xn[k]);
+        if (ph == 3 && a.trace) *(f32x4*)(a.trace + ((size_t)l * T + t) * a.H + tau * 64 + cq * 4) = xn[k];
+      }
     }
     const int ss_idx = ph == 1 ? 2 * l + 1 : 2 * l + 2;
     store_ss<T>(a.ss + ((size_t)ss_idx * (a.H / 64) + tau) * 16, lane, xn);
-    if (ph == 3 && a.trace) {
-#pragma unroll
-      for (int t = 0; t < T; ++t) a.trace[((size_t)l * T + t) * a.H + col] = xn[t];
-    }
     if (ph == 1)
       store_q8<T>(act_rec(a, l, K_X2), tau, lane, xn, stage);
     else if (l + 1 < a.L)
@@ -1023,21 +1080,25 @@ __device__ __forceinline__ bool svc_contrib(const StepArgs& a, BlockState<T>& s,
           return false;
         }
       }
+      // row-group form: lane 16 tr + cq sums rows tr + 4 j at columns 4 cq .. + 3
+      const int tr = lane >> 4, cq = lane & 15;
       f32x4 v[TP / 4];
 #pragma unroll
       for (int k = 0; k < TP / 4; ++k) v[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
       for (int c = c_lo; c <= c_hi; ++c) {
         const int k = ((have >> (NMB * c)) & 1ull) ? 0 : 1;
 #pragma unroll
-        for (int j = 0; j < TP / 4; ++j) v[j] += *(const f32x4*)&s.mb[c][k][lane][4 * j];
+        for (int j = 0; j < TP / 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[j][i] += s.mb[c][k][cq * 4 + i][tr + 4 * j];
       }
       for (int c = c_lo; c <= c_hi; ++c) {
         const int k = ((have >> (NMB * c)) & 1ull) ? 0 : 1;
         if (lane == 0) lds_st(&s.tag[c][k], 0);
       }
-      const int off = ((tm * cm + rank) * 64 + lane) * TP * 4;
+      const int off = (tm * cm + rank) * TP * 64 * 4 + (tr * 64 + cq * 4) * 4;
 #pragma unroll
-      for (int j = 0; j < TP / 4; ++j) st16(part, off + j * 16, v[j]);
+      for (int j = 0; j < TP / 4; ++j) st16(part, off + j * 4 * 64 * 4, v[j]);
     }
     // contributions: lane i counts this block's (tile, matrix) pairs of tile tau0 + i
     const int tm1 = tm0 + ntm - 1;
@@ -1062,20 +1123,29 @@ __device__ __forceinline__ bool svc_own(const StepArgs& a, BlockState<T>& s, int
   const int nm = ph == 2 ? 2 : 1;
   const int tm0 = uniform(s.plan.kp[ph][0]), ntm = uniform(s.plan.kp[ph][1]);
   const int own0 = uniform(s.plan.kp[ph][2]), nown = uniform(s.plan.kp[ph][3]);
-  float r[T], xo[2][T];
+  constexpr int G = RG<T>::G;
+  f32x4 rg[G], xo[2][G];
 #pragma unroll
-  for (int t = 0; t < T; ++t) r[t] = xo[0][t] = xo[1][t] = 0.0f;
+  for (int k = 0; k < G; ++k) rg[k] = xo[0][k] = xo[1][k] = (f32x4){0.f, 0.f, 0.f, 0.f};
   // the row factors need every tile of the phase input (its sums of squares)
   if (!wait_ge(a, s, &s.rel, q + 1)) return false;
   if (nown > 0) {
     if (ph == 0 || ph == 2) {
+      float r[T];
       rnorm_rows<T>(a, ph == 0 ? 2 * l : 2 * l + 1, lane, r);
+      const int tr = lane >> 4;
+#pragma unroll
+      for (int k = 0; k < G; ++k) {
+        float rk = 0.0f;
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          if (t == tr + 4 * k) rk = r[t];
+        rg[k] = (f32x4){rk, rk, rk, rk};
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        if (i < nown)
-#pragma unroll
-          for (int t = 0; t < T; ++t) xo[i][t] = ld_coh(a.x + (size_t)t * a.H + (own0 + i) * 64 + lane);
+        if (i < nown) load_rows<T>(a.x, a.H, own0 + i, lane, xo[i]);
     }
   }
   if (!ok) return ok;
@@ -1096,18 +1166,17 @@ __device__ __forceinline__ bool svc_own(const StepArgs& a, BlockState<T>& s, int
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    float xt[T];
+    f32x4 xt[G];
     if (o < 2) {
 #pragma unroll
-      for (int t = 0; t < T; ++t) xt[t] = o == 0 ? xo[0][t] : xo[1][t];
+      for (int k = 0; k < G; ++k) xt[k] = o == 0 ? xo[0][k] : xo[1][k];
     } else if (ph == 1 || ph == 3) {  // more owned tiles than prefetched (small grids)
-#pragma unroll
-      for (int t = 0; t < T; ++t) xt[t] = ld_coh(a.x + (size_t)t * a.H + tau * 64 + lane);
+      load_rows<T>(a.x, a.H, tau, lane, xt);
     } else {
 #pragma unroll
-      for (int t = 0; t < T; ++t) xt[t] = 0.0f;
+      for (int k = 0; k < G; ++k) xt[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
-    svc_epilogue<T>(a, q, uniform(tau), n0, n1, lane, r, xt, s.stage);
+    svc_epilogue<T>(a, q, uniform(tau), n0, n1, lane, rg, xt, s.stage);
   }
   // the owned tiles' outputs are complete: count them for the watchers
   if (nown > 0) {
@@ -1404,6 +1473,7 @@ __global__ __launch_bounds__(kBlock) void k_decode_step(StepArgs a) {
     s.rel = 0;
     s.abort = 0;
     s.gdn_done = 0;
+    for (int i = 0; i < (int)sizeof(s.stage) / 4; ++i) ((int*)s.stage)[i] = 0;
     if (blockIdx.x == 0) a.stamps[0] = wall_clock64();
   }
   __syncthreads();
