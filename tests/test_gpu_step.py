@@ -109,3 +109,84 @@ def test_decode_step_small_stack(T, gs):
     for a in range(G):
         mk.mk_deltanet_commit(st.agents[a])
         assert rel_err(to_np(st.agents[a].S), S_ref[a]) <= FP32_TOL
+
+
+# ---------------------------------------------------------------- full size
+# The benchmark's own workload and launch configuration: the 64-layer stack
+# (hidden 5120, projections 10240, FFN 17408), the 151,936-row lm_head and 48
+# Gated DeltaNet layers, one state per agent.  The oracle checks whole layers
+# teacher-forced at sampled depths, all rows of the argmax / verification,
+# and sampled GDN heads (outputs and the committed state).
+
+@pytest.fixture(scope="module")
+def full_stack():
+    torch = need_gpu()
+    import bench
+    from synth import recipes
+    mk = _mk()
+    mk.mk_init(0)
+    layers, lm = bench.build_stack(progress=False)
+    return {"layers": layers, "lm": lm, "gl": recipes.gdn_layers(bench.LAYERS)}
+
+
+@pytest.mark.parametrize("T,gs", [(12, [0, 3, 6, 9, 12]), (1, [0, 1])])
+def test_decode_step_full_size(full_stack, T, gs):
+    torch = need_gpu()
+    import bench
+    from synth import recipes
+    mk = _mk()
+    layers, lm, gl = full_stack["layers"], full_stack["lm"], full_stack["gl"]
+    G = len(gs) - 1
+    H, L = bench.HIDDEN, bench.LAYERS
+    say("decode full", T)
+    agents = bench.make_agents(G, len(gl), 5)
+    st = mk.Stack(layers, lm, gdn_layers=gl, agents=agents)
+    dry = mk.Stack(layers, lm)
+    x = recipes.stack_step_input(0, T)
+    # preview the argmax, then draft so that some groups accept some drafts
+    am_prev = torch.empty(T, dtype=torch.int32, device="cuda")
+    mk.mk_decode_step(dry, to_dev(x), gs, to_dev(np.zeros(max(T - G, 1), np.int32)), argmax=am_prev)
+    amp = to_np(am_prev)
+    drafts = []
+    for g in range(G):
+        for i in range(gs[g + 1] - gs[g] - 1):
+            drafts.append(int(amp[gs[g] + i]) if (i + g) % 3 != 2 else 7)
+    drafts = np.asarray(drafts if drafts else [0], np.int32)
+    inp = recipes.stack_gdn_inputs(0, T, len(gl))
+    gin = {k: to_dev(inp[k]) for k in ("q", "k", "v", "g", "beta")}
+    nh = len(gl) * 32
+    go = torch.empty(T, nh, 128, dtype=torch.float32, device="cuda")
+    trace = torch.empty(L, T, H, dtype=torch.float32, device="cuda")
+    am = torch.empty(T, dtype=torch.int32, device="cuda")
+    xd = to_dev(x)
+    tok, na = mk.mk_decode_step(st, xd, gs, to_dev(drafts), gdn=gin, gdn_o=go, argmax=am, trace=trace)
+    tr = to_np(trace)
+    assert np.array_equal(to_np(xd), tr[L - 1])
+    assert np.array_equal(to_np(am), amp)
+    # layers teacher-forced at sampled depths
+    for l in (0, 21, 42, L - 1):
+        Wl = {m: recipes.stack_weight(l, m) for m in MATS}
+        prev = x if l == 0 else tr[l - 1]
+        e = rel_err(tr[l], oracle.layer(prev, Wl))
+        say("layer", l, "err", e)
+        assert e <= FP32_TOL, (l, e)
+        del Wl
+    # final RMSNorm + lm_head argmax over the full vocabulary, verification
+    _check_head(recipes.stack_lm_head(), tr[L - 1], to_np(am), na, tok, gs, drafts[:T - G])
+    # Gated DeltaNet, sampled heads of every agent: outputs and committed state
+    og = to_np(go)
+    heads = [0, 517, nh - 1]
+    for a in range(G):
+        mk.mk_deltanet_commit(st.agents[a])
+    for a in range(G):
+        S0 = recipes.stack_gdn_state(a, len(gl)).reshape(nh, 128, 128)
+        S1 = to_np(st.agents[a].S)
+        r0, r1 = gs[a], gs[a + 1]
+        for hh in heads:
+            sl = {k: inp[k][r0:r1, hh:hh + 1] for k in inp}
+            Sref, oref = oracle.gdn_step(S0[hh:hh + 1].copy(), sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"],
+                                         int(na[a]))
+            assert rel_err(og[r0:r1, hh:hh + 1], oref) <= FP32_TOL, (a, hh)
+            assert rel_err(S1[hh:hh + 1], Sref) <= FP32_TOL, (a, hh)
+    del st, dry, agents
+    torch.cuda.empty_cache()
