@@ -7,41 +7,51 @@
 // committed through the accepted token); richland.au 4-agent article, "Why it
 // matters" (rows of several agents share one weight read per step).
 //
-// Phases of a step (a grid barrier after each):
+// Phases of a step:
 //   prep       q8(x) and the per-tile sums of squares of x (RMSNorm input)
 //   per layer  P_in    u  = r(x) * (P_in . q8(x))         -> q8(u)
 //              P_out   x += P_out . q8(u)                  -> q8(x), sums of squares
 //              gate/up h  = SiLU(r g) * (r u)              -> q8(h)
-//                      (+ Gated DeltaNet step per agent in GDN layers)
 //              down    x += W_down . q8(h)                 -> q8(x), sums of squares
+//              (+ one Gated DeltaNet step per agent in GDN layers, beside the pipeline)
 //   lm_prep    hid = r(x) * x, split into fp16 hi + lo fragments
 //   lm         logits, per-block argmax, last block: argmax, verify, accept
 //              lengths into the GDN states for the next step's replay
 // r(x)_t = 1/sqrt(mean(x_t^2) + 1e-6) multiplies the whole dot product of row
 // t, so the GEMV runs on q8 of the un-normalised row and the factor is applied
-// once in the epilogue.
+// once in the epilogue.  A phase opens once every tile of its input is
+// finished (no grid barrier); the step has one grid barrier, before the lm
+// phase.
 //
 // Roles inside a block of 8 waves (one block per CU):
-//   compute waves (7)  Each walks a fixed stream of weight units (64 rows x
+//   compute waves (4)  Each walks a fixed stream of weight units (64 rows x
 //                      one superblock = 9216 B) through all phases of the
-//                      step, with the loads of the next 3 units always in
-//                      flight in registers.  The stream does not stop at a
-//                      phase end: the first units of the next phase load
-//                      while the wave waits for the grid barrier that makes
-//                      that phase's activations ready.  A wave's partial
-//                      sums of a (tile, matrix) go to an LDS mailbox; it
-//                      never writes global memory, so its vector-memory
-//                      counter only ever holds its own weight loads.
-//   service wave (1)   Sums the mailboxes of its block per (tile, matrix) in
-//                      wave order, stores one partial per block, takes the
-//                      tiles' tickets (the last block to contribute runs the
-//                      tile's epilogue: sum of partials in block order,
-//                      RMSNorm factor, SiLU, residual, q8 of the outputs),
-//                      runs the block's Gated DeltaNet jobs, the prep and
-//                      lm_prep phases and the grid barrier.
+//                      step, loading each unit and the activation record of
+//                      its superblock into a private 2-slot LDS ring with
+//                      LDS-DMA; the first units of the next phase load while
+//                      the wave waits for that phase to open.  A wave's
+//                      partial sums of a (tile, matrix) go to an LDS mailbox;
+//                      it never writes global memory, so its vector-memory
+//                      counter only ever holds its own loads.
+//   contribution (1)   Sums the block's mailboxes per (tile, matrix) in wave
+//                      order, stores one partial per block and counts it on
+//                      the tile's ticket.
+//   owner (1)          For the tiles the block owns (equal shares per phase):
+//                      waits for the ticket, sums the partials in block
+//                      order, then RMSNorm factor, SiLU, residual, q8 of the
+//                      outputs into the next activation record, sums of
+//                      squares; counts its finished tiles; also prep,
+//                      lm_prep and the final grid barrier.
+//   GDN (1)            The block's Gated DeltaNet half-head jobs of every GDN
+//                      layer (nothing in the layer pipeline reads them).
+//   watcher (1)        Opens the block's phases: block 0's watcher sums the
+//                      finished-tile counters of each producer phase and
+//                      writes the number of open phases into every block's
+//                      line; the others poll their own line.
 // Each GEMV phase is a line of units, tile-major; compute wave w of W takes
-// the contiguous stretch [S*w/W, S*(w+1)/W), so a block's stretch is the
-// union of its waves' and results do not depend on timing.
+// the contiguous stretch [S*w/W, S*(w+1)/W) (the host writes each block's
+// plan), so a block's stretch is the union of its waves' and results do not
+// depend on timing.
 #include <hip/hip_runtime.h>
 #include <string.h>
 
