@@ -353,7 +353,7 @@ int mk_lmhead_verify(const uint16_t* W_f16, int32_t V, int32_t H, const float* h
   if (!ws || ws_bytes < need) return fail(MK_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   if ((r = check_ptr(ws, "workspace", 256))) return r;
   return launch_status(mk::launch_lmhead(W_f16, V, H, hid, T, gs.data(), G, drafts, argmax, n_acc, tokens, ws,
-                                         S(stream)),
+                                         device_cu_count(), S(stream)),
                        "lm_head");
 }
 

@@ -54,6 +54,32 @@ __device__ __forceinline__ T* uniform(T* p) {
   return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Data shared between workgroups of one launch is stored and loaded with
+// device-scope (sc1) accesses, which are coherent across the XCDs' L2
+// caches without whole-cache write-back or invalidation.
+__device__ __forceinline__ void st_coh(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh_i8(int8_t* p, int8_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coh(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_coh_i(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The atomic may only be performed once this wave's stores are in memory.  A
+// workgroup-scope release fence does not wait for them on this target (the
+// waves of a workgroup share one L1), so the wait is explicit; with every
+// shared store device-scope (sc1), completion means visibility to all CUs.
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ unsigned ticket_add(unsigned* p, unsigned n = 1u) {
+  stores_done();
+  return __hip_atomic_fetch_add(p, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }

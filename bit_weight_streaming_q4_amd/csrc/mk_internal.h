@@ -48,7 +48,7 @@ namespace mk {
 size_t lm_workspace_bytes(int V, int H);
 hipError_t launch_lmhead(const uint16_t* W, int V, int H, const float* hid, int T, const int32_t* gs, int G,
                          const int32_t* drafts, int32_t* argmax, int32_t* n_acc, int32_t* tokens, void* ws,
-                         hipStream_t st);
+                         int cu_count, hipStream_t st);
 
 // Gated DeltaNet: one wave per half head (dk = dv = 128).
 struct GdnArgs {

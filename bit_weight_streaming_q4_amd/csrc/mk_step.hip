@@ -60,6 +60,7 @@
 
 #include "mk.h"
 #include "mk_device.h"
+#include "mk_lm.h"
 #include "mk_gdn.h"
 #include "mk_internal.h"
 
@@ -170,24 +171,12 @@ __device__ __forceinline__ P* fresh(P* p) {
 }
 
 // Cross-workgroup data of a step (partials, residual, sums of squares,
-// activations) is stored and loaded with device-scope (sc1) accesses, which
-// are coherent across the XCDs' L2 caches without whole-cache write-back or
-// invalidation; ordering comes from waiting for the stores (workgroup-scope
-// release) before the ticket/barrier atomic.  Activations are read through
-// the scalar cache: every activation buffer is written once per launch and
-// only read after its producer phase, so no stale line can be cached.
-__device__ __forceinline__ void st_coh(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_coh_i8(int8_t* p, int8_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_coh(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int ld_coh_i(const int* p) {
-  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// activations) is stored and loaded with device-scope (sc1) accesses;
+// ordering comes from waiting for the stores before the ticket or counter
+// atomic (ticket_add).  Activations are read through the scalar cache: every
+// activation buffer is written once per launch and only read after its
+// producer phase, so no stale line can be cached.
+//
 // 16-B device-scope (sc1) accesses through a buffer resource on a
 // wave-uniform base; off is the lane's byte offset.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
@@ -199,16 +188,6 @@ __device__ __forceinline__ f32x4 ld16(const void* base, int off) {
 }
 __device__ __forceinline__ void st16(void* base, int off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, rsrc(base), off, 0, kSc1);
-}
-
-// The atomic may only be performed once this wave's stores are in memory.  A
-// workgroup-scope release fence does not wait for them on this target (the
-// waves of a workgroup share one L1), so the wait is explicit; with every
-// shared store device-scope (sc1), completion means visibility to all CUs.
-__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ unsigned ticket_add(unsigned* p, unsigned n = 1u) {
-  stores_done();
-  return __hip_atomic_fetch_add(p, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Device-coherent reads through the scalar unit (glc): they bypass the
@@ -1312,144 +1291,19 @@ __device__ __forceinline__ void gdn_wave(const StepArgs& a, int lane) {
       for (long j = j0; j < j1; ++j) gdn_job(a, l, j, lane);
 }
 
-// One 64-wide hidden chunk of 64 vocabulary rows: the weight fragments of
-// the 4 row groups and the hi/lo fragments of the hidden rows.
-struct LmChunk {
-  u32x4 wa[4][2];
-  u32x4 bh0, bh1, bl0, bl1;
-};
-
-__device__ __forceinline__ void lm_load(const StepArgs& a, int v0, int c, int l, int vl, int kq, LmChunk& x) {
-  const u32x4* fp = (const u32x4*)(a.frag + ((size_t)c * 64 + l) * 32);
-  x.bh0 = fp[0];
-  x.bh1 = fp[1];
-  x.bl0 = fp[2];
-  x.bl1 = fp[3];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const int v = v0 + 16 * g + vl;
-    const int vv = v < a.V ? v : a.V - 1;  // in-range row; results of rows >= V are never used
-    const u32x4* wpp = (const u32x4*)(a.lm + (size_t)vv * a.H + 64 * c + 16 * kq);
-    x.wa[g][0] = wpp[0];
-    x.wa[g][1] = wpp[1];
-  }
-}
-
-__device__ __forceinline__ void lm_mfma(const LmChunk& x, f32x4 (&acc)[4]) {
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x.wa[g][0]),
-                                                    __builtin_bit_cast(f16x8, x.bh0), acc[g], 0, 0, 0);
-    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x.wa[g][0]),
-                                                    __builtin_bit_cast(f16x8, x.bl0), acc[g], 0, 0, 0);
-    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x.wa[g][1]),
-                                                    __builtin_bit_cast(f16x8, x.bh1), acc[g], 0, 0, 0);
-    acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x.wa[g][1]),
-                                                    __builtin_bit_cast(f16x8, x.bl1), acc[g], 0, 0, 0);
-  }
-}
-
-__device__ __forceinline__ bool lm_better(float va, int ia, float vb, int ib) {
-  if (ia < 0) return false;
-  if (ib < 0) return true;
-  if (va != va) return false;
-  if (vb != vb) return true;
-  return va > vb || (va == vb && ia < ib);
-}
-
+// The lm_head stream over the final hidden rows (fragments written by
+// lm_prep), then the argmax and the accept compare in the last block.
 __device__ __forceinline__ void lm_phase(const StepArgs& a, float (*red)[64][16]) {
-  constexpr int NW = kWavesPerBlock, TPT = 16;  // waves; threads per row t in the scans (256 of the block)
-  __shared__ int last;
   __shared__ int fin[16];
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
-  const int vl = l & 15, kq = l >> 4;
-  const int nc = a.H / 64;
-  const int c0 = (nc * w) / NW, c1 = (nc * (w + 1)) / NW;
-  const int nblk = (a.V + 63) / 64;
-  const bool scan = threadIdx.x < 16 * TPT;  // threads that scan: row t_own, every TPT-th vocabulary row
-  const int t_own = scan ? threadIdx.x / TPT : 0, part = threadIdx.x % TPT;
-  float best = 0.0f;
-  int bidx = -1;
-  for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
-    const int v0 = blk * 64;
-    f32x4 acc[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) acc[g] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    LmChunk b0c, b1c;  // ping-pong: the next chunk's loads are issued before this chunk's MFMAs
-    // The loads are unconditional (a chunk past the wave's range re-reads its
-    // last one, unused) and the scheduling barriers pin their position, so
-    // that both buffers keep their registers and a load is always in flight.
-    if (c0 < c1) {
-      lm_load(a, v0, c0, l, vl, kq, b0c);
-      for (int c = c0; c < c1; c += 2) {
-        lm_load(a, v0, c + 1 < c1 ? c + 1 : c1 - 1, l, vl, kq, b1c);
-        __builtin_amdgcn_sched_barrier(0);
-        lm_mfma(b0c, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        lm_load(a, v0, c + 2 < c1 ? c + 2 : c1 - 1, l, vl, kq, b0c);
-        __builtin_amdgcn_sched_barrier(0);
-        if (c + 1 < c1) lm_mfma(b1c, acc);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[w][16 * g + 4 * kq + i][vl] = acc[g][i];
-    __syncthreads();
-    for (int r = part; r < 64 && scan; r += TPT) {
-      const int v = v0 + r;
-      if (v >= a.V) break;
-      float xv = red[0][r][t_own];
-#pragma unroll
-      for (int q = 1; q < NW; ++q) xv += red[q][r][t_own];
-      if (lm_better(xv, v, best, bidx)) {
-        best = xv;
-        bidx = v;
-      }
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int m = TPT / 2; m >= 1; m >>= 1) {
-    const float ov = __shfl_xor(best, m, TPT);
-    const int oi = __shfl_xor(bidx, m, TPT);
-    if (lm_better(ov, oi, best, bidx)) {
-      best = ov;
-      bidx = oi;
-    }
-  }
-  if (scan && part == 0) {
-    st_coh(a.lm_val + (size_t)blockIdx.x * 16 + t_own, best);
-    st_coh((float*)a.lm_idx + (size_t)blockIdx.x * 16 + t_own, __builtin_bit_cast(float, bidx));
-  }
-  stores_done();  // every wave's stores are in memory before thread 0 takes the ticket
-  __syncthreads();
-  if (threadIdx.x == 0) last = (ticket_add(a.lm_ticket) == gridDim.x - 1);
-  __syncthreads();
-  if (!last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  best = 0.0f;
-  bidx = -1;
-  for (int b = part; b < (int)gridDim.x && scan; b += TPT) {
-    const float xv = ld_coh(a.lm_val + (size_t)b * 16 + t_own);
-    const int iv = ld_coh_i(a.lm_idx + (size_t)b * 16 + t_own);
-    if (lm_better(xv, iv, best, bidx)) {
-      best = xv;
-      bidx = iv;
-    }
-  }
-#pragma unroll
-  for (int m = TPT / 2; m >= 1; m >>= 1) {
-    const float ov = __shfl_xor(best, m, TPT);
-    const int oi = __shfl_xor(bidx, m, TPT);
-    if (lm_better(ov, oi, best, bidx)) {
-      best = ov;
-      bidx = oi;
-    }
-  }
-  if (scan && part == 0) fin[t_own] = bidx;
-  __syncthreads();
+  LmStream ls;
+  ls.W = a.lm;
+  ls.frag = a.frag;
+  ls.V = a.V;
+  ls.H = a.H;
+  ls.val = a.lm_val;
+  ls.idx = a.lm_idx;
+  ls.ticket = a.lm_ticket;
+  if (!lm_stream<kWavesPerBlock>(ls, red, fin)) return;
   if (threadIdx.x == 0) {
     for (int t = 0; t < a.T; ++t) a.out[48 + t] = fin[t];
     for (int g = 0; g < a.G; ++g) {
