@@ -186,6 +186,55 @@ def _time_calls(fn, n, warm=3):
     return e0.elapsed_time(e1) / n
 
 
+def _time_graph(fn, n, out, state=(), reps=3):
+    """Mean ms per call of fn(i), i < n, captured once in a HIP graph and
+    replayed, so that no host launch cost is in the figure.  Every checked
+    replay starts from the same device state (the tensors in state are
+    restored) and its output out() must equal that of the same n calls made
+    eagerly, with eager calls in between; returns (ms, same)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    snap = [t.clone() for t in state]
+
+    def restore():
+        for t, v in zip(state, snap):
+            t.copy_(v)
+
+    for i in range(n):
+        fn(i)
+    torch.cuda.synchronize()
+    ref = out().clone()
+    restore()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    same = True
+    for _ in range(2):
+        restore()
+        g.replay()
+        torch.cuda.synchronize()
+        same = same and bool(torch.equal(out(), ref))
+        fn(0)
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * n)
+    del g
+    restore()
+    return ms, same
+
+
 def kernel_bench(lm, device="cuda"):
     """The standalone entry points at the pages' single-kernel workloads, each
     on rotating device copies of its weights (more bytes than the 256 MB
@@ -199,11 +248,20 @@ def kernel_bench(lm, device="cuda"):
     from synth import recipes
     out = {}
 
-    def rec(name, ms, nbytes):
+    def rec(name, fn, n, res, nbytes, state=()):
+        """fn(i) timed eagerly (host launches included) and replayed from a
+        HIP graph of n calls; res() is the output the graph check compares."""
+        ms_eager = _time_calls(fn, n)
+        ms, same = _time_graph(fn, n, res, state)
+        if not same:
+            log(f"kernel {name}: graph replay differs from eager calls; reporting the eager time")
+            ms = ms_eager
         gbs = nbytes / (ms * 1e-3) / 1e9
         out[name] = {"us": round(ms * 1e3, 2), "gb_s": round(gbs, 1), "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4),
-                     "bytes": int(nbytes)}
-        log(f"kernel {name}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s")
+                     "bytes": int(nbytes), "us_eager_calls": round(ms_eager * 1e3, 2),
+                     "timing": "hip graph replay" if same else "eager calls"}
+        log(f"kernel {name}: {ms * 1e3:.2f} us ({out[name]['timing']}; eager {ms_eager * 1e3:.2f} us), "
+            f"{gbs:.0f} GB/s")
 
     # T-row GEMV, 64 copies (944 MB)
     W = mk.pack_to_device(recipes.gemv_weight(), device)
@@ -212,8 +270,8 @@ def kernel_bench(lm, device="cuda"):
         x = torch.from_numpy(recipes.rows_f32(T, HIDDEN)).to(device)
         y = torch.empty(T, HIDDEN, dtype=torch.float32, device=device)
         ws = mk.workspace(mk.mk_qgemv_rows_workspace(T, HIDDEN, HIDDEN), device)
-        ms = _time_calls(lambda i: mk.mk_qgemv_rows(copies[i % 64], x, y, ws=ws), 128)
-        rec(f"qgemv_5120x5120_T{T}", ms, HIDDEN * HIDDEN // 256 * 144 + T * 2 * HIDDEN * 4)
+        rec(f"qgemv_5120x5120_T{T}", lambda i: mk.mk_qgemv_rows(copies[i % 64], x, y, ws=ws), 128, lambda: y,
+            HIDDEN * HIDDEN // 256 * 144 + T * 2 * HIDDEN * 4)
     del copies, W
     # FFN block, 4 copies (602 MB)
     fw = recipes.ffn_weights()
@@ -224,8 +282,8 @@ def kernel_bench(lm, device="cuda"):
         x = torch.from_numpy(recipes.rows_f32(T, HIDDEN)).to(device)
         y = torch.empty(T, HIDDEN, dtype=torch.float32, device=device)
         ws = mk.workspace(mk.mk_ffn_rows_workspace(T, HIDDEN, FFN), device)
-        ms = _time_calls(lambda i: mk.mk_ffn_rows(*sets[i % 4], x, y, ws=ws), 32)
-        rec(f"ffn_5120_17408_T{T}", ms, 3 * HIDDEN * FFN // 256 * 144 + T * (2 * HIDDEN + 2 * FFN) * 4)
+        rec(f"ffn_5120_17408_T{T}", lambda i: mk.mk_ffn_rows(*sets[i % 4], x, y, ws=ws), 32, lambda: y,
+            3 * HIDDEN * FFN // 256 * 144 + T * 2 * HIDDEN * 4)
     del sets, g0, u0, d0
     torch.cuda.empty_cache()
     # lm_head + verify, T = 5 (one group, 4 drafts); full vocabulary and draft prefix
@@ -237,8 +295,8 @@ def kernel_bench(lm, device="cuda"):
     tok = torch.empty(T, dtype=torch.int32, device=device)
     for V in (VOCAB, recipes.DRAFT_VOCAB):
         ws = mk.workspace(mk.mk_lmhead_verify_workspace(V, HIDDEN, T), device)
-        ms = _time_calls(lambda i: mk.mk_lmhead_verify(lm, hid, None, drafts, am, na, tok, ws=ws, V=V), 20)
-        rec(f"lmhead_verify_V{V}_T{T}", ms, V * HIDDEN * 2 + T * HIDDEN * 4)
+        rec(f"lmhead_verify_V{V}_T{T}", lambda i: mk.mk_lmhead_verify(lm, hid, None, drafts, am, na, tok, ws=ws, V=V),
+            20, lambda: torch.cat([am, na, tok]), V * HIDDEN * 2 + T * HIDDEN * 4)
     # Gated DeltaNet step + commit, 48 x 32 heads, T = 5, seeded accept lengths
     nh = 48 * 32
     st = mk.DeltaNetState(nh, T, device=device,
@@ -251,9 +309,9 @@ def kernel_bench(lm, device="cuda"):
     def gdn(i):
         st.n_acc[0:1].fill_(int(acc[i % 64]))
         mk.mk_deltanet_step(st, *gin, o)
-    ms = _time_calls(gdn, 32)
     io = T * nh * (3 * 128 + 2) * 4 + T * nh * 128 * 4
-    rec(f"deltanet_step_48x32_T{T}", ms, 2 * nh * 128 * 128 * 4 + io + nh * 258 * 4 * (T - 1) * 2)
+    rec(f"deltanet_step_48x32_T{T}", gdn, 32, lambda: torch.cat([o.flatten(), st.S.flatten()]),
+        2 * nh * 128 * 128 * 4 + io + nh * 258 * 4 * (T - 1) * 2, state=(st.S, st.ring, st.n_acc))
     del st
     torch.cuda.empty_cache()
     return out

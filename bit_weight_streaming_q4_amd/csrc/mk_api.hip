@@ -229,14 +229,15 @@ int mk_quantize_rows(const float* x, int32_t T, int32_t K, int8_t* a8, float* s,
   if ((r = check_ptr(x, "x")) || (r = check_ptr(a8, "a8")) || (r = check_ptr(s, "s")) ||
       (r = check_ptr(gsum, "gsum")))
     return r;
-  return launch_status(mk::launch_quantize(x, T, K, a8, s, gsum, nullptr, S(stream)), "quantize");
+  return launch_status(mk::launch_quantize(x, T, K, a8, s, gsum, nullptr, nullptr, 0, S(stream)), "quantize");
 }
 
 // ------------------------------------------------------------------ GEMV
+// Workspace: quantized activation rows, tile counters, block partials.
 size_t mk_qgemv_rows_workspace(int32_t T, int32_t n_out, int32_t n_in) {
   if (T < 1 || T > MK_T_MAX || n_out <= 0 || n_in <= 0 || n_in % 256) return 0;
   const mk::GemvPlan p = mk::plan_gemv(T, n_out, n_in, 1, device_cu_count());
-  return qact_bytes(T, n_in) + align256(p.partial_elems * 4);
+  return qact_bytes(T, n_in) + align256((size_t)p.ntiles * 4) + align256(p.partial_elems * 4);
 }
 
 int mk_qgemv_rows_ex(const mk_q4k* W, const float* x, int32_t T, float* y, int32_t path, void* ws,
@@ -254,13 +255,14 @@ int mk_qgemv_rows_ex(const mk_q4k* W, const float* x, int32_t T, float* y, int32
   const mk::GemvPlan p = mk::plan_gemv(T, W->n_out, W->n_in, 1, device_cu_count());
   uint8_t* wp = (uint8_t*)ws;
   const mk::QActBuf act = carve_qact(wp, T, W->n_in);
+  unsigned* tickets = (unsigned*)wp;
+  wp += align256((size_t)p.ntiles * 4);
   float* partial = (float*)wp;
-  hipError_t e = mk::launch_quantize(x, T, W->n_in, act.a8, nullptr, nullptr, act.ssg, S(stream));
+  hipError_t e = mk::launch_quantize(x, T, W->n_in, act.a8, nullptr, nullptr, act.ssg, tickets, p.ntiles, S(stream));
   if (e != hipSuccess) return launch_status(e, "quantize");
   const uint8_t* wb[2] = {(const uint8_t*)W->blocks, nullptr};
-  e = mk::launch_gemv(wb, p, act, eng, partial, S(stream));
-  if (e != hipSuccess) return launch_status(e, "gemv");
-  return launch_status(mk::launch_reduce(partial, p, T, W->n_out, y, S(stream)), "reduce");
+  const mk::GemvEpi epi = {tickets, mk::kEpiStore, W->n_out, y, nullptr, nullptr};
+  return launch_status(mk::launch_gemv(wb, p, act, eng, partial, epi, S(stream)), "gemv");
 }
 
 int mk_qgemv_rows(const mk_q4k* W, const float* x, int32_t T, float* y, void* ws, size_t ws_bytes, void* stream) {
@@ -268,13 +270,16 @@ int mk_qgemv_rows(const mk_q4k* W, const float* x, int32_t T, float* y, void* ws
 }
 
 // ------------------------------------------------------------------ FFN
+// Workspace: x's activation rows, tile counters (gate/up, then down), the
+// gate/up partials, h's activation rows (written by the gate/up tile
+// epilogues), the down partials.
 size_t mk_ffn_rows_workspace(int32_t T, int32_t H, int32_t F) {
   if (T < 1 || T > MK_T_MAX || H <= 0 || F <= 0 || H % 256 || F % 256) return 0;
   const int cu = device_cu_count();
   const mk::GemvPlan pg = mk::plan_gemv(T, F, H, 2, cu);
   const mk::GemvPlan pd = mk::plan_gemv(T, H, F, 1, cu);
-  return qact_bytes(T, H) + align256(pg.partial_elems * 4) + align256((size_t)T * F * 4) + qact_bytes(T, F) +
-         align256(pd.partial_elems * 4);
+  return qact_bytes(T, H) + align256((size_t)(pg.ntiles + pd.ntiles) * 4) + align256(pg.partial_elems * 4) +
+         qact_bytes(T, F) + align256(pd.partial_elems * 4);
 }
 
 int mk_ffn_rows(const mk_q4k* gate, const mk_q4k* up, const mk_q4k* down, const float* x, int32_t T, float* y,
@@ -296,25 +301,22 @@ int mk_ffn_rows(const mk_q4k* gate, const mk_q4k* up, const mk_q4k* down, const 
   const mk::GemvPlan pd = mk::plan_gemv(T, H, F, 1, cu);
   uint8_t* wp = (uint8_t*)ws;
   const mk::QActBuf ax = carve_qact(wp, T, H);
+  unsigned* tickets = (unsigned*)wp;
+  wp += align256((size_t)(pg.ntiles + pd.ntiles) * 4);
   float* part_gu = (float*)wp;
   wp += align256(pg.partial_elems * 4);
-  float* h = (float*)wp;
-  wp += align256((size_t)T * F * 4);
-  if (h_out) h = h_out;
   const mk::QActBuf ah = carve_qact(wp, T, F);
   float* part_d = (float*)wp;
   const int eng = pick_path(MK_PATH_AUTO, T);
   hipStream_t st = S(stream);
-  hipError_t e = mk::launch_quantize(x, T, H, ax.a8, nullptr, nullptr, ax.ssg, st);
+  hipError_t e = mk::launch_quantize(x, T, H, ax.a8, nullptr, nullptr, ax.ssg, tickets, pg.ntiles + pd.ntiles, st);
   if (e != hipSuccess) return launch_status(e, "quantize x");
   const uint8_t* wgu[2] = {(const uint8_t*)gate->blocks, (const uint8_t*)up->blocks};
-  if ((e = mk::launch_gemv(wgu, pg, ax, eng, part_gu, st)) != hipSuccess) return launch_status(e, "gate/up");
-  if ((e = mk::launch_reduce_silu(part_gu, pg, T, F, h, st)) != hipSuccess) return launch_status(e, "silu");
-  if ((e = mk::launch_quantize(h, T, F, ah.a8, nullptr, nullptr, ah.ssg, st)) != hipSuccess)
-    return launch_status(e, "quantize h");
+  const mk::GemvEpi eg = {tickets, mk::kEpiSiluQ8, F, h_out, ah.a8, ah.ssg};
+  if ((e = mk::launch_gemv(wgu, pg, ax, eng, part_gu, eg, st)) != hipSuccess) return launch_status(e, "gate/up");
   const uint8_t* wd[2] = {(const uint8_t*)down->blocks, nullptr};
-  if ((e = mk::launch_gemv(wd, pd, ah, eng, part_d, st)) != hipSuccess) return launch_status(e, "down");
-  return launch_status(mk::launch_reduce(part_d, pd, T, H, y, st), "reduce down");
+  const mk::GemvEpi ed = {tickets + pg.ntiles, mk::kEpiStore, H, y, nullptr, nullptr};
+  return launch_status(mk::launch_gemv(wd, pd, ah, eng, part_d, ed, st), "down");
 }
 
 // ------------------------------------------------------------------ lm_head

@@ -217,18 +217,42 @@ __device__ __forceinline__ void load_unit_m(const uint8_t* __restrict__ u, int n
           (const uint32_t*)(u + kHdrBytes + j * kSubBytes + (16 * grp + nl) * 16 + kq * 4));
 }
 
-__device__ __forceinline__ void mfma_unit(const UnitM& x, int b, const QAct& act, int nl, int kq,
-                                          float (&acc)[4][4]) {
+// Activation rows of one superblock in the matrix-core operand order, as the
+// engine reads them from LDS (kActSbBytes per superblock b):
+//   [0, 4096)     A operand of sub-block j at j*512: lane 16*kq + t holds
+//                 a8[t][256b + 32j + 8kq .. +7] (zeros for t >= T)
+//   [4096, 5120)  (s, s*gsum) of group 8b + j for rows t = 0..15: float2 at
+//                 4096 + (16j + t) * 8
+constexpr int kActSbBytes = 5120;
+
+// Stages superblocks [lo, lo + n) of the quantized rows into LDS in that
+// layout; every thread of the 256-thread block takes part.
+__device__ __forceinline__ void stage_act(const QAct& act, int lo, int n, uint8_t* lds) {
+  for (int i = threadIdx.x; i < n * 512; i += 256) {
+    const int sb = i >> 9, j = (i >> 6) & 7, kq = (i >> 4) & 3, t = i & 15;
+    uint2 v = make_uint2(0u, 0u);
+    if (t < act.T) v = *(const uint2*)(act.a8 + (size_t)t * act.K + (size_t)(lo + sb) * 256 + j * 32 + kq * 8);
+    *(uint2*)(lds + sb * kActSbBytes + j * 512 + (16 * kq + t) * 8) = v;
+  }
+  for (int i = threadIdx.x; i < n * 64; i += 256) {
+    const int sb = i >> 6, q = i & 63;
+    *(u32x4*)(lds + sb * kActSbBytes + 4096 + q * 16) =
+        *(const u32x4*)((const uint8_t*)act.ssg + (size_t)(lo + sb) * 1024 + q * 16);
+  }
+}
+
+// One unit against the staged activation rows of its superblock (act, LDS).
+// The activation reads are LDS reads, so they never wait behind the next
+// unit's global loads.
+__device__ __forceinline__ void mfma_unit(const UnitM& x, const uint8_t* act, int nl, int kq, float (&acc)[4][4]) {
   Hdr hd[4];
 #pragma unroll
   for (int grp = 0; grp < 4; ++grp) decode_hdr(x.h[grp], hd[grp]);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int g = b * 8 + j;
-    long aop = 0;
-    if (nl < act.T) aop = *(const long*)(act.a8 + (size_t)nl * act.K + (size_t)g * 32 + kq * 8);
-    const f32x4 s01 = *(const f32x4*)(act.ssg + ((size_t)g * kTPad + 4 * kq) * 2);
-    const f32x4 s23 = *(const f32x4*)(act.ssg + ((size_t)g * kTPad + 4 * kq + 2) * 2);
+    const long aop = *(const long*)(act + j * 512 + (16 * kq + nl) * 8);
+    const f32x4 s01 = *(const f32x4*)(act + 4096 + (16 * j + 4 * kq) * 8);
+    const f32x4 s23 = *(const f32x4*)(act + 4096 + (16 * j + 4 * kq + 2) * 8);
     const float sv[4] = {s01.x, s01.z, s23.x, s23.z};
     const float sg[4] = {s01.y, s01.w, s23.y, s23.w};
 #pragma unroll
@@ -243,21 +267,6 @@ __device__ __forceinline__ void mfma_unit(const UnitM& x, int b, const QAct& act
         acc[grp][i] = __builtin_fmaf(-hd[grp].dm[j], sg[i], acc[grp][i]);
       }
     }
-  }
-}
-
-__device__ __forceinline__ void mfma_range(const uint8_t* __restrict__ tile, int b0, int b1, const QAct& act,
-                                           int lane, float (&acc)[4][4]) {
-  if (b0 >= b1) return;
-  const int nl = lane & 15, kq = lane >> 4;
-  UnitM u0, u1;
-  load_unit_m(tile + (size_t)b0 * kUnitBytes, nl, kq, u0);
-  for (int b = b0; b < b1; b += 2) {
-    if (b + 1 < b1) load_unit_m(tile + (size_t)(b + 1) * kUnitBytes, nl, kq, u1);
-    mfma_unit(u0, b, act, nl, kq, acc);
-    if (b + 1 >= b1) break;
-    if (b + 2 < b1) load_unit_m(tile + (size_t)(b + 2) * kUnitBytes, nl, kq, u0);
-    mfma_unit(u1, b + 1, act, nl, kq, acc);
   }
 }
 

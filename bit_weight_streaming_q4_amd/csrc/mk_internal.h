@@ -12,7 +12,7 @@ int set_error(int status, const char* fmt, ...);
 constexpr int kTPadHost = 16;         // activation-scale rows padded to 16
 constexpr int kUnitBytesHost = 9216;  // 64 rows x 144 B per superblock
 constexpr int kDot4MaxT = 8;          // dot4 engine instances exist for T = 1..8
-constexpr int kDot4MaxTAuto = 7;      // automatic choice: dot4 below 8 rows, matrix cores from 8
+constexpr int kDot4MaxTAuto = 8;      // automatic choice: dot4 up to 8 rows, matrix cores from 9
 
 struct QActBuf {
   int8_t* a8;    // [T][K]
@@ -21,9 +21,10 @@ struct QActBuf {
 };
 
 // x [T][K] -> a8/s/gsum (API arrays, each may be null) and/or the internal
-// record (ssg may be null).  Zero-fills ssg rows T..15.
+// record (ssg may be null).  Zero-fills ssg rows T..15, and zero[0..nzero)
+// (the tile counters of the GEMV launches that follow on the stream).
 hipError_t launch_quantize(const float* x, int T, int K, int8_t* a8, float* s, int32_t* gsum, float2* ssg,
-                           hipStream_t st);
+                           unsigned* zero, int nzero, hipStream_t st);
 
 struct GemvPlan {
   int ntiles, nsb, per_wg, ksplit, nmat;
@@ -31,15 +32,23 @@ struct GemvPlan {
 };
 GemvPlan plan_gemv(int T, int n_out, int n_in, int nmat, int cu_count);
 
-// Writes partial[mat][ks][t][tile*64 + r] for both matrices of W (nmat 1 or 2).
-hipError_t launch_gemv(const uint8_t* const* W, const GemvPlan& p, const QActBuf& act, int path, float* partial,
-                       hipStream_t st);
+// What the last block of each tile does with the summed split-K partials.
+enum { kEpiStore = 0, kEpiSiluQ8 = 1 };
+struct GemvEpi {
+  unsigned* tickets;  // [ntiles], zero when the GEMV starts (launch_quantize clears them)
+  int kind;           // kEpiStore: y[t][o] = sum_ks partial[0][ks][t][o], o < n_out
+                      // kEpiSiluQ8: h = SiLU(sum partial[0]) * sum partial[1], written to y if
+                      //   not null and quantized into h8 / hssg (the next GEMV's activation rows)
+  int n_out;
+  float* y;
+  int8_t* h8;
+  float2* hssg;
+};
 
-// y[t][o] = sum_ks partial[0][ks][t][o], o < n_out.
-hipError_t launch_reduce(const float* partial, const GemvPlan& p, int T, int n_out, float* y, hipStream_t st);
-// h[t][o] = SiLU(sum_ks partial[0]) * sum_ks partial[1].
-hipError_t launch_reduce_silu(const float* partial, const GemvPlan& p, int T, int n_out, float* h,
-                              hipStream_t st);
+// Writes partial[mat][ks][t][tile*64 + r] for both matrices of W (nmat 1 or
+// 2) and runs the epilogue of each tile in the block that completes it.
+hipError_t launch_gemv(const uint8_t* const* W, const GemvPlan& p, const QActBuf& act, int path, float* partial,
+                       const GemvEpi& epi, hipStream_t st);
 
 }  // namespace mk
 

@@ -112,8 +112,13 @@ size_t mk_qgemv_rows_workspace(int32_t T, int32_t n_out, int32_t n_in);
 int mk_qgemv_rows(const mk_q4k* W, const float* x, int32_t T, float* y, void* ws, size_t ws_bytes, void* stream);
 
 /* Same, with the inner-product engine chosen explicitly:
- * MK_PATH_AUTO (by T), MK_PATH_DOT4 (packed int8 dot products, T <= 8) or
- * MK_PATH_MFMA (int8 matrix cores, rows padded to 16). */
+ * MK_PATH_AUTO (dot4 for T <= 8, matrix cores from T = 9), MK_PATH_DOT4
+ * (packed int8 dot products, T <= 8) or MK_PATH_MFMA (int8 matrix cores,
+ * rows padded to 16).  Both engines give bit-identical results.
+ * Launches: the activation quantizer (which also clears the tile counters in
+ * the workspace), then the GEMV, whose last block per 64-row tile adds the
+ * tile's split-K partials in a fixed order; no memset, so the call can be
+ * captured in a HIP graph.  Calls that share a workspace must not overlap. */
 enum { MK_PATH_AUTO = 0, MK_PATH_DOT4 = 1, MK_PATH_MFMA = 2 };
 int mk_qgemv_rows_ex(const mk_q4k* W, const float* x, int32_t T, float* y, int32_t path, void* ws,
                      size_t ws_bytes, void* stream);
@@ -121,7 +126,8 @@ int mk_qgemv_rows_ex(const mk_q4k* W, const float* x, int32_t T, float* y, int32
 /* ------------------------------------------------------------------ FFN block */
 /* y = W_down . q8(SiLU(W_gate . q8(x)) * (W_up . q8(x))); gate, up are
  * F x H, down is H x F.  x, y [T][H] fp32; h_out (optional, NULL to skip)
- * receives the fp32 intermediate [T][F]. */
+ * receives the fp32 intermediate [T][F].  Three launches: quantizer, gate/up
+ * (whose tile epilogues apply SiLU(g) * u and quantize h), down. */
 size_t mk_ffn_rows_workspace(int32_t T, int32_t H, int32_t F);
 int mk_ffn_rows(const mk_q4k* gate, const mk_q4k* up, const mk_q4k* down, const float* x, int32_t T, float* y,
                 float* h_out, void* ws, size_t ws_bytes, void* stream);

@@ -170,3 +170,78 @@ def test_ffn_full_size_five_rows():
     assert rel_err(hg, ref_h) <= FP32_TOL
     assert rel_err(yg, oracle.qgemv(Ws["down"], hg)) <= FP32_TOL
     assert rel_err(yg, ref_y) <= FP32_TOL, rel_err(yg, ref_y)
+
+
+@pytest.mark.parametrize("T", [1, 3, 8, 12, 16])
+def test_ffn_small_rows_vs_oracle(T):
+    """FFN block at H = 512, F = 768 (gate/up 3 tiles x 2 superblocks per row,
+    down 8 tiles x 3): h at tolerance; y teacher-forced on the GPU's h and end
+    to end; a call without h_out gives the same y bit for bit."""
+    torch = need_gpu()
+    mk = _mk()
+    H, F = 512, 768
+    Ws = {m: synth.q4k_fields(20 + i, T, n_out, n_in)
+          for i, (m, n_out, n_in) in enumerate([("gate", F, H), ("up", F, H), ("down", H, F)])}
+    x = synth.normal_f32(23, T, 0, T * H).reshape(T, H)
+    say("ffn small", T)
+    g, u, d = (mk.Q4K.from_fields(Ws[k]) for k in ("gate", "up", "down"))
+    xd = to_dev(x)
+    y = torch.empty(T, H, dtype=torch.float32, device="cuda")
+    h = torch.empty(T, F, dtype=torch.float32, device="cuda")
+    mk.mk_ffn_rows(g, u, d, xd, y, h_out=h)
+    yg, hg = to_np(y), to_np(h)
+    ref_y, ref_h = oracle.ffn(Ws["gate"], Ws["up"], Ws["down"], x, return_h=True)
+    assert rel_err(hg, ref_h) <= FP32_TOL
+    assert rel_err(yg, oracle.qgemv(Ws["down"], hg)) <= FP32_TOL
+    assert rel_err(yg, ref_y) <= FP32_TOL, rel_err(yg, ref_y)
+    y2 = torch.empty_like(y)
+    mk.mk_ffn_rows(g, u, d, xd, y2)
+    assert np.array_equal(to_np(y2), yg)
+
+
+def test_gemv_ffn_graph_replay_matches_eager():
+    """The GEMV and FFN entry points captured in one HIP graph (no memset
+    nodes: the quantizer clears the tile counters) and replayed three times,
+    with eager calls in between, give the eager results bit for bit."""
+    torch = need_gpu()
+    mk = _mk()
+    N, K, T = 320, 1536, 5
+    W = synth.q4k_fields(30, 1, N, K)
+    Wd = mk.Q4K.from_fields(W)
+    H, F = 512, 768
+    Ws = {m: synth.q4k_fields(31 + i, 1, n_out, n_in)
+          for i, (m, n_out, n_in) in enumerate([("gate", F, H), ("up", F, H), ("down", H, F)])}
+    g, u, d = (mk.Q4K.from_fields(Ws[k]) for k in ("gate", "up", "down"))
+    xa = to_dev(synth.normal_f32(32, 1, 0, T * K).reshape(T, K))
+    xb = to_dev(synth.normal_f32(33, 1, 0, T * H).reshape(T, H))
+    ya = torch.empty(T, N, dtype=torch.float32, device="cuda")
+    yb = torch.empty(T, H, dtype=torch.float32, device="cuda")
+    wsa = mk.workspace(mk.mk_qgemv_rows_workspace(T, N, K))
+    wsb = mk.workspace(mk.mk_ffn_rows_workspace(T, H, F))
+
+    def calls():
+        mk.mk_qgemv_rows(Wd, xa, ya, ws=wsa)
+        mk.mk_ffn_rows(g, u, d, xb, yb, ws=wsb)
+
+    calls()
+    torch.cuda.synchronize()
+    ref_a, ref_b = to_np(ya), to_np(yb)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for rep in range(3):
+        ya.zero_()
+        yb.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        say("graph replay", rep)
+        assert np.array_equal(to_np(ya), ref_a), rep
+        assert np.array_equal(to_np(yb), ref_b), rep
+        calls()
+        torch.cuda.synchronize()
