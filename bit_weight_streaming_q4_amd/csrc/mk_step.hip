@@ -635,6 +635,33 @@ __device__ __forceinline__ void slot_dot4(lds_u8* sl, int b_unused, int lane, fl
 // exact sub-block sums P[t = 4q + i][row 16 nb + n].  The combine adds
 // s[t][j] * d * sc_j * P, and the min term - dmin * m_j * (s*gsum)[t][j] is a
 // v_mfma_f32_16x16x4_f32 over j into the same accumulator.
+// Integer products of sub-block j for the 4 row groups nb of the unit in
+// slot sl: p[nb] = C[t = 4q + i][n] of A = activation rows, B = codes of rows
+// 16 nb + n.
+__device__ __forceinline__ void mfma_sub(lds_u8* sl, lds_u8* act, int j, int q, int n, i32x4 (&p)[4]) {
+  const uint64_t aop = *(lds_u64*)(act + ((j * 4 + q) * 16 + n) * 8);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const uint32_t cw = *(const lds_u32*)(sl + kHdrBytes + j * kSubBytes + (16 * nb + n) * 16 + q * 4);
+    const uint64_t bop = (uint64_t)(cw & 0x0F0F0F0Fu) | ((uint64_t)((cw >> 4) & 0x0F0F0F0Fu) << 32);
+    const i32x4 z = {0, 0, 0, 0};
+    p[nb] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)aop, (long)bop, z, 0, 0, 0);
+  }
+}
+
+// acc[nb][i] += P * (d * sc_j) * s[t = 4q + i][j] for the products of sub-block j.
+__device__ __forceinline__ void scale_sub(lds_f32* sc, int j, int q, const float (&d)[4], const uint32_t (&sc03)[4],
+                                          const uint32_t (&sc47)[4], const i32x4 (&p)[4], f32x4 (&acc)[4]) {
+  const f32x4 st = *(const lds_f32x4*)(sc + j * 16 + 4 * q);  // s of rows t = 4q .. 4q + 3
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const uint32_t scw = j < 4 ? sc03[nb] : sc47[nb];
+    const float f = d[nb] * (float)((scw >> (8 * (j & 3))) & 0xffu);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[nb][i] = __builtin_fmaf((float)p[nb][i], f * st[i], acc[nb][i]);
+  }
+}
+
 __device__ __forceinline__ void slot_mfma(lds_u8* sl, int lane, f32x4 (&acc)[4]) {
   const int q = lane >> 4, n = lane & 15;
   lds_u8* act = sl + kUnitBytes;
@@ -663,21 +690,16 @@ __device__ __forceinline__ void slot_mfma(lds_u8* sl, int lane, f32x4 (&acc)[4])
     acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(am0, bm0, acc[nb], 0, 0, 0);
     acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(am1, bm1, acc[nb], 0, 0, 0);
   }
+  // The 4 products of sub-block j + 1 are issued before the scaling of
+  // sub-block j, so that the matrix cores run under the scaling arithmetic.
+  i32x4 p0[4], p1[4];
+  mfma_sub(sl, act, 0, q, n, p0);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint64_t aop = *(lds_u64*)(act + ((j * 4 + q) * 16 + n) * 8);
-    const f32x4 st = *(const lds_f32x4*)(sc + j * 16 + 4 * q);  // s of rows t = 4q .. 4q + 3
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const uint32_t cw = *(const lds_u32*)(sl + kHdrBytes + j * kSubBytes + (16 * nb + n) * 16 + q * 4);
-      const uint64_t bop = (uint64_t)(cw & 0x0F0F0F0Fu) | ((uint64_t)((cw >> 4) & 0x0F0F0F0Fu) << 32);
-      const i32x4 z = {0, 0, 0, 0};
-      const i32x4 p = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)aop, (long)bop, z, 0, 0, 0);
-      const uint32_t scw = j < 4 ? sc03[nb] : sc47[nb];
-      const float f = d[nb] * (float)((scw >> (8 * (j & 3))) & 0xffu);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[nb][i] = __builtin_fmaf((float)p[i], f * st[i], acc[nb][i]);
-    }
+  for (int j = 0; j < 8; j += 2) {
+    mfma_sub(sl, act, j + 1, q, n, p1);
+    scale_sub(sc, j, q, d, sc03, sc47, p0, acc);
+    if (j + 2 < 8) mfma_sub(sl, act, j + 2, q, n, p0);
+    scale_sub(sc, j + 1, q, d, sc03, sc47, p1, acc);
   }
 }
 
