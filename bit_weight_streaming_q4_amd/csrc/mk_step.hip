@@ -635,28 +635,44 @@ __device__ __forceinline__ void slot_dot4(lds_u8* sl, int b_unused, int lane, fl
 // exact sub-block sums P[t = 4q + i][row 16 nb + n].  The combine adds
 // s[t][j] * d * sc_j * P, and the min term - dmin * m_j * (s*gsum)[t][j] is a
 // v_mfma_f32_16x16x4_f32 over j into the same accumulator.
-// Integer products of sub-block j for the 4 row groups nb of the unit in
-// slot sl: p[nb] = C[t = 4q + i][n] of A = activation rows, B = codes of rows
-// 16 nb + n.
-__device__ __forceinline__ void mfma_sub(lds_u8* sl, lds_u8* act, int j, int q, int n, i32x4 (&p)[4]) {
-  const uint64_t aop = *(lds_u64*)(act + ((j * 4 + q) * 16 + n) * 8);
+// LDS operands of sub-block j of the unit in slot sl: the activation A
+// fragment, the codes of rows 16 nb + n (dword q) and the scales s of rows
+// t = 4q .. 4q + 3.
+struct SubOps {
+  uint64_t aop;
+  uint32_t cw[4];
+  f32x4 st;
+};
+
+__device__ __forceinline__ void read_sub(lds_u8* sl, lds_u8* act, lds_f32* sc, int j, int q, int n, SubOps& o) {
+  o.aop = *(lds_u64*)(act + ((j * 4 + q) * 16 + n) * 8);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+    o.cw[nb] = *(const lds_u32*)(sl + kHdrBytes + j * kSubBytes + (16 * nb + n) * 16 + q * 4);
+  o.st = *(const lds_f32x4*)(sc + j * 16 + 4 * q);
+}
+
+// Integer products of one sub-block for the 4 row groups: p[nb] = C[t = 4q + i][n].
+__device__ __forceinline__ void mfma_sub(const SubOps& o, i32x4 (&p)[4]) {
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
-    const uint32_t cw = *(const lds_u32*)(sl + kHdrBytes + j * kSubBytes + (16 * nb + n) * 16 + q * 4);
-    const uint64_t bop = (uint64_t)(cw & 0x0F0F0F0Fu) | ((uint64_t)((cw >> 4) & 0x0F0F0F0Fu) << 32);
+    const uint64_t bop = (uint64_t)(o.cw[nb] & 0x0F0F0F0Fu) | ((uint64_t)((o.cw[nb] >> 4) & 0x0F0F0F0Fu) << 32);
     const i32x4 z = {0, 0, 0, 0};
-    p[nb] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)aop, (long)bop, z, 0, 0, 0);
+    p[nb] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)o.aop, (long)bop, z, 0, 0, 0);
   }
 }
 
+// Byte k of a dword whose bytes are already below 64, as a float (one
+// byte-select conversion).
+__device__ __forceinline__ float byte_f32(uint32_t w, int k) { return (float)((w >> (8 * k)) & 0xffu); }
+
 // acc[nb][i] += P * (d * sc_j) * s[t = 4q + i][j] for the products of sub-block j.
-__device__ __forceinline__ void scale_sub(lds_f32* sc, int j, int q, const float (&d)[4], const uint32_t (&sc03)[4],
-                                          const uint32_t (&sc47)[4], const i32x4 (&p)[4], f32x4 (&acc)[4]) {
-  const f32x4 st = *(const lds_f32x4*)(sc + j * 16 + 4 * q);  // s of rows t = 4q .. 4q + 3
+__device__ __forceinline__ void scale_sub(int j, const float (&d)[4], const uint32_t (&sc03)[4],
+                                          const uint32_t (&sc47)[4], const f32x4 st, const i32x4 (&p)[4],
+                                          f32x4 (&acc)[4]) {
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
-    const uint32_t scw = j < 4 ? sc03[nb] : sc47[nb];
-    const float f = d[nb] * (float)((scw >> (8 * (j & 3))) & 0xffu);
+    const float f = d[nb] * byte_f32(j < 4 ? sc03[nb] : sc47[nb], j & 3);
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[nb][i] = __builtin_fmaf((float)p[nb][i], f * st[i], acc[nb][i]);
   }
@@ -670,14 +686,20 @@ __device__ __forceinline__ void slot_mfma(lds_u8* sl, int lane, f32x4 (&acc)[4])
   u32x4 h[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) h[nb] = *(const lds_u32x4*)(sl + (16 * nb + n) * 16);
+  // operands of the first two sub-blocks are read with the headers
+  SubOps o0, o1;
+  read_sub(sl, act, sc, 0, q, n, o0);
+  read_sub(sl, act, sc, 1, q, n, o1);
   float d[4], dmin[4];
   uint32_t sc03[4], sc47[4];
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
     d[nb] = f16_bits_to_f32(h[nb].x & 0xffffu);
     dmin[nb] = f16_bits_to_f32(h[nb].x >> 16);
-    sc03[nb] = h[nb].y & 0x3F3F3F3Fu;
-    sc47[nb] = h[nb].z & 0x3F3F3F3Fu;
+    // masked out of the compiler's sight, so that each scale below is one
+    // byte-select conversion rather than a field extract and a conversion
+    asm("v_and_b32 %0, %1, %2" : "=v"(sc03[nb]) : "v"(h[nb].y), "v"(0x3F3F3F3Fu));
+    asm("v_and_b32 %0, %1, %2" : "=v"(sc47[nb]) : "v"(h[nb].z), "v"(0x3F3F3F3Fu));
   }
   // min term: B[k][n] = -dmin * m_k for k = q (first MFMA) and q + 4 (second)
 #pragma unroll
@@ -690,16 +712,19 @@ __device__ __forceinline__ void slot_mfma(lds_u8* sl, int lane, f32x4 (&acc)[4])
     acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(am0, bm0, acc[nb], 0, 0, 0);
     acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(am1, bm1, acc[nb], 0, 0, 0);
   }
-  // The 4 products of sub-block j + 1 are issued before the scaling of
-  // sub-block j, so that the matrix cores run under the scaling arithmetic.
-  i32x4 p0[4], p1[4];
-  mfma_sub(sl, act, 0, q, n, p0);
+  // Three stages in flight: the LDS operands of sub-block j + 2 are read and
+  // the products of sub-block j + 1 issued before sub-block j is scaled (the
+  // loop is unrolled, so every sub-block's values have registers of their own).
+  SubOps o[8];
+  i32x4 p[8][4];
+  o[0] = o0;
+  o[1] = o1;
+  mfma_sub(o[0], p[0]);
 #pragma unroll
-  for (int j = 0; j < 8; j += 2) {
-    mfma_sub(sl, act, j + 1, q, n, p1);
-    scale_sub(sc, j, q, d, sc03, sc47, p0, acc);
-    if (j + 2 < 8) mfma_sub(sl, act, j + 2, q, n, p0);
-    scale_sub(sc, j + 1, q, d, sc03, sc47, p1, acc);
+  for (int j = 0; j < 8; ++j) {
+    if (j + 2 < 8) read_sub(sl, act, sc, j + 2, q, n, o[j + 2]);
+    if (j + 1 < 8) mfma_sub(o[j + 1], p[j + 1]);
+    scale_sub(j, d, sc03, sc47, o[j].st, p[j], acc);
   }
 }
 
