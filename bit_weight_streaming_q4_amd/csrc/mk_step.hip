@@ -525,19 +525,33 @@ __device__ __forceinline__ uint32_t slot_lds(BlockState<T>& s, int c, int k) {
 // compute wave issues no other vector-memory operation while loads are in
 // flight.
 // COH: device-scope (sc1) loads, for data other CUs wrote during the launch.
+#define MK_DMA1(C) "global_load_lds_dwordx4 %[a], off" C "\n\t"
+#define MK_DMA_NEXT "v_lshl_add_u64 %[a], %[a], 0, %[k]\n\ts_add_u32 m0, m0, 0x400\n\t"
+#define MK_DMA5(C) MK_DMA1(C) MK_DMA_NEXT MK_DMA1(C) MK_DMA_NEXT MK_DMA1(C) MK_DMA_NEXT MK_DMA1(C) MK_DMA_NEXT MK_DMA1(C)
+#define MK_DMA9(C) MK_DMA5(C) MK_DMA_NEXT MK_DMA1(C) MK_DMA_NEXT MK_DMA1(C) MK_DMA_NEXT MK_DMA1(C) MK_DMA_NEXT MK_DMA1(C)
 template <int N, bool COH>
 __device__ __forceinline__ void dma(uint32_t lds, const uint8_t* g) {
+  static_assert((N == 9 && !COH) || (N == 5 && COH), "instantiated shapes only");
   const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds);
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    if (COH)
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off sc1" ::"s"(l0 + i * 1024), "v"(g + i * 1024)
-                   : "memory", "m0");
-    else
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l0 + i * 1024), "v"(g + i * 1024)
-                   : "memory", "m0");
-  }
+  uint64_t addr = (uint64_t)(uintptr_t)g;
+  const uint64_t step = 1024;
+  // One statement for all N loads: the address and M0 advance inside it, so
+  // no compiler-placed instruction (or wait) falls between the loads.
+  if constexpr (N == 9)
+    asm volatile("s_mov_b32 m0, %[m]\n\t" MK_DMA9("")
+                 : [a] "+v"(addr)
+                 : [m] "s"(l0), [k] "s"(step)
+                 : "memory", "m0", "scc");
+  else
+    asm volatile("s_mov_b32 m0, %[m]\n\t" MK_DMA5(" sc1")
+                 : [a] "+v"(addr)
+                 : [m] "s"(l0), [k] "s"(step)
+                 : "memory", "m0", "scc");
 }
+#undef MK_DMA9
+#undef MK_DMA5
+#undef MK_DMA_NEXT
+#undef MK_DMA1
 
 // Waits until at most n of this wave's vector-memory operations are in flight.
 __device__ __forceinline__ void wait_ops(int n) {
@@ -553,28 +567,68 @@ __device__ __forceinline__ void wait_ops(int n) {
 // operations its loads still count (weights 9, activations 5).
 struct Slot {
   int q, tm, b;
-  int ops;     // DMA operations issued for this slot
+  int wops;    // weight DMA operations issued for this slot's unit
+  int aops;    // activation DMA operations issued after them (0 if not yet)
   bool act;    // activations loaded (or in flight)
 };
 
-// Starts the weight loads of the cursor's unit into slot lds (and its
-// activations if phase `open` is the unit's, i.e. they are ready), records
-// the unit and moves on.  Returns the number of operations issued.
-__device__ __forceinline__ void issue(const StepArgs& a, const uint8_t* const (*wt)[5], WaveUnits wu, Cursor& c, int w,
-                                      int lane, uint32_t lds, int open, Slot& sl) {
+// Starts the weight loads of the cursor's unit into slot lds, records the
+// unit and moves the cursor on.
+__device__ __forceinline__ void issue_w(const StepArgs& a, const uint8_t* const (*wt)[5], WaveUnits wu, Cursor& c,
+                                        int w, int lane, uint32_t lds, Slot& sl) {
   sl.q = c.q;
   sl.tm = c.tm;
   sl.b = c.b;
-  sl.ops = 0;
+  sl.wops = 0;
+  sl.aops = 0;
   sl.act = false;
   if (c.q >= 4 * a.L) return;
   const int tau = c.nm == 2 ? c.tm >> 1 : c.tm;
   const uint8_t* W = (c.nm == 2 && (c.tm & 1)) ? c.W1 : c.W0;
   dma<9, false>(lds, W + ((size_t)tau * c.nsb + c.b) * kUnitBytes + lane * 16);
-  sl.ops = 9;
+  sl.wops = 9;
+  if (++c.b == c.nsb) {
+    c.b = 0;
+    ++c.tm;
+  }
+  if (++c.u >= c.u1) {
+    ++c.q;
+    cursor_settle(a, wt, wu, c, w);
+  }
+}
+
+// Starts the activation loads of slot sl's unit once its phase is open (it
+// is the consumer's current phase `open`).  The slot's activation region
+// must no longer be read: with WAIT, every LDS read of the wave is waited
+// for first; without, the caller has used every value it read.
+template <bool WAIT>
+__device__ __forceinline__ void issue_a(const StepArgs& a, int lane, uint32_t lds, int open, Slot& sl) {
+  if (!sl.wops || sl.act || sl.q != open) return;
+  if (WAIT) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  dma<5, true>(lds + kUnitBytes, phase_input(a, sl.q >> 2, sl.q & 3) + (size_t)sl.b * kActBytes + lane * 16);
+  sl.aops = 5;
+  sl.act = true;
+}
+
+// Starts the weight loads of the cursor's unit into slot lds and, if phase
+// `open` is the unit's (its activations are ready), its activation loads;
+// records the unit and moves the cursor on (the dot4 engine's refill).
+__device__ __forceinline__ void issue_wa(const StepArgs& a, const uint8_t* const (*wt)[5], WaveUnits wu, Cursor& c, int w,
+                                      int lane, uint32_t lds, int open, Slot& sl) {
+  sl.q = c.q;
+  sl.tm = c.tm;
+  sl.b = c.b;
+  sl.wops = 0;
+  sl.aops = 0;
+  sl.act = false;
+  if (c.q >= 4 * a.L) return;
+  const int tau = c.nm == 2 ? c.tm >> 1 : c.tm;
+  const uint8_t* W = (c.nm == 2 && (c.tm & 1)) ? c.W1 : c.W0;
+  dma<9, false>(lds, W + ((size_t)tau * c.nsb + c.b) * kUnitBytes + lane * 16);
+  sl.wops = 9;
   if (c.q == open) {
     dma<5, true>(lds + kUnitBytes, phase_input(a, c.q >> 2, c.q & 3) + (size_t)c.b * kActBytes + lane * 16);
-    sl.ops = 14;
+    sl.aops = 5;
     sl.act = true;
   }
   if (++c.b == c.nsb) {
@@ -596,11 +650,12 @@ typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
 
 __device__ __forceinline__ lds_u8* as_lds(const uint8_t* p) { return (lds_u8*)p; }
 
-// dot4 engine on a slot (lane = output row): the unit's codes and header from
-// LDS, the activations as wave-uniform LDS reads (every lane the same address).
+// dot4 engine on a slot (lane = output row): the unit's codes and header
+// from LDS, the activations as wave-uniform LDS reads (every lane the same
+// address).  The weight reads stay next to their use: issuing them apart
+// from the arithmetic measured slower.
 template <int T>
-__device__ __forceinline__ void slot_dot4(lds_u8* sl, int b_unused, int lane, float (&acc)[T]) {
-  (void)b_unused;
+__device__ __forceinline__ void slot_dot4(lds_u8* sl, int lane, float (&acc)[T]) {
   const lds_u32x4* w = (const lds_u32x4*)(sl + lane * 16);
   Unit x;
   x.h = w[0];
@@ -640,23 +695,37 @@ __device__ __forceinline__ void slot_dot4(lds_u8* sl, int b_unused, int lane, fl
 // t = 4q .. 4q + 3.
 struct SubOps {
   uint64_t aop;
-  uint32_t cw[4];
   f32x4 st;
 };
 
-__device__ __forceinline__ void read_sub(lds_u8* sl, lds_u8* act, lds_f32* sc, int j, int q, int n, SubOps& o) {
+__device__ __forceinline__ void read_sub(lds_u8* act, lds_f32* sc, int j, int q, int n, SubOps& o) {
   o.aop = *(lds_u64*)(act + ((j * 4 + q) * 16 + n) * 8);
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-    o.cw[nb] = *(const lds_u32*)(sl + kHdrBytes + j * kSubBytes + (16 * nb + n) * 16 + q * 4);
   o.st = *(const lds_f32x4*)(sc + j * 16 + 4 * q);
 }
 
+// A unit's weights in the matrix-core operand layout: the headers of rows
+// 16 nb + n and, per sub-block j, dword q of the codes of those rows.
+struct WregM {
+  u32x4 h[4];
+  uint32_t cw[8][4];
+};
+
+__device__ __forceinline__ void read_w_mfma(lds_u8* sl, int lane, WregM& x) {
+  const int q = lane >> 4, n = lane & 15;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) x.h[nb] = *(const lds_u32x4*)(sl + (16 * nb + n) * 16);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      x.cw[j][nb] = *(const lds_u32*)(sl + kHdrBytes + j * kSubBytes + (16 * nb + n) * 16 + q * 4);
+}
+
 // Integer products of one sub-block for the 4 row groups: p[nb] = C[t = 4q + i][n].
-__device__ __forceinline__ void mfma_sub(const SubOps& o, i32x4 (&p)[4]) {
+__device__ __forceinline__ void mfma_sub(const SubOps& o, const uint32_t (&cw)[4], i32x4 (&p)[4]) {
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) {
-    const uint64_t bop = (uint64_t)(o.cw[nb] & 0x0F0F0F0Fu) | ((uint64_t)((o.cw[nb] >> 4) & 0x0F0F0F0Fu) << 32);
+    const uint64_t bop = (uint64_t)(cw[nb] & 0x0F0F0F0Fu) | ((uint64_t)((cw[nb] >> 4) & 0x0F0F0F0Fu) << 32);
     const i32x4 z = {0, 0, 0, 0};
     p[nb] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)o.aop, (long)bop, z, 0, 0, 0);
   }
@@ -678,18 +747,17 @@ __device__ __forceinline__ void scale_sub(int j, const float (&d)[4], const uint
   }
 }
 
-__device__ __forceinline__ void slot_mfma(lds_u8* sl, int lane, f32x4 (&acc)[4]) {
+// Matrix-core engine on a unit whose weights are in registers (x) and whose
+// activation record is in slot sl.
+__device__ __forceinline__ void slot_mfma(const WregM& x, lds_u8* sl, int lane, f32x4 (&acc)[4]) {
   const int q = lane >> 4, n = lane & 15;
   lds_u8* act = sl + kUnitBytes;
   lds_f32* sc = (lds_f32*)(act + kActA);
-  // headers of rows 16 nb + n
-  u32x4 h[4];
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) h[nb] = *(const lds_u32x4*)(sl + (16 * nb + n) * 16);
-  // operands of the first two sub-blocks are read with the headers
+  const u32x4 (&h)[4] = x.h;
+  // activation operands of the first two sub-blocks
   SubOps o0, o1;
-  read_sub(sl, act, sc, 0, q, n, o0);
-  read_sub(sl, act, sc, 1, q, n, o1);
+  read_sub(act, sc, 0, q, n, o0);
+  read_sub(act, sc, 1, q, n, o1);
   float d[4], dmin[4];
   uint32_t sc03[4], sc47[4];
 #pragma unroll
@@ -719,11 +787,11 @@ __device__ __forceinline__ void slot_mfma(lds_u8* sl, int lane, f32x4 (&acc)[4])
   i32x4 p[8][4];
   o[0] = o0;
   o[1] = o1;
-  mfma_sub(o[0], p[0]);
+  mfma_sub(o[0], x.cw[0], p[0]);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    if (j + 2 < 8) read_sub(sl, act, sc, j + 2, q, n, o[j + 2]);
-    if (j + 1 < 8) mfma_sub(o[j + 1], p[j + 1]);
+    if (j + 2 < 8) read_sub(act, sc, j + 2, q, n, o[j + 2]);
+    if (j + 1 < 8) mfma_sub(o[j + 1], x.cw[j + 1], p[j + 1]);
     scale_sub(j, d, sc03, sc47, o[j].st, p[j], acc);
   }
 }
@@ -830,11 +898,14 @@ __device__ __forceinline__ void finish_early(BlockState<T>& s, int c, int lane, 
   }
 }
 
-// Consumes the unit of slot `cur` (the other slot `oth` holds the next one).
+// The dot4 engine's stream (T <= 2): as below, but each slot is refilled
+// after its unit's arithmetic, which measured faster for this short
+// arithmetic.  Consumes the unit of slot `cur` (the other slot `oth` holds
+// the next one).
 // Entering a new phase: wait for its barrier, then start the activation
 // loads of both slots' units of that phase, and wait for all loads.
 template <int T>
-__device__ __forceinline__ void consume(const StepArgs& a, BlockState<T>& s, int c, int lane, Consumer<T>& k,
+__device__ __forceinline__ void consume_dot4(const StepArgs& a, BlockState<T>& s, int c, int lane, Consumer<T>& k,
                                         Slot& cur, Slot& oth, int kcur, uint32_t lcur, uint32_t loth, bool& ok) {
   if (cur.q != k.q) {
     advance_to<T>(a, s, c, lane, k, cur.q, ok);
@@ -842,13 +913,13 @@ __device__ __forceinline__ void consume(const StepArgs& a, BlockState<T>& s, int
       dma<5, true>(lcur + kUnitBytes, phase_input(a, cur.q >> 2, cur.q & 3) + (size_t)cur.b * kActBytes + lane * 16);
       cur.act = true;
     }
-    if (oth.q == cur.q && oth.ops && !oth.act) {
+    if (oth.q == cur.q && oth.wops && !oth.act) {
       dma<5, true>(loth + kUnitBytes, phase_input(a, oth.q >> 2, oth.q & 3) + (size_t)oth.b * kActBytes + lane * 16);
       oth.act = true;
     }
     wait_ops(0);
   } else {
-    wait_ops(oth.ops);  // this slot's loads are older than the other slot's
+    wait_ops(oth.wops + oth.aops);  // this slot's loads are older than the other slot's
   }
   if (cur.tm != k.tm) {
     if (k.tm >= 0) flush<T>(s, c, lane, k, ok);
@@ -856,14 +927,11 @@ __device__ __forceinline__ void consume(const StepArgs& a, BlockState<T>& s, int
     acc_zero<T>(k);
   }
   lds_u8* sl = as_lds(&s.ring[c][kcur][0]);
-  if constexpr (UseMfma<T>::value)
-    slot_mfma(sl, lane, k.macc);
-  else
-    slot_dot4<T>(sl, cur.b, lane, k.acc);
+  slot_dot4<T>(sl, lane, k.acc);
 }
 
 template <int T>
-__device__ __forceinline__ void compute_wave(const StepArgs& a, BlockState<T>& s, int c, int lane) {
+__device__ __forceinline__ void compute_wave_dot4(const StepArgs& a, BlockState<T>& s, int c, int lane) {
   const int w = c;  // the plan indexes compute waves within the block
   const int qend = 4 * a.L;
   const uint32_t l0 = slot_lds(s, c, 0), l1 = slot_lds(s, c, 1);
@@ -873,8 +941,8 @@ __device__ __forceinline__ void compute_wave(const StepArgs& a, BlockState<T>& s
   cur.q = 0;
   cursor_settle(a, wt, wu, cur, w);
   Slot s0, s1;
-  issue(a, wt, wu, cur, w, lane, l0, -1, s0);
-  issue(a, wt, wu, cur, w, lane, l1, -1, s1);
+  issue_wa(a, wt, wu, cur, w, lane, l0, -1, s0);
+  issue_wa(a, wt, wu, cur, w, lane, l1, -1, s1);
   Consumer<T> k;
   k.q = -1;
   k.tm = -1;
@@ -884,17 +952,98 @@ __device__ __forceinline__ void compute_wave(const StepArgs& a, BlockState<T>& s
   bool ok = true;
   while (ok) {
     if (s0.q >= qend) break;
-    consume<T>(a, s, c, lane, k, s0, s1, 0, l0, l1, ok);
+    consume_dot4<T>(a, s, c, lane, k, s0, s1, 0, l0, l1, ok);
     finish_early<T>(s, c, lane, k, s1.q, s1.tm, ok);
     // the slot's LDS reads have completed (their values were used) before it is refilled
-    issue(a, wt, wu, cur, w, lane, l0, k.q, s0);
+    issue_wa(a, wt, wu, cur, w, lane, l0, k.q, s0);
     if (s1.q >= qend) break;
-    consume<T>(a, s, c, lane, k, s1, s0, 1, l1, l0, ok);
+    consume_dot4<T>(a, s, c, lane, k, s1, s0, 1, l1, l0, ok);
     finish_early<T>(s, c, lane, k, s0.q, s0.tm, ok);
-    issue(a, wt, wu, cur, w, lane, l1, k.q, s1);
+    issue_wa(a, wt, wu, cur, w, lane, l1, k.q, s1);
   }
   advance_to<T>(a, s, c, lane, k, qend, ok);  // finishes the phases after the last unit
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load outlives the stream (also after an abort)
+}
+
+// Consumes the unit of slot `cur` (the other slot `oth` holds the next one).
+// Entering a new phase: wait for it to open, then start the activation
+// loads of both slots' units of that phase, and wait for all loads.  The
+// unit's weights are copied into registers and the slot's weight region is
+// refilled with the stream's next unit before the matrix-core arithmetic
+// starts; the activation region is refilled after it.
+template <int T>
+__device__ __forceinline__ void consume(const StepArgs& a, BlockState<T>& s, int c, int lane, Consumer<T>& k,
+                                        const uint8_t* const (*wt)[5], WaveUnits wu, Cursor& cs, Slot& cur,
+                                        Slot& oth, int kcur, uint32_t lcur, uint32_t loth, bool& ok) {
+  if (cur.q != k.q) {
+    advance_to<T>(a, s, c, lane, k, cur.q, ok);
+    if (!cur.act) {
+      dma<5, true>(lcur + kUnitBytes, phase_input(a, cur.q >> 2, cur.q & 3) + (size_t)cur.b * kActBytes + lane * 16);
+      cur.act = true;
+    }
+    if (oth.q == cur.q && oth.wops && !oth.act) {
+      dma<5, true>(loth + kUnitBytes, phase_input(a, oth.q >> 2, oth.q & 3) + (size_t)oth.b * kActBytes + lane * 16);
+      oth.aops = 5;
+      oth.act = true;
+    }
+    wait_ops(0);
+  } else {
+    wait_ops(oth.wops + oth.aops);  // issued after this slot's loads: the other slot's
+  }
+  if (cur.tm != k.tm) {
+    if (k.tm >= 0) flush<T>(s, c, lane, k, ok);
+    k.tm = cur.tm;
+    acc_zero<T>(k);
+  }
+  lds_u8* sl = as_lds(&s.ring[c][kcur][0]);
+  {
+    WregM x;
+    read_w_mfma(sl, lane, x);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the weight region is read before it is refilled
+    issue_w(a, wt, wu, cs, c, lane, lcur, cur);
+    slot_mfma(x, sl, lane, k.macc);
+    finish_early<T>(s, c, lane, k, oth.q, oth.tm, ok);
+    issue_a<true>(a, lane, lcur, k.q, cur);
+  }
+}
+
+template <int T>
+__device__ __forceinline__ void compute_wave_mfma(const StepArgs& a, BlockState<T>& s, int c, int lane) {
+  const int w = c;  // the plan indexes compute waves within the block
+  const int qend = 4 * a.L;
+  const uint32_t l0 = slot_lds(s, c, 0), l1 = slot_lds(s, c, 1);
+  const uint8_t* const(*wt)[5] = s.wt;
+  WaveUnits wu = s.plan.wu;
+  Cursor cur;
+  cur.q = 0;
+  cursor_settle(a, wt, wu, cur, w);
+  Slot s0, s1;
+  issue_w(a, wt, wu, cur, w, lane, l0, s0);
+  issue_w(a, wt, wu, cur, w, lane, l1, s1);
+  Consumer<T> k;
+  k.q = -1;
+  k.tm = -1;
+  k.nflush = 0;
+  k.done = 0;
+  acc_zero<T>(k);
+  bool ok = true;
+  while (ok) {
+    if (s0.q >= qend) break;
+    consume<T>(a, s, c, lane, k, wt, wu, cur, s0, s1, 0, l0, l1, ok);
+    if (s1.q >= qend) break;
+    consume<T>(a, s, c, lane, k, wt, wu, cur, s1, s0, 1, l1, l0, ok);
+  }
+  advance_to<T>(a, s, c, lane, k, qend, ok);  // finishes the phases after the last unit
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load outlives the stream (also after an abort)
+}
+
+// A compute wave's stream of units through every phase of the step.
+template <int T>
+__device__ __forceinline__ void compute_wave(const StepArgs& a, BlockState<T>& s, int c, int lane) {
+  if constexpr (UseMfma<T>::value)
+    compute_wave_mfma<T>(a, s, c, lane);
+  else
+    compute_wave_dot4<T>(a, s, c, lane);
 }
 
 __device__ __forceinline__ void gdn_job(const StepArgs& a, int layer, long j, int lane) {
