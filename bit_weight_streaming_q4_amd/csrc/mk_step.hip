@@ -254,6 +254,7 @@ __device__ __forceinline__ void lds_st(int* p, int v) {
 // (phase q is open once every tile of its input is finished).  After the last GEMV phase the ring area
 // holds the lm phase's cross-wave reduction.
 constexpr int kSlots = 2;
+constexpr int kMbRow = 68;  // mailbox row stride in floats: 64 rows + 4 (spreads the flush writes over the banks)
 template <int T>
 struct MbCount {
   static constexpr int value = 2;
@@ -263,7 +264,7 @@ struct BlockState {
   static constexpr int NMB = MbCount<T>::value;
   uint8_t ring[kCompute][kSlots][kSlotBytes] __attribute__((aligned(16)));
   const uint8_t* wt[kMaxLayers][5];  // the weight table, copied at the start
-  float mb[kCompute][NMB][64][TPad<T>::value] __attribute__((aligned(16)));  // [row of the tile][t]
+  float mb[kCompute][NMB][TPad<T>::value][kMbRow] __attribute__((aligned(16)));  // [t][row of the tile]
   uint8_t stage[1024 + 256] __attribute__((aligned(16)));  // one tile's record part, staged by the service wave
   BlockPlan plan __attribute__((aligned(16)));
   int tag[kCompute][NMB];
@@ -841,10 +842,12 @@ __device__ __forceinline__ void flush(BlockState<T>& s, int c, int lane, Consume
     const int q = lane >> 4, n = lane & 15;
     if (4 * q < TPad<T>::value)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) *(f32x4*)&s.mb[c][slot][16 * nb + n][4 * q] = k.macc[nb];
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s.mb[c][slot][4 * q + i][16 * nb + n] = k.macc[nb][i];
   } else {
 #pragma unroll
-    for (int t = 0; t < T; ++t) s.mb[c][slot][lane][t] = k.acc[t];
+    for (int t = 0; t < T; ++t) s.mb[c][slot][t][lane] = k.acc[t];
   }
   if (lane == 0) lds_st(&s.tag[c][slot], ((k.q + 1) << 16) | k.tm);
   ++k.nflush;
@@ -1273,9 +1276,7 @@ __device__ __forceinline__ bool svc_contrib(const StepArgs& a, BlockState<T>& s,
       for (int c = c_lo; c <= c_hi; ++c) {
         const int k = ((have >> (NMB * c)) & 1ull) ? 0 : 1;
 #pragma unroll
-        for (int j = 0; j < TP / 4; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[j][i] += s.mb[c][k][cq * 4 + i][tr + 4 * j];
+        for (int j = 0; j < TP / 4; ++j) v[j] += *(const f32x4*)&s.mb[c][k][tr + 4 * j][cq * 4];
       }
       for (int c = c_lo; c <= c_hi; ++c) {
         const int k = ((have >> (NMB * c)) & 1ull) ? 0 : 1;
