@@ -206,15 +206,22 @@ struct UnitM {
   uint32_t c[4][8]; // dword kq of (row 16*grp + nl, sub-block j)
 };
 
-__device__ __forceinline__ void load_unit_m(const uint8_t* __restrict__ u, int nl, int kq, UnitM& x) {
+
+// A unit loaded with lane = row (load_unit) into the matrix-core operand
+// layout, through the wave's LDS area ar (kUnitBytes): the unit is written in
+// its global byte layout, then lane 16*kq + nl reads the headers of rows
+// 16*grp + nl and dword kq of their codes.  LDS operations of one wave
+// complete in order, so a later call's writes never pass these reads.
+__device__ __forceinline__ void transpose_unit(const Unit& u, uint8_t* ar, int nl, int kq, int lane, UnitM& x) {
+  *(u32x4*)(ar + lane * 16) = u.h;
 #pragma unroll
-  for (int grp = 0; grp < 4; ++grp) x.h[grp] = *(const u32x4*)(u + (16 * grp + nl) * 16);
+  for (int j = 0; j < 8; ++j) *(u32x4*)(ar + kHdrBytes + j * kSubBytes + lane * 16) = u.c[j];
+#pragma unroll
+  for (int grp = 0; grp < 4; ++grp) x.h[grp] = *(const u32x4*)(ar + (16 * grp + nl) * 16);
 #pragma unroll
   for (int grp = 0; grp < 4; ++grp)
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      x.c[grp][j] = __builtin_nontemporal_load(
-          (const uint32_t*)(u + kHdrBytes + j * kSubBytes + (16 * grp + nl) * 16 + kq * 4));
+    for (int j = 0; j < 8; ++j) x.c[grp][j] = *(const uint32_t*)(ar + kHdrBytes + j * kSubBytes + (16 * grp + nl) * 16 + kq * 4);
 }
 
 // Activation rows of one superblock in the matrix-core operand order, as the

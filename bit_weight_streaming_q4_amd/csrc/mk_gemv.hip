@@ -127,10 +127,15 @@ __global__ __launch_bounds__(256) void k_gemv_dot4(GemvArgs a) {
 }
 
 // Block = 4 waves on one 64-row tile, as above; the block's activation rows
-// (superblocks [lo, hi)) are staged in LDS while each wave's first unit loads.
+// (superblocks [lo, hi)) are staged in LDS while each wave's first unit
+// loads.  A unit is loaded with 9 16-B loads per lane (lane = row, as for
+// dot4) and the next unit's loads are in flight while the current one is
+// transposed through the wave's LDS area into the matrix-core operand
+// layout and multiplied.
 __global__ __launch_bounds__(256) void k_gemv_mfma(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t act_lds[];  // per_wg x kActSbBytes
-  __shared__ float red[4][kTPad][64];
+  // per wave: one unit in its global byte layout; after the loop, the wave sums
+  __shared__ __attribute__((aligned(16))) uint8_t wl[4][kUnitBytes];
   const int tile = blockIdx.x, ks = blockIdx.y, mat = blockIdx.z;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int nl = lane & 15, kq = lane >> 4;
@@ -143,17 +148,28 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemvArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[g][i] = 0.0f;
   const uint8_t* tileW = a.W[mat] + (size_t)tile * a.nsb * kUnitBytes;
-  UnitM u0, u1;  // ping-pong buffers: the next unit's loads are issued before this unit's arithmetic
-  if (b0 < b1) load_unit_m(tileW + (size_t)b0 * kUnitBytes, nl, kq, u0);
+  uint8_t* mine = &wl[w][0];
+  Unit ua, ub;  // ping-pong buffers: the next unit's loads are issued before this unit's arithmetic
+  if (b0 < b1) load_unit(tileW + (size_t)b0 * kUnitBytes, lane, ua);
   stage_act(a.act, lo, n, act_lds);
   __syncthreads();
   for (int b = b0; b < b1; b += 2) {
-    if (b + 1 < b1) load_unit_m(tileW + (size_t)(b + 1) * kUnitBytes, nl, kq, u1);
-    mfma_unit(u0, act_lds + (b - lo) * kActSbBytes, nl, kq, acc);
+    if (b + 1 < b1) load_unit(tileW + (size_t)(b + 1) * kUnitBytes, lane, ub);
+    {
+      UnitM x;
+      transpose_unit(ua, mine, nl, kq, lane, x);
+      mfma_unit(x, act_lds + (b - lo) * kActSbBytes, nl, kq, acc);
+    }
     if (b + 1 >= b1) break;
-    if (b + 2 < b1) load_unit_m(tileW + (size_t)(b + 2) * kUnitBytes, nl, kq, u0);
-    mfma_unit(u1, act_lds + (b + 1 - lo) * kActSbBytes, nl, kq, acc);
+    if (b + 2 < b1) load_unit(tileW + (size_t)(b + 2) * kUnitBytes, lane, ua);
+    {
+      UnitM x;
+      transpose_unit(ub, mine, nl, kq, lane, x);
+      mfma_unit(x, act_lds + (b + 1 - lo) * kActSbBytes, nl, kq, acc);
+    }
   }
+  __syncthreads();  // every wave is done with its unit area before it holds the sums
+  float(*red)[kTPad][64] = (float(*)[kTPad][64])&wl[0][0];
 #pragma unroll
   for (int g = 0; g < 4; ++g)
 #pragma unroll
