@@ -63,7 +63,10 @@ def _check_head(W16, x_final, am, na, tok, gs, drafts):
     return r["top1"]
 
 
-@pytest.mark.parametrize("T,gs", [(1, [0, 1]), (5, [0, 5]), (12, [0, 3, 6, 9, 12])])
+# T = 2 and 3 are the last dot4 and the first matrix-core instances; 16 is
+# the largest T (4 agents x 4 rows).
+@pytest.mark.parametrize("T,gs", [(1, [0, 1]), (2, [0, 2]), (3, [0, 3]), (5, [0, 5]), (8, [0, 2, 4, 6, 8]),
+                                  (12, [0, 3, 6, 9, 12]), (16, [0, 4, 8, 12, 16])])
 def test_decode_step_small_stack(T, gs):
     torch = need_gpu()
     mk = _mk()
