@@ -34,7 +34,7 @@ PEAK_HBM_GBS = 8000.0
 HIDDEN, PROJ, FFN, VOCAB, LAYERS = 5120, 10240, 17408, 151936, 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_step_T12.json")
 KERNEL_SOURCES = ["bit_weight_streaming_q4_amd/csrc/mk_step.hip", "bit_weight_streaming_q4_amd/csrc/mk_device.h",
-                  "bit_weight_streaming_q4_amd/csrc/mk_gdn.h"]
+                  "bit_weight_streaming_q4_amd/csrc/mk_gdn.h", "bit_weight_streaming_q4_amd/csrc/mk_lm.h"]
 
 
 def log(*a):

@@ -47,13 +47,9 @@ constexpr int kLmWaves = 8;
 #endif
 constexpr int kLmBlocksPerCu = MK_LM_BLOCKS_PER_CU;  // resident lm_head blocks per CU
 
-// A persistent grid (a few blocks per CU) streams the vocabulary through
-// lm_stream; the last block to finish writes the argmax of every row and
-// runs the accept compare of every group.
-__global__ __launch_bounds__(64 * kLmWaves) void k_lmhead(LmArgs a) {
-  __shared__ float red[kLmWaves][64][16];
-  __shared__ int fin[16];
-  if (!lm_stream<kLmWaves>(a.s, red, fin)) return;
+// The last block's verification: argmax of every row and the accept compare
+// of every group.
+__device__ __forceinline__ void lm_verify(const LmArgs& a, const int* fin) {
   if (threadIdx.x < a.T) a.argmax[threadIdx.x] = fin[threadIdx.x];
   if (threadIdx.x == 0) {
     for (int g = 0; g < a.G; ++g) {
@@ -64,6 +60,43 @@ __global__ __launch_bounds__(64 * kLmWaves) void k_lmhead(LmArgs a) {
       a.n_acc[g] = acc_n;
       for (int i = 0; i < n; ++i) a.tokens[r + i] = i < acc_n ? dr[i] : (i == acc_n ? fin[r + acc_n] : -1);
     }
+  }
+}
+
+// A persistent grid (a few blocks per CU) streams the vocabulary through
+// lm_stream; the last block to finish writes the argmax of every row and
+// runs the accept compare of every group.
+__global__ __launch_bounds__(64 * kLmWaves) void k_lmhead(LmArgs a) {
+  __shared__ float red[kLmWaves][64][16];
+  __shared__ int fin[16];
+  if (!lm_stream<kLmWaves>(a.s, red, fin)) return;
+  lm_verify(a, fin);
+}
+
+// The same with the weights staged through LDS (H = 512 NSEG): one block of
+// 8 waves per CU, 4 stages.
+template <int NSEG>
+__global__ __launch_bounds__(512) void k_lmhead_staged(LmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t stages[4 * kLmStageBytes];
+  __shared__ int fin[16];
+  if (!lm_stream_staged<4, NSEG>(a.s, stages, fin)) return;
+  lm_verify(a, fin);
+}
+
+typedef void (*LmKernel)(LmArgs);
+static LmKernel staged_kernel(int nseg) {
+  switch (nseg) {
+    case 1: return k_lmhead_staged<1>;
+    case 2: return k_lmhead_staged<2>;
+    case 3: return k_lmhead_staged<3>;
+    case 4: return k_lmhead_staged<4>;
+    case 5: return k_lmhead_staged<5>;
+    case 6: return k_lmhead_staged<6>;
+    case 7: return k_lmhead_staged<7>;
+    case 8: return k_lmhead_staged<8>;
+    case 9: return k_lmhead_staged<9>;
+    case 10: return k_lmhead_staged<10>;
+    default: return nullptr;  // longer rows: the register-streamed kernel
   }
 }
 
@@ -98,8 +131,15 @@ hipError_t launch_lmhead(const uint16_t* W, int V, int H, const float* hid, int 
   a.argmax = argmax;
   a.n_acc = n_acc;
   a.tokens = tokens;
-  const int grid = std::min(nblk, cu_count * kLmBlocksPerCu);
-  hipLaunchKernelGGL(k_lmhead, dim3(grid), dim3(64 * kLmWaves), 0, st, a);
+  const LmKernel ks = H % 512 ? nullptr : staged_kernel(H / 512);
+  if (ks) {
+    // one block per CU (and no more blocks than the winner arrays hold)
+    const int grid = std::min(nblk, cu_count);
+    hipLaunchKernelGGL(ks, dim3(grid), dim3(512), 0, st, a);
+  } else {
+    const int grid = std::min(nblk, cu_count * kLmBlocksPerCu);
+    hipLaunchKernelGGL(k_lmhead, dim3(grid), dim3(64 * kLmWaves), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -1489,8 +1489,11 @@ __device__ __forceinline__ void gdn_wave(const StepArgs& a, int lane) {
 }
 
 // The lm_head stream over the final hidden rows (fragments written by
-// lm_prep), then the argmax and the accept compare in the last block.
-__device__ __forceinline__ void lm_phase(const StepArgs& a, float (*red)[64][16]) {
+// lm_prep), then the argmax and the accept compare in the last block.  The
+// ring area, free after the last GEMV phase, holds the LDS-staged stream's
+// three stages (hidden size 5120 or 512) or the other stream's cross-wave
+// sums.
+__device__ __forceinline__ void lm_phase(const StepArgs& a, uint8_t* ring) {
   __shared__ int fin[16];
   LmStream ls;
   ls.W = a.lm;
@@ -1500,7 +1503,15 @@ __device__ __forceinline__ void lm_phase(const StepArgs& a, float (*red)[64][16]
   ls.val = a.lm_val;
   ls.idx = a.lm_idx;
   ls.ticket = a.lm_ticket;
-  if (!lm_stream<kWavesPerBlock>(ls, red, fin)) return;
+  static_assert(kWavesPerBlock == 8, "the staged stream runs on 8 waves");
+  bool last;
+  if (a.H == 5120)
+    last = lm_stream_staged<3, 10>(ls, ring, fin);
+  else if (a.H == 512)
+    last = lm_stream_staged<3, 1>(ls, ring, fin);
+  else
+    last = lm_stream<kWavesPerBlock>(ls, (float (*)[64][16])ring, fin);
+  if (!last) return;
   if (threadIdx.x == 0) {
     for (int t = 0; t < a.T; ++t) a.out[48 + t] = fin[t];
     for (int g = 0; g < a.G; ++g) {
@@ -1554,7 +1565,8 @@ __global__ __launch_bounds__(kBlock) void k_decode_step(StepArgs a) {
   // every wave of the block takes part in the lm phase once lm_prep is done
   if (!wait_ge(a, s, &s.rel, 4 * a.L + 2)) return;
   static_assert(sizeof(s.ring) >= sizeof(float) * kWavesPerBlock * 64 * 16, "lm reduction does not fit the ring");
-  lm_phase(a, (float (*)[64][16]) & s.ring[0][0][0]);
+  static_assert(sizeof(s.ring) >= 3 * kLmStageBytes, "the lm stages do not fit the ring");
+  lm_phase(a, &s.ring[0][0][0]);
   if (blockIdx.x == 0 && threadIdx.x == 0) a.stamps[kMaxStamps - 1] = wall_clock64();
 }
 
