@@ -88,6 +88,7 @@ def lib():
     L.mk_decode_step_stamps.argtypes = [P, i32, P, P, i32, P]
     L.mk_decode_step_last_ms.argtypes = [P]
     L.mk_decode_step_last_ms.restype = ctypes.c_float
+    L.mk_read_probe.argtypes = [P, sz, P, P]
     _lib = L
     return L
 
@@ -173,6 +174,13 @@ def workspace(nbytes: int, device="cuda"):
 
 
 # --------------------------------------------------------------------- compute
+def mk_read_probe(buf, sink, stream=None):
+    """Reads every byte of the device tensor buf once (measurement aid);
+    sink is a 1-element int32 device tensor."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().mk_read_probe(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "mk_read_probe")
+
+
 def mk_quantize_rows(x, a8, s, gsum, stream=None):
     T, K = x.shape
     _check(lib().mk_quantize_rows(_ptr(x), T, K, _ptr(a8), _ptr(s), _ptr(gsum), _stream(stream)),

@@ -409,4 +409,29 @@ int mk_deltanet_commit(const mk_deltanet* st, void* stream) {
   return launch_status(mk::launch_gdn_commit(a, S(stream)), "deltanet commit");
 }
 
+// ------------------------------------------------------------------ read probe
+// Measurement aid: every thread reads 16-B words of the buffer with
+// nontemporal loads, grid-stride, and folds them into one word; a word that
+// depends on every load is stored so that no load can be dropped.
+typedef uint32_t probe_v4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void k_read_probe(const probe_v4* __restrict__ p, size_t n16, uint32_t* sink) {
+  uint32_t acc = 0;
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) {
+    const probe_v4 v = __builtin_nontemporal_load(p + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9e3779b9u) *sink = acc;  // practically never taken, but not removable
+}
+
+int mk_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  int r;
+  if ((r = check_ptr(buf, "buf")) || (r = check_ptr(sink, "sink", 4))) return r;
+  if (bytes % 16) return fail(MK_ERR_SHAPE, "read probe: %zu bytes is not a multiple of 16", bytes);
+  const int cu = device_cu_count();
+  hipLaunchKernelGGL(k_read_probe, dim3(8 * (cu > 0 ? cu : 256)), dim3(256), 0, S(stream), (const probe_v4*)buf,
+                     bytes / 16, sink);
+  return launch_status(hipGetLastError(), "read probe");
+}
+
 }  // extern "C"

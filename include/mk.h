@@ -233,6 +233,14 @@ float mk_decode_step_last_ms(const mk_stack* st);
 int mk_decode_step_stamps(const mk_stack* st, int32_t T, const void* ws, uint64_t* h_stamps, int32_t n_max,
                           int64_t* h_clock_hz);
 
+/* Measurement aid, not a step of the method: reads `bytes` bytes of buf
+ * (device, 16-B aligned, bytes % 16 == 0) once with 16-B nontemporal loads
+ * spread over the whole device, and may write one word to *sink (device, 4-B
+ * aligned) so that the loads cannot be dropped.  The time of a call over a
+ * buffer far larger than the caches is the read bandwidth the device
+ * attains, reported beside the 8 TB/s peak.  Asynchronous on `stream`. */
+int mk_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
