@@ -797,10 +797,123 @@ __device__ __forceinline__ void slot_mfma(const WregM& x, lds_u8* sl, int lane, 
   }
 }
 
+// Matrix-core engine for at most 8 (padded) rows: two sub-blocks per
+// v_mfma_i32_16x16x64_i8, in block-diagonal form.  Lane l = 16 q + n, half
+// h = q / 2.  In both operands, lane group q carries K chunks 2 (q % 2) and
+// 2 (q % 2) + 1 (8 values each) of sub-block 2 jp + h, so the product's rows
+// 0..7 are sub-block 2 jp (activation rows t = 0..7, zero where h = 1) and
+// rows 8..15 are sub-block 2 jp + 1 (activation rows t = 0..7 placed at 8..15,
+// zero where h = 0).  Every output lane then holds a result: lane (q, n) has
+// rows t = 4 (q % 2) + i of weight row n for sub-block 2 jp + h, and the two
+// halves are added across lanes l and l + 32 when the partial is handed over.
+struct WregP {
+  u32x4 h[4];
+  uint64_t cw[4][4];  // [pair jp][row group nb]: chunks 2 (q % 2), + 1 of sub-block 2 jp + h
+};
+
+__device__ __forceinline__ void read_w_pk(lds_u8* sl, int lane, WregP& x) {
+  const int q = lane >> 4, n = lane & 15, hh = q >> 1;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) x.h[nb] = *(const lds_u32x4*)(sl + (16 * nb + n) * 16);
+#pragma unroll
+  for (int jp = 0; jp < 4; ++jp)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      x.cw[jp][nb] = *(lds_u64*)(sl + kHdrBytes + (2 * jp + hh) * kSubBytes + (16 * nb + n) * 16 + (q & 1) * 8);
+}
+
+struct SubOpsP {
+  u32x4 aop;  // 16 activation bytes (zero off the diagonal)
+  f32x4 st;   // s of rows t = 4 (q % 2) .. + 3 of sub-block 2 jp + h
+};
+
+// Off-diagonal lanes read row 15 of the record, which is zero for T <= 8.
+__device__ __forceinline__ void read_sub_pk(lds_u8* act, lds_f32* sc, int jp, int q, int n, SubOpsP& o) {
+  const int hh = q >> 1;
+  const bool diag = (n < 8) == (hh == 0);
+  const int tt = diag ? n - 8 * hh : 15;
+  const int jj = 2 * jp + hh, c0 = 2 * (q & 1);
+  const uint64_t a0 = *(lds_u64*)(act + ((jj * 4 + c0) * 16 + tt) * 8);
+  const uint64_t a1 = *(lds_u64*)(act + ((jj * 4 + c0 + 1) * 16 + tt) * 8);
+  o.aop = (u32x4){(uint32_t)a0, (uint32_t)(a0 >> 32), (uint32_t)a1, (uint32_t)(a1 >> 32)};
+  o.st = *(const lds_f32x4*)(sc + jj * 16 + 4 * (q & 1));
+}
+
+__device__ __forceinline__ void mfma_sub_pk(const SubOpsP& o, const uint64_t (&cw)[4], i32x4 (&p)[4]) {
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const uint32_t w0 = (uint32_t)cw[nb], w1 = (uint32_t)(cw[nb] >> 32);
+    const u32x4 b = {w0 & 0x0F0F0F0Fu, (w0 >> 4) & 0x0F0F0F0Fu, w1 & 0x0F0F0F0Fu, (w1 >> 4) & 0x0F0F0F0Fu};
+    const i32x4 z = {0, 0, 0, 0};
+    p[nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, o.aop), __builtin_bit_cast(i32x4, b), z,
+                                                  0, 0, 0);
+  }
+}
+
+// acc[nb][i] += P * (d * sc) * s for the products of pair jp; sc03h/sc47h hold
+// this lane's sub-block scales shifted so that byte 2 (jp % 2) is sub-block
+// 2 jp + h.
+__device__ __forceinline__ void scale_sub_pk(int jp, const float (&d)[4], const uint32_t (&sc03h)[4],
+                                             const uint32_t (&sc47h)[4], const f32x4 st, const i32x4 (&p)[4],
+                                             f32x4 (&acc)[4]) {
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const float f = d[nb] * byte_f32(jp < 2 ? sc03h[nb] : sc47h[nb], 2 * (jp & 1));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[nb][i] = __builtin_fmaf((float)p[nb][i], f * st[i], acc[nb][i]);
+  }
+}
+
+__device__ __forceinline__ void slot_mfma_pk(const WregP& x, lds_u8* sl, int lane, f32x4 (&acc)[4]) {
+  const int q = lane >> 4, n = lane & 15, hh = q >> 1;
+  lds_u8* act = sl + kUnitBytes;
+  lds_f32* sc = (lds_f32*)(act + kActA);
+  const u32x4 (&h)[4] = x.h;
+  SubOpsP o[4];
+  read_sub_pk(act, sc, 0, q, n, o[0]);
+  read_sub_pk(act, sc, 1, q, n, o[1]);
+  float d[4], dmin[4];
+  uint32_t sc03[4], sc47[4], sc03h[4], sc47h[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    d[nb] = f16_bits_to_f32(h[nb].x & 0xffffu);
+    dmin[nb] = f16_bits_to_f32(h[nb].x >> 16);
+    asm("v_and_b32 %0, %1, %2" : "=v"(sc03[nb]) : "v"(h[nb].y), "v"(0x3F3F3F3Fu));
+    asm("v_and_b32 %0, %1, %2" : "=v"(sc47[nb]) : "v"(h[nb].z), "v"(0x3F3F3F3Fu));
+    sc03h[nb] = sc03[nb] >> (8 * hh);
+    sc47h[nb] = sc47[nb] >> (8 * hh);
+  }
+  // min term, as in slot_mfma: its rows t >= 8 have zero activation sums, so
+  // it lands in lanes q < 2 only
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const uint32_t m03 = (h[nb].w & 0x0F0F0F0Fu) | ((h[nb].y >> 2) & 0x30303030u);
+    const uint32_t m47 = ((h[nb].w >> 4) & 0x0F0F0F0Fu) | ((h[nb].z >> 2) & 0x30303030u);
+    const float bm0 = -dmin[nb] * (float)((m03 >> (8 * q)) & 0xffu);
+    const float bm1 = -dmin[nb] * (float)((m47 >> (8 * q)) & 0xffu);
+    const float am0 = sc[128 + q * 16 + n], am1 = sc[128 + (q + 4) * 16 + n];
+    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(am0, bm0, acc[nb], 0, 0, 0);
+    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(am1, bm1, acc[nb], 0, 0, 0);
+  }
+  i32x4 p[4][4];
+  mfma_sub_pk(o[0], x.cw[0], p[0]);
+#pragma unroll
+  for (int jp = 0; jp < 4; ++jp) {
+    if (jp + 2 < 4) read_sub_pk(act, sc, jp + 2, q, n, o[jp + 2]);
+    if (jp + 1 < 4) mfma_sub_pk(o[jp + 1], x.cw[jp + 1], p[jp + 1]);
+    scale_sub_pk(jp, d, sc03h, sc47h, o[jp].st, p[jp], acc);
+  }
+}
+
 // Which engine a T-row instance uses.
 template <int T>
 struct UseMfma {
   static constexpr bool value = T > 2;
+};
+// The packed matrix-core engine serves instances of at most 8 padded rows.
+template <int T>
+struct PackMfma {
+  static constexpr bool value = T > 2 && TPad<T>::value <= 8;
 };
 
 // What a compute wave accumulates: the open (tile, matrix) of phase q.  The
@@ -838,6 +951,13 @@ __device__ __forceinline__ void flush(BlockState<T>& s, int c, int lane, Consume
     }
   }
   if constexpr (UseMfma<T>::value) {
+    if constexpr (PackMfma<T>::value) {
+      // the packed engine's lanes l + 32 hold the second sub-block of each pair
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) k.macc[nb][i] += __shfl_xor(k.macc[nb][i], 32, 64);
+    }
     // C layout: lane 16 q + n holds rows t = 4q .. 4q + 3 of tile row 16 nb + n
     const int q = lane >> 4, n = lane & 15;
     if (4 * q < TPad<T>::value)
@@ -999,15 +1119,21 @@ __device__ __forceinline__ void consume(const StepArgs& a, BlockState<T>& s, int
     acc_zero<T>(k);
   }
   lds_u8* sl = as_lds(&s.ring[c][kcur][0]);
-  {
+  if constexpr (PackMfma<T>::value) {
+    WregP x;
+    read_w_pk(sl, lane, x);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the weight region is read before it is refilled
+    issue_w(a, wt, wu, cs, c, lane, lcur, cur);
+    slot_mfma_pk(x, sl, lane, k.macc);
+  } else {
     WregM x;
     read_w_mfma(sl, lane, x);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the weight region is read before it is refilled
     issue_w(a, wt, wu, cs, c, lane, lcur, cur);
     slot_mfma(x, sl, lane, k.macc);
-    finish_early<T>(s, c, lane, k, oth.q, oth.tm, ok);
-    issue_a<true>(a, lane, lcur, k.q, cur);
   }
+  finish_early<T>(s, c, lane, k, oth.q, oth.tm, ok);
+  issue_a<true>(a, lane, lcur, k.q, cur);
 }
 
 template <int T>
