@@ -905,15 +905,16 @@ __device__ __forceinline__ void slot_mfma_pk(const WregP& x, lds_u8* sl, int lan
   }
 }
 
-// Which engine a T-row instance uses.
+// Which engine a T-row instance uses: dot4 for one row (its arithmetic is
+// short enough to hide under the loads), the packed matrix-core engine up to
+// 8 padded rows, the plain one above.
 template <int T>
 struct UseMfma {
-  static constexpr bool value = T > 2;
+  static constexpr bool value = T > 1;
 };
-// The packed matrix-core engine serves instances of at most 8 padded rows.
 template <int T>
 struct PackMfma {
-  static constexpr bool value = T > 2 && TPad<T>::value <= 8;
+  static constexpr bool value = UseMfma<T>::value && TPad<T>::value <= 8;
 };
 
 // What a compute wave accumulates: the open (tile, matrix) of phase q.  The
@@ -1021,7 +1022,7 @@ __device__ __forceinline__ void finish_early(BlockState<T>& s, int c, int lane, 
   }
 }
 
-// The dot4 engine's stream (T <= 2): as below, but each slot is refilled
+// The dot4 engine's stream (T = 1): as below, but each slot is refilled
 // after its unit's arithmetic, which measured faster for this short
 // arithmetic.  Consumes the unit of slot `cur` (the other slot `oth` holds
 // the next one).
