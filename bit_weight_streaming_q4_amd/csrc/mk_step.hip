@@ -1606,13 +1606,23 @@ __device__ __forceinline__ void watch_wave(const StepArgs& a, BlockState<T>& s, 
 // Nothing in the step consumes their outputs, so they run beside the layer
 // pipeline instead of inside one of its phases; the block's last barrier
 // waits for them (see service_wave).
+// Jobs are numbered over the whole step (GDN layer i, job j: i * nj + j) and
+// dealt to the blocks round-robin, so that the blocks share them evenly
+// even when a layer has fewer jobs than there are blocks (one agent: 64 jobs
+// per layer for 256 blocks).  The GDN wave shares its SIMD with a compute
+// wave, so an uneven share would slow that block's streaming.
 __device__ __forceinline__ void gdn_wave(const StepArgs& a, int lane) {
   if (a.n_agents <= 0) return;
   const long nj = (long)a.n_agents * kGdnHeadsPerLayer * 2;
-  const long j0 = nj * blockIdx.x / gridDim.x, j1 = nj * (blockIdx.x + 1) / gridDim.x;
-  for (int l = 0; l < a.L; ++l)
-    if (layer_is_gdn(a, l))
-      for (long j = j0; j < j1; ++j) gdn_job(a, l, j, lane);
+  const long nb = gridDim.x;
+  long i = 0;  // GDN layers seen
+  for (int l = 0; l < a.L; ++l) {
+    if (!layer_is_gdn(a, l)) continue;
+    long j = ((long)blockIdx.x - i * nj) % nb;
+    if (j < 0) j += nb;
+    for (; j < nj; j += nb) gdn_job(a, l, j, lane);
+    ++i;
+  }
 }
 
 // The lm_head stream over the final hidden rows (fragments written by
