@@ -17,13 +17,14 @@ the order the pages give them.  Each function names the step it follows:
   C6 lmhead/verify  logits, argmax, accepted-prefix length, emitted tokens
   C7 gdn_step       gated delta rule with commit through the accepted row
   C8 decode_step    composition of one whole step
+  A1 attn_decode    full-attention decode of T rows over an fp16 KV cache
 
 Pages: richland.au "Fusing the whole speculative-decoding cycle into one CUDA
 kernel" (section "What shipped"), richland.au "OpenJet's CUDA megakernel runs
 4 coding agents" (section "Why it matters"), pulse-3k2 "UPDATE: ... KL
 divergence" (section "Decode accuracy").
 
-Parity status: C1-C4, C6 and C7 are pinned by tests against brute force,
+Parity status: C1-C4, C6, C7 and A1 are pinned by tests against brute force,
 closed forms and library routines.  C5's glue (pre-RMSNorm, identity mixer)
 and C8's composition are readings of the pages: parity unpinned beyond the
 pinned parts they compose.
@@ -76,6 +77,7 @@ def _load():
     lib.orc_verify.argtypes = [P, P, i32, P, P, P]
     lib.orc_gdn_rows.argtypes = [P, i32, i32, P, P, P, P, P, i32, i64, i64, i64, P, i64, ctypes.c_int]
     lib.orc_gdn_step.argtypes = [P, i32, i32, i32, P, P, P, P, P, i32, i32, P]
+    lib.orc_attn_decode.argtypes = [P, P, i32, i32, P, P, i32, i32, i32, P, P, i32, P]
     _lib = lib
     return lib
 
@@ -271,3 +273,28 @@ def gdn_step(S, q, k, v, g, beta, a):
     o = np.empty((T, nh, dv), np.float32)
     _load().orc_gdn_step(_p(S32), nh, dk, dv, _p(q), _p(k), _p(v), _p(g), _p(beta), T, int(a), _p(o))
     return S32.reshape(shp), o
+
+
+def attn_decode(q, gate, kc, vc, ctx, group_start=None) -> np.ndarray:
+    """A1: full-attention decode.  q, gate (or None) fp32 [T][Hq][d]; kc fp16
+    bits [G][Hkv][cap][d]; vc fp16 bits [G][Hkv][d][cap] (dimension-major);
+    ctx [G] positions cached before the step; group_start [G+1] (None = one
+    group).  Row i of group g sees positions 0..ctx[g]+i.  Returns o fp32
+    [T][Hq][d]."""
+    q = _c(q, np.float32)
+    T, Hq, d = q.shape
+    kc = _c(kc, np.uint16)
+    vc = _c(vc, np.uint16)
+    G, Hkv, cap, dk = kc.shape
+    if dk != d or vc.shape != (G, Hkv, d, cap) or Hq % Hkv:
+        raise ValueError("attention: shape mismatch")
+    ctx = _c(np.asarray(ctx), np.int32)
+    gs = _c(np.asarray([0, T] if group_start is None else group_start), np.int32)
+    if len(ctx) != G or len(gs) != G + 1 or gs[0] != 0 or gs[-1] != T or np.any(np.diff(gs) <= 0):
+        raise ValueError("attention: bad groups")
+    if np.any(ctx < 0) or np.any(ctx + np.diff(gs) > cap):
+        raise ValueError("attention: context exceeds the cache")
+    gate = _c(gate, np.float32) if gate is not None else None
+    o = np.empty((T, Hq, d), np.float32)
+    _load().orc_attn_decode(_p(q), _p(gate), T, Hq, _p(kc), _p(vc), Hkv, d, cap, _p(ctx), _p(gs), G, _p(o))
+    return o

@@ -349,3 +349,74 @@ void orc_gdn_step(float* S, int32_t nh, int32_t dk, int32_t dv, const float* q, 
     free(Sd);
   }
 }
+
+/* Full-attention decode of T query rows over a per-agent KV cache (the
+ * model's full-attention layers; richland.au "Fusing the whole
+ * speculative-decoding cycle into one CUDA kernel", section "What shipped":
+ * split-K flash decoding over an fp16 KV cache).  Definition written out:
+ *   row t of group g (index i in the group, ctx[g] cached positions before
+ *   the step) and query head hq see positions j = 0 .. ctx[g] + i, the
+ *   group's own newer rows hidden (causal among drafts);
+ *   s_j = (q_t,hq . K_j) / sqrt(d),   w_j = exp(s_j - max s),
+ *   o = (sum_j w_j V_j) / (sum_j w_j),  then o *= 1 / (1 + exp(-gate)) if a
+ *   gate is given (the output gate of gated attention).
+ * KV head of query head hq: hq / (Hq / Hkv) (grouped queries).
+ * Layouts: q, gate, o [T][Hq][d] fp32; kc [G][Hkv][cap][d] and vc
+ * [G][Hkv][d][cap] fp16 bits (V stored dimension-major); ctx [G];
+ * gs [G+1] group starts.  Every accumulation is in double, the output is
+ * rounded once to fp32. */
+void orc_attn_decode(const float* q, const float* gate, int32_t T, int32_t Hq, const uint16_t* kc,
+                     const uint16_t* vc, int32_t Hkv, int32_t d, int32_t cap, const int32_t* ctx,
+                     const int32_t* gs, int32_t G, float* o) {
+  float* f16 = (float*)malloc(sizeof(float) * 65536);
+  for (int b = 0; b < 65536; ++b) f16[b] = orc_f16_to_f32((uint16_t)b);
+  const int gqa = Hq / Hkv;
+  const double inv_sqrt_d = 1.0 / sqrt((double)d);
+#pragma omp parallel
+  {
+    double* s = NULL;
+    int64_t s_cap = 0;
+    double* acc = (double*)malloc(sizeof(double) * d);
+#pragma omp for schedule(dynamic)
+    for (int64_t th = 0; th < (int64_t)T * Hq; ++th) {
+      const int t = (int)(th / Hq), hq = (int)(th % Hq);
+      int g = 0;
+      while (!(gs[g] <= t && t < gs[g + 1])) ++g;
+      const int64_t n = (int64_t)ctx[g] + (t - gs[g]) + 1;
+      const int h = hq / gqa;
+      const uint16_t* K = kc + ((int64_t)g * Hkv + h) * cap * d;
+      const uint16_t* V = vc + ((int64_t)g * Hkv + h) * d * cap;
+      const float* qr = q + th * d;
+      if (n > s_cap) {
+        free(s);
+        s_cap = n;
+        s = (double*)malloc(sizeof(double) * n);
+      }
+      double mx = -INFINITY;
+      for (int64_t j = 0; j < n; ++j) {
+        double dot = 0.0;
+        for (int k = 0; k < d; ++k) dot += (double)qr[k] * (double)f16[K[j * d + k]];
+        s[j] = dot * inv_sqrt_d;
+        if (s[j] > mx) mx = s[j];
+      }
+      double den = 0.0;
+      for (int64_t j = 0; j < n; ++j) {
+        s[j] = exp(s[j] - mx);
+        den += s[j];
+      }
+      for (int k = 0; k < d; ++k) {
+        double a = 0.0;
+        for (int64_t j = 0; j < n; ++j) a += s[j] * (double)f16[V[(int64_t)k * cap + j]];
+        acc[k] = a / den;
+      }
+      for (int k = 0; k < d; ++k) {
+        double y = acc[k];
+        if (gate) y *= 1.0 / (1.0 + exp(-(double)gate[th * d + k]));
+        o[th * d + k] = (float)y;
+      }
+    }
+    free(acc);
+    free(s);
+  }
+  free(f16);
+}

@@ -122,3 +122,50 @@ def gdn_step(step, T, n_layers=48, heads=GDN_HEADS, dk=GDN_DK, dv=GDN_DV, seed=G
 def gdn_accept_lengths(n_steps, T=5, seed=GDN_SEED):
     """Seeded accept lengths, uniform on 0..T-1."""
     return uniform_i32(seed, 2, 0, n_steps, 0, T - 1)
+
+
+# ---------------------------------------------------------------- full attention
+# 16 of the 64 layers run full attention.  Head geometry (a reading: the
+# pages give none): 32 query heads and 8 KV heads of 128, which with an
+# output gate of the query's width fills the 10240-wide input projection
+# exactly (q 4096 + gate 4096 + k 1024 + v 1024).
+ATTN_SEED = 5
+ATTN_Q_HEADS = 32
+ATTN_KV_HEADS = 8
+ATTN_D = 128
+F16_NAN = 0x7E00
+
+
+def attn_cap(ctx, sizes, align=64):
+    need = max(int(c) + int(n) for c, n in zip(ctx, sizes))
+    return (need + align - 1) // align * align
+
+
+def attn_inputs(ctx, sizes, Hq=ATTN_Q_HEADS, Hkv=ATTN_KV_HEADS, d=ATTN_D, cap=None, seed=ATTN_SEED, layer=0,
+                gate=True, fill=F16_NAN):
+    """One attention layer's decode inputs for G agents.
+
+    Agent g has ctx[g] cached positions and sizes[g] new rows (token +
+    drafts), whose k and v already sit at positions ctx[g] .. ctx[g] +
+    sizes[g] - 1.  K cache [G][Hkv][cap][d] and V cache [G][Hkv][d][cap]
+    (dimension-major) hold fp16 N(0, 1) values; slots past an agent's last
+    position hold ``fill`` (a NaN by default, so that a kernel that reads
+    them into its result is caught).  q and gate are fp32 N(0, 1)
+    [T][Hq][d].  Returns q, gate (or None), k, v, ctx, group_start.
+    """
+    G = len(ctx)
+    if cap is None:
+        cap = attn_cap(ctx, sizes)
+    kc = np.full((G, Hkv, cap, d), fill, np.uint16)
+    vc = np.full((G, Hkv, d, cap), fill, np.uint16)
+    for g in range(G):
+        n = int(ctx[g]) + int(sizes[g])
+        for h in range(Hkv):
+            sub = g * Hkv + h
+            kc[g, h, :n, :] = normal_f16(seed, 100 + layer, sub, n * d).reshape(n, d)
+            vc[g, h, :, :n] = normal_f16(seed, 200 + layer, sub, n * d).reshape(n, d).T
+    T = int(sum(sizes))
+    q = normal_f32(seed, 300 + layer, 0, T * Hq * d).reshape(T, Hq, d)
+    gt = normal_f32(seed, 400 + layer, 0, T * Hq * d).reshape(T, Hq, d) if gate else None
+    gs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    return {"q": q, "gate": gt, "k": kc, "v": vc, "ctx": np.asarray(ctx, np.int32), "group_start": gs}

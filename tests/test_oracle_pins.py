@@ -384,3 +384,144 @@ def test_stack_bytes_match_the_pages_arithmetic():
     ms = fig["weights_per_step_gb"]["value"] / fig["rtx3090_bandwidth_gb_s"]["value"] * 1e3
     assert abs(ms - fig["weight_read_ms"]["value"]) < 0.5
     assert len(recipes.gdn_layers()) == fig["layers_gdn"]["value"]
+
+
+# ----------------------------------------------------------------- A1 attention
+def _attn_small(ctx, sizes, Hq=4, Hkv=2, d=8, gate=True, fill=recipes.F16_NAN):
+    return recipes.attn_inputs(ctx, sizes, Hq=Hq, Hkv=Hkv, d=d, gate=gate, fill=fill, seed=11)
+
+
+def _run_attn(orc, a):
+    return orc.attn_decode(a["q"], a["gate"], a["k"], a["v"], a["ctx"], a["group_start"])
+
+
+def test_attn_brute_force_decimal(orc):
+    """A1 against a 50-digit decimal evaluation of softmax(q K^T / sqrt(d)) V
+    with the output gate, on two agents of unequal context and group size
+    (every fp16 and fp32 input converts to Decimal exactly)."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    a = _attn_small([5, 0], [2, 3])
+    o = _run_attn(orc, a)
+    q, gt, K, V, ctx, gs = a["q"], a["gate"], a["k"], a["v"], a["ctx"], a["group_start"]
+    T, Hq, d = q.shape
+    Hkv = K.shape[1]
+    Kf = _f16(K)
+    Vf = _f16(V)
+    sd = Decimal(d).sqrt()
+    worst = 0.0
+    for g in range(len(ctx)):
+        for i in range(gs[g + 1] - gs[g]):
+            t = gs[g] + i
+            for hq in range(Hq):
+                h = hq // (Hq // Hkv)
+                n = ctx[g] + i + 1
+                s = [sum(Decimal(float(q[t, hq, k])) * Decimal(float(Kf[g, h, j, k])) for k in range(d)) / sd
+                     for j in range(n)]
+                m = max(s)
+                w = [(x - m).exp() for x in s]
+                den = sum(w)
+                for k in range(d):
+                    y = sum(w[j] * Decimal(float(Vf[g, h, k, j])) for j in range(n)) / den
+                    y = y / (1 + (-Decimal(float(gt[t, hq, k]))).exp())
+                    worst = max(worst, abs(float(y) - float(o[t, hq, k])) / max(abs(float(y)), 1e-30))
+    assert worst < 1e-6, worst
+
+
+def test_attn_equal_keys_give_the_mean_of_visible_values(orc):
+    """A1 closed form: when every key of a head is the same vector, all
+    visible positions weigh the same, so row i of a group returns the plain
+    mean of V over positions 0..ctx+i (no gate)."""
+    a = _attn_small([7, 3], [3, 2], gate=False)
+    a["k"][:] = a["k"][:, :, :1, :]  # position 0's key everywhere (also the unused slots)
+    o = _run_attn(orc, a)
+    Vf = _f16(a["v"])
+    for g in range(2):
+        for i in range(a["group_start"][g + 1] - a["group_start"][g]):
+            n = a["ctx"][g] + i + 1
+            t = a["group_start"][g] + i
+            for hq in range(4):
+                ref = Vf[g, hq // 2, :, :n].mean(axis=1)
+                np.testing.assert_allclose(o[t, hq], ref, rtol=1e-6, atol=1e-7)
+
+
+def test_attn_causal_bound_is_inclusive_of_own_row_only(orc):
+    """A1 causal mask: a key planted at position ctx+i dominates row i of the
+    group, while the same key at position ctx+i+1 (the group's next row) is
+    invisible to row i."""
+    d = 8
+    for offset, visible in ((0, True), (1, False)):
+        a = _attn_small([4, 9], [3, 3], d=d, gate=False)
+        a["k"][:] = 0
+        a["q"][:] = 0
+        a["q"][:, :, 0] = 1.0
+        t, g, i = 4, 1, 1  # group 1, row 1
+        p = a["ctx"][g] + i + offset
+        a["k"][g, :, p, 0] = synth.f64_to_f16_bits(64.0)
+        o = _run_attn(orc, a)
+        Vf = _f16(a["v"])
+        n = a["ctx"][g] + i + 1
+        for hq in range(4):
+            h = hq // 2
+            if visible:
+                np.testing.assert_allclose(o[t, hq], Vf[g, h, :, p], rtol=1e-6, atol=1e-6)
+            else:
+                np.testing.assert_allclose(o[t, hq], Vf[g, h, :, :n].mean(axis=1), rtol=1e-6, atol=1e-7)
+
+
+def test_attn_query_heads_share_kv_heads_in_groups(orc):
+    """A1 grouped queries: query head hq reads KV head hq // (Hq / Hkv).  With
+    V of KV head h equal to h + 1 everywhere the output is exactly that."""
+    a = _attn_small([6], [2], Hq=8, Hkv=2, gate=False)
+    for h in range(2):
+        a["v"][:, h] = synth.f64_to_f16_bits(h + 1.0)
+    o = _run_attn(orc, a)
+    for hq in range(8):
+        assert np.all(o[:, hq] == hq // 4 + 1.0)
+
+
+def test_attn_value_cache_is_dimension_major(orc):
+    """A1 layout: V [G][Hkv][d][cap].  With V[..][k][j] = k the output is k
+    for every row and head."""
+    a = _attn_small([10, 2], [2, 1], gate=False)
+    for k in range(8):
+        a["v"][:, :, k, :] = synth.f64_to_f16_bits(float(k))
+    o = _run_attn(orc, a)
+    assert np.all(o == np.arange(8, dtype=np.float32)[None, None, :])
+
+
+def test_attn_zero_gate_halves_the_output(orc):
+    """A1 gate: sigmoid(0) = 1/2, so a zero gate halves the ungated output
+    exactly."""
+    a = _attn_small([5, 1], [2, 2], gate=False)
+    o0 = _run_attn(orc, a)
+    a["gate"] = np.zeros_like(a["q"])
+    o1 = _run_attn(orc, a)
+    assert np.array_equal(o1, o0 * np.float32(0.5))
+
+
+def test_attn_ignores_slots_past_the_last_position(orc):
+    """A1 reads nothing past position ctx+n-1: NaN-filled and zero-filled
+    unused slots give the same result."""
+    a = _attn_small([3, 8], [3, 2], fill=recipes.F16_NAN)
+    b = _attn_small([3, 8], [3, 2], fill=0)
+    assert np.array_equal(_run_attn(orc, a), _run_attn(orc, b))
+    assert np.isfinite(_run_attn(orc, a)).all()
+
+
+def test_attn_large_scores_stay_finite(orc):
+    """A1 is shift invariant: scores of about 2e6 (where exp alone overflows)
+    still give the closed-form mean when all keys are equal."""
+    a = _attn_small([5, 2], [2, 2], gate=False)
+    a["k"][:] = 0
+    a["k"][:, :, :, 0] = synth.f64_to_f16_bits(60000.0)
+    a["q"][:] = 0
+    a["q"][:, :, 0] = 100.0
+    o = _run_attn(orc, a)
+    Vf = _f16(a["v"])
+    for g in range(2):
+        for i in range(2):
+            n = a["ctx"][g] + i + 1
+            t = a["group_start"][g] + i
+            for hq in range(4):
+                np.testing.assert_allclose(o[t, hq], Vf[g, hq // 2, :, :n].mean(axis=1), rtol=1e-6, atol=1e-7)
