@@ -89,6 +89,9 @@ def lib():
     L.mk_decode_step_last_ms.argtypes = [P]
     L.mk_decode_step_last_ms.restype = ctypes.c_float
     L.mk_read_probe.argtypes = [P, sz, P, P]
+    L.mk_attn_decode_workspace.argtypes = [i32, i32, i32, P, P, i32]
+    L.mk_attn_decode_workspace.restype = sz
+    L.mk_attn_decode.argtypes = [P, P, i32, i32, P, P, i32, i32, i32, P, P, i32, P, P, sz, P]
     _lib = L
     return L
 
@@ -229,6 +232,31 @@ def mk_lmhead_verify(W16, hid, group_start, drafts, argmax, n_acc, tokens, ws=No
         ws = workspace(mk_lmhead_verify_workspace(V, H, T), hid.device)
     _check(lib().mk_lmhead_verify(_ptr(W16), V, H, _ptr(hid), T, gs, G, _ptr(drafts), _ptr(argmax), _ptr(n_acc),
                                   _ptr(tokens), _ptr(ws), ws.numel(), _stream(stream)), "mk_lmhead_verify")
+
+
+def _attn_groups(T, ctx, group_start):
+    ctx_np = np.ascontiguousarray(ctx, np.int32)
+    gs_np = np.ascontiguousarray([0, T] if group_start is None else group_start, np.int32)
+    return ctx_np, gs_np, len(gs_np) - 1
+
+
+def mk_attn_decode_workspace(T: int, Hq: int, Hkv: int, ctx, group_start=None) -> int:
+    ctx_np, gs_np, G = _attn_groups(T, ctx, group_start)
+    return int(lib().mk_attn_decode_workspace(T, Hq, Hkv, ctx_np.ctypes.data, gs_np.ctypes.data, G))
+
+
+def mk_attn_decode(q, gate, k_cache, v_cache, ctx, group_start, o, ws=None, stream=None):
+    """q, gate (or None), o: fp32 [T][Hq][128]; k_cache int16/uint16 bits
+    [G][Hkv][cap][128]; v_cache [G][Hkv][128][cap]; ctx, group_start: host
+    sequences (group_start None = one group)."""
+    T, Hq, d = q.shape
+    G_, Hkv, cap, _ = k_cache.shape
+    ctx_np, gs_np, G = _attn_groups(T, ctx, group_start)
+    if ws is None:
+        ws = workspace(max(mk_attn_decode_workspace(T, Hq, Hkv, ctx_np, gs_np), 256), q.device)
+    _check(lib().mk_attn_decode(_ptr(q), _ptr(gate), T, Hq, _ptr(k_cache), _ptr(v_cache), Hkv, d, cap,
+                                ctx_np.ctypes.data, gs_np.ctypes.data, G, _ptr(o), _ptr(ws), ws.numel(),
+                                _stream(stream)), "mk_attn_decode")
 
 
 class DeltaNetState:

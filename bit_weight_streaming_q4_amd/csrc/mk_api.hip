@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <math.h>
 #include <mutex>
 #include <vector>
 
@@ -422,6 +424,72 @@ __global__ __launch_bounds__(256) void k_read_probe(const probe_v4* __restrict__
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   if (acc == 0x9e3779b9u) *sink = acc;  // practically never taken, but not removable
+}
+
+// ------------------------------------------------------------------ attention
+static int check_attn(int32_t T, int32_t Hq, int32_t Hkv, int32_t d, int32_t cap, const int32_t* h_ctx,
+                      const int32_t* h_group_start, int32_t G, std::vector<int32_t>& gs) {
+  int r;
+  if ((r = check_T(T))) return r;
+  if (d != 128) return fail(MK_ERR_SHAPE, "attention: d = %d (128 required)", d);
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv) return fail(MK_ERR_SHAPE, "attention: Hq = %d, Hkv = %d", Hq, Hkv);
+  if (cap <= 0 || cap % 64) return fail(MK_ERR_SHAPE, "attention: cap = %d is not a positive multiple of 64", cap);
+  if (!h_ctx) return fail(MK_ERR_ARG, "attention: h_ctx is null");
+  if (G > MK_ATTN_MAX_G) return fail(MK_ERR_RANGE, "attention: G = %d > %d", G, MK_ATTN_MAX_G);
+  if ((r = check_groups(h_group_start, G, T, gs))) return r;
+  const int gqa = Hq / Hkv;
+  for (int g = 0; g < G; ++g) {
+    const int n = gs[g + 1] - gs[g];
+    if (h_ctx[g] < 0 || (long)h_ctx[g] + n > cap)
+      return fail(MK_ERR_RANGE, "attention: agent %d: ctx %d + %d rows exceeds cap %d", g, h_ctx[g], n, cap);
+    if (n * gqa > 64) return fail(MK_ERR_RANGE, "attention: agent %d: %d rows x %d query heads > 64", g, n, gqa);
+  }
+  return MK_OK;
+}
+
+size_t mk_attn_decode_workspace(int32_t T, int32_t Hq, int32_t Hkv, const int32_t* h_ctx,
+                                const int32_t* h_group_start, int32_t G) {
+  std::vector<int32_t> gs;
+  if (check_attn(T, Hq, Hkv, 128, 1 << 30, h_ctx, h_group_start, G, gs)) return 0;
+  const mk::AttnPlan p = mk::plan_attn(G, h_ctx, gs.data(), Hkv, device_cu_count());
+  return mk::attn_workspace_bytes(T, Hq, p);
+}
+
+int mk_attn_decode(const float* q, const float* gate, int32_t T, int32_t Hq, const uint16_t* k_cache,
+                   const uint16_t* v_cache, int32_t Hkv, int32_t d, int32_t cap, const int32_t* h_ctx,
+                   const int32_t* h_group_start, int32_t G, float* o, void* ws, size_t ws_bytes, void* stream) {
+  int r;
+  std::vector<int32_t> gs;
+  if ((r = check_attn(T, Hq, Hkv, d, cap, h_ctx, h_group_start, G, gs))) return r;
+  if ((r = check_ptr(q, "q")) || (r = check_ptr(k_cache, "k_cache")) || (r = check_ptr(v_cache, "v_cache")) ||
+      (r = check_ptr(o, "o")))
+    return r;
+  if (gate && !aligned(gate, 16)) return fail(MK_ERR_ALIGN, "gate not 16-B aligned");
+  const mk::AttnPlan p = mk::plan_attn(G, h_ctx, gs.data(), Hkv, device_cu_count());
+  const size_t need = mk::attn_workspace_bytes(T, Hq, p);
+  if (!ws || ws_bytes < need) return fail(MK_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if ((r = check_ptr(ws, "workspace", 256))) return r;
+  mk::AttnArgs a = {};
+  a.q = q;
+  a.gate = gate;
+  a.o = o;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.qscale = (float)(1.4426950408889634 / sqrt(128.0));
+  a.T = T;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.gqa = Hq / Hkv;
+  a.cap = cap;
+  a.G = G;
+  int nmax = 0;
+  for (int g = 0; g < G; ++g) {
+    a.ctx[g] = h_ctx[g];
+    nmax = std::max(nmax, gs[g + 1] - gs[g]);
+  }
+  for (int g = 0; g <= G; ++g) a.gs[g] = gs[g];
+  const int nb = (nmax * a.gqa + 15) / 16;
+  return launch_status(mk::launch_attn(a, p, nb, ws, S(stream)), "attention");
 }
 
 int mk_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

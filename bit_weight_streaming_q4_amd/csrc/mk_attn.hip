@@ -1,0 +1,313 @@
+// mk_attn.hip — full-attention decode of T query rows over an fp16 KV cache
+// (richland.au, "Fusing the whole speculative-decoding cycle into one CUDA
+// kernel", section "What shipped": the attention layers decode with split-K
+// flash decoding over an fp16 KV cache, tensor-core products on K/V tiles).
+//
+// Work split: one wave owns one item = (agent g, KV head h, split s), the
+// positions [s*chunk, min(L_g, (s+1)*chunk)) of that agent's cache, and all
+// query columns that read KV head h: the agent's n_g rows x the Hq/Hkv query
+// heads of the group (NQ <= 16*NB columns).  A second launch merges the
+// splits of each (row, query head) and applies the output gate.
+//
+// Per 64-position tile the wave computes the transposed scores
+//   S^T[pos][col] = K[pos] . q[col]            (v_mfma_f32_16x16x32_f16)
+// and accumulates
+//   O^T[dim][col] += V^T[dim][pos] P^T[pos][col]
+// so that every lane holds one query column in both products: the online
+// softmax (running max, rescale) stays inside the lane and its three
+// neighbours at distance 16, 32, 48.  The MFMA k index is permuted so that
+// each lane's operands are 16 contiguous bytes: K rows are position-major
+// (lane group j reads dims 32m + 8j .. +7 of its position in product m), and
+// the V cache is dimension-major, so a lane reads 8 consecutive positions of
+// one dimension.  Score block b (16 positions) maps its row r to position
+// 32(b/2) + 8(r/4) + 4(b%2) + r%4, which puts positions 32hh + 8j .. +7 of
+// half tile hh in lane group j: exactly the B operand the PV product needs.
+//
+// Precision: K and V are fp16 (exact in the products).  q * log2(e)/sqrt(d)
+// and the probabilities p are split into fp16 hi + lo parts (split_f16), so
+// both products carry about 22 bits; accumulation is fp32.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "mk.h"
+#include "mk_internal.h"
+
+namespace mk {
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;
+constexpr int kTile = 64;
+constexpr int kWaves = 4;
+
+__device__ __forceinline__ h8 as_h8(u4 u) { return __builtin_bit_cast(h8, u); }
+__device__ __forceinline__ u4 as_u4(h8 h) { return __builtin_bit_cast(u4, h); }
+
+__device__ __forceinline__ f4 mma(u4 a, u4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a), as_h8(b), c, 0, 0, 0);
+}
+
+// x = hi + lo with hi, lo fp16.  The residual is taken from the packed hi
+// bits themselves: the compiler may round the packing conversion and a
+// separate scalar conversion of the same value differently on exact ties,
+// and a residual from the other hi would then add the wrong sign.
+__device__ __forceinline__ void split_f16(const float (&x)[8], u4& hi_out, u4& lo_out) {
+  h8 hi;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) hi[j] = (_Float16)x[j];
+  u4 hb = as_u4(hi);
+  asm volatile("" : "+v"(hb));
+  const h8 hr = as_h8(hb);
+  h8 lo;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) lo[j] = (_Float16)(x[j] - (float)hr[j]);
+  hi_out = hb;
+  lo_out = as_u4(lo);
+}
+
+template <int NB>
+__global__ __launch_bounds__(256) void k_attn_split(const AttnArgs a) {
+  __shared__ u4 qs[kWaves][NB][4][2][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int it = blockIdx.x * kWaves + w;
+  if (it >= a.n_items) return;  // the whole wave leaves; waves share nothing
+  int g = 0;
+  while (it >= a.item0[g + 1]) ++g;
+  const int loc = it - a.item0[g], ns = a.nsplit[g];
+  const int h = loc / ns, s = loc - h * ns;
+  const int r0 = a.gs[g], ng = a.gs[g + 1] - r0, ctx = a.ctx[g], Lg = ctx + ng;
+  const int p0 = s * a.chunk, p1 = min(Lg, p0 + a.chunk);
+  const int gqa = a.gqa, NQ = ng * gqa;
+  const int col = lane & 15, grp = lane >> 4;
+
+  // Query columns: scaled, split into fp16 hi + lo, parked in this lane's own
+  // LDS slots (read back every tile, so they need no registers meanwhile).
+  int lim[NB];  // positions < lim[nb] are visible to this lane's column
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int c = nb * 16 + col;
+    const bool valid = c < NQ;
+    const int row = r0 + (valid ? c / gqa : 0), hq = h * gqa + (valid ? c % gqa : 0);
+    lim[nb] = valid ? min(ctx + c / gqa + 1, p1) : 0;
+    const float* qr = a.q + ((size_t)row * a.Hq + hq) * kD + 8 * grp;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      float4 u0 = make_float4(0.f, 0.f, 0.f, 0.f), u1 = u0;
+      if (valid) {
+        u0 = *(const float4*)(qr + 32 * m);
+        u1 = *(const float4*)(qr + 32 * m + 4);
+      }
+      const float x[8] = {u0.x * a.qscale, u0.y * a.qscale, u0.z * a.qscale, u0.w * a.qscale,
+                          u1.x * a.qscale, u1.y * a.qscale, u1.z * a.qscale, u1.w * a.qscale};
+      u4 hi, lo;
+      split_f16(x, hi, lo);
+      qs[w][nb][m][0][lane] = hi;
+      qs[w][nb][m][1][lane] = lo;
+    }
+  }
+
+  const uint16_t* Kb = a.k + (size_t)(g * a.Hkv + h) * a.cap * kD;
+  const uint16_t* Vb = a.v + (size_t)(g * a.Hkv + h) * kD * a.cap;
+  f4 acc[NB][8];
+  float mrow[NB], lsum[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    mrow[nb] = -INFINITY;
+    lsum[nb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[nb][db] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Tiles start at multiples of 64 below L_g <= cap and cap % 64 == 0, so
+  // every load of a tile stays inside this head's cache rows; positions past
+  // L_g are masked (scores) or zeroed (values) below.
+  for (int t0 = p0; t0 < p1; t0 += kTile) {
+    u4 kr[4][4], vr[2][8];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int pos = t0 + 32 * (b >> 1) + 8 * (col >> 2) + 4 * (b & 1) + (col & 3);
+      const u4* src = (const u4*)(Kb + (size_t)pos * kD + 8 * grp);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) kr[b][m] = src[4 * m];
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+        vr[hh][db] = *(const u4*)(Vb + (size_t)(16 * db + col) * a.cap + t0 + 32 * hh + 8 * grp);
+    if (t0 + kTile > Lg) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          h8 v = as_h8(vr[hh][db]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (t0 + 32 * hh + 8 * grp + j >= Lg) v[j] = (_Float16)0.f;
+          vr[hh][db] = as_u4(v);
+        }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      u4 qh[4], ql[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        qh[m] = qs[w][nb][m][0][lane];
+        ql[m] = qs[w][nb][m][1][lane];
+      }
+      f4 sc[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        f4 c = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          c = mma(kr[b][m], qh[m], c);
+          c = mma(kr[b][m], ql[m], c);
+        }
+        sc[b] = c;
+      }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pos = t0 + 32 * (b >> 1) + 8 * grp + 4 * (b & 1) + i;
+          const float x = pos < lim[nb] ? sc[b][i] : -INFINITY;
+          sc[b][i] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mnew = fmaxf(mrow[nb], tmax);
+      const float muse = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = exp2f(mrow[nb] - muse);
+      mrow[nb] = mnew;
+      float ps = 0.f;
+      float pv[2][8];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = exp2f(sc[b][i] - muse);
+          ps += p;
+          pv[b >> 1][4 * (b & 1) + i] = p;
+        }
+      u4 ph[2], pl[2];
+      split_f16(pv[0], ph[0], pl[0]);
+      split_f16(pv[1], ph[1], pl[1]);
+      lsum[nb] = lsum[nb] * alpha + ps;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) acc[nb][db] *= alpha;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          acc[nb][db] = mma(vr[hh][db], ph[hh], acc[nb][db]);
+          acc[nb][db] = mma(vr[hh][db], pl[hh], acc[nb][db]);
+        }
+    }
+  }
+
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    float l = lsum[nb];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int c = nb * 16 + col;
+    if (c < NQ) {
+      const int row = r0 + c / gqa, hq = h * gqa + c % gqa;
+      const size_t base = ((size_t)row * a.Hq + hq) * a.smax + s;
+      float* po = a.part_o + base * kD + 4 * grp;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *(f4*)(po + 16 * db) = acc[nb][db];
+      if (grp == 0) *(float2*)(a.part_ml + 2 * base) = make_float2(mrow[nb], l);
+    }
+  }
+}
+
+// o[row][hq] = sum_s w_s o_s / sum_s w_s l_s with w_s = 2^(m_s - max m),
+// then the output gate.  One block of 128 threads per (row, query head).
+__global__ __launch_bounds__(128) void k_attn_combine(const AttnArgs a) {
+  const int th = blockIdx.x, row = th / a.Hq, d = threadIdx.x;
+  int g = 0;
+  while (row >= a.gs[g + 1]) ++g;
+  const int ns = a.nsplit[g];
+  const float2* ml = (const float2*)a.part_ml + (size_t)th * a.smax;
+  const float* po = a.part_o + (size_t)th * a.smax * kD + d;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[s].x);
+  float L = 0.f, y = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float2 v = ml[s];
+    const float wgt = exp2f(v.x - M);
+    L += wgt * v.y;
+    y += wgt * po[(size_t)s * kD];
+  }
+  y /= L;
+  if (a.gate) y *= 1.f / (1.f + expf(-a.gate[(size_t)th * kD + d]));
+  a.o[(size_t)th * kD + d] = y;
+}
+
+}  // namespace
+
+AttnPlan plan_attn(int G, const int32_t* ctx, const int32_t* gs, int Hkv, int cu_count) {
+  AttnPlan p = {};
+  long W = 0, Lmax = 0;
+  for (int g = 0; g < G; ++g) {
+    const long L = (long)ctx[g] + (gs[g + 1] - gs[g]);
+    W += L * Hkv;
+    Lmax = L > Lmax ? L : Lmax;
+  }
+  // Two waves per SIMD over the device, at least four tiles per item unless
+  // the contexts are short, and at most kAttnMaxSplit splits per head.
+  const long target = 8L * (cu_count > 0 ? cu_count : 256);
+  auto up64 = [](long x) { return (x + kTile - 1) / kTile * kTile; };
+  long chunk = up64((W + target - 1) / target);
+  if (chunk < 4 * kTile) chunk = 4 * kTile;
+  const long need = up64((Lmax + kAttnMaxSplit - 1) / kAttnMaxSplit);
+  if (chunk < need) chunk = need;
+  p.chunk = (int)chunk;
+  p.item0[0] = 0;
+  for (int g = 0; g < G; ++g) {
+    const long L = (long)ctx[g] + (gs[g + 1] - gs[g]);
+    p.nsplit[g] = (int)((L + chunk - 1) / chunk);
+    p.smax = p.nsplit[g] > p.smax ? p.nsplit[g] : p.smax;
+    p.item0[g + 1] = p.item0[g] + p.nsplit[g] * Hkv;
+  }
+  p.n_items = p.item0[G];
+  return p;
+}
+
+size_t attn_workspace_bytes(int T, int Hq, const AttnPlan& p) {
+  const size_t n = (size_t)T * Hq * p.smax;
+  return (n * kD * 4 + 255) / 256 * 256 + (n * 8 + 255) / 256 * 256;
+}
+
+hipError_t launch_attn(AttnArgs a, const AttnPlan& p, int nb, void* ws, hipStream_t st) {
+  const size_t n = (size_t)a.T * a.Hq * p.smax;
+  a.part_o = (float*)ws;
+  a.part_ml = (float*)((char*)ws + (n * kD * 4 + 255) / 256 * 256);
+  a.chunk = p.chunk;
+  a.smax = p.smax;
+  a.n_items = p.n_items;
+  for (int g = 0; g <= a.G; ++g) a.item0[g] = p.item0[g];
+  for (int g = 0; g < a.G; ++g) a.nsplit[g] = p.nsplit[g];
+  const dim3 grid((p.n_items + kWaves - 1) / kWaves);
+  switch (nb) {
+    case 1: k_attn_split<1><<<grid, 256, 0, st>>>(a); break;
+    case 2: k_attn_split<2><<<grid, 256, 0, st>>>(a); break;
+    case 3: k_attn_split<3><<<grid, 256, 0, st>>>(a); break;
+    case 4: k_attn_split<4><<<grid, 256, 0, st>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_attn_combine<<<a.T * a.Hq, 128, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace mk

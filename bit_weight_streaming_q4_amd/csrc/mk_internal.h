@@ -72,3 +72,29 @@ struct GdnArgs {
 hipError_t launch_gdn_step(const GdnArgs& a, hipStream_t st);
 hipError_t launch_gdn_commit(const GdnArgs& a, hipStream_t st);
 }  // namespace mk
+
+// Full-attention decode (mk_attn.hip).
+#define MK_ATTN_MAX_G 16
+namespace mk {
+constexpr int kAttnMaxSplit = 256;  // splits per (agent, KV head)
+struct AttnPlan {
+  int chunk, smax, n_items;
+  int nsplit[MK_ATTN_MAX_G], item0[MK_ATTN_MAX_G + 1];
+};
+struct AttnArgs {
+  const float* q;       // [T][Hq][128]
+  const float* gate;    // [T][Hq][128] or null
+  float* o;             // [T][Hq][128]
+  const uint16_t* k;    // [G][Hkv][cap][128]
+  const uint16_t* v;    // [G][Hkv][128][cap]
+  float* part_o;        // [T][Hq][smax][128] unnormalised split outputs
+  float* part_ml;       // [T][Hq][smax][2] split max (log2 units) and sum
+  float qscale;         // log2(e) / sqrt(128)
+  int T, Hq, Hkv, gqa, cap, G, chunk, smax, n_items;
+  int ctx[MK_ATTN_MAX_G], gs[MK_ATTN_MAX_G + 1], nsplit[MK_ATTN_MAX_G], item0[MK_ATTN_MAX_G + 1];
+};
+AttnPlan plan_attn(int G, const int32_t* ctx, const int32_t* gs, int Hkv, int cu_count);
+size_t attn_workspace_bytes(int T, int Hq, const AttnPlan& p);
+// nb = number of 16-column blocks, ceil(max group rows * Hq/Hkv / 16), 1..4.
+hipError_t launch_attn(AttnArgs a, const AttnPlan& p, int nb, void* ws, hipStream_t st);
+}  // namespace mk

@@ -233,6 +233,35 @@ float mk_decode_step_last_ms(const mk_stack* st);
 int mk_decode_step_stamps(const mk_stack* st, int32_t T, const void* ws, uint64_t* h_stamps, int32_t n_max,
                           int64_t* h_clock_hz);
 
+/* ------------------------------------------------------- full attention */
+/* Decode-time attention of the full-attention layers over an fp16 KV cache,
+ * by split-K flash decoding (richland.au, "Fusing the whole speculative-
+ * decoding cycle into one CUDA kernel", section "What shipped").  Rows are
+ * split into G agents by h_group_start as in mk_lmhead_verify; agent g has
+ * h_ctx[g] positions cached before this step, and its n_g new rows (token +
+ * drafts) have their k, v already stored at positions h_ctx[g] ..
+ * h_ctx[g] + n_g - 1.  Row i of agent g sees positions 0 .. h_ctx[g] + i
+ * (causal among the drafts).  For query head hq and its KV head
+ * h = hq / (Hq / Hkv):
+ *   o[t][hq] = sum_j softmax_j(q[t][hq] . K[g][h][j] / sqrt(d)) V[g][h][.][j],
+ * then o *= 1 / (1 + exp(-gate)) elementwise when gate is not NULL (the
+ * output gate of gated attention).
+ *   q, gate, o  [T][Hq][d] fp32 (device; gate may be NULL)
+ *   k_cache     [G][Hkv][cap][d] fp16 bits (device), position-major
+ *   v_cache     [G][Hkv][d][cap] fp16 bits (device), dimension-major
+ *   h_ctx [G], h_group_start [G+1] (host; NULL = one group of T rows)
+ * d = 128; cap % 64 == 0; h_ctx[g] + n_g <= cap; n_g * Hq/Hkv <= 64;
+ * G <= 16.  Slots past an agent's last position are never used (they may
+ * hold anything).  Two launches (split pass, merge + gate); the workspace
+ * size depends on the contexts and the device (mk_attn_decode_workspace).
+ * fp32 accumulation; the products carry about 22 bits (q and the softmax
+ * weights are split into two fp16 parts). */
+size_t mk_attn_decode_workspace(int32_t T, int32_t Hq, int32_t Hkv, const int32_t* h_ctx,
+                                const int32_t* h_group_start, int32_t G);
+int mk_attn_decode(const float* q, const float* gate, int32_t T, int32_t Hq, const uint16_t* k_cache,
+                   const uint16_t* v_cache, int32_t Hkv, int32_t d, int32_t cap, const int32_t* h_ctx,
+                   const int32_t* h_group_start, int32_t G, float* o, void* ws, size_t ws_bytes, void* stream);
+
 /* Measurement aid, not a step of the method: reads `bytes` bytes of buf
  * (device, 16-B aligned, bytes % 16 == 0) once with 16-B nontemporal loads
  * spread over the whole device, and may write one word to *sink (device, 4-B
