@@ -240,8 +240,9 @@ def kernel_bench(lm, device="cuda"):
     on rotating device copies of its weights (more bytes than the 256 MB
     Infinity Cache, so every call streams from HBM): the T-row GEMV (5120 x
     5120), the FFN block (5120 -> 17408 -> 5120, T = 5), lm_head + verify
-    (151936 x 5120 and the 32768-row draft prefix, T = 5) and the Gated
-    DeltaNet step + commit (48 x 32 heads of 128 x 128, T = 5)."""
+    (151936 x 5120 and the 32768-row draft prefix, T = 5), the Gated
+    DeltaNet step + commit (48 x 32 heads of 128 x 128, T = 5) and
+    full-attention decode over an fp16 KV cache."""
     import torch
 
     import bit_weight_streaming_q4_amd as mk
@@ -336,7 +337,35 @@ def kernel_bench(lm, device="cuda"):
     del flush
     del st
     torch.cuda.empty_cache()
+    # Full-attention decode (32 query / 8 KV heads of 128, gated, fp16 cache):
+    # 4 agents x 32768 cached positions with 3 rows each (T = 12), and one
+    # agent at 81920 positions (the long end of the fp16 cache) with T = 5.
+    # Two caches alternate, so successive calls stream from HBM.
+    for ctx, sizes in (([32768] * 4, [3] * 4), ([81920], [5])):
+        a = recipes.attn_inputs(ctx, sizes)
+        q = torch.from_numpy(a["q"]).to(device)
+        gt = torch.from_numpy(a["gate"]).to(device)
+        kc = torch.from_numpy(a["k"].view(np.int16)).to(device)
+        vc = torch.from_numpy(a["v"].view(np.int16)).to(device)
+        del a
+        caches = [(kc, vc), (kc.clone(), vc.clone())]
+        o = torch.empty_like(q)
+        T = int(sum(sizes))
+        gs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+        ws = mk.workspace(mk.mk_attn_decode_workspace(T, q.shape[1], kc.shape[1], ctx, gs), device)
+        nbytes = attn_bytes(ctx, sizes)
+        rec(f"attn_decode_{len(ctx)}x{ctx[0]}_T{T}",
+            lambda i: mk.mk_attn_decode(q, gt, *caches[i % 2], ctx, gs, o, ws=ws), 16, lambda: o, nbytes)
+        del caches, kc, vc
+        torch.cuda.empty_cache()
     return out
+
+
+def attn_bytes(ctx, sizes, Hq=32, Hkv=8, d=128) -> int:
+    """Algorithmic bytes of one attention decode call: every visible K and V
+    row once (fp16) plus q, gate and o (fp32)."""
+    kv = sum(int(c) + int(n) for c, n in zip(ctx, sizes)) * Hkv * d * 2 * 2
+    return kv + int(sum(sizes)) * Hq * d * 4 * 3
 
 
 def read_probe(device="cuda", gib=4, reps=5):

@@ -6,8 +6,10 @@
 // Work split: one wave owns one item = (agent g, KV head h, split s), the
 // positions [s*chunk, min(L_g, (s+1)*chunk)) of that agent's cache, and all
 // query columns that read KV head h: the agent's n_g rows x the Hq/Hkv query
-// heads of the group (NQ <= 16*NB columns).  A second launch merges the
-// splits of each (row, query head) and applies the output gate.
+// heads of the group (NQ <= 16*NB columns).  The four waves of a block take
+// four adjacent splits of one head and merge them through LDS into one
+// partial; a second launch merges the partials of each (row, query head)
+// and applies the output gate.
 //
 // Per 64-position tile the wave computes the transposed scores
 //   S^T[pos][col] = K[pos] . q[col]            (v_mfma_f32_16x16x32_f16)
@@ -43,6 +45,7 @@ typedef unsigned u4 __attribute__((ext_vector_type(4)));
 constexpr int kD = 128;
 constexpr int kTile = 64;
 constexpr int kWaves = 4;
+constexpr int kMergeFloats = 34;  // per lane and column block: 32 outputs, max, sum
 
 __device__ __forceinline__ h8 as_h8(u4 u) { return __builtin_bit_cast(h8, u); }
 __device__ __forceinline__ u4 as_u4(h8 h) { return __builtin_bit_cast(u4, h); }
@@ -69,12 +72,19 @@ __device__ __forceinline__ void split_f16(const float (&x)[8], u4& hi_out, u4& l
   lo_out = as_u4(lo);
 }
 
+// One column block fits two waves per SIMD (256 registers with the matrix
+// accumulators); more column blocks run one wave per SIMD.
 template <int NB>
-__global__ __launch_bounds__(256) void k_attn_split(const AttnArgs a) {
-  __shared__ u4 qs[kWaves][NB][4][2][64];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 2 : 1)))
+void k_attn_split(const AttnArgs a) {
+  // q slots [w][nb][m][hi/lo][lane] during the loop; afterwards the four
+  // waves' results [w][nb][34][lane] for the merge.
+  __shared__ float smem[kWaves * NB * kMergeFloats * 64];
+  u4* qs = (u4*)smem;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // The item count is a multiple of 4 and the grid has one block per 4 items,
+  // so no wave is idle; a block's waves take splits 4q .. 4q+3 of one head.
   const int it = blockIdx.x * kWaves + w;
-  if (it >= a.n_items) return;  // the whole wave leaves; waves share nothing
   int g = 0;
   while (it >= a.item0[g + 1]) ++g;
   const int loc = it - a.item0[g], ns = a.nsplit[g];
@@ -105,8 +115,8 @@ __global__ __launch_bounds__(256) void k_attn_split(const AttnArgs a) {
                           u1.x * a.qscale, u1.y * a.qscale, u1.z * a.qscale, u1.w * a.qscale};
       u4 hi, lo;
       split_f16(x, hi, lo);
-      qs[w][nb][m][0][lane] = hi;
-      qs[w][nb][m][1][lane] = lo;
+      qs[(((w * NB + nb) * 4 + m) * 2 + 0) * 64 + lane] = hi;
+      qs[(((w * NB + nb) * 4 + m) * 2 + 1) * 64 + lane] = lo;
     }
   }
 
@@ -156,8 +166,8 @@ __global__ __launch_bounds__(256) void k_attn_split(const AttnArgs a) {
       u4 qh[4], ql[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        qh[m] = qs[w][nb][m][0][lane];
-        ql[m] = qs[w][nb][m][1][lane];
+        qh[m] = qs[(((w * NB + nb) * 4 + m) * 2 + 0) * 64 + lane];
+        ql[m] = qs[(((w * NB + nb) * 4 + m) * 2 + 1) * 64 + lane];
       }
       f4 sc[4];
 #pragma unroll
@@ -212,44 +222,110 @@ __global__ __launch_bounds__(256) void k_attn_split(const AttnArgs a) {
     }
   }
 
+  // Merge the block's four splits: wave i's column max m_i, sums l_i and
+  // outputs weigh 2^(m_i - max m); wave w then writes dims 32w .. 32w+31 of
+  // the block's partial.  Empty splits (m = -inf) weigh zero.
+  __syncthreads();
+  float* mb = smem;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    float l = lsum[nb];
+    float* dst = mb + (w * NB + nb) * kMergeFloats * 64 + lane;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(4 * db + i) * 64] = acc[nb][db][i];
+    dst[32 * 64] = mrow[nb];
+    dst[33 * 64] = lsum[nb];
+  }
+  __syncthreads();
+  const int q4 = s >> 2;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    float mi[kWaves], M = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      mi[i] = mb[((i * NB + nb) * kMergeFloats + 32) * 64 + lane];
+      M = fmaxf(M, mi[i]);
+    }
+    const float muse = M == -INFINITY ? 0.f : M;
+    float wt[kWaves], l = 0.f;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      wt[i] = exp2f(mi[i] - muse);
+      l += wt[i] * mb[((i * NB + nb) * kMergeFloats + 33) * 64 + lane];
+    }
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
     const int c = nb * 16 + col;
     if (c < NQ) {
       const int row = r0 + c / gqa, hq = h * gqa + c % gqa;
-      const size_t base = ((size_t)row * a.Hq + hq) * a.smax + s;
+      const size_t base = ((size_t)row * a.Hq + hq) * a.smax + q4;
       float* po = a.part_o + base * kD + 4 * grp;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) *(f4*)(po + 16 * db) = acc[nb][db];
-      if (grp == 0) *(float2*)(a.part_ml + 2 * base) = make_float2(mrow[nb], l);
+      for (int k = 0; k < 2; ++k) {
+        const int db = 2 * w + k;
+        f4 v = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) {
+          const float* src = mb + ((i * NB + nb) * kMergeFloats + 4 * db) * 64 + lane;
+          v += wt[i] * f4{src[0], src[64], src[128], src[192]};
+        }
+        *(f4*)(po + 16 * db) = v;
+      }
+      if (w == 0 && grp == 0) *(float2*)(a.part_ml + 2 * base) = make_float2(M, l);
     }
   }
 }
 
-// o[row][hq] = sum_s w_s o_s / sum_s w_s l_s with w_s = 2^(m_s - max m),
-// then the output gate.  One block of 128 threads per (row, query head).
-__global__ __launch_bounds__(128) void k_attn_combine(const AttnArgs a) {
-  const int th = blockIdx.x, row = th / a.Hq, d = threadIdx.x;
+// o[row][hq] = sum_q w_q o_q / sum_q w_q l_q with w_q = 2^(m_q - max m), then
+// the output gate.  One block of 4 waves per (row, query head): wave w folds
+// partials q = w, w+4, ... with a running max, each lane two dimensions; the
+// four results merge through LDS.
+__global__ __launch_bounds__(256) void k_attn_combine(const AttnArgs a) {
+  __shared__ float red[kWaves][4][64];
+  const int th = blockIdx.x, row = th / a.Hq, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int g = 0;
   while (row >= a.gs[g + 1]) ++g;
-  const int ns = a.nsplit[g];
+  const int nq = a.nsplit[g] / kWaves;
   const float2* ml = (const float2*)a.part_ml + (size_t)th * a.smax;
-  const float* po = a.part_o + (size_t)th * a.smax * kD + d;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[s].x);
-  float L = 0.f, y = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float2 v = ml[s];
-    const float wgt = exp2f(v.x - M);
-    L += wgt * v.y;
-    y += wgt * po[(size_t)s * kD];
+  const float* po = a.part_o + (size_t)th * a.smax * kD + 2 * lane;
+  float m = -INFINITY, l = 0.f, y0 = 0.f, y1 = 0.f;
+  for (int q = w; q < nq; q += kWaves) {
+    const float2 v = ml[q];
+    const float2 o = *(const float2*)(po + (size_t)q * kD);
+    const float mn = fmaxf(m, v.x);
+    if (mn == -INFINITY) continue;
+    const float ao = exp2f(m - mn), aq = exp2f(v.x - mn);
+    l = l * ao + v.y * aq;
+    y0 = y0 * ao + o.x * aq;
+    y1 = y1 * ao + o.y * aq;
+    m = mn;
   }
-  y /= L;
-  if (a.gate) y *= 1.f / (1.f + expf(-a.gate[(size_t)th * kD + d]));
-  a.o[(size_t)th * kD + d] = y;
+  red[w][0][lane] = m;
+  red[w][1][lane] = l;
+  red[w][2][lane] = y0;
+  red[w][3][lane] = y1;
+  __syncthreads();
+  if (w != 0) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) M = fmaxf(M, red[i][0][lane]);
+  float L = 0.f, z0 = 0.f, z1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    const float wt = exp2f(red[i][0][lane] - M);
+    L += wt * red[i][1][lane];
+    z0 += wt * red[i][2][lane];
+    z1 += wt * red[i][3][lane];
+  }
+  z0 /= L;
+  z1 /= L;
+  if (a.gate) {
+    const float2 gt = *(const float2*)(a.gate + (size_t)th * kD + 2 * lane);
+    z0 *= 1.f / (1.f + expf(-gt.x));
+    z1 *= 1.f / (1.f + expf(-gt.y));
+  }
+  *(float2*)(a.o + (size_t)th * kD + 2 * lane) = make_float2(z0, z1);
 }
 
 }  // namespace
@@ -274,8 +350,8 @@ AttnPlan plan_attn(int G, const int32_t* ctx, const int32_t* gs, int Hkv, int cu
   p.item0[0] = 0;
   for (int g = 0; g < G; ++g) {
     const long L = (long)ctx[g] + (gs[g + 1] - gs[g]);
-    p.nsplit[g] = (int)((L + chunk - 1) / chunk);
-    p.smax = p.nsplit[g] > p.smax ? p.nsplit[g] : p.smax;
+    p.nsplit[g] = (int)((L + chunk - 1) / chunk + kWaves - 1) / kWaves * kWaves;
+    p.smax = p.nsplit[g] / kWaves > p.smax ? p.nsplit[g] / kWaves : p.smax;
     p.item0[g + 1] = p.item0[g] + p.nsplit[g] * Hkv;
   }
   p.n_items = p.item0[G];
@@ -296,7 +372,7 @@ hipError_t launch_attn(AttnArgs a, const AttnPlan& p, int nb, void* ws, hipStrea
   a.n_items = p.n_items;
   for (int g = 0; g <= a.G; ++g) a.item0[g] = p.item0[g];
   for (int g = 0; g < a.G; ++g) a.nsplit[g] = p.nsplit[g];
-  const dim3 grid((p.n_items + kWaves - 1) / kWaves);
+  const dim3 grid(p.n_items / kWaves);
   switch (nb) {
     case 1: k_attn_split<1><<<grid, 256, 0, st>>>(a); break;
     case 2: k_attn_split<2><<<grid, 256, 0, st>>>(a); break;
@@ -306,7 +382,7 @@ hipError_t launch_attn(AttnArgs a, const AttnPlan& p, int nb, void* ws, hipStrea
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_attn_combine<<<a.T * a.Hq, 128, 0, st>>>(a);
+  k_attn_combine<<<a.T * a.Hq, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

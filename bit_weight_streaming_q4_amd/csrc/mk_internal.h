@@ -87,8 +87,8 @@ struct AttnArgs {
   float* o;             // [T][Hq][128]
   const uint16_t* k;    // [G][Hkv][cap][128]
   const uint16_t* v;    // [G][Hkv][128][cap]
-  float* part_o;        // [T][Hq][smax][128] unnormalised split outputs
-  float* part_ml;       // [T][Hq][smax][2] split max (log2 units) and sum
+  float* part_o;        // [T][Hq][smax][128] unnormalised block outputs (4 splits each)
+  float* part_ml;       // [T][Hq][smax][2] block max (log2 units) and sum
   float qscale;         // log2(e) / sqrt(128)
   int T, Hq, Hkv, gqa, cap, G, chunk, smax, n_items;
   int ctx[MK_ATTN_MAX_G], gs[MK_ATTN_MAX_G + 1], nsplit[MK_ATTN_MAX_G], item0[MK_ATTN_MAX_G + 1];
