@@ -338,9 +338,12 @@ AttnPlan plan_attn(int G, const int32_t* ctx, const int32_t* gs, int Hkv, int cu
     W += L * Hkv;
     Lmax = L > Lmax ? L : Lmax;
   }
-  // Two waves per SIMD over the device, at least four tiles per item unless
-  // the contexts are short, and at most kAttnMaxSplit splits per head.
-  const long target = 8L * (cu_count > 0 ? cu_count : 256);
+  // About one wave per SIMD over the device (one block of four per CU), at
+  // least four tiles per item unless the contexts are short, and at most
+  // kAttnMaxSplit splits per head.  Measured on the 4 x 32768 and 81920
+  // workloads, four items per CU beat eight (the per-item set-up and merge
+  // cost more than the second wave per SIMD gains), and 16 or 32 were slower.
+  const long target = 4L * (cu_count > 0 ? cu_count : 256);
   auto up64 = [](long x) { return (x + kTile - 1) / kTile * kTile; };
   long chunk = up64((W + target - 1) / target);
   if (chunk < 4 * kTile) chunk = 4 * kTile;
