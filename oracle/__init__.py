@@ -18,13 +18,14 @@ the order the pages give them.  Each function names the step it follows:
   C7 gdn_step       gated delta rule with commit through the accepted row
   C8 decode_step    composition of one whole step
   A1 attn_decode    full-attention decode of T rows over an fp16 KV cache
+  A2 attn_decode_q8 the same over a q8_0 KV cache
 
 Pages: richland.au "Fusing the whole speculative-decoding cycle into one CUDA
 kernel" (section "What shipped"), richland.au "OpenJet's CUDA megakernel runs
 4 coding agents" (section "Why it matters"), pulse-3k2 "UPDATE: ... KL
 divergence" (section "Decode accuracy").
 
-Parity status: C1-C4, C6, C7 and A1 are pinned by tests against brute force,
+Parity status: C1-C4, C6, C7, A1 and A2 are pinned by tests against brute force,
 closed forms and library routines.  C5's glue (pre-RMSNorm, identity mixer)
 and C8's composition are readings of the pages: parity unpinned beyond the
 pinned parts they compose.
@@ -78,6 +79,7 @@ def _load():
     lib.orc_gdn_rows.argtypes = [P, i32, i32, P, P, P, P, P, i32, i64, i64, i64, P, i64, ctypes.c_int]
     lib.orc_gdn_step.argtypes = [P, i32, i32, i32, P, P, P, P, P, i32, i32, P]
     lib.orc_attn_decode.argtypes = [P, P, i32, i32, P, P, i32, i32, i32, P, P, i32, P]
+    lib.orc_attn_decode_q8.argtypes = [P, P, i32, i32, P, P, P, P, i32, i32, i32, P, P, i32, P]
     _lib = lib
     return lib
 
@@ -297,4 +299,31 @@ def attn_decode(q, gate, kc, vc, ctx, group_start=None) -> np.ndarray:
     gate = _c(gate, np.float32) if gate is not None else None
     o = np.empty((T, Hq, d), np.float32)
     _load().orc_attn_decode(_p(q), _p(gate), T, Hq, _p(kc), _p(vc), Hkv, d, cap, _p(ctx), _p(gs), G, _p(o))
+    return o
+
+
+def attn_decode_q8(q, gate, k8, ks, v8, vs, ctx, group_start=None) -> np.ndarray:
+    """A2: attention over q8_0 caches.  k8 int8 [G][Hkv][cap][d] with ks fp16
+    bits [G][Hkv][cap][d/32]; v8 int8 [G][Hkv][d][cap] with vs fp16 bits
+    [G][Hkv][cap/32][d]; otherwise as attn_decode."""
+    q = _c(q, np.float32)
+    T, Hq, d = q.shape
+    k8 = _c(k8, np.int8)
+    v8 = _c(v8, np.int8)
+    ks = _c(ks, np.uint16)
+    vs = _c(vs, np.uint16)
+    G, Hkv, cap, dk = k8.shape
+    if (dk != d or d % 32 or cap % 32 or v8.shape != (G, Hkv, d, cap) or ks.shape != (G, Hkv, cap, d // 32)
+            or vs.shape != (G, Hkv, cap // 32, d) or Hq % Hkv):
+        raise ValueError("attention q8: shape mismatch")
+    ctx = _c(np.asarray(ctx), np.int32)
+    gs = _c(np.asarray([0, T] if group_start is None else group_start), np.int32)
+    if len(ctx) != G or len(gs) != G + 1 or gs[0] != 0 or gs[-1] != T or np.any(np.diff(gs) <= 0):
+        raise ValueError("attention q8: bad groups")
+    if np.any(ctx < 0) or np.any(ctx + np.diff(gs) > cap):
+        raise ValueError("attention q8: context exceeds the cache")
+    gate = _c(gate, np.float32) if gate is not None else None
+    o = np.empty((T, Hq, d), np.float32)
+    _load().orc_attn_decode_q8(_p(q), _p(gate), T, Hq, _p(k8), _p(ks), _p(v8), _p(vs), Hkv, d, cap, _p(ctx),
+                               _p(gs), G, _p(o))
     return o

@@ -365,11 +365,60 @@ void orc_gdn_step(float* S, int32_t nh, int32_t dk, int32_t dv, const float* q, 
  * [G][Hkv][d][cap] fp16 bits (V stored dimension-major); ctx [G];
  * gs [G+1] group starts.  Every accumulation is in double, the output is
  * rounded once to fp32. */
+/* K and V element readers: fp16 caches, or q8_0 caches (blocks of 32 int8
+ * codes with one fp16 scale; value = f32(scale) * code, exact in double). */
+typedef struct {
+  const uint16_t *kc, *vc;        /* fp16: [G][Hkv][cap][d], [G][Hkv][d][cap] */
+  const int8_t *k8, *v8;          /* q8_0 codes, same layouts */
+  const uint16_t *ks, *vs;        /* q8_0 scales: [G][Hkv][cap][d/32], [G][Hkv][cap/32][d] */
+  const float* f16;               /* fp16 bit pattern -> value */
+  int64_t cap, d;
+} kv_src;
+
+static double k_at(const kv_src* c, int64_t gh, int64_t j, int k) {
+  if (c->kc) return (double)c->f16[c->kc[(gh * c->cap + j) * c->d + k]];
+  return (double)c->f16[c->ks[(gh * c->cap + j) * (c->d / 32) + k / 32]] * (double)c->k8[(gh * c->cap + j) * c->d + k];
+}
+
+static double v_at(const kv_src* c, int64_t gh, int64_t j, int k) {
+  if (c->vc) return (double)c->f16[c->vc[(gh * c->d + k) * c->cap + j]];
+  return (double)c->f16[c->vs[(gh * (c->cap / 32) + j / 32) * c->d + k]] * (double)c->v8[(gh * c->d + k) * c->cap + j];
+}
+
+static void attn_rows(const float* q, const float* gate, int32_t T, int32_t Hq, const kv_src* c, int32_t Hkv,
+                      const int32_t* ctx, const int32_t* gs, float* o);
+
 void orc_attn_decode(const float* q, const float* gate, int32_t T, int32_t Hq, const uint16_t* kc,
                      const uint16_t* vc, int32_t Hkv, int32_t d, int32_t cap, const int32_t* ctx,
                      const int32_t* gs, int32_t G, float* o) {
   float* f16 = (float*)malloc(sizeof(float) * 65536);
   for (int b = 0; b < 65536; ++b) f16[b] = orc_f16_to_f32((uint16_t)b);
+  kv_src c = {kc, vc, NULL, NULL, NULL, NULL, f16, cap, d};
+  (void)G;
+  attn_rows(q, gate, T, Hq, &c, Hkv, ctx, gs, o);
+  free(f16);
+}
+
+/* The same attention over q8_0 caches (the pages keep the KV cache in q8_0
+ * above about 80K positions; richland.au, "Fusing the whole speculative-
+ * decoding cycle into one CUDA kernel", section "What shipped").  k8 [G][Hkv]
+ * [cap][d] with ks [G][Hkv][cap][d/32] (scale of dims 32i..32i+31 of a
+ * position); v8 [G][Hkv][d][cap] with vs [G][Hkv][cap/32][d] (scale of
+ * positions 32i..32i+31 of a dimension).  d % 32 == 0, cap % 32 == 0. */
+void orc_attn_decode_q8(const float* q, const float* gate, int32_t T, int32_t Hq, const int8_t* k8,
+                        const uint16_t* ks, const int8_t* v8, const uint16_t* vs, int32_t Hkv, int32_t d,
+                        int32_t cap, const int32_t* ctx, const int32_t* gs, int32_t G, float* o) {
+  float* f16 = (float*)malloc(sizeof(float) * 65536);
+  for (int b = 0; b < 65536; ++b) f16[b] = orc_f16_to_f32((uint16_t)b);
+  kv_src c = {NULL, NULL, k8, v8, ks, vs, f16, cap, d};
+  (void)G;
+  attn_rows(q, gate, T, Hq, &c, Hkv, ctx, gs, o);
+  free(f16);
+}
+
+static void attn_rows(const float* q, const float* gate, int32_t T, int32_t Hq, const kv_src* c, int32_t Hkv,
+                      const int32_t* ctx, const int32_t* gs, float* o) {
+  const int d = (int)c->d;
   const int gqa = Hq / Hkv;
   const double inv_sqrt_d = 1.0 / sqrt((double)d);
 #pragma omp parallel
@@ -383,9 +432,7 @@ void orc_attn_decode(const float* q, const float* gate, int32_t T, int32_t Hq, c
       int g = 0;
       while (!(gs[g] <= t && t < gs[g + 1])) ++g;
       const int64_t n = (int64_t)ctx[g] + (t - gs[g]) + 1;
-      const int h = hq / gqa;
-      const uint16_t* K = kc + ((int64_t)g * Hkv + h) * cap * d;
-      const uint16_t* V = vc + ((int64_t)g * Hkv + h) * d * cap;
+      const int64_t gh = (int64_t)g * Hkv + hq / gqa;
       const float* qr = q + th * d;
       if (n > s_cap) {
         free(s);
@@ -395,7 +442,7 @@ void orc_attn_decode(const float* q, const float* gate, int32_t T, int32_t Hq, c
       double mx = -INFINITY;
       for (int64_t j = 0; j < n; ++j) {
         double dot = 0.0;
-        for (int k = 0; k < d; ++k) dot += (double)qr[k] * (double)f16[K[j * d + k]];
+        for (int k = 0; k < d; ++k) dot += (double)qr[k] * k_at(c, gh, j, k);
         s[j] = dot * inv_sqrt_d;
         if (s[j] > mx) mx = s[j];
       }
@@ -406,7 +453,7 @@ void orc_attn_decode(const float* q, const float* gate, int32_t T, int32_t Hq, c
       }
       for (int k = 0; k < d; ++k) {
         double a = 0.0;
-        for (int64_t j = 0; j < n; ++j) a += s[j] * (double)f16[V[(int64_t)k * cap + j]];
+        for (int64_t j = 0; j < n; ++j) a += s[j] * v_at(c, gh, j, k);
         acc[k] = a / den;
       }
       for (int k = 0; k < d; ++k) {
@@ -418,5 +465,4 @@ void orc_attn_decode(const float* q, const float* gate, int32_t T, int32_t Hq, c
     free(acc);
     free(s);
   }
-  free(f16);
 }

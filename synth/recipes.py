@@ -169,3 +169,36 @@ def attn_inputs(ctx, sizes, Hq=ATTN_Q_HEADS, Hkv=ATTN_KV_HEADS, d=ATTN_D, cap=No
     gt = normal_f32(seed, 400 + layer, 0, T * Hq * d).reshape(T, Hq, d) if gate else None
     gs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
     return {"q": q, "gate": gt, "k": kc, "v": vc, "ctx": np.asarray(ctx, np.int32), "group_start": gs}
+
+
+def attn_inputs_q8(ctx, sizes, Hq=ATTN_Q_HEADS, Hkv=ATTN_KV_HEADS, d=ATTN_D, cap=None, seed=ATTN_SEED, layer=0,
+                   gate=True, fill_scale=F16_NAN):
+    """The same workload over q8_0 caches: codes uniform in -127..127 and
+    fp16 scales |N(0, 0.01)| (values of about the fp16 cache's spread).
+    K codes [G][Hkv][cap][d] with scales [G][Hkv][cap][d/32]; V codes
+    [G][Hkv][d][cap] with scales [G][Hkv][cap/32][d].  Codes past an agent's
+    last position are 0x80 (-128, outside the codes' range) and scales of
+    slots or blocks holding no position are ``fill_scale`` (a NaN)."""
+    G = len(ctx)
+    if cap is None:
+        cap = attn_cap(ctx, sizes)
+    nb = d // 32
+    k8 = np.full((G, Hkv, cap, d), -128, np.int8)
+    v8 = np.full((G, Hkv, d, cap), -128, np.int8)
+    ks = np.full((G, Hkv, cap, nb), fill_scale, np.uint16)
+    vs = np.full((G, Hkv, cap // 32, d), fill_scale, np.uint16)
+    for g in range(G):
+        n = int(ctx[g]) + int(sizes[g])
+        nblk = (n + 31) // 32
+        for h in range(Hkv):
+            sub = g * Hkv + h
+            k8[g, h, :n, :] = uniform_i32(seed, 500 + layer, sub, n * d, -127, 127).reshape(n, d)
+            v8[g, h, :, :n] = uniform_i32(seed, 600 + layer, sub, n * d, -127, 127).reshape(n, d).T
+            ks[g, h, :n, :] = normal_f16(seed, 700 + layer, sub, n * nb, 0.0, 0.01, absval=True).reshape(n, nb)
+            vs[g, h, :nblk, :] = normal_f16(seed, 800 + layer, sub, nblk * d, 0.0, 0.01, absval=True).reshape(nblk, d)
+    T = int(sum(sizes))
+    q = normal_f32(seed, 300 + layer, 0, T * Hq * d).reshape(T, Hq, d)
+    gt = normal_f32(seed, 400 + layer, 0, T * Hq * d).reshape(T, Hq, d) if gate else None
+    gs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    return {"q": q, "gate": gt, "k8": k8, "ks": ks, "v8": v8, "vs": vs, "ctx": np.asarray(ctx, np.int32),
+            "group_start": gs}

@@ -525,3 +525,28 @@ def test_attn_large_scores_stay_finite(orc):
             t = a["group_start"][g] + i
             for hq in range(4):
                 np.testing.assert_allclose(o[t, hq], Vf[g, hq // 2, :, :n].mean(axis=1), rtol=1e-6, atol=1e-7)
+
+
+def test_attn_q8_equals_fp16_path_on_exact_values(orc):
+    """A2 against the pinned A1: with power-of-two scales every scale * code is
+    an exact fp16 value, so the q8_0 result must equal, bit for bit, the fp16
+    result on the dequantized caches.  Scales differ per (position, 32-dim
+    block) for K and per (32-position block, dimension) for V, which pins
+    which values each scale multiplies."""
+    a = recipes.attn_inputs_q8([45, 7], [2, 3], Hq=4, Hkv=2, d=64, gate=True, seed=13)
+    G, Hkv, cap, d = a["k8"].shape
+    e_k = synth.uniform_i32(13, 1, 0, G * Hkv * cap * (d // 32), -4, 3).reshape(G, Hkv, cap, d // 32)
+    e_v = synth.uniform_i32(13, 2, 0, G * Hkv * (cap // 32) * d, -4, 3).reshape(G, Hkv, cap // 32, d)
+    a["ks"] = np.vectorize(lambda e: synth.f64_to_f16_bits(2.0 ** e))(e_k).astype(np.uint16)
+    a["vs"] = np.vectorize(lambda e: synth.f64_to_f16_bits(2.0 ** e))(e_v).astype(np.uint16)
+    k8 = a["k8"].astype(np.float64)
+    v8 = a["v8"].astype(np.float64)
+    kval = k8 * np.repeat(2.0 ** e_k, 32, axis=3)
+    vval = v8 * np.transpose(np.repeat(2.0 ** e_v, 32, axis=2), (0, 1, 3, 2))
+    to16 = np.vectorize(synth.f64_to_f16_bits)
+    k16 = to16(kval).astype(np.uint16)
+    v16 = to16(vval).astype(np.uint16)
+    assert np.array_equal(_f16(k16), kval) and np.array_equal(_f16(v16), vval)
+    o8 = orc.attn_decode_q8(a["q"], a["gate"], a["k8"], a["ks"], a["v8"], a["vs"], a["ctx"], a["group_start"])
+    o16 = orc.attn_decode(a["q"], a["gate"], k16, v16, a["ctx"], a["group_start"])
+    assert np.array_equal(o8, o16)
