@@ -92,6 +92,7 @@ def lib():
     L.mk_attn_decode_workspace.argtypes = [i32, i32, i32, P, P, i32]
     L.mk_attn_decode_workspace.restype = sz
     L.mk_attn_decode.argtypes = [P, P, i32, i32, P, P, i32, i32, i32, P, P, i32, P, P, sz, P]
+    L.mk_attn_decode_q8.argtypes = [P, P, i32, i32, P, P, P, P, i32, i32, i32, P, P, i32, P, P, sz, P]
     _lib = L
     return L
 
@@ -257,6 +258,20 @@ def mk_attn_decode(q, gate, k_cache, v_cache, ctx, group_start, o, ws=None, stre
     _check(lib().mk_attn_decode(_ptr(q), _ptr(gate), T, Hq, _ptr(k_cache), _ptr(v_cache), Hkv, d, cap,
                                 ctx_np.ctypes.data, gs_np.ctypes.data, G, _ptr(o), _ptr(ws), ws.numel(),
                                 _stream(stream)), "mk_attn_decode")
+
+
+def mk_attn_decode_q8(q, gate, k_codes, k_scales, v_codes, v_scales, ctx, group_start, o, ws=None, stream=None):
+    """As mk_attn_decode over q8_0 caches: k_codes int8 [G][Hkv][cap][128] with
+    k_scales fp16 bits [G][Hkv][cap][4]; v_codes int8 [G][Hkv][128][cap] with
+    v_scales [G][Hkv][cap/32][128]."""
+    T, Hq, d = q.shape
+    G_, Hkv, cap, _ = k_codes.shape
+    ctx_np, gs_np, G = _attn_groups(T, ctx, group_start)
+    if ws is None:
+        ws = workspace(max(mk_attn_decode_workspace(T, Hq, Hkv, ctx_np, gs_np), 256), q.device)
+    _check(lib().mk_attn_decode_q8(_ptr(q), _ptr(gate), T, Hq, _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
+                                   _ptr(v_scales), Hkv, d, cap, ctx_np.ctypes.data, gs_np.ctypes.data, G, _ptr(o),
+                                   _ptr(ws), ws.numel(), _stream(stream)), "mk_attn_decode_q8")
 
 
 class DeltaNetState:

@@ -451,21 +451,30 @@ size_t mk_attn_decode_workspace(int32_t T, int32_t Hq, int32_t Hkv, const int32_
                                 const int32_t* h_group_start, int32_t G) {
   std::vector<int32_t> gs;
   if (check_attn(T, Hq, Hkv, 128, 1 << 30, h_ctx, h_group_start, G, gs)) return 0;
-  const mk::AttnPlan p = mk::plan_attn(G, h_ctx, gs.data(), Hkv, device_cu_count());
-  return mk::attn_workspace_bytes(T, Hq, p);
+  // the larger of the two cache formats' plans, so one size serves both
+  const mk::AttnPlan p16 = mk::plan_attn(G, h_ctx, gs.data(), Hkv, device_cu_count(), false);
+  const mk::AttnPlan p8 = mk::plan_attn(G, h_ctx, gs.data(), Hkv, device_cu_count(), true);
+  return std::max(mk::attn_workspace_bytes(T, Hq, p16), mk::attn_workspace_bytes(T, Hq, p8));
 }
 
-int mk_attn_decode(const float* q, const float* gate, int32_t T, int32_t Hq, const uint16_t* k_cache,
-                   const uint16_t* v_cache, int32_t Hkv, int32_t d, int32_t cap, const int32_t* h_ctx,
-                   const int32_t* h_group_start, int32_t G, float* o, void* ws, size_t ws_bytes, void* stream) {
+static int attn_call(const float* q, const float* gate, int32_t T, int32_t Hq, const uint16_t* k_cache,
+                     const uint16_t* v_cache, const int8_t* k_codes, const uint16_t* k_scales, const int8_t* v_codes,
+                     const uint16_t* v_scales, int32_t Hkv, int32_t d, int32_t cap, const int32_t* h_ctx,
+                     const int32_t* h_group_start, int32_t G, float* o, void* ws, size_t ws_bytes, void* stream) {
   int r;
   std::vector<int32_t> gs;
   if ((r = check_attn(T, Hq, Hkv, d, cap, h_ctx, h_group_start, G, gs))) return r;
-  if ((r = check_ptr(q, "q")) || (r = check_ptr(k_cache, "k_cache")) || (r = check_ptr(v_cache, "v_cache")) ||
-      (r = check_ptr(o, "o")))
+  const bool q8 = k_codes || v_codes;
+  if ((r = check_ptr(q, "q")) || (r = check_ptr(o, "o"))) return r;
+  if (q8) {
+    if ((r = check_ptr(k_codes, "k_codes")) || (r = check_ptr(k_scales, "k_scales")) ||
+        (r = check_ptr(v_codes, "v_codes")) || (r = check_ptr(v_scales, "v_scales")))
+      return r;
+  } else if ((r = check_ptr(k_cache, "k_cache")) || (r = check_ptr(v_cache, "v_cache"))) {
     return r;
+  }
   if (gate && !aligned(gate, 16)) return fail(MK_ERR_ALIGN, "gate not 16-B aligned");
-  const mk::AttnPlan p = mk::plan_attn(G, h_ctx, gs.data(), Hkv, device_cu_count());
+  const mk::AttnPlan p = mk::plan_attn(G, h_ctx, gs.data(), Hkv, device_cu_count(), q8);
   const size_t need = mk::attn_workspace_bytes(T, Hq, p);
   if (!ws || ws_bytes < need) return fail(MK_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   if ((r = check_ptr(ws, "workspace", 256))) return r;
@@ -475,6 +484,10 @@ int mk_attn_decode(const float* q, const float* gate, int32_t T, int32_t Hq, con
   a.o = o;
   a.k = k_cache;
   a.v = v_cache;
+  a.k8 = k_codes;
+  a.v8 = v_codes;
+  a.ks = k_scales;
+  a.vs = v_scales;
   a.qscale = (float)(1.4426950408889634 / sqrt(128.0));
   a.T = T;
   a.Hq = Hq;
@@ -489,7 +502,23 @@ int mk_attn_decode(const float* q, const float* gate, int32_t T, int32_t Hq, con
   }
   for (int g = 0; g <= G; ++g) a.gs[g] = gs[g];
   const int nb = (nmax * a.gqa + 15) / 16;
-  return launch_status(mk::launch_attn(a, p, nb, ws, S(stream)), "attention");
+  return launch_status(mk::launch_attn(a, p, nb, q8, ws, S(stream)), "attention");
+}
+
+int mk_attn_decode(const float* q, const float* gate, int32_t T, int32_t Hq, const uint16_t* k_cache,
+                   const uint16_t* v_cache, int32_t Hkv, int32_t d, int32_t cap, const int32_t* h_ctx,
+                   const int32_t* h_group_start, int32_t G, float* o, void* ws, size_t ws_bytes, void* stream) {
+  return attn_call(q, gate, T, Hq, k_cache, v_cache, nullptr, nullptr, nullptr, nullptr, Hkv, d, cap, h_ctx,
+                   h_group_start, G, o, ws, ws_bytes, stream);
+}
+
+int mk_attn_decode_q8(const float* q, const float* gate, int32_t T, int32_t Hq, const int8_t* k_codes,
+                      const uint16_t* k_scales, const int8_t* v_codes, const uint16_t* v_scales, int32_t Hkv,
+                      int32_t d, int32_t cap, const int32_t* h_ctx, const int32_t* h_group_start, int32_t G,
+                      float* o, void* ws, size_t ws_bytes, void* stream) {
+  if (!k_codes || !v_codes) return fail(MK_ERR_ARG, "attention q8: null codes");
+  return attn_call(q, gate, T, Hq, nullptr, nullptr, k_codes, k_scales, v_codes, v_scales, Hkv, d, cap, h_ctx,
+                   h_group_start, G, o, ws, ws_bytes, stream);
 }
 
 int mk_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

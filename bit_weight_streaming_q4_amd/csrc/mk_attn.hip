@@ -74,7 +74,30 @@ __device__ __forceinline__ void split_f16(const float (&x)[8], u4& hi_out, u4& l
 
 // One column block fits two waves per SIMD (256 registers with the matrix
 // accumulators); more column blocks run one wave per SIMD.
-template <int NB>
+// Eight q8_0 codes (two dwords of int8) -> eight fp16 values, exactly: each
+// byte, sign-flipped to c + 128, becomes the low byte of the fp16 1024 + c + 128
+// (exponent byte 0x64), and 1152 is subtracted in packed fp16.
+// The empty asm keeps each conversion at its use: with several column
+// blocks the compiler would otherwise hold every converted operand of the
+// tile at once and spill.
+__device__ __forceinline__ u4 codes_f16(uint2 c) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  asm volatile("" : "+v"(c));
+  const unsigned x0 = c.x ^ 0x80808080u, x1 = c.y ^ 0x80808080u;
+  const h2 off = {(_Float16)1152.f, (_Float16)1152.f};
+  u4 r;
+  r[0] = __builtin_bit_cast(unsigned, __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u)) - off);
+  r[1] = __builtin_bit_cast(unsigned, __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u)) - off);
+  r[2] = __builtin_bit_cast(unsigned, __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u)) - off);
+  r[3] = __builtin_bit_cast(unsigned, __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u)) - off);
+  return r;
+}
+
+// Q8: the cache holds q8_0 blocks (32 int8 codes, one fp16 scale).  Each score
+// product m covers exactly the 32-dim block m of a K row, and each P.V
+// product exactly one 32-position block of a V row, so a product runs on the
+// codes (exact in fp16) and its result is scaled per row in fp32.
+template <int NB, bool Q8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 2 : 1)))
 void k_attn_split(const AttnArgs a) {
   // q slots [w][nb][m][hi/lo][lane] during the loop; afterwards the four
@@ -120,8 +143,13 @@ void k_attn_split(const AttnArgs a) {
     }
   }
 
-  const uint16_t* Kb = a.k + (size_t)(g * a.Hkv + h) * a.cap * kD;
-  const uint16_t* Vb = a.v + (size_t)(g * a.Hkv + h) * kD * a.cap;
+  const size_t gh = (size_t)g * a.Hkv + h;
+  const uint16_t* Kb = a.k + gh * a.cap * kD;
+  const uint16_t* Vb = a.v + gh * kD * a.cap;
+  const int8_t* K8 = a.k8 + gh * a.cap * kD;
+  const int8_t* V8 = a.v8 + gh * kD * a.cap;
+  const uint16_t* KS = a.ks + gh * a.cap * (kD / 32);
+  const uint16_t* VS = a.vs + gh * (a.cap / 32) * kD;
   f4 acc[NB][8];
   float mrow[NB], lsum[NB];
 #pragma unroll
@@ -136,31 +164,60 @@ void k_attn_split(const AttnArgs a) {
   // every load of a tile stays inside this head's cache rows; positions past
   // L_g are masked (scores) or zeroed (values) below.
   for (int t0 = p0; t0 < p1; t0 += kTile) {
-    u4 kr[4][4], vr[2][8];
+    u4 kr[4][4], vr[2][8];        // fp16 operands
+    uint2 k8[4][4], v8[2][8];     // Q8: codes
+    u4 ksc[4][2];                 // Q8: K scales [b][row i / 2] -> halves (i % 2) * 4 + m
+    uint2 vsc[2][8];              // Q8: V scales of dims 16db + 4grp .. +3, block t0/32 + hh
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int pos = t0 + 32 * (b >> 1) + 8 * (col >> 2) + 4 * (b & 1) + (col & 3);
-      const u4* src = (const u4*)(Kb + (size_t)pos * kD + 8 * grp);
+      if constexpr (Q8) {
+        const uint2* src = (const uint2*)(K8 + (size_t)pos * kD + 8 * grp);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) kr[b][m] = src[4 * m];
+        for (int m = 0; m < 4; ++m) k8[b][m] = src[4 * m];
+        const u4* ss = (const u4*)(KS + (size_t)(t0 + 32 * (b >> 1) + 8 * grp + 4 * (b & 1)) * (kD / 32));
+        ksc[b][0] = ss[0];
+        ksc[b][1] = ss[1];
+      } else {
+        const u4* src = (const u4*)(Kb + (size_t)pos * kD + 8 * grp);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) kr[b][m] = src[4 * m];
+      }
     }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
-        vr[hh][db] = *(const u4*)(Vb + (size_t)(16 * db + col) * a.cap + t0 + 32 * hh + 8 * grp);
-    if (t0 + kTile > Lg) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          h8 v = as_h8(vr[hh][db]);
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (t0 + 32 * hh + 8 * grp + j >= Lg) v[j] = (_Float16)0.f;
-          vr[hh][db] = as_u4(v);
+      for (int db = 0; db < 8; ++db) {
+        if constexpr (Q8) {
+          v8[hh][db] = *(const uint2*)(V8 + (size_t)(16 * db + col) * a.cap + t0 + 32 * hh + 8 * grp);
+          vsc[hh][db] = *(const uint2*)(VS + (size_t)((t0 >> 5) + hh) * kD + 16 * db + 4 * grp);
+        } else {
+          vr[hh][db] = *(const u4*)(Vb + (size_t)(16 * db + col) * a.cap + t0 + 32 * hh + 8 * grp);
         }
+      }
+    auto zero_tail = [&](int hh, u4 r) -> u4 {  // V positions past L_g contribute nothing
+      h8 v = as_h8(r);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (t0 + 32 * hh + 8 * grp + j >= Lg) v[j] = (_Float16)0.f;
+      return as_u4(v);
+    };
+    if constexpr (!Q8) {
+      if (t0 + kTile > Lg) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int db = 0; db < 8; ++db) vr[hh][db] = zero_tail(hh, vr[hh][db]);
+      }
     }
+    auto v_operand = [&](int hh, int db) -> u4 {
+      if constexpr (Q8) {
+        const u4 r = codes_f16(v8[hh][db]);
+        return t0 + kTile > Lg ? zero_tail(hh, r) : r;
+      } else {
+        return vr[hh][db];
+      }
+    };
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       u4 qh[4], ql[4];
@@ -175,8 +232,16 @@ void k_attn_split(const AttnArgs a) {
         f4 c = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          c = mma(kr[b][m], qh[m], c);
-          c = mma(kr[b][m], ql[m], c);
+          if constexpr (Q8) {
+            const u4 kf = codes_f16(k8[b][m]);
+            f4 t = mma(kf, qh[m], f4{0.f, 0.f, 0.f, 0.f});
+            t = mma(kf, ql[m], t);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) c[i] += (float)as_h8(ksc[b][i >> 1])[(i & 1) * 4 + m] * t[i];
+          } else {
+            c = mma(kr[b][m], qh[m], c);
+            c = mma(kr[b][m], ql[m], c);
+          }
         }
         sc[b] = c;
       }
@@ -216,8 +281,20 @@ void k_attn_split(const AttnArgs a) {
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-          acc[nb][db] = mma(vr[hh][db], ph[hh], acc[nb][db]);
-          acc[nb][db] = mma(vr[hh][db], pl[hh], acc[nb][db]);
+          const u4 vo = v_operand(hh, db);
+          if constexpr (Q8) {
+            f4 t = mma(vo, ph[hh], f4{0.f, 0.f, 0.f, 0.f});
+            t = mma(vo, pl[hh], t);
+            // a block holding no position of this agent may carry any scale
+            const bool live = t0 + 32 * hh < Lg;
+            const uint2 sv = vsc[hh][db];
+            const h8 s8 = as_h8(u4{sv.x, sv.y, 0u, 0u});
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[nb][db][i] += (live ? (float)s8[i] : 0.f) * t[i];
+          } else {
+            acc[nb][db] = mma(vo, ph[hh], acc[nb][db]);
+            acc[nb][db] = mma(vo, pl[hh], acc[nb][db]);
+          }
         }
     }
   }
@@ -330,7 +407,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(const AttnArgs a) {
 
 }  // namespace
 
-AttnPlan plan_attn(int G, const int32_t* ctx, const int32_t* gs, int Hkv, int cu_count) {
+AttnPlan plan_attn(int G, const int32_t* ctx, const int32_t* gs, int Hkv, int cu_count, bool q8) {
   AttnPlan p = {};
   long W = 0, Lmax = 0;
   for (int g = 0; g < G; ++g) {
@@ -338,12 +415,15 @@ AttnPlan plan_attn(int G, const int32_t* ctx, const int32_t* gs, int Hkv, int cu
     W += L * Hkv;
     Lmax = L > Lmax ? L : Lmax;
   }
-  // About one wave per SIMD over the device (one block of four per CU), at
-  // least four tiles per item unless the contexts are short, and at most
-  // kAttnMaxSplit splits per head.  Measured on the 4 x 32768 and 81920
-  // workloads, four items per CU beat eight (the per-item set-up and merge
-  // cost more than the second wave per SIMD gains), and 16 or 32 were slower.
-  const long target = 4L * (cu_count > 0 ? cu_count : 256);
+  // fp16 caches: about one wave per SIMD over the device (one block of four
+  // per CU), at least four tiles per item unless the contexts are short, and
+  // at most kAttnMaxSplit splits per head.  Measured on the 4 x 32768 and
+  // 81920 workloads, four items per CU beat eight (the per-item set-up and
+  // merge cost more than the second wave per SIMD gains), and 16 or 32 were
+  // slower.  q8_0 caches carry half the bytes per position and more
+  // arithmetic per byte, and take eight items per CU so that a second wave
+  // per SIMD covers each wave's latency.
+  const long target = (q8 ? 8L : 4L) * (cu_count > 0 ? cu_count : 256);
   auto up64 = [](long x) { return (x + kTile - 1) / kTile * kTile; };
   long chunk = up64((W + target - 1) / target);
   if (chunk < 4 * kTile) chunk = 4 * kTile;
@@ -366,7 +446,7 @@ size_t attn_workspace_bytes(int T, int Hq, const AttnPlan& p) {
   return (n * kD * 4 + 255) / 256 * 256 + (n * 8 + 255) / 256 * 256;
 }
 
-hipError_t launch_attn(AttnArgs a, const AttnPlan& p, int nb, void* ws, hipStream_t st) {
+hipError_t launch_attn(AttnArgs a, const AttnPlan& p, int nb, bool q8, void* ws, hipStream_t st) {
   const size_t n = (size_t)a.T * a.Hq * p.smax;
   a.part_o = (float*)ws;
   a.part_ml = (float*)((char*)ws + (n * kD * 4 + 255) / 256 * 256);
@@ -376,11 +456,15 @@ hipError_t launch_attn(AttnArgs a, const AttnPlan& p, int nb, void* ws, hipStrea
   for (int g = 0; g <= a.G; ++g) a.item0[g] = p.item0[g];
   for (int g = 0; g < a.G; ++g) a.nsplit[g] = p.nsplit[g];
   const dim3 grid(p.n_items / kWaves);
-  switch (nb) {
-    case 1: k_attn_split<1><<<grid, 256, 0, st>>>(a); break;
-    case 2: k_attn_split<2><<<grid, 256, 0, st>>>(a); break;
-    case 3: k_attn_split<3><<<grid, 256, 0, st>>>(a); break;
-    case 4: k_attn_split<4><<<grid, 256, 0, st>>>(a); break;
+  switch (nb * 2 + (q8 ? 1 : 0)) {
+    case 2: k_attn_split<1, false><<<grid, 256, 0, st>>>(a); break;
+    case 3: k_attn_split<1, true><<<grid, 256, 0, st>>>(a); break;
+    case 4: k_attn_split<2, false><<<grid, 256, 0, st>>>(a); break;
+    case 5: k_attn_split<2, true><<<grid, 256, 0, st>>>(a); break;
+    case 6: k_attn_split<3, false><<<grid, 256, 0, st>>>(a); break;
+    case 7: k_attn_split<3, true><<<grid, 256, 0, st>>>(a); break;
+    case 8: k_attn_split<4, false><<<grid, 256, 0, st>>>(a); break;
+    case 9: k_attn_split<4, true><<<grid, 256, 0, st>>>(a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();

@@ -87,14 +87,19 @@ struct AttnArgs {
   float* o;             // [T][Hq][128]
   const uint16_t* k;    // [G][Hkv][cap][128]
   const uint16_t* v;    // [G][Hkv][128][cap]
+  const int8_t* k8;     // q8_0 cache: K codes [G][Hkv][cap][128]
+  const int8_t* v8;     //             V codes [G][Hkv][128][cap]
+  const uint16_t* ks;   //             K scales [G][Hkv][cap][4]
+  const uint16_t* vs;   //             V scales [G][Hkv][cap/32][128]
   float* part_o;        // [T][Hq][smax][128] unnormalised block outputs (4 splits each)
   float* part_ml;       // [T][Hq][smax][2] block max (log2 units) and sum
   float qscale;         // log2(e) / sqrt(128)
   int T, Hq, Hkv, gqa, cap, G, chunk, smax, n_items;
   int ctx[MK_ATTN_MAX_G], gs[MK_ATTN_MAX_G + 1], nsplit[MK_ATTN_MAX_G], item0[MK_ATTN_MAX_G + 1];
 };
-AttnPlan plan_attn(int G, const int32_t* ctx, const int32_t* gs, int Hkv, int cu_count);
+AttnPlan plan_attn(int G, const int32_t* ctx, const int32_t* gs, int Hkv, int cu_count, bool q8);
 size_t attn_workspace_bytes(int T, int Hq, const AttnPlan& p);
 // nb = number of 16-column blocks, ceil(max group rows * Hq/Hkv / 16), 1..4.
-hipError_t launch_attn(AttnArgs a, const AttnPlan& p, int nb, void* ws, hipStream_t st);
+// q8 selects the q8_0 cache pointers (k8, v8, ks, vs) instead of k, v.
+hipError_t launch_attn(AttnArgs a, const AttnPlan& p, int nb, bool q8, void* ws, hipStream_t st);
 }  // namespace mk

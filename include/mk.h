@@ -262,6 +262,21 @@ int mk_attn_decode(const float* q, const float* gate, int32_t T, int32_t Hq, con
                    const uint16_t* v_cache, int32_t Hkv, int32_t d, int32_t cap, const int32_t* h_ctx,
                    const int32_t* h_group_start, int32_t G, float* o, void* ws, size_t ws_bytes, void* stream);
 
+/* The same attention over a q8_0 KV cache (the pages switch the cache to
+ * q8_0 above about 80K positions; same page and section).  A q8_0 block is
+ * 32 int8 codes with one fp16 scale; a value is f32(scale) * code.
+ *   k_codes  [G][Hkv][cap][d] int8, position-major
+ *   k_scales [G][Hkv][cap][d/32] fp16 bits: scale of dims 32i..32i+31 of a position
+ *   v_codes  [G][Hkv][d][cap] int8, dimension-major
+ *   v_scales [G][Hkv][cap/32][d] fp16 bits: scale of positions 32i..32i+31 of a dimension
+ * All device, 16-B aligned.  Every other argument, the workspace (the same
+ * mk_attn_decode_workspace) and the errors are those of mk_attn_decode.
+ * Scales of blocks that hold no visible position are never used. */
+int mk_attn_decode_q8(const float* q, const float* gate, int32_t T, int32_t Hq, const int8_t* k_codes,
+                      const uint16_t* k_scales, const int8_t* v_codes, const uint16_t* v_scales, int32_t Hkv,
+                      int32_t d, int32_t cap, const int32_t* h_ctx, const int32_t* h_group_start, int32_t G,
+                      float* o, void* ws, size_t ws_bytes, void* stream);
+
 /* Measurement aid, not a step of the method: reads `bytes` bytes of buf
  * (device, 16-B aligned, bytes % 16 == 0) once with 16-B nontemporal loads
  * spread over the whole device, and may write one word to *sink (device, 4-B

@@ -98,3 +98,54 @@ def test_attn_rejects_bad_arguments():
     assert call(ctx_=np.array([63], np.int32)) == -4   # ctx + rows > cap
     assert call(wsz=16) == -5           # workspace too small
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ q8_0 cache
+def _run_q8(torch, mk, a):
+    dev = "cuda"
+    q = torch.from_numpy(a["q"]).to(dev)
+    gate = torch.from_numpy(a["gate"]).to(dev) if a["gate"] is not None else None
+    k8 = torch.from_numpy(a["k8"]).to(dev)
+    v8 = torch.from_numpy(a["v8"]).to(dev)
+    ks = torch.from_numpy(a["ks"].view(np.int16)).to(dev)
+    vs = torch.from_numpy(a["vs"].view(np.int16)).to(dev)
+    o = torch.full_like(q, float("nan"))
+    mk.mk_attn_decode_q8(q, gate, k8, ks, v8, vs, a["ctx"], a["group_start"], o)
+    torch.cuda.synchronize()
+    return o.cpu().numpy()
+
+
+def _check_q8(orc, torch, mk, a, label):
+    say("attention q8", label, "ctx", list(a["ctx"])[:4], "groups", list(a["group_start"])[:5],
+        "Hq", a["q"].shape[1], "Hkv", a["k8"].shape[1], "cap", a["k8"].shape[2])
+    y = _run_q8(torch, mk, a)
+    ref = orc.attn_decode_q8(a["q"], a["gate"], a["k8"], a["ks"], a["v8"], a["vs"], a["ctx"], a["group_start"])
+    assert np.isfinite(y).all(), label
+    e, n = rel_err(y, ref), norm_err(y, ref)
+    say(label, "rel", e, "norm", n)
+    assert e <= FP32_TOL, (label, e)
+    assert n <= 1e-5, (label, n)
+    return y
+
+
+Q8_CASES = [c for c in CASES if c[0] in ("4 agents x 3 rows, ragged contexts", "1 agent x 5 rows (two column blocks)",
+                                         "T = 1, ragged tail", "T = 16, one group (four column blocks)",
+                                         "unequal groups, many splits", "16 agents x 1 row")]
+
+
+@pytest.mark.parametrize("label,ctx,sizes,Hq,Hkv,gate", Q8_CASES, ids=[c[0] for c in Q8_CASES])
+def test_attn_q8_parity(orc, label, ctx, sizes, Hq, Hkv, gate):
+    torch = need_gpu()
+    import bit_weight_streaming_q4_amd as mk
+    a = recipes.attn_inputs_q8(ctx, sizes, Hq=Hq, Hkv=Hkv, gate=gate)
+    _check_q8(orc, torch, mk, a, label)
+
+
+def test_attn_q8_full_size_long_context(orc):
+    """One agent at 131072 cached positions in q8_0 (the pages' long-context
+    setting), T = 5; every output compared, two calls bit-identical."""
+    torch = need_gpu()
+    import bit_weight_streaming_q4_amd as mk
+    a = recipes.attn_inputs_q8([131072], [5])
+    y1 = _check_q8(orc, torch, mk, a, "q8 long context T = 5")
+    assert np.array_equal(y1, _run_q8(torch, mk, a)), "two calls differ"
