@@ -242,7 +242,7 @@ def kernel_bench(lm, device="cuda"):
     5120), the FFN block (5120 -> 17408 -> 5120, T = 5), lm_head + verify
     (151936 x 5120 and the 32768-row draft prefix, T = 5), the Gated
     DeltaNet step + commit (48 x 32 heads of 128 x 128, T = 5) and
-    full-attention decode over an fp16 KV cache."""
+    full-attention decode over fp16 and q8_0 KV caches."""
     import torch
 
     import bit_weight_streaming_q4_amd as mk
@@ -358,7 +358,36 @@ def kernel_bench(lm, device="cuda"):
             lambda i: mk.mk_attn_decode(q, gt, *caches[i % 2], ctx, gs, o, ws=ws), 16, lambda: o, nbytes)
         del caches, kc, vc
         torch.cuda.empty_cache()
+    # The same over a q8_0 cache: 4 x 32768 at T = 12, and one agent at 131072
+    # positions (the pages' long-context setting, where the cache is q8_0).
+    for ctx, sizes in (([32768] * 4, [3] * 4), ([131072], [5])):
+        a = recipes.attn_inputs_q8(ctx, sizes)
+        q = torch.from_numpy(a["q"]).to(device)
+        gt = torch.from_numpy(a["gate"]).to(device)
+        t = [torch.from_numpy(a["k8"]).to(device), torch.from_numpy(a["ks"].view(np.int16)).to(device),
+             torch.from_numpy(a["v8"]).to(device), torch.from_numpy(a["vs"].view(np.int16)).to(device)]
+        del a
+        sets = [t, [x.clone() for x in t]]
+        o = torch.empty_like(q)
+        T = int(sum(sizes))
+        gs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+        ws = mk.workspace(mk.mk_attn_decode_workspace(T, q.shape[1], t[0].shape[1], ctx, gs), device)
+        rec(f"attn_decode_q8_{len(ctx)}x{ctx[0]}_T{T}",
+            lambda i: mk.mk_attn_decode_q8(q, gt, *sets[i % 2], ctx, gs, o, ws=ws), 16, lambda: o,
+            attn_bytes_q8(ctx, sizes))
+        del sets, t
+        torch.cuda.empty_cache()
     return out
+
+
+def attn_bytes_q8(ctx, sizes, Hq=32, Hkv=8, d=128) -> int:
+    """Algorithmic bytes of one q8_0 attention call: every visible K and V
+    code once, the K scales of visible positions, the V scales of the 32-
+    position blocks holding them, plus q, gate and o (fp32)."""
+    L = [int(c) + int(n) for c, n in zip(ctx, sizes)]
+    codes = sum(L) * Hkv * d * 2
+    scales = sum(L) * Hkv * (d // 32) * 2 + sum((x + 31) // 32 for x in L) * Hkv * d * 2
+    return codes + scales + int(sum(sizes)) * Hq * d * 4 * 3
 
 
 def attn_bytes(ctx, sizes, Hq=32, Hkv=8, d=128) -> int:
