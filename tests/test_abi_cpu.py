@@ -121,3 +121,38 @@ def test_workspace_queries_are_host_only():
     assert mk.mk_ffn_rows_workspace(5, 5120, 17408) > 0
     assert mk.mk_lmhead_verify_workspace(151936, 5120, 5) > 151936 // 64 * 16 * 8
     assert mk.mk_q4k_bytes(5120, 5120) == 14_745_600
+
+
+def test_attention_validation_and_workspace_on_the_host():
+    """mk_attn_decode / mk_attn_decode_q8 reject bad shapes, ranges, pointers
+    and workspaces before any GPU work; the workspace query is host-only,
+    0 for invalid arguments and grows with the rows and the contexts."""
+    L = mk.lib()
+    fake = 1 << 20
+    x = ctypes.c_void_p(fake)
+    ctx = np.array([100, 7], np.int32)
+    gs = np.array([0, 3, 6], np.int32)
+    P = lambda a: a.ctypes.data
+
+    def call(T=6, Hq=32, Hkv=8, d=128, cap=128, ctx_=ctx, gs_=gs, G=2, ws_bytes=1 << 30, q=x, ws=x):
+        return L.mk_attn_decode(q, None, T, Hq, x, x, Hkv, d, cap, P(ctx_), P(gs_), G, x, ws, ws_bytes, None)
+
+    assert call(d=64) == mk.MK_ERR_SHAPE
+    assert call(cap=100) == mk.MK_ERR_SHAPE
+    assert call(Hkv=3) == mk.MK_ERR_SHAPE
+    assert call(T=17, gs_=np.array([0, 3, 17], np.int32)) == mk.MK_ERR_RANGE
+    assert call(ctx_=np.array([126, 7], np.int32)) == mk.MK_ERR_RANGE          # 126 + 3 > cap
+    assert call(T=17 - 1, gs_=np.array([0, 1, 16], np.int32), Hq=64) == mk.MK_ERR_RANGE  # 15 rows x 8 > 64
+    assert call(gs_=np.array([0, 3, 5], np.int32)) == mk.MK_ERR_RANGE          # groups must end at T
+    assert call(q=ctypes.c_void_p(fake + 4)) == mk.MK_ERR_ALIGN
+    assert call(q=None) == mk.MK_ERR_ARG
+    assert call(ws_bytes=16) == mk.MK_ERR_WORKSPACE
+    assert L.mk_attn_decode_q8(x, None, 6, 32, None, x, x, x, 8, 128, 128, P(ctx), P(gs), 2, x, x, 1 << 30,
+                               None) == mk.MK_ERR_ARG
+    # workspace query
+    W = lambda T, c, g: L.mk_attn_decode_workspace(T, 32, 8, P(np.array(c, np.int32)), P(np.array(g, np.int32)),
+                                                   len(c))
+    assert W(6, [100, 7], [0, 3, 6]) > 0
+    assert W(6, [100, 7], [0, 3, 5]) == 0
+    assert W(12, [32768] * 4, [0, 3, 6, 9, 12]) > W(12, [1024] * 4, [0, 3, 6, 9, 12])
+    assert W(12, [4096] * 4, [0, 3, 6, 9, 12]) > W(4, [4096] * 4, [0, 1, 2, 3, 4])

@@ -149,3 +149,53 @@ def test_attn_q8_full_size_long_context(orc):
     a = recipes.attn_inputs_q8([131072], [5])
     y1 = _check_q8(orc, torch, mk, a, "q8 long context T = 5")
     assert np.array_equal(y1, _run_q8(torch, mk, a)), "two calls differ"
+
+
+def test_attn_graph_replay_matches_eager():
+    """Both attention entry points captured in a HIP graph: three replays,
+    with eager calls on other inputs in between, each bit-identical to the
+    eager call (the calls use no memset and no allocation)."""
+    torch = need_gpu()
+    import bit_weight_streaming_q4_amd as mk
+    a = recipes.attn_inputs([300, 41, 1000], [3, 2, 3])
+    b = recipes.attn_inputs_q8([300, 41, 1000], [3, 2, 3])
+    dev = "cuda"
+    q = torch.from_numpy(a["q"]).to(dev)
+    gt = torch.from_numpy(a["gate"]).to(dev)
+    k = torch.from_numpy(a["k"].view(np.int16)).to(dev)
+    v = torch.from_numpy(a["v"].view(np.int16)).to(dev)
+    t8 = [torch.from_numpy(b["k8"]).to(dev), torch.from_numpy(b["ks"].view(np.int16)).to(dev),
+          torch.from_numpy(b["v8"]).to(dev), torch.from_numpy(b["vs"].view(np.int16)).to(dev)]
+    ctx, gs = a["ctx"], a["group_start"]
+    ws = mk.workspace(mk.mk_attn_decode_workspace(8, 32, 8, ctx, gs))
+    o, o8 = torch.empty_like(q), torch.empty_like(q)
+
+    def calls():
+        mk.mk_attn_decode(q, gt, k, v, ctx, gs, o, ws=ws)
+        mk.mk_attn_decode_q8(q, gt, *t8, ctx, gs, o8, ws=ws)
+
+    say("attention graph capture", "ctx", list(ctx))
+    calls()
+    torch.cuda.synchronize()
+    ref, ref8 = o.clone(), o8.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    other = recipes.attn_inputs([50], [2], gate=False)
+    oq = torch.from_numpy(other["q"]).to(dev)
+    ok_ = torch.from_numpy(other["k"].view(np.int16)).to(dev)
+    ov = torch.from_numpy(other["v"].view(np.int16)).to(dev)
+    for _ in range(3):
+        o.fill_(float("nan"))
+        o8.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref) and torch.equal(o8, ref8)
+        mk.mk_attn_decode(oq, None, ok_, ov, other["ctx"], other["group_start"], torch.empty_like(oq))
+        torch.cuda.synchronize()
