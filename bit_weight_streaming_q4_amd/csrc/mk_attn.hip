@@ -143,13 +143,24 @@ void k_attn_split(const AttnArgs a) {
     }
   }
 
+  // This head's rows of the cache format in use (the other format's
+  // pointers are null and stay untouched).
   const size_t gh = (size_t)g * a.Hkv + h;
-  const uint16_t* Kb = a.k + gh * a.cap * kD;
-  const uint16_t* Vb = a.v + gh * kD * a.cap;
-  const int8_t* K8 = a.k8 + gh * a.cap * kD;
-  const int8_t* V8 = a.v8 + gh * kD * a.cap;
-  const uint16_t* KS = a.ks + gh * a.cap * (kD / 32);
-  const uint16_t* VS = a.vs + gh * (a.cap / 32) * kD;
+  const uint16_t* Kb = nullptr;
+  const uint16_t* Vb = nullptr;
+  const int8_t* K8 = nullptr;
+  const int8_t* V8 = nullptr;
+  const uint16_t* KS = nullptr;
+  const uint16_t* VS = nullptr;
+  if constexpr (Q8) {
+    K8 = a.k8 + gh * a.cap * kD;
+    V8 = a.v8 + gh * kD * a.cap;
+    KS = a.ks + gh * a.cap * (kD / 32);
+    VS = a.vs + gh * (a.cap / 32) * kD;
+  } else {
+    Kb = a.k + gh * a.cap * kD;
+    Vb = a.v + gh * kD * a.cap;
+  }
   f4 acc[NB][8];
   float mrow[NB], lsum[NB];
 #pragma unroll
