@@ -63,16 +63,21 @@ def _check_head(W16, x_final, am, na, tok, gs, drafts):
     return r["top1"]
 
 
-# T = 2 and 3 are the last dot4 and the first matrix-core instances; 16 is
-# the largest T (4 agents x 4 rows).
-@pytest.mark.parametrize("T,gs", [(1, [0, 1]), (2, [0, 2]), (3, [0, 3]), (5, [0, 5]), (8, [0, 2, 4, 6, 8]),
-                                  (12, [0, 3, 6, 9, 12]), (16, [0, 4, 8, 12, 16])])
+# T = 1 runs the dot4 engine; T = 2..8 the packed matrix-core engine (8
+# padded rows, two sub-blocks per product); T = 9..16 the 16-row engine.
+# 2 and 9 are the first instances of the two matrix-core engines, 8 and 16
+# their largest; 6 has three agents of unequal size (1, 2 and 3 rows), 11 one
+# group that fills neither the rows nor a whole agent count.
+@pytest.mark.parametrize("T,gs", [(1, [0, 1]), (2, [0, 2]), (3, [0, 3]), (5, [0, 5]), (6, [0, 1, 3, 6]),
+                                  (8, [0, 2, 4, 6, 8]), (9, [0, 9]), (11, [0, 11]), (12, [0, 3, 6, 9, 12]),
+                                  (16, [0, 4, 8, 12, 16])])
 def test_decode_step_small_stack(T, gs):
     torch = need_gpu()
     mk = _mk()
     L, H, P, F, V = 4, 512, 1024, 768, 1000
     G = len(gs) - 1
-    st, dry, fields, W16, S0, nh = small_stack(mk, 21, L, H, P, F, V, G)
+    T_max = max(5, max(gs[g + 1] - gs[g] for g in range(G)))  # each agent's ring holds its longest group
+    st, dry, fields, W16, S0, nh = small_stack(mk, 21, L, H, P, F, V, G, T_max=T_max)
     S_ref = [s.copy() for s in S0]
     for step in range(3):
         x = synth.normal_f32(21, 10000 + step, 0, T * H).reshape(T, H)
