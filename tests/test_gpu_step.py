@@ -67,10 +67,12 @@ def _check_head(W16, x_final, am, na, tok, gs, drafts):
 # padded rows, two sub-blocks per product); T = 9..16 the 16-row engine.
 # 2 and 9 are the first instances of the two matrix-core engines, 8 and 16
 # their largest; 6 has three agents of unequal size (1, 2 and 3 rows), 11 one
-# group that fills neither the rows nor a whole agent count.
+# group that fills neither the rows nor a whole agent count.  The last two
+# run eight agents of two rows, and a ten-row chunk of a new prompt riding
+# beside two agents of three rows (each group with its own GDN state).
 @pytest.mark.parametrize("T,gs", [(1, [0, 1]), (2, [0, 2]), (3, [0, 3]), (5, [0, 5]), (6, [0, 1, 3, 6]),
                                   (8, [0, 2, 4, 6, 8]), (9, [0, 9]), (11, [0, 11]), (12, [0, 3, 6, 9, 12]),
-                                  (16, [0, 4, 8, 12, 16])])
+                                  (16, [0, 4, 8, 12, 16]), (16, list(range(0, 17, 2))), (16, [0, 10, 13, 16])])
 def test_decode_step_small_stack(T, gs):
     torch = need_gpu()
     mk = _mk()
