@@ -310,8 +310,8 @@ void k_attn_split(const AttnArgs a) {
     }
   }
 
-  // Merge the block's four splits: wave i's column max m_i, sums l_i and
-  // outputs weigh 2^(m_i - max m); wave w then writes dims 32w .. 32w+31 of
+  // Merge the block's splits: wave i's column max m_i, sums l_i and outputs
+  // weigh 2^(m_i - max m); wave w then writes its share of the dimensions of
   // the block's partial.  Empty splits (m = -inf) weigh zero.
   __syncthreads();
   float* mb = smem;
@@ -350,8 +350,8 @@ void k_attn_split(const AttnArgs a) {
       const size_t base = ((size_t)row * a.Hq + hq) * a.smax + q4;
       float* po = a.part_o + base * kD + 4 * grp;
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int db = 2 * w + k;
+      for (int k = 0; k < 8 / kWaves; ++k) {
+        const int db = (8 / kWaves) * w + k;
         f4 v = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < kWaves; ++i) {
