@@ -262,8 +262,8 @@ def mk_attn_decode(q, gate, k_cache, v_cache, ctx, group_start, o, ws=None, stre
 
 def mk_attn_decode_q8(q, gate, k_codes, k_scales, v_codes, v_scales, ctx, group_start, o, ws=None, stream=None):
     """As mk_attn_decode over q8_0 caches: k_codes int8 [G][Hkv][cap][128] with
-    k_scales fp16 bits [G][Hkv][cap][4]; v_codes int8 [G][Hkv][128][cap] with
-    v_scales [G][Hkv][cap/32][128]."""
+    k_scales fp16 bits [G][Hkv][cap][4]; v_codes int8 [G][Hkv][cap/64][128][64]
+    (tile-major) with v_scales [G][Hkv][cap/32][128]."""
     T, Hq, d = q.shape
     G_, Hkv, cap, _ = k_codes.shape
     ctx_np, gs_np, G = _attn_groups(T, ctx, group_start)

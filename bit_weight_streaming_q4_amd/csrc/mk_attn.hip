@@ -200,7 +200,7 @@ void k_attn_split(const AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         if constexpr (Q8) {
-          v8[hh][db] = *(const uint2*)(V8 + (size_t)(16 * db + col) * a.cap + t0 + 32 * hh + 8 * grp);
+          v8[hh][db] = *(const uint2*)(V8 + ((size_t)(t0 >> 6) * kD + 16 * db + col) * kTile + 32 * hh + 8 * grp);
           vsc[hh][db] = *(const uint2*)(VS + (size_t)((t0 >> 5) + hh) * kD + 16 * db + 4 * grp);
         } else {
           vr[hh][db] = *(const u4*)(Vb + (size_t)(16 * db + col) * a.cap + t0 + 32 * hh + 8 * grp);

@@ -88,7 +88,7 @@ struct AttnArgs {
   const uint16_t* k;    // [G][Hkv][cap][128]
   const uint16_t* v;    // [G][Hkv][128][cap]
   const int8_t* k8;     // q8_0 cache: K codes [G][Hkv][cap][128]
-  const int8_t* v8;     //             V codes [G][Hkv][128][cap]
+  const int8_t* v8;     //             V codes [G][Hkv][cap/64][128][64] (tile-major)
   const uint16_t* ks;   //             K scales [G][Hkv][cap][4]
   const uint16_t* vs;   //             V scales [G][Hkv][cap/32][128]
   float* part_o;        // [T][Hq][smax][128] unnormalised block outputs (4 splits each)

@@ -267,7 +267,9 @@ int mk_attn_decode(const float* q, const float* gate, int32_t T, int32_t Hq, con
  * 32 int8 codes with one fp16 scale; a value is f32(scale) * code.
  *   k_codes  [G][Hkv][cap][d] int8, position-major
  *   k_scales [G][Hkv][cap][d/32] fp16 bits: scale of dims 32i..32i+31 of a position
- *   v_codes  [G][Hkv][d][cap] int8, dimension-major
+ *   v_codes  [G][Hkv][cap/64][d][64] int8, tile-major: positions 64t..64t+63
+ *            of every dimension together, so that one 64-position tile of a
+ *            head is one contiguous run
  *   v_scales [G][Hkv][cap/32][d] fp16 bits: scale of positions 32i..32i+31 of a dimension
  * All device, 16-B aligned.  Every other argument, the workspace (the same
  * mk_attn_decode_workspace) and the errors are those of mk_attn_decode.

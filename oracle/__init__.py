@@ -304,8 +304,8 @@ def attn_decode(q, gate, kc, vc, ctx, group_start=None) -> np.ndarray:
 
 def attn_decode_q8(q, gate, k8, ks, v8, vs, ctx, group_start=None) -> np.ndarray:
     """A2: attention over q8_0 caches.  k8 int8 [G][Hkv][cap][d] with ks fp16
-    bits [G][Hkv][cap][d/32]; v8 int8 [G][Hkv][d][cap] with vs fp16 bits
-    [G][Hkv][cap/32][d]; otherwise as attn_decode."""
+    bits [G][Hkv][cap][d/32]; v8 int8 [G][Hkv][cap/64][d][64] (tile-major)
+    with vs fp16 bits [G][Hkv][cap/32][d]; otherwise as attn_decode."""
     q = _c(q, np.float32)
     T, Hq, d = q.shape
     k8 = _c(k8, np.int8)
@@ -313,7 +313,7 @@ def attn_decode_q8(q, gate, k8, ks, v8, vs, ctx, group_start=None) -> np.ndarray
     ks = _c(ks, np.uint16)
     vs = _c(vs, np.uint16)
     G, Hkv, cap, dk = k8.shape
-    if (dk != d or d % 32 or cap % 32 or v8.shape != (G, Hkv, d, cap) or ks.shape != (G, Hkv, cap, d // 32)
+    if (dk != d or d % 32 or cap % 64 or v8.shape != (G, Hkv, cap // 64, d, 64) or ks.shape != (G, Hkv, cap, d // 32)
             or vs.shape != (G, Hkv, cap // 32, d) or Hq % Hkv):
         raise ValueError("attention q8: shape mismatch")
     ctx = _c(np.asarray(ctx), np.int32)

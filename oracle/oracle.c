@@ -369,7 +369,7 @@ void orc_gdn_step(float* S, int32_t nh, int32_t dk, int32_t dv, const float* q, 
  * codes with one fp16 scale; value = f32(scale) * code, exact in double). */
 typedef struct {
   const uint16_t *kc, *vc;        /* fp16: [G][Hkv][cap][d], [G][Hkv][d][cap] */
-  const int8_t *k8, *v8;          /* q8_0 codes, same layouts */
+  const int8_t *k8, *v8;          /* q8_0 codes: [G][Hkv][cap][d], [G][Hkv][cap/64][d][64] */
   const uint16_t *ks, *vs;        /* q8_0 scales: [G][Hkv][cap][d/32], [G][Hkv][cap/32][d] */
   const float* f16;               /* fp16 bit pattern -> value */
   int64_t cap, d;
@@ -382,7 +382,8 @@ static double k_at(const kv_src* c, int64_t gh, int64_t j, int k) {
 
 static double v_at(const kv_src* c, int64_t gh, int64_t j, int k) {
   if (c->vc) return (double)c->f16[c->vc[(gh * c->d + k) * c->cap + j]];
-  return (double)c->f16[c->vs[(gh * (c->cap / 32) + j / 32) * c->d + k]] * (double)c->v8[(gh * c->d + k) * c->cap + j];
+  return (double)c->f16[c->vs[(gh * (c->cap / 32) + j / 32) * c->d + k]] *
+         (double)c->v8[((gh * (c->cap / 64) + j / 64) * c->d + k) * 64 + j % 64];
 }
 
 static void attn_rows(const float* q, const float* gate, int32_t T, int32_t Hq, const kv_src* c, int32_t Hkv,
@@ -403,8 +404,9 @@ void orc_attn_decode(const float* q, const float* gate, int32_t T, int32_t Hq, c
  * above about 80K positions; richland.au, "Fusing the whole speculative-
  * decoding cycle into one CUDA kernel", section "What shipped").  k8 [G][Hkv]
  * [cap][d] with ks [G][Hkv][cap][d/32] (scale of dims 32i..32i+31 of a
- * position); v8 [G][Hkv][d][cap] with vs [G][Hkv][cap/32][d] (scale of
- * positions 32i..32i+31 of a dimension).  d % 32 == 0, cap % 32 == 0. */
+ * position); v8 [G][Hkv][cap/64][d][64] (tile-major: positions 64t..64t+63
+ * of every dimension together) with vs [G][Hkv][cap/32][d] (scale of
+ * positions 32i..32i+31 of a dimension).  d % 32 == 0, cap % 64 == 0. */
 void orc_attn_decode_q8(const float* q, const float* gate, int32_t T, int32_t Hq, const int8_t* k8,
                         const uint16_t* ks, const int8_t* v8, const uint16_t* vs, int32_t Hkv, int32_t d,
                         int32_t cap, const int32_t* ctx, const int32_t* gs, int32_t G, float* o) {

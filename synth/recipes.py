@@ -176,7 +176,8 @@ def attn_inputs_q8(ctx, sizes, Hq=ATTN_Q_HEADS, Hkv=ATTN_KV_HEADS, d=ATTN_D, cap
     """The same workload over q8_0 caches: codes uniform in -127..127 and
     fp16 scales |N(0, 0.01)| (values of about the fp16 cache's spread).
     K codes [G][Hkv][cap][d] with scales [G][Hkv][cap][d/32]; V codes
-    [G][Hkv][d][cap] with scales [G][Hkv][cap/32][d].  Codes past an agent's
+    tile-major [G][Hkv][cap/64][d][64] (positions 64t..64t+63 of every
+    dimension together) with scales [G][Hkv][cap/32][d].  Codes past an agent's
     last position are 0x80 (-128, outside the codes' range) and scales of
     slots or blocks holding no position are ``fill_scale`` (a NaN)."""
     G = len(ctx)
@@ -196,6 +197,7 @@ def attn_inputs_q8(ctx, sizes, Hq=ATTN_Q_HEADS, Hkv=ATTN_KV_HEADS, d=ATTN_D, cap
             v8[g, h, :, :n] = uniform_i32(seed, 600 + layer, sub, n * d, -127, 127).reshape(n, d).T
             ks[g, h, :n, :] = normal_f16(seed, 700 + layer, sub, n * nb, 0.0, 0.01, absval=True).reshape(n, nb)
             vs[g, h, :nblk, :] = normal_f16(seed, 800 + layer, sub, nblk * d, 0.0, 0.01, absval=True).reshape(nblk, d)
+    v8 = np.ascontiguousarray(v8.reshape(G, Hkv, d, cap // 64, 64).transpose(0, 1, 3, 2, 4))
     T = int(sum(sizes))
     q = normal_f32(seed, 300 + layer, 0, T * Hq * d).reshape(T, Hq, d)
     gt = normal_f32(seed, 400 + layer, 0, T * Hq * d).reshape(T, Hq, d) if gate else None

@@ -533,14 +533,14 @@ def test_attn_q8_equals_fp16_path_on_exact_values(orc):
     result on the dequantized caches.  Scales differ per (position, 32-dim
     block) for K and per (32-position block, dimension) for V, which pins
     which values each scale multiplies."""
-    a = recipes.attn_inputs_q8([45, 7], [2, 3], Hq=4, Hkv=2, d=64, gate=True, seed=13)
+    a = recipes.attn_inputs_q8([45, 7], [2, 3], Hq=4, Hkv=2, d=64, gate=True, seed=13)  # V codes tile-major
     G, Hkv, cap, d = a["k8"].shape
     e_k = synth.uniform_i32(13, 1, 0, G * Hkv * cap * (d // 32), -4, 3).reshape(G, Hkv, cap, d // 32)
     e_v = synth.uniform_i32(13, 2, 0, G * Hkv * (cap // 32) * d, -4, 3).reshape(G, Hkv, cap // 32, d)
     a["ks"] = np.vectorize(lambda e: synth.f64_to_f16_bits(2.0 ** e))(e_k).astype(np.uint16)
     a["vs"] = np.vectorize(lambda e: synth.f64_to_f16_bits(2.0 ** e))(e_v).astype(np.uint16)
     k8 = a["k8"].astype(np.float64)
-    v8 = a["v8"].astype(np.float64)
+    v8 = a["v8"].transpose(0, 1, 3, 2, 4).reshape(G, Hkv, d, cap).astype(np.float64)  # back to [d][cap]
     kval = k8 * np.repeat(2.0 ** e_k, 32, axis=3)
     vval = v8 * np.transpose(np.repeat(2.0 ** e_v, 32, axis=2), (0, 1, 3, 2))
     to16 = np.vectorize(synth.f64_to_f16_bits)
