@@ -13,7 +13,7 @@ Each agent replays the largest possible number of ring rows every step
 (T_agent - 1), which makes the Gated DeltaNet part of the step its most
 expensive; drafts are uniform random ids.
 
-Prints ONE JSON line.  --gpus N > 1 exits: this build runs on one GPU.
+Prints ONE JSON line.  --gpus N > 1 exits: the benchmark runs on one GPU.
 """
 from __future__ import annotations
 
@@ -468,7 +468,7 @@ def main():
                     help="only run a plain 1 GiB device copy (calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus})", file=sys.stderr)
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -160,7 +160,7 @@ int mk_lmhead_verify(const uint16_t* W_f16, int32_t V, int32_t H, const float* h
  *         next step to replay ring rows 1..n_acc[0] (the decode step writes
  *         it from its verification); [1] the half holding the last step's rows.
  *         Zero-initialise both before the first step.
- * dk = dv = 128 (this build).  2 <= T_max <= 16. */
+ * dk = dv = 128 (the only head size supported).  2 <= T_max <= 16. */
 typedef struct {
   float* S;
   float* ring;

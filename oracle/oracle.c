@@ -28,7 +28,7 @@
  * (-ffp-contract=off); fp32 where the definition says fp32, double for every
  * accumulation; outputs rounded to fp32 where the GPU's dataflow stores fp32.
  *
- * Readings of the pages where they are silent (each also listed in the design doc):
+ * Readings of the pages where they are silent:
  *   - activation scale s = fl32(amax/127) by IEEE division, codes
  *     clamp(rne(fl32(x/s)), -127, 127), amax == 0 gives s = 0 and codes 0;
  *   - the delta rule is S <- g (I - beta k k^T) S + beta k v^T with S of shape
