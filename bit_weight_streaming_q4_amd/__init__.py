@@ -80,6 +80,7 @@ def lib():
     L.mk_lmhead_verify.argtypes = [P, i32, i32, P, i32, P, i32, P, P, P, P, P, sz, P]
     L.mk_deltanet_step.argtypes = [ctypes.POINTER(mk_deltanet), i32, P, P, P, P, P, i32, P, P]
     L.mk_deltanet_commit.argtypes = [ctypes.POINTER(mk_deltanet), P]
+    L.mk_deltanet_status.argtypes = [ctypes.POINTER(mk_deltanet), P]
     L.mk_stack_create.argtypes = [ctypes.POINTER(mk_stack_desc), ctypes.POINTER(ctypes.c_void_p)]
     L.mk_stack_destroy.argtypes = [P]
     L.mk_decode_step_workspace.argtypes = [P, i32]
@@ -276,13 +277,14 @@ def mk_attn_decode_q8(q, gate, k_codes, k_scales, v_codes, v_scales, ctx, group_
 
 class DeltaNetState:
     """Device buffers of one Gated DeltaNet state: S [nh][128][128], the
-    two-half ring [2][nh][T_max-1][258] and n_acc = [accept length, ring half]."""
+    two-half ring [2][nh][T_max-1][258] and n_acc = [accept length, ring half,
+    status word, unused]."""
 
     def __init__(self, nh: int, T_max: int, device="cuda", S=None):
         import torch
         self.S = torch.zeros(nh, 128, 128, dtype=torch.float32, device=device) if S is None else S
         self.ring = torch.zeros(2, nh, T_max - 1, 258, dtype=torch.float32, device=device)
-        self.n_acc = torch.zeros(2, dtype=torch.int32, device=device)
+        self.n_acc = torch.zeros(4, dtype=torch.int32, device=device)
         self.nh, self.T_max = nh, T_max
         self.c = mk_deltanet(self.S.data_ptr(), self.ring.data_ptr(), self.n_acc.data_ptr(), nh, 128, 128, T_max)
 
@@ -295,6 +297,16 @@ def mk_deltanet_step(st: DeltaNetState, q, k, v, g, beta, o, use_prev_acc: bool 
 
 def mk_deltanet_commit(st: DeltaNetState, stream=None):
     _check(lib().mk_deltanet_commit(ctypes.byref(st.c), _stream(stream)), "mk_deltanet_commit")
+
+
+def mk_deltanet_status(st: DeltaNetState, stream=None) -> int:
+    """Synchronises, reads and clears the state's status word; returns
+    MK_ERR_RANGE if an out-of-range accept length was read since the last
+    call (nothing was replayed then), else MK_OK."""
+    r = lib().mk_deltanet_status(ctypes.byref(st.c), _stream(stream))
+    if r not in (MK_OK, MK_ERR_RANGE):
+        _check(r, "mk_deltanet_status")
+    return int(r)
 
 
 # --------------------------------------------------------------------- decode step

@@ -411,6 +411,20 @@ int mk_deltanet_commit(const mk_deltanet* st, void* stream) {
   return launch_status(mk::launch_gdn_commit(a, S(stream)), "deltanet commit");
 }
 
+int mk_deltanet_status(const mk_deltanet* st, void* stream) {
+  int r;
+  if ((r = check_dn(st))) return r;
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, st->n_acc + 2, sizeof(v), hipMemcpyDeviceToHost, S(stream)) != hipSuccess ||
+      hipStreamSynchronize(S(stream)) != hipSuccess)
+    return fail(MK_ERR_LAUNCH, "deltanet status: readback failed");
+  if (!v) return ok();
+  if (hipMemsetAsync(st->n_acc + 2, 0, sizeof(int32_t), S(stream)) != hipSuccess ||
+      hipStreamSynchronize(S(stream)) != hipSuccess)
+    return fail(MK_ERR_LAUNCH, "deltanet status: clear failed");
+  return fail(MK_ERR_RANGE, "deltanet: an accept length outside 0..T_max-1 was read (nothing was replayed)");
+}
+
 // ------------------------------------------------------------------ read probe
 // Measurement aid: every thread reads 16-B words of the buffer with
 // nontemporal loads, grid-stride, and folds them into one word; a word that

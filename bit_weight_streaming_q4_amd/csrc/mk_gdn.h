@@ -154,6 +154,14 @@ __device__ __forceinline__ void gdn_half_commit(float* Sh, const float* ring_rd,
   for (int i = 0; i < kD; ++i) Sw[(size_t)i * kD] = S[i];
 }
 
-__device__ __forceinline__ int clamp_acc(int n, int T_max) { return n < 0 ? 0 : (n > T_max - 1 ? T_max - 1 : n); }
+// The accept length n_acc[0] to replay: 0..T_max-1.  A value outside that
+// range replays nothing, and `report` (one lane of the launch) sets the
+// state's status word n_acc[2].
+__device__ __forceinline__ int checked_acc(int32_t* n_acc, int T_max, bool report) {
+  const int n = *as_const<int32_t>(n_acc);
+  if (n >= 0 && n < T_max) return n;
+  if (report) n_acc[2] = 1;
+  return 0;
+}
 
 }  // namespace mk

@@ -13,7 +13,7 @@ __global__ __launch_bounds__(64) void k_gdn_step(GdnArgs a) {
   x.S = a.S + (size_t)h * kD * kD;
   x.ring_rd = a.ring + ((size_t)par * a.nh + h) * (a.T_max - 1) * kRingRow;
   x.ring_wr = a.ring + ((size_t)(par ^ 1) * a.nh + h) * (a.T_max - 1) * kRingRow;
-  x.nrep = a.use_prev ? clamp_acc(*as_const<int32_t>(a.n_acc), a.T_max) : 0;
+  x.nrep = a.use_prev ? checked_acc(a.n_acc, a.T_max, h == 0 && half == 0 && lane == 0) : 0;
   x.q = a.q + (size_t)h * kD;
   x.k = a.k + (size_t)h * kD;
   x.v = a.v + (size_t)h * kD;
@@ -33,7 +33,8 @@ __global__ __launch_bounds__(64) void k_gdn_commit(GdnArgs a) {
   const int h = blockIdx.x, half = blockIdx.y, lane = threadIdx.x;
   const int par = *as_const<int32_t>(a.n_acc + 1) & 1;
   const float* rd = a.ring + ((size_t)par * a.nh + h) * (a.T_max - 1) * kRingRow;
-  gdn_half_commit(a.S + (size_t)h * kD * kD, rd, clamp_acc(*as_const<int32_t>(a.n_acc), a.T_max), half, lane);
+  gdn_half_commit(a.S + (size_t)h * kD * kD, rd, checked_acc(a.n_acc, a.T_max, h == 0 && half == 0 && lane == 0),
+                  half, lane);
 }
 
 // After a step: its rows are in the other ring half.

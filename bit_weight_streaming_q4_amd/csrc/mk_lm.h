@@ -66,12 +66,11 @@ __device__ __forceinline__ void lm_mfma(const LmChunk& x, f32x4 (&acc)[4]) {
 }
 
 // (value, index) order of the argmax: the larger value wins, then the lower
-// index; NaN never wins; index -1 means "no candidate".
+// index; index -1 means "no candidate".  A NaN candidate never wins, not even
+// over "no candidate", so a row whose logits are all NaN keeps index -1.
 __device__ __forceinline__ bool lm_better(float va, int ia, float vb, int ib) {
-  if (ia < 0) return false;
-  if (ib < 0) return true;
-  if (va != va) return false;
-  if (vb != vb) return true;
+  if (ia < 0 || va != va) return false;
+  if (ib < 0 || vb != vb) return true;
   return va > vb || (va == vb && ia < ib);
 }
 

@@ -14,18 +14,39 @@ namespace mk {
 
 // hid [T][H] fp32 -> fragments [H/64][64 lanes][hi 16 | lo 16] fp16 for the
 // B operand: lane l = 16*kq + t holds h = 64c + 16kq + e, e = 0..15 of row t
-// (zeros for t >= T).
-__global__ __launch_bounds__(64) void k_lm_prep(const float* __restrict__ hid, int T, int H,
-                                                _Float16* __restrict__ frag, unsigned* __restrict__ ticket) {
-  const int c = blockIdx.x, l = threadIdx.x;
-  if (c == 0 && l == 0) *ticket = 0u;  // the lm_head kernel's arrival counter
-  const int t = l & 15, kq = l >> 4;
-  _Float16* o = frag + ((size_t)c * 64 + l) * 32;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const float x = t < T ? hid[(size_t)t * H + 64 * c + 16 * kq + e] : 0.0f;
+// (zeros for t >= T).  One block per row t < 16.
+// Each row is first multiplied by the power of two 2^k that brings its
+// largest magnitude into [2^14, 2^15), so that hi never overflows fp16 and
+// lo stays out of the fp16 subnormals for every element that matters.  The
+// scaling is exact and multiplies every logit of the row by the same 2^k,
+// so the argmax is unchanged; rows are accepted at any fp32 magnitude (a row
+// holding inf or only zeros is left unscaled).
+__global__ __launch_bounds__(256) void k_lm_prep(const float* __restrict__ hid, int T, int H,
+                                                 _Float16* __restrict__ frag, unsigned* __restrict__ ticket) {
+  __shared__ float wmax[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (t == 0 && tid == 0) *ticket = 0u;  // the lm_head kernel's arrival counter
+  const float* row = hid + (size_t)t * H;
+  int k = 0;
+  if (t < T) {
+    float m = 0.0f;
+    for (int i = tid; i < H; i += 256) m = __builtin_fmaxf(m, __builtin_fabsf(row[i]));  // NaN is ignored
+    for (int o = 32; o >= 1; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o, 64));
+    if ((tid & 63) == 0) wmax[tid >> 6] = m;
+    __syncthreads();
+    m = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+    if (m > 0.0f && m <= 3.402823466e38f) {
+      int e;
+      __builtin_frexpf(m, &e);  // m = f * 2^e, f in [0.5, 1)
+      k = 15 - e;
+    }
+  }
+  for (int i = tid; i < H; i += 256) {
+    const int c = i >> 6, r = i & 63, l = 16 * (r >> 4) + t, e = r & 15;
+    const float x = t < T ? __builtin_ldexpf(row[i], k) : 0.0f;
     const _Float16 hi = (_Float16)x;
     const _Float16 lo = (_Float16)(x - (float)hi);
+    _Float16* o = frag + ((size_t)c * 64 + l) * 32;
     o[e] = hi;
     o[16 + e] = lo;
   }
@@ -115,7 +136,7 @@ hipError_t launch_lmhead(const uint16_t* W, int V, int H, const float* hid, int 
   float* pval = (float*)p;
   p += ((size_t)nblk * 16 * 4 + 255) / 256 * 256;
   int32_t* pidx = (int32_t*)p;
-  hipLaunchKernelGGL(k_lm_prep, dim3(H / 64), dim3(64), 0, st, hid, T, H, frag, ticket);
+  hipLaunchKernelGGL(k_lm_prep, dim3(16), dim3(256), 0, st, hid, T, H, frag, ticket);
   LmArgs a;
   a.s.W = W;
   a.s.frag = frag;

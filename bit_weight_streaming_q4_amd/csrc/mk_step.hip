@@ -56,6 +56,10 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <map>
+#include <math.h>
+#include <mutex>
 #include <vector>
 
 #include "mk.h"
@@ -92,6 +96,10 @@ constexpr int kPartBatch = 8;                 // partials loaded per batch in an
 constexpr float kRmsEps = 1e-6f;
 constexpr unsigned kSpinLimit = 1u << 26;  // bound of every wait (~seconds)
 constexpr int kMaxStamps = 4 * kMaxLayers + 8;
+// Bits of the device error word.
+constexpr int kErrWatchdog = 1;  // a bounded wait ran out
+constexpr int kErrTables = 2;    // the workspace holds another stack's weight table and plans
+constexpr int kErrAccept = 4;    // an agent state's accept length was outside 0..T_max-1
 
 enum { K_X = 0, K_U = 1, K_X2 = 2, K_H = 3 };
 
@@ -156,6 +164,9 @@ struct StepArgs {
   int32_t* out;  // [0] error word, [16..31] n_acc, [32..47] tokens, [48..63] argmax
   uint64_t* stamps;  // [kMaxStamps]: block 0's clock after each barrier
   const BlockPlan* plans;  // [grid]
+  const uint64_t* ws_tag;  // the workspace's record of the stack whose tables it holds
+  uint64_t tag;            // this stack's tag
+  float lm_pre;            // exact power-of-two prescale of the lm_head input rows
 };
 
 __device__ __forceinline__ bool layer_is_gdn(const StepArgs& a, int l) {
@@ -284,7 +295,7 @@ __device__ __forceinline__ bool wait_ge(const StepArgs& a, BlockState<T>& s, con
     __builtin_amdgcn_s_sleep(1);
     if (++spins > kSpinLimit || lds_ld(&s.abort)) {
       lds_st(&s.abort, 1);
-      if ((threadIdx.x & 63) == 0) atomicOr(a.err, 1);
+      if ((threadIdx.x & 63) == 0) atomicOr(a.err, kErrWatchdog);
       return false;
     }
   }
@@ -1192,7 +1203,8 @@ __device__ __forceinline__ void gdn_job(const StepArgs& a, int layer, long j, in
   x.S = Sa + (size_t)hh * kD * kD;
   x.ring_rd = Ra + ((size_t)par * a.nh + hh) * (a.T_max - 1) * kRingRow;
   x.ring_wr = Ra + ((size_t)(par ^ 1) * a.nh + hh) * (a.T_max - 1) * kRingRow;
-  x.nrep = clamp_acc(*as_const<int32_t>(na), a.T_max);
+  x.nrep = checked_acc(const_cast<int32_t*>(na), a.T_max, lane == 0);
+  if (x.nrep != *as_const<int32_t>(na) && lane == 0) atomicOr(a.err, kErrAccept);  // nothing replayed
   x.q = a.gq + ((size_t)r0 * a.nh + hh) * kD;
   x.k = a.gk + ((size_t)r0 * a.nh + hh) * kD;
   x.v = a.gv + ((size_t)r0 * a.nh + hh) * kD;
@@ -1226,8 +1238,11 @@ __device__ __forceinline__ bool svc_barrier(const StepArgs& a, BlockState<T>& s,
     unsigned spins = 0;
     while (__hip_atomic_load(a.bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit || __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-        atomicOr(a.err, 1);
+      // another block giving up (its watchdog bit) ends this wait too; the
+      // other bits report conditions the step runs through
+      if (++spins > kSpinLimit ||
+          (__hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & kErrWatchdog)) {
+        atomicOr(a.err, kErrWatchdog);
         fail = 1;
         break;
       }
@@ -1391,7 +1406,7 @@ __device__ __forceinline__ bool svc_contrib(const StepArgs& a, BlockState<T>& s,
         __builtin_amdgcn_s_sleep(1);
         if (++spins > kSpinLimit || lds_ld(&s.abort)) {
           lds_st(&s.abort, 1);
-          if (lane == 0) atomicOr(a.err, 1);
+          if (lane == 0) atomicOr(a.err, kErrWatchdog);
           return false;
         }
       }
@@ -1474,7 +1489,7 @@ __device__ __forceinline__ bool svc_own(const StepArgs& a, BlockState<T>& s, int
       __builtin_amdgcn_s_sleep(1);
       if (++spins > kSpinLimit || lds_ld(&s.abort)) {
         lds_st(&s.abort, 1);
-        if (lane == 0) atomicOr(a.err, 1);
+        if (lane == 0) atomicOr(a.err, kErrWatchdog);
         return false;
       }
     }
@@ -1508,7 +1523,7 @@ __device__ __forceinline__ void svc_lm_prep(const StepArgs& a, int lane, const f
   float r = 0.0f;
 #pragma unroll
   for (int i = 0; i < T; ++i)
-    if (t == i) r = rt[i];
+    if (t == i) r = rt[i] * a.lm_pre;
   const int tt = t < a.T ? t : 0;  // every lane loads an in-range value
   for (int c = blockIdx.x; c < nc; c += gridDim.x) {
     float* o = (float*)(a.frag + ((size_t)c * 64 + lane) * 32);
@@ -1573,7 +1588,7 @@ __device__ __forceinline__ void watch_wave(const StepArgs& a, BlockState<T>& s, 
         __builtin_amdgcn_s_sleep(1);
         if (++spins > kSpinLimit / 8 || lds_ld(&s.abort)) {
           lds_st(&s.abort, 1);
-          if (lane == 0) atomicOr(a.err, 1);
+          if (lane == 0) atomicOr(a.err, kErrWatchdog);
           return;
         }
       }
@@ -1595,7 +1610,7 @@ __device__ __forceinline__ void watch_wave(const StepArgs& a, BlockState<T>& s, 
       __builtin_amdgcn_s_sleep(1);
       if (++spins > kSpinLimit / 8 || lds_ld(&s.abort)) {
         lds_st(&s.abort, 1);
-        if (lane == 0) atomicOr(a.err, 1);
+        if (lane == 0) atomicOr(a.err, kErrWatchdog);
         return;
       }
     }
@@ -1672,6 +1687,15 @@ __global__ __launch_bounds__(kBlock) void k_decode_step(StepArgs a) {
   __shared__ BlockState<T> s;
   const int lane = threadIdx.x & 63;
   const int wib = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // The weight table and block plans in the workspace must be this stack's
+  // (written before the launch; every block reads the same tag, so either
+  // every block runs or none does).
+  if (threadIdx.x == 0) s.abort = *a.ws_tag != a.tag;
+  __syncthreads();
+  if (s.abort) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) atomicOr(a.err, kErrTables);
+    return;
+  }
   if (threadIdx.x < BlockState<T>::NMB * kCompute) (&s.tag[0][0])[threadIdx.x] = 0;
   if (threadIdx.x < kCompute) s.done[threadIdx.x] = 0;
   // the weight table is written before the launch: plain loads are safe
@@ -1748,7 +1772,7 @@ struct mk_stack {
   std::vector<uint8_t> gdn_flag;
   int n_gdn_layers = 0;
   int8_t gdn_idx[kMaxLayers];
-  void* uploaded_ws = nullptr;  // workspace that holds the current weight table and block plans
+  uint64_t tag = 0;              // unique per stack; written into a workspace with its tables
   std::vector<BlockPlan> plans;  // for plans_grid blocks
   int plans_grid = -1;
   hipEvent_t ev[2] = {nullptr, nullptr};  // around the last launch (no device memory)
@@ -1759,12 +1783,21 @@ namespace {
 
 size_t a256(size_t n) { return (n + 255) / 256 * 256; }
 
+// Which stack's weight table and block plans each workspace holds.  A
+// workspace is bound to the last stack that ran a step on it; a step by
+// another stack uploads its own tables again.  The kernel checks the tag
+// written beside the tables, so a workspace that some other call wrote in
+// between is caught on the device.
+std::mutex g_ws_mu;
+std::map<const void*, uint64_t> g_ws_tables;
+std::atomic<uint64_t> g_next_tag{1};
+
 struct StepLayout {
   int grid, Wc;
   int cmax[4];
   size_t off_ctrl, n_ctrl;  // zeroed before each launch: barrier, tickets
   size_t off_rdy, off_open, part_half;
-  size_t off_plans;
+  size_t off_plans, off_tag;
   size_t off_out, off_stamps, off_tickets, off_lmticket, off_table, off_act, off_ss, off_part, off_frag, off_lmv,
       off_lmi, total;
   size_t act_layer, act_off[4];
@@ -1825,6 +1858,8 @@ StepLayout layout(const mk_stack* st, int T) {
   o += 256;
   y.off_stamps = o;
   o += a256(sizeof(uint64_t) * kMaxStamps);
+  y.off_tag = o;
+  o += 256;
   y.off_table = o;
   o += a256(sizeof(LayerW) * d.n_layers);
   y.off_plans = o;
@@ -1971,6 +2006,7 @@ int mk_stack_create(const mk_stack_desc* desc, mk_stack** out) {
       st->dn.push_back(s);
     }
   }
+  st->tag = g_next_tag.fetch_add(1);
   if (hipEventCreate(&st->ev[0]) != hipSuccess || hipEventCreate(&st->ev[1]) != hipSuccess) {
     st->ev[0] = st->ev[1] = nullptr;
   }
@@ -1980,6 +2016,11 @@ int mk_stack_create(const mk_stack_desc* desc, mk_stack** out) {
 
 void mk_stack_destroy(mk_stack* st) {
   if (!st) return;
+  {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    for (auto it = g_ws_tables.begin(); it != g_ws_tables.end();)
+      it = it->second == st->tag ? g_ws_tables.erase(it) : std::next(it);
+  }
   for (int i = 0; i < 2; ++i)
     if (st->ev[i]) hipEventDestroy(st->ev[i]);
   delete st;
@@ -2026,18 +2067,26 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
   if ((uintptr_t)ws % 256) return sfail(MK_ERR_ALIGN, "decode: workspace not 256-B aligned");
   hipStream_t s = (hipStream_t)stream;
   uint8_t* w8 = (uint8_t*)ws;
+  bool fresh_plans = false;
   if (st->plans_grid != y.grid) {
     if (!make_plans(st->d, y.grid, st->plans)) return sfail(MK_ERR_SHAPE, "decode: shapes too small for the grid's work plan");
     st->plans_grid = y.grid;
-    st->uploaded_ws = nullptr;
+    fresh_plans = true;
   }
-  if (st->uploaded_ws != ws) {
-    if (hipMemcpyAsync(w8 + y.off_table, st->layers.data(), sizeof(LayerW) * st->layers.size(),
-                       hipMemcpyHostToDevice, s) != hipSuccess ||
-        hipMemcpyAsync(w8 + y.off_plans, st->plans.data(), sizeof(BlockPlan) * st->plans.size(), hipMemcpyHostToDevice,
-                       s) != hipSuccess)
-      return sfail(MK_ERR_LAUNCH, "decode: weight table upload failed");
-    st->uploaded_ws = ws;
+  {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    auto it = g_ws_tables.find(ws);
+    if (fresh_plans || it == g_ws_tables.end() || it->second != st->tag) {
+      if (hipMemcpyAsync(w8 + y.off_table, st->layers.data(), sizeof(LayerW) * st->layers.size(),
+                         hipMemcpyHostToDevice, s) != hipSuccess ||
+          hipMemcpyAsync(w8 + y.off_plans, st->plans.data(), sizeof(BlockPlan) * st->plans.size(),
+                         hipMemcpyHostToDevice, s) != hipSuccess ||
+          hipMemcpyAsync(w8 + y.off_tag, &st->tag, sizeof(uint64_t), hipMemcpyHostToDevice, s) != hipSuccess) {
+        g_ws_tables.erase(ws);
+        return sfail(MK_ERR_LAUNCH, "decode: weight table upload failed");
+      }
+      g_ws_tables[ws] = st->tag;
+    }
   }
   if (hipMemsetAsync(w8 + y.off_ctrl, 0, y.n_ctrl, s) != hipSuccess ||
       hipMemsetAsync(w8 + y.off_out, 0, 256, s) != hipSuccess)
@@ -2101,6 +2150,12 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
   a.frag = (_Float16*)(w8 + y.off_frag);
   a.lm_val = (float*)(w8 + y.off_lmv);
   a.lm_idx = (int*)(w8 + y.off_lmi);
+  a.ws_tag = (const uint64_t*)(w8 + y.off_tag);
+  a.tag = st->tag;
+  // |RMSNorm(x)_i| <= sqrt(hidden) for every row, so 2^k with
+  // sqrt(hidden) * 2^k <= 2^14 keeps every lm_head input far inside fp16's
+  // range; the scaling is exact and leaves the argmax unchanged.
+  a.lm_pre = ldexpf(1.0f, (int)floor(log2(16384.0 / sqrt((double)d.hidden))));
   void* args[] = {&a};
   if (st->ev[0]) hipEventRecord(st->ev[0], s);
   hipError_t e = hipLaunchCooperativeKernel((const void*)step_kernel(T), dim3(y.grid), dim3(kBlock), args, 0, s);
@@ -2117,7 +2172,17 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
     return sfail(MK_ERR_LAUNCH, "decode: readback failed");
   st->last_ms = -1.0f;
   if (st->ev[0] && st->ev[1]) hipEventElapsedTime(&st->last_ms, st->ev[0], st->ev[1]);
-  if (hout[0]) return sfail(MK_ERR_DEVICE, "decode: grid-barrier watchdog fired");
+  if (hout[0] & kErrTables) {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    g_ws_tables.erase(ws);
+    return sfail(MK_ERR_WORKSPACE,
+                 "decode: the workspace no longer holds this stack's tables (another call wrote it); nothing ran, "
+                 "the next call uploads them again");
+  }
+  if (hout[0] & kErrWatchdog) return sfail(MK_ERR_DEVICE, "decode: grid-barrier watchdog fired");
+  if (hout[0] & kErrAccept)
+    return sfail(MK_ERR_RANGE, "decode: an agent state's accept length was outside 0..T_max-1 (nothing was replayed)");
+  if (hout[0]) return sfail(MK_ERR_DEVICE, "decode: device error word set");
   for (int g = 0; g < G; ++g) h_n_acc[g] = hout[16 + g];
   for (int t = 0; t < T; ++t) h_tokens[t] = hout[32 + t];
   set_error(MK_OK, "");

@@ -103,7 +103,12 @@ int mk_q4k_unpack(const void* h_blocks, int32_t n_out, int32_t n_in, uint16_t* h
 int mk_quantize_rows(const float* x, int32_t T, int32_t K, int8_t* a8, float* s, int32_t* gsum, void* stream);
 
 /* ----------------------------------------------------------------- T-row GEMV */
-/* y[t][o] = sum_k w[o][k] * s[t][k/32] * a8[t][k] for the quantized rows of x:
+/* richland.au, "Fusing the whole speculative-decoding cycle into one CUDA
+ * kernel", section "What shipped" (the GEMV shares its activations so that T
+ * rows cost about the memory time of one), and the 4-agent article, section
+ * "Why it matters" (each loaded weight is multiplied against every stacked row
+ * while it is on chip).
+ * y[t][o] = sum_k w[o][k] * s[t][k/32] * a8[t][k] for the quantized rows of x:
  * every weight block is read from HBM once and multiplied against all T rows.
  * Integer sub-block sums (32 codes x 32 int8 values) are exact; they are
  * combined with d, dmin, sc, m and the activation scales in fp32.
@@ -133,7 +138,12 @@ int mk_ffn_rows(const mk_q4k* gate, const mk_q4k* up, const mk_q4k* down, const 
                 float* h_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------- lm_head + verify */
-/* logits[t][v] = sum_h f32(W[v][h]) * hid[t][h] (fp16 weights widened exactly,
+/* richland.au single-stream article, section "What shipped" (lm_head and
+ * verification run on the device; only accepted tokens go back to the host),
+ * and pulse-3k2 "UPDATE: ... KL divergence 0.0009 vs llama.cpp", section
+ * "Decode accuracy vs llama.cpp" (greedy output equals the main model's greedy
+ * choice).
+ * logits[t][v] = sum_h f32(W[v][h]) * hid[t][h] (fp16 weights widened exactly,
  * fp32 hidden, fp32 accumulation); argmax[t] = lowest index of the maximum
  * (NaN never wins; -1 if all logits of the row are NaN).  Rows are split into
  * G groups by h_group_start[0..G] (host array, h_group_start[0] = 0,
@@ -144,22 +154,35 @@ int mk_ffn_rows(const mk_q4k* gate, const mk_q4k* up, const mk_q4k* down, const 
  * i = 0..n_acc[g] receives the accepted drafts then the argmax of row n_acc[g]
  * (other slots are set to -1).  A draft id outside [0, V) is a mismatch.
  * W [V][H] fp16 bits, hid [T][H], drafts [T-G] int32 (may be NULL if T == G),
- * argmax [T], n_acc [G], tokens [T] (all device).  H % 64 == 0. */
+ * argmax [T], n_acc [G], tokens [T] (all device).  H % 64 == 0.
+ * Range of hid: any fp32 values.  Each row is multiplied by an exact power of
+ * two that brings its largest magnitude into [2^14, 2^15) before it is split
+ * into the two fp16 parts the matrix cores take, so neither part overflows and
+ * every element within 2^-24 of the row's largest keeps about 22 bits; the
+ * scaling multiplies every logit of a row by the same power of two and leaves
+ * the argmax unchanged.  A row holding inf is not scaled. */
 size_t mk_lmhead_verify_workspace(int32_t V, int32_t H, int32_t T);
 int mk_lmhead_verify(const uint16_t* W_f16, int32_t V, int32_t H, const float* hid, int32_t T,
                      const int32_t* h_group_start, int32_t G, const int32_t* drafts, int32_t* argmax,
                      int32_t* n_acc, int32_t* tokens, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------- Gated DeltaNet */
-/* State of nh independent heads (e.g. layers x heads) with rollback ring.
+/* richland.au single-stream article, section "What shipped": the recurrent
+ * state is committed only through the surely-accepted token, and drafted rows
+ * are replayed from a small (k, v, g, beta) ring.  The delta rule itself
+ * (S <- g (I - beta k k^T) S + beta k v^T, o = S^T q) follows the workload
+ * definition that accompanies the pages.
+ * State of nh independent heads (e.g. layers x heads) with rollback ring.
  *   S     [nh][dk][dv] fp32, S[h][i][j] (i key index, j value index)
  *   ring  [2][nh][T_max-1][dk+dv+2] fp32: two halves used on alternate steps;
  *         a step stores its rows 1..T-1 as (k, v, g, beta) in one half while
  *         it replays the previous step's rows from the other half
- *   n_acc 2 int32 (device): [0] accept length of the last step, read by the
+ *   n_acc 4 int32 (device): [0] accept length of the last step, read by the
  *         next step to replay ring rows 1..n_acc[0] (the decode step writes
- *         it from its verification); [1] the half holding the last step's rows.
- *         Zero-initialise both before the first step.
+ *         it from its verification); [1] the half holding the last step's rows;
+ *         [2] status word: set to 1 by a step or commit that read an accept
+ *         length outside 0..T_max-1 (it then replays nothing);
+ *         [3] unused.  Zero-initialise all four before the first step.
  * dk = dv = 128 (the only head size supported).  2 <= T_max <= 16. */
 typedef struct {
   float* S;
@@ -169,19 +192,31 @@ typedef struct {
 } mk_deltanet;
 
 /* One step, per head: replay ring rows 1..a (a = n_acc[0] if use_prev_acc,
- * else 0; a is clamped to 0..T_max-1), then for t = 0..T-1:
+ * else 0; a value outside 0..T_max-1 replays nothing and sets n_acc[2], which
+ * mk_deltanet_status reports), then for t = 0..T-1:
  *   S <- g_t (I - beta_t k_t k_t^T) S + beta_t k_t v_t^T,   o_t = S^T q_t,
  * committing S after row 0 and storing rows 1..T-1 in the ring.
  * q, k [T][nh][dk]; v [T][nh][dv]; g, beta [T][nh]; o [T][nh][dv].  1 <= T <= T_max. */
 int mk_deltanet_step(const mk_deltanet* st, int32_t use_prev_acc, const float* q, const float* k, const float* v,
                      const float* g, const float* beta, int32_t T, float* o, void* stream);
 
-/* Replays ring rows 1..a (a = n_acc[0], clamped) into S without new rows, so
- * that S holds the state through the accepted row; then sets n_acc[0] = 0. */
+/* Replays ring rows 1..a (a = n_acc[0]; outside 0..T_max-1: nothing, and
+ * n_acc[2] is set) into S without new rows, so that S holds the state through
+ * the accepted row; then sets n_acc[0] = 0. */
 int mk_deltanet_commit(const mk_deltanet* st, void* stream);
 
+/* Synchronises `stream`, reads the status word n_acc[2] and clears it.
+ * Returns MK_ERR_RANGE if a step or commit since the last call read an accept
+ * length outside 0..T_max-1, else MK_OK. */
+int mk_deltanet_status(const mk_deltanet* st, void* stream);
+
 /* --------------------------------------------------- persistent decode step */
-/* A synthetic layer stack: per layer a = RMSNorm(x); x += P_out.q8(P_in.q8(a));
+/* richland.au single-stream article, section "What shipped" (one persistent
+ * launch runs the main model over T = 1 + n_draft rows, lm_head and the
+ * verification; the host reads back only the accepted tokens), and the
+ * 4-agent article, section "Why it matters" (all agents' rows share one
+ * weight read per step).
+ * A synthetic layer stack: per layer a = RMSNorm(x); x += P_out.q8(P_in.q8(a));
  * a = RMSNorm(x); x += W_down.q8(SiLU(W_gate.q8(a)) * W_up.q8(a)).  RMSNorm has
  * unit gain and eps 1e-6; the norm scale is applied to the activation scales
  * (equal in exact arithmetic to quantizing the normalised row).  Layers with
@@ -214,7 +249,18 @@ size_t mk_decode_step_workspace(const mk_stack* st, int32_t T);
  *   the stack has no GDN layers), gdn_o [T][nh][dv] (device, may be NULL),
  *   h_tokens [T], h_n_acc [G] (host outputs), d_argmax [T] (device, optional),
  *   trace (device, optional): [n_layers][T][hidden] residual after each layer.
- * Returns MK_ERR_DEVICE if the device error word is set (grid-barrier watchdog). */
+ * The workspace holds the stack's weight table and work plans: it is bound
+ * to the last stack that ran a step on it.  A step by another stack uploads
+ * its own tables first (host-side record per workspace).  If some other call
+ * wrote the workspace in between, the kernel sees a foreign tag, nothing
+ * runs, and the call returns MK_ERR_WORKSPACE; the next call uploads the
+ * tables again.  Steps that share a workspace must not overlap.
+ * The lm_head input rows are RMSNorm outputs, so |value| <= sqrt(hidden); they
+ * are multiplied by the exact power of two 2^k with sqrt(hidden) 2^k <= 2^14
+ * before the fp16 split (the argmax is unchanged).
+ * Returns MK_ERR_DEVICE if a bounded device wait ran out (watchdog), and
+ * MK_ERR_RANGE if an agent state's accept length was outside 0..T_max-1
+ * (that agent then replays nothing; its n_acc[2] is set as well). */
 int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_start, int32_t G,
                    const int32_t* drafts, const float* gdn_q, const float* gdn_k, const float* gdn_v,
                    const float* gdn_g, const float* gdn_beta, float* gdn_o, int32_t* h_tokens, int32_t* h_n_acc,

@@ -25,10 +25,13 @@ kernel" (section "What shipped"), richland.au "OpenJet's CUDA megakernel runs
 4 coding agents" (section "Why it matters"), pulse-3k2 "UPDATE: ... KL
 divergence" (section "Decode accuracy").
 
-Parity status: C1-C4, C6, C7, A1 and A2 are pinned by tests against brute force,
-closed forms and library routines.  C5's glue (pre-RMSNorm, identity mixer)
-and C8's composition are readings of the pages: parity unpinned beyond the
-pinned parts they compose.
+Parity status: every function is pinned in tests/test_oracle_pins.py against
+something other than itself: C1-C4, C6, C7, A1 and A2 against brute force,
+closed forms and library routines; C5 (the layer glue, a reading of the pages:
+pre-RMSNorm, identity mixer, fp32 residual) against an identity case and an
+independent float64 numpy evaluation of the same definition; C8 against
+planted drafts, a float64 numpy argmax and a full-matrix delta-rule recompute
+of the committed state.
 """
 from __future__ import annotations
 
@@ -199,11 +202,68 @@ def residual_add(x, y) -> np.ndarray:
 
 
 def layer(x, Wl) -> np.ndarray:
-    """C5 (one synthetic layer; reading of the pages, parity unpinned beyond
-    its parts): x += P_out.q8(P_in.q8(RMSNorm x)); x += FFN(RMSNorm x)."""
+    """C5 (one synthetic layer; the glue is a reading of the pages: the
+    workload lists only the projections and the FFN): pre-RMSNorm with unit
+    gain, identity mixer, fp32 residual:
+    x += P_out.q8(P_in.q8(RMSNorm x)); x += FFN(RMSNorm x)."""
     u = qgemv(Wl["p_in"], rmsnorm(x))
     x = residual_add(x, qgemv(Wl["p_out"], u))
     return residual_add(x, ffn(Wl["gate"], Wl["up"], Wl["down"], rmsnorm(x)))
+
+
+def decode_step(x, layers, W16, group_start, drafts, gdn=None, n_layers=None, teacher=None, progress=None) -> dict:
+    """C8: one whole decode step, composed in the pages' order (richland.au
+    single-stream article, "What shipped"; the 4-agent article, "Why it
+    matters"): the T rows x [T][H] pass every layer (C5); the final residual
+    is RMSNorm'ed and goes through lm_head with its argmax (C6); each group's
+    drafts are verified against its rows' argmax (C6); then each agent's Gated
+    DeltaNet state absorbs the agent's rows 0..n_acc of this step (C7), so the
+    committed state ends at the accepted token.
+
+    layers: list of per-layer field dicts (p_in, p_out, gate, up, down), or a
+    callable l -> dict (then n_layers is required) so that a large stack is
+    generated one layer at a time.
+    teacher: optional [L][T][H] residuals of another path; layer l > 0 then
+    starts from teacher[l - 1] instead of the oracle's own layer l - 1, and
+    the lm_head input is teacher[L - 1] (stage-wise comparison).
+    gdn: None, or a dict with "S" (list of per-agent states [nh][dk][dv]) and
+    the step's rows "q", "k", "v" [T][nh][d], "g", "beta" [T][nh].
+    progress: optional callable (l, trace_l) run after each layer.
+    Returns trace [L][T][H] (residual after each layer), hid, argmax, n_acc,
+    tokens and, with gdn, the committed states "S" and outputs "gdn_o"."""
+    x = _c(np.atleast_2d(x), np.float32)
+    if callable(layers):
+        if n_layers is None:
+            raise ValueError("n_layers is required with a layer generator")
+        get = layers
+    else:
+        n_layers = len(layers)
+        get = layers.__getitem__
+    trace = np.empty((n_layers,) + x.shape, np.float32)
+    cur = x
+    for l in range(n_layers):
+        if teacher is not None and l > 0:
+            cur = _c(teacher[l - 1], np.float32)
+        cur = layer(cur, get(l))
+        trace[l] = cur
+        if progress is not None:
+            progress(l, cur)
+    final = trace[-1] if teacher is None else _c(teacher[-1], np.float32)
+    hid = rmsnorm(final)
+    r = lmhead(W16, hid)
+    n_acc, tokens = verify(r["top1"], group_start, drafts)
+    out = {"trace": trace, "hid": hid, "argmax": r["top1"], "lm": r, "n_acc": n_acc, "tokens": tokens}
+    if gdn is not None:
+        gs = list(group_start)
+        S_new, o_all = [], np.empty_like(_c(gdn["v"], np.float32))
+        for a in range(len(gs) - 1):
+            r0, r1 = gs[a], gs[a + 1]
+            S1, o = gdn_step(gdn["S"][a], gdn["q"][r0:r1], gdn["k"][r0:r1], gdn["v"][r0:r1], gdn["g"][r0:r1],
+                             gdn["beta"][r0:r1], int(n_acc[a]))
+            S_new.append(S1)
+            o_all[r0:r1] = o
+        out["S"], out["gdn_o"] = S_new, o_all
+    return out
 
 
 def lmhead(W16, hid, return_logits=False) -> dict:

@@ -75,24 +75,61 @@ def test_gdn_chain_equivalence_bit_exact():
     assert np.array_equal(to_np(st.S), Sa)
 
 
-def test_gdn_full_size_steps():
-    """48 layers x 32 heads of 128 x 128 fp32 state ~ N(0, .01), T = 5,
-    seeded accept lengths in 0..4 (first steps of the 256-step workload)."""
+def test_gdn_full_size_256_steps():
+    """The Gated DeltaNet workload as defined: 48 layers x 32 heads of 128 x
+    128 fp32 state ~ N(0, .01), T = 5 rows per step, seeded accept lengths in
+    0..4, 256 steps.  The GPU runs every head of every step; the oracle
+    follows every 8th head (192 of 1536) through all 256 steps: their outputs
+    at every step and their committed state at the end."""
     torch = need_gpu()
     mk = _mk()
-    nh, T, steps = 48 * 32, 5, 4
-    S0 = recipes.gdn_initial_state()
+    nh, T, steps = 48 * 32, 5, 256
+    heads = np.arange(0, nh, 8)
+    S0 = recipes.gdn_initial_state().reshape(nh, 128, 128)
     accepts = recipes.gdn_accept_lengths(steps)
-    st = mk.DeltaNetState(nh, 5, S=to_dev(S0.reshape(nh, 128, 128)))
-    S = S0.reshape(nh, 128, 128).copy()
+    st = mk.DeltaNetState(nh, 5, S=to_dev(S0))
+    S = S0[heads].copy()
+    o = torch.empty(T, nh, 128, dtype=torch.float32, device="cuda")
+    worst = 0.0
     for s in range(steps):
         inp = recipes.gdn_step(s, T)
         q, k, v, g, b = _inputs_dev(inp)
-        o = torch.empty(T, nh, 128, dtype=torch.float32, device="cuda")
-        say("gdn full step", s)
+        if s % 32 == 0:
+            say("gdn 256 steps: step", s, "worst so far", worst)
         mk.mk_deltanet_step(st, q, k, v, g, b, o, use_prev_acc=s > 0)
         st.n_acc[0] = int(accepts[s])
-        S, oref = oracle.gdn_step(S, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], int(accepts[s]))
-        assert rel_err(to_np(o), oref) <= FP32_TOL
+        sub = {n: np.ascontiguousarray(inp[n][:, heads]) for n in ("q", "k", "v", "g", "beta")}
+        S, oref = oracle.gdn_step(S, sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], int(accepts[s]))
+        e = rel_err(to_np(o)[:, heads], oref)
+        worst = max(worst, e)
+        assert e <= FP32_TOL, (s, e)
     mk.mk_deltanet_commit(st)
-    assert rel_err(to_np(st.S), S) <= FP32_TOL
+    assert mk.mk_deltanet_status(st) == mk.MK_OK
+    e = rel_err(to_np(st.S)[heads], S)
+    say("gdn 256 steps: outputs worst", worst, "committed state", e)
+    assert e <= FP32_TOL, e
+
+
+def test_gdn_accept_length_out_of_range_is_reported():
+    """An accept length outside 0..T_max-1 in the state replays nothing and
+    is reported by mk_deltanet_status (then cleared)."""
+    torch = need_gpu()
+    mk = _mk()
+    nh, T = 4, 5
+    S0 = synth.normal_f32(4, 11, 0, nh * 128 * 128, 0.0, 0.01).reshape(nh, 128, 128)
+    ref = mk.DeltaNetState(nh, 5, S=to_dev(S0.copy()))
+    bad = mk.DeltaNetState(nh, 5, S=to_dev(S0.copy()))
+    for st, acc in ((ref, 0), (bad, 7)):
+        for s in range(2):
+            inp = steps_inputs(s, T, nh)
+            q, k, v, g, b = _inputs_dev(inp)
+            o = torch.empty(T, nh, 128, dtype=torch.float32, device="cuda")
+            mk.mk_deltanet_step(st, q, k, v, g, b, o, use_prev_acc=s > 0)
+            st.n_acc[0] = acc
+    assert mk.mk_deltanet_status(ref) == mk.MK_OK
+    assert mk.mk_deltanet_status(bad) == mk.MK_ERR_RANGE
+    assert mk.mk_deltanet_status(bad) == mk.MK_OK  # cleared by the read
+    assert np.array_equal(to_np(bad.S), to_np(ref.S))  # the bad step replayed nothing
+    mk.mk_deltanet_commit(bad)  # n_acc[0] = 7 again: nothing replayed, reported
+    assert mk.mk_deltanet_status(bad) == mk.MK_ERR_RANGE
+    assert np.array_equal(to_np(bad.S), to_np(ref.S))

@@ -19,7 +19,7 @@ def _mk():
 def test_quantize_bit_exact():
     torch = need_gpu()
     mk = _mk()
-    T, K = 16, 65536
+    T, K = 16, 655360  # 1.05e7 values
     x = synth.normal_f32(5, 1, 0, T * K).reshape(T, K)
     x[0, :32] = 0.0  # all-zero group
     # exact half-way cases: group max 127 gives s = 1, then n + 0.5 values

@@ -108,3 +108,49 @@ def test_lmhead_full_vocab_and_draft_prefix():
     say("lmhead full T=12")
     am, na, tok = _run(mk, torch, Wd, hid, gs, drafts)
     _check(W, hid, am, na, tok, gs, drafts)
+
+
+def test_lmhead_all_nan_row():
+    """A hidden row of NaN has no argmax (-1): it accepts no draft, and as
+    the bonus row it emits -1 (same rule as the oracle)."""
+    torch = need_gpu()
+    mk = _mk()
+    V, H = 1000, 512
+    W = synth.normal_f16(3, 63, 0, V * H, 0.0, 0.02).reshape(V, H)
+    hid = synth.normal_f32(3, 64, 0, 3 * H).reshape(3, H)
+    r = oracle.lmhead(W, hid)
+    for nan_row, drafts in ((0, [r["top1"][0], r["top1"][1]]), (2, [r["top1"][0], r["top1"][1]]),
+                            (1, [r["top1"][0], -1])):
+        h = hid.copy()
+        h[nan_row] = np.nan
+        say("lmhead NaN row", nan_row)
+        am, na, tok = _run(mk, torch, to_dev(W), h, None, drafts)
+        assert am[nan_row] == -1
+        ro = oracle.lmhead(W, h)
+        assert ro["top1"][nan_row] == -1
+        _check(W, h, am, na, tok, None, np.asarray(drafts, np.int32))
+        n_ref = {0: 0, 2: 2, 1: 1}[nan_row]
+        assert na[0] == n_ref and tok[n_ref] == am[n_ref]
+
+
+def test_lmhead_hidden_rows_at_any_scale():
+    """Rows scaled by 2^-20 and 2^16 (max |x| far above fp16's 65504) give,
+    bit for bit, the argmax of the unscaled rows (the per-row power-of-two
+    prescale), which is the oracle's argmax outside the near-tie carve-out."""
+    torch = need_gpu()
+    mk = _mk()
+    V, H, T = 4000, 5120, 5
+    W = synth.normal_f16(3, 65, 0, V * H, 0.0, 0.02).reshape(V, H)
+    Wd = to_dev(W)
+    hid = synth.normal_f32(3, 66, 0, T * H).reshape(T, H)
+    r = oracle.lmhead(W, hid)
+    drafts = [int(r["top1"][i]) for i in range(T - 1)]
+    base = _run(mk, torch, Wd, hid, None, drafts)
+    _check(W, hid, *base, None, np.asarray(drafts, np.int32))
+    for e in (-20, 16, -60, 100):
+        hs = (hid.astype(np.float64) * 2.0 ** e).astype(np.float32)
+        assert np.array_equal(hs.astype(np.float64) / 2.0 ** e, hid)  # the scaling is exact
+        say("lmhead scaled 2 **", e)
+        got = _run(mk, torch, Wd, hs, None, drafts)
+        for a, b in zip(got, base):
+            assert np.array_equal(a, b), e

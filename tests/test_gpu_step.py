@@ -139,7 +139,7 @@ def full_stack():
     return {"layers": layers, "lm": lm, "gl": recipes.gdn_layers(bench.LAYERS)}
 
 
-@pytest.mark.parametrize("T,gs", [(12, [0, 3, 6, 9, 12]), (1, [0, 1])])
+@pytest.mark.parametrize("T,gs", [(12, [0, 3, 6, 9, 12]), (1, [0, 1]), (5, [0, 5])])
 def test_decode_step_full_size(full_stack, T, gs):
     torch = need_gpu()
     import bench
@@ -173,14 +173,17 @@ def test_decode_step_full_size(full_stack, T, gs):
     tr = to_np(trace)
     assert np.array_equal(to_np(xd), tr[L - 1])
     assert np.array_equal(to_np(am), amp)
-    # layers teacher-forced at sampled depths
-    for l in (0, 21, 42, L - 1):
-        Wl = {m: recipes.stack_weight(l, m) for m in MATS}
+    # layers teacher-forced: every layer at T = 12 (the benchmark's rows),
+    # sampled depths at T = 1 and 5
+    bufs = {}
+    for l in (range(L) if T == 12 else (0, 21, 42, L - 1)):
+        for m in MATS:
+            bufs[m] = recipes.stack_weight(l, m, out=bufs.get(m))
         prev = x if l == 0 else tr[l - 1]
-        e = rel_err(tr[l], oracle.layer(prev, Wl))
+        e = rel_err(tr[l], oracle.layer(prev, bufs))
         say("layer", l, "err", e)
         assert e <= FP32_TOL, (l, e)
-        del Wl
+    del bufs
     # final RMSNorm + lm_head argmax over the full vocabulary, verification
     _check_head(recipes.stack_lm_head(), tr[L - 1], to_np(am), na, tok, gs, drafts[:T - G])
     # Gated DeltaNet, sampled heads of every agent: outputs and committed state
@@ -200,3 +203,65 @@ def test_decode_step_full_size(full_stack, T, gs):
             assert rel_err(S1[hh:hh + 1], Sref) <= FP32_TOL, (a, hh)
     del st, dry, agents
     torch.cuda.empty_cache()
+
+
+def test_decode_step_workspace_bound_to_its_stack():
+    """Two stacks that share one workspace each get their own results (the
+    tables are uploaded again when the other stack ran last); a workspace
+    that another call overwrote is refused (MK_ERR_WORKSPACE, nothing runs)
+    and the next call runs normally."""
+    torch = need_gpu()
+    mk = _mk()
+    L, H, P, F, V, T = 2, 512, 1024, 768, 1000, 5
+    gs = [0, T]
+    stA, _, _, _, _, _ = small_stack(mk, 41, L, H, P, F, V, 1, gdn=False)
+    stB, _, _, _, _, _ = small_stack(mk, 42, L, H, P, F, V, 1, gdn=False)
+    drafts = to_dev(np.array([1, 2, 3, 4], np.int32))
+    x = synth.normal_f32(41, 10000, 0, T * H).reshape(T, H)
+
+    def run(st, ws):
+        xd = to_dev(x)
+        tr = torch.empty(L, T, H, dtype=torch.float32, device="cuda")
+        tok, na = mk.mk_decode_step(st, xd, gs, drafts, trace=tr, ws=ws)
+        return to_np(tr), tok, na
+
+    refA = run(stA, stA.workspace(T))
+    refB = run(stB, stB.workspace(T))
+    assert not np.array_equal(refA[0], refB[0])
+    shared = mk.workspace(max(stA.workspace_bytes(T), stB.workspace_bytes(T)))
+    for st, ref in ((stA, refA), (stB, refB), (stA, refA), (stA, refA), (stB, refB)):
+        say("shared workspace", "A" if st is stA else "B")
+        got = run(st, shared)
+        assert all(np.array_equal(g, r) for g, r in zip(got, ref))
+    shared.zero_()  # another call wrote the workspace
+    with pytest.raises(mk.MkError) as ei:
+        run(stB, shared)
+    assert ei.value.status == mk.MK_ERR_WORKSPACE
+    got = run(stB, shared)
+    assert all(np.array_equal(g, r) for g, r in zip(got, refB))
+
+
+def test_decode_step_accept_length_out_of_range():
+    """An agent state whose accept length is outside 0..T_max-1 is reported
+    (MK_ERR_RANGE) and that agent replays nothing."""
+    torch = need_gpu()
+    mk = _mk()
+    L, H, P, F, V, T = 4, 512, 1024, 768, 1000, 6
+    gs = [0, 3, 6]
+    st, _, _, _, S0, nh = small_stack(mk, 43, L, H, P, F, V, 2)
+    x = synth.normal_f32(43, 10000, 0, T * H).reshape(T, H)
+    inp = synth.gdn_step_inputs(43, 20000, T, nh, 128, 128)
+    gin = {k: to_dev(inp[k]) for k in ("q", "k", "v", "g", "beta")}
+    go = torch.empty(T, nh, 128, dtype=torch.float32, device="cuda")
+    drafts = to_dev(np.array([1, 2, 3, 4], np.int32))
+    st.agents[1].n_acc[0] = 9
+    say("decode accept out of range")
+    with pytest.raises(mk.MkError) as ei:
+        mk.mk_decode_step(st, to_dev(x), gs, drafts, gdn=gin, gdn_o=go)
+    assert ei.value.status == mk.MK_ERR_RANGE
+    assert mk.mk_deltanet_status(st.agents[1]) == mk.MK_ERR_RANGE
+    assert mk.mk_deltanet_status(st.agents[0]) == mk.MK_OK
+    # agent 1 replayed nothing: its outputs are those of its rows on S0
+    og = to_np(go)
+    _, o_ref = oracle.gdn_step(S0[1], inp["q"][3:], inp["k"][3:], inp["v"][3:], inp["g"][3:], inp["beta"][3:], 0)
+    assert rel_err(og[3:], o_ref) <= FP32_TOL
