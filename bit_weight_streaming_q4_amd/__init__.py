@@ -72,6 +72,7 @@ def lib():
     L.mk_qgemv_rows_workspace.restype = sz
     L.mk_qgemv_rows.argtypes = [ctypes.POINTER(mk_q4k), P, i32, P, P, sz, P]
     L.mk_qgemv_rows_ex.argtypes = [ctypes.POINTER(mk_q4k), P, i32, P, i32, P, sz, P]
+    L.mk_qgemv_rows_noalloc.argtypes = [ctypes.POINTER(mk_q4k), P, i32, P, i32, P]
     L.mk_ffn_rows_workspace.argtypes = [i32, i32, i32]
     L.mk_ffn_rows_workspace.restype = sz
     L.mk_ffn_rows.argtypes = [ctypes.POINTER(mk_q4k)] * 3 + [P, i32, P, P, P, sz, P]
@@ -202,6 +203,14 @@ def mk_qgemv_rows(W: Q4K, x, y, ws=None, path: int = MK_PATH_AUTO, stream=None):
         ws = workspace(mk_qgemv_rows_workspace(T, W.n_out, W.n_in), x.device)
     _check(lib().mk_qgemv_rows_ex(ctypes.byref(W.c), _ptr(x), T, _ptr(y), path, _ptr(ws), ws.numel(),
                                   _stream(stream)), "mk_qgemv_rows")
+
+
+def mk_qgemv_rows_noalloc(W: Q4K, x, y, path: int = MK_PATH_AUTO, stream=None):
+    """mk_qgemv_rows with its workspace in the library's static per-GPU
+    scratch array (allocates nothing; calls on one GPU must not overlap)."""
+    T = x.shape[0]
+    _check(lib().mk_qgemv_rows_noalloc(ctypes.byref(W.c), _ptr(x), T, _ptr(y), path, _stream(stream)),
+           "mk_qgemv_rows_noalloc")
 
 
 def mk_ffn_rows_workspace(T: int, H: int, F: int) -> int:

@@ -37,6 +37,12 @@ int mk::set_error(int status, const char* fmt, ...) {
   return status;
 }
 
+// Workspace of mk_qgemv_rows_noalloc: one array per GPU, held until the
+// process ends.  Host code never uses this name as an address (in host code
+// it is only a stand-in for the symbol); scratch_device_ptr() returns the
+// device address that hipGetSymbolAddress gives for the current device.
+__device__ __attribute__((aligned(256))) uint8_t scratch[MK_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 int ok() {
@@ -65,6 +71,27 @@ int device_cu_count() {
 }
 
 hipStream_t S(void* s) { return (hipStream_t)s; }
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch;  // device address of `scratch` per device (null = not looked up)
+
+// The current device's copy of `scratch`, looked up once per device with
+// that device current.
+int scratch_device_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MK_ERR_DEVICE, "no current HIP device");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((int)g_scratch.size() <= dev) g_scratch.resize(dev + 1, nullptr);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MK_ERR_DEVICE, "scratch array address on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MK_OK;
+}
 
 int launch_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(MK_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
@@ -138,6 +165,9 @@ int mk_init(int device) {
   if (device < 0 || device >= n) return fail(MK_ERR_RANGE, "device %d outside 0..%d", device, n - 1);
   if (hipSetDevice(device) != hipSuccess) return fail(MK_ERR_DEVICE, "hipSetDevice(%d) failed", device);
   device_cu_count();
+  void* p;
+  int r;
+  if ((r = scratch_device_ptr(&p))) return r;
   return ok();
 }
 
@@ -269,6 +299,18 @@ int mk_qgemv_rows_ex(const mk_q4k* W, const float* x, int32_t T, float* y, int32
 
 int mk_qgemv_rows(const mk_q4k* W, const float* x, int32_t T, float* y, void* ws, size_t ws_bytes, void* stream) {
   return mk_qgemv_rows_ex(W, x, T, y, MK_PATH_AUTO, ws, ws_bytes, stream);
+}
+
+int mk_qgemv_rows_noalloc(const mk_q4k* W, const float* x, int32_t T, float* y, int32_t path, void* stream) {
+  int r;
+  if ((r = check_q4k(W, "W")) || (r = check_T(T))) return r;
+  const size_t need = mk_qgemv_rows_workspace(T, W->n_out, W->n_in);
+  if (need > MK_NOALLOC_SCRATCH_BYTES)
+    return fail(MK_ERR_WORKSPACE, "noalloc: a %d x %d GEMV at T = %d needs %zu bytes of workspace, above the %u-byte "
+                "scratch array", W->n_out, W->n_in, T, need, (unsigned)MK_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((r = scratch_device_ptr(&ws))) return r;
+  return mk_qgemv_rows_ex(W, x, T, y, path, ws, MK_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // ------------------------------------------------------------------ FFN

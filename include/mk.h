@@ -128,6 +128,21 @@ enum { MK_PATH_AUTO = 0, MK_PATH_DOT4 = 1, MK_PATH_MFMA = 2 };
 int mk_qgemv_rows_ex(const mk_q4k* W, const float* x, int32_t T, float* y, int32_t path, void* ws,
                      size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * T-row GEMV as mk_qgemv_rows_ex (same engines, bit-identical results), with
+ * its workspace in a static device array of MK_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) that each GPU the library runs on holds until the process ends.
+ * A call whose workspace (mk_qgemv_rows_workspace) would exceed the array
+ * returns MK_ERR_WORKSPACE and enqueues nothing; every shape of the 27B-class
+ * stack fits at any T.  Allocates nothing: no hipMalloc or hipFree, no
+ * allocating library call.  Every call on one GPU shares that GPU's array,
+ * which keeps the last call's contents (the launches clear the counters that
+ * must start at zero themselves, without a memset): calls that overlap on one
+ * GPU (several streams or threads) race. */
+#define MK_NOALLOC_SCRATCH_BYTES (16u << 20)
+int mk_qgemv_rows_noalloc(const mk_q4k* W, const float* x, int32_t T, float* y, int32_t path, void* stream);
+
 /* ------------------------------------------------------------------ FFN block */
 /* y = W_down . q8(SiLU(W_gate . q8(x)) * (W_up . q8(x))); gate, up are
  * F x H, down is H x F.  x, y [T][H] fp32; h_out (optional, NULL to skip)
