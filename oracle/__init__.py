@@ -17,6 +17,9 @@ the order the pages give them.  Each function names the step it follows:
   C6 lmhead/verify  logits, argmax, accepted-prefix length, emitted tokens
   C7 gdn_step       gated delta rule with commit through the accepted row
   C8 decode_step    composition of one whole step
+  F1 topk_rows      the k largest logits of each row (sampling mode)
+  F2 sample_weights target weights softmax(top-k / temperature)
+  F3 sample_verify  sampling-mode verification that keeps the target distribution
   A1 attn_decode    full-attention decode of T rows over an fp16 KV cache
   A2 attn_decode_q8 the same over a q8_0 KV cache
 
@@ -299,6 +302,102 @@ def verify(argmax, group_start, drafts):
     tokens = np.full(len(argmax), -1, np.int32)
     _load().orc_verify(_p(argmax), _p(gs), G, _p(drafts), _p(n_acc), _p(tokens))
     return n_acc, tokens
+
+
+def topk_rows(logits, k):
+    """F1: per row, the k largest logits (NaN never counts), ties broken
+    towards the lower vocabulary index; returns (idx, val) [T][k'] with
+    k' = min(k, number of non-NaN logits), each row ordered by ascending
+    vocabulary index (the order the sampler walks)."""
+    lg = np.atleast_2d(np.asarray(logits, np.float64))
+    T, V = lg.shape
+    out_i, out_v = [], []
+    for t in range(T):
+        ok = np.flatnonzero(~np.isnan(lg[t]))
+        order = ok[np.lexsort((ok, -lg[t, ok]))][:k]  # value descending, then index ascending
+        sel = np.sort(order)
+        out_i.append(sel.astype(np.int32))
+        out_v.append(lg[t, sel])
+    kk = min(len(a) for a in out_i)
+    return np.stack([a[:kk] for a in out_i]), np.stack([a[:kk] for a in out_v])
+
+
+def sample_weights(vals, temperature):
+    """F2: unnormalised target weights of one row's top-k candidates,
+    exp((l - max l) / temperature), in float64."""
+    v = np.asarray(vals, np.float64)
+    return np.exp((v - v.max()) / float(temperature))
+
+
+def _inverse_cdf(w, u, skip=None):
+    """Index j of the candidate picked by u in [0, 1): walk the candidates in
+    the given (ascending vocabulary) order, the first whose cumulative
+    weight exceeds u * total; candidate `skip` has weight 0.  Also returns
+    the distance of u * total from the nearest cumulative boundary, relative
+    to the total (for the comparison carve-out)."""
+    w = np.array(w, np.float64)
+    if skip is not None:
+        w[skip] = 0.0
+    tot = w.sum()
+    x = u * tot
+    c = np.cumsum(w)
+    j = int(np.searchsorted(c, x, side="right"))
+    j = min(j, len(w) - 1)
+    while w[j] == 0.0 and j > 0:  # past the end by rounding: the last candidate with weight
+        j -= 1
+    gap = float(np.min(np.abs(c - x)) / tot) if tot > 0 else 0.0
+    return j, gap
+
+
+def sample_verify(topk_idx, topk_val, group_start, drafts, temperature, u_acc, u_samp):
+    """F3: sampling-mode verification of drafted rows, keeping the target
+    distribution (pulse-3k2, "UPDATE: ... KL divergence 0.0009 vs llama.cpp",
+    "Decode accuracy vs llama.cpp": sampling keeps the same distribution as
+    without drafts; top_k capped at 32 per the single-stream and 4-agent
+    pages' limits).  The rule (a reading: the pages give none) is
+    speculative sampling with each draft a deterministic proposal.  Row i of
+    a group has the target p_i = softmax(top-k logits / temperature).  For
+    i = 0, 1, ...: draft d_i is accepted when u_acc[i] < p_i(d_i)
+    (p_i(d) = 0 for a token outside the top-k or outside [0, V)); at the
+    first rejection the row emits a sample of p_i with d_i removed and
+    renormalised (u_samp[i], inverse CDF over the candidates in ascending
+    vocabulary order) and the group stops; if every draft is accepted, the
+    last row emits a sample of p (its bonus token).  Each emitted token is
+    then distributed exactly as p_i: P(d) = p(d) + 0, and for x != d,
+    (1 - p(d)) p(x) / (1 - p(d)) = p(x).
+    Returns n_acc [G], tokens [T] (-1 past the emitted ones) and, per row, the
+    decision margin (distance of u from its decision boundary, relative)."""
+    gs = list(group_start)
+    G = len(gs) - 1
+    T = gs[-1]
+    drafts = np.asarray(drafts, np.int64)
+    n_acc = np.zeros(G, np.int32)
+    tokens = np.full(T, -1, np.int32)
+    margin = np.full(T, np.inf)
+    for g in range(G):
+        r, n = gs[g], gs[g + 1] - gs[g]
+        a = 0
+        while True:
+            t = r + a
+            w = sample_weights(topk_val[t], temperature)
+            tot = w.sum()
+            if a < n - 1:
+                d = int(drafts[r - g + a])
+                hit = np.flatnonzero(topk_idx[t] == d)
+                pd = w[hit[0]] / tot if len(hit) else 0.0
+                margin[t] = abs(u_acc[t] - pd)
+                if u_acc[t] < pd:
+                    tokens[t] = d
+                    a += 1
+                    continue
+                j, gap = _inverse_cdf(w, u_samp[t], skip=hit[0] if len(hit) else None)
+            else:
+                j, gap = _inverse_cdf(w, u_samp[t])
+            margin[t] = min(margin[t], gap)
+            tokens[t] = int(topk_idx[t][j])
+            break
+        n_acc[g] = a
+    return n_acc, tokens, margin
 
 
 def gdn_rows(S, q, k, v, g, beta, literal=False):

@@ -700,3 +700,111 @@ def test_attn_q8_equals_fp16_path_on_exact_values(orc):
     o8 = orc.attn_decode_q8(a["q"], a["gate"], a["k8"], a["ks"], a["v8"], a["vs"], a["ctx"], a["group_start"])
     o16 = orc.attn_decode(a["q"], a["gate"], k16, v16, a["ctx"], a["group_start"])
     assert np.array_equal(o8, o16)
+
+
+# ----------------------------------------------------------------- F1-F3 sampling-mode verification
+def test_topk_rows_vs_brute_force_with_ties_and_nan(orc):
+    rng = np.random.default_rng(40)
+    lg = np.round(rng.standard_normal((4, 300)) * 3, 1)  # rounding plants many exact ties
+    lg[1, 17] = np.nan
+    lg[1, 200] = np.nan
+    lg[2, :] = 0.0  # every logit tied
+    for k in (1, 5, 32):
+        idx, val = orc.topk_rows(lg, k)
+        for t in range(4):
+            cand = [v for v in range(300) if not np.isnan(lg[t, v])]
+            best = sorted(cand, key=lambda v: (-lg[t, v], v))[:k]
+            assert list(idx[t]) == sorted(best)
+            assert np.array_equal(val[t], lg[t, sorted(best)])
+    assert list(orc.topk_rows(lg, 3)[0][2]) == [0, 1, 2]  # all tied: lowest indices
+
+
+def _row(seed, k=6):
+    rng = np.random.default_rng(seed)
+    idx = np.sort(rng.choice(1000, size=k, replace=False)).astype(np.int32)
+    val = rng.standard_normal(k) * 2.0
+    return idx, val
+
+
+def test_sample_verify_keeps_the_target_distribution_exactly(orc):
+    # One row with a draft: integrate over u_acc and u_samp.  P(emit d) =
+    # p(d); for x != d, P(emit x) = (1 - p(d)) * (length of the u_samp
+    # interval that picks x with d removed); that must equal p(x).
+    idx, val = _row(41)
+    tau = 0.6
+    w = orc.sample_weights(val, tau)
+    p = w / w.sum()
+    grid = (np.arange(40000) + 0.5) / 40000
+    for d in (int(idx[np.argmax(p)]), int(idx[np.argmin(p)]), 999999, -3):
+        j = np.flatnonzero(idx == d)
+        pd = p[j[0]] if len(j) else 0.0
+        picks = np.zeros(len(idx))
+        for u in grid:
+            picks[orc._inverse_cdf(w, u, skip=j[0] if len(j) else None)[0]] += 1
+        emit = (1 - pd) * picks / len(grid)
+        if len(j):
+            assert picks[j[0]] == 0
+            emit[j[0]] += pd
+        assert np.abs(emit - p).max() < 1e-4, d
+        # the decision itself: accept exactly when u_acc < p(d)
+        for ua in (0.0, pd * 0.999, pd, min(pd * 1.001 + 1e-9, 0.999)):
+            n, tok, _ = orc.sample_verify(idx[None].repeat(2, 0), val[None].repeat(2, 0), [0, 2], [d], tau,
+                                          np.array([ua, 0.5]), np.array([0.3, 0.3]))
+            assert (n[0] == 1) == (ua < pd)
+
+
+def test_sample_verify_chi_square_over_a_group(orc):
+    # T = 3 rows, 2 drafts from a proposal that differs from the target; the
+    # first emitted token follows p_0, and the second (when d_0 was accepted)
+    # follows p_1.  A sampler that does not remove the rejected draft fails.
+    rows = [_row(50 + i, k=8) for i in range(3)]
+    idx = np.stack([r[0] for r in rows])
+    val = np.stack([r[1] for r in rows])
+    tau = 0.6
+    p = [orc.sample_weights(val[i], tau) / orc.sample_weights(val[i], tau).sum() for i in range(3)]
+    rng = np.random.default_rng(51)
+    trials = 6000
+    first, second = {}, {}
+    n_first_acc = 0
+    bad_first = {}
+    for tr in range(trials):
+        # drafts: the most likely token of the row with probability 0.5, else a uniform candidate
+        dr = [int(idx[i][np.argmax(p[i])]) if rng.random() < 0.5 else int(rng.choice(idx[i])) for i in range(2)]
+        ua, us = rng.random(3), rng.random(3)
+        n, tok, _ = orc.sample_verify(idx, val, [0, 3], dr, tau, ua, us)
+        first[tok[0]] = first.get(tok[0], 0) + 1
+        if n[0] >= 1:
+            n_first_acc += 1
+            second[tok[1]] = second.get(tok[1], 0) + 1
+        # planted mistake: on rejection sample p without removing the draft
+        pd = p[0][list(idx[0]).index(dr[0])]
+        if ua[0] < pd:
+            b = dr[0]
+        else:
+            b = int(idx[0][orc._inverse_cdf(orc.sample_weights(val[0], tau), us[0])[0]])
+        bad_first[b] = bad_first.get(b, 0) + 1
+
+    def chi2(counts, i, n):
+        obs = np.array([counts.get(int(v), 0) for v in idx[i]], np.float64)
+        return float((((obs - n * p[i]) ** 2) / (n * p[i])).sum())
+
+    crit = 24.3  # 7 dof, p = 0.001
+    assert chi2(first, 0, trials) < crit
+    assert chi2(second, 1, n_first_acc) < crit
+    assert chi2(bad_first, 0, trials) > 3 * crit
+
+
+def test_sample_verify_reduces_to_greedy(orc):
+    # top_k = 1, or a temperature near 0, makes every target one-hot on the
+    # argmax: the outcome is exactly the greedy verification (C6)
+    rng = np.random.default_rng(52)
+    lg = rng.standard_normal((6, 400)) * 3
+    am = np.argmax(lg, 1).astype(np.int32)
+    gs = [0, 3, 6]
+    drafts = np.array([am[0], am[1], am[3], (am[4] + 1) % 400], np.int32)
+    n_ref, t_ref = orc.verify(am, gs, drafts)
+    for k, tau in ((1, 0.6), (32, 1e-4)):
+        idx, val = orc.topk_rows(lg, k)
+        for trial in range(20):
+            n, tok, _ = orc.sample_verify(idx, val, gs, drafts, tau, rng.random(6), rng.random(6))
+            assert np.array_equal(n, n_ref) and np.array_equal(tok, t_ref), (k, tau)
