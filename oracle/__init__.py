@@ -306,27 +306,30 @@ def verify(argmax, group_start, drafts):
 
 def topk_rows(logits, k):
     """F1: per row, the k largest logits (NaN never counts), ties broken
-    towards the lower vocabulary index; returns (idx, val) [T][k'] with
-    k' = min(k, number of non-NaN logits), each row ordered by ascending
-    vocabulary index (the order the sampler walks)."""
+    towards the lower vocabulary index; returns (idx, val) [T][k], each row's
+    candidates in ascending vocabulary order (the order the sampler walks),
+    padded with idx -1 and val -inf when a row has fewer than k non-NaN
+    logits."""
     lg = np.atleast_2d(np.asarray(logits, np.float64))
     T, V = lg.shape
-    out_i, out_v = [], []
+    out_i = np.full((T, k), -1, np.int32)
+    out_v = np.full((T, k), -np.inf)
     for t in range(T):
         ok = np.flatnonzero(~np.isnan(lg[t]))
         order = ok[np.lexsort((ok, -lg[t, ok]))][:k]  # value descending, then index ascending
         sel = np.sort(order)
-        out_i.append(sel.astype(np.int32))
-        out_v.append(lg[t, sel])
-    kk = min(len(a) for a in out_i)
-    return np.stack([a[:kk] for a in out_i]), np.stack([a[:kk] for a in out_v])
+        out_i[t, :len(sel)] = sel
+        out_v[t, :len(sel)] = lg[t, sel]
+    return out_i, out_v
 
 
 def sample_weights(vals, temperature):
     """F2: unnormalised target weights of one row's top-k candidates,
-    exp((l - max l) / temperature), in float64."""
+    exp((l - max l) / temperature), in float64 (padding slots, -inf, weigh 0)."""
     v = np.asarray(vals, np.float64)
-    return np.exp((v - v.max()) / float(temperature))
+    if not np.isfinite(v).any():
+        return np.zeros_like(v)
+    return np.exp((v - v[np.isfinite(v)].max()) / float(temperature))
 
 
 def _inverse_cdf(w, u, skip=None):
@@ -381,9 +384,13 @@ def sample_verify(topk_idx, topk_val, group_start, drafts, temperature, u_acc, u
             t = r + a
             w = sample_weights(topk_val[t], temperature)
             tot = w.sum()
+            if tot == 0.0:  # no candidate (every logit NaN): the draft is rejected and nothing is emitted
+                tokens[t] = -1
+                margin[t] = np.inf
+                break
             if a < n - 1:
                 d = int(drafts[r - g + a])
-                hit = np.flatnonzero(topk_idx[t] == d)
+                hit = np.flatnonzero((topk_idx[t] == d) & (d >= 0))
                 pd = w[hit[0]] / tot if len(hit) else 0.0
                 margin[t] = abs(u_acc[t] - pd)
                 if u_acc[t] < pd:

@@ -717,6 +717,16 @@ def test_topk_rows_vs_brute_force_with_ties_and_nan(orc):
             assert list(idx[t]) == sorted(best)
             assert np.array_equal(val[t], lg[t, sorted(best)])
     assert list(orc.topk_rows(lg, 3)[0][2]) == [0, 1, 2]  # all tied: lowest indices
+    # a row with fewer non-NaN logits than k is padded; an all-NaN row has no candidate
+    lg2 = np.full((2, 10), np.nan)
+    lg2[0, [3, 7]] = [1.0, 2.0]
+    idx, val = orc.topk_rows(lg2, 4)
+    assert list(idx[0]) == [3, 7, -1, -1] and list(idx[1]) == [-1] * 4
+    assert np.isneginf(val[1]).all()
+    n, tok, _ = orc.sample_verify(idx, val, [0, 1, 2], [], 0.6, np.zeros(2), np.full(2, 0.99))
+    assert list(tok) == [7, -1] and list(n) == [0, 0]
+    n, tok, _ = orc.sample_verify(idx[::-1].copy(), val[::-1].copy(), [0, 2], [3], 0.6, np.zeros(2), np.zeros(2))
+    assert list(tok) == [-1, -1] and n[0] == 0  # the all-NaN row accepts nothing and emits nothing
 
 
 def _row(seed, k=6):
