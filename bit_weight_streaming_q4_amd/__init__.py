@@ -79,6 +79,9 @@ def lib():
     L.mk_lmhead_verify_workspace.argtypes = [i32, i32, i32]
     L.mk_lmhead_verify_workspace.restype = sz
     L.mk_lmhead_verify.argtypes = [P, i32, i32, P, i32, P, i32, P, P, P, P, P, sz, P]
+    L.mk_lmhead_sample_workspace.argtypes = [i32, i32, i32]
+    L.mk_lmhead_sample_workspace.restype = sz
+    L.mk_lmhead_sample.argtypes = [P, i32, i32, P, i32, P, i32, P, i32, ctypes.c_float, P, P, P, P, P, P, P, sz, P]
     L.mk_deltanet_step.argtypes = [ctypes.POINTER(mk_deltanet), i32, P, P, P, P, P, i32, P, P]
     L.mk_deltanet_commit.argtypes = [ctypes.POINTER(mk_deltanet), P]
     L.mk_deltanet_status.argtypes = [ctypes.POINTER(mk_deltanet), P]
@@ -243,6 +246,30 @@ def mk_lmhead_verify(W16, hid, group_start, drafts, argmax, n_acc, tokens, ws=No
         ws = workspace(mk_lmhead_verify_workspace(V, H, T), hid.device)
     _check(lib().mk_lmhead_verify(_ptr(W16), V, H, _ptr(hid), T, gs, G, _ptr(drafts), _ptr(argmax), _ptr(n_acc),
                                   _ptr(tokens), _ptr(ws), ws.numel(), _stream(stream)), "mk_lmhead_verify")
+
+
+def mk_lmhead_sample_workspace(V: int, H: int, T: int) -> int:
+    return int(lib().mk_lmhead_sample_workspace(V, H, T))
+
+
+def mk_lmhead_sample(W16, hid, group_start, drafts, top_k, temperature, u_acc, u_samp, n_acc, tokens,
+                     topk_idx=None, topk_logit=None, ws=None, V=None, stream=None):
+    """Sampling-mode verification: u_acc, u_samp fp32 [T] device tensors of
+    the caller's uniforms; topk_idx int32 [T][32] / topk_logit fp32 [T][32]
+    optional outputs."""
+    H = W16.shape[1]
+    V = W16.shape[0] if V is None else V
+    T = hid.shape[0]
+    if group_start is None:
+        gs, G = None, 1
+    else:
+        gs_np = np.ascontiguousarray(group_start, np.int32)
+        gs, G = gs_np.ctypes.data, len(gs_np) - 1
+    if ws is None:
+        ws = workspace(mk_lmhead_sample_workspace(V, H, T), hid.device)
+    _check(lib().mk_lmhead_sample(_ptr(W16), V, H, _ptr(hid), T, gs, G, _ptr(drafts), int(top_k), float(temperature),
+                                  _ptr(u_acc), _ptr(u_samp), _ptr(topk_idx), _ptr(topk_logit), _ptr(n_acc),
+                                  _ptr(tokens), _ptr(ws), ws.numel(), _stream(stream)), "mk_lmhead_sample")
 
 
 def _attn_groups(T, ctx, group_start):

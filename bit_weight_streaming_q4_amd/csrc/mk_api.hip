@@ -403,6 +403,67 @@ int mk_lmhead_verify(const uint16_t* W_f16, int32_t V, int32_t H, const float* h
                        "lm_head");
 }
 
+// ------------------------------------------------------------------ sampling-mode verify
+// Workspace: the lm_head stream's (ticket, fragments, block winners), the
+// rows' prescale exponents, every logit [T][V], the candidates [T][32] x 2.
+size_t mk_lmhead_sample_workspace(int32_t V, int32_t H, int32_t T) {
+  if (V <= 0 || H <= 0 || H % 64 || T < 1 || T > MK_T_MAX) return 0;
+  return mk::lm_workspace_bytes(V, H) + 256 + align256((size_t)T * V * 4) + 2 * align256((size_t)T * mk::kTopKMax * 4);
+}
+
+int mk_lmhead_sample(const uint16_t* W_f16, int32_t V, int32_t H, const float* hid, int32_t T,
+                     const int32_t* h_group_start, int32_t G, const int32_t* drafts, int32_t top_k, float temperature,
+                     const float* u_acc, const float* u_samp, int32_t* topk_idx, float* topk_logit, int32_t* n_acc,
+                     int32_t* tokens, void* ws, size_t ws_bytes, void* stream) {
+  int r;
+  if ((r = check_T(T))) return r;
+  if (V <= 0 || H <= 0 || H % 64) return fail(MK_ERR_SHAPE, "sample: V = %d, H = %d (H % 64 == 0)", V, H);
+  if (top_k < 1 || top_k > mk::kTopKMax) return fail(MK_ERR_RANGE, "sample: top_k = %d outside 1..%d", top_k, mk::kTopKMax);
+  if (!(temperature > 0.0f) || !(temperature < 3.0e38f))
+    return fail(MK_ERR_RANGE, "sample: temperature %g is not a positive finite value", (double)temperature);
+  if ((r = check_ptr(W_f16, "W")) || (r = check_ptr(hid, "hid")) || (r = check_ptr(u_acc, "u_acc", 4)) ||
+      (r = check_ptr(u_samp, "u_samp", 4)) || (r = check_ptr(n_acc, "n_acc", 4)) || (r = check_ptr(tokens, "tokens", 4)))
+    return r;
+  if (topk_idx && (r = check_ptr(topk_idx, "topk_idx", 4))) return r;
+  if (topk_logit && (r = check_ptr(topk_logit, "topk_logit", 4))) return r;
+  std::vector<int32_t> gs;
+  if ((r = check_groups(h_group_start, G, T, gs))) return r;
+  if (T > G && (r = check_ptr(drafts, "drafts", 4))) return r;
+  const size_t need = mk_lmhead_sample_workspace(V, H, T);
+  if (!ws || ws_bytes < need) return fail(MK_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if ((r = check_ptr(ws, "workspace", 256))) return r;
+  uint8_t* p = (uint8_t*)ws;
+  void* lm_ws = p;
+  p += mk::lm_workspace_bytes(V, H);
+  int* row_exp = (int*)p;
+  p += 256;
+  float* logits = (float*)p;
+  p += align256((size_t)T * V * 4);
+  int32_t* cidx = topk_idx ? topk_idx : (int32_t*)p;
+  p += align256((size_t)T * mk::kTopKMax * 4);
+  float* cval = topk_logit ? topk_logit : (float*)p;
+  hipError_t e = mk::launch_lm_stream(W_f16, V, H, hid, T, gs.data(), G, drafts, nullptr, nullptr, nullptr, lm_ws,
+                                      device_cu_count(), S(stream), logits, row_exp);
+  if (e != hipSuccess) return launch_status(e, "sample: lm_head");
+  mk::SampleArgs a = {};
+  a.logits = logits;
+  a.row_exp = row_exp;
+  a.V = V;
+  a.T = T;
+  a.k = top_k;
+  a.cand_idx = cidx;
+  a.cand_val = cval;
+  a.G = G;
+  for (int i = 0; i <= MK_LM_MAX_G; ++i) a.gs[i] = i <= G ? gs[i] : T;
+  a.drafts = drafts;
+  a.temperature = temperature;
+  a.u_acc = u_acc;
+  a.u_samp = u_samp;
+  a.n_acc = n_acc;
+  a.tokens = tokens;
+  return launch_status(mk::launch_sample(a, S(stream)), "sample");
+}
+
 // ------------------------------------------------------------------ Gated DeltaNet
 static int check_dn(const mk_deltanet* st) {
   int r;

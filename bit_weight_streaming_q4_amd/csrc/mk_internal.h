@@ -58,6 +58,29 @@ size_t lm_workspace_bytes(int V, int H);
 hipError_t launch_lmhead(const uint16_t* W, int V, int H, const float* hid, int T, const int32_t* gs, int G,
                          const int32_t* drafts, int32_t* argmax, int32_t* n_acc, int32_t* tokens, void* ws,
                          int cu_count, hipStream_t st);
+hipError_t launch_lm_stream(const uint16_t* W, int V, int H, const float* hid, int T, const int32_t* gs, int G,
+                            const int32_t* drafts, int32_t* argmax, int32_t* n_acc, int32_t* tokens, void* ws,
+                            int cu_count, hipStream_t st, float* logits, int* row_exp);
+
+// Sampling-mode verification (mk_sample.hip): top-k of each row's logits,
+// then the speculative-sampling accept/resample pass.
+constexpr int kTopKMax = 32;
+struct SampleArgs {
+  const float* logits;   // [T][V], row t scaled by 2^row_exp[t]
+  const int* row_exp;    // [16]
+  int V, T, k;
+  int32_t* cand_idx;     // [T][32], ascending vocabulary index, -1 past the row's candidates
+  float* cand_val;       // [T][32], the logits (unscaled), -inf past the candidates
+  int G;
+  int gs[MK_LM_MAX_G + 1];
+  const int32_t* drafts;
+  float temperature;
+  const float* u_acc;    // [T]
+  const float* u_samp;   // [T]
+  int32_t* n_acc;        // [G]
+  int32_t* tokens;       // [T]
+};
+hipError_t launch_sample(const SampleArgs& a, hipStream_t st);
 
 // Gated DeltaNet: one wave per half head (dk = dv = 128).
 struct GdnArgs {

@@ -23,6 +23,8 @@ struct LmStream {
   float* val;        // [gridDim.x][16] per-block winners (value)
   int* idx;          // [gridDim.x][16] per-block winners (vocabulary index)
   unsigned* ticket;  // arrival counter; zero when the launch starts
+  float* logits;     // optional [logits_T][V] output of every logit (null: none)
+  int logits_T;      // rows of `logits` (rows t < logits_T are stored)
 };
 
 // One 64-wide hidden chunk of 64 vocabulary rows: the weight fragments of
@@ -136,6 +138,7 @@ __device__ __forceinline__ bool lm_stream(const LmStream& a, float (*red)[64][16
         float xv = red[0][r][t_own];
 #pragma unroll
         for (int q = 1; q < NW; ++q) xv += red[q][r][t_own];
+        if (a.logits && t_own < a.logits_T) a.logits[(size_t)t_own * a.V + v] = xv;
         if (lm_better(xv, v, best, bidx)) {
           best = xv;
           bidx = v;
@@ -345,6 +348,7 @@ __device__ __forceinline__ bool lm_stream_staged(const LmStream& a, uint8_t* sta
       float xv = red[0][r][t_own];
 #pragma unroll
       for (int q = 1; q < NW; ++q) xv += red[q][r][t_own];
+      if (a.logits && t_own < a.logits_T) a.logits[(size_t)t_own * a.V + v] = xv;
       if (lm_better(xv, v, best, bidx)) {
         best = xv;
         bidx = v;

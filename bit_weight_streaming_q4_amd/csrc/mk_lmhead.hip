@@ -21,8 +21,11 @@ namespace mk {
 // scaling is exact and multiplies every logit of the row by the same 2^k,
 // so the argmax is unchanged; rows are accepted at any fp32 magnitude (a row
 // holding inf or only zeros is left unscaled).
+// row_exp (optional, [16]) receives each row's k, so that a caller that
+// needs the logits themselves can scale them back exactly by 2^-k.
 __global__ __launch_bounds__(256) void k_lm_prep(const float* __restrict__ hid, int T, int H,
-                                                 _Float16* __restrict__ frag, unsigned* __restrict__ ticket) {
+                                                 _Float16* __restrict__ frag, unsigned* __restrict__ ticket,
+                                                 int* __restrict__ row_exp) {
   __shared__ float wmax[4];
   const int t = blockIdx.x, tid = threadIdx.x;
   if (t == 0 && tid == 0) *ticket = 0u;  // the lm_head kernel's arrival counter
@@ -41,6 +44,7 @@ __global__ __launch_bounds__(256) void k_lm_prep(const float* __restrict__ hid, 
       k = 15 - e;
     }
   }
+  if (row_exp && tid == 0) row_exp[t] = k;
   for (int i = tid; i < H; i += 256) {
     const int c = i >> 6, r = i & 63, l = 16 * (r >> 4) + t, e = r & 15;
     const float x = t < T ? __builtin_ldexpf(row[i], k) : 0.0f;
@@ -60,6 +64,7 @@ struct LmArgs {
   int32_t* argmax;
   int32_t* n_acc;
   int32_t* tokens;
+  int verify;  // the last block writes argmax and runs the greedy accept compare
 };
 
 constexpr int kLmWaves = 8;
@@ -90,7 +95,7 @@ __device__ __forceinline__ void lm_verify(const LmArgs& a, const int* fin) {
 __global__ __launch_bounds__(64 * kLmWaves) void k_lmhead(LmArgs a) {
   __shared__ float red[kLmWaves][64][16];
   __shared__ int fin[16];
-  if (!lm_stream<kLmWaves>(a.s, red, fin)) return;
+  if (!lm_stream<kLmWaves>(a.s, red, fin) || !a.verify) return;
   lm_verify(a, fin);
 }
 
@@ -100,7 +105,7 @@ template <int NSEG>
 __global__ __launch_bounds__(512) void k_lmhead_staged(LmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t stages[4 * kLmStageBytes];
   __shared__ int fin[16];
-  if (!lm_stream_staged<4, NSEG>(a.s, stages, fin)) return;
+  if (!lm_stream_staged<4, NSEG>(a.s, stages, fin) || !a.verify) return;
   lm_verify(a, fin);
 }
 
@@ -127,6 +132,15 @@ int lm_nblocks(int V) { return (V + 63) / 64; }
 hipError_t launch_lmhead(const uint16_t* W, int V, int H, const float* hid, int T, const int32_t* gs, int G,
                          const int32_t* drafts, int32_t* argmax, int32_t* n_acc, int32_t* tokens, void* ws,
                          int cu_count, hipStream_t st) {
+  return launch_lm_stream(W, V, H, hid, T, gs, G, drafts, argmax, n_acc, tokens, ws, cu_count, st, nullptr, nullptr);
+}
+
+// The lm_head stream with the greedy verification (logits == null), or
+// writing every logit to logits [T][V] (scaled rows: logit * 2^row_exp[t])
+// without it.
+hipError_t launch_lm_stream(const uint16_t* W, int V, int H, const float* hid, int T, const int32_t* gs, int G,
+                            const int32_t* drafts, int32_t* argmax, int32_t* n_acc, int32_t* tokens, void* ws,
+                            int cu_count, hipStream_t st, float* logits, int* row_exp) {
   uint8_t* p = (uint8_t*)ws;
   uint32_t* ticket = (uint32_t*)p;
   p += 256;
@@ -136,7 +150,7 @@ hipError_t launch_lmhead(const uint16_t* W, int V, int H, const float* hid, int 
   float* pval = (float*)p;
   p += ((size_t)nblk * 16 * 4 + 255) / 256 * 256;
   int32_t* pidx = (int32_t*)p;
-  hipLaunchKernelGGL(k_lm_prep, dim3(16), dim3(256), 0, st, hid, T, H, frag, ticket);
+  hipLaunchKernelGGL(k_lm_prep, dim3(16), dim3(256), 0, st, hid, T, H, frag, ticket, row_exp);
   LmArgs a;
   a.s.W = W;
   a.s.frag = frag;
@@ -145,6 +159,9 @@ hipError_t launch_lmhead(const uint16_t* W, int V, int H, const float* hid, int 
   a.s.val = pval;
   a.s.idx = pidx;
   a.s.ticket = ticket;
+  a.s.logits = logits;
+  a.s.logits_T = logits ? T : 0;
+  a.verify = logits ? 0 : 1;
   a.T = T;
   a.G = G;
   for (int i = 0; i <= MK_LM_MAX_G; ++i) a.gs[i] = i <= G ? gs[i] : T;

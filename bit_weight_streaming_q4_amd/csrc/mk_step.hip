@@ -1655,6 +1655,8 @@ __device__ __forceinline__ void lm_phase(const StepArgs& a, uint8_t* ring) {
   ls.val = a.lm_val;
   ls.idx = a.lm_idx;
   ls.ticket = a.lm_ticket;
+  ls.logits = nullptr;
+  ls.logits_T = 0;
   static_assert(kWavesPerBlock == 8, "the staged stream runs on 8 waves");
   bool last;
   if (a.H == 5120)

@@ -181,6 +181,39 @@ int mk_lmhead_verify(const uint16_t* W_f16, int32_t V, int32_t H, const float* h
                      const int32_t* h_group_start, int32_t G, const int32_t* drafts, int32_t* argmax,
                      int32_t* n_acc, int32_t* tokens, void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------- sampling-mode verification */
+/* pulse-3k2, "UPDATE: ... KL divergence 0.0009 vs llama.cpp", section
+ * "Decode accuracy vs llama.cpp": with sampling, speculative decoding keeps
+ * the same distribution as without drafts; top_k is capped at 32
+ * (richland.au single-stream article, "Caveats"; 4-agent article, limits).
+ * The pages give no acceptance rule; this is speculative sampling with each
+ * draft a deterministic proposal.  Logits as in mk_lmhead_verify.  Row t's
+ * target p_t is the softmax of its top_k largest logits (NaN never counts,
+ * ties go to the lower index) divided by `temperature`.  Groups and drafts
+ * as in mk_lmhead_verify.  In group g, draft i is accepted when
+ * u_acc[row i] < p_i(draft i) (0 for a token outside the top_k); at the first
+ * rejection, row i emits a sample of p_i with the draft removed, picked by
+ * u_samp[row i] through the inverse CDF over the candidates in ascending
+ * vocabulary order; if every draft is accepted, the last row emits a sample
+ * of its p (u_samp).  Every emitted token is then distributed exactly as the
+ * row's p.  A row whose logits are all NaN has no candidate: it rejects its
+ * draft and emits -1.
+ *   u_acc, u_samp [T] fp32 in [0, 1) (device): the caller's uniform numbers
+ *   topk_idx [T][32] int32, topk_logit [T][32] fp32 (device, optional, NULL
+ *     to skip): each row's candidates in ascending vocabulary order, unused
+ *     slots -1 / -inf
+ *   n_acc [G], tokens [T] (device) as in mk_lmhead_verify.
+ * 1 <= top_k <= 32 and 0 < temperature < inf (MK_ERR_RANGE otherwise);
+ * H % 64 == 0.  Four launches: lm_head prep, the lm_head stream writing every
+ * logit into the workspace, top-k per row, the accept / resample pass.
+ * The hidden rows are prescaled as in mk_lmhead_verify; the logits returned
+ * in topk_logit are scaled back exactly. */
+size_t mk_lmhead_sample_workspace(int32_t V, int32_t H, int32_t T);
+int mk_lmhead_sample(const uint16_t* W_f16, int32_t V, int32_t H, const float* hid, int32_t T,
+                     const int32_t* h_group_start, int32_t G, const int32_t* drafts, int32_t top_k, float temperature,
+                     const float* u_acc, const float* u_samp, int32_t* topk_idx, float* topk_logit, int32_t* n_acc,
+                     int32_t* tokens, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------- Gated DeltaNet */
 /* richland.au single-stream article, section "What shipped": the recurrent
  * state is committed only through the surely-accepted token, and drafted rows

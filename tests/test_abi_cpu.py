@@ -113,6 +113,18 @@ def test_host_validation_before_any_gpu_work():
     dn = mk.mk_deltanet(fake, fake, fake, 4, 128, 128, 5)
     assert L.mk_deltanet_step(ctypes.byref(dn), 0, x, x, x, x, x, 6, x, None) == mk.MK_ERR_RANGE
     assert L.mk_status_string(mk.MK_ERR_WORKSPACE) == b"workspace too small"
+    # sampling verify: top_k in 1..32, a positive finite temperature
+    f = ctypes.c_float
+    for k, tau in ((0, 0.6), (33, 0.6), (8, 0.0), (8, -1.0), (8, float("inf")), (8, float("nan"))):
+        assert L.mk_lmhead_sample(x, 100, 512, x, 5, None, 1, x, k, f(tau), x, x, None, None, x, x, x, 1 << 30,
+                                  None) == mk.MK_ERR_RANGE, (k, tau)
+    assert L.mk_lmhead_sample(x, 100, 512, x, 5, None, 1, x, 8, f(0.6), None, x, None, None, x, x, x, 1 << 30,
+                              None) == mk.MK_ERR_ARG
+    assert L.mk_lmhead_sample(x, 100, 512, x, 5, None, 1, x, 8, f(0.6), x, x, None, None, x, x, x, 64,
+                              None) == mk.MK_ERR_WORKSPACE
+    # the no-allocation GEMV refuses shapes whose workspace exceeds its array, before any device call
+    Wbig = _q4k(fake, 32768, 32768)
+    assert L.mk_qgemv_rows_noalloc(ctypes.byref(Wbig), x, 16, x, 0, None) == mk.MK_ERR_WORKSPACE
 
 
 def test_workspace_queries_are_host_only():
@@ -120,6 +132,7 @@ def test_workspace_queries_are_host_only():
     assert mk.mk_qgemv_rows_workspace(0, 5120, 5120) == 0
     assert mk.mk_ffn_rows_workspace(5, 5120, 17408) > 0
     assert mk.mk_lmhead_verify_workspace(151936, 5120, 5) > 151936 // 64 * 16 * 8
+    assert mk.mk_lmhead_sample_workspace(151936, 5120, 12) > 12 * 151936 * 4
     assert mk.mk_q4k_bytes(5120, 5120) == 14_745_600
 
 
