@@ -17,6 +17,8 @@ the order the pages give them.  Each function names the step it follows:
   C6 lmhead/verify  logits, argmax, accepted-prefix length, emitted tokens
   C7 gdn_step       gated delta rule with commit through the accepted row
   C8 decode_step    composition of one whole step
+  M1 mtp_block      one pass of the synthetic MTP draft head
+  M2 mtp_draft      catch-up rows, then the draft steps (draft vocabulary prefix)
   F1 topk_rows      the k largest logits of each row (sampling mode)
   F2 sample_weights target weights softmax(top-k / temperature)
   F3 sample_verify  sampling-mode verification that keeps the target distribution
@@ -267,6 +269,58 @@ def decode_step(x, layers, W16, group_start, drafts, gdn=None, n_layers=None, te
             o_all[r0:r1] = o
         out["S"], out["gdn_o"] = S_new, o_all
     return out
+
+
+def mtp_block(mtp, E16, tokens, h_rows) -> np.ndarray:
+    """M1: one pass of the synthetic MTP draft head over rows (token, hidden):
+    z = [RMSNorm(f32 E[token]) ; RMSNorm(hidden)] (2H), u = fc . q8(z),
+    x' = u + FFN(RMSNorm(u)).  A token outside [0, V) contributes a zero
+    embedding.  Returns x' [rows][H] (rounded to fp32 at every stage the GPU
+    stores).  The head's layers are a reading: the pages name only the
+    head's work (richland.au single-stream article, "What shipped": MTP
+    catch-up rows for accepted tokens, then n_draft draft steps)."""
+    tokens = np.asarray(tokens, np.int64)
+    h_rows = _c(np.atleast_2d(h_rows), np.float32)
+    V, H = E16.shape
+    e = np.zeros((len(tokens), H), np.float32)
+    for i, t in enumerate(tokens):
+        if 0 <= t < V:
+            e[i] = np.asarray(E16[t], np.uint16).view(np.float16).astype(np.float32)
+    z = np.concatenate([rmsnorm(e), rmsnorm(h_rows)], axis=1)
+    u = qgemv(mtp["fc"], z)
+    return residual_add(u, ffn(mtp["gate"], mtp["up"], mtp["down"], rmsnorm(u)))
+
+
+def mtp_draft(mtp, E16, V_draft, hidden, tokens, group_start, n_acc, n_draft) -> dict:
+    """M2: the on-device MTP draft loop of one step (richland.au single-stream
+    article, "What shipped": catch-up rows for the accepted tokens, then the
+    draft steps, drafting over the 32,768 most frequent tokens).  Group g's
+    catch-up rows are its rows i = 0..n_acc[g]: main-model hidden (final
+    residual) of row i with the token emitted after it, tokens[gs[g] + i] (the
+    accepted drafts, then the bonus token).  The last catch-up row gives
+    draft 1 = argmax over the first V_draft rows of E16 (tied lm_head) of
+    RMSNorm(x'); draft k + 1 comes from a pass over (draft k, x' of draft k's
+    pass), one row per group.  Returns drafts [n_draft][G], "catchup" (x' of
+    every catch-up row, dict row -> [H]) and "chain" (x' [n_draft][G][H] of
+    the row that produced each draft)."""
+    gs = list(group_start)
+    G = len(gs) - 1
+    hidden = _c(np.atleast_2d(hidden), np.float32)
+    drafts = np.zeros((n_draft, G), np.int32)
+    chain = np.zeros((n_draft, G, hidden.shape[1]), np.float32)
+    catchup = {}
+    Wd = E16[:V_draft]
+    for g in range(G):
+        rows = list(range(gs[g], gs[g] + int(n_acc[g]) + 1))
+        xp = mtp_block(mtp, E16, [tokens[r] for r in rows], hidden[rows])
+        for j, r in enumerate(rows):
+            catchup[r] = xp[j]
+        chain[0, g] = xp[-1]
+    drafts[0] = lmhead(Wd, rmsnorm(chain[0]))["top1"]
+    for k in range(1, n_draft):
+        chain[k] = mtp_block(mtp, E16, drafts[k - 1], chain[k - 1])
+        drafts[k] = lmhead(Wd, rmsnorm(chain[k]))["top1"]
+    return {"drafts": drafts, "catchup": catchup, "chain": chain}
 
 
 def lmhead(W16, hid, return_logits=False) -> dict:

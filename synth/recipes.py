@@ -83,6 +83,19 @@ def stack_lm_head(vocab=VOCAB, hidden=HIDDEN, seed=STACK_SEED, r0=0, r1=None):
     return normal_f16(seed, 30000, 0, (r1 - r0) * hidden, 0.0, 0.02, start=r0 * hidden).reshape(r1 - r0, hidden)
 
 
+# ---------------------------------------------------------------- MTP draft head
+MTP_BASE = 60000
+
+
+def mtp_weights(hidden=HIDDEN, ffn=FFN, seed=STACK_SEED, base=MTP_BASE):
+    """The synthetic MTP draft head: fc (hidden x 2 hidden) and one FFN of
+    the stack's shape, Q4_K-style fields with the stack's distributions."""
+    return {"fc": q4k_fields(seed, base + 0, hidden, 2 * hidden),
+            "gate": q4k_fields(seed, base + 1, ffn, hidden),
+            "up": q4k_fields(seed, base + 2, ffn, hidden),
+            "down": q4k_fields(seed, base + 3, hidden, ffn)}
+
+
 # ---------------------------------------------------------------- lm_head + verify
 LM_SEED = 3
 

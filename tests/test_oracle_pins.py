@@ -818,3 +818,89 @@ def test_sample_verify_reduces_to_greedy(orc):
         for trial in range(20):
             n, tok, _ = orc.sample_verify(idx, val, gs, drafts, tau, rng.random(6), rng.random(6))
             assert np.array_equal(n, n_ref) and np.array_equal(tok, t_ref), (k, tau)
+
+
+# ----------------------------------------------------------------- M1-M2 MTP draft loop
+def _small_mtp(seed, H=256, F=512):
+    return {"fc": synth.q4k_fields(seed, 600, H, 2 * H), "gate": synth.q4k_fields(seed, 601, F, H),
+            "up": synth.q4k_fields(seed, 602, F, H), "down": synth.q4k_fields(seed, 603, H, F)}
+
+
+def _np_mtp_block(m, E16, toks, h32, variant="ok"):
+    V, H = E16.shape
+    e = np.zeros((len(toks), H), np.float32)
+    for i, t in enumerate(toks):
+        if 0 <= t < V:
+            e[i] = _f16(E16[t]).astype(np.float32)
+    hn = _np_rms(h32) if variant != "no_hnorm" else h32
+    z = np.concatenate([_np_rms(e), hn] if variant != "swapped" else [hn, _np_rms(e)], axis=1)
+    u = _np_gemv(m["fc"], z)
+    a = _np_rms(u)
+    y = _np_gemv(m["down"], _np_silu_mul(_np_gemv(m["gate"], a), _np_gemv(m["up"], a)))
+    if variant == "no_residual":
+        return y
+    return (u.astype(np.float64) + y.astype(np.float64)).astype(np.float32)
+
+
+def test_mtp_block_vs_independent_float64_evaluation(orc):
+    H, V = 256, 300
+    m = _small_mtp(70)
+    E16 = synth.normal_f16(70, 604, 0, V * H, 0.0, 0.02).reshape(V, H)
+    h = synth.normal_f32(70, 605, 0, 4 * H, 0.0, 3.0).reshape(4, H)
+    toks = [5, 299, -1, 300]  # the last two contribute zero embeddings
+    got = orc.mtp_block(m, E16, toks, h)
+    assert _z6(got, _np_mtp_block(m, E16, toks, h)) <= 1e-5
+    for bad in ("swapped", "no_hnorm"):
+        assert _z6(got, _np_mtp_block(m, E16, toks, h, bad)) > 1e-2, bad
+    # with W_down at d = dmin = 0 the block is u itself, so a dropped residual is caught
+    m0 = dict(m, down=_zero_scales(m["down"]))
+    got0 = orc.mtp_block(m0, E16, toks, h)
+    assert _z6(got0, _np_mtp_block(m0, E16, toks, h)) <= 1e-5
+    assert np.abs(got0).max() > 0 and np.abs(_np_mtp_block(m0, E16, toks, h, "no_residual")).max() == 0
+
+
+def test_mtp_draft_catch_up_rows_chain_and_vocabulary(orc):
+    H, V, Vd, T, nd = 256, 500, 200, 6, 3
+    m = _small_mtp(71)
+    E16 = synth.normal_f16(71, 606, 0, V * H, 0.0, 0.02).reshape(V, H)
+    hidden = synth.normal_f32(71, 607, 0, T * H, 0.0, 2.0).reshape(T, H)
+    gs = [0, 3, 6]
+    tokens = np.array([11, 250, -1, 40, 41, 499], np.int32)
+    n_acc = [1, 2]
+    out = orc.mtp_draft(m, E16, Vd, hidden, tokens, gs, n_acc, nd)
+    d = out["drafts"]
+    assert d.shape == (nd, 2) and (d >= 0).all() and (d < Vd).all()
+    assert sorted(out["catchup"]) == [0, 1, 3, 4, 5]  # rows 0..n_acc of each group
+    # catch-up rows and the chain against the independent evaluation; each draft is
+    # numpy's float64 argmax over the draft-vocabulary prefix
+    for g, rows in enumerate(([0, 1], [3, 4, 5])):
+        ref = _np_mtp_block(m, E16, [tokens[r] for r in rows], hidden[rows])
+        for j, r in enumerate(rows):
+            assert _z6(out["catchup"][r], ref[j]) <= 1e-5
+        prev = ref[-1]
+        for k in range(nd):
+            if k:
+                prev = _np_mtp_block(m, E16, [d[k - 1, g]], prev[None])[0]
+            assert _z6(out["chain"][k, g], prev) <= 1e-5
+            lg = _np_rms(out["chain"][k, g][None]).astype(np.float64) @ _f16(E16[:Vd]).T
+            assert d[k, g] == np.argmax(lg[0])
+    # rows after n_acc (drafts that were rejected) do not matter; row n_acc does
+    t2, h2 = tokens.copy(), hidden.copy()
+    t2[2], h2[2] = 7, 0.0
+    assert np.array_equal(orc.mtp_draft(m, E16, Vd, h2, t2, gs, n_acc, nd)["drafts"], d)
+    t3 = tokens.copy()
+    t3[1] = 12
+    assert not np.array_equal(orc.mtp_draft(m, E16, Vd, hidden, t3, gs, n_acc, nd)["chain"][0, 0],
+                              out["chain"][0, 0])
+
+
+def test_mtp_draft_of_an_all_zero_head_is_token_zero(orc):
+    # fc and W_down at zero: x' = 0, RMSNorm(0) = 0, every logit is 0 and the
+    # tie goes to the lowest index at every draft step
+    H, V = 256, 300
+    m = _small_mtp(72)
+    m["fc"], m["down"] = _zero_scales(m["fc"]), _zero_scales(m["down"])
+    E16 = synth.normal_f16(72, 606, 0, V * H, 0.0, 0.02).reshape(V, H)
+    hidden = synth.normal_f32(72, 607, 0, 2 * H).reshape(2, H)
+    out = orc.mtp_draft(m, E16, 100, hidden, [3, 4], [0, 2], [1], 3)
+    assert (out["drafts"] == 0).all() and (out["chain"] == 0).all()
