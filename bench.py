@@ -108,17 +108,21 @@ def make_agents(n_agents, n_gdn_layers, T_max, device="cuda"):
 
 
 def step_inputs(T, steps, n_gdn_layers, device="cuda"):
+    """Seeded inputs of `steps` distinct steps: the T input rows and the
+    Gated DeltaNet rows of every GDN layer (one set per step)."""
     import torch
 
     from synth import recipes
     xs = [torch.from_numpy(recipes.stack_step_input(s, T)).to(device) for s in range(steps)]
-    g = recipes.stack_gdn_inputs(0, T, n_gdn_layers)
-    gin = {k: torch.from_numpy(v).to(device) for k, v in g.items()}
-    return xs, gin
+    gins = []
+    for s in range(steps):
+        g = recipes.stack_gdn_inputs(s, T, n_gdn_layers)
+        gins.append({k: torch.from_numpy(v).to(device) for k, v in g.items()})
+    return xs, gins
 
 
 # ------------------------------------------------------------------ timing
-def time_steps(stack, T, gs, n_agents, xs, gin, steps, warmup):
+def time_steps(stack, T, gs, n_agents, xs, gins, steps, warmup):
     import torch
 
     import bit_weight_streaming_q4_amd as mk
@@ -127,7 +131,7 @@ def time_steps(stack, T, gs, n_agents, xs, gin, steps, warmup):
     G = len(gs) - 1
     drafts = torch.from_numpy(np.ascontiguousarray(
         recipes.uniform_i32(2, 50000 + T, 0, max(T - G, 1), 0, VOCAB - 1))).to(dev)
-    nh = gin["q"].shape[1]
+    nh = gins[0]["q"].shape[1]
     go = torch.empty(T, nh, 128, dtype=torch.float32, device=dev)
     ws = stack.workspace(T, dev)
     xbuf = torch.empty_like(xs[0])
@@ -137,24 +141,29 @@ def time_steps(stack, T, gs, n_agents, xs, gin, steps, warmup):
         xbuf.copy_(xs[i % len(xs)])
         for a in stack.agents:
             a.n_acc[0:1].fill_(t_agent - 1)  # replay the most ring rows possible
-        return mk.mk_decode_step(stack, xbuf, gs, drafts, gdn=gin, gdn_o=go, ws=ws)
+        return mk.mk_decode_step(stack, xbuf, gs, drafts, gdn=gins[i % len(gins)], gdn_o=go, ws=ws)
 
     for i in range(warmup):
         one(i)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    kernel_ms = []
+    kernel_ms, wall_ms = [], []
     t0 = time.perf_counter()
     ev0.record()
     for i in range(steps):
-        one(warmup + i)
+        t1 = time.perf_counter()
+        one(warmup + i)  # returns after the step's one synchronisation
+        wall_ms.append((time.perf_counter() - t1) * 1e3)
         kernel_ms.append(mk.mk_decode_step_last_ms(stack))
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_event = ev0.elapsed_time(ev1) / steps
     r = {"ms_per_step": wall * 1e3 / steps, "ms_event": ms_event, "kernel_ms": float(np.mean(kernel_ms)),
-         "kernel_ms_p10_p90": [float(np.percentile(kernel_ms, 10)), float(np.percentile(kernel_ms, 90))]}
+         "kernel_ms_median": float(np.median(kernel_ms)),
+         "kernel_ms_p10_p90": [float(np.percentile(kernel_ms, 10)), float(np.percentile(kernel_ms, 90))],
+         "step_ms_median": float(np.median(wall_ms)),
+         "step_ms_p10_p90": [float(np.percentile(wall_ms, 10)), float(np.percentile(wall_ms, 90))]}
     if os.environ.get("MK_BENCH_PHASES"):
         st = mk.mk_decode_step_stamps(stack, T, ws)
         L = (len(st) - 8) // 4  # stamps: start, prep, 4 per layer, lm_prep, ..., end
@@ -298,6 +307,35 @@ def kernel_bench(lm, device="cuda"):
         ws = mk.workspace(mk.mk_lmhead_verify_workspace(V, HIDDEN, T), device)
         rec(f"lmhead_verify_V{V}_T{T}", lambda i: mk.mk_lmhead_verify(lm, hid, None, drafts, am, na, tok, ws=ws, V=V),
             20, lambda: torch.cat([am, na, tok]), V * HIDDEN * 2 + T * HIDDEN * 4)
+    # sampling-mode verification: 4 agents x 3 rows, top_k 32, temperature 0.6
+    T12, gs12 = 12, [0, 3, 6, 9, 12]
+    hid12 = torch.from_numpy(recipes.lm_hidden(T12, trial=1)).to(device)
+    dr12 = torch.from_numpy(recipes.uniform_i32(3, 51, 0, 8, 0, VOCAB - 1)).to(device)
+    ua = torch.from_numpy(recipes.uniform_f64(3, 52, 0, T12).astype(np.float32)).to(device)
+    us = torch.from_numpy(recipes.uniform_f64(3, 53, 0, T12).astype(np.float32)).to(device)
+    na4 = torch.empty(4, dtype=torch.int32, device=device)
+    tok12 = torch.empty(T12, dtype=torch.int32, device=device)
+    ws = mk.workspace(mk.mk_lmhead_sample_workspace(VOCAB, HIDDEN, T12), device)
+    rec(f"lmhead_sample_V{VOCAB}_T{T12}_k32",
+        lambda i: mk.mk_lmhead_sample(lm, hid12, gs12, dr12, 32, 0.6, ua, us, na4, tok12, ws=ws), 10,
+        lambda: torch.cat([na4, tok12]), VOCAB * HIDDEN * 2 + T12 * HIDDEN * 4)
+    del ws
+    # the on-device MTP draft loop: 4 agents x 3 rows with 2 drafts each, and
+    # one sequence of 5 rows with 4 drafts (passes x (fc + FFN + draft prefix))
+    head = mk.MtpHead.from_fields(recipes.mtp_weights(), device)
+    head_bytes = (2 * HIDDEN * HIDDEN + 3 * HIDDEN * FFN) // 256 * 144 + recipes.DRAFT_VOCAB * HIDDEN * 2
+    for T, gs, nd, n_acc in ((12, [0, 3, 6, 9, 12], 2, [2, 0, 1, 2]), (5, [0, 5], 4, [3])):
+        hidm = torch.from_numpy(recipes.stack_step_input(60, T)).to(device)
+        toks = torch.from_numpy(recipes.uniform_i32(3, 54, T, T, 0, VOCAB - 1)).to(device)
+        nacc = torch.tensor(n_acc, dtype=torch.int32, device=device)
+        dr = torch.empty(nd, len(gs) - 1, dtype=torch.int32, device=device)
+        ws = mk.workspace(mk.mk_mtp_draft_workspace(head, recipes.DRAFT_VOCAB, T, len(gs) - 1), device)
+        rec(f"mtp_draft_T{T}_G{len(gs) - 1}_n{nd}",
+            lambda i: mk.mk_mtp_draft(head, lm, recipes.DRAFT_VOCAB, hidm, gs, toks, nacc, nd, dr, ws=ws), 8,
+            lambda: dr.flatten(), nd * head_bytes)
+        del ws
+    del head
+    torch.cuda.empty_cache()
     # Gated DeltaNet step + commit, 48 x 32 heads, T = 5, seeded accept lengths
     nh = 48 * 32
     st = mk.DeltaNetState(nh, T, device=device,
@@ -421,6 +459,102 @@ def read_probe(device="cuda", gib=4, reps=5):
     return round(gbs, 1)
 
 
+# ------------------------------------------------------------------ lm_head workload: accept lengths
+def accept_histogram(lm, trials=200, device="cuda"):
+    """The lm_head + verify workload over `trials` seeded trials: T = 5 rows,
+    4 drafts, draft i the argmax of row i with probability 0.7 (the argmax
+    from a first call), else a uniform id.  Returns the n_acc histogram, its
+    mean against 0.7 + 0.49 + 0.343 + 0.2401 = 1.7731 and the chi-square
+    against P(k) = 0.7^k 0.3 (k < 4), 0.7^4."""
+    import torch
+
+    import bit_weight_streaming_q4_amd as mk
+    from synth import recipes
+    T = 5
+    am = torch.empty(T, dtype=torch.int32, device=device)
+    na = torch.empty(1, dtype=torch.int32, device=device)
+    tok = torch.empty(T, dtype=torch.int32, device=device)
+    zero = torch.zeros(T - 1, dtype=torch.int32, device=device)
+    ws = mk.workspace(mk.mk_lmhead_verify_workspace(VOCAB, HIDDEN, T), device)
+    hist = np.zeros(5, np.int64)
+    for tr in range(trials):
+        hid = torch.from_numpy(recipes.lm_hidden(T, trial=tr)).to(device)
+        mk.mk_lmhead_verify(lm, hid, None, zero, am, na, tok, ws=ws)
+        top = am.cpu().numpy()
+        dr = torch.from_numpy(recipes.drafts_from_argmax(top[:T - 1], VOCAB, trial=tr)).to(device)
+        mk.mk_lmhead_verify(lm, hid, None, dr, am, na, tok, ws=ws)
+        hist[int(na.item())] += 1
+    p = np.array([0.3, 0.21, 0.147, 0.1029, 0.2401])
+    chi2 = float((((hist - trials * p) ** 2) / (trials * p)).sum())
+    mean = float((hist * np.arange(5)).sum() / trials)
+    log(f"accept lengths over {trials} trials: {hist.tolist()}, mean {mean:.4f} (expected 1.7731), chi2 {chi2:.2f}")
+    return {"trials": trials, "histogram": hist.tolist(), "mean": round(mean, 4), "expected_mean": 1.7731,
+            "chi2_4dof": round(chi2, 2), "chi2_crit_p001": 18.47}
+
+
+def manifest(seeds):
+    """What the numbers were measured on: device, software versions, clocks,
+    a hash of the sources, the seeds and the host cores."""
+    import platform
+    import subprocess
+
+    import torch
+    h = hashlib.sha256()
+    for root in ("bit_weight_streaming_q4_amd/csrc", "include", "oracle", "synth"):
+        for f in sorted(os.listdir(os.path.join(ROOT, root))):
+            if f.endswith((".hip", ".h", ".c", ".py")):
+                with open(os.path.join(ROOT, root, f), "rb") as fh:
+                    h.update(fh.read())
+    with open(os.path.join(ROOT, "bench.py"), "rb") as fh:
+        h.update(fh.read())
+    prop = torch.cuda.get_device_properties(0)
+    m = {"gpu": torch.cuda.get_device_name(0), "arch": getattr(prop, "gcnArchName", ""),
+         "compute_units": prop.multi_processor_count, "hbm_bytes": prop.total_memory,
+         "torch": torch.__version__, "hip": torch.version.hip, "python": platform.python_version(),
+         "host_cores": len(os.sched_getaffinity(0)), "source_sha256_16": h.hexdigest()[:16], "seeds": seeds}
+    try:
+        with open("/sys/module/amdgpu/version") as f:
+            m["amdgpu_driver"] = f.read().strip()
+    except OSError:
+        m["amdgpu_driver"] = None
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        clk = json.loads(r.stdout) if r.returncode == 0 and r.stdout.strip().startswith("{") else {}
+        card = next(iter(clk.values()), {}) if clk else {}
+        m["clocks"] = {k: v for k, v in card.items() if "clk" in k.lower()} or None
+    except (OSError, ValueError, subprocess.SubprocessError):
+        m["clocks"] = None
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"], capture_output=True, text=True,
+                           timeout=10)
+        m["git_sha"] = r.stdout.strip() if r.returncode == 0 else None
+    except (OSError, subprocess.SubprocessError):
+        m["git_sha"] = None
+    return m
+
+
+def cpu_baseline_one_core(T=12):
+    """The oracle on one core (OMP_NUM_THREADS=1, in a child process that
+    touches no GPU): the first layer's P_in GEMV (5120 -> 10240) at T = 12,
+    reported as weight GB/s."""
+    import subprocess
+    code = ("import json, time, sys; sys.path.insert(0, %r)\n"
+            "import oracle\nfrom synth import recipes\n"
+            "W = recipes.stack_weight(0, 'p_in'); x = recipes.stack_step_input(0, %d)\n"
+            "oracle.qgemv(W, x[:1])\n"
+            "t0 = time.perf_counter(); oracle.qgemv(W, x); dt = time.perf_counter() - t0\n"
+            "print(json.dumps({'s': dt}))\n") % (ROOT, T)
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=600)
+    if r.returncode != 0:
+        log(f"one-core oracle run failed: {r.stderr[-300:]}")
+        return None
+    dt = json.loads(r.stdout.strip().splitlines()[-1])["s"]
+    nbytes = PROJ * HIDDEN // 256 * 144
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"layer 0 P_in ({PROJ} x {HIDDEN}) at T={T}, {dt:.2f} s"}
+
+
 # ------------------------------------------------------------------ CPU baseline
 def cpu_baseline(T=12, budget_s=20.0):
     """The oracle (as it stands) on a bounded sample of the same step at
@@ -464,6 +598,8 @@ def main():
     ap.add_argument("--no-kernels", action="store_true", help="skip the standalone entry-point timings")
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--sweep", action="store_true", help="also time the step at every T in 1..12 and 16")
+    ap.add_argument("--series", type=int, default=100,
+                    help="also time this many seeded T = 12 steps, each with its own inputs (0: skip)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the HBM byte counters)")
     args = ap.parse_args()
@@ -494,6 +630,7 @@ def main():
     gl = recipes.gdn_layers(L)
     layers, lm = build_stack(layers=L)
     results = {}
+    series = None
     configs = [(12, [0, 3, 6, 9, 12], 4), (5, [0, 5], 1), (1, [0, 1], 1)]
     if args.sweep:  # one verify group of T rows, one agent
         configs += [(T, [0, T], 1) for T in (2, 3, 4, 6, 7, 8, 9, 10, 11, 16)]
@@ -502,9 +639,9 @@ def main():
             continue
         agents = make_agents(n_agents, len(gl), max(5, gs[1] - gs[0]))  # ring rows for the longest group
         stack = mk.Stack(layers, lm, gdn_layers=gl, agents=agents)
-        xs, gin = step_inputs(T, min(args.steps + args.warmup, 8), len(gl))
+        xs, gins = step_inputs(T, min(args.steps + args.warmup, 8), len(gl))
         log(f"timing T={T}")
-        r = time_steps(stack, T, gs, n_agents, xs, gin, args.steps, args.warmup)
+        r = time_steps(stack, T, gs, n_agents, xs, gins, args.steps, args.warmup)
         b = step_bytes(T, n_agents, L)
         r["bytes"] = b
         r["weight_gb_s"] = (b["weights"] + b["lm_head"]) / (r["ms_event"] * 1e-3) / 1e9
@@ -514,7 +651,23 @@ def main():
         results[T] = r
         log(f"T={T}: {r['ms_per_step']:.3f} ms/step (events {r['ms_event']:.3f}, kernel {r['kernel_ms']:.3f}), "
             f"weights {r['weight_gb_s']:.0f} GB/s, total {r['total_gb_s']:.0f} GB/s, kernel {r['kernel_gb_s']:.0f} GB/s")
+        if T == 12 and not args.only_primary and args.series:
+            # the stack workload as defined: 100 seeded steps, each with its own input rows and GDN rows
+            del xs, gins
+            torch.cuda.empty_cache()
+            xs, gins = step_inputs(T, args.series, len(gl))
+            log(f"timing T=12 over {args.series} seeded steps")
+            rs = time_steps(stack, T, gs, n_agents, xs, gins, args.series, 0)
+            series = {"steps": args.series, "kernel_ms_mean": round(rs["kernel_ms"], 4),
+                      "kernel_ms_median": round(rs["kernel_ms_median"], 4),
+                      "kernel_ms_p10_p90": [round(v, 4) for v in rs["kernel_ms_p10_p90"]],
+                      "step_ms_median": round(rs["step_ms_median"], 4),
+                      "step_ms_p10_p90": [round(v, 4) for v in rs["step_ms_p10_p90"]],
+                      "weight_gb_s_median_kernel": round((b["weights"] + b["lm_head"]) / (rs["kernel_ms_median"] * 1e-3)
+                                                         / 1e9, 1)}
+        stack.close()
         del stack, agents
+        del xs, gins
         torch.cuda.empty_cache()
     p = results[12]
     traffic = None
@@ -523,8 +676,13 @@ def main():
         if tj.get("kernel_source_hash") == kernel_source_hash():
             traffic = tj.get("bytes_per_launch")
     kernels = None if args.no_kernels else kernel_bench(lm)
+    accepts = None if args.no_kernels else accept_histogram(lm)
     attainable = read_probe()
     cpu = None if args.no_cpu_baseline else cpu_baseline()
+    if cpu is not None:
+        cpu["one_core"] = cpu_baseline_one_core()
+    seeds = {"stack": recipes.STACK_SEED, "lm_head": recipes.LM_SEED, "gdn": recipes.GDN_SEED,
+             "mtp": recipes.STACK_SEED, "step_inputs": "stack seed, tensors 10000 + step and 20000 + step"}
     out = {
         "metric": "weight-stream GB/s (% of 8 TB/s) and decode steps/s at T=1,5,12 rows",
         "value": round(p["weight_gb_s"], 1),
@@ -548,8 +706,16 @@ def main():
                                       "rows_steps_per_s": round(r["steps_per_s"] * T, 1),
                                       "weight_gb_s": round(r["weight_gb_s"], 1),
                                       "total_gb_s": round(r["total_gb_s"], 1),
-                                      "kernel_ms": round(r["kernel_ms"], 4)} for T, r in sorted(results.items())},
+                                      "kernel_ms": round(r["kernel_ms"], 4),
+                                      "kernel_ms_median": round(r["kernel_ms_median"], 4),
+                                      "kernel_ms_p10_p90": [round(v, 4) for v in r["kernel_ms_p10_p90"]],
+                                      "step_ms_median": round(r["step_ms_median"], 4),
+                                      "step_ms_p10_p90": [round(v, 4) for v in r["step_ms_p10_p90"]]}
+                             for T, r in sorted(results.items())},
+                   "seeded_series_T12": series,
+                   "lm_head_accept_lengths": accepts,
                    "standalone_kernels": kernels},
+        "manifest": manifest(seeds),
         "roofline": {"bound": "hbm", "achieved": round(p["kernel_gb_s"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(p["kernel_gb_s"] / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "k_decode_step<12>", "kernel_ms": round(p["kernel_ms"], 4),
@@ -558,6 +724,11 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+    # explicit teardown: every device object of the run is released here, with
+    # the device idle, not in finalizers at interpreter exit
+    del layers, lm
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

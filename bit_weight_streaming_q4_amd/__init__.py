@@ -37,6 +37,10 @@ class mk_deltanet(ctypes.Structure):
                 ("nh", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("T_max", ctypes.c_int32)]
 
 
+class mk_mtp(ctypes.Structure):
+    _fields_ = [("fc", mk_q4k), ("gate", mk_q4k), ("up", mk_q4k), ("down", mk_q4k)]
+
+
 class mk_stack_desc(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("proj", ctypes.c_int32),
                 ("ffn", ctypes.c_int32), ("vocab", ctypes.c_int32),
@@ -82,6 +86,9 @@ def lib():
     L.mk_lmhead_sample_workspace.argtypes = [i32, i32, i32]
     L.mk_lmhead_sample_workspace.restype = sz
     L.mk_lmhead_sample.argtypes = [P, i32, i32, P, i32, P, i32, P, i32, ctypes.c_float, P, P, P, P, P, P, P, sz, P]
+    L.mk_mtp_draft_workspace.argtypes = [ctypes.POINTER(mk_mtp), i32, i32, i32]
+    L.mk_mtp_draft_workspace.restype = sz
+    L.mk_mtp_draft.argtypes = [ctypes.POINTER(mk_mtp), P, i32, i32, P, i32, P, i32, P, P, i32, P, P, P, sz, P]
     L.mk_deltanet_step.argtypes = [ctypes.POINTER(mk_deltanet), i32, P, P, P, P, P, i32, P, P]
     L.mk_deltanet_commit.argtypes = [ctypes.POINTER(mk_deltanet), P]
     L.mk_deltanet_status.argtypes = [ctypes.POINTER(mk_deltanet), P]
@@ -272,6 +279,41 @@ def mk_lmhead_sample(W16, hid, group_start, drafts, top_k, temperature, u_acc, u
                                   _ptr(tokens), _ptr(ws), ws.numel(), _stream(stream)), "mk_lmhead_sample")
 
 
+class MtpHead:
+    """The synthetic MTP draft head on the device: fc (H x 2H) and one FFN
+    (gate, up: F x H; down: H x F), each a Q4K."""
+
+    def __init__(self, fc: Q4K, gate: Q4K, up: Q4K, down: Q4K):
+        self.fc, self.gate, self.up, self.down = fc, gate, up, down
+        self.c = mk_mtp(fc.c, gate.c, up.c, down.c)
+
+    @classmethod
+    def from_fields(cls, f: dict, device="cuda"):
+        return cls(*[Q4K.from_fields(f[k], device) for k in ("fc", "gate", "up", "down")])
+
+
+def mk_mtp_draft_workspace(head: MtpHead, V_draft: int, T: int, G: int) -> int:
+    return int(lib().mk_mtp_draft_workspace(ctypes.byref(head.c), V_draft, T, G))
+
+
+def mk_mtp_draft(head: MtpHead, embed16, V_draft, hidden, group_start, tokens, n_acc, n_draft, drafts, trace=None,
+                 ws=None, stream=None):
+    """On-device MTP draft loop: hidden fp32 [T][H], tokens int32 [T],
+    n_acc int32 [G] and drafts int32 [n_draft][G] are device tensors."""
+    V = embed16.shape[0]
+    T = hidden.shape[0]
+    if group_start is None:
+        gs, G = None, 1
+    else:
+        gs_np = np.ascontiguousarray(group_start, np.int32)
+        gs, G = gs_np.ctypes.data, len(gs_np) - 1
+    if ws is None:
+        ws = workspace(mk_mtp_draft_workspace(head, V_draft, T, G), hidden.device)
+    _check(lib().mk_mtp_draft(ctypes.byref(head.c), _ptr(embed16), V, V_draft, _ptr(hidden), T, gs, G, _ptr(tokens),
+                              _ptr(n_acc), int(n_draft), _ptr(drafts), _ptr(trace), _ptr(ws), ws.numel(),
+                              _stream(stream)), "mk_mtp_draft")
+
+
 def _attn_groups(T, ctx, group_start):
     ctx_np = np.ascontiguousarray(ctx, np.int32)
     gs_np = np.ascontiguousarray([0, T] if group_start is None else group_start, np.int32)
@@ -378,11 +420,21 @@ class Stack:
         self.h = h
         self._ws = {}
 
+    def close(self):
+        """Destroys the host-side descriptor (and its two HIP events) now."""
+        if getattr(self, "h", None):
+            lib().mk_stack_destroy(self.h)
+            self.h = None
+
     def __del__(self):
+        # No HIP call while the interpreter is finalizing: the runtime (or a
+        # profiler wrapped around it) may already be tearing down.  The
+        # descriptor is then left to the process exit.
+        import sys
+        if sys.is_finalizing():
+            return
         try:
-            if getattr(self, "h", None):
-                lib().mk_stack_destroy(self.h)
-                self.h = None
+            self.close()
         except Exception:
             pass
 

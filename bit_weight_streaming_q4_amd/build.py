@@ -20,7 +20,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}"]
-SOURCES = ["mk_api.hip", "mk_gemv.hip", "mk_lmhead.hip", "mk_gdn.hip", "mk_step.hip", "mk_attn.hip", "mk_sample.hip"]
+SOURCES = ["mk_api.hip", "mk_gemv.hip", "mk_lmhead.hip", "mk_gdn.hip", "mk_step.hip", "mk_attn.hip", "mk_sample.hip", "mk_mtp.hip"]
 
 
 def _compile(src: str, objdir: str) -> str:

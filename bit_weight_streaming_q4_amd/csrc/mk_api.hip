@@ -464,6 +464,119 @@ int mk_lmhead_sample(const uint16_t* W_f16, int32_t V, int32_t H, const float* h
   return launch_status(mk::launch_sample(a, S(stream)), "sample");
 }
 
+// ------------------------------------------------------------------ MTP draft loop
+namespace {
+
+int check_mtp(const mk_mtp* m, int32_t* H, int32_t* F) {
+  int r;
+  if (!m) return fail(MK_ERR_ARG, "mtp: null head");
+  if ((r = check_q4k(&m->fc, "mtp fc")) || (r = check_q4k(&m->gate, "mtp gate")) ||
+      (r = check_q4k(&m->up, "mtp up")) || (r = check_q4k(&m->down, "mtp down")))
+    return r;
+  *H = m->fc.n_out;
+  *F = m->gate.n_out;
+  if (*H % 256 || m->fc.n_in != 2 * *H || m->gate.n_in != *H || m->up.n_out != *F || m->up.n_in != *H ||
+      m->down.n_out != *H || m->down.n_in != *F)
+    return fail(MK_ERR_SHAPE, "mtp: fc must be H x 2H (H %% 256 == 0), gate/up F x H, down H x F");
+  return MK_OK;
+}
+
+struct MtpLayout {
+  size_t z, u, a, y, xp, prev, hid, dead, lmi, gemv, ffn, lm, total;
+  size_t ws_gemv, ws_ffn, ws_lm;
+};
+
+MtpLayout mtp_layout(int H, int F, int V_draft, int T, int G) {
+  MtpLayout y;
+  size_t o = 0;
+  auto take = [&](size_t n) { const size_t at = o; o += align256(n); return at; };
+  y.z = take((size_t)T * 2 * H * 4);
+  y.u = take((size_t)T * H * 4);
+  y.a = take((size_t)T * H * 4);
+  y.y = take((size_t)T * H * 4);
+  y.xp = take((size_t)T * H * 4);
+  y.prev = take((size_t)G * H * 4);
+  y.hid = take((size_t)G * H * 4);
+  y.dead = take((size_t)G * 4);
+  y.lmi = take((size_t)2 * G * 4);
+  y.ws_gemv = std::max(mk_qgemv_rows_workspace(T, H, 2 * H), mk_qgemv_rows_workspace(G, H, 2 * H));
+  y.ws_ffn = std::max(mk_ffn_rows_workspace(T, H, F), mk_ffn_rows_workspace(G, H, F));
+  y.ws_lm = mk::lm_workspace_bytes(V_draft, H);
+  y.gemv = take(y.ws_gemv);
+  y.ffn = take(y.ws_ffn);
+  y.lm = take(y.ws_lm);
+  y.total = o;
+  return y;
+}
+
+}  // namespace
+
+size_t mk_mtp_draft_workspace(const mk_mtp* m, int32_t V_draft, int32_t T, int32_t G) {
+  int32_t H, F;
+  if (check_mtp(m, &H, &F) || V_draft <= 0 || T < 1 || T > MK_T_MAX || G < 1 || G > T || G > MK_LM_MAX_G) return 0;
+  return mtp_layout(H, F, V_draft, T, G).total;
+}
+
+int mk_mtp_draft(const mk_mtp* m, const uint16_t* embed_f16, int32_t V, int32_t V_draft, const float* hidden,
+                 int32_t T, const int32_t* h_group_start, int32_t G, const int32_t* tokens, const int32_t* n_acc,
+                 int32_t n_draft, int32_t* drafts, float* trace, void* ws, size_t ws_bytes, void* stream) {
+  int r;
+  int32_t H, F;
+  if ((r = check_mtp(m, &H, &F)) || (r = check_T(T))) return r;
+  if (V <= 0 || V_draft <= 0 || V_draft > V) return fail(MK_ERR_RANGE, "mtp: V_draft = %d outside 1..V (%d)", V_draft, V);
+  if (n_draft < 1 || n_draft > MK_T_MAX) return fail(MK_ERR_RANGE, "mtp: n_draft = %d outside 1..%d", n_draft, MK_T_MAX);
+  if ((r = check_ptr(embed_f16, "embed")) || (r = check_ptr(hidden, "hidden")) || (r = check_ptr(tokens, "tokens", 4)) ||
+      (r = check_ptr(n_acc, "n_acc", 4)) || (r = check_ptr(drafts, "drafts", 4)))
+    return r;
+  if (trace && (r = check_ptr(trace, "trace"))) return r;
+  std::vector<int32_t> gs;
+  if ((r = check_groups(h_group_start, G, T, gs))) return r;
+  const MtpLayout y = mtp_layout(H, F, V_draft, T, G);
+  if (!ws || ws_bytes < y.total) return fail(MK_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, y.total);
+  if ((r = check_ptr(ws, "workspace", 256))) return r;
+  uint8_t* w8 = (uint8_t*)ws;
+  mk::MtpArgs a = {};
+  a.embed = embed_f16;
+  a.V = V;
+  a.H = H;
+  a.T = T;
+  a.G = G;
+  for (int i = 0; i <= MK_LM_MAX_G; ++i) a.gs[i] = i <= G ? gs[i] : T;
+  a.hidden = hidden;
+  a.tokens = tokens;
+  a.n_acc = n_acc;
+  a.drafts = drafts;
+  a.z = (float*)(w8 + y.z);
+  a.u = (float*)(w8 + y.u);
+  a.y = (float*)(w8 + y.y);
+  a.xp = (float*)(w8 + y.xp);
+  a.prev = (float*)(w8 + y.prev);
+  a.hid = (float*)(w8 + y.hid);
+  a.dead = (int32_t*)(w8 + y.dead);
+  a.trace = trace;
+  float* an = (float*)(w8 + y.a);
+  int32_t* lm_nacc = (int32_t*)(w8 + y.lmi);
+  int32_t* lm_tok = lm_nacc + G;
+  std::vector<int32_t> gs1(G + 1);
+  for (int g = 0; g <= G; ++g) gs1[g] = g;  // the lm_head pass: one row per group, no drafts
+  hipStream_t st = S(stream);
+  const int cu = device_cu_count();
+  for (int pass = 0; pass < n_draft; ++pass) {
+    const int rows = pass == 0 ? T : G;
+    hipError_t e = mk::launch_mtp_in(a, pass, rows, st);
+    if (e != hipSuccess) return launch_status(e, "mtp: input rows");
+    if ((r = mk_qgemv_rows_ex(&m->fc, a.z, rows, a.u, MK_PATH_AUTO, w8 + y.gemv, y.ws_gemv, stream))) return r;
+    if ((e = mk::launch_rms_rows(a.u, an, rows, H, st)) != hipSuccess) return launch_status(e, "mtp: norm");
+    if ((r = mk_ffn_rows(&m->gate, &m->up, &m->down, an, rows, a.y, nullptr, w8 + y.ffn, y.ws_ffn, stream))) return r;
+    const int trace_row0 = pass == 0 ? 0 : T + (pass - 1) * G;
+    if ((e = mk::launch_mtp_out(a, pass, rows, trace_row0, st)) != hipSuccess) return launch_status(e, "mtp: output rows");
+    if ((e = mk::launch_lmhead(embed_f16, V_draft, H, a.hid, G, gs1.data(), G, nullptr, drafts + (size_t)pass * G,
+                               lm_nacc, lm_tok, w8 + y.lm, cu, st)) != hipSuccess)
+      return launch_status(e, "mtp: draft lm_head");
+  }
+  return ok();
+}
+
 // ------------------------------------------------------------------ Gated DeltaNet
 static int check_dn(const mk_deltanet* st) {
   int r;

@@ -82,6 +82,29 @@ struct SampleArgs {
 };
 hipError_t launch_sample(const SampleArgs& a, hipStream_t st);
 
+// MTP draft loop (mk_mtp.hip): the row kernels around the GEMV, FFN and
+// lm_head launches of each pass.
+struct MtpArgs {
+  const uint16_t* embed;  // [V][H] fp16 bits (the tied lm_head)
+  int V, H, T, G;
+  int gs[MK_LM_MAX_G + 1];
+  const float* hidden;    // [T][H] main-model final residual
+  const int32_t* tokens;  // [T] emitted tokens of the step
+  const int32_t* n_acc;   // [G]
+  int32_t* drafts;        // [n_draft][G]
+  float* z;               // [T][2H] pass input
+  float* u;               // [T][H] fc output
+  float* y;               // [T][H] FFN output
+  float* xp;              // [T][H] x' = u + y
+  float* prev;            // [G][H] x' of the row that continues each group's chain
+  float* hid;             // [G][H] RMSNorm(prev): the lm_head input
+  int32_t* dead;          // [G] groups whose accept length was out of range
+  float* trace;           // optional [T + G (n_draft - 1)][H]
+};
+hipError_t launch_mtp_in(const MtpArgs& a, int pass, int rows, hipStream_t st);
+hipError_t launch_rms_rows(const float* in, float* out, int rows, int H, hipStream_t st);
+hipError_t launch_mtp_out(const MtpArgs& a, int pass, int rows, int trace_row0, hipStream_t st);
+
 // Gated DeltaNet: one wave per half head (dk = dv = 128).
 struct GdnArgs {
   float* S;              // [nh][128][128]

@@ -214,6 +214,44 @@ int mk_lmhead_sample(const uint16_t* W_f16, int32_t V, int32_t H, const float* h
                      const float* u_acc, const float* u_samp, int32_t* topk_idx, float* topk_logit, int32_t* n_acc,
                      int32_t* tokens, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------- MTP draft loop */
+/* richland.au single-stream article, section "What shipped": after the
+ * verification, MTP catch-up rows for the accepted tokens, then n_draft MTP
+ * draft steps, with drafting restricted to the 32,768 most frequent tokens;
+ * the 4-agent article, section "Why it matters": every agent drafts its own
+ * tokens in the same rows.  The pages name the head's work, not its layers;
+ * the synthetic head here is one pass of
+ *   z = [RMSNorm(f32 E[token]) ; RMSNorm(hidden)],  u = fc . q8(z),
+ *   x' = u + FFN(RMSNorm(u))   (FFN as in the stack),
+ * with the embedding E tied to the lm_head.  A draft is the argmax of
+ * RMSNorm(x') over the first V_draft rows of E (lowest index on ties, NaN never
+ * wins).
+ * Pass 0 (catch-up) runs every row t of the step: group g's rows
+ * i = 0..n_acc[g] pair the main model's final residual hidden[gs[g] + i] with
+ * the token emitted after it, tokens[gs[g] + i] (the accepted drafts, then
+ * the bonus token, as mk_lmhead_verify writes them); row gs[g] + n_acc[g]
+ * gives group g's draft 1.  Pass k = 1..n_draft-1 runs one row per group:
+ * draft k with the x' of the row that produced it gives draft k + 1.  Every
+ * pass reads the head's weights once for all of its rows; n_acc and the
+ * drafts are read on the device, so the loop never returns to the host.
+ *   m: fc is H x 2H (H % 256 == 0); gate, up F x H; down H x F
+ *   embed_f16 [V][H] fp16 bits (device), V_draft <= V
+ *   hidden [T][H] fp32, tokens [T] int32, n_acc [G] int32 (device)
+ *   drafts [n_draft][G] int32 (device output); a group whose n_acc is outside
+ *     0..rows-1 gets -1 for every draft
+ *   trace (device, optional): [T + G (n_draft - 1)][H] x' of every row of
+ *     every pass (pass 0's rows past a group's n_acc are not catch-up rows:
+ *     they run on zero inputs and their values carry no meaning)
+ * 1 <= T <= 16, groups as in mk_lmhead_verify, 1 <= n_draft <= 16.
+ * Asynchronous on `stream` (several launches per pass). */
+typedef struct {
+  mk_q4k fc, gate, up, down;
+} mk_mtp;
+size_t mk_mtp_draft_workspace(const mk_mtp* m, int32_t V_draft, int32_t T, int32_t G);
+int mk_mtp_draft(const mk_mtp* m, const uint16_t* embed_f16, int32_t V, int32_t V_draft, const float* hidden,
+                 int32_t T, const int32_t* h_group_start, int32_t G, const int32_t* tokens, const int32_t* n_acc,
+                 int32_t n_draft, int32_t* drafts, float* trace, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------- Gated DeltaNet */
 /* richland.au single-stream article, section "What shipped": the recurrent
  * state is committed only through the surely-accepted token, and drafted rows

@@ -122,6 +122,19 @@ def test_host_validation_before_any_gpu_work():
                               None) == mk.MK_ERR_ARG
     assert L.mk_lmhead_sample(x, 100, 512, x, 5, None, 1, x, 8, f(0.6), x, x, None, None, x, x, x, 64,
                               None) == mk.MK_ERR_WORKSPACE
+    # MTP draft loop: head shapes must chain, V_draft <= V, n_draft in 1..16
+    fc, g_, u_, d_ = _q4k(fake, 512, 1024), _q4k(fake, 768, 512), _q4k(fake, 768, 512), _q4k(fake, 512, 768)
+    head = mk.mk_mtp(fc, g_, u_, d_)
+    bad = mk.mk_mtp(_q4k(fake, 512, 768), g_, u_, d_)
+    assert L.mk_mtp_draft(ctypes.byref(bad), x, 1000, 300, x, 5, None, 1, x, x, 2, x, None, x, 1 << 30,
+                          None) == mk.MK_ERR_SHAPE
+    assert L.mk_mtp_draft(ctypes.byref(head), x, 1000, 1001, x, 5, None, 1, x, x, 2, x, None, x, 1 << 30,
+                          None) == mk.MK_ERR_RANGE
+    assert L.mk_mtp_draft(ctypes.byref(head), x, 1000, 300, x, 5, None, 1, x, x, 0, x, None, x, 1 << 30,
+                          None) == mk.MK_ERR_RANGE
+    assert L.mk_mtp_draft(ctypes.byref(head), x, 1000, 300, x, 5, None, 1, x, x, 2, x, None, x, 64,
+                          None) == mk.MK_ERR_WORKSPACE
+    assert mk.lib().mk_mtp_draft_workspace(ctypes.byref(head), 300, 5, 1) > 5 * 1024 * 4
     # the no-allocation GEMV refuses shapes whose workspace exceeds its array, before any device call
     Wbig = _q4k(fake, 32768, 32768)
     assert L.mk_qgemv_rows_noalloc(ctypes.byref(Wbig), x, 16, x, 0, None) == mk.MK_ERR_WORKSPACE
