@@ -407,8 +407,9 @@ int mk_lmhead_verify(const uint16_t* W_f16, int32_t V, int32_t H, const float* h
 // Workspace: the lm_head stream's (ticket, fragments, block winners), the
 // rows' prescale exponents, every logit [T][V], the candidates [T][32] x 2.
 size_t mk_lmhead_sample_workspace(int32_t V, int32_t H, int32_t T) {
-  if (V <= 0 || H <= 0 || H % 64 || T < 1 || T > MK_T_MAX) return 0;
-  return mk::lm_workspace_bytes(V, H) + 256 + align256((size_t)T * V * 4) + 2 * align256((size_t)T * mk::kTopKMax * 4);
+  if (V <= 0 || V > mk::kSampleMaxVocab || H <= 0 || H % 64 || T < 1 || T > MK_T_MAX) return 0;
+  return mk::lm_workspace_bytes(V, H) + 256 + align256((size_t)T * V * 4) + 2 * align256((size_t)T * mk::kTopKMax * 4) +
+         align256(mk::sample_part_bytes(V, T));
 }
 
 int mk_lmhead_sample(const uint16_t* W_f16, int32_t V, int32_t H, const float* hid, int32_t T,
@@ -417,7 +418,8 @@ int mk_lmhead_sample(const uint16_t* W_f16, int32_t V, int32_t H, const float* h
                      int32_t* tokens, void* ws, size_t ws_bytes, void* stream) {
   int r;
   if ((r = check_T(T))) return r;
-  if (V <= 0 || H <= 0 || H % 64) return fail(MK_ERR_SHAPE, "sample: V = %d, H = %d (H % 64 == 0)", V, H);
+  if (V <= 0 || V > mk::kSampleMaxVocab || H <= 0 || H % 64)
+    return fail(MK_ERR_SHAPE, "sample: V = %d (at most %d), H = %d (H %% 64 == 0)", V, mk::kSampleMaxVocab, H);
   if (top_k < 1 || top_k > mk::kTopKMax) return fail(MK_ERR_RANGE, "sample: top_k = %d outside 1..%d", top_k, mk::kTopKMax);
   if (!(temperature > 0.0f) || !(temperature < 3.0e38f))
     return fail(MK_ERR_RANGE, "sample: temperature %g is not a positive finite value", (double)temperature);
@@ -442,6 +444,8 @@ int mk_lmhead_sample(const uint16_t* W_f16, int32_t V, int32_t H, const float* h
   int32_t* cidx = topk_idx ? topk_idx : (int32_t*)p;
   p += align256((size_t)T * mk::kTopKMax * 4);
   float* cval = topk_logit ? topk_logit : (float*)p;
+  p += align256((size_t)T * mk::kTopKMax * 4);
+  void* part = p;
   hipError_t e = mk::launch_lm_stream(W_f16, V, H, hid, T, gs.data(), G, drafts, nullptr, nullptr, nullptr, lm_ws,
                                       device_cu_count(), S(stream), logits, row_exp);
   if (e != hipSuccess) return launch_status(e, "sample: lm_head");
@@ -461,7 +465,7 @@ int mk_lmhead_sample(const uint16_t* W_f16, int32_t V, int32_t H, const float* h
   a.u_samp = u_samp;
   a.n_acc = n_acc;
   a.tokens = tokens;
-  return launch_status(mk::launch_sample(a, S(stream)), "sample");
+  return launch_status(mk::launch_sample(a, part, S(stream)), "sample");
 }
 
 // ------------------------------------------------------------------ MTP draft loop

@@ -80,7 +80,10 @@ struct SampleArgs {
   int32_t* n_acc;        // [G]
   int32_t* tokens;       // [T]
 };
-hipError_t launch_sample(const SampleArgs& a, hipStream_t st);
+// part: the first level's candidates, sample_part_bytes(V, T) bytes.
+constexpr int kSampleMaxVocab = 1 << 21;  // the second level's candidates fit its LDS up to this vocabulary
+size_t sample_part_bytes(int V, int T);
+hipError_t launch_sample(const SampleArgs& a, void* part, hipStream_t st);
 
 // MTP draft loop (mk_mtp.hip): the row kernels around the GEMV, FFN and
 // lm_head launches of each pass.

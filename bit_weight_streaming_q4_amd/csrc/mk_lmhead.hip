@@ -12,28 +12,35 @@
 
 namespace mk {
 
-// hid [T][H] fp32 -> fragments [H/64][64 lanes][hi 16 | lo 16] fp16 for the
-// B operand: lane l = 16*kq + t holds h = 64c + 16kq + e, e = 0..15 of row t
-// (zeros for t >= T).  One block per row t < 16.
-// Each row is first multiplied by the power of two 2^k that brings its
-// largest magnitude into [2^14, 2^15), so that hi never overflows fp16 and
-// lo stays out of the fp16 subnormals for every element that matters.  The
-// scaling is exact and multiplies every logit of the row by the same 2^k,
-// so the argmax is unchanged; rows are accepted at any fp32 magnitude (a row
-// holding inf or only zeros is left unscaled).
-// row_exp (optional, [16]) receives each row's k, so that a caller that
-// needs the logits themselves can scale them back exactly by 2^-k.
-__global__ __launch_bounds__(256) void k_lm_prep(const float* __restrict__ hid, int T, int H,
-                                                 _Float16* __restrict__ frag, unsigned* __restrict__ ticket,
-                                                 int* __restrict__ row_exp) {
+// Each lm_head input row is multiplied by the power of two 2^k that brings
+// its largest magnitude into [2^14, 2^15), so that the fp16 hi part never
+// overflows and the lo part stays out of the fp16 subnormals for every
+// element that matters.  The scaling is exact and multiplies every logit of
+// the row by the same 2^k, so the argmax is unchanged; rows are accepted at
+// any fp32 magnitude (a row holding inf or only zeros is left unscaled).
+// One block per row t < 16 writes row_exp[t] = k (0 for t >= T); block 0 also
+// clears the lm_head kernel's arrival counter.
+__global__ __launch_bounds__(256) void k_lm_rowexp(const float* __restrict__ hid, int T, int H,
+                                                   int* __restrict__ row_exp, unsigned* __restrict__ ticket) {
   __shared__ float wmax[4];
   const int t = blockIdx.x, tid = threadIdx.x;
-  if (t == 0 && tid == 0) *ticket = 0u;  // the lm_head kernel's arrival counter
-  const float* row = hid + (size_t)t * H;
+  if (t == 0 && tid == 0) *ticket = 0u;
   int k = 0;
   if (t < T) {
+    const float* row = hid + (size_t)t * H;
     float m = 0.0f;
-    for (int i = tid; i < H; i += 256) m = __builtin_fmaxf(m, __builtin_fabsf(row[i]));  // NaN is ignored
+    if (H % 1024 == 0 && H <= 8192) {  // all of the thread's loads in flight together
+      f32x4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v[j] = 1024 * j < H ? *(const f32x4*)(row + 1024 * j + 4 * tid) : (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) m = __builtin_fmaxf(m, __builtin_fabsf(v[j][e]));
+    } else {
+      for (int i = tid; i < H; i += 256) m = __builtin_fmaxf(m, __builtin_fabsf(row[i]));  // NaN is ignored
+    }
     for (int o = 32; o >= 1; o >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, o, 64));
     if ((tid & 63) == 0) wmax[tid >> 6] = m;
     __syncthreads();
@@ -44,13 +51,27 @@ __global__ __launch_bounds__(256) void k_lm_prep(const float* __restrict__ hid, 
       k = 15 - e;
     }
   }
-  if (row_exp && tid == 0) row_exp[t] = k;
-  for (int i = tid; i < H; i += 256) {
-    const int c = i >> 6, r = i & 63, l = 16 * (r >> 4) + t, e = r & 15;
-    const float x = t < T ? __builtin_ldexpf(row[i], k) : 0.0f;
+  if (tid == 0) row_exp[t] = k;
+}
+
+// hid [T][H] fp32, scaled by 2^row_exp[t] -> fragments [H/64][64 lanes][hi 16 | lo 16]
+// fp16 for the B operand: lane l = 16*kq + t holds h = 64c + 16kq + e,
+// e = 0..15 of row t (zeros for t >= T).
+__global__ __launch_bounds__(64) void k_lm_prep(const float* __restrict__ hid, int T, int H,
+                                                _Float16* __restrict__ frag, const int* __restrict__ row_exp) {
+  const int c = blockIdx.x, l = threadIdx.x;
+  const int t = l & 15, kq = l >> 4;
+  const int k = row_exp[t];
+  _Float16* o = frag + ((size_t)c * 64 + l) * 32;
+  f32x4 v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    v[q] = t < T ? *(const f32x4*)(hid + (size_t)t * H + 64 * c + 16 * kq + 4 * q) : (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float x = __builtin_ldexpf(v[e >> 2][e & 3], k);
     const _Float16 hi = (_Float16)x;
     const _Float16 lo = (_Float16)(x - (float)hi);
-    _Float16* o = frag + ((size_t)c * 64 + l) * 32;
     o[e] = hi;
     o[16 + e] = lo;
   }
@@ -142,7 +163,8 @@ hipError_t launch_lm_stream(const uint16_t* W, int V, int H, const float* hid, i
                             const int32_t* drafts, int32_t* argmax, int32_t* n_acc, int32_t* tokens, void* ws,
                             int cu_count, hipStream_t st, float* logits, int* row_exp) {
   uint8_t* p = (uint8_t*)ws;
-  uint32_t* ticket = (uint32_t*)p;
+  uint32_t* ticket = (uint32_t*)p;            // word 0 of the first 256 B
+  int* rexp = row_exp ? row_exp : (int*)(p + 64);  // words 16..31 (unless the caller keeps them)
   p += 256;
   _Float16* frag = (_Float16*)p;
   p += (lm_frag_bytes(H) + 255) / 256 * 256;
@@ -150,7 +172,8 @@ hipError_t launch_lm_stream(const uint16_t* W, int V, int H, const float* hid, i
   float* pval = (float*)p;
   p += ((size_t)nblk * 16 * 4 + 255) / 256 * 256;
   int32_t* pidx = (int32_t*)p;
-  hipLaunchKernelGGL(k_lm_prep, dim3(16), dim3(256), 0, st, hid, T, H, frag, ticket, row_exp);
+  hipLaunchKernelGGL(k_lm_rowexp, dim3(16), dim3(256), 0, st, hid, T, H, rexp, ticket);
+  hipLaunchKernelGGL(k_lm_prep, dim3(H / 64), dim3(64), 0, st, hid, T, H, frag, rexp);
   LmArgs a;
   a.s.W = W;
   a.s.frag = frag;

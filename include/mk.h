@@ -204,8 +204,11 @@ int mk_lmhead_verify(const uint16_t* W_f16, int32_t V, int32_t H, const float* h
  *     slots -1 / -inf
  *   n_acc [G], tokens [T] (device) as in mk_lmhead_verify.
  * 1 <= top_k <= 32 and 0 < temperature < inf (MK_ERR_RANGE otherwise);
- * H % 64 == 0.  Four launches: lm_head prep, the lm_head stream writing every
- * logit into the workspace, top-k per row, the accept / resample pass.
+ * H % 64 == 0; V <= 2^21 (MK_ERR_SHAPE).  Six launches: the rows' prescale
+ * exponents, the lm_head fragments, the lm_head stream writing every logit
+ * into the workspace, the top-k of every 8192-logit chunk (staged in LDS),
+ * the top-k of every row from its chunks' candidates, the accept / resample
+ * pass.
  * The hidden rows are prescaled as in mk_lmhead_verify; the logits returned
  * in topk_logit are scaled back exactly. */
 size_t mk_lmhead_sample_workspace(int32_t V, int32_t H, int32_t T);
