@@ -587,6 +587,55 @@ def cpu_baseline(T=12, budget_s=20.0):
             "sample": f"{layers} of {LAYERS} layers + {lmrows} of {VOCAB} lm_head rows at T={T}, {dt:.1f} s of oracle time"}
 
 
+# ------------------------------------------------------------------ HBM traffic record
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_per_dispatch(d, counter, kernel_sub):
+    """Mean over the matching dispatches of the counter's value (summed over
+    its instances within a dispatch)."""
+    per = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if kernel_sub in r.get("Kernel_Name", "") and r.get("Counter_Name") == counter:
+            k = r.get("Dispatch_Id") or r.get("Correlation_Id")
+            per[k] = per.get(k, 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise ValueError(f"no {counter} rows for {kernel_sub} under {d}")
+    return float(np.mean(list(per.values()))), len(per)
+
+
+def traffic_record(root):
+    """The traffic record of k_decode_step<12> from rocprofv3 output under
+    root: trace/ (--kernel-trace --stats), fetch/ and write/ (--pmc FETCH_SIZE,
+    WRITE_SIZE on the bench), copy_fetch/ and copy_write/ (the same counters on
+    --copy-probe).  Counter values are KiB per dispatch; each is scaled by what
+    the same counter reads for the plain 1 GiB copy."""
+    kern = "k_decode_step<12>"
+    stats = [r for r in _csv_rows(os.path.join(root, "trace"), "kernel_stats.csv") if kern in r.get("Name", "")]
+    avg_ns, calls = float(stats[0]["AverageNs"]), int(stats[0]["Calls"])
+    fetch, nf = _counter_per_dispatch(os.path.join(root, "fetch"), "FETCH_SIZE", kern)
+    write, nw = _counter_per_dispatch(os.path.join(root, "write"), "WRITE_SIZE", kern)
+    # the copy probe's device-to-device copies (its first dispatch is the fill of the source)
+    cf, _ = _counter_per_dispatch(os.path.join(root, "copy_fetch"), "FETCH_SIZE", "copyBuffer")
+    cw, _ = _counter_per_dispatch(os.path.join(root, "copy_write"), "WRITE_SIZE", "copyBuffer")
+    copy_bytes = 1 << 30
+    fs, ws = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    rd, wr = fetch * 1024 * fs, write * 1024 * ws
+    return {"kernel": kern, "kernel_source_hash": kernel_source_hash(), "fetch_size_kib_per_dispatch": fetch,
+            "write_size_kib_per_dispatch": write, "dispatches_fetch": nf, "dispatches_write": nw,
+            "copy_probe_bytes": copy_bytes, "copy_probe_fetch_kib": cf, "copy_probe_write_kib": cw,
+            "fetch_scale": fs, "write_scale": ws, "bytes_per_launch": int(rd + wr), "read_bytes_per_launch": int(rd),
+            "write_bytes_per_launch": int(wr), "algorithmic_bytes_per_launch": step_bytes(12, 4)["total"],
+            "kernel_avg_ns": avg_ns, "kernel_calls": calls}
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
@@ -600,12 +649,20 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="also time the step at every T in 1..12 and 16")
     ap.add_argument("--series", type=int, default=100,
                     help="also time this many seeded T = 12 steps, each with its own inputs (0: skip)")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="write the traffic record from rocprofv3 output under DIR (no GPU work) and exit")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_from:
+        rec = traffic_record(args.traffic_from)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec), flush=True)
+        return
     import torch
 
     import __graft_entry__

@@ -265,3 +265,47 @@ def test_decode_step_accept_length_out_of_range():
     og = to_np(go)
     _, o_ref = oracle.gdn_step(S0[1], inp["q"][3:], inp["k"][3:], inp["v"][3:], inp["g"][3:], inp["beta"][3:], 0)
     assert rel_err(og[3:], o_ref) <= FP32_TOL
+
+
+@pytest.mark.parametrize("gs_ride,rows", [([0, 10, 13, 16], (0, 10)), ([0, 3, 6, 16], (6, 16))])
+def test_decode_step_prompt_chunk_is_bit_identical(gs_ride, rows):
+    """A new prompt's chunk riding in a step beside other agents' rows gives,
+    bit for bit, what the chunk gives when the step processes it on its own:
+    residuals after every layer, argmax, Gated DeltaNet outputs and the
+    chunk's committed state (the 4-agent article, "Why it matters").  Both
+    steps run the 16-row matrix-core engine (T = 16 and T = 10)."""
+    torch = need_gpu()
+    mk = _mk()
+    L, H, P, F, V = 4, 512, 1024, 768, 1000
+    T = gs_ride[-1]
+    r0, r1 = rows
+    n = r1 - r0
+    ci = [g for g in range(len(gs_ride) - 1) if gs_ride[g] == r0][0]  # the chunk's group
+    x = synth.normal_f32(51, 10000, 0, T * H).reshape(T, H)
+    ride, _, _, _, S0, nh = small_stack(mk, 51, L, H, P, F, V, len(gs_ride) - 1, T_max=n)
+    inp = synth.gdn_step_inputs(51, 20000, T, nh, 128, 128)
+    # the chunk alone: one agent whose state is the riding chunk's agent state
+    alone, _, _, _, _, _ = small_stack(mk, 51, L, H, P, F, V, 1, T_max=n)
+    alone.agents[0].S.copy_(to_dev(S0[ci].copy()))
+    out = {}
+    for name, st, xs, gs, sl in (("ride", ride, x, gs_ride, slice(0, T)), ("alone", alone, x[r0:r1], [0, n],
+                                                                          slice(r0, r1))):
+        Tn = xs.shape[0]
+        G = len(gs) - 1
+        drafts = to_dev(np.arange(1, Tn - G + 1, dtype=np.int32) if Tn > G else np.zeros(1, np.int32))
+        gin = {k: to_dev(np.ascontiguousarray(inp[k][sl])) for k in ("q", "k", "v", "g", "beta")}
+        go = torch.empty(Tn, nh, 128, dtype=torch.float32, device="cuda")
+        tr = torch.empty(L, Tn, H, dtype=torch.float32, device="cuda")
+        am = torch.empty(Tn, dtype=torch.int32, device="cuda")
+        say("prompt chunk", name, gs)
+        mk.mk_decode_step(st, to_dev(xs), gs, drafts, gdn=gin, gdn_o=go, argmax=am, trace=tr)
+        a = st.agents[ci if name == "ride" else 0]
+        st.agents[ci if name == "ride" else 0].n_acc[0] = n - 1  # commit the whole chunk
+        mk.mk_deltanet_commit(a)
+        out[name] = (to_np(tr), to_np(am), to_np(go), to_np(a.S))
+    tr_r, am_r, go_r, S_r = out["ride"]
+    tr_a, am_a, go_a, S_a = out["alone"]
+    assert np.array_equal(tr_r[:, r0:r1], tr_a)
+    assert np.array_equal(am_r[r0:r1], am_a)
+    assert np.array_equal(go_r[r0:r1], go_a)
+    assert np.array_equal(S_r, S_a)
