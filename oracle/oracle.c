@@ -29,8 +29,10 @@
  * accumulation; outputs rounded to fp32 where the GPU's dataflow stores fp32.
  *
  * Readings of the pages where they are silent:
- *   - activation scale s = fl32(amax/127) by IEEE division, codes
- *     clamp(rne(fl32(x/s)), -127, 127), amax == 0 gives s = 0 and codes 0;
+ *   - activation scale s = fl32(amax/127) by IEEE division (amax over the
+ *     group's non-NaN elements), codes clamp(rne(fl32(x/s)), -127, 127);
+ *     s == 0 (an all-zero group, or amax/127 underflowing) gives zero codes,
+ *     and an element whose x/s is NaN codes as 0;
  *   - the delta rule is S <- g (I - beta k k^T) S + beta k v^T with S of shape
  *     dk x dv and o = S^T q after the update; the literal printed form
  *     S <- g S (I - beta k k^T) + beta k v^T is kept behind a flag;
@@ -94,14 +96,18 @@ void orc_quantize_rows(const float* x, int32_t T, int32_t K, int8_t* a8, float* 
       }
       int8_t* ag = a8 + t * K + g * 32;
       int32_t sum = 0;
-      if (amax == 0.0f) {
+      /* amax/127 is 0 for an all-zero group and also when it underflows (amax
+       * at most 63 * 2^-149); such a group has no usable scale and gets s = 0
+       * and zero codes */
+      const float sg = amax / 127.0f;
+      if (sg == 0.0f) {
         s[t * ng + g] = 0.0f;
         for (int i = 0; i < 32; ++i) ag[i] = 0;
       } else {
-        const float sg = amax / 127.0f;
         s[t * ng + g] = sg;
         for (int i = 0; i < 32; ++i) {
           float r = nearbyintf(xg[i] / sg); /* round-half-to-even (default mode) */
+          if (r != r) r = 0.0f;             /* a NaN element (or inf/inf) codes as 0 */
           if (r > 127.0f) r = 127.0f;
           if (r < -127.0f) r = -127.0f;
           ag[i] = (int8_t)r;

@@ -104,6 +104,37 @@ def test_quantizer_identity_and_round_half_even(orc):
     assert list(a8[0, 1:9]) == [0, 2, 2, 0, -2, -2, 4, 126]
 
 
+def test_quantizer_underflowing_scale_nan_and_inf(orc):
+    """Groups with no usable scale and non-finite elements, from the reading:
+    s = fl32(amax / 127) over the non-NaN elements; s == 0 (amax at most
+    63 * 2^-149, where amax / 127 rounds to zero) or an all-NaN group gives
+    s = 0 and zero codes; a NaN quotient codes as 0."""
+    tiny = np.float32(2.0 ** -149)
+    x = np.zeros((6, 32), np.float32)
+    k = np.arange(32) - 16
+    x[0] = (k % 4) * tiny                              # amax 3 * 2^-149
+    x[1] = np.where(k == 0, 63, -(k % 7)) * tiny       # amax 63 * 2^-149: 63/127 * 2^-149 rounds to 0
+    x[2] = np.clip(k * 4, -64, 64) * tiny              # amax 64 * 2^-149: s = 2^-149 exactly
+    x[3] = synth.normal_f32(11, 2, 0, 32)
+    x[3, 5] = np.nan
+    x[4] = np.nan
+    x[5] = synth.normal_f32(11, 3, 0, 32)
+    x[5, 7] = np.inf
+    x[5, 9] = -np.inf
+    a8, s, gs = orc.quantize_rows(x)
+    assert np.array_equal(s[:2, 0], [0.0, 0.0]) and not a8[:2].any() and not gs[:2].any()
+    assert s[2, 0] == tiny and np.array_equal(a8[2], np.clip(k * 4, -64, 64))
+    # a NaN element: amax and the other codes as if it were 0, its code 0
+    x3 = x[3:4].copy()
+    x3[0, 5] = 0.0
+    a8z, sz, _ = orc.quantize_rows(x3)
+    assert s[3, 0] == sz[0, 0] and np.array_equal(a8[3], a8z[0]) and a8[3, 5] == 0
+    assert s[4, 0] == 0.0 and not a8[4].any()
+    # infinite amax: every finite element codes as 0 and inf / inf is NaN -> 0
+    assert np.isinf(s[5, 0]) and not a8[5].any() and gs[5, 0] == 0
+    assert np.array_equal(gs[:, 0], a8.astype(np.int64).sum(1))
+
+
 # ----------------------------------------------------------------- C1 + C3 GEMV
 def _brute_gemv(W, a8, s):
     """Exact rational y[t][o] = sum_k (d*sc*q - dmin*m) * s * a8 from the definition."""
