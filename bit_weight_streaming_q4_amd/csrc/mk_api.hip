@@ -269,7 +269,9 @@ int mk_quantize_rows(const float* x, int32_t T, int32_t K, int8_t* a8, float* s,
 size_t mk_qgemv_rows_workspace(int32_t T, int32_t n_out, int32_t n_in) {
   if (T < 1 || T > MK_T_MAX || n_out <= 0 || n_in <= 0 || n_in % 256) return 0;
   const mk::GemvPlan p = mk::plan_gemv(T, n_out, n_in, 1, device_cu_count());
-  return qact_bytes(T, n_in) + align256((size_t)p.ntiles * 4) + align256(p.partial_elems * 4);
+  const size_t std_path = qact_bytes(T, n_in) + align256((size_t)p.ntiles * 4) + align256(p.partial_elems * 4);
+  const size_t step_path = mk::engine_gemv_workspace(T, n_out, n_in);
+  return std_path > step_path ? std_path : step_path;
 }
 
 int mk_qgemv_rows_ex(const mk_q4k* W, const float* x, int32_t T, float* y, int32_t path, void* ws,
@@ -277,7 +279,15 @@ int mk_qgemv_rows_ex(const mk_q4k* W, const float* x, int32_t T, float* y, int32
   int r;
   if ((r = check_q4k(W, "W")) || (r = check_T(T)) || (r = check_ptr(x, "x")) || (r = check_ptr(y, "y")))
     return r;
-  if (path < MK_PATH_AUTO || path > MK_PATH_MFMA) return fail(MK_ERR_ARG, "unknown path %d", path);
+  if (path < MK_PATH_AUTO || path > MK_PATH_STEP) return fail(MK_ERR_ARG, "unknown path %d", path);
+  if (path == MK_PATH_STEP) {
+    const size_t need = mk_qgemv_rows_workspace(T, W->n_out, W->n_in);
+    if (!ws || ws_bytes < need) return fail(MK_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    if ((r = check_ptr(ws, "workspace", 256))) return r;
+    return launch_status(mk::launch_engine_gemv((const uint8_t*)W->blocks, W->n_out, W->n_in, x, T, y, (uint8_t*)ws,
+                                                 S(stream)),
+                         "step-engine gemv");
+  }
   const int eng = pick_path(path, T);
   if (eng == MK_PATH_DOT4 && T > mk::kDot4MaxT)
     return fail(MK_ERR_RANGE, "dot4 path supports T <= %d (T = %d)", mk::kDot4MaxT, T);

@@ -355,16 +355,19 @@ __device__ __forceinline__ int sum64_i(int v) {
 }
 
 __device__ __forceinline__ Q8 quant_group32(float x) {
+  // amax over the group's non-NaN lanes (fmax drops a NaN operand)
   const float amax = max32(__builtin_fabsf(x));
+  const float s = amax / 127.0f;
   Q8 r;
-  if (amax == 0.0f) {
+  if (!(s > 0.0f)) {
+    // an all-zero group, a scale that underflows, or a group of NaN only
     r.s = 0.0f;
     r.a8 = 0;
   } else {
-    r.s = amax / 127.0f;
-    float q = __builtin_rintf(x / r.s);
-    q = __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
-    r.a8 = (int)q;
+    r.s = s;
+    const float q = __builtin_rintf(x / s);
+    // a NaN quotient (a NaN element, or inf / inf) codes as 0
+    r.a8 = q == q ? (int)__builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f) : 0;
   }
   r.gsum = sum32_i(r.a8);
   return r;

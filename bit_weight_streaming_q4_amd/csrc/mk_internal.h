@@ -30,6 +30,12 @@ struct GemvPlan {
   int ntiles, nsb, per_wg, ksplit, nmat;
   size_t partial_elems;  // nmat * ksplit * T * ntiles*64
 };
+// The step's engines on a plain T-row GEMV (records by the step's epilogue
+// quantizer); workspace: the records, then the split partials.
+size_t engine_gemv_workspace(int T, int N, int K);
+hipError_t launch_engine_gemv(const uint8_t* W, int N, int K, const float* x, int T, float* y, uint8_t* ws,
+                              hipStream_t st);
+
 GemvPlan plan_gemv(int T, int n_out, int n_in, int nmat, int cu_count);
 
 // What the last block of each tile does with the summed split-K partials.

@@ -402,13 +402,16 @@ __device__ __forceinline__ void store_q8(uint8_t* rec, int tau, int lane, const 
     float amax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(x[0]), __builtin_fabsf(x[1])),
                                  __builtin_fmaxf(__builtin_fabsf(x[2]), __builtin_fabsf(x[3])));
     amax = max8(amax);
-    float sc = 0.0f;
+    float sc = amax / 127.0f;
     int c[4] = {0, 0, 0, 0};
-    if (amax != 0.0f) {
-      sc = amax / 127.0f;
+    if (sc > 0.0f) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        c[i] = (int)__builtin_fminf(__builtin_fmaxf(__builtin_rintf(x[i] / sc), -127.0f), 127.0f);
+      for (int i = 0; i < 4; ++i) {
+        const float r = __builtin_rintf(x[i] / sc);
+        c[i] = r == r ? (int)__builtin_fminf(__builtin_fmaxf(r, -127.0f), 127.0f) : 0;
+      }
+    } else {
+      sc = 0.0f;  // all zero, an underflowing scale, or NaN only: zero codes
     }
     const int gsum = sum8_i(c[0] + c[1] + c[2] + c[3]);
     *(uint32_t*)(cb + t * 8) =
@@ -1760,6 +1763,146 @@ static StepKernel step_kernel(int T) {
     case 15: return kernel_for<15>();
     case 16: return kernel_for<16>();
     default: return nullptr;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The step's engines on a plain T-row GEMV (the MK_PATH_STEP path of
+// mk_qgemv_rows_ex).  The activation records are written by the step's own
+// epilogue quantizer (store_q8) and every unit goes through the engine the
+// step uses for T rows, so that the integer sums of those engines and the
+// record layout can be checked exactly outside the persistent launch.
+
+// Activation record part of the 64-column tile blockIdx.x of x [T][K].
+template <int T>
+__global__ __launch_bounds__(64) void k_engine_records(const float* __restrict__ x, int K, uint8_t* rec) {
+  __shared__ uint8_t stage[1024 + 256] __attribute__((aligned(16)));
+  const int lane = threadIdx.x, tau = blockIdx.x;
+  // rows >= TPad stay zero in the stage, as in the step
+  for (int i = lane; i < (1024 + 256) / 4; i += 64) ((int*)stage)[i] = 0;
+  __syncthreads();
+  f32x4 v[RG<T>::G];
+  load_rows<T>(x, K, tau, lane, v);
+  store_q8<T>(rec, tau, lane, v, stage);
+}
+
+// Superblocks [per * blockIdx.y, + per) of 64-row tile blockIdx.x: each unit
+// and its record are copied into an LDS slot and run through the step's
+// engine; the wave's sums go to part[blockIdx.y][t][row].
+template <int T>
+__global__ __launch_bounds__(64) void k_engine_gemv(const uint8_t* __restrict__ W, const uint8_t* __restrict__ rec,
+                                                     int nsb, int N, int per, float* __restrict__ part) {
+  __shared__ uint8_t slot[kSlotBytes] __attribute__((aligned(16)));
+  const int lane = threadIdx.x, tile = blockIdx.x;
+  const int b0 = blockIdx.y * per, b1 = min(nsb, b0 + per);
+  float acc[T];
+  f32x4 macc[4];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = 0.0f;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) macc[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int b = b0; b < b1; ++b) {
+    const uint8_t* u = W + ((size_t)tile * nsb + b) * kUnitBytes;
+    const uint8_t* r = rec + (size_t)b * kActBytes;
+#pragma unroll
+    for (int i = 0; i < kUnitBytes / 1024; ++i)
+      *(u32x4*)(slot + i * 1024 + lane * 16) = *(const u32x4*)(u + i * 1024 + lane * 16);
+#pragma unroll
+    for (int i = 0; i < kActBytes / 1024; ++i)
+      *(u32x4*)(slot + kUnitBytes + i * 1024 + lane * 16) = *(const u32x4*)(r + i * 1024 + lane * 16);
+    __syncthreads();
+    lds_u8* sl = as_lds(slot);
+    if constexpr (!UseMfma<T>::value) {
+      slot_dot4<T>(sl, lane, acc);
+    } else if constexpr (PackMfma<T>::value) {
+      WregP xw;
+      read_w_pk(sl, lane, xw);
+      slot_mfma_pk(xw, sl, lane, macc);
+    } else {
+      WregM xw;
+      read_w_mfma(sl, lane, xw);
+      slot_mfma(xw, sl, lane, macc);
+    }
+    __syncthreads();
+  }
+  float* out = part + (size_t)blockIdx.y * T * N;
+  if constexpr (UseMfma<T>::value) {
+    if constexpr (PackMfma<T>::value) {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) macc[nb][i] += __shfl_xor(macc[nb][i], 32, 64);
+    }
+    // C layout: lane 16 q + n holds rows t = 4q .. 4q + 3 of tile row 16 nb + n
+    const int q = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * q + i, o = tile * 64 + 16 * nb + n;
+        if (t < T && o < N) out[(size_t)t * N + o] = macc[nb][i];
+      }
+  } else {
+    const int o = tile * 64 + lane;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+      if (o < N) out[(size_t)t * N + o] = acc[t];
+  }
+}
+
+// y = the sum of the split partials, in split order.
+__global__ __launch_bounds__(256) void k_engine_sum(const float* __restrict__ part, int nsplit, int n,
+                                                    float* __restrict__ y) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float v = part[i];
+  for (int sp = 1; sp < nsplit; ++sp) v += part[(size_t)sp * n + i];
+  y[i] = v;
+}
+
+// Superblocks per split: at most 8 splits.
+static int engine_per(int nsb) { return (nsb + 7) / 8; }
+
+size_t engine_gemv_workspace(int T, int N, int K) {
+  const int nsb = K / 256, per = engine_per(nsb), nsplit = (nsb + per - 1) / per;
+  const size_t rec = ((size_t)nsb * kActBytes + 255) & ~(size_t)255;
+  return rec + (size_t)nsplit * T * N * sizeof(float);
+}
+
+template <int T>
+static hipError_t engine_gemv_t(const uint8_t* W, int N, int K, const float* x, float* y, uint8_t* ws,
+                                hipStream_t st) {
+  const int nsb = K / 256, per = engine_per(nsb), nsplit = (nsb + per - 1) / per, ntiles = (N + 63) / 64;
+  uint8_t* rec = ws;
+  float* part = (float*)(ws + (((size_t)nsb * kActBytes + 255) & ~(size_t)255));
+  hipLaunchKernelGGL(k_engine_records<T>, dim3(K / 64), dim3(64), 0, st, x, K, rec);
+  hipLaunchKernelGGL(k_engine_gemv<T>, dim3(ntiles, nsplit), dim3(64), 0, st, W, (const uint8_t*)rec, nsb, N, per,
+                     part);
+  const int n = T * N;
+  hipLaunchKernelGGL(k_engine_sum, dim3((n + 255) / 256), dim3(256), 0, st, (const float*)part, nsplit, n, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_engine_gemv(const uint8_t* W, int N, int K, const float* x, int T, float* y, uint8_t* ws,
+                              hipStream_t st) {
+  switch (T) {
+    case 1: return engine_gemv_t<1>(W, N, K, x, y, ws, st);
+    case 2: return engine_gemv_t<2>(W, N, K, x, y, ws, st);
+    case 3: return engine_gemv_t<3>(W, N, K, x, y, ws, st);
+    case 4: return engine_gemv_t<4>(W, N, K, x, y, ws, st);
+    case 5: return engine_gemv_t<5>(W, N, K, x, y, ws, st);
+    case 6: return engine_gemv_t<6>(W, N, K, x, y, ws, st);
+    case 7: return engine_gemv_t<7>(W, N, K, x, y, ws, st);
+    case 8: return engine_gemv_t<8>(W, N, K, x, y, ws, st);
+    case 9: return engine_gemv_t<9>(W, N, K, x, y, ws, st);
+    case 10: return engine_gemv_t<10>(W, N, K, x, y, ws, st);
+    case 11: return engine_gemv_t<11>(W, N, K, x, y, ws, st);
+    case 12: return engine_gemv_t<12>(W, N, K, x, y, ws, st);
+    case 13: return engine_gemv_t<13>(W, N, K, x, y, ws, st);
+    case 14: return engine_gemv_t<14>(W, N, K, x, y, ws, st);
+    case 15: return engine_gemv_t<15>(W, N, K, x, y, ws, st);
+    case 16: return engine_gemv_t<16>(W, N, K, x, y, ws, st);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -97,8 +97,10 @@ int mk_q4k_unpack(const void* h_blocks, int32_t n_out, int32_t n_in, uint16_t* h
 
 /* ------------------------------------------------------ activation quantizer */
 /* Per row t and group of 32 consecutive elements: s = amax/127 (IEEE fp32
- * division; 0 when the group is all zero), a8 = clamp(rne(x/s), -127, 127),
- * gsum = sum of a8.  x [T][K], a8 [T][K], s and gsum [T][K/32]; K % 32 == 0.
+ * division, amax over the group's non-NaN elements), a8 = clamp(rne(x/s),
+ * -127, 127), gsum = sum of a8.  When s is 0 (an all-zero group, or amax at
+ * most 63 * 2^-149 so that amax/127 underflows) or the group is all NaN, s = 0
+ * and every code is 0; an element whose x/s is NaN codes as 0.  x [T][K], a8 [T][K], s and gsum [T][K/32]; K % 32 == 0.
  * Bit-identical to the CPU definition. */
 int mk_quantize_rows(const float* x, int32_t T, int32_t K, int8_t* a8, float* s, int32_t* gsum, void* stream);
 
@@ -120,11 +122,22 @@ int mk_qgemv_rows(const mk_q4k* W, const float* x, int32_t T, float* y, void* ws
  * MK_PATH_AUTO (dot4 for T <= 8, matrix cores from T = 9), MK_PATH_DOT4
  * (packed int8 dot products, T <= 8) or MK_PATH_MFMA (int8 matrix cores,
  * rows padded to 16).  Both engines give bit-identical results.
+ * MK_PATH_STEP runs the decode step's own engines and activation records on
+ * the same GEMV, so that they can be checked outside the persistent launch:
+ * the records are written by the step's epilogue quantizer (the rule of
+ * mk_quantize_rows) and each 64-row unit goes through the engine the step
+ * uses for T rows (dot4 at T = 1; two sub-blocks per 16x16x64 int8 matrix
+ * product up to 8 padded rows; one sub-block per 16x16x32 product above).
+ * Its results equal the other paths' up to the order of the fp32 sums.  The
+ * workspace then begins with the records, one per superblock b of x (5120 B):
+ * codes [sub-block j][octet q][row t < 16][8 B] (the 8 codes of elements
+ * 256 b + 32 j + 8 q .. + 7; rows >= T zero), then s [j][t] and s * gsum
+ * [j][t] as fp32 ([8][16] each).
  * Launches: the activation quantizer (which also clears the tile counters in
  * the workspace), then the GEMV, whose last block per 64-row tile adds the
  * tile's split-K partials in a fixed order; no memset, so the call can be
  * captured in a HIP graph.  Calls that share a workspace must not overlap. */
-enum { MK_PATH_AUTO = 0, MK_PATH_DOT4 = 1, MK_PATH_MFMA = 2 };
+enum { MK_PATH_AUTO = 0, MK_PATH_DOT4 = 1, MK_PATH_MFMA = 2, MK_PATH_STEP = 3 };
 int mk_qgemv_rows_ex(const mk_q4k* W, const float* x, int32_t T, float* y, int32_t path, void* ws,
                      size_t ws_bytes, void* stream);
 

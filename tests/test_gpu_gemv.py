@@ -28,6 +28,17 @@ def test_quantize_bit_exact():
     x[2, :32] = (np.arange(32) - 16) * 3.0 + 1.5
     x[2, 31] = -127.0 * 3.0
     x[3, :32] *= 1e-30  # tiny magnitudes (s subnormal-adjacent)
+    # groups with no usable scale and non-finite elements
+    tiny = np.float32(2.0 ** -149)
+    k = np.arange(32) - 16
+    x[4, :32] = (k % 4) * tiny  # amax/127 underflows: s = 0, zero codes
+    x[4, 32:64] = np.where(k == 0, 63, -(k % 7)) * tiny  # the largest amax that underflows
+    x[4, 64:96] = np.clip(k * 4, -64, 64) * tiny  # s = 2^-149 exactly
+    x[4, 96:128] *= 1e-40  # subnormal inputs with a subnormal scale
+    x[5, 5] = np.nan  # one NaN element
+    x[5, 32:64] = np.nan  # a group of NaN only
+    x[5, 70] = np.inf  # infinite amax
+    x[5, 71] = -np.inf
     say("quantize", T, K)
     xd = to_dev(x)
     a8 = torch.empty(T, K, dtype=torch.int8, device="cuda")
@@ -245,3 +256,100 @@ def test_gemv_ffn_graph_replay_matches_eager():
         assert np.array_equal(to_np(yb), ref_b), rep
         calls()
         torch.cuda.synchronize()
+
+
+# --------------------------------------------------------- the step's engines
+def _step_path(mk, torch, W, x, ws=None):
+    Wd = mk.Q4K.from_fields(W)
+    T = x.shape[0]
+    y = torch.empty(T, W["n_out"], dtype=torch.float32, device="cuda")
+    if ws is None:
+        ws = mk.workspace(mk.mk_qgemv_rows_workspace(T, W["n_out"], W["n_in"]), "cuda")
+    mk.mk_qgemv_rows(Wd, to_dev(x), y, ws=ws, path=mk.MK_PATH_STEP)
+    return to_np(y), ws
+
+
+def _decode_records(ws, T, K):
+    """The step's activation records at the start of the workspace, decoded
+    into a8 [16][K], s and s*gsum [16][K/32] (layout stated in mk.h)."""
+    nsb = K // 256
+    raw = to_np(ws)[: nsb * 5120].reshape(nsb, 5120)
+    codes = raw[:, :4096].view(np.int8).reshape(nsb, 8, 4, 16, 8)  # [b][j][q][t][e]
+    a8 = codes.transpose(3, 0, 1, 2, 4).reshape(16, K)
+    s = raw[:, 4096:4608].copy().view(np.float32).reshape(nsb, 8, 16).transpose(2, 0, 1).reshape(16, K // 32)
+    sg = raw[:, 4608:].copy().view(np.float32).reshape(nsb, 8, 16).transpose(2, 0, 1).reshape(16, K // 32)
+    return a8, s, sg
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 8, 9, 12, 16])
+def test_step_engines_integer_families_are_exact(T):
+    """The decode step's three engines (dot4 at T = 1, the packed 16x16x64
+    matrix-core engine up to 8 padded rows, the 16x16x32 engine above) give
+    the exact integer results of the E1-E3 families bit for bit, like the
+    standalone engines."""
+    torch = need_gpu()
+    mk = _mk()
+    N, K = 192, 1024
+    one = 0x3C00
+    rng = np.random.default_rng(11)
+    sc = rng.integers(0, 64, size=(N, K // 256, 8)).astype(np.uint8)
+    m = rng.integers(0, 64, size=(N, K // 256, 8)).astype(np.uint8)
+    fams = {"E1": _family(N, K, one, 0, 1, 0, 1), "E2": _family(N, K, 0, one, 0, 1, 2),
+            "E3": _family(N, K, one, one, sc, m, 3)}
+    x = _int_rows(T, K, 40 + T)
+    xi = x.astype(np.int64).reshape(T, K // 32, 32)
+    for name, W in fams.items():
+        qi = W["q"].astype(np.int64).reshape(N, K // 32, 32)
+        P = np.einsum("tgi,ogi->tog", xi, qi)
+        dd = 1 if name != "E2" else 0
+        dm = 1 if name != "E1" else 0
+        exp = dd * (P * W["sc"].reshape(N, -1).astype(np.int64)[None]).sum(-1) - \
+            dm * (xi.sum(-1)[:, None, :] * W["m"].reshape(N, -1).astype(np.int64)[None]).sum(-1)
+        say("step engine family", name, T)
+        y, _ = _step_path(mk, torch, W, x)
+        assert np.array_equal(y, exp.astype(np.float32)), (name, T)
+
+
+@pytest.mark.parametrize("T", [1, 5, 8, 12, 16])
+def test_step_records_bit_exact(T):
+    """The step's fused epilogue quantizer (store_q8) writes records whose
+    codes, scales and scaled code sums equal the oracle's quantizer bit for
+    bit, edge groups included; rows T..15 are zero."""
+    torch = need_gpu()
+    mk = _mk()
+    K = 2048
+    x = synth.normal_f32(6, 100 + T, 0, T * K).reshape(T, K)
+    tiny = np.float32(2.0 ** -149)
+    k = np.arange(32) - 16
+    x[0, :32] = 0.0
+    x[0, 32:64] = (k % 4) * tiny
+    x[0, 64:96] = np.clip(k * 4, -64, 64) * tiny
+    x[0, 96:128] *= 1e-40
+    x[-1, 130] = np.nan
+    x[-1, 160:192] = np.nan
+    x[-1, 200] = np.inf
+    x[0, 256:288] = np.arange(32) - 15.5
+    x[0, 256] = 127.0
+    W = synth.q4k_fields(6, 7, 64, K)
+    say("step records", T)
+    _, ws = _step_path(mk, torch, W, x)
+    a8, s, sg = _decode_records(ws, T, K)
+    ra8, rs, rgs = oracle.quantize_rows(x)
+    assert np.array_equal(a8[:T], ra8)
+    assert np.array_equal(s[:T].view(np.uint32), rs.view(np.uint32))
+    with np.errstate(invalid="ignore"):
+        rsg = (rs * rgs.astype(np.float32)).astype(np.float32)
+    assert np.array_equal(sg[:T], rsg, equal_nan=True)
+    assert not a8[T:].any() and not s[T:].any() and not sg[T:].any()
+
+
+@pytest.mark.parametrize("N,K", [(200, 768), (64, 256)])
+def test_step_engines_vs_oracle(N, K):
+    torch = need_gpu()
+    mk = _mk()
+    W = synth.q4k_fields(9, N + K, N, K)
+    for T in (1, 3, 8, 9, 16):
+        x = synth.normal_f32(9, 900 + T, 0, T * K).reshape(T, K)
+        say("step engine vs oracle", N, K, T)
+        y, _ = _step_path(mk, torch, W, x)
+        assert rel_err(y, oracle.qgemv(W, x)) <= FP32_TOL, T
