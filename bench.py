@@ -646,7 +646,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true", help="skip the standalone entry-point timings")
     ap.add_argument("--layers", type=int, default=LAYERS)
-    ap.add_argument("--sweep", action="store_true", help="also time the step at every T in 1..12 and 16")
+    ap.add_argument("--sweep", action="store_true", help="also time the step at every T in 1..16")
     ap.add_argument("--series", type=int, default=100,
                     help="also time this many seeded T = 12 steps, each with its own inputs (0: skip)")
     ap.add_argument("--traffic-from", metavar="DIR",
@@ -690,7 +690,7 @@ def main():
     series = None
     configs = [(12, [0, 3, 6, 9, 12], 4), (5, [0, 5], 1), (1, [0, 1], 1)]
     if args.sweep:  # one verify group of T rows, one agent
-        configs += [(T, [0, T], 1) for T in (2, 3, 4, 6, 7, 8, 9, 10, 11, 16)]
+        configs += [(T, [0, T], 1) for T in (2, 3, 4, 6, 7, 8, 9, 10, 11, 13, 14, 15, 16)]
     for T, gs, n_agents in configs:
         if args.only_primary and T != 12:
             continue

@@ -92,7 +92,6 @@ constexpr int kActA = 8 * 4 * 16 * 8;        // 4096
 constexpr int kActBytes = kActA + 2 * 8 * 16 * 4;  // 5120
 // An LDS slot holds one weight unit and the activations of its superblock.
 constexpr int kSlotBytes = kUnitBytes + kActBytes;
-constexpr int kPartBatch = 8;                 // partials loaded per batch in an epilogue
 constexpr float kRmsEps = 1e-6f;
 constexpr unsigned kSpinLimit = 1u << 26;  // bound of every wait (~seconds)
 constexpr int kMaxStamps = 4 * kMaxLayers + 8;
@@ -121,6 +120,14 @@ static_assert(sizeof(BlockPlan) % 16 == 0, "plans are copied in 16-B words");
 template <int T>
 struct TPad {
   static constexpr int value = (T + 3) & ~3;
+};
+
+// Partials loaded per batch in an epilogue: 8, or 6 from 13 rows, where 8
+// batches of four row groups do not fit the owner wave's registers beside the
+// residual rows and row factors it holds for its tiles.
+template <int T>
+struct PartBatch {
+  static constexpr int value = TPad<T>::value > 12 ? 6 : 8;
 };
 
 struct LayerW {
@@ -1280,7 +1287,7 @@ __device__ __forceinline__ void svc_prep(const StepArgs& a, int lane, uint8_t* s
 
 // Sum of the block partials of (tile, matrix) pairs tau*nm + m, m < nm (n0
 // and n1 contributing blocks), in block order, in row-group form; all loads
-// of up to kPartBatch partials are issued together.  A partial is
+// of up to PartBatch partials are issued together.  A partial is
 // [TP rows][64 columns].
 template <int T>
 __device__ __forceinline__ void sum_partials(const StepArgs& a, int q, int nm, int tau, int n0, int n1, int lane,
@@ -1293,10 +1300,11 @@ __device__ __forceinline__ void sum_partials(const StepArgs& a, int q, int nm, i
   const int lo = ((lane >> 4) * 64 + (lane & 15) * 4) * 4;  // bytes: row tr, column 4 cq
 #pragma unroll
   for (int k = 0; k < G; ++k) v0[k] = v1[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  for (int e0 = 0; e0 < n; e0 += kPartBatch) {
-    f32x4 tmp[kPartBatch][G];
+  constexpr int B = PartBatch<T>::value;
+  for (int e0 = 0; e0 < n; e0 += B) {
+    f32x4 tmp[B][G];
 #pragma unroll
-    for (int i = 0; i < kPartBatch; ++i) {
+    for (int i = 0; i < B; ++i) {
       const int e = e0 + i < n ? e0 + i : n - 1;  // in-range address; extra values are not added
       const int m = e < n0 ? 0 : 1, r = e < n0 ? e : e - n0;
       const int off = ((tm0 + m) * cm + r) * TP * 64 * 4 + lo;
@@ -1304,7 +1312,7 @@ __device__ __forceinline__ void sum_partials(const StepArgs& a, int q, int nm, i
       for (int k = 0; k < G; ++k) tmp[i][k] = ld16(part, off + k * 4 * 64 * 4);
     }
 #pragma unroll
-    for (int i = 0; i < kPartBatch; ++i) {
+    for (int i = 0; i < B; ++i) {
       if (e0 + i >= n) break;
 #pragma unroll
       for (int k = 0; k < G; ++k) {
