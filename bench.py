@@ -688,7 +688,8 @@ def main():
     layers, lm = build_stack(layers=L)
     results = {}
     series = None
-    configs = [(12, [0, 3, 6, 9, 12], 4), (5, [0, 5], 1), (1, [0, 1], 1)]
+    # the metric's rows (T = 12, 5, 1), then eight agents of three rows (T = 24)
+    configs = [(12, [0, 3, 6, 9, 12], 4), (5, [0, 5], 1), (1, [0, 1], 1), (24, list(range(0, 25, 3)), 8)]
     if args.sweep:  # one verify group of T rows, one agent
         configs += [(T, [0, T], 1) for T in (2, 3, 4, 6, 7, 8, 9, 10, 11, 13, 14, 15, 16)]
     for T, gs, n_agents in configs:
@@ -705,6 +706,7 @@ def main():
         r["total_gb_s"] = b["total"] / (r["ms_event"] * 1e-3) / 1e9
         r["kernel_gb_s"] = b["total"] / (r["kernel_ms"] * 1e-3) / 1e9
         r["steps_per_s"] = 1e3 / r["ms_per_step"]
+        r["agents"] = n_agents
         results[T] = r
         log(f"T={T}: {r['ms_per_step']:.3f} ms/step (events {r['ms_event']:.3f}, kernel {r['kernel_ms']:.3f}), "
             f"weights {r['weight_gb_s']:.0f} GB/s, total {r['total_gb_s']:.0f} GB/s, kernel {r['kernel_gb_s']:.0f} GB/s")
@@ -758,7 +760,8 @@ def main():
                                "persistent launch per step",
                    "rows": 12, "layers": L, "weight_bytes_per_step": p["bytes"]["weights"] + p["bytes"]["lm_head"],
                    "pct_of_8TBs": round(100 * p["weight_gb_s"] / PEAK_HBM_GBS, 2),
-                   "per_T": {str(T): {"ms_per_step": round(r["ms_per_step"], 4),
+                   "per_T": {str(T): {"agents": r["agents"], "lm_head_streams": (T + 15) // 16,
+                                      "ms_per_step": round(r["ms_per_step"], 4),
                                       "steps_per_s": round(r["steps_per_s"], 2),
                                       "rows_steps_per_s": round(r["steps_per_s"] * T, 1),
                                       "weight_gb_s": round(r["weight_gb_s"], 1),

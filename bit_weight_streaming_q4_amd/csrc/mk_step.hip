@@ -99,6 +99,12 @@ constexpr int kMaxStamps = 4 * kMaxLayers + 8;
 constexpr int kErrWatchdog = 1;  // a bounded wait ran out
 constexpr int kErrTables = 2;    // the workspace holds another stack's weight table and plans
 constexpr int kErrAccept = 4;    // an agent state's accept length was outside 0..T_max-1
+// Words of the step's output block (zeroed before each launch).
+constexpr int kOutNacc = 16;   // accept length per group
+constexpr int kOutTok = 32;    // emitted tokens per row
+constexpr int kOutTop = 64;    // argmax per row
+constexpr int kOutPass = 96;   // lm streams whose rows are handed over
+constexpr int kOutWords = 128;
 
 enum { K_X = 0, K_U = 1, K_X2 = 2, K_H = 3 };
 
@@ -127,7 +133,26 @@ struct TPad {
 // residual rows and row factors it holds for its tiles.
 template <int T>
 struct PartBatch {
-  static constexpr int value = TPad<T>::value > 12 ? 6 : 8;
+  static constexpr int value = TPad<T>::value > 16 ? 2 : TPad<T>::value > 12 ? 6 : 8;
+};
+
+// More than 16 rows (up to kStepTMax): the activation record of a superblock
+// is two 16-row records (rows 0..15, then rows 16..31), each unit runs through
+// the 16-row matrix-core engine once per half with its weights held in
+// registers, and a compute wave keeps one weight region and two activation
+// regions in LDS.
+constexpr int kStepTMax = 24;
+template <int T>
+struct Big {
+  static constexpr bool value = T > 16;
+};
+template <int T>
+struct RecBytes {  // bytes per superblock of an activation record
+  static constexpr int value = Big<T>::value ? 2 * kActBytes : kActBytes;
+};
+template <int T>
+struct SsRows {  // sums-of-squares slots per 64-column tile
+  static constexpr int value = Big<T>::value ? 32 : 16;
 };
 
 struct LayerW {
@@ -163,12 +188,13 @@ struct StepArgs {
   uint8_t* act;         // activation records, [layer][kind] (see kActBytes)
   size_t act_layer;     // bytes per layer
   size_t act_off[4];    // bytes from the layer's first record, per kind
-  float* ss;  // [(2L+1)][H/64][16]
+  float* ss;  // [(2L+1)][H/64][SsRows]
   float* part;
-  _Float16* frag;
+  _Float16* frag;     // lm_head input fragments, one set per 16 rows
+  size_t frag_half;   // halves between the sets
   float* lm_val;
   int* lm_idx;
-  int32_t* out;  // [0] error word, [16..31] n_acc, [32..47] tokens, [48..63] argmax
+  int32_t* out;  // [0] error word, [16..31] n_acc, [32..63] tokens, [64..95] argmax, [96] first lm pass done
   uint64_t* stamps;  // [kMaxStamps]: block 0's clock after each barrier
   const BlockPlan* plans;  // [grid]
   const uint64_t* ws_tag;  // the workspace's record of the stack whose tables it holds
@@ -275,15 +301,22 @@ constexpr int kSlots = 2;
 constexpr int kMbRow = 68;  // mailbox row stride in floats: 64 rows + 4 (spreads the flush writes over the banks)
 template <int T>
 struct MbCount {
-  static constexpr int value = 2;
+  static constexpr int value = Big<T>::value ? 1 : 2;
+};
+// Per compute wave: two slots of [weights | activations], or above 16 rows
+// one weight region and two activation regions of two 16-row halves.
+constexpr int kStageBytes = 1024 + 256;  // one tile's part of a 16-row record
+template <int T>
+struct RingBytes {
+  static constexpr int value = Big<T>::value ? kUnitBytes + 2 * RecBytes<T>::value : kSlots * kSlotBytes;
 };
 template <int T>
 struct BlockState {
   static constexpr int NMB = MbCount<T>::value;
-  uint8_t ring[kCompute][kSlots][kSlotBytes] __attribute__((aligned(16)));
+  uint8_t ring[kCompute][RingBytes<T>::value] __attribute__((aligned(16)));
   const uint8_t* wt[kMaxLayers][5];  // the weight table, copied at the start
   float mb[kCompute][NMB][TPad<T>::value][kMbRow] __attribute__((aligned(16)));  // [t][row of the tile]
-  uint8_t stage[1024 + 256] __attribute__((aligned(16)));  // one tile's record part, staged by the service wave
+  uint8_t stage[(Big<T>::value ? 2 : 1) * kStageBytes] __attribute__((aligned(16)));  // staged record parts
   BlockPlan plan __attribute__((aligned(16)));
   int tag[kCompute][NMB];
   int done[kCompute];
@@ -395,15 +428,14 @@ __device__ __forceinline__ float sum16(float v) {
 // that each goes out as one 16-B store per lane.  Group g of row t: lanes
 // 16 tr + 8 g .. + 7; each lane's 4 codes are one dword of the record:
 // sub-block j = g, octet q = (cq % 8) / 2, bytes 4 (cq % 2) .. + 3.
-template <int T>
-__device__ __forceinline__ void store_q8(uint8_t* rec, int tau, int lane, const f32x4 (&val)[RG<T>::G],
-                                         uint8_t* stage) {
+template <int G>
+__device__ __forceinline__ void store_q8_part(uint8_t* blk, int tau, int lane, const f32x4* val, uint8_t* stage) {
   const int tr = lane >> 4, cq = lane & 15;
   const int jj = cq >> 3, q = (cq & 7) >> 1;
   uint8_t* cb = stage + (jj * 4 + q) * 128 + (cq & 1) * 4;
   float* sst = (float*)(stage + 1024);  // [s: 2 x 16][s * gsum: 2 x 16]
 #pragma unroll
-  for (int k = 0; k < RG<T>::G; ++k) {
+  for (int k = 0; k < G; ++k) {
     const int t = tr + 4 * k;
     const f32x4 x = val[k];
     float amax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(x[0]), __builtin_fabsf(x[1])),
@@ -428,7 +460,6 @@ __device__ __forceinline__ void store_q8(uint8_t* rec, int tau, int lane, const 
       sst[32 + jj * 16 + t] = sc * (float)gsum;
     }
   }
-  uint8_t* blk = rec + (size_t)(tau >> 2) * kActBytes;
   st16(blk, (tau & 3) * 1024 + lane * 16, *(const f32x4*)(stage + lane * 16));
   if (lane < 16) {
     const int j0 = (tau & 3) * 2;
@@ -437,7 +468,23 @@ __device__ __forceinline__ void store_q8(uint8_t* rec, int tau, int lane, const 
   }
 }
 
-// Sums of squares of the tile's rows (row-group form) into its 16 slots
+// The tile's part of the activation record rec (superblock tau / 4): rows
+// 0..15 in the first 16-row record, rows 16..31 (more than 16 rows) in the
+// second, each staged in a stage area of its own (its rows above the ones
+// written stay zero).
+template <int T>
+__device__ __forceinline__ void store_q8(uint8_t* rec, int tau, int lane, const f32x4 (&val)[RG<T>::G],
+                                         uint8_t* stage) {
+  uint8_t* blk = rec + (size_t)(tau >> 2) * RecBytes<T>::value;
+  if constexpr (Big<T>::value) {
+    store_q8_part<4>(blk, tau, lane, val, stage);
+    store_q8_part<RG<T>::G - 4>(blk + kActBytes, tau, lane, val + 4, stage + kStageBytes);
+  } else {
+    store_q8_part<RG<T>::G>(blk, tau, lane, val, stage);
+  }
+}
+
+// Sums of squares of the tile's rows (row-group form) into its slots
 // (slot t < TP; rows >= T are zero).
 template <int T>
 __device__ __forceinline__ void store_ss(float* ss16, int lane, const f32x4 (&x)[RG<T>::G]) {
@@ -470,14 +517,14 @@ __device__ __forceinline__ int wave_sum_i(int v) { return sum64_i(v); }
 __device__ __forceinline__ float wave_sum(float v) { return sum64(v); }
 
 // r[t] = 1/sqrt(mean(x_t^2) + eps) from the per-tile sums of squares of
-// record ss_idx ([tile][16]): lane i adds tiles i, i+64, ... in order (the
+// record ss_idx ([tile][SsRows]): lane i adds tiles i, i+64, ... in order (the
 // loads of two such chunks are issued together), then the lanes are summed;
 // the same order for every caller.
 template <int T>
 __device__ __forceinline__ void rnorm_rows(const StepArgs& a, int ss_idx, int lane, float (&r)[T]) {
   constexpr int TP = TPad<T>::value;
   const int ntH = a.H / 64;
-  const float* ss = a.ss + (size_t)ss_idx * ntH * 16;
+  const float* ss = a.ss + (size_t)ss_idx * ntH * SsRows<T>::value;
   f32x4 acc[TP / 4];
 #pragma unroll
   for (int i = 0; i < TP / 4; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -488,7 +535,7 @@ __device__ __forceinline__ void rnorm_rows(const StepArgs& a, int ss_idx, int la
       const int tile = (k0 + k) * 64 + lane;
       const int tl = tile < ntH ? tile : 0;  // in-range address; the value is not added
 #pragma unroll
-      for (int i = 0; i < TP / 4; ++i) v[k][i] = ld16(ss, tl * 64 + i * 16);
+      for (int i = 0; i < TP / 4; ++i) v[k][i] = ld16(ss, tl * SsRows<T>::value * 4 + i * 16);
     }
 #pragma unroll
     for (int k = 0; k < 2; ++k)
@@ -537,7 +584,7 @@ __device__ __forceinline__ void cursor_settle(const StepArgs& a, const uint8_t* 
 // LDS address (for M0) of slot k of compute wave c.
 template <int T>
 __device__ __forceinline__ uint32_t slot_lds(BlockState<T>& s, int c, int k) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&s.ring[c][k][0];
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&s.ring[c][k * kSlotBytes];
 }
 
 // n LDS-DMA loads of 1 KB (16 B per lane) from global g (this lane's first
@@ -553,7 +600,7 @@ __device__ __forceinline__ uint32_t slot_lds(BlockState<T>& s, int c, int k) {
 #define MK_DMA9(C) MK_DMA5(C) MK_DMA_NEXT MK_DMA1(C) MK_DMA_NEXT MK_DMA1(C) MK_DMA_NEXT MK_DMA1(C) MK_DMA_NEXT MK_DMA1(C)
 template <int N, bool COH>
 __device__ __forceinline__ void dma(uint32_t lds, const uint8_t* g) {
-  static_assert((N == 9 && !COH) || (N == 5 && COH), "instantiated shapes only");
+  static_assert((N == 9 && !COH) || ((N == 5 || N == 10) && COH), "instantiated shapes only");
   const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds);
   uint64_t addr = (uint64_t)(uintptr_t)g;
   const uint64_t step = 1024;
@@ -564,8 +611,13 @@ __device__ __forceinline__ void dma(uint32_t lds, const uint8_t* g) {
                  : [a] "+v"(addr)
                  : [m] "s"(l0), [k] "s"(step)
                  : "memory", "m0", "scc");
-  else
+  else if constexpr (N == 5)
     asm volatile("s_mov_b32 m0, %[m]\n\t" MK_DMA5(" sc1")
+                 : [a] "+v"(addr)
+                 : [m] "s"(l0), [k] "s"(step)
+                 : "memory", "m0", "scc");
+  else
+    asm volatile("s_mov_b32 m0, %[m]\n\t" MK_DMA5(" sc1") MK_DMA_NEXT MK_DMA5(" sc1")
                  : [a] "+v"(addr)
                  : [m] "s"(l0), [k] "s"(step)
                  : "memory", "m0", "scc");
@@ -769,11 +821,10 @@ __device__ __forceinline__ void scale_sub(int j, const float (&d)[4], const uint
   }
 }
 
-// Matrix-core engine on a unit whose weights are in registers (x) and whose
-// activation record is in slot sl.
-__device__ __forceinline__ void slot_mfma(const WregM& x, lds_u8* sl, int lane, f32x4 (&acc)[4]) {
+// Matrix-core engine on a unit whose weights are in registers (x), against
+// the 16-row activation record at act.
+__device__ __forceinline__ void act_mfma(const WregM& x, lds_u8* act, int lane, f32x4 (&acc)[4]) {
   const int q = lane >> 4, n = lane & 15;
-  lds_u8* act = sl + kUnitBytes;
   lds_f32* sc = (lds_f32*)(act + kActA);
   const u32x4 (&h)[4] = x.h;
   // activation operands of the first two sub-blocks
@@ -816,6 +867,11 @@ __device__ __forceinline__ void slot_mfma(const WregM& x, lds_u8* sl, int lane, 
     if (j + 1 < 8) mfma_sub(o[j + 1], x.cw[j + 1], p[j + 1]);
     scale_sub(j, d, sc03, sc47, o[j].st, p[j], acc);
   }
+}
+
+// The same on a slot: its activation record follows the unit's weights.
+__device__ __forceinline__ void slot_mfma(const WregM& x, lds_u8* sl, int lane, f32x4 (&acc)[4]) {
+  act_mfma(x, sl + kUnitBytes, lane, acc);
 }
 
 // Matrix-core engine for at most 8 (padded) rows: two sub-blocks per
@@ -949,6 +1005,7 @@ struct Consumer {
   int done;   // phases reported finished
   float acc[T];
   f32x4 macc[4];
+  f32x4 macc2[4];  // rows 16..31 (more than 16 rows)
 };
 
 template <int T>
@@ -956,7 +1013,7 @@ __device__ __forceinline__ void acc_zero(Consumer<T>& k) {
 #pragma unroll
   for (int t = 0; t < T; ++t) k.acc[t] = 0.0f;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) k.macc[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < 4; ++nb) k.macc[nb] = k.macc2[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 }
 
 // Writes the open partial to the wave's mailbox as [t][64 rows of the tile].
@@ -987,6 +1044,13 @@ __device__ __forceinline__ void flush(BlockState<T>& s, int c, int lane, Consume
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) s.mb[c][slot][4 * q + i][16 * nb + n] = k.macc[nb][i];
+    if constexpr (Big<T>::value) {
+      if (16 + 4 * q < TPad<T>::value)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s.mb[c][slot][16 + 4 * q + i][16 * nb + n] = k.macc2[nb][i];
+    }
   } else {
 #pragma unroll
     for (int t = 0; t < T; ++t) s.mb[c][slot][t][lane] = k.acc[t];
@@ -1071,7 +1135,7 @@ __device__ __forceinline__ void consume_dot4(const StepArgs& a, BlockState<T>& s
     k.tm = cur.tm;
     acc_zero<T>(k);
   }
-  lds_u8* sl = as_lds(&s.ring[c][kcur][0]);
+  lds_u8* sl = as_lds(&s.ring[c][kcur * kSlotBytes]);
   slot_dot4<T>(sl, lane, k.acc);
 }
 
@@ -1140,7 +1204,7 @@ __device__ __forceinline__ void consume(const StepArgs& a, BlockState<T>& s, int
     k.tm = cur.tm;
     acc_zero<T>(k);
   }
-  lds_u8* sl = as_lds(&s.ring[c][kcur][0]);
+  lds_u8* sl = as_lds(&s.ring[c][kcur * kSlotBytes]);
   if constexpr (PackMfma<T>::value) {
     WregP x;
     read_w_pk(sl, lane, x);
@@ -1188,10 +1252,89 @@ __device__ __forceinline__ void compute_wave_mfma(const StepArgs& a, BlockState<
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load outlives the stream (also after an abort)
 }
 
+// More than 16 rows: one weight region and two activation regions per
+// compute wave (unit n's activations in region n % 2).  Consuming unit n:
+// wait for its loads, issued while unit n - 1 was computed; copy its weights
+// into registers; issue the next unit's weights into the weight region and,
+// if the next unit's phase is open, its activations into the other region;
+// then run the 16-row engine on rows 0..15 and on rows 16..31 of the record.
+// Entering a new phase: wait for it to open and start the unit's activation
+// loads first.
+template <int T>
+__device__ __forceinline__ void consume_big(const StepArgs& a, BlockState<T>& s, int c, int lane, Consumer<T>& k,
+                                            const uint8_t* const (*wt)[5], WaveUnits wu, Cursor& cs, Slot& cur,
+                                            Slot& nxt, uint32_t lw, uint32_t lcur, uint32_t lnxt, lds_u8* wreg,
+                                            lds_u8* acur, bool& ok) {
+  if (cur.q != k.q) advance_to<T>(a, s, c, lane, k, cur.q, ok);
+  if (!cur.act) {
+    dma<10, true>(lcur, phase_input(a, cur.q >> 2, cur.q & 3) + (size_t)cur.b * RecBytes<T>::value + lane * 16);
+    cur.act = true;
+  }
+  wait_ops(0);
+  if (cur.tm != k.tm) {
+    if (k.tm >= 0) flush<T>(s, c, lane, k, ok);
+    k.tm = cur.tm;
+    acc_zero<T>(k);
+  }
+  WregM x;
+  read_w_mfma(wreg, lane, x);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the weight region is read before it is refilled
+  issue_w(a, wt, wu, cs, c, lane, lw, nxt);
+  // the other activation region held the previous unit, whose arithmetic is done
+  if (nxt.wops && nxt.q == k.q) {
+    dma<10, true>(lnxt, phase_input(a, nxt.q >> 2, nxt.q & 3) + (size_t)nxt.b * RecBytes<T>::value + lane * 16);
+    nxt.act = true;
+  }
+  act_mfma(x, acur, lane, k.macc);
+  act_mfma(x, acur + kActBytes, lane, k.macc2);
+  finish_early<T>(s, c, lane, k, nxt.q, nxt.tm, ok);
+}
+
+template <int T>
+__device__ __forceinline__ void compute_wave_big(const StepArgs& a, BlockState<T>& s, int c, int lane) {
+  const int qend = 4 * a.L;
+  uint8_t* base = &s.ring[c][0];
+  const uint32_t lw = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)base;
+  const uint32_t la0 = lw + kUnitBytes, la1 = la0 + RecBytes<T>::value;
+  lds_u8* wreg = as_lds(base);
+  lds_u8* a0 = as_lds(base + kUnitBytes);
+  lds_u8* a1 = as_lds(base + kUnitBytes + RecBytes<T>::value);
+  const uint8_t* const(*wt)[5] = s.wt;
+  WaveUnits wu = s.plan.wu;
+  Cursor cur;
+  cur.q = 0;
+  cursor_settle(a, wt, wu, cur, c);
+  Slot s0, s1;
+  issue_w(a, wt, wu, cur, c, lane, lw, s0);
+  s1.q = qend;
+  s1.tm = -1;
+  s1.b = 0;
+  s1.wops = 0;
+  s1.aops = 0;
+  s1.act = false;
+  Consumer<T> k;
+  k.q = -1;
+  k.tm = -1;
+  k.nflush = 0;
+  k.done = 0;
+  acc_zero<T>(k);
+  bool ok = true;
+  while (ok) {
+    if (s0.q >= qend) break;
+    consume_big<T>(a, s, c, lane, k, wt, wu, cur, s0, s1, lw, la0, la1, wreg, a0, ok);
+    if (s1.q >= qend) break;
+    consume_big<T>(a, s, c, lane, k, wt, wu, cur, s1, s0, lw, la1, la0, wreg, a1, ok);
+  }
+  advance_to<T>(a, s, c, lane, k, qend, ok);  // finishes the phases after the last unit
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load outlives the stream (also after an abort)
+}
+
 // A compute wave's stream of units through every phase of the step.
 template <int T>
 __device__ __forceinline__ void compute_wave(const StepArgs& a, BlockState<T>& s, int c, int lane) {
-  if constexpr (UseMfma<T>::value)
+  if constexpr (Big<T>::value)
+    compute_wave_big<T>(a, s, c, lane);
+  else if constexpr (UseMfma<T>::value)
     compute_wave_mfma<T>(a, s, c, lane);
   else
     compute_wave_dot4<T>(a, s, c, lane);
@@ -1275,7 +1418,7 @@ __device__ __forceinline__ void svc_prep(const StepArgs& a, int lane, uint8_t* s
   for (int tau = blockIdx.x; tau < ntH; tau += gridDim.x) {
     f32x4 xv[RG<T>::G];
     load_rows<T>(a.x, a.H, tau, lane, xv);
-    store_ss<T>(a.ss + (size_t)tau * 16, lane, xv);
+    store_ss<T>(a.ss + (size_t)tau * SsRows<T>::value, lane, xv);
     store_q8<T>(act_rec(a, 0, K_X), tau, lane, xv, stage);
   }
   const int n = ntH > (int)blockIdx.x ? (ntH - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
@@ -1369,7 +1512,7 @@ __device__ __forceinline__ void svc_epilogue(const StepArgs& a, int q, int tau, 
       }
     }
     const int ss_idx = ph == 1 ? 2 * l + 1 : 2 * l + 2;
-    store_ss<T>(a.ss + ((size_t)ss_idx * (a.H / 64) + tau) * 16, lane, xn);
+    store_ss<T>(a.ss + ((size_t)ss_idx * (a.H / 64) + tau) * SsRows<T>::value, lane, xn);
     if (ph == 1)
       store_q8<T>(act_rec(a, l, K_X2), tau, lane, xn, stage);
     else if (l + 1 < a.L)
@@ -1463,9 +1606,14 @@ __device__ __forceinline__ bool svc_own(const StepArgs& a, BlockState<T>& s, int
   const int tm0 = uniform(s.plan.kp[ph][0]), ntm = uniform(s.plan.kp[ph][1]);
   const int own0 = uniform(s.plan.kp[ph][2]), nown = uniform(s.plan.kp[ph][3]);
   constexpr int G = RG<T>::G;
-  f32x4 rg[G], xo[2][G];
+  constexpr int NPRE = Big<T>::value ? 1 : 2;  // owned tiles whose residual rows are loaded at the phase start
+  f32x4 rg[G], xo[NPRE][G];
 #pragma unroll
-  for (int k = 0; k < G; ++k) rg[k] = xo[0][k] = xo[1][k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < G; ++k) {
+    rg[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NPRE; ++i) xo[i][k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
   // the row factors need every tile of the phase input (its sums of squares)
   if (!wait_ge(a, s, &s.rel, q + 1)) return false;
   if (nown > 0) {
@@ -1483,7 +1631,7 @@ __device__ __forceinline__ bool svc_own(const StepArgs& a, BlockState<T>& s, int
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < NPRE; ++i)
         if (i < nown) load_rows<T>(a.x, a.H, own0 + i, lane, xo[i]);
     }
   }
@@ -1506,9 +1654,9 @@ __device__ __forceinline__ bool svc_own(const StepArgs& a, BlockState<T>& s, int
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     f32x4 xt[G];
-    if (o < 2) {
+    if (o < NPRE) {
 #pragma unroll
-      for (int k = 0; k < G; ++k) xt[k] = o == 0 ? xo[0][k] : xo[1][k];
+      for (int k = 0; k < G; ++k) xt[k] = o == 0 ? xo[0][k] : xo[NPRE - 1][k];
     } else if (ph == 1 || ph == 3) {  // more owned tiles than prefetched (small grids)
       load_rows<T>(a.x, a.H, tau, lane, xt);
     } else {
@@ -1531,24 +1679,30 @@ template <int T>
 __device__ __forceinline__ void svc_lm_prep(const StepArgs& a, int lane, const float (&rt)[T]) {
   const int nc = a.H / 64;
   const int t = lane & 15, kq = lane >> 4;
-  float r = 0.0f;
+  // one set of fragments per 16 rows
 #pragma unroll
-  for (int i = 0; i < T; ++i)
-    if (t == i) r = rt[i] * a.lm_pre;
-  const int tt = t < a.T ? t : 0;  // every lane loads an in-range value
-  for (int c = blockIdx.x; c < nc; c += gridDim.x) {
-    float* o = (float*)(a.frag + ((size_t)c * 64 + lane) * 32);
-    float xr[16];
+  for (int h = 0; h < (Big<T>::value ? 2 : 1); ++h) {
+    const int row = 16 * h + t;
+    float r = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) xr[e] = ld_coh(a.x + (size_t)tt * a.H + 64 * c + 16 * kq + e);
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    for (int i = 0; i < T; ++i)
+      if (row == i) r = rt[i] * a.lm_pre;
+    const int tt = row < a.T ? row : 0;  // every lane loads an in-range value
+    _Float16* frag = a.frag + h * a.frag_half;
+    for (int c = blockIdx.x; c < nc; c += gridDim.x) {
+      float* o = (float*)(frag + ((size_t)c * 64 + lane) * 32);
+      float xr[16];
 #pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      const float x0 = t < a.T ? r * xr[e] : 0.0f, x1 = t < a.T ? r * xr[e + 1] : 0.0f;
-      const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-      const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
-      st_coh(o + e / 2, __builtin_bit_cast(float, (h2){h0, h1}));
-      st_coh(o + 8 + e / 2, __builtin_bit_cast(float, (h2){l0, l1}));
+      for (int e = 0; e < 16; ++e) xr[e] = ld_coh(a.x + (size_t)tt * a.H + 64 * c + 16 * kq + e);
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const float x0 = row < a.T ? r * xr[e] : 0.0f, x1 = row < a.T ? r * xr[e + 1] : 0.0f;
+        const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+        const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+        st_coh(o + e / 2, __builtin_bit_cast(float, (h2){h0, h1}));
+        st_coh(o + 8 + e / 2, __builtin_bit_cast(float, (h2){l0, l1}));
+      }
     }
   }
 }
@@ -1658,34 +1812,64 @@ __device__ __forceinline__ void gdn_wave(const StepArgs& a, int lane) {
 // sums.
 __device__ __forceinline__ void lm_phase(const StepArgs& a, uint8_t* ring) {
   __shared__ int fin[16];
-  LmStream ls;
-  ls.W = a.lm;
-  ls.frag = a.frag;
-  ls.V = a.V;
-  ls.H = a.H;
-  ls.val = a.lm_val;
-  ls.idx = a.lm_idx;
-  ls.ticket = a.lm_ticket;
-  ls.logits = nullptr;
-  ls.logits_T = 0;
-  static_assert(kWavesPerBlock == 8, "the staged stream runs on 8 waves");
-  bool last;
-  if (a.H == 5120)
-    last = lm_stream_staged<3, 10>(ls, ring, fin);
-  else if (a.H == 512)
-    last = lm_stream_staged<3, 1>(ls, ring, fin);
-  else
-    last = lm_stream<kWavesPerBlock>(ls, (float (*)[64][16])ring, fin);
+  __shared__ int tops[32];  // the argmax of every row
+  // one stream over the vocabulary per 16 rows
+  const int npass = (a.T + 15) / 16;
+  bool last = false;
+  for (int h = 0; h < npass; ++h) {
+    LmStream ls;
+    ls.W = a.lm;
+    ls.frag = a.frag + h * a.frag_half;
+    ls.V = a.V;
+    ls.H = a.H;
+    ls.val = a.lm_val + (size_t)h * gridDim.x * 16;
+    ls.idx = a.lm_idx + (size_t)h * gridDim.x * 16;
+    ls.ticket = a.lm_ticket + h * kRdyStride;
+    ls.logits = nullptr;
+    ls.logits_T = 0;
+    static_assert(kWavesPerBlock == 8, "the staged stream runs on 8 waves");
+    if (a.H == 5120)
+      last = lm_stream_staged<3, 10>(ls, ring, fin);
+    else if (a.H == 512)
+      last = lm_stream_staged<3, 1>(ls, ring, fin);
+    else
+      last = lm_stream<kWavesPerBlock>(ls, (float (*)[64][16])ring, fin);
+    if (last && h + 1 < npass) {
+      // the last block of an earlier stream hands its rows to the last block of the final one
+      if (threadIdx.x < 16) __hip_atomic_store(a.out + kOutTop + 16 * h + threadIdx.x, fin[threadIdx.x],
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      stores_done();
+      __syncthreads();
+      if (threadIdx.x == 0) ticket_add((unsigned*)(a.out + kOutPass));
+    }
+  }
   if (!last) return;
+  if (threadIdx.x == 0 && npass > 1) {
+    unsigned spins = 0;
+    while (__hip_atomic_load(a.out + kOutPass, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < npass - 1) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit) {
+        atomicOr(a.err, kErrWatchdog);
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
+  __syncthreads();
+  if (threadIdx.x < 16 * npass)
+    tops[threadIdx.x] = (int)threadIdx.x >= 16 * (npass - 1)
+                            ? fin[threadIdx.x - 16 * (npass - 1)]
+                            : __hip_atomic_load(a.out + kOutTop + threadIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
   if (threadIdx.x == 0) {
-    for (int t = 0; t < a.T; ++t) a.out[48 + t] = fin[t];
+    for (int t = 0; t < a.T; ++t) a.out[kOutTop + t] = tops[t];
     for (int g = 0; g < a.G; ++g) {
       const int r = a.gs[g], n = a.gs[g + 1] - a.gs[g];
       const int32_t* dr = a.drafts + (r - g);
       int k = 0;
-      while (k < n - 1 && fin[r + k] >= 0 && dr[k] == fin[r + k]) ++k;
-      a.out[16 + g] = k;
-      for (int i = 0; i < n; ++i) a.out[32 + r + i] = i < k ? dr[i] : (i == k ? fin[r + k] : -1);
+      while (k < n - 1 && tops[r + k] >= 0 && dr[k] == tops[r + k]) ++k;
+      a.out[kOutNacc + g] = k;
+      for (int i = 0; i < n; ++i) a.out[kOutTok + r + i] = i < k ? dr[i] : (i == k ? tops[r + k] : -1);
       if (g < a.n_agents) {
         a.nacc[g][0] = k;      // replayed by the next step
         a.nacc[g][1] ^= 1;     // this step's rows are in the other ring half
@@ -1740,7 +1924,7 @@ __global__ __launch_bounds__(kBlock) void k_decode_step(StepArgs a) {
   if (!wait_ge(a, s, &s.rel, 4 * a.L + 2)) return;
   static_assert(sizeof(s.ring) >= sizeof(float) * kWavesPerBlock * 64 * 16, "lm reduction does not fit the ring");
   static_assert(sizeof(s.ring) >= 3 * kLmStageBytes, "the lm stages do not fit the ring");
-  lm_phase(a, &s.ring[0][0][0]);
+  lm_phase(a, &s.ring[0][0]);
   if (blockIdx.x == 0 && threadIdx.x == 0) a.stamps[kMaxStamps - 1] = wall_clock64();
 }
 
@@ -1770,6 +1954,14 @@ static StepKernel step_kernel(int T) {
     case 14: return kernel_for<14>();
     case 15: return kernel_for<15>();
     case 16: return kernel_for<16>();
+    case 17: return kernel_for<17>();
+    case 18: return kernel_for<18>();
+    case 19: return kernel_for<19>();
+    case 20: return kernel_for<20>();
+    case 21: return kernel_for<21>();
+    case 22: return kernel_for<22>();
+    case 23: return kernel_for<23>();
+    case 24: return kernel_for<24>();
     default: return nullptr;
   }
 }
@@ -1954,6 +2146,7 @@ struct StepLayout {
   size_t off_out, off_stamps, off_tickets, off_lmticket, off_table, off_act, off_ss, off_part, off_frag, off_lmv,
       off_lmi, total;
   size_t act_layer, act_off[4];
+  size_t frag_half;  // lm_head input fragments per 16 rows (fp16 elements)
 };
 
 int host_wave_of(long S, int W, long p) { return (int)(((p + 1) * (long)W - 1) / S); }
@@ -1989,7 +2182,8 @@ StepLayout layout(const mk_stack* st, int T) {
   for (int i = 0; i < 4; ++i) y.cmax[i] = y.Wc ? plan_cmax((long)ntiles[i] * nms[i], nsbs[i], y.Wc) : 1;
   // (each count must fit a byte of the packed kernel argument)
   // activation records: kActBytes per superblock of each input (x, u, x2, h)
-  auto rec = [](int K) { return (size_t)(K / 256) * kActBytes; };
+  const int halves = T > 16 ? 2 : 1;  // 16-row record halves, lm streams
+  auto rec = [halves](int K) { return (size_t)(K / 256) * kActBytes * halves; };
   y.act_off[K_X] = 0;
   y.act_off[K_U] = rec(d.hidden);
   y.act_off[K_X2] = y.act_off[K_U] + rec(d.proj);
@@ -2008,7 +2202,7 @@ StepLayout layout(const mk_stack* st, int T) {
   o += a256((size_t)d.n_layers * 4 * kTicketTiles * kTicketStride * 4);
   y.n_ctrl = o - y.off_ctrl;
   y.off_out = o;
-  o += 256;
+  o += a256(kOutWords * 4);
   y.off_stamps = o;
   o += a256(sizeof(uint64_t) * kMaxStamps);
   y.off_tag = o;
@@ -2020,7 +2214,7 @@ StepLayout layout(const mk_stack* st, int T) {
   y.off_act = o;
   o += y.act_layer * d.n_layers;
   y.off_ss = o;
-  o += a256((size_t)(2 * d.n_layers + 1) * (d.hidden / 64) * 16 * 4);
+  o += a256((size_t)(2 * d.n_layers + 1) * (d.hidden / 64) * (T > 16 ? 32 : 16) * 4);
   y.off_part = o;
   size_t part = 0;
   const int tp = (T + 3) & ~3;
@@ -2028,11 +2222,12 @@ StepLayout layout(const mk_stack* st, int T) {
   y.part_half = a256(part) / 4;  // floats; two buffers, by phase parity
   o += 2 * a256(part);
   y.off_frag = o;
-  o += a256((size_t)(d.hidden / 64) * 64 * 32 * 2);
+  y.frag_half = a256((size_t)(d.hidden / 64) * 64 * 32 * 2) / 2;
+  o += halves * y.frag_half * 2;
   y.off_lmv = o;
-  o += a256((size_t)y.grid * 16 * 4);
+  o += a256((size_t)y.grid * 16 * 4 * halves);
   y.off_lmi = o;
-  o += a256((size_t)y.grid * 16 * 4);
+  o += a256((size_t)y.grid * 16 * 4 * halves);
   y.total = o;
   return y;
 }
@@ -2182,7 +2377,7 @@ void mk_stack_destroy(mk_stack* st) {
 float mk_decode_step_last_ms(const mk_stack* st) { return st ? st->last_ms : -1.0f; }
 
 size_t mk_decode_step_workspace(const mk_stack* st, int32_t T) {
-  if (!st || T < 1 || T > MK_T_MAX) return 0;
+  if (!st || T < 1 || T > kStepTMax) return 0;
   return layout(st, T).total;
 }
 
@@ -2191,7 +2386,7 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
                    const float* gdn_g, const float* gdn_beta, float* gdn_o, int32_t* h_tokens, int32_t* h_n_acc,
                    int32_t* d_argmax, float* trace, void* ws, size_t ws_bytes, void* stream) {
   if (!st) return sfail(MK_ERR_ARG, "decode: null stack");
-  if (T < 1 || T > MK_T_MAX) return sfail(MK_ERR_RANGE, "decode: T outside 1..16");
+  if (T < 1 || T > kStepTMax) return sfail(MK_ERR_RANGE, "decode: T outside 1..24");
   if (!x || ((uintptr_t)x % 16)) return sfail(MK_ERR_ALIGN, "decode: x null or misaligned");
   if (!h_tokens || !h_n_acc) return sfail(MK_ERR_ARG, "decode: null host output");
   std::vector<int> gs;
@@ -2242,7 +2437,7 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
     }
   }
   if (hipMemsetAsync(w8 + y.off_ctrl, 0, y.n_ctrl, s) != hipSuccess ||
-      hipMemsetAsync(w8 + y.off_out, 0, 256, s) != hipSuccess)
+      hipMemsetAsync(w8 + y.off_out, 0, kOutWords * 4, s) != hipSuccess)
     return sfail(MK_ERR_LAUNCH, "decode: control reset failed");
   StepArgs a;
   memset(&a, 0, sizeof(a));
@@ -2301,6 +2496,7 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
   a.ss = (float*)(w8 + y.off_ss);
   a.part = (float*)(w8 + y.off_part);
   a.frag = (_Float16*)(w8 + y.off_frag);
+  a.frag_half = y.frag_half;
   a.lm_val = (float*)(w8 + y.off_lmv);
   a.lm_idx = (int*)(w8 + y.off_lmi);
   a.ws_tag = (const uint64_t*)(w8 + y.off_tag);
@@ -2317,9 +2513,9 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
     return set_error(e == hipErrorCooperativeLaunchTooLarge ? MK_ERR_COOP : MK_ERR_LAUNCH,
                      "decode: cooperative launch failed: %s", hipGetErrorString(e));
   if (d_argmax &&
-      hipMemcpyAsync(d_argmax, w8 + y.off_out + 48 * 4, T * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+      hipMemcpyAsync(d_argmax, w8 + y.off_out + kOutTop * 4, T * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
     return sfail(MK_ERR_LAUNCH, "decode: argmax copy failed");
-  int32_t hout[64];
+  int32_t hout[kOutWords];
   if (hipMemcpyAsync(hout, w8 + y.off_out, sizeof(hout), hipMemcpyDeviceToHost, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess)
     return sfail(MK_ERR_LAUNCH, "decode: readback failed");
@@ -2336,8 +2532,8 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
   if (hout[0] & kErrAccept)
     return sfail(MK_ERR_RANGE, "decode: an agent state's accept length was outside 0..T_max-1 (nothing was replayed)");
   if (hout[0]) return sfail(MK_ERR_DEVICE, "decode: device error word set");
-  for (int g = 0; g < G; ++g) h_n_acc[g] = hout[16 + g];
-  for (int t = 0; t < T; ++t) h_tokens[t] = hout[32 + t];
+  for (int g = 0; g < G; ++g) h_n_acc[g] = hout[kOutNacc + g];
+  for (int t = 0; t < T; ++t) h_tokens[t] = hout[kOutTok + t];
   set_error(MK_OK, "");
   return MK_OK;
 }

@@ -31,7 +31,8 @@
  *     negative MK_ERR_* code, enqueues nothing and records a message that
  *     mk_last_error() returns (thread-local).  No call prints or aborts.
  *   - Alignment: Q4K blobs 256 B, every other buffer 16 B (MK_ERR_ALIGN).
- *   - Row counts T are 1..16 (MK_ERR_RANGE).  Reduction orders are fixed, so
+ *   - Row counts T are 1..16 (MK_T_MAX), and 1..24 for mk_decode_step
+ *     (MK_STEP_T_MAX) (MK_ERR_RANGE).  Reduction orders are fixed, so
  *     a call is bit-reproducible for the same inputs and the same T.
  *   - Concurrent calls on different streams need distinct workspaces.
  */
@@ -58,6 +59,7 @@ enum {
 };
 
 #define MK_T_MAX 16
+#define MK_STEP_T_MAX 24 /* rows of one decode step: up to 8 agents x 3 rows */
 
 const char* mk_status_string(int status);
 const char* mk_last_error(void);
@@ -345,6 +347,9 @@ size_t mk_decode_step_workspace(const mk_stack* st, int32_t T);
 
 /* One decode step in ONE persistent launch, then one D->H copy of the
  * emitted tokens and accept lengths and one stream synchronisation.
+ * 1 <= T <= MK_STEP_T_MAX (24: the 4-agent article, section "Caveats",
+ * allows up to 8 agents, 3 rows each); above 16 rows every weight is still
+ * read once, and the lm_head is streamed once per 16 rows.
  *   x [T][hidden] (in: step input rows; out: final residual),
  *   h_group_start as in mk_lmhead_verify (G groups == agents when GDN is on),
  *   drafts [T-G] (device), gdn_* [T][nh][d] (device seeded inputs, NULL when

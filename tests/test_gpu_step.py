@@ -69,10 +69,15 @@ def _check_head(W16, x_final, am, na, tok, gs, drafts):
 # their largest; 6 has three agents of unequal size (1, 2 and 3 rows), 11 one
 # group that fills neither the rows nor a whole agent count.  The last two
 # run eight agents of two rows, and a ten-row chunk of a new prompt riding
-# beside two agents of three rows (each group with its own GDN state).
+# beside two agents of three rows (each group with its own GDN state).  Above
+# 16 rows the record has two 16-row halves and the lm_head is streamed once
+# per half: 17 (one row in the second half), 20, eight agents of three rows
+# (24), and a twelve-row chunk beside four agents of three rows.
 @pytest.mark.parametrize("T,gs", [(1, [0, 1]), (2, [0, 2]), (3, [0, 3]), (5, [0, 5]), (6, [0, 1, 3, 6]),
                                   (8, [0, 2, 4, 6, 8]), (9, [0, 9]), (11, [0, 11]), (12, [0, 3, 6, 9, 12]),
-                                  (16, [0, 4, 8, 12, 16]), (16, list(range(0, 17, 2))), (16, [0, 10, 13, 16])])
+                                  (16, [0, 4, 8, 12, 16]), (16, list(range(0, 17, 2))), (16, [0, 10, 13, 16]),
+                                  (17, [0, 8, 17]), (20, [0, 4, 8, 12, 16, 20]), (24, list(range(0, 25, 3))),
+                                  (24, [0, 3, 6, 9, 12, 24])])
 def test_decode_step_small_stack(T, gs):
     torch = need_gpu()
     mk = _mk()
@@ -139,7 +144,7 @@ def full_stack():
     return {"layers": layers, "lm": lm, "gl": recipes.gdn_layers(bench.LAYERS)}
 
 
-@pytest.mark.parametrize("T,gs", [(12, [0, 3, 6, 9, 12]), (1, [0, 1]), (5, [0, 5])])
+@pytest.mark.parametrize("T,gs", [(12, [0, 3, 6, 9, 12]), (1, [0, 1]), (5, [0, 5]), (24, list(range(0, 25, 3)))])
 def test_decode_step_full_size(full_stack, T, gs):
     torch = need_gpu()
     import bench
@@ -174,7 +179,7 @@ def test_decode_step_full_size(full_stack, T, gs):
     assert np.array_equal(to_np(xd), tr[L - 1])
     assert np.array_equal(to_np(am), amp)
     # layers teacher-forced: every layer at T = 12 (the benchmark's rows),
-    # sampled depths at T = 1 and 5
+    # sampled depths at T = 1, 5 and 24 (eight agents of three rows)
     bufs = {}
     for l in (range(L) if T == 12 else (0, 21, 42, L - 1)):
         for m in MATS:
@@ -267,13 +272,16 @@ def test_decode_step_accept_length_out_of_range():
     assert rel_err(og[3:], o_ref) <= FP32_TOL
 
 
-@pytest.mark.parametrize("gs_ride,rows", [([0, 10, 13, 16], (0, 10)), ([0, 3, 6, 16], (6, 16))])
+@pytest.mark.parametrize("gs_ride,rows", [([0, 10, 13, 16], (0, 10)), ([0, 3, 6, 16], (6, 16)),
+                                          ([0, 3, 6, 9, 12, 24], (12, 24))])
 def test_decode_step_prompt_chunk_is_bit_identical(gs_ride, rows):
     """A new prompt's chunk riding in a step beside other agents' rows gives,
     bit for bit, what the chunk gives when the step processes it on its own:
     residuals after every layer, argmax, Gated DeltaNet outputs and the
-    chunk's committed state (the 4-agent article, "Why it matters").  Both
-    steps run the 16-row matrix-core engine (T = 16 and T = 10)."""
+    chunk's committed state (the 4-agent article, "Why it matters").  Every
+    step here runs the 16-row matrix-core engine: on the whole record (T = 16,
+    10 and 12) or on each of its two halves (T = 24, the chunk's rows 12..23
+    straddling them)."""
     torch = need_gpu()
     mk = _mk()
     L, H, P, F, V = 4, 512, 1024, 768, 1000
