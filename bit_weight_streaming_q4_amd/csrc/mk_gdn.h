@@ -37,50 +37,53 @@ __device__ __forceinline__ float* after_w(float* p, float dep) {
 }
 
 // One row of the delta rule on the column this lane owns; k and q are
-// streamed 8 floats at a time, two chunks ahead of their use.
-// Pass 1: u = S^T k.  Pass 2: S <- g S + k c with c = beta (v - g u), fused
-// with o = S^T q on the updated column when WITH_Q.
-template <bool WITH_Q>
+// streamed CH floats at a time (one scalar load each), two chunks ahead of
+// their use.  Pass 1: u = S^T k.  Pass 2: S <- g S + k c with
+// c = beta (v - g u), fused with o = S^T q on the updated column when WITH_Q.
+// The arithmetic and its order do not depend on CH.
+template <bool WITH_Q, int CH = 8>
 __device__ __forceinline__ float gdn_row(float (&S)[kD], const float* kp, const float* qp, float vj, float g,
                                          float beta) {
+  typedef float vec __attribute__((ext_vector_type(CH)));
+  constexpr int NC = kD / CH;
   kp = uniform(kp);
   if constexpr (WITH_Q) qp = uniform(qp);
   float u = 0.0f;
-  f32x8 k0 = *as_const<f32x8>(kp), k1 = *as_const<f32x8>(kp + 8);
+  vec k0 = *as_const<vec>(kp), k1 = *as_const<vec>(kp + CH);
 #pragma unroll
-  for (int c = 0; c < kD / 8; ++c) {
+  for (int c = 0; c < NC; ++c) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) u = __builtin_fmaf(k0[e], S[8 * c + e], u);
+    for (int e = 0; e < CH; ++e) u = __builtin_fmaf(k0[e], S[CH * c + e], u);
     k0 = k1;
-    if (c + 2 < kD / 8) k1 = *as_const<f32x8>(after(kp, u) + 8 * (c + 2));
+    if (c + 2 < NC) k1 = *as_const<vec>(after(kp, u) + CH * (c + 2));
   }
   const float cc = beta * (vj - g * u);
   float o = 0.0f;
-  k0 = *as_const<f32x8>(after(kp, cc));
-  k1 = *as_const<f32x8>(after(kp, cc) + 8);
+  k0 = *as_const<vec>(after(kp, cc));
+  k1 = *as_const<vec>(after(kp, cc) + CH);
   if constexpr (WITH_Q) {
-    f32x8 q0 = *as_const<f32x8>(qp), q1 = *as_const<f32x8>(qp + 8);
+    vec q0 = *as_const<vec>(qp), q1 = *as_const<vec>(qp + CH);
 #pragma unroll
-    for (int c = 0; c < kD / 8; ++c) {
+    for (int c = 0; c < NC; ++c) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        S[8 * c + e] = __builtin_fmaf(k0[e], cc, g * S[8 * c + e]);
-        o = __builtin_fmaf(q0[e], S[8 * c + e], o);
+      for (int e = 0; e < CH; ++e) {
+        S[CH * c + e] = __builtin_fmaf(k0[e], cc, g * S[CH * c + e]);
+        o = __builtin_fmaf(q0[e], S[CH * c + e], o);
       }
       k0 = k1;
       q0 = q1;
-      if (c + 2 < kD / 8) {
-        k1 = *as_const<f32x8>(after(kp, o) + 8 * (c + 2));
-        q1 = *as_const<f32x8>(after(qp, o) + 8 * (c + 2));
+      if (c + 2 < NC) {
+        k1 = *as_const<vec>(after(kp, o) + CH * (c + 2));
+        q1 = *as_const<vec>(after(qp, o) + CH * (c + 2));
       }
     }
   } else {
 #pragma unroll
-    for (int c = 0; c < kD / 8; ++c) {
+    for (int c = 0; c < NC; ++c) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) S[8 * c + e] = __builtin_fmaf(k0[e], cc, g * S[8 * c + e]);
+      for (int e = 0; e < CH; ++e) S[CH * c + e] = __builtin_fmaf(k0[e], cc, g * S[CH * c + e]);
       k0 = k1;
-      if (c + 2 < kD / 8) k1 = *as_const<f32x8>(after(kp, S[8 * c + 7]) + 8 * (c + 2));
+      if (c + 2 < NC) k1 = *as_const<vec>(after(kp, S[CH * c + CH - 1]) + CH * (c + 2));
     }
   }
   return o;
@@ -100,6 +103,7 @@ struct GdnHalf {
   int T, half;
 };
 
+template <int CH = 8>
 __device__ __forceinline__ void gdn_half_step(const GdnHalf& a, int lane) {
   const int j = 64 * a.half + lane;
   float S[kD];
@@ -112,12 +116,12 @@ __device__ __forceinline__ void gdn_half_step(const GdnHalf& a, int lane) {
     const float* row = a.ring_rd + (size_t)r * kRingRow;
     const float vj = row[kD + j];
     const float g = *as_const<float>(row + 2 * kD), beta = *as_const<float>(row + 2 * kD + 1);
-    gdn_row<false>(S, row, nullptr, vj, g, beta);
+    gdn_row<false, CH>(S, row, nullptr, vj, g, beta);
   }
   {
     // row 0 (the token accepted on the previous step) is committed right away
     const float g = *as_const<float>(a.g), beta = *as_const<float>(a.beta);
-    const float o0 = gdn_row<true>(S, a.k, a.q, a.v[j], g, beta);
+    const float o0 = gdn_row<true, CH>(S, a.k, a.q, a.v[j], g, beta);
     a.o[j] = o0;
     float* Sw = after_w(uniform(a.S), o0) + j;
 #pragma unroll
@@ -127,7 +131,7 @@ __device__ __forceinline__ void gdn_half_step(const GdnHalf& a, int lane) {
     const float* kt = a.k + t * a.sqk;
     const float vj = a.v[t * a.sv + j];
     const float g = *as_const<float>(a.g + t * a.sgb), beta = *as_const<float>(a.beta + t * a.sgb);
-    a.o[t * a.so + j] = gdn_row<true>(S, kt, a.q + t * a.sqk, vj, g, beta);
+    a.o[t * a.so + j] = gdn_row<true, CH>(S, kt, a.q + t * a.sqk, vj, g, beta);
     float* row = a.ring_wr + (size_t)(t - 1) * kRingRow;
     row[j] = kt[j];
     row[kD + j] = vj;
@@ -137,6 +141,7 @@ __device__ __forceinline__ void gdn_half_step(const GdnHalf& a, int lane) {
 }
 
 // Replays ring rows into the committed state (no new rows).
+template <int CH = 8>
 __device__ __forceinline__ void gdn_half_commit(float* Sh, const float* ring_rd, int nrep, int half, int lane) {
   if (nrep <= 0) return;
   const int j = 64 * half + lane;
@@ -147,7 +152,7 @@ __device__ __forceinline__ void gdn_half_commit(float* Sh, const float* ring_rd,
     const float* row = ring_rd + (size_t)r * kRingRow;
     const float vj = row[kD + j];
     const float g = *as_const<float>(row + 2 * kD), beta = *as_const<float>(row + 2 * kD + 1);
-    gdn_row<false>(S, row, nullptr, vj, g, beta);
+    gdn_row<false, CH>(S, row, nullptr, vj, g, beta);
   }
   float* Sw = after_w(uniform(Sh), S[kD - 1]) + j;
 #pragma unroll

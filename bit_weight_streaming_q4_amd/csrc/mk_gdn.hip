@@ -26,14 +26,16 @@ __global__ __launch_bounds__(64) void k_gdn_step(GdnArgs a) {
   x.so = (size_t)a.nh * kD;
   x.T = a.T;
   x.half = half;
-  gdn_half_step(x, lane);
+  // 128-B chunks of k and q (two 64-B scalar loads each): a quarter of the
+  // dependent scalar loads per row pass of 32-B chunks
+  gdn_half_step<32>(x, lane);
 }
 
 __global__ __launch_bounds__(64) void k_gdn_commit(GdnArgs a) {
   const int h = blockIdx.x, half = blockIdx.y, lane = threadIdx.x;
   const int par = *as_const<int32_t>(a.n_acc + 1) & 1;
   const float* rd = a.ring + ((size_t)par * a.nh + h) * (a.T_max - 1) * kRingRow;
-  gdn_half_commit(a.S + (size_t)h * kD * kD, rd, checked_acc(a.n_acc, a.T_max, h == 0 && half == 0 && lane == 0),
+  gdn_half_commit<32>(a.S + (size_t)h * kD * kD, rd, checked_acc(a.n_acc, a.T_max, h == 0 && half == 0 && lane == 0),
                   half, lane);
 }
 
