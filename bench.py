@@ -496,7 +496,6 @@ def manifest(seeds):
     """What the numbers were measured on: device, software versions, clocks,
     a hash of the sources, the seeds and the host cores."""
     import platform
-    import subprocess
 
     import torch
     h = hashlib.sha256()
@@ -517,26 +516,37 @@ def manifest(seeds):
             m["amdgpu_driver"] = f.read().strip()
     except OSError:
         m["amdgpu_driver"] = None
+    m.update(HOST_FACTS)
+    return m
+
+
+# Facts that come from other programs (clocks, git), gathered by host_facts()
+# before this process touches the GPU: a child process started from a process
+# that has initialised the GPU must not exec another program.
+HOST_FACTS = {"clocks": None, "git_sha": None}
+
+
+def host_facts():
+    import subprocess
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
         clk = json.loads(r.stdout) if r.returncode == 0 and r.stdout.strip().startswith("{") else {}
         card = next(iter(clk.values()), {}) if clk else {}
-        m["clocks"] = {k: v for k, v in card.items() if "clk" in k.lower()} or None
+        HOST_FACTS["clocks"] = {k: v for k, v in card.items() if "clk" in k.lower()} or None
     except (OSError, ValueError, subprocess.SubprocessError):
-        m["clocks"] = None
+        pass
     try:
         r = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"], capture_output=True, text=True,
                            timeout=10)
-        m["git_sha"] = r.stdout.strip() if r.returncode == 0 else None
+        HOST_FACTS["git_sha"] = r.stdout.strip() if r.returncode == 0 else None
     except (OSError, subprocess.SubprocessError):
-        m["git_sha"] = None
-    return m
+        pass
 
 
 def cpu_baseline_one_core(T=12):
     """The oracle on one core (OMP_NUM_THREADS=1, in a child process that
-    touches no GPU): the first layer's P_in GEMV (5120 -> 10240) at T = 12,
-    reported as weight GB/s."""
+    touches no GPU, started before this process touches the GPU): the first
+    layer's P_in GEMV (5120 -> 10240) at T = 12, reported as weight GB/s."""
     import subprocess
     code = ("import json, time, sys; sys.path.insert(0, %r)\n"
             "import oracle\nfrom synth import recipes\n"
@@ -663,6 +673,12 @@ def main():
             json.dump(rec, f, indent=1)
         print(json.dumps(rec), flush=True)
         return
+    # every child process starts here, before this process touches the GPU
+    one_core = None
+    if not args.copy_probe:
+        host_facts()
+        if not args.no_cpu_baseline:
+            one_core = cpu_baseline_one_core()
     import torch
 
     import __graft_entry__
@@ -739,7 +755,7 @@ def main():
     attainable = read_probe()
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     if cpu is not None:
-        cpu["one_core"] = cpu_baseline_one_core()
+        cpu["one_core"] = one_core
     seeds = {"stack": recipes.STACK_SEED, "lm_head": recipes.LM_SEED, "gdn": recipes.GDN_SEED,
              "mtp": recipes.STACK_SEED, "step_inputs": "stack seed, tensors 10000 + step and 20000 + step"}
     out = {
