@@ -663,6 +663,9 @@ def main():
                     help="write the traffic record from rocprofv3 output under DIR (no GPU work) and exit")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the HBM byte counters)")
+    ap.add_argument("--no-children", action="store_true",
+                    help="start no child process (no clocks, git SHA or one-core oracle run): for runs under a "
+                         "profiler that initialises the GPU in this process before it starts")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus})", file=sys.stderr)
@@ -675,7 +678,7 @@ def main():
         return
     # every child process starts here, before this process touches the GPU
     one_core = None
-    if not args.copy_probe:
+    if not args.copy_probe and not args.no_children:
         host_facts()
         if not args.no_cpu_baseline:
             one_core = cpu_baseline_one_core()
