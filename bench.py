@@ -18,6 +18,7 @@ Prints ONE JSON line.  --gpus N > 1 exits: the benchmark runs on one GPU.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -122,7 +123,7 @@ def step_inputs(T, steps, n_gdn_layers, device="cuda"):
 
 
 # ------------------------------------------------------------------ timing
-def time_steps(stack, T, gs, n_agents, xs, gins, steps, warmup):
+def time_steps(stack, T, gs, n_agents, xs, gins, steps, warmup, attn=None):
     import torch
 
     import bit_weight_streaming_q4_amd as mk
@@ -133,7 +134,12 @@ def time_steps(stack, T, gs, n_agents, xs, gins, steps, warmup):
         recipes.uniform_i32(2, 50000 + T, 0, max(T - G, 1), 0, VOCAB - 1))).to(dev)
     nh = gins[0]["q"].shape[1]
     go = torch.empty(T, nh, 128, dtype=torch.float32, device=dev)
-    ws = stack.workspace(T, dev)
+    if attn is None:
+        ws = stack.workspace(T, dev)
+    else:
+        gsa = np.asarray(gs, np.int32)
+        ws = mk.workspace(int(mk.lib().mk_decode_step_attn_workspace(stack.h, T, gsa.ctypes.data, G,
+                                                                       ctypes.byref(attn))), dev)
     xbuf = torch.empty_like(xs[0])
     t_agent = T // n_agents
 
@@ -141,7 +147,7 @@ def time_steps(stack, T, gs, n_agents, xs, gins, steps, warmup):
         xbuf.copy_(xs[i % len(xs)])
         for a in stack.agents:
             a.n_acc[0:1].fill_(t_agent - 1)  # replay the most ring rows possible
-        return mk.mk_decode_step(stack, xbuf, gs, drafts, gdn=gins[i % len(gins)], gdn_o=go, ws=ws)
+        return mk.mk_decode_step(stack, xbuf, gs, drafts, gdn=gins[i % len(gins)], gdn_o=go, ws=ws, attn=attn)
 
     for i in range(warmup):
         one(i)
@@ -177,6 +183,54 @@ def time_steps(stack, T, gs, n_agents, xs, gins, steps, warmup):
         log(f"T={T} P_out with GDN {per[[l for l in range(n_layers) if l % 4 != 3], 1].mean():.1f} us, "
             f"without {per[[l for l in range(n_layers) if l % 4 == 3], 1].mean():.1f} us")
     return r
+
+
+def attention_step(layers, lm, gl, steps, warmup, n_attn=16, ctx=32768):
+    """The T = 12 step with its 16 full-attention layers' attention in the
+    launch: 4 agents of 3 rows, each with `ctx` cached positions per layer
+    (fp16, 32 query / 8 KV heads of 128, gated).  Every layer's caches hold the
+    same seeded values (the bytes read per layer are what matters here)."""
+    import torch
+
+    import bit_weight_streaming_q4_amd as mk
+    from synth import recipes
+    T, gs, G = 12, [0, 3, 6, 9, 12], 4
+    sizes = [3] * G
+    cap = recipes.attn_cap([ctx] * G, sizes)
+    t0 = time.time()
+    a = recipes.step_attn_inputs(n_attn, [ctx] * G, sizes, cap=cap)
+    k1, v1 = torch.from_numpy(a["k"]).to("cuda"), torch.from_numpy(a["v"]).to("cuda")
+    kc = torch.empty((n_attn,) + tuple(k1.shape), dtype=k1.dtype, device="cuda")
+    vc = torch.empty((n_attn,) + tuple(v1.shape), dtype=v1.dtype, device="cuda")
+    for i in range(n_attn):
+        kc[i].copy_(k1)
+        vc[i].copy_(v1)
+    del k1, v1
+    q, gate = torch.from_numpy(a["q"]).to("cuda"), torch.from_numpy(a["gate"]).to("cuda")
+    o = torch.empty_like(q)
+    log(f"attention inputs: {n_attn} layers x {G} agents x {ctx} positions ({time.time() - t0:.1f}s)")
+    at = mk.step_attn(q, kc, vc, o, a["ctx"], gate=gate)
+    agents = make_agents(G, len(gl), 5)
+    stack = mk.Stack(layers, lm, gdn_layers=gl, agents=agents)
+    xs, gins = step_inputs(T, min(steps + warmup, 8), len(gl))
+    log(f"timing T=12 with attention")
+    r = time_steps(stack, T, gs, G, xs, gins, steps, warmup, attn=at)
+    b = step_bytes(T, G, len(layers))
+    kv = n_attn * sum(ctx + n for n in sizes) * recipes.ATTN_KV_HEADS * 128 * 2 * 2
+    io = n_attn * T * recipes.ATTN_Q_HEADS * 128 * 4 * 3
+    total = b["total"] + kv + io
+    out = {"attention_layers": n_attn, "agents": G, "positions_per_agent": ctx, "rows": T,
+           "ms_per_step": round(r["ms_per_step"], 4), "kernel_ms": round(r["kernel_ms"], 4),
+           "kernel_ms_median": round(r["kernel_ms_median"], 4),
+           "attention_bytes": int(kv + io), "total_bytes": int(total),
+           "total_gb_s_kernel": round(total / (r["kernel_ms"] * 1e-3) / 1e9, 1),
+           "frac_of_8TBs": round(total / (r["kernel_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    log(f"T=12 with attention: kernel {r['kernel_ms']:.3f} ms, {out['total_gb_s_kernel']:.0f} GB/s over "
+        f"{total / 1e9:.2f} GB")
+    stack.close()
+    del stack, agents, kc, vc, q, gate, o, at, xs, gins
+    torch.cuda.empty_cache()
+    return out
 
 
 # ------------------------------------------------------------------ standalone entry points
@@ -663,6 +717,8 @@ def main():
                     help="write the traffic record from rocprofv3 output under DIR (no GPU work) and exit")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the HBM byte counters)")
+    ap.add_argument("--no-attention", action="store_true",
+                    help="skip the T = 12 step with the attention layers in the launch")
     ap.add_argument("--no-children", action="store_true",
                     help="start no child process (no clocks, git SHA or one-core oracle run): for runs under a "
                          "profiler that initialises the GPU in this process before it starts")
@@ -753,6 +809,8 @@ def main():
         tj = json.load(open(TRAFFIC_FILE))
         if tj.get("kernel_source_hash") == kernel_source_hash():
             traffic = tj.get("bytes_per_launch")
+    attention = None if (args.no_attention or args.only_primary) else attention_step(layers, lm, gl, args.steps,
+                                                                                       args.warmup)
     kernels = None if args.no_kernels else kernel_bench(lm)
     accepts = None if args.no_kernels else accept_histogram(lm)
     attainable = read_probe()
@@ -792,6 +850,7 @@ def main():
                                       "step_ms_p10_p90": [round(v, 4) for v in r["step_ms_p10_p90"]]}
                              for T, r in sorted(results.items())},
                    "seeded_series_T12": series,
+                   "with_attention_T12": attention,
                    "lm_head_accept_lengths": accepts,
                    "standalone_kernels": kernels},
         "manifest": manifest(seeds),

@@ -38,6 +38,12 @@ class mk_deltanet(ctypes.Structure):
                 ("nh", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("T_max", ctypes.c_int32)]
 
 
+class mk_step_attn(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("cap", ctypes.c_int32),
+                ("h_ctx", ctypes.c_void_p), ("q", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+                ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("o", ctypes.c_void_p)]
+
+
 class mk_mtp(ctypes.Structure):
     _fields_ = [("fc", mk_q4k), ("gate", mk_q4k), ("up", mk_q4k), ("down", mk_q4k)]
 
@@ -98,6 +104,10 @@ def lib():
     L.mk_decode_step_workspace.argtypes = [P, i32]
     L.mk_decode_step_workspace.restype = sz
     L.mk_decode_step.argtypes = [P, P, i32, P, i32, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+    L.mk_decode_step_attn.argtypes = [P, P, i32, P, i32, P, P, P, P, P, P, P, P, P, P, P, ctypes.POINTER(mk_step_attn),
+                                      P, sz, P]
+    L.mk_decode_step_attn_workspace.argtypes = [P, i32, P, i32, ctypes.POINTER(mk_step_attn)]
+    L.mk_decode_step_attn_workspace.restype = sz
     L.mk_decode_step_stamps.argtypes = [P, i32, P, P, i32, P]
     L.mk_decode_step_last_ms.argtypes = [P]
     L.mk_decode_step_last_ms.restype = ctypes.c_float
@@ -448,11 +458,24 @@ class Stack:
         return self._ws[T]
 
 
+def step_attn(q, k_cache, v_cache, o, ctx, gate=None):
+    """The attention of a step's full-attention layers (mk_step_attn): q, gate,
+    o [n_layers][T][Hq][128] fp32; k_cache [n_layers][G][Hkv][cap][128] and
+    v_cache [n_layers][G][Hkv][128][cap] fp16 (device); ctx: cached positions
+    per agent.  The returned structure keeps its arguments alive."""
+    ctx = np.ascontiguousarray(ctx, np.int32)
+    a = mk_step_attn(int(q.shape[0]), int(q.shape[2]), int(k_cache.shape[2]), int(k_cache.shape[3]), ctx.ctypes.data,
+                     _ptr(q), _ptr(gate), _ptr(k_cache), _ptr(v_cache), _ptr(o))
+    a._keep = (ctx, q, gate, k_cache, v_cache, o)
+    return a
+
+
 def mk_decode_step(st: Stack, x, group_start=None, drafts=None, gdn=None, gdn_o=None, argmax=None, trace=None,
-                   ws=None, stream=None):
+                   ws=None, stream=None, attn=None):
     """One decode step in one persistent launch.  x [T][hidden] (in/out).
     gdn: dict of q, k, v, g, beta device tensors [T][nh][..] (None without GDN
-    layers).  Returns (tokens [T] int32 host, n_acc [G] int32 host)."""
+    layers).  attn: a step_attn(...) for the full-attention layers (None:
+    none).  Returns (tokens [T] int32 host, n_acc [G] int32 host)."""
     T = x.shape[0]
     if group_start is None:
         gs, G = None, 1
@@ -462,13 +485,25 @@ def mk_decode_step(st: Stack, x, group_start=None, drafts=None, gdn=None, gdn_o=
         gs, G = gsa.ctypes.data, len(gsa) - 1
     tokens = np.full(T, -1, np.int32)
     n_acc = np.zeros(G, np.int32)
-    if ws is None:
-        ws = st.workspace(T, x.device)
     g = gdn or {}
-    _check(lib().mk_decode_step(st.h, _ptr(x), T, gs, G, _ptr(drafts), _ptr(g.get("q")), _ptr(g.get("k")),
-                                _ptr(g.get("v")), _ptr(g.get("g")), _ptr(g.get("beta")), _ptr(gdn_o),
-                                tokens.ctypes.data, n_acc.ctypes.data, _ptr(argmax), _ptr(trace), _ptr(ws),
-                                ws.numel(), _stream(stream)), "mk_decode_step")
+    if attn is None:
+        if ws is None:
+            ws = st.workspace(T, x.device)
+        _check(lib().mk_decode_step(st.h, _ptr(x), T, gs, G, _ptr(drafts), _ptr(g.get("q")), _ptr(g.get("k")),
+                                    _ptr(g.get("v")), _ptr(g.get("g")), _ptr(g.get("beta")), _ptr(gdn_o),
+                                    tokens.ctypes.data, n_acc.ctypes.data, _ptr(argmax), _ptr(trace), _ptr(ws),
+                                    ws.numel(), _stream(stream)), "mk_decode_step")
+        return tokens, n_acc
+    if ws is None:
+        need = int(lib().mk_decode_step_attn_workspace(st.h, T, gs, G, ctypes.byref(attn)))
+        if need == 0:
+            raise MkError(MK_ERR_ARG, "mk_decode_step_attn_workspace: invalid attention arguments")
+        ws = workspace(need, x.device)
+    _check(lib().mk_decode_step_attn(st.h, _ptr(x), T, gs, G, _ptr(drafts), _ptr(g.get("q")), _ptr(g.get("k")),
+                                     _ptr(g.get("v")), _ptr(g.get("g")), _ptr(g.get("beta")), _ptr(gdn_o),
+                                     tokens.ctypes.data, n_acc.ctypes.data, _ptr(argmax), _ptr(trace),
+                                     ctypes.byref(attn), _ptr(ws), ws.numel(), _stream(stream)),
+           "mk_decode_step_attn")
     return tokens, n_acc
 
 

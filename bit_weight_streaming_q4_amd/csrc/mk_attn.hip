@@ -33,65 +33,16 @@
 #include <stdint.h>
 
 #include "mk.h"
+#include "mk_attn.h"
 #include "mk_internal.h"
 
 namespace mk {
 namespace {
 
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef unsigned u4 __attribute__((ext_vector_type(4)));
+using namespace attn;
 
-constexpr int kD = 128;
-constexpr int kTile = 64;
 constexpr int kWaves = 4;
 constexpr int kMergeFloats = 34;  // per lane and column block: 32 outputs, max, sum
-
-__device__ __forceinline__ h8 as_h8(u4 u) { return __builtin_bit_cast(h8, u); }
-__device__ __forceinline__ u4 as_u4(h8 h) { return __builtin_bit_cast(u4, h); }
-
-__device__ __forceinline__ f4 mma(u4 a, u4 b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a), as_h8(b), c, 0, 0, 0);
-}
-
-// x = hi + lo with hi, lo fp16.  The residual is taken from the packed hi
-// bits themselves: the compiler may round the packing conversion and a
-// separate scalar conversion of the same value differently on exact ties,
-// and a residual from the other hi would then add the wrong sign.
-__device__ __forceinline__ void split_f16(const float (&x)[8], u4& hi_out, u4& lo_out) {
-  h8 hi;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) hi[j] = (_Float16)x[j];
-  u4 hb = as_u4(hi);
-  asm volatile("" : "+v"(hb));
-  const h8 hr = as_h8(hb);
-  h8 lo;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) lo[j] = (_Float16)(x[j] - (float)hr[j]);
-  hi_out = hb;
-  lo_out = as_u4(lo);
-}
-
-// One column block fits two waves per SIMD (256 registers with the matrix
-// accumulators); more column blocks run one wave per SIMD.
-// Eight q8_0 codes (two dwords of int8) -> eight fp16 values, exactly: each
-// byte, sign-flipped to c + 128, becomes the low byte of the fp16 1024 + c + 128
-// (exponent byte 0x64), and 1152 is subtracted in packed fp16.
-// The empty asm keeps each conversion at its use: with several column
-// blocks the compiler would otherwise hold every converted operand of the
-// tile at once and spill.
-__device__ __forceinline__ u4 codes_f16(uint2 c) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  asm volatile("" : "+v"(c));
-  const unsigned x0 = c.x ^ 0x80808080u, x1 = c.y ^ 0x80808080u;
-  const h2 off = {(_Float16)1152.f, (_Float16)1152.f};
-  u4 r;
-  r[0] = __builtin_bit_cast(unsigned, __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u)) - off);
-  r[1] = __builtin_bit_cast(unsigned, __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u)) - off);
-  r[2] = __builtin_bit_cast(unsigned, __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u)) - off);
-  r[3] = __builtin_bit_cast(unsigned, __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u)) - off);
-  return r;
-}
 
 // Q8: the cache holds q8_0 blocks (32 int8 codes, one fp16 scale).  Each score
 // product m covers exactly the 32-dim block m of a K row, and each P.V
@@ -146,20 +97,16 @@ void k_attn_split(const AttnArgs a) {
   // This head's rows of the cache format in use (the other format's
   // pointers are null and stay untouched).
   const size_t gh = (size_t)g * a.Hkv + h;
-  const uint16_t* Kb = nullptr;
-  const uint16_t* Vb = nullptr;
-  const int8_t* K8 = nullptr;
-  const int8_t* V8 = nullptr;
-  const uint16_t* KS = nullptr;
-  const uint16_t* VS = nullptr;
+  KVHead kv = {};
+  kv.cap = a.cap;
   if constexpr (Q8) {
-    K8 = a.k8 + gh * a.cap * kD;
-    V8 = a.v8 + gh * kD * a.cap;
-    KS = a.ks + gh * a.cap * (kD / 32);
-    VS = a.vs + gh * (a.cap / 32) * kD;
+    kv.K8 = a.k8 + gh * a.cap * kD;
+    kv.V8 = a.v8 + gh * kD * a.cap;
+    kv.KS = a.ks + gh * a.cap * (kD / 32);
+    kv.VS = a.vs + gh * (a.cap / 32) * kD;
   } else {
-    Kb = a.k + gh * a.cap * kD;
-    Vb = a.v + gh * kD * a.cap;
+    kv.K = a.k + gh * a.cap * kD;
+    kv.V = a.v + gh * kD * a.cap;
   }
   f4 acc[NB][8];
   float mrow[NB], lsum[NB];
@@ -171,64 +118,9 @@ void k_attn_split(const AttnArgs a) {
     for (int db = 0; db < 8; ++db) acc[nb][db] = f4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Tiles start at multiples of 64 below L_g <= cap and cap % 64 == 0, so
-  // every load of a tile stays inside this head's cache rows; positions past
-  // L_g are masked (scores) or zeroed (values) below.
   for (int t0 = p0; t0 < p1; t0 += kTile) {
-    u4 kr[4][4], vr[2][8];        // fp16 operands
-    uint2 k8[4][4], v8[2][8];     // Q8: codes
-    u4 ksc[4][2];                 // Q8: K scales [b][row i / 2] -> halves (i % 2) * 4 + m
-    uint2 vsc[2][8];              // Q8: V scales of dims 16db + 4grp .. +3, block t0/32 + hh
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int pos = t0 + 32 * (b >> 1) + 8 * (col >> 2) + 4 * (b & 1) + (col & 3);
-      if constexpr (Q8) {
-        const uint2* src = (const uint2*)(K8 + (size_t)pos * kD + 8 * grp);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) k8[b][m] = src[4 * m];
-        const u4* ss = (const u4*)(KS + (size_t)(t0 + 32 * (b >> 1) + 8 * grp + 4 * (b & 1)) * (kD / 32));
-        ksc[b][0] = ss[0];
-        ksc[b][1] = ss[1];
-      } else {
-        const u4* src = (const u4*)(Kb + (size_t)pos * kD + 8 * grp);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) kr[b][m] = src[4 * m];
-      }
-    }
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        if constexpr (Q8) {
-          v8[hh][db] = *(const uint2*)(V8 + ((size_t)(t0 >> 6) * kD + 16 * db + col) * kTile + 32 * hh + 8 * grp);
-          vsc[hh][db] = *(const uint2*)(VS + (size_t)((t0 >> 5) + hh) * kD + 16 * db + 4 * grp);
-        } else {
-          vr[hh][db] = *(const u4*)(Vb + (size_t)(16 * db + col) * a.cap + t0 + 32 * hh + 8 * grp);
-        }
-      }
-    auto zero_tail = [&](int hh, u4 r) -> u4 {  // V positions past L_g contribute nothing
-      h8 v = as_h8(r);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (t0 + 32 * hh + 8 * grp + j >= Lg) v[j] = (_Float16)0.f;
-      return as_u4(v);
-    };
-    if constexpr (!Q8) {
-      if (t0 + kTile > Lg) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int db = 0; db < 8; ++db) vr[hh][db] = zero_tail(hh, vr[hh][db]);
-      }
-    }
-    auto v_operand = [&](int hh, int db) -> u4 {
-      if constexpr (Q8) {
-        const u4 r = codes_f16(v8[hh][db]);
-        return t0 + kTile > Lg ? zero_tail(hh, r) : r;
-      } else {
-        return vr[hh][db];
-      }
-    };
+    KVTile x;
+    load_tile<Q8>(kv, t0, Lg, col, grp, x);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       u4 qh[4], ql[4];
@@ -237,76 +129,7 @@ void k_attn_split(const AttnArgs a) {
         qh[m] = qs[(((w * NB + nb) * 4 + m) * 2 + 0) * 64 + lane];
         ql[m] = qs[(((w * NB + nb) * 4 + m) * 2 + 1) * 64 + lane];
       }
-      f4 sc[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        f4 c = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          if constexpr (Q8) {
-            const u4 kf = codes_f16(k8[b][m]);
-            f4 t = mma(kf, qh[m], f4{0.f, 0.f, 0.f, 0.f});
-            t = mma(kf, ql[m], t);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) c[i] += (float)as_h8(ksc[b][i >> 1])[(i & 1) * 4 + m] * t[i];
-          } else {
-            c = mma(kr[b][m], qh[m], c);
-            c = mma(kr[b][m], ql[m], c);
-          }
-        }
-        sc[b] = c;
-      }
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int pos = t0 + 32 * (b >> 1) + 8 * grp + 4 * (b & 1) + i;
-          const float x = pos < lim[nb] ? sc[b][i] : -INFINITY;
-          sc[b][i] = x;
-          tmax = fmaxf(tmax, x);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float mnew = fmaxf(mrow[nb], tmax);
-      const float muse = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = exp2f(mrow[nb] - muse);
-      mrow[nb] = mnew;
-      float ps = 0.f;
-      float pv[2][8];
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = exp2f(sc[b][i] - muse);
-          ps += p;
-          pv[b >> 1][4 * (b & 1) + i] = p;
-        }
-      u4 ph[2], pl[2];
-      split_f16(pv[0], ph[0], pl[0]);
-      split_f16(pv[1], ph[1], pl[1]);
-      lsum[nb] = lsum[nb] * alpha + ps;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) acc[nb][db] *= alpha;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          const u4 vo = v_operand(hh, db);
-          if constexpr (Q8) {
-            f4 t = mma(vo, ph[hh], f4{0.f, 0.f, 0.f, 0.f});
-            t = mma(vo, pl[hh], t);
-            // a block holding no position of this agent may carry any scale
-            const bool live = t0 + 32 * hh < Lg;
-            const uint2 sv = vsc[hh][db];
-            const h8 s8 = as_h8(u4{sv.x, sv.y, 0u, 0u});
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[nb][db][i] += (live ? (float)s8[i] : 0.f) * t[i];
-          } else {
-            acc[nb][db] = mma(vo, ph[hh], acc[nb][db]);
-            acc[nb][db] = mma(vo, pl[hh], acc[nb][db]);
-          }
-        }
+      tile_update<Q8>(x, t0, Lg, lim[nb], grp, qh, ql, acc[nb], mrow[nb], lsum[nb]);
     }
   }
 

@@ -66,6 +66,7 @@
 #include "mk_device.h"
 #include "mk_lm.h"
 #include "mk_gdn.h"
+#include "mk_attn.h"
 #include "mk_internal.h"
 
 namespace mk {
@@ -200,6 +201,20 @@ struct StepArgs {
   const uint64_t* ws_tag;  // the workspace's record of the stack whose tables it holds
   uint64_t tag;            // this stack's tag
   float lm_pre;            // exact power-of-two prescale of the lm_head input rows
+  // full-attention items, run beside the layer pipeline like the GDN jobs
+  int n_attn;                          // attention layers (0: none)
+  int attn_Hq, attn_Hkv, attn_gqa, attn_cap, attn_chunk;
+  int attn_ctx[kMaxAgents];            // cached positions per agent before this step's rows
+  int attn_nsplit[kMaxAgents];         // splits per (agent, KV head)
+  int attn_item0[kMaxAgents + 1];      // first item of each agent within a layer
+  float attn_qscale;                   // log2(e) / sqrt(128)
+  const float* attn_q;                 // [n_attn][T][Hq][128]
+  const float* attn_gate;              // [n_attn][T][Hq][128] or null
+  const uint16_t* attn_k;              // [n_attn][G][Hkv][cap][128] fp16
+  const uint16_t* attn_v;              // [n_attn][G][Hkv][128][cap] fp16
+  float* attn_o;                       // [n_attn][T][Hq][128]
+  float* attn_part;                    // per item: [16 columns][128] outputs, then (max, sum) per column
+  unsigned* attn_ticket;               // per (layer, agent, KV head): splits finished, 64 B apart
 };
 
 __device__ __forceinline__ bool layer_is_gdn(const StepArgs& a, int l) {
@@ -1782,6 +1797,118 @@ __device__ __forceinline__ void watch_wave(const StepArgs& a, BlockState<T>& s, 
   }
 }
 
+// ------------------------------------------------------------ attention items
+// Split-K flash decoding of the full-attention layers beside the layer
+// pipeline, like the GDN jobs (the outputs are not fed back).  Item (layer i,
+// agent g, KV head h, split s) covers positions [s chunk, min(L_g, (s + 1)
+// chunk)) of the agent's cache (L_g = cached positions + the agent's n_g new
+// rows, whose k and v are already in the cache), for the agent's n_g rows x
+// Hq/Hkv query heads of KV head h (one block of 16 query columns; row r of
+// the agent sees positions up to ctx + r).  Its partial goes to the
+// workspace, and the last split of (i, g, h) to finish merges all of them
+// and applies the output gate.  The tile arithmetic is that of the
+// standalone attention launches (mk_attn.h).
+constexpr int kAttnPartFloats = 16 * 128 + 16 * 2;
+
+__device__ __forceinline__ void attn_item(const StepArgs& a, int i, int j, int lane) {
+  int g = 0;
+  while (j >= a.attn_item0[g + 1]) ++g;
+  g = uniform(g);
+  const int ns = uniform(a.attn_nsplit[g]);
+  const int per = uniform(a.attn_item0[a.G]);
+  const int jg = uniform(a.attn_item0[g]);
+  const int loc = j - jg;
+  const int h = loc / ns, s = loc - h * ns;
+  const int r0 = uniform(a.gs[g]), ng = uniform(a.gs[g + 1]) - r0;
+  const int ctx = uniform(a.attn_ctx[g]), Lg = ctx + ng;
+  const int p0 = s * a.attn_chunk, p1 = min(Lg, p0 + a.attn_chunk);
+  const int gqa = a.attn_gqa, NQ = ng * gqa, Hq = a.attn_Hq;
+  const int col = lane & 15, grp = lane >> 4;
+  const bool valid = col < NQ;
+  const int row = r0 + (valid ? col / gqa : 0), hq = h * gqa + (valid ? col % gqa : 0);
+  const int lim = valid ? min(ctx + col / gqa + 1, p1) : 0;  // positions below lim are visible to this column
+  // this lane's query column, scaled and split into fp16 hi + lo
+  attn::u4 qh[4], ql[4];
+  const float* qr = a.attn_q + (((size_t)i * a.T + row) * Hq + hq) * 128 + 8 * grp;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    float4 u0 = make_float4(0.f, 0.f, 0.f, 0.f), u1 = u0;
+    if (valid) {
+      u0 = *(const float4*)(qr + 32 * m);
+      u1 = *(const float4*)(qr + 32 * m + 4);
+    }
+    const float q = a.attn_qscale;
+    const float x[8] = {u0.x * q, u0.y * q, u0.z * q, u0.w * q, u1.x * q, u1.y * q, u1.z * q, u1.w * q};
+    attn::split_f16(x, qh[m], ql[m]);
+  }
+  const size_t gh = ((size_t)i * a.G + g) * a.attn_Hkv + h;
+  attn::KVHead kv = {};
+  kv.cap = a.attn_cap;
+  kv.K = a.attn_k + gh * kv.cap * 128;
+  kv.V = a.attn_v + gh * 128 * kv.cap;
+  attn::f4 acc[8];
+  float mrow = -INFINITY, lsum = 0.f;
+#pragma unroll
+  for (int db = 0; db < 8; ++db) acc[db] = attn::f4{0.f, 0.f, 0.f, 0.f};
+  for (int t0 = p0; t0 < p1; t0 += attn::kTile) {
+    attn::KVTile x;
+    attn::load_tile<false>(kv, t0, Lg, col, grp, x);
+    attn::tile_update<false>(x, t0, Lg, lim, grp, qh, ql, acc, mrow, lsum);
+  }
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  // the item's partial: lane (col, grp) holds dims 16 db + 4 grp .. + 3 of column col
+  float* po = a.attn_part + ((size_t)i * per + j) * kAttnPartFloats;
+#pragma unroll
+  for (int db = 0; db < 8; ++db) st16(po, (col * 128 + 16 * db + 4 * grp) * 4, acc[db]);
+  if (grp == 0) {
+    st_coh(po + 2048 + 2 * col, mrow);
+    st_coh(po + 2048 + 2 * col + 1, lsum);
+  }
+  int last = 0;
+  if (lane == 0) last = ticket_add(a.attn_ticket + gh * 16) == (unsigned)(ns - 1);
+  if (!__shfl(last, 0, 64)) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  // merge the splits: lane (col, grp) takes dims 32 grp .. 32 grp + 31 of column col
+  const float* pb = a.attn_part + ((size_t)i * per + jg + (size_t)h * ns) * kAttnPartFloats;
+  float m = -INFINITY, l = 0.f;
+  attn::f4 y[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) y[k] = attn::f4{0.f, 0.f, 0.f, 0.f};
+  for (int s2 = 0; s2 < ns; ++s2) {
+    const float* ps = pb + (size_t)s2 * kAttnPartFloats;
+    const float ms = ld_coh(ps + 2048 + 2 * col), ls = ld_coh(ps + 2048 + 2 * col + 1);
+    const float mn = fmaxf(m, ms);
+    if (mn == -INFINITY) continue;
+    const float ao = exp2f(m - mn), as = exp2f(ms - mn);
+    l = l * ao + ls * as;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = y[k] * ao + ld16(ps, (col * 128 + 32 * grp + 4 * k) * 4) * as;
+    m = mn;
+  }
+  if (!valid) return;
+  const size_t ob = (((size_t)i * a.T + row) * Hq + hq) * 128 + 32 * grp;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    attn::f4 v = y[k] / l;
+    if (a.attn_gate) {
+      const float4 gt = *(const float4*)(a.attn_gate + ob + 4 * k);
+      v[0] *= 1.f / (1.f + expf(-gt.x));
+      v[1] *= 1.f / (1.f + expf(-gt.y));
+      v[2] *= 1.f / (1.f + expf(-gt.z));
+      v[3] *= 1.f / (1.f + expf(-gt.w));
+    }
+    *(attn::f4*)(a.attn_o + ob + 4 * k) = v;
+  }
+}
+
+__device__ __forceinline__ void attn_items(const StepArgs& a, int lane) {
+  if (a.n_attn <= 0) return;
+  const int per = uniform(a.attn_item0[a.G]);
+  const long total = (long)a.n_attn * per;
+  for (long it = blockIdx.x; it < total; it += gridDim.x) attn_item(a, (int)(it / per), (int)(it % per), lane);
+}
+
 // The block's share of every GDN layer's half-head jobs, in layer order.
 // Nothing in the step consumes their outputs, so they run beside the layer
 // pipeline instead of inside one of its phases; the block's last barrier
@@ -1917,6 +2044,7 @@ __global__ __launch_bounds__(kBlock) void k_decode_step(StepArgs a) {
     watch_wave<T>(a, s, lane);
   } else {
     gdn_wave(a, lane);
+    attn_items(a, lane);
     stores_done();
     if (lane == 0) lds_st(&s.gdn_done, 1);
   }
@@ -2298,6 +2426,53 @@ bool make_plans(const mk_stack_desc& d, int grid, std::vector<BlockPlan>& out) {
   return true;
 }
 
+// The attention items of a step: positions per split (a multiple of 64),
+// splits per (agent, KV head) and the first item of each agent in a layer.
+// The items of all attention layers are dealt to the grid's GDN waves; the
+// split is chosen so that each wave gets about 16 items and no item is
+// shorter than 4 tiles.
+struct AttnStepPlan {
+  int chunk, per;
+  int nsplit[kMaxAgents], item0[kMaxAgents + 1];
+  size_t part_bytes, ticket_bytes;
+};
+
+int attn_check(const mk_step_attn* at, int T, const std::vector<int>& gs, int G, AttnStepPlan& p) {
+  if (!at || at->n_layers < 1) return sfail(MK_ERR_ARG, "attention: no layers");
+  if (at->Hq < 1 || at->Hkv < 1 || at->Hq % at->Hkv) return sfail(MK_ERR_SHAPE, "attention: Hq must be a multiple of Hkv");
+  if (at->cap <= 0 || at->cap % 64) return sfail(MK_ERR_SHAPE, "attention: cap must be a positive multiple of 64");
+  if (G > kMaxAgents) return sfail(MK_ERR_RANGE, "attention: at most 16 agents");
+  if (!at->h_ctx || !at->q || !at->k_cache || !at->v_cache || !at->o) return sfail(MK_ERR_ARG, "attention: null pointer");
+  const void* ptrs[5] = {at->q, at->gate, at->k_cache, at->v_cache, at->o};
+  for (const void* q : ptrs)
+    if ((uintptr_t)q % 16) return sfail(MK_ERR_ALIGN, "attention: a buffer is not 16-B aligned");
+  const int gqa = at->Hq / at->Hkv;
+  long W = 0;
+  for (int g = 0; g < G; ++g) {
+    const int ng = gs[g + 1] - gs[g];
+    if (ng * gqa > 16) return sfail(MK_ERR_SHAPE, "attention: an agent's rows x Hq/Hkv exceed 16 query columns");
+    if (at->h_ctx[g] < 0 || (long)at->h_ctx[g] + ng > at->cap)
+      return sfail(MK_ERR_RANGE, "attention: cached positions + new rows exceed cap");
+    W += ((long)at->h_ctx[g] + ng) * at->Hkv;
+  }
+  const long target = 16L * 256;  // items over the step
+  long chunk = ((long)at->n_layers * W + target - 1) / target;
+  chunk = (chunk + 63) / 64 * 64;
+  if (chunk < 4 * 64) chunk = 4 * 64;
+  p.chunk = (int)chunk;
+  p.item0[0] = 0;
+  for (int g = 0; g < G; ++g) {
+    const long L = (long)at->h_ctx[g] + (gs[g + 1] - gs[g]);
+    p.nsplit[g] = (int)((L + chunk - 1) / chunk);
+    p.item0[g + 1] = p.item0[g] + p.nsplit[g] * at->Hkv;
+  }
+  p.per = p.item0[G];
+  p.part_bytes = a256((size_t)at->n_layers * p.per * (16 * 128 + 32) * 4);
+  p.ticket_bytes = a256((size_t)at->n_layers * G * at->Hkv * 64);
+  (void)T;
+  return MK_OK;
+}
+
 int valid_q(const mk_q4k& w, int n_out, int n_in) {
   return w.blocks && w.n_out == n_out && w.n_in == n_in && ((uintptr_t)w.blocks % 256) == 0;
 }
@@ -2385,6 +2560,33 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
                    const int32_t* drafts, const float* gdn_q, const float* gdn_k, const float* gdn_v,
                    const float* gdn_g, const float* gdn_beta, float* gdn_o, int32_t* h_tokens, int32_t* h_n_acc,
                    int32_t* d_argmax, float* trace, void* ws, size_t ws_bytes, void* stream) {
+  return mk_decode_step_attn(st, x, T, h_group_start, G, drafts, gdn_q, gdn_k, gdn_v, gdn_g, gdn_beta, gdn_o,
+                             h_tokens, h_n_acc, d_argmax, trace, nullptr, ws, ws_bytes, stream);
+}
+
+size_t mk_decode_step_attn_workspace(const mk_stack* st, int32_t T, const int32_t* h_group_start, int32_t G,
+                                     const mk_step_attn* attn) {
+  if (!st || T < 1 || T > kStepTMax) return 0;
+  const size_t base = layout(st, T).total;
+  if (!attn) return base;
+  std::vector<int> gs;
+  if (!h_group_start) {
+    if (G != 1) return 0;
+    gs = {0, T};
+  } else {
+    if (G < 1 || G > MK_LM_MAX_G) return 0;
+    gs.assign(h_group_start, h_group_start + G + 1);
+  }
+  AttnStepPlan ap;
+  if (attn_check(attn, T, gs, G, ap) != MK_OK) return 0;
+  return base + ap.part_bytes + ap.ticket_bytes;
+}
+
+int mk_decode_step_attn(mk_stack* st, float* x, int32_t T, const int32_t* h_group_start, int32_t G,
+                        const int32_t* drafts, const float* gdn_q, const float* gdn_k, const float* gdn_v,
+                        const float* gdn_g, const float* gdn_beta, float* gdn_o, int32_t* h_tokens, int32_t* h_n_acc,
+                        int32_t* d_argmax, float* trace, const mk_step_attn* attn, void* ws, size_t ws_bytes,
+                        void* stream) {
   if (!st) return sfail(MK_ERR_ARG, "decode: null stack");
   if (T < 1 || T > kStepTMax) return sfail(MK_ERR_RANGE, "decode: T outside 1..24");
   if (!x || ((uintptr_t)x % 16)) return sfail(MK_ERR_ALIGN, "decode: x null or misaligned");
@@ -2409,9 +2611,15 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
     for (int g = 0; g < G; ++g)
       if (gs[g + 1] - gs[g] > st->dn[g].T_max) return sfail(MK_ERR_RANGE, "decode: group longer than its T_max");
   }
+  AttnStepPlan ap = {};
+  if (attn) {
+    const int r = attn_check(attn, T, gs, G, ap);
+    if (r != MK_OK) return r;
+  }
   const StepLayout y = layout(st, T);
   if (y.grid < 1) return sfail(MK_ERR_COOP, "decode: the step kernel does not fit on a compute unit");
-  if (!ws || ws_bytes < y.total) return set_error(MK_ERR_WORKSPACE, "decode: workspace %zu < %zu bytes", ws_bytes, y.total);
+  const size_t need = y.total + (attn ? ap.part_bytes + ap.ticket_bytes : 0);
+  if (!ws || ws_bytes < need) return set_error(MK_ERR_WORKSPACE, "decode: workspace %zu < %zu bytes", ws_bytes, need);
   if ((uintptr_t)ws % 256) return sfail(MK_ERR_ALIGN, "decode: workspace not 256-B aligned");
   hipStream_t s = (hipStream_t)stream;
   uint8_t* w8 = (uint8_t*)ws;
@@ -2437,7 +2645,8 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
     }
   }
   if (hipMemsetAsync(w8 + y.off_ctrl, 0, y.n_ctrl, s) != hipSuccess ||
-      hipMemsetAsync(w8 + y.off_out, 0, kOutWords * 4, s) != hipSuccess)
+      hipMemsetAsync(w8 + y.off_out, 0, kOutWords * 4, s) != hipSuccess ||
+      (attn && hipMemsetAsync(w8 + y.total + ap.part_bytes, 0, ap.ticket_bytes, s) != hipSuccess))
     return sfail(MK_ERR_LAUNCH, "decode: control reset failed");
   StepArgs a;
   memset(&a, 0, sizeof(a));
@@ -2505,6 +2714,27 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
   // sqrt(hidden) * 2^k <= 2^14 keeps every lm_head input far inside fp16's
   // range; the scaling is exact and leaves the argmax unchanged.
   a.lm_pre = ldexpf(1.0f, (int)floor(log2(16384.0 / sqrt((double)d.hidden))));
+  if (attn) {
+    a.n_attn = attn->n_layers;
+    a.attn_Hq = attn->Hq;
+    a.attn_Hkv = attn->Hkv;
+    a.attn_gqa = attn->Hq / attn->Hkv;
+    a.attn_cap = attn->cap;
+    a.attn_chunk = ap.chunk;
+    for (int g = 0; g < G; ++g) {
+      a.attn_ctx[g] = attn->h_ctx[g];
+      a.attn_nsplit[g] = ap.nsplit[g];
+    }
+    for (int g = 0; g <= kMaxAgents; ++g) a.attn_item0[g] = g <= G ? ap.item0[g] : ap.item0[G];
+    a.attn_qscale = (float)(1.4426950408889634 / sqrt(128.0));  // log2(e) / sqrt(d)
+    a.attn_q = attn->q;
+    a.attn_gate = attn->gate;
+    a.attn_k = attn->k_cache;
+    a.attn_v = attn->v_cache;
+    a.attn_o = attn->o;
+    a.attn_part = (float*)(w8 + y.total);
+    a.attn_ticket = (unsigned*)(w8 + y.total + ap.part_bytes);
+  }
   void* args[] = {&a};
   if (st->ev[0]) hipEventRecord(st->ev[0], s);
   hipError_t e = hipLaunchCooperativeKernel((const void*)step_kernel(T), dim3(y.grid), dim3(kBlock), args, 0, s);

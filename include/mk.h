@@ -373,6 +373,41 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
                    const float* gdn_g, const float* gdn_beta, float* gdn_o, int32_t* h_tokens, int32_t* h_n_acc,
                    int32_t* d_argmax, float* trace, void* ws, size_t ws_bytes, void* stream);
 
+/* The same step with the full-attention layers' attention in the persistent
+ * launch (richland.au single-stream article, "What shipped": 16 full gated
+ * attention layers beside 48 Gated DeltaNet layers, decoded by split-K flash
+ * decoding; the 4-agent article, "Why it matters": what grows with the
+ * agents is attention, each agent reading its own KV cache).  Like the
+ * Gated DeltaNet steps, the attention runs on the caller's seeded inputs
+ * beside the layer pipeline (its output is not fed back), so that its
+ * reads and time are part of the step.  For each of n_layers layers and each
+ * agent g (the verify groups of h_group_start), the result is that of
+ * mk_attn_decode on that layer's q, gate and caches:
+ *   q, gate, o   [n_layers][T][Hq][128] fp32 (gate may be NULL)
+ *   k_cache      [n_layers][G][Hkv][cap][128] fp16 bits, position-major
+ *   v_cache      [n_layers][G][Hkv][128][cap] fp16 bits, dimension-major
+ *   h_ctx        host [G]: positions cached before this step's rows; the
+ *                agent's n_g new rows are at h_ctx[g] .. h_ctx[g] + n_g - 1
+ * cap % 64 == 0, h_ctx[g] + n_g <= cap, n_g * Hq/Hkv <= 16 (MK_ERR_SHAPE /
+ * MK_ERR_RANGE otherwise).  attn == NULL is mk_decode_step.  The workspace
+ * (mk_decode_step_attn_workspace) adds the split partials to the step's. */
+typedef struct {
+  int32_t n_layers, Hq, Hkv, cap;
+  const int32_t* h_ctx;
+  const float* q;
+  const float* gate;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  float* o;
+} mk_step_attn;
+size_t mk_decode_step_attn_workspace(const mk_stack* st, int32_t T, const int32_t* h_group_start, int32_t G,
+                                     const mk_step_attn* attn);
+int mk_decode_step_attn(mk_stack* st, float* x, int32_t T, const int32_t* h_group_start, int32_t G,
+                        const int32_t* drafts, const float* gdn_q, const float* gdn_k, const float* gdn_v,
+                        const float* gdn_g, const float* gdn_beta, float* gdn_o, int32_t* h_tokens, int32_t* h_n_acc,
+                        int32_t* d_argmax, float* trace, const mk_step_attn* attn, void* ws, size_t ws_bytes,
+                        void* stream);
+
 /* Duration in ms of the last mk_decode_step's persistent launch on this
  * stack, from HIP events recorded around the launch on its stream (-1 if
  * unavailable). */

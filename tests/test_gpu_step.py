@@ -317,3 +317,47 @@ def test_decode_step_prompt_chunk_is_bit_identical(gs_ride, rows):
     assert np.array_equal(am_r[r0:r1], am_a)
     assert np.array_equal(go_r[r0:r1], go_a)
     assert np.array_equal(S_r, S_a)
+
+
+@pytest.mark.parametrize("ctx,cap,n_layers", [([0, 100, 517, 1000], 1024, 2), ([32768, 32768, 30000, 12345], 32832, 1)])
+def test_decode_step_attention_beside_the_pipeline(ctx, cap, n_layers):
+    """The full-attention layers' split-K flash decoding inside the persistent
+    step (four agents of three rows, 32 query and 8 KV heads of 128, gated,
+    fp16 caches whose unused slots hold NaN): every layer's output equals the
+    oracle's attention on that layer's inputs, and the rest of the step is
+    bit-identical to the same step without attention."""
+    torch = need_gpu()
+    mk = _mk()
+    from synth import recipes
+    L, H, P, F, V = 4, 512, 1024, 768, 1000
+    gs = [0, 3, 6, 9, 12]
+    T, G = 12, 4
+    layers_in = [recipes.attn_inputs(ctx, [3] * G, cap=cap, layer=i) for i in range(n_layers)]
+    q = to_dev(np.stack([a["q"] for a in layers_in]))
+    gate = to_dev(np.stack([a["gate"] for a in layers_in]))
+    kc = to_dev(np.stack([a["k"] for a in layers_in]))
+    vc = to_dev(np.stack([a["v"] for a in layers_in]))
+    o = torch.full((n_layers, T, 32, 128), float("nan"), dtype=torch.float32, device="cuda")
+    runs = {}
+    for name in ("plain", "attn"):
+        st, _, fields, W16, S0, nh = small_stack(mk, 61, L, H, P, F, V, G, T_max=3)
+        x = synth.normal_f32(61, 10000, 0, T * H).reshape(T, H)
+        inp = synth.gdn_step_inputs(61, 20000, T, nh, 128, 128)
+        gin = {k: to_dev(inp[k]) for k in ("q", "k", "v", "g", "beta")}
+        go = torch.empty(T, nh, 128, dtype=torch.float32, device="cuda")
+        tr = torch.empty(L, T, H, dtype=torch.float32, device="cuda")
+        drafts = to_dev(np.arange(1, T - G + 1, dtype=np.int32))
+        at = mk.step_attn(q, kc, vc, o, ctx, gate=gate) if name == "attn" else None
+        say("decode with attention", name, ctx)
+        tok, na = mk.mk_decode_step(st, to_dev(x), gs, drafts, gdn=gin, gdn_o=go, trace=tr, attn=at)
+        mk.mk_deltanet_commit(st.agents[0])
+        runs[name] = (tok, na, to_np(tr), to_np(go), to_np(st.agents[0].S))
+        del st
+    for a, b in zip(runs["plain"], runs["attn"]):
+        assert np.array_equal(a, b)
+    og = to_np(o)
+    for i, a in enumerate(layers_in):
+        ref = oracle.attn_decode(a["q"], a["gate"], a["k"], a["v"], a["ctx"], a["group_start"])
+        e = rel_err(og[i], ref)
+        say("attention layer", i, "err", e)
+        assert e <= FP32_TOL, (i, e)
