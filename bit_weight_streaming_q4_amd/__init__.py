@@ -21,6 +21,7 @@ MK_ERR_WORKSPACE, MK_ERR_LAUNCH, MK_ERR_COOP, MK_ERR_DEVICE = -5, -6, -7, -8
 MK_PATH_AUTO, MK_PATH_DOT4, MK_PATH_MFMA, MK_PATH_STEP = 0, 1, 2, 3
 MK_T_MAX = 16
 MK_STEP_T_MAX = 24
+MK_ATTN_CAP_MAX = 1 << 26
 
 
 class MkError(RuntimeError):

@@ -678,6 +678,7 @@ static int check_attn(int32_t T, int32_t Hq, int32_t Hkv, int32_t d, int32_t cap
   if (d != 128) return fail(MK_ERR_SHAPE, "attention: d = %d (128 required)", d);
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv) return fail(MK_ERR_SHAPE, "attention: Hq = %d, Hkv = %d", Hq, Hkv);
   if (cap <= 0 || cap % 64) return fail(MK_ERR_SHAPE, "attention: cap = %d is not a positive multiple of 64", cap);
+  if (cap > MK_ATTN_CAP_MAX) return fail(MK_ERR_RANGE, "attention: cap = %d > %d", cap, MK_ATTN_CAP_MAX);
   if (!h_ctx) return fail(MK_ERR_ARG, "attention: h_ctx is null");
   if (G > MK_ATTN_MAX_G) return fail(MK_ERR_RANGE, "attention: G = %d > %d", G, MK_ATTN_MAX_G);
   if ((r = check_groups(h_group_start, G, T, gs))) return r;
@@ -694,7 +695,7 @@ static int check_attn(int32_t T, int32_t Hq, int32_t Hkv, int32_t d, int32_t cap
 size_t mk_attn_decode_workspace(int32_t T, int32_t Hq, int32_t Hkv, const int32_t* h_ctx,
                                 const int32_t* h_group_start, int32_t G) {
   std::vector<int32_t> gs;
-  if (check_attn(T, Hq, Hkv, 128, 1 << 30, h_ctx, h_group_start, G, gs)) return 0;
+  if (check_attn(T, Hq, Hkv, 128, MK_ATTN_CAP_MAX, h_ctx, h_group_start, G, gs)) return 0;
   // the larger of the two cache formats' plans, so one size serves both
   const mk::AttnPlan p16 = mk::plan_attn(G, h_ctx, gs.data(), Hkv, device_cu_count(), false);
   const mk::AttnPlan p8 = mk::plan_attn(G, h_ctx, gs.data(), Hkv, device_cu_count(), true);

@@ -95,36 +95,53 @@ __device__ __forceinline__ u4 zero_tail(u4 r, int t0, int hh, int grp, int Lg) {
 }
 
 // Loads tile t0 (a multiple of 64 below L_g <= cap, cap % 64 == 0, so every
-// load stays inside the head's cache rows).
+// load stays inside the head's cache rows).  Each load is a wave-uniform base
+// (the tile, the row block, the dimension block) plus one 32-bit byte offset
+// per lane, so that the tile's 32 loads share two lane offsets instead of
+// holding a 64-bit address each.
 template <bool Q8>
 __device__ __forceinline__ void load_tile(const KVHead& c, int t0, int Lg, int col, int grp, KVTile& x) {
+  // lane offsets: K row 8 (col / 4) + col % 4 of the row block, dims 8 grp..;
+  // V row (dimension) col of the dimension block, positions 8 grp..
+  const uint32_t krow = 8 * (col >> 2) + (col & 3);
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    const int pos = t0 + 32 * (b >> 1) + 8 * (col >> 2) + 4 * (b & 1) + (col & 3);
+    const int r0 = t0 + 32 * (b >> 1) + 4 * (b & 1);  // the row block's first position (uniform)
     if constexpr (Q8) {
-      const uint2* src = (const uint2*)(c.K8 + (size_t)pos * kD + 8 * grp);
+      const char* kb = (const char*)(c.K8 + (size_t)r0 * kD);
+      const uint32_t kl = krow * kD + 8 * grp;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) x.k8[b][m] = src[4 * m];
-      const u4* ss = (const u4*)(c.KS + (size_t)(t0 + 32 * (b >> 1) + 8 * grp + 4 * (b & 1)) * (kD / 32));
-      x.ksc[b][0] = ss[0];
-      x.ksc[b][1] = ss[1];
+      for (int m = 0; m < 4; ++m) x.k8[b][m] = *(const uint2*)(kb + kl + 32 * m);
+      const char* sb = (const char*)(c.KS + (size_t)r0 * (kD / 32));
+      const uint32_t sl = 8 * grp * (kD / 32) * 2;
+      x.ksc[b][0] = *(const u4*)(sb + sl);
+      x.ksc[b][1] = *(const u4*)(sb + sl + 16);
     } else {
-      const u4* src = (const u4*)(c.K + (size_t)pos * kD + 8 * grp);
+      const char* kb = (const char*)(c.K + (size_t)r0 * kD);
+      const uint32_t kl = (krow * kD + 8 * grp) * 2;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) x.kr[b][m] = src[4 * m];
+      for (int m = 0; m < 4; ++m) x.kr[b][m] = *(const u4*)(kb + kl + 64 * m);
     }
   }
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
+  for (int db = 0; db < 8; ++db) {
+    if constexpr (Q8) {
+      const char* vb = (const char*)(c.V8 + ((size_t)(t0 >> 6) * kD + 16 * db) * kTile);
+      const uint32_t vl = col * kTile + 8 * grp;
+      const char* sb = (const char*)(c.VS + (size_t)(t0 >> 5) * kD + 16 * db);
+      const uint32_t sl = 8 * grp;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      if constexpr (Q8) {
-        x.v8[hh][db] = *(const uint2*)(c.V8 + ((size_t)(t0 >> 6) * kD + 16 * db + col) * kTile + 32 * hh + 8 * grp);
-        x.vsc[hh][db] = *(const uint2*)(c.VS + (size_t)((t0 >> 5) + hh) * kD + 16 * db + 4 * grp);
-      } else {
-        x.vr[hh][db] = *(const u4*)(c.V + (size_t)(16 * db + col) * c.cap + t0 + 32 * hh + 8 * grp);
+      for (int hh = 0; hh < 2; ++hh) {
+        x.v8[hh][db] = *(const uint2*)(vb + vl + 32 * hh);
+        x.vsc[hh][db] = *(const uint2*)(sb + sl + hh * kD * 2);
       }
+    } else {
+      const char* vb = (const char*)(c.V + (size_t)16 * db * c.cap + t0);
+      const uint32_t vl = ((uint32_t)col * (uint32_t)c.cap + 8 * grp) * 2;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) x.vr[hh][db] = *(const u4*)(vb + vl + 64 * hh);
     }
+  }
   if constexpr (!Q8) {
     if (t0 + kTile > Lg) {
 #pragma unroll

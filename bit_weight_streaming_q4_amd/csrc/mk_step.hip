@@ -2441,6 +2441,7 @@ int attn_check(const mk_step_attn* at, int T, const std::vector<int>& gs, int G,
   if (!at || at->n_layers < 1) return sfail(MK_ERR_ARG, "attention: no layers");
   if (at->Hq < 1 || at->Hkv < 1 || at->Hq % at->Hkv) return sfail(MK_ERR_SHAPE, "attention: Hq must be a multiple of Hkv");
   if (at->cap <= 0 || at->cap % 64) return sfail(MK_ERR_SHAPE, "attention: cap must be a positive multiple of 64");
+  if (at->cap > MK_ATTN_CAP_MAX) return sfail(MK_ERR_RANGE, "attention: cap above MK_ATTN_CAP_MAX");
   if (G > kMaxAgents) return sfail(MK_ERR_RANGE, "attention: at most 16 agents");
   if (!at->h_ctx || !at->q || !at->k_cache || !at->v_cache || !at->o) return sfail(MK_ERR_ARG, "attention: null pointer");
   const void* ptrs[5] = {at->q, at->gate, at->k_cache, at->v_cache, at->o};

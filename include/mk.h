@@ -60,6 +60,9 @@ enum {
 
 #define MK_T_MAX 16
 #define MK_STEP_T_MAX 24 /* rows of one decode step: up to 8 agents x 3 rows */
+/* Largest KV cache capacity (positions per agent and KV head) of the
+ * attention calls: the kernels address a head's cache with 32-bit byte offsets. */
+#define MK_ATTN_CAP_MAX (1 << 26)
 
 const char* mk_status_string(int status);
 const char* mk_last_error(void);
@@ -388,7 +391,7 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
  *   v_cache      [n_layers][G][Hkv][128][cap] fp16 bits, dimension-major
  *   h_ctx        host [G]: positions cached before this step's rows; the
  *                agent's n_g new rows are at h_ctx[g] .. h_ctx[g] + n_g - 1
- * cap % 64 == 0, h_ctx[g] + n_g <= cap, n_g * Hq/Hkv <= 16 (MK_ERR_SHAPE /
+ * cap % 64 == 0, cap <= MK_ATTN_CAP_MAX, h_ctx[g] + n_g <= cap, n_g * Hq/Hkv <= 16 (MK_ERR_SHAPE /
  * MK_ERR_RANGE otherwise).  attn == NULL is mk_decode_step.  The workspace
  * (mk_decode_step_attn_workspace) adds the split partials to the step's. */
 typedef struct {
@@ -438,7 +441,7 @@ int mk_decode_step_stamps(const mk_stack* st, int32_t T, const void* ws, uint64_
  *   k_cache     [G][Hkv][cap][d] fp16 bits (device), position-major
  *   v_cache     [G][Hkv][d][cap] fp16 bits (device), dimension-major
  *   h_ctx [G], h_group_start [G+1] (host; NULL = one group of T rows)
- * d = 128; cap % 64 == 0; h_ctx[g] + n_g <= cap; n_g * Hq/Hkv <= 64;
+ * d = 128; cap % 64 == 0; cap <= MK_ATTN_CAP_MAX; h_ctx[g] + n_g <= cap; n_g * Hq/Hkv <= 64;
  * G <= 16.  Slots past an agent's last position are never used (they may
  * hold anything).  Two launches (split pass, merge + gate); the workspace
  * size depends on the contexts and the device (mk_attn_decode_workspace).

@@ -165,6 +165,7 @@ def test_attention_validation_and_workspace_on_the_host():
 
     assert call(d=64) == mk.MK_ERR_SHAPE
     assert call(cap=100) == mk.MK_ERR_SHAPE
+    assert call(cap=mk.MK_ATTN_CAP_MAX + 64) == mk.MK_ERR_RANGE
     assert call(Hkv=3) == mk.MK_ERR_SHAPE
     assert call(T=17, gs_=np.array([0, 3, 17], np.int32)) == mk.MK_ERR_RANGE
     assert call(ctx_=np.array([126, 7], np.int32)) == mk.MK_ERR_RANGE          # 126 + 3 > cap
