@@ -319,20 +319,24 @@ def test_decode_step_prompt_chunk_is_bit_identical(gs_ride, rows):
     assert np.array_equal(S_r, S_a)
 
 
-@pytest.mark.parametrize("ctx,cap,n_layers", [([0, 100, 517, 1000], 1024, 2), ([32768, 32768, 30000, 12345], 32832, 1)])
-def test_decode_step_attention_beside_the_pipeline(ctx, cap, n_layers):
+@pytest.mark.parametrize("ctx,sizes,cap,n_layers", [([0, 100, 517, 1000], [3, 3, 3, 3], 1024, 2),
+                                                    ([0, 64, 200, 4999], [1, 4, 3, 4], 5056, 1),
+                                                    ([32768, 32768, 30000, 12345], [3, 3, 3, 3], 32832, 1)])
+def test_decode_step_attention_beside_the_pipeline(ctx, sizes, cap, n_layers):
     """The full-attention layers' split-K flash decoding inside the persistent
-    step (four agents of three rows, 32 query and 8 KV heads of 128, gated,
-    fp16 caches whose unused slots hold NaN): every layer's output equals the
-    oracle's attention on that layer's inputs, and the rest of the step is
-    bit-identical to the same step without attention."""
+    step (four agents of 12 rows in all, 32 query and 8 KV heads of 128,
+    gated, fp16 caches whose unused slots hold NaN; an agent with no cached
+    position and one row; ragged groups of 1 to 4 rows): every layer's output
+    equals the oracle's attention on that layer's inputs, and the rest of the
+    step is bit-identical to the same step without attention."""
     torch = need_gpu()
     mk = _mk()
     from synth import recipes
     L, H, P, F, V = 4, 512, 1024, 768, 1000
-    gs = [0, 3, 6, 9, 12]
+    gs = [0] + list(np.cumsum(sizes))
     T, G = 12, 4
-    layers_in = [recipes.attn_inputs(ctx, [3] * G, cap=cap, layer=i) for i in range(n_layers)]
+    assert gs[-1] == T
+    layers_in = [recipes.attn_inputs(ctx, sizes, cap=cap, layer=i) for i in range(n_layers)]
     q = to_dev(np.stack([a["q"] for a in layers_in]))
     gate = to_dev(np.stack([a["gate"] for a in layers_in]))
     kc = to_dev(np.stack([a["k"] for a in layers_in]))
@@ -340,7 +344,7 @@ def test_decode_step_attention_beside_the_pipeline(ctx, cap, n_layers):
     o = torch.full((n_layers, T, 32, 128), float("nan"), dtype=torch.float32, device="cuda")
     runs = {}
     for name in ("plain", "attn"):
-        st, _, fields, W16, S0, nh = small_stack(mk, 61, L, H, P, F, V, G, T_max=3)
+        st, _, fields, W16, S0, nh = small_stack(mk, 61, L, H, P, F, V, G, T_max=max(sizes))
         x = synth.normal_f32(61, 10000, 0, T * H).reshape(T, H)
         inp = synth.gdn_step_inputs(61, 20000, T, nh, 128, 128)
         gin = {k: to_dev(inp[k]) for k in ("q", "k", "v", "g", "beta")}
