@@ -131,9 +131,49 @@ mk::QActBuf carve_qact(uint8_t*& p, int T, int K) {
   return q;
 }
 
+// The automatic choice follows the measured 5120 x 5120 crossover: the dot4
+// launches up to kDot4MaxTAuto rows, the streaming engines above.
 int pick_path(int path, int T) {
-  if (path == MK_PATH_DOT4 || path == MK_PATH_MFMA) return path;
-  return T <= mk::kDot4MaxTAuto ? MK_PATH_DOT4 : MK_PATH_MFMA;
+  if (path != MK_PATH_AUTO) return path;
+  return T <= mk::kDot4MaxTAuto ? MK_PATH_DOT4 : MK_PATH_STEP;
+}
+
+// The FFN on the dot4 GEMV launches (fewer than kFfnStreamMinT rows): x's
+// activation rows, tile counters (gate/up, then down), the gate/up partials,
+// h's activation rows (written by the gate/up tile epilogues), the down
+// partials.
+size_t ffn_std_workspace(int T, int H, int F) {
+  const int cu = device_cu_count();
+  const mk::GemvPlan pg = mk::plan_gemv(T, F, H, 2, cu);
+  const mk::GemvPlan pd = mk::plan_gemv(T, H, F, 1, cu);
+  return qact_bytes(T, H) + align256((size_t)(pg.ntiles + pd.ntiles) * 4) + align256(pg.partial_elems * 4) +
+         qact_bytes(T, F) + align256(pd.partial_elems * 4);
+}
+
+int ffn_std(const mk_q4k* gate, const mk_q4k* up, const mk_q4k* down, const float* x, int T, float* y, float* h_out,
+            void* ws, void* stream) {
+  const int H = gate->n_in, F = gate->n_out;
+  const int cu = device_cu_count();
+  const mk::GemvPlan pg = mk::plan_gemv(T, F, H, 2, cu);
+  const mk::GemvPlan pd = mk::plan_gemv(T, H, F, 1, cu);
+  uint8_t* wp = (uint8_t*)ws;
+  const mk::QActBuf ax = carve_qact(wp, T, H);
+  unsigned* tickets = (unsigned*)wp;
+  wp += align256((size_t)(pg.ntiles + pd.ntiles) * 4);
+  float* part_gu = (float*)wp;
+  wp += align256(pg.partial_elems * 4);
+  const mk::QActBuf ah = carve_qact(wp, T, F);
+  float* part_d = (float*)wp;
+  const int eng = MK_PATH_DOT4;
+  hipStream_t st = S(stream);
+  hipError_t e = mk::launch_quantize(x, T, H, ax.a8, nullptr, nullptr, ax.ssg, tickets, pg.ntiles + pd.ntiles, st);
+  if (e != hipSuccess) return launch_status(e, "quantize x");
+  const uint8_t* wgu[2] = {(const uint8_t*)gate->blocks, (const uint8_t*)up->blocks};
+  const mk::GemvEpi eg = {tickets, mk::kEpiSiluQ8, F, h_out, ah.a8, ah.ssg};
+  if ((e = mk::launch_gemv(wgu, pg, ax, eng, part_gu, eg, st)) != hipSuccess) return launch_status(e, "gate/up");
+  const uint8_t* wd[2] = {(const uint8_t*)down->blocks, nullptr};
+  const mk::GemvEpi ed = {tickets + pg.ntiles, mk::kEpiStore, H, y, nullptr, nullptr};
+  return launch_status(mk::launch_gemv(wd, pd, ah, eng, part_d, ed, st), "down");
 }
 
 }  // namespace
@@ -270,7 +310,7 @@ size_t mk_qgemv_rows_workspace(int32_t T, int32_t n_out, int32_t n_in) {
   if (T < 1 || T > MK_T_MAX || n_out <= 0 || n_in <= 0 || n_in % 256) return 0;
   const mk::GemvPlan p = mk::plan_gemv(T, n_out, n_in, 1, device_cu_count());
   const size_t std_path = qact_bytes(T, n_in) + align256((size_t)p.ntiles * 4) + align256(p.partial_elems * 4);
-  const size_t step_path = mk::engine_gemv_workspace(T, n_out, n_in);
+  const size_t step_path = mk::engine_gemv_workspace(T, n_out, n_in, device_cu_count());
   return std_path > step_path ? std_path : step_path;
 }
 
@@ -280,15 +320,15 @@ int mk_qgemv_rows_ex(const mk_q4k* W, const float* x, int32_t T, float* y, int32
   if ((r = check_q4k(W, "W")) || (r = check_T(T)) || (r = check_ptr(x, "x")) || (r = check_ptr(y, "y")))
     return r;
   if (path < MK_PATH_AUTO || path > MK_PATH_STEP) return fail(MK_ERR_ARG, "unknown path %d", path);
-  if (path == MK_PATH_STEP) {
+  const int eng = pick_path(path, T);
+  if (eng == MK_PATH_STEP) {
     const size_t need = mk_qgemv_rows_workspace(T, W->n_out, W->n_in);
     if (!ws || ws_bytes < need) return fail(MK_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
     if ((r = check_ptr(ws, "workspace", 256))) return r;
     return launch_status(mk::launch_engine_gemv((const uint8_t*)W->blocks, W->n_out, W->n_in, x, T, y, (uint8_t*)ws,
-                                                 S(stream)),
+                                                 device_cu_count(), S(stream)),
                          "step-engine gemv");
   }
-  const int eng = pick_path(path, T);
   if (eng == MK_PATH_DOT4 && T > mk::kDot4MaxT)
     return fail(MK_ERR_RANGE, "dot4 path supports T <= %d (T = %d)", mk::kDot4MaxT, T);
   const size_t need = mk_qgemv_rows_workspace(T, W->n_out, W->n_in);
@@ -324,16 +364,12 @@ int mk_qgemv_rows_noalloc(const mk_q4k* W, const float* x, int32_t T, float* y, 
 }
 
 // ------------------------------------------------------------------ FFN
-// Workspace: x's activation rows, tile counters (gate/up, then down), the
-// gate/up partials, h's activation rows (written by the gate/up tile
-// epilogues), the down partials.
+// From kFfnStreamMinT rows the streaming engines (mk_step.hip; workspace:
+// x's and h's records, the tickets of both stages, the gate/up and down
+// partials), below them the dot4 launches (ffn_std).
 size_t mk_ffn_rows_workspace(int32_t T, int32_t H, int32_t F) {
   if (T < 1 || T > MK_T_MAX || H <= 0 || F <= 0 || H % 256 || F % 256) return 0;
-  const int cu = device_cu_count();
-  const mk::GemvPlan pg = mk::plan_gemv(T, F, H, 2, cu);
-  const mk::GemvPlan pd = mk::plan_gemv(T, H, F, 1, cu);
-  return qact_bytes(T, H) + align256((size_t)(pg.ntiles + pd.ntiles) * 4) + align256(pg.partial_elems * 4) +
-         qact_bytes(T, F) + align256(pd.partial_elems * 4);
+  return T < mk::kFfnStreamMinT ? ffn_std_workspace(T, H, F) : mk::engine_ffn_workspace(T, H, F, device_cu_count());
 }
 
 int mk_ffn_rows(const mk_q4k* gate, const mk_q4k* up, const mk_q4k* down, const float* x, int32_t T, float* y,
@@ -350,27 +386,11 @@ int mk_ffn_rows(const mk_q4k* gate, const mk_q4k* up, const mk_q4k* down, const 
   const size_t need = mk_ffn_rows_workspace(T, H, F);
   if (!ws || ws_bytes < need) return fail(MK_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   if ((r = check_ptr(ws, "workspace", 256))) return r;
-  const int cu = device_cu_count();
-  const mk::GemvPlan pg = mk::plan_gemv(T, F, H, 2, cu);
-  const mk::GemvPlan pd = mk::plan_gemv(T, H, F, 1, cu);
-  uint8_t* wp = (uint8_t*)ws;
-  const mk::QActBuf ax = carve_qact(wp, T, H);
-  unsigned* tickets = (unsigned*)wp;
-  wp += align256((size_t)(pg.ntiles + pd.ntiles) * 4);
-  float* part_gu = (float*)wp;
-  wp += align256(pg.partial_elems * 4);
-  const mk::QActBuf ah = carve_qact(wp, T, F);
-  float* part_d = (float*)wp;
-  const int eng = pick_path(MK_PATH_AUTO, T);
-  hipStream_t st = S(stream);
-  hipError_t e = mk::launch_quantize(x, T, H, ax.a8, nullptr, nullptr, ax.ssg, tickets, pg.ntiles + pd.ntiles, st);
-  if (e != hipSuccess) return launch_status(e, "quantize x");
-  const uint8_t* wgu[2] = {(const uint8_t*)gate->blocks, (const uint8_t*)up->blocks};
-  const mk::GemvEpi eg = {tickets, mk::kEpiSiluQ8, F, h_out, ah.a8, ah.ssg};
-  if ((e = mk::launch_gemv(wgu, pg, ax, eng, part_gu, eg, st)) != hipSuccess) return launch_status(e, "gate/up");
-  const uint8_t* wd[2] = {(const uint8_t*)down->blocks, nullptr};
-  const mk::GemvEpi ed = {tickets + pg.ntiles, mk::kEpiStore, H, y, nullptr, nullptr};
-  return launch_status(mk::launch_gemv(wd, pd, ah, eng, part_d, ed, st), "down");
+  if (T < mk::kFfnStreamMinT) return ffn_std(gate, up, down, x, T, y, h_out, ws, stream);
+  return launch_status(mk::launch_engine_ffn((const uint8_t*)gate->blocks, (const uint8_t*)up->blocks,
+                                              (const uint8_t*)down->blocks, H, F, x, T, y, h_out, (uint8_t*)ws,
+                                              device_cu_count(), S(stream)),
+                       "ffn");
 }
 
 // ------------------------------------------------------------------ lm_head

@@ -12,7 +12,8 @@ int set_error(int status, const char* fmt, ...);
 constexpr int kTPadHost = 16;         // activation-scale rows padded to 16
 constexpr int kUnitBytesHost = 9216;  // 64 rows x 144 B per superblock
 constexpr int kDot4MaxT = 8;          // dot4 engine instances exist for T = 1..8
-constexpr int kDot4MaxTAuto = 8;      // automatic choice: dot4 up to 8 rows, matrix cores from 9
+constexpr int kDot4MaxTAuto = 4;      // automatic choice: dot4 up to 4 rows, the streaming engines from 5
+constexpr int kFfnStreamMinT = 4;     // mk_ffn_rows: dot4 launches below 4 rows, the streaming engines from 4
 
 struct QActBuf {
   int8_t* a8;    // [T][K]
@@ -30,11 +31,14 @@ struct GemvPlan {
   int ntiles, nsb, per_wg, ksplit, nmat;
   size_t partial_elems;  // nmat * ksplit * T * ntiles*64
 };
-// The step's engines on a plain T-row GEMV (records by the step's epilogue
-// quantizer); workspace: the records, then the split partials.
-size_t engine_gemv_workspace(int T, int N, int K);
-hipError_t launch_engine_gemv(const uint8_t* W, int N, int K, const float* x, int T, float* y, uint8_t* ws,
+// The streaming GEMV and FFN on the step's engines and records (T <= 16);
+// cu: the device's compute units (one block per CU).
+size_t engine_gemv_workspace(int T, int N, int K, int cu);
+hipError_t launch_engine_gemv(const uint8_t* W, int N, int K, const float* x, int T, float* y, uint8_t* ws, int cu,
                               hipStream_t st);
+size_t engine_ffn_workspace(int T, int H, int F, int cu);
+hipError_t launch_engine_ffn(const uint8_t* gate, const uint8_t* up, const uint8_t* down, int H, int F, const float* x,
+                             int T, float* y, float* h_out, uint8_t* ws, int cu, hipStream_t st);
 
 GemvPlan plan_gemv(int T, int n_out, int n_in, int nmat, int cu_count);
 

@@ -615,7 +615,7 @@ __device__ __forceinline__ uint32_t slot_lds(BlockState<T>& s, int c, int k) {
 #define MK_DMA9(C) MK_DMA5(C) MK_DMA_NEXT MK_DMA1(C) MK_DMA_NEXT MK_DMA1(C) MK_DMA_NEXT MK_DMA1(C) MK_DMA_NEXT MK_DMA1(C)
 template <int N, bool COH>
 __device__ __forceinline__ void dma(uint32_t lds, const uint8_t* g) {
-  static_assert((N == 9 && !COH) || ((N == 5 || N == 10) && COH), "instantiated shapes only");
+  static_assert((N == 9 && !COH) || N == 5 || (N == 10 && COH), "instantiated shapes only");
   const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds);
   uint64_t addr = (uint64_t)(uintptr_t)g;
   const uint64_t step = 1024;
@@ -623,6 +623,11 @@ __device__ __forceinline__ void dma(uint32_t lds, const uint8_t* g) {
   // no compiler-placed instruction (or wait) falls between the loads.
   if constexpr (N == 9)
     asm volatile("s_mov_b32 m0, %[m]\n\t" MK_DMA9("")
+                 : [a] "+v"(addr)
+                 : [m] "s"(l0), [k] "s"(step)
+                 : "memory", "m0", "scc");
+  else if constexpr (N == 5 && !COH)
+    asm volatile("s_mov_b32 m0, %[m]\n\t" MK_DMA5("")
                  : [a] "+v"(addr)
                  : [m] "s"(l0), [k] "s"(step)
                  : "memory", "m0", "scc");
@@ -1810,7 +1815,11 @@ __device__ __forceinline__ void watch_wave(const StepArgs& a, BlockState<T>& s, 
 // standalone attention launches (mk_attn.h).
 constexpr int kAttnPartFloats = 16 * 128 + 16 * 2;
 
-__device__ __forceinline__ void attn_item(const StepArgs& a, int i, int j, int lane) {
+__device__ __forceinline__ void attn_item(const StepArgs& a, int i, int j, int lane_in) {
+  // lane-dependent addresses are rebuilt per item: hoisted out of the item
+  // loop they stay live through the tile loop and spill
+  int lane = lane_in;
+  asm volatile("" : "+v"(lane));
   int g = 0;
   while (j >= a.attn_item0[g + 1]) ++g;
   g = uniform(g);
@@ -2095,65 +2104,102 @@ static StepKernel step_kernel(int T) {
 }
 
 // ---------------------------------------------------------------------------
-// The step's engines on a plain T-row GEMV (the MK_PATH_STEP path of
-// mk_qgemv_rows_ex).  The activation records are written by the step's own
-// epilogue quantizer (store_q8) and every unit goes through the engine the
-// step uses for T rows, so that the integer sums of those engines and the
-// record layout can be checked exactly outside the persistent launch.
+// Streaming GEMV: the standalone T-row GEMV and FFN (T <= 16) on the step's
+// engines and activation records (the MK_PATH_STEP path of mk_qgemv_rows_ex,
+// and mk_ffn_rows).  The records are written by the step's own epilogue
+// quantizer (store_q8) and every unit goes through the engine the step uses
+// for T rows, so the integer sums of those engines and the record layout
+// can also be checked exactly outside the persistent launch.
+//
+// A stage's units form a line, tile-major over (tile, matrix) pairs.  Blocks
+// of 4 compute waves and 1 service wave, one block per CU; compute wave gw of
+// Wc takes units [U gw / Wc, U (gw + 1) / Wc) and streams them through a
+// private 2-slot LDS ring (each slot: the unit and the record of its
+// superblock, both by LDS-DMA), so the next unit's loads are in flight during
+// the current unit's arithmetic.  The sums of each (tile, matrix) go to one of
+// the wave's two LDS mailboxes; the service wave adds the block's mailboxes in
+// wave order, stores one partial per (tile, matrix, block) and counts it on
+// the tile's ticket, and the block whose count completes a tile adds the
+// tile's partials in block order and runs the epilogue: y, or SiLU(gate) * up
+// quantized into the next stage's record.  No block waits for another, so
+// the launch needs no co-residency.
 
-// Activation record part of the 64-column tile blockIdx.x of x [T][K].
+// Activation record part of the 64-column tile blockIdx.x of x [T][K]; block
+// 0 also clears the nzero ticket words of the stages that follow.
 template <int T>
-__global__ __launch_bounds__(64) void k_engine_records(const float* __restrict__ x, int K, uint8_t* rec) {
-  __shared__ uint8_t stage[1024 + 256] __attribute__((aligned(16)));
+__global__ __launch_bounds__(64) void k_engine_records(const float* __restrict__ x, int K, uint8_t* rec,
+                                                       unsigned* zero, int nzero) {
+  __shared__ uint8_t stage[kStageBytes] __attribute__((aligned(16)));
   const int lane = threadIdx.x, tau = blockIdx.x;
+  if (tau == 0)
+    for (int i = lane; i < nzero; i += 64) zero[i] = 0u;
   // rows >= TPad stay zero in the stage, as in the step
-  for (int i = lane; i < (1024 + 256) / 4; i += 64) ((int*)stage)[i] = 0;
+  for (int i = lane; i < kStageBytes / 4; i += 64) ((int*)stage)[i] = 0;
   __syncthreads();
   f32x4 v[RG<T>::G];
   load_rows<T>(x, K, tau, lane, v);
   store_q8<T>(rec, tau, lane, v, stage);
 }
 
-// Superblocks [per * blockIdx.y, + per) of 64-row tile blockIdx.x: each unit
-// and its record are copied into an LDS slot and run through the step's
-// engine; the wave's sums go to part[blockIdx.y][t][row].
+struct StreamArgs {
+  const uint8_t* W0;
+  const uint8_t* W1;   // the second matrix of a pair (gate/up), else W0
+  const uint8_t* rec;  // input records [nsb][kActBytes]
+  float* part;         // [(tile, matrix)][cmax][TP][64]
+  unsigned* tickets;   // [ntiles], kTicketStride words apart, zero at launch
+  float* y;            // epi 0: y [T][N]; epi 1: h [T][N] or null
+  uint8_t* rec_out;    // epi 1: the records of h
+  int nsb, ntiles, mshift, U, cmax, N, epi;  // mshift: log2 of the matrices per tile (0 or 1)
+};
+
+constexpr int kStreamThreads = 64 * (kCompute + 1);
+
 template <int T>
-__global__ __launch_bounds__(64) void k_engine_gemv(const uint8_t* __restrict__ W, const uint8_t* __restrict__ rec,
-                                                     int nsb, int N, int per, float* __restrict__ part) {
-  __shared__ uint8_t slot[kSlotBytes] __attribute__((aligned(16)));
-  const int lane = threadIdx.x, tile = blockIdx.x;
-  const int b0 = blockIdx.y * per, b1 = min(nsb, b0 + per);
-  float acc[T];
-  f32x4 macc[4];
-#pragma unroll
-  for (int t = 0; t < T; ++t) acc[t] = 0.0f;
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) macc[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  for (int b = b0; b < b1; ++b) {
-    const uint8_t* u = W + ((size_t)tile * nsb + b) * kUnitBytes;
-    const uint8_t* r = rec + (size_t)b * kActBytes;
-#pragma unroll
-    for (int i = 0; i < kUnitBytes / 1024; ++i)
-      *(u32x4*)(slot + i * 1024 + lane * 16) = *(const u32x4*)(u + i * 1024 + lane * 16);
-#pragma unroll
-    for (int i = 0; i < kActBytes / 1024; ++i)
-      *(u32x4*)(slot + kUnitBytes + i * 1024 + lane * 16) = *(const u32x4*)(r + i * 1024 + lane * 16);
-    __syncthreads();
-    lds_u8* sl = as_lds(slot);
-    if constexpr (!UseMfma<T>::value) {
-      slot_dot4<T>(sl, lane, acc);
-    } else if constexpr (PackMfma<T>::value) {
-      WregP xw;
-      read_w_pk(sl, lane, xw);
-      slot_mfma_pk(xw, sl, lane, macc);
-    } else {
-      WregM xw;
-      read_w_mfma(sl, lane, xw);
-      slot_mfma(xw, sl, lane, macc);
+struct StreamState {
+  uint8_t ring[kCompute][kSlots * kSlotBytes] __attribute__((aligned(16)));
+  float mb[kCompute][2][TPad<T>::value][kMbRow] __attribute__((aligned(16)));  // [t][row of the tile]
+  uint8_t stage[kStageBytes] __attribute__((aligned(16)));
+  int tag[kCompute][2];  // (tile, matrix) + 1 of a full mailbox, 0 when free
+  int abort;
+};
+
+// The part holding unit u when a line of U units is cut into n parts, part p
+// being [U p / n, U (p + 1) / n).
+__device__ __forceinline__ int part_of(long u, int n, long U) { return (int)(((u + 1) * n - 1) / U); }
+
+// Blocks contributing to (tile, matrix) tm, and the first of them.
+__device__ __forceinline__ int stream_first_block(const StreamArgs& a, int tm) {
+  return part_of((long)tm * a.nsb, (int)gridDim.x, a.U);
+}
+__device__ __forceinline__ int stream_blocks(const StreamArgs& a, int tm) {
+  return part_of((long)tm * a.nsb + a.nsb - 1, (int)gridDim.x, a.U) - stream_first_block(a, tm) + 1;
+}
+
+// Starts the weight loads of unit (tm, b) into the slot at LDS address lds,
+// then (separately) the loads of the record of its superblock.
+__device__ __forceinline__ void stream_issue_w(const StreamArgs& a, uint32_t lds, int tm, int b, int lane) {
+  const size_t w0 = opaque((size_t)a.W0), w1 = opaque((size_t)a.W1);
+  const uint8_t* W = (const uint8_t*)((tm & ((1 << a.mshift) - 1)) ? w1 : w0);
+  dma<9, false>(lds, W + ((size_t)(tm >> a.mshift) * a.nsb + b) * kUnitBytes + lane * 16);
+}
+__device__ __forceinline__ void stream_issue_a(const StreamArgs& a, uint32_t lds, int b, int lane) {
+  dma<5, false>(lds + kUnitBytes, a.rec + (size_t)b * kActBytes + lane * 16);
+}
+
+// The wave's sums of (tile, matrix) tm into mailbox nflush % 2, as [t][row].
+template <int T>
+__device__ __forceinline__ void stream_flush(StreamState<T>& s, int c, int lane, int tm, int nflush, float (&acc)[T],
+                                             f32x4 (&macc)[4], bool& ok) {
+  const int slot = nflush & 1;
+  unsigned spins = 0;
+  while (ok && lds_ld(&s.tag[c][slot]) != 0) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > kSpinLimit || lds_ld(&s.abort)) {
+      lds_st(&s.abort, 1);
+      ok = false;
     }
-    __syncthreads();
   }
-  float* out = part + (size_t)blockIdx.y * T * N;
+  if (!ok) return;
   if constexpr (UseMfma<T>::value) {
     if constexpr (PackMfma<T>::value) {
 #pragma unroll
@@ -2161,78 +2207,366 @@ __global__ __launch_bounds__(64) void k_engine_gemv(const uint8_t* __restrict__ 
 #pragma unroll
         for (int i = 0; i < 4; ++i) macc[nb][i] += __shfl_xor(macc[nb][i], 32, 64);
     }
-    // C layout: lane 16 q + n holds rows t = 4q .. 4q + 3 of tile row 16 nb + n
     const int q = lane >> 4, n = lane & 15;
+    if (4 * q < TPad<T>::value)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 4 * q + i, o = tile * 64 + 16 * nb + n;
-        if (t < T && o < N) out[(size_t)t * N + o] = macc[nb][i];
-      }
+        for (int i = 0; i < 4; ++i) s.mb[c][slot][4 * q + i][16 * nb + n] = macc[nb][i];
   } else {
-    const int o = tile * 64 + lane;
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-      if (o < N) out[(size_t)t * N + o] = acc[t];
+    for (int t = 0; t < T; ++t) s.mb[c][slot][t][lane] = acc[t];
   }
-}
-
-// y = the sum of the split partials, in split order.
-__global__ __launch_bounds__(256) void k_engine_sum(const float* __restrict__ part, int nsplit, int n,
-                                                    float* __restrict__ y) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  float v = part[i];
-  for (int sp = 1; sp < nsplit; ++sp) v += part[(size_t)sp * n + i];
-  y[i] = v;
-}
-
-// Superblocks per split: at most 8 splits.
-static int engine_per(int nsb) { return (nsb + 7) / 8; }
-
-size_t engine_gemv_workspace(int T, int N, int K) {
-  const int nsb = K / 256, per = engine_per(nsb), nsplit = (nsb + per - 1) / per;
-  const size_t rec = ((size_t)nsb * kActBytes + 255) & ~(size_t)255;
-  return rec + (size_t)nsplit * T * N * sizeof(float);
+  if (lane == 0) lds_st(&s.tag[c][slot], tm + 1);
 }
 
 template <int T>
-static hipError_t engine_gemv_t(const uint8_t* W, int N, int K, const float* x, float* y, uint8_t* ws,
-                                hipStream_t st) {
-  const int nsb = K / 256, per = engine_per(nsb), nsplit = (nsb + per - 1) / per, ntiles = (N + 63) / 64;
+__device__ __forceinline__ void stream_compute(const StreamArgs& a, StreamState<T>& s, int c, int lane) {
+  const int Wc = (int)gridDim.x * kCompute, gw = (int)blockIdx.x * kCompute + c;
+  const long U = a.U;
+  const int u0 = (int)(U * gw / Wc), u1 = (int)(U * (gw + 1) / Wc);
+  if (u0 >= u1) return;
+  const int nsb = a.nsb;
+  const uint32_t l[2] = {(uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&s.ring[c][0],
+                         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)&s.ring[c][kSlotBytes]};
+  int itm = u0 / nsb, ib = u0 - itm * nsb;  // the next unit to load
+  int ctm = itm;                            // (tile, matrix) of the unit consumed next
+  int cb = ib;
+  stream_issue_w(a, l[0], itm, ib, lane);
+  stream_issue_a(a, l[0], ib, lane);
+  if (++ib == nsb) ib = 0, ++itm;
+  if (u0 + 1 < u1) {
+    stream_issue_w(a, l[1], itm, ib, lane);
+    stream_issue_a(a, l[1], ib, lane);
+    if (++ib == nsb) ib = 0, ++itm;
+  }
+  float acc[T];
+  f32x4 macc[4];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = 0.0f;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) macc[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  int open = ctm, nflush = 0;
+  bool ok = true;
+  for (int u = u0; u < u1 && ok; ++u) {
+    const int k = (u - u0) & 1;
+    // this slot's 14 loads were issued before the other slot's
+    if (u + 1 < u1)
+      wait_ops(14);
+    else
+      wait_ops(0);
+    if (ctm != open) {
+      stream_flush<T>(s, c, lane, open, nflush++, acc, macc, ok);
+      open = ctm;
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[t] = 0.0f;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) macc[nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+    lds_u8* sl = as_lds(&s.ring[c][k * kSlotBytes]);
+    const bool refill = u + 2 < u1;
+    // The matrix-core engines copy the unit's weights into registers and
+    // refill the slot's weight region before their arithmetic (so those loads
+    // have two units' arithmetic to arrive); the record region, which the
+    // arithmetic reads, is refilled after it.  Loads complete in issue order
+    // (weights of u + 2, record of u + 2, weights of u + 3, ...), so waiting
+    // for all but the next unit's 14 loads still means this slot is in.
+    if constexpr (!UseMfma<T>::value) {
+      slot_dot4<T>(sl, lane, acc);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (refill) stream_issue_w(a, l[k], itm, ib, lane);
+    } else if constexpr (PackMfma<T>::value) {
+      WregP xw;
+      read_w_pk(sl, lane, xw);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (refill) stream_issue_w(a, l[k], itm, ib, lane);
+      slot_mfma_pk(xw, sl, lane, macc);
+    } else {
+      WregM xw;
+      read_w_mfma(sl, lane, xw);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (refill) stream_issue_w(a, l[k], itm, ib, lane);
+      slot_mfma(xw, sl, lane, macc);
+    }
+    // every LDS read of the record has completed before it is refilled
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (refill) {
+      stream_issue_a(a, l[k], ib, lane);
+      if (++ib == nsb) ib = 0, ++itm;
+    }
+    if (++cb == nsb) cb = 0, ++ctm;
+  }
+  if (ok) stream_flush<T>(s, c, lane, open, nflush, acc, macc, ok);
+  wait_ops(0);  // no load outlives the wave
+}
+
+// The epilogue of tile tau: its partials added in block order (row-group
+// form: lane 16 tr + cq holds rows tr + 4 k at columns 4 cq .. + 3).
+template <int T>
+__device__ __forceinline__ void stream_epilogue(const StreamArgs& a, StreamState<T>& s, int tau, int lane) {
+  constexpr int TP = TPad<T>::value, G = RG<T>::G;
+  const int tr = lane >> 4, cq = lane & 15;
+  const int nm = 1 << a.mshift;
+  f32x4 v[2][G];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int k = 0; k < G; ++k) v[m][k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < nm; ++m) {
+    const int tm = (tau << a.mshift) + m;
+    const int n = stream_blocks(a, tm);
+    const float* pb = a.part + (size_t)tm * a.cmax * TP * 64;
+    for (int r0 = 0; r0 < n; r0 += 4) {
+      f32x4 t[4][G];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i < n ? r0 + i : n - 1;  // in-range address; extra values are not added
+#pragma unroll
+        for (int k = 0; k < G; ++k) t[i][k] = ld16(pb, ((r * TP + tr + 4 * k) * 64 + cq * 4) * 4);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (r0 + i >= n) break;
+#pragma unroll
+        for (int k = 0; k < G; ++k) {
+          if (m == 0)
+            v[0][k] += t[i][k];
+          else
+            v[1][k] += t[i][k];
+        }
+      }
+    }
+  }
+  // rows >= T of a partial are not results (the dot-product engine leaves them unset)
+#pragma unroll
+  for (int k = 0; k < G; ++k)
+    if (tr + 4 * k >= T) v[0][k] = v[1][k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int col = tau * 64 + cq * 4;
+  if (a.epi == 0) {
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const int t = tr + 4 * k;
+      if (t >= T) continue;
+      if (col + 3 < a.N) {
+        st16(a.y, (t * a.N + col) * 4, v[0][k]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (col + i < a.N) a.y[(size_t)t * a.N + col + i] = v[0][k][i];
+      }
+    }
+    return;
+  }
+  f32x4 h[G];
+#pragma unroll
+  for (int k = 0; k < G; ++k)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float g = v[0][k][i], u = v[1][k][i];
+      h[k][i] = g * u / (1.0f + expf(-g));
+    }
+  if (a.y)
+#pragma unroll
+    for (int k = 0; k < G; ++k)
+      if (tr + 4 * k < T) st16(a.y, ((tr + 4 * k) * a.N + col) * 4, h[k]);
+  store_q8<T>(a.rec_out, tau, lane, h, s.stage);
+}
+
+template <int T>
+__device__ __forceinline__ void stream_service(const StreamArgs& a, StreamState<T>& s, int lane) {
+  constexpr int TP = TPad<T>::value;
+  const int nblk = (int)gridDim.x, Wc = nblk * kCompute, blk = (int)blockIdx.x;
+  const long U = a.U;
+  // every block holds units (the grid has at most U blocks), so every block
+  // between the first and the last of a (tile, matrix) contributes to it
+  const int ub0 = (int)(U * blk / nblk), ub1 = (int)(U * (blk + 1) / nblk);
+  if (ub0 >= ub1) return;
+  const int nsb = a.nsb;
+  const int tr = lane >> 4, cq = lane & 15;
+  for (int tm = ub0 / nsb; tm <= (ub1 - 1) / nsb; ++tm) {
+    // the block's waves holding units of tm (a wave's stretch may be empty
+    // when the line has fewer units than the grid has compute waves)
+    unsigned cmask = 0;
+    for (int c = 0; c < kCompute; ++c) {
+      const long gw = (long)blk * kCompute + c;
+      const long w0 = U * gw / Wc, w1 = U * (gw + 1) / Wc;
+      if (max(w0, (long)tm * nsb) < min(w1, (long)(tm + 1) * nsb)) cmask |= 1u << c;
+    }
+    const int want = tm + 1;
+    uint64_t have = 0;
+    unsigned spins = 0;
+    while (true) {
+      const int tg = lane < 2 * kCompute ? lds_ld(&s.tag[lane >> 1][lane & 1]) : 0;
+      have = __ballot(tg == want);
+      bool all = true;
+      for (int c = 0; c < kCompute; ++c)
+        if ((cmask >> c) & 1u) all = all && ((have >> (2 * c)) & 3ull) != 0;
+      if (all) break;
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit || lds_ld(&s.abort)) {
+        lds_st(&s.abort, 1);
+        return;
+      }
+    }
+    f32x4 v[TP / 4];
+#pragma unroll
+    for (int j = 0; j < TP / 4; ++j) v[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < kCompute; ++c) {
+      if (!((cmask >> c) & 1u)) continue;
+      const int k = ((have >> (2 * c)) & 1ull) ? 0 : 1;
+#pragma unroll
+      for (int j = 0; j < TP / 4; ++j) v[j] += *(const f32x4*)&s.mb[c][k][tr + 4 * j][cq * 4];
+    }
+    for (int c = 0; c < kCompute; ++c) {
+      if (!((cmask >> c) & 1u)) continue;
+      const int k = ((have >> (2 * c)) & 1ull) ? 0 : 1;
+      if (lane == 0) lds_st(&s.tag[c][k], 0);
+    }
+    float* pp = a.part + ((size_t)tm * a.cmax + (blk - stream_first_block(a, tm))) * TP * 64;
+#pragma unroll
+    for (int j = 0; j < TP / 4; ++j) st16(pp, ((tr + 4 * j) * 64 + cq * 4) * 4, v[j]);
+    // count the partial on the tile's ticket; the block completing the tile runs its epilogue
+    const int tau = tm >> a.mshift;
+    int expect = 0;
+    for (int m = 0; m < (1 << a.mshift); ++m) expect += stream_blocks(a, (tau << a.mshift) + m);
+    unsigned old = 0;
+    if (lane == 0) old = ticket_add(a.tickets + (size_t)tau * kTicketStride);  // after the partial's stores
+    old = __shfl(old, 0, 64);
+    if ((int)old == expect - 1) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      stream_epilogue<T>(a, s, tau, lane);
+    }
+  }
+}
+
+template <int T>
+__global__ __launch_bounds__(kStreamThreads) void k_stream(StreamArgs a) {
+  __shared__ StreamState<T> s;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (threadIdx.x < 2 * kCompute) (&s.tag[0][0])[threadIdx.x] = 0;
+  if (threadIdx.x == 0) s.abort = 0;
+  for (int i = threadIdx.x; i < kStageBytes / 4; i += kStreamThreads) ((int*)s.stage)[i] = 0;
+  __syncthreads();
+  if (w < kCompute)
+    stream_compute<T>(a, s, w, lane);
+  else
+    stream_service<T>(a, s, lane);
+}
+
+// The launch shape of one stage: blocks (at most one per CU, at least one
+// unit per compute wave where possible) and the partial slots per (tile,
+// matrix): a (tile, matrix) has nsb consecutive units, so it meets at most
+// floor((nsb - 1) nblk / U) + 2 blocks.
+struct StreamPlan {
+  int nblk, ntiles, nsb, nm, U, cmax;
+};
+
+static StreamPlan stream_plan(int N, int K, int nm, int cu) {
+  StreamPlan p;
+  p.ntiles = (N + 63) / 64;
+  p.nsb = K / 256;
+  p.nm = nm;
+  p.U = p.ntiles * nm * p.nsb;
+  const int c = cu > 0 ? cu : 256;
+  p.nblk = std::max(1, std::min(c, (p.U + kCompute - 1) / kCompute));
+  p.cmax = (int)(((long)(p.nsb - 1) * p.nblk) / p.U) + 2;
+  return p;
+}
+
+static size_t stream_part_bytes(int T, const StreamPlan& p) {
+  return (((size_t)p.ntiles * p.nm * p.cmax * ((T + 3) & ~3) * 64 * 4) + 255) & ~(size_t)255;
+}
+
+static size_t rec_bytes(int K) { return (((size_t)(K / 256) * kActBytes) + 255) & ~(size_t)255; }
+static size_t ticket_bytes(int ntiles) { return (((size_t)ntiles * kTicketStride * 4) + 255) & ~(size_t)255; }
+
+template <int T>
+static void launch_stream_t(const StreamPlan& p, const uint8_t* W0, const uint8_t* W1, const uint8_t* rec, float* part,
+                            unsigned* tickets, int epi, float* y, uint8_t* rec_out, int N, hipStream_t st) {
+  StreamArgs a;
+  a.W0 = W0;
+  a.W1 = W1 ? W1 : W0;
+  a.rec = rec;
+  a.part = part;
+  a.tickets = tickets;
+  a.y = y;
+  a.rec_out = rec_out;
+  a.nsb = p.nsb;
+  a.ntiles = p.ntiles;
+  a.mshift = p.nm == 2 ? 1 : 0;
+  a.U = p.U;
+  a.cmax = p.cmax;
+  a.N = N;
+  a.epi = epi;
+  hipLaunchKernelGGL(k_stream<T>, dim3(p.nblk), dim3(kStreamThreads), 0, st, a);
+}
+
+template <int T>
+static void launch_records_t(const float* x, int K, uint8_t* rec, unsigned* zero, int nzero, hipStream_t st) {
+  hipLaunchKernelGGL(k_engine_records<T>, dim3(K / 64), dim3(64), 0, st, x, K, rec, zero, nzero);
+}
+
+#define MK_T_CASES(F, ...)                  \
+  switch (T) {                              \
+    case 1: F<1>(__VA_ARGS__); break;       \
+    case 2: F<2>(__VA_ARGS__); break;       \
+    case 3: F<3>(__VA_ARGS__); break;       \
+    case 4: F<4>(__VA_ARGS__); break;       \
+    case 5: F<5>(__VA_ARGS__); break;       \
+    case 6: F<6>(__VA_ARGS__); break;       \
+    case 7: F<7>(__VA_ARGS__); break;       \
+    case 8: F<8>(__VA_ARGS__); break;       \
+    case 9: F<9>(__VA_ARGS__); break;       \
+    case 10: F<10>(__VA_ARGS__); break;     \
+    case 11: F<11>(__VA_ARGS__); break;     \
+    case 12: F<12>(__VA_ARGS__); break;     \
+    case 13: F<13>(__VA_ARGS__); break;     \
+    case 14: F<14>(__VA_ARGS__); break;     \
+    case 15: F<15>(__VA_ARGS__); break;     \
+    case 16: F<16>(__VA_ARGS__); break;     \
+    default: return hipErrorInvalidValue;   \
+  }
+
+// Workspace of the GEMV: x's records, the tickets, the partials.
+size_t engine_gemv_workspace(int T, int N, int K, int cu) {
+  const StreamPlan p = stream_plan(N, K, 1, cu);
+  return rec_bytes(K) + ticket_bytes(p.ntiles) + stream_part_bytes(T, p);
+}
+
+hipError_t launch_engine_gemv(const uint8_t* W, int N, int K, const float* x, int T, float* y, uint8_t* ws, int cu,
+                              hipStream_t st) {
+  const StreamPlan p = stream_plan(N, K, 1, cu);
   uint8_t* rec = ws;
-  float* part = (float*)(ws + (((size_t)nsb * kActBytes + 255) & ~(size_t)255));
-  hipLaunchKernelGGL(k_engine_records<T>, dim3(K / 64), dim3(64), 0, st, x, K, rec);
-  hipLaunchKernelGGL(k_engine_gemv<T>, dim3(ntiles, nsplit), dim3(64), 0, st, W, (const uint8_t*)rec, nsb, N, per,
-                     part);
-  const int n = T * N;
-  hipLaunchKernelGGL(k_engine_sum, dim3((n + 255) / 256), dim3(256), 0, st, (const float*)part, nsplit, n, y);
+  unsigned* tk = (unsigned*)(ws + rec_bytes(K));
+  float* part = (float*)(ws + rec_bytes(K) + ticket_bytes(p.ntiles));
+  MK_T_CASES(launch_records_t, x, K, rec, tk, p.ntiles * kTicketStride, st)
+  MK_T_CASES(launch_stream_t, p, W, nullptr, rec, part, tk, 0, y, nullptr, N, st)
   return hipGetLastError();
 }
 
-hipError_t launch_engine_gemv(const uint8_t* W, int N, int K, const float* x, int T, float* y, uint8_t* ws,
-                              hipStream_t st) {
-  switch (T) {
-    case 1: return engine_gemv_t<1>(W, N, K, x, y, ws, st);
-    case 2: return engine_gemv_t<2>(W, N, K, x, y, ws, st);
-    case 3: return engine_gemv_t<3>(W, N, K, x, y, ws, st);
-    case 4: return engine_gemv_t<4>(W, N, K, x, y, ws, st);
-    case 5: return engine_gemv_t<5>(W, N, K, x, y, ws, st);
-    case 6: return engine_gemv_t<6>(W, N, K, x, y, ws, st);
-    case 7: return engine_gemv_t<7>(W, N, K, x, y, ws, st);
-    case 8: return engine_gemv_t<8>(W, N, K, x, y, ws, st);
-    case 9: return engine_gemv_t<9>(W, N, K, x, y, ws, st);
-    case 10: return engine_gemv_t<10>(W, N, K, x, y, ws, st);
-    case 11: return engine_gemv_t<11>(W, N, K, x, y, ws, st);
-    case 12: return engine_gemv_t<12>(W, N, K, x, y, ws, st);
-    case 13: return engine_gemv_t<13>(W, N, K, x, y, ws, st);
-    case 14: return engine_gemv_t<14>(W, N, K, x, y, ws, st);
-    case 15: return engine_gemv_t<15>(W, N, K, x, y, ws, st);
-    case 16: return engine_gemv_t<16>(W, N, K, x, y, ws, st);
-    default: return hipErrorInvalidValue;
-  }
+// Workspace of the FFN: x's records, h's records, the tickets of both stages,
+// the partials of gate/up, then of down.
+size_t engine_ffn_workspace(int T, int H, int F, int cu) {
+  const StreamPlan pg = stream_plan(F, H, 2, cu), pd = stream_plan(H, F, 1, cu);
+  return rec_bytes(H) + rec_bytes(F) + ticket_bytes(pg.ntiles + pd.ntiles) + stream_part_bytes(T, pg) +
+         stream_part_bytes(T, pd);
 }
+
+hipError_t launch_engine_ffn(const uint8_t* gate, const uint8_t* up, const uint8_t* down, int H, int F, const float* x,
+                             int T, float* y, float* h_out, uint8_t* ws, int cu, hipStream_t st) {
+  const StreamPlan pg = stream_plan(F, H, 2, cu), pd = stream_plan(H, F, 1, cu);
+  uint8_t* rx = ws;
+  uint8_t* rh = rx + rec_bytes(H);
+  unsigned* tk = (unsigned*)(rh + rec_bytes(F));
+  unsigned* tkd = tk + (size_t)pg.ntiles * kTicketStride;
+  float* pgu = (float*)((uint8_t*)tk + ticket_bytes(pg.ntiles + pd.ntiles));
+  float* pdn = (float*)((uint8_t*)pgu + stream_part_bytes(T, pg));
+  MK_T_CASES(launch_records_t, x, H, rx, tk, (pg.ntiles + pd.ntiles) * kTicketStride, st)
+  MK_T_CASES(launch_stream_t, pg, gate, up, rx, pgu, tk, 1, h_out, rh, F, st)
+  MK_T_CASES(launch_stream_t, pd, down, nullptr, rh, pdn, tkd, 0, y, nullptr, H, st)
+  return hipGetLastError();
+}
+#undef MK_T_CASES
 
 }  // namespace mk
 

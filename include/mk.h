@@ -124,18 +124,21 @@ size_t mk_qgemv_rows_workspace(int32_t T, int32_t n_out, int32_t n_in);
 int mk_qgemv_rows(const mk_q4k* W, const float* x, int32_t T, float* y, void* ws, size_t ws_bytes, void* stream);
 
 /* Same, with the inner-product engine chosen explicitly:
- * MK_PATH_AUTO (dot4 for T <= 8, matrix cores from T = 9), MK_PATH_DOT4
- * (packed int8 dot products, T <= 8) or MK_PATH_MFMA (int8 matrix cores,
- * rows padded to 16).  Both engines give bit-identical results.
- * MK_PATH_STEP runs the decode step's own engines and activation records on
- * the same GEMV, so that they can be checked outside the persistent launch:
- * the records are written by the step's epilogue quantizer (the rule of
- * mk_quantize_rows) and each 64-row unit goes through the engine the step
- * uses for T rows (dot4 at T = 1; two sub-blocks per 16x16x64 int8 matrix
- * product up to 8 padded rows; one sub-block per 16x16x32 product above).
- * Its results equal the other paths' up to the order of the fp32 sums.  The
- * workspace then begins with the records, one per superblock b of x (5120 B):
- * codes [sub-block j][octet q][row t < 16][8 B] (the 8 codes of elements
+ * MK_PATH_AUTO (MK_PATH_DOT4 for T <= 4, MK_PATH_STEP from T = 5: the
+ * faster one on the 5120 x 5120 workload), MK_PATH_DOT4 (packed int8 dot
+ * products, T <= 8) or MK_PATH_MFMA (int8 matrix cores, rows padded to 16);
+ * those two give bit-identical results.
+ * MK_PATH_STEP streams the matrix through the decode step's own engines and
+ * activation records: the records are written by the step's epilogue
+ * quantizer (the rule of mk_quantize_rows) and each 64-row unit goes through
+ * the engine the step uses for T rows (dot4 at T = 1; two sub-blocks per
+ * 16x16x64 int8 matrix product up to 8 padded rows; one sub-block per
+ * 16x16x32 product above), loaded by LDS-DMA two units ahead of the
+ * arithmetic, one block of 4 streaming waves per CU.  Its results equal the
+ * other paths' up to the order of the fp32 sums, and the step's engines can
+ * be checked through it outside the persistent launch.  The workspace then
+ * begins with the records, one per superblock b of x (5120 B): codes
+ * [sub-block j][octet q][row t < 16][8 B] (the 8 codes of elements
  * 256 b + 32 j + 8 q .. + 7; rows >= T zero), then s [j][t] and s * gsum
  * [j][t] as fp32 ([8][16] each).
  * Launches: the activation quantizer (which also clears the tile counters in
@@ -165,7 +168,9 @@ int mk_qgemv_rows_noalloc(const mk_q4k* W, const float* x, int32_t T, float* y, 
 /* y = W_down . q8(SiLU(W_gate . q8(x)) * (W_up . q8(x))); gate, up are
  * F x H, down is H x F.  x, y [T][H] fp32; h_out (optional, NULL to skip)
  * receives the fp32 intermediate [T][F].  Three launches: quantizer, gate/up
- * (whose tile epilogues apply SiLU(g) * u and quantize h), down. */
+ * (whose tile epilogues apply SiLU(g) * u and quantize h), down; from T = 4
+ * on the engines of MK_PATH_STEP, below on those of MK_PATH_DOT4 (the faster
+ * ones on the 5120 -> 17408 -> 5120 workload). */
 size_t mk_ffn_rows_workspace(int32_t T, int32_t H, int32_t F);
 int mk_ffn_rows(const mk_q4k* gate, const mk_q4k* up, const mk_q4k* down, const float* x, int32_t T, float* y,
                 float* h_out, void* ws, size_t ws_bytes, void* stream);

@@ -29,11 +29,11 @@ def _pair(mk, torch, W, x, path):
     return to_np(y), to_np(y_ref)
 
 
-@pytest.mark.parametrize("path", ["auto", "dot4", "mfma"])
+@pytest.mark.parametrize("path", ["auto", "dot4", "mfma", "step"])
 def test_noalloc_equals_workspace_call_twice(path):
     torch = need_gpu()
     mk = _mk()
-    p = {"auto": mk.MK_PATH_AUTO, "dot4": mk.MK_PATH_DOT4, "mfma": mk.MK_PATH_MFMA}[path]
+    p = {"auto": mk.MK_PATH_AUTO, "dot4": mk.MK_PATH_DOT4, "mfma": mk.MK_PATH_MFMA, "step": mk.MK_PATH_STEP}[path]
     # first call: the model's 5120 x 5120 shape (several tiles); second: a
     # smaller ragged one, so the array holds the first call's leftovers
     for (N, K, T) in ((5120, 5120, 8 if path == "dot4" else 12), (130, 768, 3)):
