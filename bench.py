@@ -35,7 +35,8 @@ PEAK_HBM_GBS = 8000.0
 HIDDEN, PROJ, FFN, VOCAB, LAYERS = 5120, 10240, 17408, 151936, 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode_step_T12.json")
 KERNEL_SOURCES = ["bit_weight_streaming_q4_amd/csrc/mk_step.hip", "bit_weight_streaming_q4_amd/csrc/mk_device.h",
-                  "bit_weight_streaming_q4_amd/csrc/mk_gdn.h", "bit_weight_streaming_q4_amd/csrc/mk_lm.h"]
+                  "bit_weight_streaming_q4_amd/csrc/mk_gdn.h", "bit_weight_streaming_q4_amd/csrc/mk_lm.h",
+                  "bit_weight_streaming_q4_amd/csrc/mk_attn.h"]
 
 
 def log(*a):
@@ -717,6 +718,9 @@ def main():
                     help="write the traffic record from rocprofv3 output under DIR (no GPU work) and exit")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the HBM byte counters)")
+    ap.add_argument("--ffn-calls", type=int, metavar="T", default=0,
+                    help="only make 24 eager mk_ffn_rows calls at T rows on rotating weight copies (for a kernel "
+                         "trace of the FFN's launches)")
     ap.add_argument("--no-attention", action="store_true",
                     help="skip the T = 12 step with the attention layers in the launch")
     ap.add_argument("--no-children", action="store_true",
@@ -734,7 +738,7 @@ def main():
         return
     # every child process starts here, before this process touches the GPU
     one_core = None
-    if not args.copy_probe and not args.no_children:
+    if not args.copy_probe and not args.ffn_calls and not args.no_children:
         host_facts()
         if not args.no_cpu_baseline:
             one_core = cpu_baseline_one_core()
@@ -757,6 +761,21 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_read": src.numel() * 4, "copy_probe_bytes_written": dst.numel() * 4,
                           "launches": 3}), flush=True)
+        return
+    if args.ffn_calls:
+        T = args.ffn_calls
+        fw = recipes.ffn_weights()
+        g0, u0, d0 = (mk.pack_to_device(fw[m], "cuda") for m in ("gate", "up", "down"))
+        del fw
+        sets = [(g0, u0, d0)] + [tuple(mk.Q4K(w.blocks.clone(), w.n_out, w.n_in) for w in (g0, u0, d0))
+                                 for _ in range(3)]
+        x = torch.from_numpy(recipes.rows_f32(T, HIDDEN)).to("cuda")
+        y = torch.empty(T, HIDDEN, dtype=torch.float32, device="cuda")
+        ws = mk.workspace(mk.mk_ffn_rows_workspace(T, HIDDEN, FFN), "cuda")
+        for i in range(24):
+            mk.mk_ffn_rows(*sets[i % 4], x, y, ws=ws)
+        torch.cuda.synchronize()
+        print(json.dumps({"ffn_calls": 24, "rows": T}), flush=True)
         return
     L = args.layers
     gl = recipes.gdn_layers(L)
