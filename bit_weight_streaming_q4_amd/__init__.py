@@ -42,7 +42,9 @@ class mk_deltanet(ctypes.Structure):
 class mk_step_attn(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("cap", ctypes.c_int32),
                 ("h_ctx", ctypes.c_void_p), ("q", ctypes.c_void_p), ("gate", ctypes.c_void_p),
-                ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("o", ctypes.c_void_p)]
+                ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("o", ctypes.c_void_p),
+                ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("v_scales", ctypes.c_void_p)]
 
 
 class mk_mtp(ctypes.Structure):
@@ -466,8 +468,21 @@ def step_attn(q, k_cache, v_cache, o, ctx, gate=None):
     per agent.  The returned structure keeps its arguments alive."""
     ctx = np.ascontiguousarray(ctx, np.int32)
     a = mk_step_attn(int(q.shape[0]), int(q.shape[2]), int(k_cache.shape[2]), int(k_cache.shape[3]), ctx.ctypes.data,
-                     _ptr(q), _ptr(gate), _ptr(k_cache), _ptr(v_cache), _ptr(o))
+                     _ptr(q), _ptr(gate), _ptr(k_cache), _ptr(v_cache), _ptr(o), None, None, None, None)
     a._keep = (ctx, q, gate, k_cache, v_cache, o)
+    return a
+
+
+def step_attn_q8(q, k_codes, k_scales, v_codes, v_scales, o, ctx, gate=None):
+    """The same over a q8_0 cache: k_codes [n_layers][G][Hkv][cap][128] int8,
+    k_scales [n_layers][G][Hkv][cap][4] fp16 bits, v_codes
+    [n_layers][G][Hkv][cap/64][128][64] int8, v_scales
+    [n_layers][G][Hkv][cap/32][128] fp16 bits (device)."""
+    ctx = np.ascontiguousarray(ctx, np.int32)
+    a = mk_step_attn(int(q.shape[0]), int(q.shape[2]), int(k_codes.shape[2]), int(k_codes.shape[3]), ctx.ctypes.data,
+                     _ptr(q), _ptr(gate), None, None, _ptr(o), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
+                     _ptr(v_scales))
+    a._keep = (ctx, q, gate, k_codes, k_scales, v_codes, v_scales, o)
     return a
 
 

@@ -210,8 +210,13 @@ struct StepArgs {
   float attn_qscale;                   // log2(e) / sqrt(128)
   const float* attn_q;                 // [n_attn][T][Hq][128]
   const float* attn_gate;              // [n_attn][T][Hq][128] or null
-  const uint16_t* attn_k;              // [n_attn][G][Hkv][cap][128] fp16
+  const uint16_t* attn_k;              // [n_attn][G][Hkv][cap][128] fp16 (null: q8_0 cache)
   const uint16_t* attn_v;              // [n_attn][G][Hkv][128][cap] fp16
+  const int8_t* attn_k8;               // q8_0: [n_attn][G][Hkv][cap][128] codes
+  const uint16_t* attn_ks;             //       [n_attn][G][Hkv][cap][4] fp16 scales
+  const int8_t* attn_v8;               //       [n_attn][G][Hkv][cap/64][128][64] codes
+  const uint16_t* attn_vs;             //       [n_attn][G][Hkv][cap/32][128] fp16 scales
+  int attn_q8;                         // the cache is q8_0
   float* attn_o;                       // [n_attn][T][Hq][128]
   float* attn_part;                    // per item: [16 columns][128] outputs, then (max, sum) per column
   unsigned* attn_ticket;               // per (layer, agent, KV head): splits finished, 64 B apart
@@ -1815,6 +1820,7 @@ __device__ __forceinline__ void watch_wave(const StepArgs& a, BlockState<T>& s, 
 // standalone attention launches (mk_attn.h).
 constexpr int kAttnPartFloats = 16 * 128 + 16 * 2;
 
+template <bool Q8>
 __device__ __forceinline__ void attn_item(const StepArgs& a, int i, int j, int lane_in) {
   // lane-dependent addresses are rebuilt per item: hoisted out of the item
   // loop they stay live through the tile loop and spill
@@ -1853,16 +1859,23 @@ __device__ __forceinline__ void attn_item(const StepArgs& a, int i, int j, int l
   const size_t gh = ((size_t)i * a.G + g) * a.attn_Hkv + h;
   attn::KVHead kv = {};
   kv.cap = a.attn_cap;
-  kv.K = a.attn_k + gh * kv.cap * 128;
-  kv.V = a.attn_v + gh * 128 * kv.cap;
+  if constexpr (Q8) {
+    kv.K8 = a.attn_k8 + gh * kv.cap * 128;
+    kv.KS = a.attn_ks + gh * kv.cap * 4;
+    kv.V8 = a.attn_v8 + gh * 128 * kv.cap;
+    kv.VS = a.attn_vs + gh * (kv.cap / 32) * 128;
+  } else {
+    kv.K = a.attn_k + gh * kv.cap * 128;
+    kv.V = a.attn_v + gh * 128 * kv.cap;
+  }
   attn::f4 acc[8];
   float mrow = -INFINITY, lsum = 0.f;
 #pragma unroll
   for (int db = 0; db < 8; ++db) acc[db] = attn::f4{0.f, 0.f, 0.f, 0.f};
   for (int t0 = p0; t0 < p1; t0 += attn::kTile) {
     attn::KVTile x;
-    attn::load_tile<false>(kv, t0, Lg, col, grp, x);
-    attn::tile_update<false>(x, t0, Lg, lim, grp, qh, ql, acc, mrow, lsum);
+    attn::load_tile<Q8>(kv, t0, Lg, col, grp, x);
+    attn::tile_update<Q8>(x, t0, Lg, lim, grp, qh, ql, acc, mrow, lsum);
   }
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
@@ -1915,7 +1928,10 @@ __device__ __forceinline__ void attn_items(const StepArgs& a, int lane) {
   if (a.n_attn <= 0) return;
   const int per = uniform(a.attn_item0[a.G]);
   const long total = (long)a.n_attn * per;
-  for (long it = blockIdx.x; it < total; it += gridDim.x) attn_item(a, (int)(it / per), (int)(it % per), lane);
+  if (a.attn_q8)
+    for (long it = blockIdx.x; it < total; it += gridDim.x) attn_item<true>(a, (int)(it / per), (int)(it % per), lane);
+  else
+    for (long it = blockIdx.x; it < total; it += gridDim.x) attn_item<false>(a, (int)(it / per), (int)(it % per), lane);
 }
 
 // The block's share of every GDN layer's half-head jobs, in layer order.
@@ -2777,8 +2793,15 @@ int attn_check(const mk_step_attn* at, int T, const std::vector<int>& gs, int G,
   if (at->cap <= 0 || at->cap % 64) return sfail(MK_ERR_SHAPE, "attention: cap must be a positive multiple of 64");
   if (at->cap > MK_ATTN_CAP_MAX) return sfail(MK_ERR_RANGE, "attention: cap above MK_ATTN_CAP_MAX");
   if (G > kMaxAgents) return sfail(MK_ERR_RANGE, "attention: at most 16 agents");
-  if (!at->h_ctx || !at->q || !at->k_cache || !at->v_cache || !at->o) return sfail(MK_ERR_ARG, "attention: null pointer");
-  const void* ptrs[5] = {at->q, at->gate, at->k_cache, at->v_cache, at->o};
+  if (!at->h_ctx || !at->q || !at->o) return sfail(MK_ERR_ARG, "attention: null pointer");
+  const bool f16 = at->k_cache || at->v_cache;
+  const bool q8 = at->k_codes || at->k_scales || at->v_codes || at->v_scales;
+  if (f16 == q8) return sfail(MK_ERR_ARG, "attention: give either the fp16 or the q8_0 cache");
+  if (f16 && !(at->k_cache && at->v_cache)) return sfail(MK_ERR_ARG, "attention: fp16 cache pointer missing");
+  if (q8 && !(at->k_codes && at->k_scales && at->v_codes && at->v_scales))
+    return sfail(MK_ERR_ARG, "attention: q8_0 cache pointer missing");
+  const void* ptrs[9] = {at->q, at->gate, at->k_cache, at->v_cache, at->o, at->k_codes, at->k_scales, at->v_codes,
+                         at->v_scales};
   for (const void* q : ptrs)
     if ((uintptr_t)q % 16) return sfail(MK_ERR_ALIGN, "attention: a buffer is not 16-B aligned");
   const int gqa = at->Hq / at->Hkv;
@@ -3066,6 +3089,11 @@ int mk_decode_step_attn(mk_stack* st, float* x, int32_t T, const int32_t* h_grou
     a.attn_gate = attn->gate;
     a.attn_k = attn->k_cache;
     a.attn_v = attn->v_cache;
+    a.attn_k8 = attn->k_codes;
+    a.attn_ks = attn->k_scales;
+    a.attn_v8 = attn->v_codes;
+    a.attn_vs = attn->v_scales;
+    a.attn_q8 = attn->k_codes != nullptr;
     a.attn_o = attn->o;
     a.attn_part = (float*)(w8 + y.total);
     a.attn_ticket = (unsigned*)(w8 + y.total + ap.part_bytes);

@@ -392,12 +392,20 @@ int mk_decode_step(mk_stack* st, float* x, int32_t T, const int32_t* h_group_sta
  * agent g (the verify groups of h_group_start), the result is that of
  * mk_attn_decode on that layer's q, gate and caches:
  *   q, gate, o   [n_layers][T][Hq][128] fp32 (gate may be NULL)
- *   k_cache      [n_layers][G][Hkv][cap][128] fp16 bits, position-major
- *   v_cache      [n_layers][G][Hkv][128][cap] fp16 bits, dimension-major
  *   h_ctx        host [G]: positions cached before this step's rows; the
  *                agent's n_g new rows are at h_ctx[g] .. h_ctx[g] + n_g - 1
- * cap % 64 == 0, cap <= MK_ATTN_CAP_MAX, h_ctx[g] + n_g <= cap, n_g * Hq/Hkv <= 16 (MK_ERR_SHAPE /
- * MK_ERR_RANGE otherwise).  attn == NULL is mk_decode_step.  The workspace
+ * and either an fp16 cache (the q8_0 pointers NULL):
+ *   k_cache      [n_layers][G][Hkv][cap][128] fp16 bits, position-major
+ *   v_cache      [n_layers][G][Hkv][128][cap] fp16 bits, dimension-major
+ * or a q8_0 cache (k_cache and v_cache NULL; the layouts of
+ * mk_attn_decode_q8 with a leading layer dimension; the result is that of
+ * mk_attn_decode_q8):
+ *   k_codes [n_layers][G][Hkv][cap][128] int8, k_scales [n_layers][G][Hkv][cap][4],
+ *   v_codes [n_layers][G][Hkv][cap/64][128][64] int8, v_scales [n_layers][G][Hkv][cap/32][128]
+ * All device, 16-B aligned.  cap % 64 == 0, cap <= MK_ATTN_CAP_MAX,
+ * h_ctx[g] + n_g <= cap, n_g * Hq/Hkv <= 16 (MK_ERR_SHAPE / MK_ERR_RANGE
+ * otherwise); neither or both cache formats given is MK_ERR_ARG.
+ * attn == NULL is mk_decode_step.  The workspace
  * (mk_decode_step_attn_workspace) adds the split partials to the step's. */
 typedef struct {
   int32_t n_layers, Hq, Hkv, cap;
@@ -407,6 +415,10 @@ typedef struct {
   const uint16_t* k_cache;
   const uint16_t* v_cache;
   float* o;
+  const int8_t* k_codes;
+  const uint16_t* k_scales;
+  const int8_t* v_codes;
+  const uint16_t* v_scales;
 } mk_step_attn;
 size_t mk_decode_step_attn_workspace(const mk_stack* st, int32_t T, const int32_t* h_group_start, int32_t G,
                                      const mk_step_attn* attn);

@@ -319,16 +319,18 @@ def test_decode_step_prompt_chunk_is_bit_identical(gs_ride, rows):
     assert np.array_equal(S_r, S_a)
 
 
+@pytest.mark.parametrize("fmt", ["f16", "q8"])
 @pytest.mark.parametrize("ctx,sizes,cap,n_layers", [([0, 100, 517, 1000], [3, 3, 3, 3], 1024, 2),
                                                     ([0, 64, 200, 4999], [1, 4, 3, 4], 5056, 1),
                                                     ([32768, 32768, 30000, 12345], [3, 3, 3, 3], 32832, 1)])
-def test_decode_step_attention_beside_the_pipeline(ctx, sizes, cap, n_layers):
+def test_decode_step_attention_beside_the_pipeline(ctx, sizes, cap, n_layers, fmt):
     """The full-attention layers' split-K flash decoding inside the persistent
     step (four agents of 12 rows in all, 32 query and 8 KV heads of 128,
-    gated, fp16 caches whose unused slots hold NaN; an agent with no cached
-    position and one row; ragged groups of 1 to 4 rows): every layer's output
-    equals the oracle's attention on that layer's inputs, and the rest of the
-    step is bit-identical to the same step without attention."""
+    gated; fp16 caches whose unused slots hold NaN, or q8_0 caches whose
+    unused codes are out of range and unused scales NaN; an agent with no
+    cached position and one row; ragged groups of 1 to 4 rows): every layer's
+    output equals the oracle's attention on that layer's inputs, and the rest
+    of the step is bit-identical to the same step without attention."""
     torch = need_gpu()
     mk = _mk()
     from synth import recipes
@@ -336,11 +338,12 @@ def test_decode_step_attention_beside_the_pipeline(ctx, sizes, cap, n_layers):
     gs = [0] + list(np.cumsum(sizes))
     T, G = 12, 4
     assert gs[-1] == T
-    layers_in = [recipes.attn_inputs(ctx, sizes, cap=cap, layer=i) for i in range(n_layers)]
+    gen = recipes.attn_inputs if fmt == "f16" else recipes.attn_inputs_q8
+    layers_in = [gen(ctx, sizes, cap=cap, layer=i) for i in range(n_layers)]
     q = to_dev(np.stack([a["q"] for a in layers_in]))
     gate = to_dev(np.stack([a["gate"] for a in layers_in]))
-    kc = to_dev(np.stack([a["k"] for a in layers_in]))
-    vc = to_dev(np.stack([a["v"] for a in layers_in]))
+    caches = [to_dev(np.stack([a[k] for a in layers_in]))
+              for k in (("k", "v") if fmt == "f16" else ("k8", "ks", "v8", "vs"))]
     o = torch.full((n_layers, T, 32, 128), float("nan"), dtype=torch.float32, device="cuda")
     runs = {}
     for name in ("plain", "attn"):
@@ -351,7 +354,10 @@ def test_decode_step_attention_beside_the_pipeline(ctx, sizes, cap, n_layers):
         go = torch.empty(T, nh, 128, dtype=torch.float32, device="cuda")
         tr = torch.empty(L, T, H, dtype=torch.float32, device="cuda")
         drafts = to_dev(np.arange(1, T - G + 1, dtype=np.int32))
-        at = mk.step_attn(q, kc, vc, o, ctx, gate=gate) if name == "attn" else None
+        at = None
+        if name == "attn":
+            at = mk.step_attn(q, *caches, o, ctx, gate=gate) if fmt == "f16" else \
+                mk.step_attn_q8(q, *caches, o, ctx, gate=gate)
         say("decode with attention", name, ctx)
         tok, na = mk.mk_decode_step(st, to_dev(x), gs, drafts, gdn=gin, gdn_o=go, trace=tr, attn=at)
         mk.mk_deltanet_commit(st.agents[0])
@@ -361,7 +367,37 @@ def test_decode_step_attention_beside_the_pipeline(ctx, sizes, cap, n_layers):
         assert np.array_equal(a, b)
     og = to_np(o)
     for i, a in enumerate(layers_in):
-        ref = oracle.attn_decode(a["q"], a["gate"], a["k"], a["v"], a["ctx"], a["group_start"])
+        if fmt == "f16":
+            ref = oracle.attn_decode(a["q"], a["gate"], a["k"], a["v"], a["ctx"], a["group_start"])
+        else:
+            ref = oracle.attn_decode_q8(a["q"], a["gate"], a["k8"], a["ks"], a["v8"], a["vs"], a["ctx"],
+                                        a["group_start"])
         e = rel_err(og[i], ref)
         say("attention layer", i, "err", e)
         assert e <= FP32_TOL, (i, e)
+
+
+def test_decode_step_attention_cache_format_checks():
+    """mk_step_attn takes exactly one cache format: neither, both, or a
+    partial set of pointers gives no workspace (the call fails with
+    MK_ERR_ARG); a misaligned q8_0 pointer fails the alignment check.  Only
+    the host checks run (no launch)."""
+    torch = need_gpu()
+    mk = _mk()
+    import ctypes
+    st, *_ = small_stack(mk, 61, 4, 512, 1024, 768, 1000, 4, T_max=3)
+    gs = np.array([0, 3, 6, 9, 12], np.int32)
+    ctx = np.array([0, 10, 20, 30], np.int32)
+    P = 1 << 20  # aligned stand-in addresses: the checks read no memory
+
+    def ws(k=None, v=None, k8=None, ks=None, v8=None, vs=None):
+        a = mk.mk_step_attn(1, 32, 8, 64, ctx.ctypes.data, P, None, k, v, P, k8, ks, v8, vs)
+        return mk.lib().mk_decode_step_attn_workspace(st.h, 12, gs.ctypes.data, 4, ctypes.byref(a))
+
+    assert ws(k=P, v=P) > 0
+    assert ws(k8=P, ks=P, v8=P, vs=P) > 0
+    assert ws() == 0
+    assert ws(k=P, v=P, k8=P, ks=P, v8=P, vs=P) == 0
+    assert ws(k=P) == 0
+    assert ws(k8=P, ks=P, v8=P) == 0
+    assert ws(k8=P, ks=P + 2, v8=P, vs=P) == 0
