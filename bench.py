@@ -186,11 +186,12 @@ def time_steps(stack, T, gs, n_agents, xs, gins, steps, warmup, attn=None):
     return r
 
 
-def attention_step(layers, lm, gl, steps, warmup, n_attn=16, ctx=32768):
+def attention_step(layers, lm, gl, steps, warmup, q8=False, n_attn=16, ctx=32768):
     """The T = 12 step with its 16 full-attention layers' attention in the
     launch: 4 agents of 3 rows, each with `ctx` cached positions per layer
-    (fp16, 32 query / 8 KV heads of 128, gated).  Every layer's caches hold the
-    same seeded values (the bytes read per layer are what matters here)."""
+    (fp16 or q8_0 cache, 32 query / 8 KV heads of 128, gated).  Every layer's
+    caches hold the same seeded values (the bytes read per layer are what
+    matters here)."""
     import torch
 
     import bit_weight_streaming_q4_amd as mk
@@ -199,37 +200,42 @@ def attention_step(layers, lm, gl, steps, warmup, n_attn=16, ctx=32768):
     sizes = [3] * G
     cap = recipes.attn_cap([ctx] * G, sizes)
     t0 = time.time()
-    a = recipes.step_attn_inputs(n_attn, [ctx] * G, sizes, cap=cap)
-    k1, v1 = torch.from_numpy(a["k"]).to("cuda"), torch.from_numpy(a["v"]).to("cuda")
-    kc = torch.empty((n_attn,) + tuple(k1.shape), dtype=k1.dtype, device="cuda")
-    vc = torch.empty((n_attn,) + tuple(v1.shape), dtype=v1.dtype, device="cuda")
-    for i in range(n_attn):
-        kc[i].copy_(k1)
-        vc[i].copy_(v1)
-    del k1, v1
+    a = recipes.step_attn_inputs(n_attn, [ctx] * G, sizes, cap=cap, q8=q8)
+    caches = []
+    for key in (("k8", "ks", "v8", "vs") if q8 else ("k", "v")):
+        one = torch.from_numpy(a[key]).to("cuda")
+        c = torch.empty((n_attn,) + tuple(one.shape), dtype=one.dtype, device="cuda")
+        for i in range(n_attn):
+            c[i].copy_(one)
+        caches.append(c)
+        del one
     q, gate = torch.from_numpy(a["q"]).to("cuda"), torch.from_numpy(a["gate"]).to("cuda")
     o = torch.empty_like(q)
-    log(f"attention inputs: {n_attn} layers x {G} agents x {ctx} positions ({time.time() - t0:.1f}s)")
-    at = mk.step_attn(q, kc, vc, o, a["ctx"], gate=gate)
+    fmt = "q8_0" if q8 else "fp16"
+    log(f"attention inputs ({fmt}): {n_attn} layers x {G} agents x {ctx} positions ({time.time() - t0:.1f}s)")
+    at = (mk.step_attn_q8 if q8 else mk.step_attn)(q, *caches, o, a["ctx"], gate=gate)
     agents = make_agents(G, len(gl), 5)
     stack = mk.Stack(layers, lm, gdn_layers=gl, agents=agents)
     xs, gins = step_inputs(T, min(steps + warmup, 8), len(gl))
-    log(f"timing T=12 with attention")
+    log(f"timing T=12 with attention ({fmt})")
     r = time_steps(stack, T, gs, G, xs, gins, steps, warmup, attn=at)
     b = step_bytes(T, G, len(layers))
-    kv = n_attn * sum(ctx + n for n in sizes) * recipes.ATTN_KV_HEADS * 128 * 2 * 2
+    # bytes per cached position and KV head: fp16 K and V rows, or q8_0 codes
+    # (2 x 128) and scales (K: 4 per position, V: 128 per 32 positions)
+    per_pos = 2 * 128 * 2 if not q8 else 2 * 128 + 4 * 2 + 128 * 2 // 32
+    kv = n_attn * sum(ctx + n for n in sizes) * recipes.ATTN_KV_HEADS * per_pos
     io = n_attn * T * recipes.ATTN_Q_HEADS * 128 * 4 * 3
     total = b["total"] + kv + io
-    out = {"attention_layers": n_attn, "agents": G, "positions_per_agent": ctx, "rows": T,
+    out = {"cache": fmt, "attention_layers": n_attn, "agents": G, "positions_per_agent": ctx, "rows": T,
            "ms_per_step": round(r["ms_per_step"], 4), "kernel_ms": round(r["kernel_ms"], 4),
            "kernel_ms_median": round(r["kernel_ms_median"], 4),
            "attention_bytes": int(kv + io), "total_bytes": int(total),
            "total_gb_s_kernel": round(total / (r["kernel_ms"] * 1e-3) / 1e9, 1),
            "frac_of_8TBs": round(total / (r["kernel_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    log(f"T=12 with attention: kernel {r['kernel_ms']:.3f} ms, {out['total_gb_s_kernel']:.0f} GB/s over "
+    log(f"T=12 with attention ({fmt}): kernel {r['kernel_ms']:.3f} ms, {out['total_gb_s_kernel']:.0f} GB/s over "
         f"{total / 1e9:.2f} GB")
     stack.close()
-    del stack, agents, kc, vc, q, gate, o, at, xs, gins
+    del stack, agents, caches, q, gate, o, at, xs, gins
     torch.cuda.empty_cache()
     return out
 
@@ -828,8 +834,10 @@ def main():
         tj = json.load(open(TRAFFIC_FILE))
         if tj.get("kernel_source_hash") == kernel_source_hash():
             traffic = tj.get("bytes_per_launch")
-    attention = None if (args.no_attention or args.only_primary) else attention_step(layers, lm, gl, args.steps,
-                                                                                       args.warmup)
+    attention = attention_q8 = None
+    if not (args.no_attention or args.only_primary):
+        attention = attention_step(layers, lm, gl, args.steps, args.warmup)
+        attention_q8 = attention_step(layers, lm, gl, args.steps, args.warmup, q8=True)
     kernels = None if args.no_kernels else kernel_bench(lm)
     accepts = None if args.no_kernels else accept_histogram(lm)
     attainable = read_probe()
@@ -870,6 +878,7 @@ def main():
                              for T, r in sorted(results.items())},
                    "seeded_series_T12": series,
                    "with_attention_T12": attention,
+                   "with_attention_q8_T12": attention_q8,
                    "lm_head_accept_lengths": accepts,
                    "standalone_kernels": kernels},
         "manifest": manifest(seeds),

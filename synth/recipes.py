@@ -184,20 +184,23 @@ def attn_inputs(ctx, sizes, Hq=ATTN_Q_HEADS, Hkv=ATTN_KV_HEADS, d=ATTN_D, cap=No
     return {"q": q, "gate": gt, "k": kc, "v": vc, "ctx": np.asarray(ctx, np.int32), "group_start": gs}
 
 
-def step_attn_inputs(n_layers, ctx, sizes, cap=None, gate=True):
+def step_attn_inputs(n_layers, ctx, sizes, cap=None, gate=True, q8=False):
     """The full-attention layers of a decode step: q and gate [n_layers][T][Hq][d]
-    with per-layer seeds (as attn_inputs with layer = i), and one layer's K and
-    V caches (attn_inputs with layer = 0), which the caller copies into every
-    layer's cache: generating all of them takes a minute at 4 x 32768
-    positions, and the bytes each layer reads are the same either way."""
-    first = attn_inputs(ctx, sizes, cap=cap, layer=0, gate=gate)
+    with per-layer seeds (as attn_inputs with layer = i), and one layer's
+    caches (attn_inputs, or attn_inputs_q8 when q8, with layer = 0), which the
+    caller copies into every layer's cache: generating all of them takes a
+    minute at 4 x 32768 positions, and the bytes each layer reads are the same
+    either way."""
+    first = (attn_inputs_q8 if q8 else attn_inputs)(ctx, sizes, cap=cap, layer=0, gate=gate)
     T = int(sum(sizes))
     n = T * ATTN_Q_HEADS * ATTN_D
     q = np.stack([normal_f32(ATTN_SEED, 300 + i, 0, n).reshape(T, ATTN_Q_HEADS, ATTN_D) for i in range(n_layers)])
     gt = np.stack([normal_f32(ATTN_SEED, 400 + i, 0, n).reshape(T, ATTN_Q_HEADS, ATTN_D)
                    for i in range(n_layers)]) if gate else None
-    return {"q": q, "gate": gt, "k": first["k"], "v": first["v"], "ctx": first["ctx"],
-            "group_start": first["group_start"]}
+    out = {"q": q, "gate": gt, "ctx": first["ctx"], "group_start": first["group_start"]}
+    for k in (("k8", "ks", "v8", "vs") if q8 else ("k", "v")):
+        out[k] = first[k]
+    return out
 
 
 def attn_inputs_q8(ctx, sizes, Hq=ATTN_Q_HEADS, Hkv=ATTN_KV_HEADS, d=ATTN_D, cap=None, seed=ATTN_SEED, layer=0,
