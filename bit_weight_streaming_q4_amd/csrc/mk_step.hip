@@ -2600,6 +2600,7 @@ struct mk_stack {
   int plans_grid = -1;
   hipEvent_t ev[2] = {nullptr, nullptr};  // around the last launch (no device memory)
   float last_ms = -1.0f;
+  int32_t* hout = nullptr;  // pinned host copy of the output block (allocated at the first step)
 };
 
 namespace {
@@ -2904,6 +2905,7 @@ void mk_stack_destroy(mk_stack* st) {
   }
   for (int i = 0; i < 2; ++i)
     if (st->ev[i]) hipEventDestroy(st->ev[i]);
+  if (st->hout) hipHostFree(st->hout);
   delete st;
 }
 
@@ -3002,8 +3004,9 @@ int mk_decode_step_attn(mk_stack* st, float* x, int32_t T, const int32_t* h_grou
       g_ws_tables[ws] = st->tag;
     }
   }
-  if (hipMemsetAsync(w8 + y.off_ctrl, 0, y.n_ctrl, s) != hipSuccess ||
-      hipMemsetAsync(w8 + y.off_out, 0, kOutWords * 4, s) != hipSuccess ||
+  // the output block follows the control words: one reset for both
+  if (y.off_out != y.off_ctrl + y.n_ctrl) return sfail(MK_ERR_LAUNCH, "decode: workspace layout");
+  if (hipMemsetAsync(w8 + y.off_ctrl, 0, y.n_ctrl + kOutWords * 4, s) != hipSuccess ||
       (attn && hipMemsetAsync(w8 + y.total + ap.part_bytes, 0, ap.ticket_bytes, s) != hipSuccess))
     return sfail(MK_ERR_LAUNCH, "decode: control reset failed");
   StepArgs a;
@@ -3108,8 +3111,11 @@ int mk_decode_step_attn(mk_stack* st, float* x, int32_t T, const int32_t* h_grou
   if (d_argmax &&
       hipMemcpyAsync(d_argmax, w8 + y.off_out + kOutTop * 4, T * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
     return sfail(MK_ERR_LAUNCH, "decode: argmax copy failed");
-  int32_t hout[kOutWords];
-  if (hipMemcpyAsync(hout, w8 + y.off_out, sizeof(hout), hipMemcpyDeviceToHost, s) != hipSuccess ||
+  // read back into pinned memory (one DMA; a pageable copy is staged)
+  if (!st->hout && hipHostMalloc((void**)&st->hout, kOutWords * 4, hipHostMallocDefault) != hipSuccess) st->hout = nullptr;
+  int32_t hlocal[kOutWords];
+  int32_t* hout = st->hout ? st->hout : hlocal;
+  if (hipMemcpyAsync(hout, w8 + y.off_out, kOutWords * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess)
     return sfail(MK_ERR_LAUNCH, "decode: readback failed");
   st->last_ms = -1.0f;
