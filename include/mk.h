@@ -369,7 +369,9 @@ size_t mk_decode_step_workspace(const mk_stack* st, int32_t T);
  * its own tables first (host-side record per workspace).  If some other call
  * wrote the workspace in between, the kernel sees a foreign tag, nothing
  * runs, and the call returns MK_ERR_WORKSPACE; the next call uploads the
- * tables again.  Steps that share a workspace must not overlap.
+ * tables again.  Steps that share a workspace, or a stack, must not overlap
+ * (a stack also holds the pinned host buffer its steps read back into and
+ * the events around its last launch).
  * The lm_head input rows are RMSNorm outputs, so |value| <= sqrt(hidden); they
  * are multiplied by the exact power of two 2^k with sqrt(hidden) 2^k <= 2^14
  * before the fp16 split (the argmax is unchanged).
