@@ -729,6 +729,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only-primary", action="store_true", help="measure T = 12 only")
+    ap.add_argument("--rows", metavar="T,T,...", help="measure only these row counts (one verify group each, except "
+                                                      "T = 12 and 24: 4 and 8 agents of 3 rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true", help="skip the standalone entry-point timings")
     ap.add_argument("--layers", type=int, default=LAYERS)
@@ -809,6 +811,8 @@ def main():
         configs += [(T, [0, T], 1) for T in (2, 3, 4, 6, 7, 8, 9, 10, 11, 13, 14, 15, 16)]
     for T, gs, n_agents in configs:
         if args.only_primary and T != 12:
+            continue
+        if args.rows and T not in [int(t) for t in args.rows.split(",")]:
             continue
         agents = make_agents(n_agents, len(gl), max(5, gs[1] - gs[0]))  # ring rows for the longest group
         stack = mk.Stack(layers, lm, gdn_layers=gl, agents=agents)

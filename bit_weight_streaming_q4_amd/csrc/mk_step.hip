@@ -1924,14 +1924,21 @@ __device__ __forceinline__ void attn_item(const StepArgs& a, int i, int j, int l
   }
 }
 
+// WITH: the kernel instance that runs attention items (either cache
+// format).  The instance for steps without attention carries none of their
+// code: their register demand (and the q8_0 items' spilled registers) would
+// otherwise cost every step.
+template <bool WITH>
 __device__ __forceinline__ void attn_items(const StepArgs& a, int lane) {
-  if (a.n_attn <= 0) return;
-  const int per = uniform(a.attn_item0[a.G]);
-  const long total = (long)a.n_attn * per;
-  if (a.attn_q8)
-    for (long it = blockIdx.x; it < total; it += gridDim.x) attn_item<true>(a, (int)(it / per), (int)(it % per), lane);
-  else
-    for (long it = blockIdx.x; it < total; it += gridDim.x) attn_item<false>(a, (int)(it / per), (int)(it % per), lane);
+  if constexpr (WITH) {
+    if (a.n_attn <= 0) return;
+    const int per = uniform(a.attn_item0[a.G]);
+    const long total = (long)a.n_attn * per;
+    if (a.attn_q8)
+      for (long it = blockIdx.x; it < total; it += gridDim.x) attn_item<true>(a, (int)(it / per), (int)(it % per), lane);
+    else
+      for (long it = blockIdx.x; it < total; it += gridDim.x) attn_item<false>(a, (int)(it / per), (int)(it % per), lane);
+  }
 }
 
 // The block's share of every GDN layer's half-head jobs, in layer order.
@@ -2031,7 +2038,7 @@ __device__ __forceinline__ void lm_phase(const StepArgs& a, uint8_t* ring) {
 }
 
 // ------------------------------------------------------------ the kernel
-template <int T>
+template <int T, bool ATTN>
 __global__ __launch_bounds__(kBlock) void k_decode_step(StepArgs a) {
   __shared__ BlockState<T> s;
   const int lane = threadIdx.x & 63;
@@ -2069,7 +2076,7 @@ __global__ __launch_bounds__(kBlock) void k_decode_step(StepArgs a) {
     watch_wave<T>(a, s, lane);
   } else {
     gdn_wave(a, lane);
-    attn_items(a, lane);
+    attn_items<ATTN>(a, lane);
     stores_done();
     if (lane == 0) lds_st(&s.gdn_done, 1);
   }
@@ -2085,36 +2092,37 @@ __global__ __launch_bounds__(kBlock) void k_decode_step(StepArgs a) {
 typedef void (*StepKernel)(StepArgs);
 
 template <int T>
-static StepKernel kernel_for() {
-  return k_decode_step<T>;
+static StepKernel kernel_for(bool attn) {
+  return attn ? k_decode_step<T, true> : k_decode_step<T, false>;
 }
 
-static StepKernel step_kernel(int T) {
+// attn: the instance that runs attention items.
+static StepKernel step_kernel(int T, bool attn = false) {
   switch (T) {
-    case 1: return kernel_for<1>();
-    case 2: return kernel_for<2>();
-    case 3: return kernel_for<3>();
-    case 4: return kernel_for<4>();
-    case 5: return kernel_for<5>();
-    case 6: return kernel_for<6>();
-    case 7: return kernel_for<7>();
-    case 8: return kernel_for<8>();
-    case 9: return kernel_for<9>();
-    case 10: return kernel_for<10>();
-    case 11: return kernel_for<11>();
-    case 12: return kernel_for<12>();
-    case 13: return kernel_for<13>();
-    case 14: return kernel_for<14>();
-    case 15: return kernel_for<15>();
-    case 16: return kernel_for<16>();
-    case 17: return kernel_for<17>();
-    case 18: return kernel_for<18>();
-    case 19: return kernel_for<19>();
-    case 20: return kernel_for<20>();
-    case 21: return kernel_for<21>();
-    case 22: return kernel_for<22>();
-    case 23: return kernel_for<23>();
-    case 24: return kernel_for<24>();
+    case 1: return kernel_for<1>(attn);
+    case 2: return kernel_for<2>(attn);
+    case 3: return kernel_for<3>(attn);
+    case 4: return kernel_for<4>(attn);
+    case 5: return kernel_for<5>(attn);
+    case 6: return kernel_for<6>(attn);
+    case 7: return kernel_for<7>(attn);
+    case 8: return kernel_for<8>(attn);
+    case 9: return kernel_for<9>(attn);
+    case 10: return kernel_for<10>(attn);
+    case 11: return kernel_for<11>(attn);
+    case 12: return kernel_for<12>(attn);
+    case 13: return kernel_for<13>(attn);
+    case 14: return kernel_for<14>(attn);
+    case 15: return kernel_for<15>(attn);
+    case 16: return kernel_for<16>(attn);
+    case 17: return kernel_for<17>(attn);
+    case 18: return kernel_for<18>(attn);
+    case 19: return kernel_for<19>(attn);
+    case 20: return kernel_for<20>(attn);
+    case 21: return kernel_for<21>(attn);
+    case 22: return kernel_for<22>(attn);
+    case 23: return kernel_for<23>(attn);
+    case 24: return kernel_for<24>(attn);
     default: return nullptr;
   }
 }
@@ -3103,7 +3111,8 @@ int mk_decode_step_attn(mk_stack* st, float* x, int32_t T, const int32_t* h_grou
   }
   void* args[] = {&a};
   if (st->ev[0]) hipEventRecord(st->ev[0], s);
-  hipError_t e = hipLaunchCooperativeKernel((const void*)step_kernel(T), dim3(y.grid), dim3(kBlock), args, 0, s);
+  hipError_t e = hipLaunchCooperativeKernel((const void*)step_kernel(T, attn != nullptr), dim3(y.grid),
+                                            dim3(kBlock), args, 0, s);
   if (st->ev[1]) hipEventRecord(st->ev[1], s);
   if (e != hipSuccess)
     return set_error(e == hipErrorCooperativeLaunchTooLarge ? MK_ERR_COOP : MK_ERR_LAUNCH,
