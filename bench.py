@@ -698,12 +698,13 @@ def _counter_per_dispatch(d, counter, kernel_sub):
 
 
 def traffic_record(root):
-    """The traffic record of k_decode_step<12> from rocprofv3 output under
+    """The traffic record of k_decode_step<12, false> (the step without
+    attention items) from rocprofv3 output under
     root: trace/ (--kernel-trace --stats), fetch/ and write/ (--pmc FETCH_SIZE,
     WRITE_SIZE on the bench), copy_fetch/ and copy_write/ (the same counters on
     --copy-probe).  Counter values are KiB per dispatch; each is scaled by what
     the same counter reads for the plain 1 GiB copy."""
-    kern = "k_decode_step<12>"
+    kern = "k_decode_step<12, false>"
     stats = [r for r in _csv_rows(os.path.join(root, "trace"), "kernel_stats.csv") if kern in r.get("Name", "")]
     avg_ns, calls = float(stats[0]["AverageNs"]), int(stats[0]["Calls"])
     fetch, nf = _counter_per_dispatch(os.path.join(root, "fetch"), "FETCH_SIZE", kern)
@@ -905,7 +906,7 @@ def main():
         "manifest": manifest(seeds),
         "roofline": {"bound": "hbm", "achieved": round(p["kernel_gb_s"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(p["kernel_gb_s"] / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": "k_decode_step<12>", "kernel_ms": round(p["kernel_ms"], 4),
+                     "kernel": "k_decode_step<12, false>", "kernel_ms": round(p["kernel_ms"], 4),
                      "algorithmic_bytes_per_launch": p["bytes"]["total"],
                      "attainable_read_gb_s": attainable},
         "cpu_baseline": cpu,
