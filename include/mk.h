@@ -134,7 +134,9 @@ int mk_qgemv_rows(const mk_q4k* W, const float* x, int32_t T, float* y, void* ws
  * the engine the step uses for T rows (dot4 at T = 1; two sub-blocks per
  * 16x16x64 int8 matrix product up to 8 padded rows; one sub-block per
  * 16x16x32 product above), loaded by LDS-DMA two units ahead of the
- * arithmetic, one block of 4 streaming waves per CU.  Its results equal the
+ * arithmetic, one block of 4 streaming waves per CU (a block's waves hand
+ * their sums over through LDS with bounded waits; blocks never wait for
+ * each other).  Its results equal the
  * other paths' up to the order of the fp32 sums, and the step's engines can
  * be checked through it outside the persistent launch.  The workspace then
  * begins with the records, one per superblock b of x (5120 B): codes
