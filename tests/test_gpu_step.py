@@ -322,13 +322,15 @@ def test_decode_step_prompt_chunk_is_bit_identical(gs_ride, rows):
 @pytest.mark.parametrize("fmt", ["f16", "q8"])
 @pytest.mark.parametrize("ctx,sizes,cap,n_layers", [([0, 100, 517, 1000], [3, 3, 3, 3], 1024, 2),
                                                     ([0, 64, 200, 4999], [1, 4, 3, 4], 5056, 1),
-                                                    ([32768, 32768, 30000, 12345], [3, 3, 3, 3], 32832, 1)])
+                                                    ([32768, 32768, 30000, 12345], [3, 3, 3, 3], 32832, 1),
+                                                    ([0, 7, 64, 129, 500, 1000, 2047, 3000], [3] * 8, 3008, 2)])
 def test_decode_step_attention_beside_the_pipeline(ctx, sizes, cap, n_layers, fmt):
     """The full-attention layers' split-K flash decoding inside the persistent
-    step (four agents of 12 rows in all, 32 query and 8 KV heads of 128,
-    gated; fp16 caches whose unused slots hold NaN, or q8_0 caches whose
-    unused codes are out of range and unused scales NaN; an agent with no
-    cached position and one row; ragged groups of 1 to 4 rows): every layer's
+    step (four agents of 12 rows in all, or eight agents of 3 rows = 24 rows
+    on the two-record path; 32 query and 8 KV heads of 128, gated; fp16
+    caches whose unused slots hold NaN, or q8_0 caches whose unused codes are
+    out of range and unused scales NaN; an agent with no cached position and
+    one row; ragged groups of 1 to 4 rows): every layer's
     output equals the oracle's attention on that layer's inputs, and the rest
     of the step is bit-identical to the same step without attention."""
     torch = need_gpu()
@@ -336,8 +338,7 @@ def test_decode_step_attention_beside_the_pipeline(ctx, sizes, cap, n_layers, fm
     from synth import recipes
     L, H, P, F, V = 4, 512, 1024, 768, 1000
     gs = [0] + list(np.cumsum(sizes))
-    T, G = 12, 4
-    assert gs[-1] == T
+    T, G = int(gs[-1]), len(sizes)
     gen = recipes.attn_inputs if fmt == "f16" else recipes.attn_inputs_q8
     layers_in = [gen(ctx, sizes, cap=cap, layer=i) for i in range(n_layers)]
     q = to_dev(np.stack([a["q"] for a in layers_in]))
@@ -360,8 +361,9 @@ def test_decode_step_attention_beside_the_pipeline(ctx, sizes, cap, n_layers, fm
                 mk.step_attn_q8(q, *caches, o, ctx, gate=gate)
         say("decode with attention", name, ctx)
         tok, na = mk.mk_decode_step(st, to_dev(x), gs, drafts, gdn=gin, gdn_o=go, trace=tr, attn=at)
-        mk.mk_deltanet_commit(st.agents[0])
-        runs[name] = (tok, na, to_np(tr), to_np(go), to_np(st.agents[0].S))
+        for ag in st.agents:
+            mk.mk_deltanet_commit(ag)
+        runs[name] = (tok, na, to_np(tr), to_np(go)) + tuple(to_np(ag.S) for ag in st.agents)
         del st
     for a, b in zip(runs["plain"], runs["attn"]):
         assert np.array_equal(a, b)
