@@ -44,11 +44,12 @@ __device__ __forceinline__ void split_f16(const float (&x)[8], u4& hi_out, u4& l
   lo_out = as_u4(lo);
 }
 
-// One column block fits two waves per SIMD (256 registers with the matrix
-// accumulators); more column blocks run one wave per SIMD.
 // Eight q8_0 codes (two dwords of int8) -> eight fp16 values, exactly: each
 // byte, sign-flipped to c + 128, becomes the low byte of the fp16 1024 + c + 128
-// (exponent byte 0x64), and 1152 is subtracted in packed fp16.
+// (exponent byte 0x64), and 1152 is subtracted in packed fp16.  (Leaving the
+// 1152 in and removing 1152 times the other operand's block sum afterwards
+// saves the subtraction, but the cancellation costs about seven bits of the
+// fp32 products.)
 // The empty asm keeps each conversion at its use: with several column
 // blocks the compiler would otherwise hold every converted operand of the
 // tile at once and spill.
@@ -85,7 +86,9 @@ struct KVTile {
   uint2 vsc[2][8];           // Q8: V scales of dims 16db + 4grp .. +3, block t0/32 + hh
 };
 
-// V positions at or past L_g contribute nothing.
+// V positions at or past L_g contribute nothing.  In the fp16 cache they may
+// hold any bits (inf or NaN times a zero probability is NaN); q8_0 codes
+// always convert to finite values, so that format needs no masking.
 __device__ __forceinline__ u4 zero_tail(u4 r, int t0, int hh, int grp, int Lg) {
   h8 v = as_h8(r);
 #pragma unroll
@@ -152,83 +155,110 @@ __device__ __forceinline__ void load_tile(const KVHead& c, int t0, int Lg, int c
   }
 }
 
-// One column block's pass over a loaded tile: the scores of this lane's
-// column (positions below lim visible), the online softmax (running max
-// mrow, this lane's share of the sum lsum) and the P.V update of acc.
-template <bool Q8>
-__device__ __forceinline__ void tile_update(const KVTile& x, int t0, int Lg, int lim, int grp, const u4 (&qh)[4],
-                                            const u4 (&ql)[4], f4 (&acc)[8], float& mrow, float& lsum) {
-  f4 sc[4];
+// One pass over a loaded tile for NF column blocks at once, so that each
+// q8_0 code is converted once for all of them.  For column block f: the
+// scores of this lane's column (positions below lim[f] visible), the online
+// softmax (running max mrow[f], this lane's share of the sum lsum[f]) and the
+// P.V update of acc[f].  Each block's arithmetic, and its order, is the same
+// for every NF.
+template <bool Q8, int NF>
+__device__ __forceinline__ void tile_update_n(const KVTile& x, int t0, int Lg, const int* lim, int grp,
+                                              const u4 (*qh)[4], const u4 (*ql)[4], f4 (*acc)[8], float* mrow,
+                                              float* lsum) {
+  f4 sc[NF][4];
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) sc[f][b] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    f4 c = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       if constexpr (Q8) {
         const u4 kf = codes_f16(x.k8[b][m]);
-        f4 t = mma(kf, qh[m], f4{0.f, 0.f, 0.f, 0.f});
-        t = mma(kf, ql[m], t);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) c[i] += (float)as_h8(x.ksc[b][i >> 1])[(i & 1) * 4 + m] * t[i];
+        for (int f = 0; f < NF; ++f) {
+          f4 t = mma(kf, qh[f][m], f4{0.f, 0.f, 0.f, 0.f});
+          t = mma(kf, ql[f][m], t);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[f][b][i] += (float)as_h8(x.ksc[b][i >> 1])[(i & 1) * 4 + m] * t[i];
+        }
       } else {
-        c = mma(x.kr[b][m], qh[m], c);
-        c = mma(x.kr[b][m], ql[m], c);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          sc[f][b] = mma(x.kr[b][m], qh[f][m], sc[f][b]);
+          sc[f][b] = mma(x.kr[b][m], ql[f][m], sc[f][b]);
+        }
       }
     }
-    sc[b] = c;
   }
-  float tmax = -INFINITY;
+  u4 ph[NF][2], pl[NF][2];
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+  for (int f = 0; f < NF; ++f) {
+    float tmax = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int pos = t0 + 32 * (b >> 1) + 8 * grp + 4 * (b & 1) + i;
-      const float v = pos < lim ? sc[b][i] : -INFINITY;
-      sc[b][i] = v;
-      tmax = fmaxf(tmax, v);
-    }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-  const float mnew = fmaxf(mrow, tmax);
-  const float muse = mnew == -INFINITY ? 0.f : mnew;
-  const float alpha = exp2f(mrow - muse);
-  mrow = mnew;
-  float ps = 0.f;
-  float pv[2][8];
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+      for (int i = 0; i < 4; ++i) {
+        const int pos = t0 + 32 * (b >> 1) + 8 * grp + 4 * (b & 1) + i;
+        const float v = pos < lim[f] ? sc[f][b][i] : -INFINITY;
+        sc[f][b][i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mnew = fmaxf(mrow[f], tmax);
+    const float muse = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = exp2f(mrow[f] - muse);
+    mrow[f] = mnew;
+    float ps = 0.f;
+    float pv[2][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = exp2f(sc[b][i] - muse);
-      ps += p;
-      pv[b >> 1][4 * (b & 1) + i] = p;
-    }
-  u4 ph[2], pl[2];
-  split_f16(pv[0], ph[0], pl[0]);
-  split_f16(pv[1], ph[1], pl[1]);
-  lsum = lsum * alpha + ps;
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-  for (int db = 0; db < 8; ++db) acc[db] *= alpha;
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2f(sc[f][b][i] - muse);
+        ps += p;
+        pv[b >> 1][4 * (b & 1) + i] = p;
+      }
+    split_f16(pv[0], ph[f][0], pl[f][0]);
+    split_f16(pv[1], ph[f][1], pl[f][1]);
+    lsum[f] = lsum[f] * alpha + ps;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[f][db] *= alpha;
+  }
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       if constexpr (Q8) {
-        u4 vo = codes_f16(x.v8[hh][db]);
-        if (t0 + kTile > Lg) vo = zero_tail(vo, t0, hh, grp, Lg);
-        f4 t = mma(vo, ph[hh], f4{0.f, 0.f, 0.f, 0.f});
-        t = mma(vo, pl[hh], t);
+        const u4 vo = codes_f16(x.v8[hh][db]);
         // a block holding no position of this agent may carry any scale
         const bool live = t0 + 32 * hh < Lg;
-        const uint2 sv = x.vsc[hh][db];
+        const uint2 sv = live ? x.vsc[hh][db] : make_uint2(0u, 0u);
         const h8 s8 = as_h8(u4{sv.x, sv.y, 0u, 0u});
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[db][i] += (live ? (float)s8[i] : 0.f) * t[i];
+        for (int f = 0; f < NF; ++f) {
+          f4 t = mma(vo, ph[f][hh], f4{0.f, 0.f, 0.f, 0.f});
+          t = mma(vo, pl[f][hh], t);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[f][db][i] = __builtin_fmaf((float)s8[i], t[i], acc[f][db][i]);
+        }
       } else {
-        acc[db] = mma(x.vr[hh][db], ph[hh], acc[db]);
-        acc[db] = mma(x.vr[hh][db], pl[hh], acc[db]);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          acc[f][db] = mma(x.vr[hh][db], ph[f][hh], acc[f][db]);
+          acc[f][db] = mma(x.vr[hh][db], pl[f][hh], acc[f][db]);
+        }
       }
     }
+}
+
+// One column block's pass over a loaded tile.
+template <bool Q8>
+__device__ __forceinline__ void tile_update(const KVTile& x, int t0, int Lg, int lim, int grp, const u4 (&qh)[4],
+                                            const u4 (&ql)[4], f4 (&acc)[8], float& mrow, float& lsum) {
+  tile_update_n<Q8, 1>(x, t0, Lg, &lim, grp, &qh, &ql, &acc, &mrow, &lsum);
 }
 
 }  // namespace attn

@@ -48,6 +48,8 @@ constexpr int kMergeFloats = 34;  // per lane and column block: 32 outputs, max,
 // product m covers exactly the 32-dim block m of a K row, and each P.V
 // product exactly one 32-position block of a V row, so a product runs on the
 // codes (exact in fp16) and its result is scaled per row in fp32.
+// One column block fits two waves per SIMD (256 registers with the matrix
+// accumulators); more column blocks run one wave per SIMD.
 template <int NB, bool Q8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 1 ? 2 : 1)))
 void k_attn_split(const AttnArgs a) {
@@ -58,7 +60,9 @@ void k_attn_split(const AttnArgs a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   // The item count is a multiple of 4 and the grid has one block per 4 items,
   // so no wave is idle; a block's waves take splits 4q .. 4q+3 of one head.
-  const int it = blockIdx.x * kWaves + w;
+  // wave-uniform, so that everything derived from it (the item, its
+  // positions, every tile test) stays in scalar registers and branches
+  const int it = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + w);
   int g = 0;
   while (it >= a.item0[g + 1]) ++g;
   const int loc = it - a.item0[g], ns = a.nsplit[g];
@@ -121,15 +125,20 @@ void k_attn_split(const AttnArgs a) {
   for (int t0 = p0; t0 < p1; t0 += kTile) {
     KVTile x;
     load_tile<Q8>(kv, t0, Lg, col, grp, x);
+    // q8_0: column blocks in pairs where they pair up, so that each code is
+    // converted once per pair
+    constexpr int NF = Q8 && NB % 2 == 0 ? 2 : 1;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      u4 qh[4], ql[4];
+    for (int nb = 0; nb < NB; nb += NF) {
+      u4 qh[NF][4], ql[NF][4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        qh[m] = qs[(((w * NB + nb) * 4 + m) * 2 + 0) * 64 + lane];
-        ql[m] = qs[(((w * NB + nb) * 4 + m) * 2 + 1) * 64 + lane];
-      }
-      tile_update<Q8>(x, t0, Lg, lim[nb], grp, qh, ql, acc[nb], mrow[nb], lsum[nb]);
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          qh[f][m] = qs[(((w * NB + nb + f) * 4 + m) * 2 + 0) * 64 + lane];
+          ql[f][m] = qs[(((w * NB + nb + f) * 4 + m) * 2 + 1) * 64 + lane];
+        }
+      tile_update_n<Q8, NF>(x, t0, Lg, lim + nb, grp, qh, ql, acc + nb, mrow + nb, lsum + nb);
     }
   }
 
