@@ -673,6 +673,101 @@ def cpu_baseline(T=12, budget_s=20.0):
             "sample": f"{layers} of {LAYERS} layers + {lmrows} of {VOCAB} lm_head rows at T={T}, {dt:.1f} s of oracle time"}
 
 
+def cpu_entry_points():
+    """The oracle (as it stands) beside each standalone call that bench times
+    on the GPU (same names as config.standalone_kernels): one bounded sample
+    of the call's workload, timed on this host's cores and scaled by the
+    sample's share of the call.  us is the oracle's time for one whole call
+    at that scale, gb_s the call's algorithmic bytes over that time."""
+    import oracle
+    from synth import recipes
+    out = {}
+
+    def put(name, dt, scale, nbytes, sample):
+        us = dt * scale * 1e6
+        out[name] = {"us": round(us, 1), "gb_s": round(nbytes / (us * 1e-6) / 1e9, 4), "sample": sample,
+                     "oracle_s": round(dt, 3)}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return time.perf_counter() - t0, r
+
+    W = recipes.gemv_weight()
+    for T in (1, 5, 12):
+        x = recipes.rows_f32(T, HIDDEN)
+        dt, _ = timed(lambda: oracle.qgemv(W, x))
+        put(f"qgemv_5120x5120_T{T}", dt, 1, HIDDEN * HIDDEN // 256 * 144 + T * 2 * HIDDEN * 4, "the whole call")
+    del W
+    fw = recipes.ffn_weights()
+    x = recipes.rows_f32(5, HIDDEN)
+    dt, _ = timed(lambda: oracle.ffn(fw["gate"], fw["up"], fw["down"], x))
+    put("ffn_5120_17408_T5", dt, 1, 3 * HIDDEN * FFN // 256 * 144 + 5 * 2 * HIDDEN * 4, "the whole call")
+    del fw
+    # lm_head + verify and the sampling verify: 1/16 of the vocabulary
+    part = 16
+    rows = VOCAB // part
+    W16 = recipes.stack_lm_head(r1=rows)
+    hid = recipes.lm_hidden(5)
+    drafts = recipes.uniform_i32(3, 50, 0, 4, 0, rows - 1)
+    dt, _ = timed(lambda: oracle.verify(oracle.lmhead(W16, hid)["top1"], [0, 5], drafts))
+    put(f"lmhead_verify_V{VOCAB}_T5", dt, part, VOCAB * HIDDEN * 2 + 5 * HIDDEN * 4,
+        f"{rows} of {VOCAB} vocabulary rows, x {part}")
+    hid12 = recipes.lm_hidden(12, trial=1)
+    gs12 = [0, 3, 6, 9, 12]
+    dr12 = recipes.uniform_i32(3, 51, 0, 8, 0, rows - 1)
+    ua, us = recipes.uniform_f64(3, 52, 0, 12), recipes.uniform_f64(3, 53, 0, 12)
+
+    def sample_call():
+        lg = oracle.lmhead(W16, hid12, return_logits=True)["logits"]
+        ti, tv = oracle.topk_rows(lg, 32)
+        return oracle.sample_verify(ti, tv, gs12, dr12, 0.6, ua, us)
+    dt, _ = timed(sample_call)
+    put(f"lmhead_sample_V{VOCAB}_T12_k32", dt, part, VOCAB * HIDDEN * 2 + 12 * HIDDEN * 4,
+        f"{rows} of {VOCAB} vocabulary rows, x {part}")
+    del W16
+    # Gated DeltaNet step: 384 of the 1536 heads, T = 5, committed through row 4
+    nh, sh = 48 * 32, 384
+    S = recipes.gdn_initial_state().reshape(nh, 128, 128)[:sh].copy()
+    g = recipes.gdn_step(0, 5)
+    gi = [np.ascontiguousarray(g[k].reshape(5, nh, -1)[:, :sh]) for k in ("q", "k", "v")]
+    gb = [np.ascontiguousarray(g[k].reshape(5, nh)[:, :sh]) for k in ("g", "beta")]
+    dt, _ = timed(lambda: oracle.gdn_step(S, *gi, *gb, 4))
+    io = 5 * nh * (3 * 128 + 2) * 4 + 5 * nh * 128 * 4
+    put("deltanet_step_48x32_T5", dt, nh / sh, 2 * nh * 128 * 128 * 4 + io + nh * 258 * 4 * 4 * 2,
+        f"{sh} of {nh} heads, x {nh // sh}")
+    del S
+    # attention: one of the four agents at 32768 positions (3 rows), x 4
+    a = recipes.attn_inputs([32768], [3])
+    dt, _ = timed(lambda: oracle.attn_decode(a["q"], a["gate"], a["k"], a["v"], a["ctx"], a["group_start"]))
+    put("attn_decode_4x32768_T12", dt, 4, attn_bytes([32768] * 4, [3] * 4), "1 of 4 agents, x 4")
+    del a
+    a = recipes.attn_inputs_q8([32768], [3])
+    dt, _ = timed(lambda: oracle.attn_decode_q8(a["q"], a["gate"], a["k8"], a["ks"], a["v8"], a["vs"], a["ctx"],
+                                                a["group_start"]))
+    put("attn_decode_q8_4x32768_T12", dt, 4, attn_bytes_q8([32768] * 4, [3] * 4), "1 of 4 agents, x 4")
+    del a
+    # MTP draft loop, 4 agents x 3 rows, 2 drafts: the catch-up pass over the
+    # accepted rows (2 + 0 + 1 + 2, plus one each) and the second pass over
+    # one row per agent, each pass with its draft lm_head over 1/16 of the
+    # 32768-row draft vocabulary (x 16 for that part)
+    mtp = recipes.mtp_weights()
+    dv = recipes.DRAFT_VOCAB // part
+    Wd = recipes.stack_lm_head(r1=dv)
+    hidm = recipes.stack_step_input(60, 12)
+    toks = recipes.uniform_i32(3, 54, 12, 12, 0, dv - 1)
+    rows0 = [0, 1, 2, 3, 6, 7, 9, 10, 11]
+    dt0, x0 = timed(lambda: oracle.mtp_block(mtp, Wd, toks[rows0], hidm[rows0]))
+    dl0, _ = timed(lambda: oracle.lmhead(Wd, oracle.rmsnorm(x0[[2, 3, 5, 8]])))
+    dt1, x1 = timed(lambda: oracle.mtp_block(mtp, Wd, toks[:4], x0[[2, 3, 5, 8]]))
+    dl1, _ = timed(lambda: oracle.lmhead(Wd, oracle.rmsnorm(x1)))
+    head_bytes = (2 * HIDDEN * HIDDEN + 3 * HIDDEN * FFN) // 256 * 144 + recipes.DRAFT_VOCAB * HIDDEN * 2
+    put("mtp_draft_T12_G4_n2", dt0 + dt1 + part * (dl0 + dl1), 1, 2 * head_bytes,
+        f"both passes; their draft lm_head over {dv} of {recipes.DRAFT_VOCAB} rows, x {part}")
+    out["mtp_draft_T12_G4_n2"]["oracle_s"] = round(dt0 + dt1 + dl0 + dl1, 3)
+    return out
+
+
 # ------------------------------------------------------------------ HBM traffic record
 def _csv_rows(d, suffix):
     import csv
@@ -865,6 +960,8 @@ def main():
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     if cpu is not None:
         cpu["one_core"] = one_core
+        if not args.no_kernels:
+            cpu["entry_points"] = cpu_entry_points()
     seeds = {"stack": recipes.STACK_SEED, "lm_head": recipes.LM_SEED, "gdn": recipes.GDN_SEED,
              "mtp": recipes.STACK_SEED, "step_inputs": "stack seed, tensors 10000 + step and 20000 + step"}
     out = {
