@@ -686,7 +686,7 @@ def cpu_entry_points():
     def put(name, dt, scale, nbytes, sample):
         us = dt * scale * 1e6
         out[name] = {"us": round(us, 1), "gb_s": round(nbytes / (us * 1e-6) / 1e9, 4), "sample": sample,
-                              "oracle_s_per_sample": round(dt, 4)}
+                     "oracle_s_per_sample": round(dt, 4)}
 
     def timed(fn, min_s=0.25):
         """Mean time of fn over as many calls as fill min_s (at least one)."""
