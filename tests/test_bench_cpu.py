@@ -28,3 +28,23 @@ def test_algorithmic_bytes_follow_the_shapes():
     L = 131077
     assert bench.attn_bytes_q8([131072], [5]) == (L * 8 * 128 * 2 + L * 8 * 4 * 2 + ((L + 31) // 32) * 8 * 128 * 2
                                                   + 5 * 32 * 128 * 12)
+
+
+def test_oracle_beside_every_timed_call_has_a_sample_and_a_rate():
+    """The CPU leg that times the oracle beside the standalone calls runs on
+    the CPU alone and names calls that the GPU leg times, each with a
+    positive time, a rate consistent with the call's bytes, and its sample."""
+    r = bench.cpu_entry_points()
+    gpu_names = {"qgemv_5120x5120_T1", "qgemv_5120x5120_T5", "qgemv_5120x5120_T12", "ffn_5120_17408_T5",
+                 f"lmhead_verify_V{bench.VOCAB}_T5", f"lmhead_sample_V{bench.VOCAB}_T12_k32",
+                 "deltanet_step_48x32_T5", "attn_decode_4x32768_T12", "attn_decode_q8_4x32768_T12",
+                 "mtp_draft_T12_G4_n2"}
+    assert set(r) == gpu_names
+    for name, v in r.items():
+        assert v["us"] > 0 and v["oracle_s_per_sample"] > 0 and v["sample"], name
+        # scaled up, never down (oracle_s_per_sample is rounded to 0.1 ms)
+        assert v["us"] + 60 >= v["oracle_s_per_sample"] * 1e6, name
+    # the whole 5120^2 GEMV call: its rate is its bytes over its time
+    g = r["qgemv_5120x5120_T1"]
+    nbytes = 5120 * 5120 // 256 * 144 + 2 * 5120 * 4
+    assert abs(g["gb_s"] - nbytes / (g["us"] * 1e-6) / 1e9) <= 1e-3 * g["gb_s"] + 1e-4
