@@ -44,6 +44,7 @@ CASES = [
     ("T = 16, no grouped queries", [517], [16], 8, 8, False),
     ("unequal groups, many splits", [20000, 3, 777], [2, 5, 1], 32, 8, True),
     ("16 agents x 1 row", list(range(0, 1600, 100)), [1] * 16, 32, 8, True),
+    ("1 agent x 10 rows (three column blocks)", [2000], [10], 32, 8, True),
 ]
 
 
@@ -130,7 +131,8 @@ def _check_q8(orc, torch, mk, a, label):
 
 Q8_CASES = [c for c in CASES if c[0] in ("4 agents x 3 rows, ragged contexts", "1 agent x 5 rows (two column blocks)",
                                          "T = 1, ragged tail", "T = 16, one group (four column blocks)",
-                                         "unequal groups, many splits", "16 agents x 1 row")]
+                                         "unequal groups, many splits", "16 agents x 1 row",
+                                         "1 agent x 10 rows (three column blocks)")]
 
 
 @pytest.mark.parametrize("label,ctx,sizes,Hq,Hkv,gate", Q8_CASES, ids=[c[0] for c in Q8_CASES])
