@@ -72,12 +72,18 @@ def _check_head(W16, x_final, am, na, tok, gs, drafts):
 # beside two agents of three rows (each group with its own GDN state).  Above
 # 16 rows the record has two 16-row halves and the lm_head is streamed once
 # per half: 17 (one row in the second half), 20, eight agents of three rows
-# (24), and a twelve-row chunk beside four agents of three rows.
+# (24), and a twelve-row chunk beside four agents of three rows.  The other
+# row counts complete the set, so that every instance of the step (T = 1 to
+# 24) runs: 13 is the first with the epilogue's six-partial batches, 19 and 23
+# put a full 16-row group beside a short one.
 @pytest.mark.parametrize("T,gs", [(1, [0, 1]), (2, [0, 2]), (3, [0, 3]), (5, [0, 5]), (6, [0, 1, 3, 6]),
                                   (8, [0, 2, 4, 6, 8]), (9, [0, 9]), (11, [0, 11]), (12, [0, 3, 6, 9, 12]),
                                   (16, [0, 4, 8, 12, 16]), (16, list(range(0, 17, 2))), (16, [0, 10, 13, 16]),
                                   (17, [0, 8, 17]), (20, [0, 4, 8, 12, 16, 20]), (24, list(range(0, 25, 3))),
-                                  (24, [0, 3, 6, 9, 12, 24])])
+                                  (24, [0, 3, 6, 9, 12, 24]),
+                                  (4, [0, 4]), (7, [0, 3, 7]), (10, [0, 5, 10]), (13, [0, 13]), (14, [0, 7, 14]),
+                                  (15, [0, 3, 6, 9, 12, 15]), (18, [0, 9, 18]), (19, [0, 16, 19]),
+                                  (21, list(range(0, 22, 3))), (22, [0, 11, 22]), (23, [0, 16, 23])])
 def test_decode_step_small_stack(T, gs):
     torch = need_gpu()
     mk = _mk()
