@@ -388,8 +388,9 @@ def test_decode_step_attention_beside_the_pipeline(ctx, sizes, cap, n_layers, fm
 def test_decode_step_attention_cache_format_checks():
     """mk_step_attn takes exactly one cache format: neither, both, or a
     partial set of pointers gives no workspace (the call fails with
-    MK_ERR_ARG); a misaligned q8_0 pointer fails the alignment check.  Only
-    the host checks run (no launch)."""
+    MK_ERR_ARG); a misaligned q8_0 pointer fails the alignment check; shapes
+    beyond the items' limits give no workspace.  Only the host checks run (no
+    launch)."""
     torch = need_gpu()
     mk = _mk()
     import ctypes
@@ -409,3 +410,22 @@ def test_decode_step_attention_cache_format_checks():
     assert ws(k=P) == 0
     assert ws(k8=P, ks=P, v8=P) == 0
     assert ws(k8=P, ks=P + 2, v8=P, vs=P) == 0
+
+    # shapes: an agent's rows x Hq/Hkv above 16 query columns, a cache length
+    # that is not a multiple of 64 or is above MK_ATTN_CAP_MAX, cached
+    # positions + new rows above the cache length, Hq not a multiple of Hkv
+    def ws2(T, groups, ctx2, Hq=32, Hkv=8, cap=64):
+        g2 = np.array(groups, np.int32)
+        c2 = np.array(ctx2, np.int32)
+        a = mk.mk_step_attn(1, Hq, Hkv, cap, c2.ctypes.data, P, None, P, P, P, None, None, None, None)
+        return mk.lib().mk_decode_step_attn_workspace(st.h, T, g2.ctypes.data, len(groups) - 1, ctypes.byref(a))
+
+    g12, g8 = [0, 3, 6, 9, 12], [0, 2, 4, 6, 8]
+    assert ws2(12, g12, [0, 10, 20, 30]) > 0
+    assert ws2(12, g12, [0, 10, 20, 30], Hq=64) == 0  # 3 rows x 8 = 24 columns
+    assert ws2(8, g8, [0, 10, 20, 30], Hq=64) > 0  # 2 rows x 8 = 16 columns
+    assert ws2(12, g12, [0, 10, 20, 30], cap=100) == 0
+    assert ws2(12, g12, [0, 10, 20, 30], cap=mk.MK_ATTN_CAP_MAX + 64) == 0
+    assert ws2(12, g12, [0, 10, 20, 62]) == 0  # 62 + 3 > 64
+    assert ws2(12, g12, [0, 10, 20, 61]) > 0
+    assert ws2(12, g12, [0, 10, 20, 30], Hkv=12) == 0
