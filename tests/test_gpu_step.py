@@ -329,14 +329,19 @@ def test_decode_step_prompt_chunk_is_bit_identical(gs_ride, rows):
 @pytest.mark.parametrize("ctx,sizes,cap,n_layers", [([0, 100, 517, 1000], [3, 3, 3, 3], 1024, 2),
                                                     ([0, 64, 200, 4999], [1, 4, 3, 4], 5056, 1),
                                                     ([32768, 32768, 30000, 12345], [3, 3, 3, 3], 32832, 1),
-                                                    ([0, 7, 64, 129, 500, 1000, 2047, 3000], [3] * 8, 3008, 2)])
+                                                    ([0, 7, 64, 129, 500, 1000, 2047, 3000], [3] * 8, 3008, 2),
+                                                    ([500], [1], 512, 1),
+                                                    ([77, 1000], [1, 4], 1024, 1),
+                                                    ([100, 300], [4, 4], 320, 1),
+                                                    (list(range(0, 480, 30)), [1] * 16, 512, 1)])
 def test_decode_step_attention_beside_the_pipeline(ctx, sizes, cap, n_layers, fmt):
     """The full-attention layers' split-K flash decoding inside the persistent
     step (four agents of 12 rows in all, or eight agents of 3 rows = 24 rows
     on the two-record path; 32 query and 8 KV heads of 128, gated; fp16
     caches whose unused slots hold NaN, or q8_0 caches whose unused codes are
     out of range and unused scales NaN; an agent with no cached position and
-    one row; ragged groups of 1 to 4 rows): every layer's
+    one row; ragged groups of 1 to 4 rows; the instances at T = 1, 5, 8 and
+    16, the last with sixteen agents of one row): every layer's
     output equals the oracle's attention on that layer's inputs, and the rest
     of the step is bit-identical to the same step without attention."""
     torch = need_gpu()
@@ -354,7 +359,7 @@ def test_decode_step_attention_beside_the_pipeline(ctx, sizes, cap, n_layers, fm
     o = torch.full((n_layers, T, 32, 128), float("nan"), dtype=torch.float32, device="cuda")
     runs = {}
     for name in ("plain", "attn"):
-        st, _, fields, W16, S0, nh = small_stack(mk, 61, L, H, P, F, V, G, T_max=max(sizes))
+        st, _, fields, W16, S0, nh = small_stack(mk, 61, L, H, P, F, V, G, T_max=max(2, max(sizes)))
         x = synth.normal_f32(61, 10000, 0, T * H).reshape(T, H)
         inp = synth.gdn_step_inputs(61, 20000, T, nh, 128, 128)
         gin = {k: to_dev(inp[k]) for k in ("q", "k", "v", "g", "beta")}
