@@ -2891,7 +2891,7 @@ int mk_stack_create(const mk_stack_desc* desc, mk_stack** out) {
       if (!s.S || !s.ring || !s.n_acc || s.dk != 128 || s.dv != 128 ||
           s.nh != st->n_gdn_layers * kGdnHeadsPerLayer || s.T_max < 2 || s.T_max > MK_T_MAX) {
         delete st;
-        return sfail(MK_ERR_SHAPE, "stack: agent state must have dk = dv = 128 and nh = gdn layers * 32");
+        return sfail(MK_ERR_SHAPE, "stack: agent state must have dk = dv = 128, nh = gdn layers * 32 and 2 <= T_max <= 16");
       }
       st->dn.push_back(s);
     }
@@ -3136,7 +3136,7 @@ int mk_decode_step_attn(mk_stack* st, float* x, int32_t T, const int32_t* h_grou
                  "decode: the workspace no longer holds this stack's tables (another call wrote it); nothing ran, "
                  "the next call uploads them again");
   }
-  if (hout[0] & kErrWatchdog) return sfail(MK_ERR_DEVICE, "decode: grid-barrier watchdog fired");
+  if (hout[0] & kErrWatchdog) return sfail(MK_ERR_DEVICE, "decode: a bounded wait in the step ran out (watchdog)");
   if (hout[0] & kErrAccept)
     return sfail(MK_ERR_RANGE, "decode: an agent state's accept length was outside 0..T_max-1 (nothing was replayed)");
   if (hout[0]) return sfail(MK_ERR_DEVICE, "decode: device error word set");
