@@ -50,7 +50,8 @@ def test_lmhead_small_ragged_groups_ties_nan():
     mk = _mk()
     V, H = 1000, 512  # V not a multiple of 64
     W = synth.normal_f16(3, 60, 0, V * H, 0.0, 0.02).reshape(V, H)
-    for T, gs in ((5, None), (12, [0, 3, 6, 9, 12]), (1, None), (16, [0, 5, 6, 16])):
+    for T, gs in ((5, None), (12, [0, 3, 6, 9, 12]), (1, None), (16, [0, 5, 6, 16]), (2, None),
+                  (8, [0, 2, 4, 6, 8]), (9, [0, 1, 9]), (16, list(range(17)))):
         hid = synth.normal_f32(3, 61, T, T * H).reshape(T, H)
         r = oracle.lmhead(W, hid)
         G = 1 if gs is None else len(gs) - 1
