@@ -21,8 +21,8 @@ def _inputs_dev(inp):
     return [to_dev(inp[k]) for k in ("q", "k", "v", "g", "beta")]
 
 
-def _run_steps(mk, torch, S0, steps, T, accepts, nh):
-    st = mk.DeltaNetState(nh, 5, S=to_dev(S0.reshape(nh, 128, 128)))
+def _run_steps(mk, torch, S0, steps, T, accepts, nh, T_max=5):
+    st = mk.DeltaNetState(nh, T_max, S=to_dev(S0.reshape(nh, 128, 128)))
     outs = []
     for s in range(steps):
         inp = steps_inputs(s, T, nh)
@@ -39,14 +39,17 @@ def steps_inputs(s, T, nh):
     return synth.gdn_step_inputs(4, 500 + s, T, nh, 128, 128)
 
 
-def test_gdn_many_steps_vs_oracle():
+# T = 5 rows per step (the workload's), the largest ring (16 rows per step,
+# up to 15 replayed), two rows on a 16-row ring, and one row (nothing to
+# replay).
+@pytest.mark.parametrize("nh,T,T_max,steps", [(24, 5, 5, 40), (8, 16, 16, 12), (8, 2, 16, 20), (8, 1, 2, 10)])
+def test_gdn_many_steps_vs_oracle(nh, T, T_max, steps):
     torch = need_gpu()
     mk = _mk()
-    nh, T, steps = 24, 5, 40
     S0 = synth.normal_f32(4, 7, 0, nh * 128 * 128, 0.0, 0.01).reshape(nh, 128, 128)
     accepts = synth.uniform_i32(4, 8, 0, steps, 0, T - 1)
-    say("gdn", nh, T, steps)
-    Sg, outs = _run_steps(mk, torch, S0, steps, T, accepts, nh)
+    say("gdn", nh, T, T_max, steps)
+    Sg, outs = _run_steps(mk, torch, S0, steps, T, accepts, nh, T_max)
     S = S0.copy()
     for s in range(steps):
         inp = steps_inputs(s, T, nh)
