@@ -2636,19 +2636,50 @@ struct StepLayout {
   size_t frag_half;  // lm_head input fragments per 16 rows (fp16 elements)
 };
 
-int host_wave_of(long S, int W, long p) { return (int)(((p + 1) * (long)W - 1) / S); }
+// Compute waves in the order they take a line's remainder units: the waves on
+// SIMDs 2 and 3 first (those SIMDs' other waves, the watcher and the owner,
+// mostly sleep), then the one beside the GDN wave, last the one beside the
+// service wave, which sums and publishes the block's contributions as the
+// phase ends.  (Measured on the 64-layer stack: 0.4 to 0.9 % off the step
+// against an even spread; handing it to the service wave's neighbour first costs 1.2 %.)
+constexpr int kRemainderOrder[kCompute] = {2, 3, 1, 0};
+
+// The split of a line of S units over the grid's Wc compute waves, as
+// contiguous ranges in wave order: wave w takes [lo[w], lo[w + 1]).  With at
+// least one unit per wave, every wave takes S / Wc units and the S % Wc left
+// over go one each to the waves of kRemainderOrder's first entries, spread
+// evenly over the blocks; a shorter line gives one unit to each of its first
+// S waves.
+struct UnitSplit {
+  std::vector<long> lo;
+  UnitSplit(long S, long Wc) : lo(Wc + 1, S) {
+    if (S < Wc) {
+      for (long w = 0; w < S; ++w) lo[w] = w;
+      return;
+    }
+    const long nb = Wc / kCompute;
+    std::vector<long> n(Wc, S / Wc);
+    long r = S % Wc;
+    for (int t = 0; t < kCompute && r > 0; ++t) {
+      const long k = std::min(r, nb), c = kRemainderOrder[t];
+      for (long b = 0; b < nb; ++b) n[b * kCompute + c] += (b + 1) * k / nb - b * k / nb;
+      r -= k;
+    }
+    lo[0] = 0;
+    for (long w = 0; w < Wc; ++w) lo[w + 1] = lo[w] + n[w];
+  }
+  // the wave whose range holds unit p (0 <= p < S)
+  long wave_of(long p) const { return (long)(std::upper_bound(lo.begin(), lo.end(), p) - lo.begin()) - 1; }
+};
 
 // Largest number of blocks that contribute to one (tile, matrix) of a line of
 // n_tm (tile, matrix) pairs of nsb units each, split over Wc compute waves.
 int plan_cmax(long n_tm, int nsb, int Wc) {
-  const long S = n_tm * nsb;
-  if (Wc > S) Wc = (int)S;  // the line is shared by at most S waves, each with a unit or more
-  int cmax = 1;
-  for (long tm = 0; tm < n_tm; ++tm) {
-    const int c = host_wave_of(S, Wc, tm * nsb + nsb - 1) / kCompute - host_wave_of(S, Wc, tm * nsb) / kCompute + 1;
-    cmax = std::max(cmax, c);
-  }
-  return cmax;
+  const UnitSplit sp(n_tm * nsb, Wc);
+  long cmax = 1;
+  for (long tm = 0; tm < n_tm; ++tm)
+    cmax = std::max(cmax, sp.wave_of(tm * nsb + nsb - 1) / kCompute - sp.wave_of(tm * nsb) / kCompute + 1);
+  return (int)cmax;
 }
 
 StepLayout layout(const mk_stack* st, int T) {
@@ -2722,7 +2753,7 @@ StepLayout layout(const mk_stack* st, int T) {
 int sfail(int status, const char* msg) { return set_error(status, "%s", msg); }
 
 // The split of every phase kind's line of units over the grid's compute
-// waves (wave w of W takes units [S w / W, S (w + 1) / W)), written per block:
+// waves (UnitSplit), written per block:
 // each compute wave's range, the (tile, matrix) pairs the block contributes
 // to with the waves and the rank of its contribution, and the tiles it owns
 // (tile tau by block tau * grid / n_tiles) with their contributor counts.
@@ -2736,9 +2767,9 @@ bool make_plans(const mk_stack_desc& d, int grid, std::vector<BlockPlan>& out) {
   memset(out.data(), 0, sizeof(BlockPlan) * out.size());
   for (int k = 0; k < 4; ++k) {
     const long nsb = nsbs[k], S = (long)ntiles[k] * nms[k] * nsb;
-    const long W = std::min(Wc, S);
-    auto lo = [&](long w) { return w >= W ? S : S * w / W; };
-    auto wave_of = [&](long p) { return (long)(((p + 1) * W - 1) / S); };
+    const UnitSplit sp(S, Wc);
+    auto lo = [&](long w) { return sp.lo[w]; };
+    auto wave_of = [&](long p) { return sp.wave_of(p); };
     auto first_block = [&](long tm) { return wave_of(tm * nsb) / kCompute; };
     auto n_blocks = [&](long tm) { return wave_of(tm * nsb + nsb - 1) / kCompute - first_block(tm) + 1; };
     for (int b = 0; b < grid; ++b) {
