@@ -583,7 +583,8 @@ def manifest(seeds):
     with open(os.path.join(ROOT, "bench.py"), "rb") as fh:
         h.update(fh.read())
     prop = torch.cuda.get_device_properties(0)
-    m = {"gpu": torch.cuda.get_device_name(0), "arch": getattr(prop, "gcnArchName", ""),
+    m = {"gpu": torch.cuda.get_device_name(0) or HOST_FACTS.get("product") or "",
+         "arch": getattr(prop, "gcnArchName", ""),
          "compute_units": prop.multi_processor_count, "hbm_bytes": prop.total_memory,
          "torch": torch.__version__, "hip": torch.version.hip, "python": platform.python_version(),
          "host_cores": len(os.sched_getaffinity(0)), "source_sha256_16": h.hexdigest()[:16], "seeds": seeds}
@@ -599,7 +600,7 @@ def manifest(seeds):
 # Facts that come from other programs (clocks, git), gathered by host_facts()
 # before this process touches the GPU: a child process started from a process
 # that has initialised the GPU must not exec another program.
-HOST_FACTS = {"clocks": None, "git_sha": None}
+HOST_FACTS = {"clocks": None, "git_sha": None, "product": None}
 
 
 def host_facts():
@@ -610,6 +611,14 @@ def host_facts():
         card = next(iter(clk.values()), {}) if clk else {}
         HOST_FACTS["clocks"] = {k: v for k, v in card.items() if "clk" in k.lower()} or None
     except (OSError, ValueError, subprocess.SubprocessError):
+        pass
+    try:
+        r = subprocess.run(["rocm-smi", "--showproductname", "--json"], capture_output=True, text=True, timeout=20)
+        prod = json.loads(r.stdout) if r.returncode == 0 and r.stdout.strip().startswith("{") else {}
+        card = next(iter(prod.values()), {}) if prod else {}
+        name = card.get("Card Series") or card.get("Card series") or card.get("Card Model") or card.get("Card model")
+        HOST_FACTS["product"] = str(name).strip() if name and str(name).strip() not in ("N/A", "") else None
+    except (OSError, ValueError, subprocess.SubprocessError, AttributeError):
         pass
     try:
         r = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"], capture_output=True, text=True,
